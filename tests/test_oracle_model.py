@@ -1,0 +1,235 @@
+"""Looped-stack pins for the oracle: the loop equations, effective depth, weight
+sharing, KV-mode semantics and the brute-force model on tiny shapes."""
+import copy
+
+import numpy as np
+import pytest
+
+from oracle import dory_oracle as O
+from tests.bruteforce import BruteModel, weights_to_lists
+from tests.helpers import SMALL, TINY, inputs, model, rownorms
+
+
+@pytest.mark.parametrize("mode", ["per_loop", "last_loop"])
+def test_bruteforce_model_prefill_and_decode(mode):
+    cfg, W, packed = model(TINY, seed=21)
+    X = inputs(TINY, 5, seed=1)
+    D = inputs(TINY, 3, seed=1, stream=1)
+    k = 2
+    seq = O.Sequence(cfg)
+    ys = [O.prefill(cfg, W, seq, X, k, mode)]
+    for i in range(3):
+        ys.append(O.decode_step(cfg, W, seq, D[i], k, mode))
+    bm = BruteModel(TINY, weights_to_lists(TINY, packed))
+    yb = [bm.chunk(X.tolist(), list(range(5)), k, mode)]
+    for i in range(3):
+        yb.append(bm.chunk([D[i].tolist()], [5 + i], k, mode))
+    for a, b in zip(ys, yb):
+        np.testing.assert_allclose(a, np.array(b), rtol=0, atol=1e-12)
+
+
+def test_every_state_is_unit_norm():
+    cfg, W, _ = model(SMALL, seed=22)
+    X = inputs(SMALL, 6, seed=2)
+    states = []
+    y = O.forward_chunk(cfg, W, X, np.arange(6), 3, "per_loop", O.KVStore(cfg), states=states)
+    assert len(states) == cfg.n_in + 3 * (cfg.n_rec + 2) + cfg.n_out
+    for _, _, s in states:
+        np.testing.assert_allclose(rownorms(s), 1.0, atol=1e-13)
+    np.testing.assert_allclose(rownorms(y), 1.0, atol=1e-13)
+
+
+def test_first_loop_input_is_x():
+    """u_1 = N(s_0 + x) = N(2x) = x."""
+    cfg, W, _ = model(SMALL, seed=23)
+    X = inputs(SMALL, 4, seed=3)
+    states = []
+    O.forward_chunk(cfg, W, X, np.arange(4), 2, "per_loop", O.KVStore(cfg), states=states)
+    x = [s for tag, i, s in states if tag == "in"][-1]
+    u1 = [s for tag, i, s in states if tag == "u" and i == 1][0]
+    np.testing.assert_allclose(u1, x, atol=1e-15)
+
+
+@pytest.mark.parametrize("k", [1, 2, 3, 4])
+def test_effective_depth(k):
+    cfg, W, _ = model(SMALL, seed=24)
+    cnt = O.Counter()
+    O.forward_chunk(cfg, W, inputs(SMALL, 2), np.arange(2), k, "last_loop", O.KVStore(cfg), cnt)
+    assert cnt.layer_calls == O.effective_depth(cfg, k) == 2 + 1 + 2 * k
+    rec = list(range(cfg.n_in, cfg.n_in + cfg.n_rec))
+    order = [l for l, _ in cnt.trace]
+    assert order == [0, 1] + rec * k + [4]
+
+
+def test_k1_equals_plain_stack():
+    cfg, W, _ = model(TINY, seed=25)
+    X = inputs(TINY, 6, seed=4)
+    a = O.forward_chunk(cfg, W, X, np.arange(6), 1, "per_loop", O.KVStore(cfg))
+    b = O.forward_plain(cfg, W, X, np.arange(6), O.KVStore(cfg))
+    np.testing.assert_allclose(a, b, atol=1e-14)
+
+
+@pytest.mark.parametrize("k", [2, 3])
+def test_looped_equals_unrolled_with_copied_weights(k):
+    """The recurrent block applied k times equals an unrolled stack holding k
+    separate copies of the recurrent weights, with the loop-boundary operations
+    written out (pins weight and residual-rate sharing across loops)."""
+    cfg, W, _ = model(TINY, seed=26)
+    X = inputs(TINY, 5, seed=5)
+    pos = np.arange(5)
+    a = O.forward_chunk(cfg, W, X, pos, k, "per_loop", O.KVStore(cfg))
+
+    kv = O.KVStore(cfg)
+    s = X.copy()
+    for l in range(cfg.n_in):
+        s = O.layer(cfg, W[l], s, pos, l, kv, 0)
+    x = s
+    for t in range(k):
+        copies = [copy.deepcopy(W[l]) for l in range(cfg.n_in, cfg.n_in + cfg.n_rec)]
+        s = O.l2n(s + x)
+        for j, lw in enumerate(copies):
+            s = O.layer(cfg, lw, s, pos, cfg.n_in + j, kv, 100 + t)
+        s = O.l2n(s)
+    for l in range(cfg.n_in + cfg.n_rec, cfg.n_layers):
+        s = O.layer(cfg, W[l], s, pos, l, kv, 0)
+    np.testing.assert_allclose(a, s, atol=1e-14)
+
+
+def _run(cfg, W, chunks, k, mode):
+    seq = O.Sequence(cfg)
+    return np.concatenate([O.prefill(cfg, W, seq, c, k, mode) for c in chunks])
+
+
+def test_modes_agree_at_one_loop():
+    cfg, W, _ = model(TINY, seed=27)
+    X = inputs(TINY, 9, seed=6)
+    chunks = [X[:5], X[5:6], X[6:7], X[7:9]]
+    np.testing.assert_allclose(_run(cfg, W, chunks, 1, "per_loop"),
+                               _run(cfg, W, chunks, 1, "last_loop"), atol=0)
+
+
+@pytest.mark.parametrize("k", [2, 3, 4])
+def test_modes_agree_on_single_chunk_prefill(k):
+    cfg, W, _ = model(TINY, seed=28)
+    X = inputs(TINY, 7, seed=7)
+    np.testing.assert_allclose(_run(cfg, W, [X], k, "per_loop"),
+                               _run(cfg, W, [X], k, "last_loop"), atol=0)
+
+
+@pytest.mark.parametrize("k", [1, 2, 3])
+def test_per_loop_incremental_equals_recompute(k):
+    """per_loop: decoding token by token equals recomputing the whole sequence in one
+    chunk, and equals any other chunking."""
+    cfg, W, _ = model(TINY, seed=29)
+    X = inputs(TINY, 9, seed=8)
+    whole = _run(cfg, W, [X], k, "per_loop")
+    tok = _run(cfg, W, [X[i:i + 1] for i in range(9)], k, "per_loop")
+    mixed = _run(cfg, W, [X[:4], X[4:5], X[5:9]], k, "per_loop")
+    np.testing.assert_allclose(tok, whole, atol=1e-13)
+    np.testing.assert_allclose(mixed, whole, atol=1e-13)
+
+
+def _last_loop_reference(cfg, W, X, k):
+    """Token-by-token last_loop written out independently: one cache entry per
+    (layer, position), overwritten by every loop; a token's own entry is written
+    before its attention reads it."""
+    T = X.shape[0]
+    Hq, Hkv, d = cfg.n_q_heads, cfg.n_kv_heads, cfg.head_dim
+    cache = {}                                 # (layer, pos) -> (k [Hkv,d], v [Hkv,d])
+
+    def attn(l, s, p):
+        lw = W[l]
+        full = O.layer_is_full(cfg, l)
+        theta = cfg.theta_full if full else cfg.theta_swa
+        pp = np.array([p])
+        q = O.rope((s @ lw.wq.T).reshape(1, Hq, d), pp, theta)
+        kk = O.rope((s @ lw.wk.T).reshape(1, Hkv, d), pp, theta)
+        q, kk = lw.s_qk * O.l2n(q), lw.s_qk * O.l2n(kk)
+        cache[(l, p)] = (kk[0], (s @ lw.wv.T).reshape(Hkv, d))
+        vis = [j for j in range(p + 1) if full or p - j < cfg.window]
+        o = []
+        for h in range(Hq):
+            hk = h * Hkv // Hq
+            Ks = np.stack([cache[(l, j)][0][hk] for j in vis])
+            Vs = np.stack([cache[(l, j)][1][hk] for j in vis])
+            o.append(O.softmax(cfg.attn_scale * Ks @ q[0, h]) @ Vs)
+        o = O.sigmoid(s @ lw.wg.T) * np.concatenate(o)[None]
+        return O.l2n(o) @ lw.wo.T
+
+    def lay(l, s, p):
+        s = O.ngpt_update(s, attn(l, s, p), W[l].alpha_attn)
+        return O.ngpt_update(s, O.mlp(cfg, W[l], s), W[l].alpha_mlp)
+
+    ys = []
+    for p in range(T):
+        s = X[p:p + 1]
+        for l in range(cfg.n_in):
+            s = lay(l, s, p)
+        x = s
+        for _ in range(k):
+            s = O.l2n(s + x)
+            for l in range(cfg.n_in, cfg.n_in + cfg.n_rec):
+                s = lay(l, s, p)
+            s = O.l2n(s)
+        for l in range(cfg.n_in + cfg.n_rec, cfg.n_layers):
+            s = lay(l, s, p)
+        ys.append(s)
+    return np.concatenate(ys)
+
+
+@pytest.mark.parametrize("k", [2, 3])
+def test_last_loop_token_by_token_reference(k):
+    cfg, W, _ = model(TINY, seed=30)
+    X = inputs(TINY, 8, seed=9)
+    tok = _run(cfg, W, [X[i:i + 1] for i in range(8)], k, "last_loop")
+    np.testing.assert_allclose(tok, _last_loop_reference(cfg, W, X, k), atol=1e-13)
+    per = _run(cfg, W, [X[i:i + 1] for i in range(8)], k, "per_loop")
+    assert np.abs(per - tok).max() > 1e-6            # the mode is wired
+
+
+def test_last_loop_depends_on_chunk_schedule():
+    cfg, W, _ = model(TINY, seed=31)
+    X = inputs(TINY, 8, seed=10)
+    a = _run(cfg, W, [X], 2, "last_loop")
+    b = _run(cfg, W, [X[:4], X[4:]], 2, "last_loop")
+    np.testing.assert_allclose(a[:4], b[:4], atol=0)
+    assert np.abs(a[4:] - b[4:]).max() > 1e-8
+
+
+@pytest.mark.parametrize("mode", ["per_loop", "last_loop"])
+def test_zero_rate_is_identity(mode):
+    cfg, W, _ = model(TINY, seed=32)
+    for lw in W:
+        lw.alpha_attn = np.zeros_like(lw.alpha_attn)
+        lw.alpha_mlp = np.zeros_like(lw.alpha_mlp)
+    X = inputs(TINY, 5, seed=11)
+    for k in (1, 3):
+        y = _run(cfg, W, [X[:3], X[3:]], k, mode)
+        np.testing.assert_allclose(y, X, atol=1e-14)
+
+
+def test_pre_projection_norms_are_scale_only():
+    cfg, W, _ = model(SMALL, seed=33)
+    X = inputs(SMALL, 6, seed=12)
+    a = _run(cfg, W, [X[:4], X[4:]], 2, "per_loop")
+    off = copy.copy(cfg)
+    off.pre_proj_norm = False
+    b = _run(off, W, [X[:4], X[4:]], 2, "per_loop")
+    np.testing.assert_allclose(a, b, atol=1e-13)
+
+
+@pytest.mark.parametrize("mode", ["per_loop", "last_loop"])
+@pytest.mark.parametrize("k", [1, 2, 4])
+def test_slot_count(mode, k):
+    cfg, W, _ = model(SMALL, seed=34)
+    seq = O.Sequence(cfg)
+    O.prefill(cfg, W, seq, inputs(SMALL, 3), k, mode)
+    assert seq.kv.slots_used() == O.attn_slots(cfg, k, mode)
+
+
+def test_deterministic():
+    cfg, W, _ = model(TINY, seed=35)
+    X = inputs(TINY, 6, seed=13)
+    a = _run(cfg, W, [X[:2], X[2:]], 2, "last_loop")
+    b = _run(cfg, W, [X[:2], X[2:]], 2, "last_loop")
+    assert np.array_equal(a, b)
