@@ -1,0 +1,211 @@
+/*
+ * dory.h — C ABI of the MI355X (gfx950) looped normalized-GPT forward pass.
+ *
+ * The model ("Dory1.0-4B: A Looped Normalized-GPT", arXiv 2611.03998): an input block
+ * of layers runs once and yields x; a shared recurrent block runs k times as
+ *   s_0 = x,  u_t = N(s_{t-1} + x),  s_t = N(F(u_t))      (paper summary, core method)
+ * and an output block runs once. Every sublayer applies the nGPT update
+ *   s <- N((1 - a) * s + a * N(sublayer(s)))            (paper summary, nGPT; arXiv §2)
+ * with N the row-wise L2 normalisation and a a per-channel rate. A layer is an
+ * attention sublayer (GQA, RoPE, sliding-window or full, sigmoid output gate, an L2
+ * norm before the output projection) followed by a SwiGLU MLP sublayer (an L2 norm
+ * before the down projection) — paper summary "technical novelty", arXiv §2.
+ * Recurrent attention layers keep k KV slots per token (per_loop) or one slot
+ * overwritten every loop (last_loop) — arXiv §6.1, model-card digest §2.
+ *
+ * Conventions for every call:
+ *  - Return value: DORY_OK or a negative DORY_ERR_* code. On error nothing has been
+ *    launched and the context is unchanged; dory_last_error() gives a message.
+ *    DORY_ERR_HIP reports a failed HIP call (possibly from earlier asynchronous work).
+ *  - "device" pointers are HIP device memory owned by the caller; the library never
+ *    allocates or frees device memory. "host" pointers are read during the call only.
+ *  - `stream` is a hipStream_t passed as void* (NULL = the default stream). Device
+ *    work is enqueued asynchronously on it; results are valid after the stream is
+ *    synchronised. Host arrays may be reused as soon as a call returns.
+ *  - One context is used from one host thread at a time.
+ *  - Matrices are row-major. A weight W is [N_out, K_in] and a projection is
+ *    y = s W^T.
+ */
+#ifndef DORY_H
+#define DORY_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* ---- status codes */
+#define DORY_OK 0
+#define DORY_ERR_INVALID_ARG (-1) /* bad argument: shape, pointer, id, range */
+#define DORY_ERR_STATE (-2)       /* call not allowed in the context's state */
+#define DORY_ERR_OUT_OF_KV (-3)   /* the bound KV pool has too few free pages */
+#define DORY_ERR_UNSUPPORTED (-4) /* valid, but not a shape/format this build runs */
+#define DORY_ERR_HIP (-5)         /* a HIP runtime call failed */
+
+/* ---- element types */
+#define DORY_DTYPE_F32 0
+#define DORY_DTYPE_BF16 1
+/* ---- weight formats */
+#define DORY_WFMT_F32 0
+#define DORY_WFMT_BF16 1
+#define DORY_WFMT_MXFP8 2 /* E4M3 codes + one E8M0 scale byte per 32 along K */
+
+/* ---- recurrent KV-cache modes (arXiv §6.1) */
+#define DORY_KV_PER_LOOP 0  /* k slots per recurrent attention layer, slot t-1 in loop t */
+#define DORY_KV_LAST_LOOP 1 /* one slot, overwritten by every loop */
+
+/* ---- attention output gate (paper summary: input-dependent sigmoid gate) */
+#define DORY_GATE_NONE 0
+#define DORY_GATE_ELEMENTWISE 1 /* o <- sigmoid(s W_g^T) * concat_h(o_h), width Hq*d */
+
+#define DORY_PAGE_TOKENS 64        /* tokens per KV page */
+#define DORY_MAX_POSITIONS 262144  /* max_position_embeddings (MXFP8 article, config) */
+#define DORY_MAX_LOOPS 8           /* base model evaluated up to k = 8 (arXiv §3.5) */
+
+typedef struct dory_ctx dory_ctx; /* opaque, library-owned */
+
+/*
+ * Model shape and runtime limits. Layer i (global physical index) is full attention
+ * iff i % full_period == full_period - 1, else sliding-window (3:1 pattern, MXFP8
+ * article "hybrid attention"; full_period = 4). RoPE base theta_full on full layers,
+ * theta_swa on sliding layers; window W counts the query itself (keys j with
+ * 0 <= p - j < W are visible). With qk_norm the rotated per-head q and k are
+ * L2-normalised and multiplied by s_qk (nGPT); attention logits are attn_scale * q.k.
+ */
+typedef struct dory_config {
+  int32_t hidden;        /* H */
+  int32_t n_q_heads;     /* Hq */
+  int32_t n_kv_heads;    /* Hkv; Hq % Hkv == 0; query head h uses KV head h / (Hq/Hkv) */
+  int32_t head_dim;      /* d, even */
+  int32_t intermediate;  /* I, SwiGLU width */
+  int32_t n_in, n_rec, n_out; /* layers per block, each >= 1 */
+  int32_t window;        /* W >= 1 */
+  int32_t full_period;   /* >= 1 */
+  double theta_swa;
+  double theta_full;
+  float attn_scale;
+  int32_t qk_norm;       /* 0 or 1 */
+  int32_t attn_gate;     /* DORY_GATE_* */
+  int32_t act_dtype;     /* DORY_DTYPE_*: activations fed to projections and KV cache */
+  int32_t weight_format; /* DORY_WFMT_*; F32 needs act F32; BF16/MXFP8 need act BF16 */
+  int32_t max_loops;     /* 1..DORY_MAX_LOOPS */
+  int32_t max_seqs;      /* live sequences at once */
+  int32_t max_seq_len;   /* positions per sequence, <= DORY_MAX_POSITIONS */
+  int32_t max_rows;      /* rows per prefill call (sum of n_new) or per decode step */
+} dory_config;
+
+/*
+ * One physical layer's parameters (device pointers, caller-owned, must stay valid
+ * while the context uses them). Weight element type follows weight_format
+ * (float, bf16 stored as uint16, or E4M3 bytes).
+ *  w_qkvg [Hq*d + 2*Hkv*d + G, H]  rows: q | k | v | gate (G = Hq*d with the gate, else 0)
+ *  w_o    [H, Hq*d]
+ *  w_gu   [2*I, H]                 rows: SwiGLU gate | up
+ *  w_down [H, I]
+ *  s_*    MXFP8 only: E8M0 scale bytes [rows, K/32] of the matching matrix (else NULL)
+ *  alpha_attn, alpha_mlp [H] float: effective per-channel rates (arXiv §2: 0.05 init)
+ *  s_qk   [d] float: effective query-key scale
+ */
+typedef struct dory_layer_weights {
+  const void* w_qkvg;
+  const void* w_o;
+  const void* w_gu;
+  const void* w_down;
+  const uint8_t* s_qkvg;
+  const uint8_t* s_o;
+  const uint8_t* s_gu;
+  const uint8_t* s_down;
+  const float* alpha_attn;
+  const float* alpha_mlp;
+  const float* s_qk;
+} dory_layer_weights;
+
+/* Create a context for cfg. Checks shapes, formats and limits (INVALID_ARG /
+ * UNSUPPORTED). Loops default to min(2, max_loops) (MXFP8 article: default 2), mode to
+ * per_loop. Makes no HIP call. */
+int dory_create(const dory_config* cfg, dory_ctx** out);
+int dory_destroy(dory_ctx* ctx);
+/* Message of the context's last error ("" if none). ctx may be NULL for create errors
+ * (then the thread's last create message is returned). Owned by the library. */
+const char* dory_last_error(const dory_ctx* ctx);
+
+/* Sizes the caller allocates: bytes of one KV page (DORY_PAGE_TOKENS tokens of K and V
+ * for all KV heads) and the workspace the context needs. */
+int dory_query_sizes(const dory_config* cfg, size_t* page_bytes, size_t* workspace_bytes);
+/* KV pages that n_seqs sequences of seq_len tokens hold with k loops in `mode`
+ * (sliding layers keep a ring of ceil((W + max_rows - 1)/64) + 1 pages). */
+int dory_kv_pages_needed(const dory_config* cfg, int mode, int k, int64_t seq_len,
+                         int64_t n_seqs, int64_t* pages);
+
+int dory_bind_weights(dory_ctx* ctx, int layer, const dory_layer_weights* w);
+/* KV pool: device memory of `bytes` (a whole number of pages used). Only while no
+ * sequence is live (STATE). */
+int dory_bind_kv_pool(dory_ctx* ctx, void* pool, size_t bytes);
+/* Workspace: device memory, >= workspace_bytes, 256-byte aligned. It holds the page
+ * tables, so it belongs to the context until destroy or rebind (STATE while live). */
+int dory_bind_workspace(dory_ctx* ctx, void* ws, size_t bytes);
+
+/* Loop count k (1..max_loops, else INVALID_ARG). In per_loop mode returns STATE while
+ * a live sequence was built with a different k; in last_loop mode allowed any time. */
+int dory_set_loops(dory_ctx* ctx, int k);
+int dory_get_loops(const dory_ctx* ctx, int* k);
+/* KV mode (DORY_KV_*). STATE while any sequence is live. */
+int dory_set_kv_mode(dory_ctx* ctx, int mode);
+int dory_get_kv_mode(const dory_ctx* ctx, int* mode);
+
+/*
+ * Prefill: append n_new[i] tokens to sequence seq_ids[i] for i < n_seqs (host arrays).
+ * A new id starts a sequence at position 0; a live id continues it (chunked prefill).
+ * x_in  device float [sum n_new, H]: unit-norm input states, rows grouped by sequence
+ *       in seq_ids order, positions increasing.
+ * y_out device float [sum n_new, H]: final states (output of the output block).
+ * Errors: INVALID_ARG (ids repeated, n_new < 1, sum n_new > max_rows, position would
+ * reach max_seq_len, too many live sequences, null pointers), STATE (weights, pool or
+ * workspace unbound), OUT_OF_KV (pool too small; nothing reserved), HIP.
+ * In last_loop mode results depend on the chunk schedule (earlier chunks' tokens are
+ * seen with their final-loop entries).
+ */
+int dory_prefill(dory_ctx* ctx, void* stream, int n_seqs, const int32_t* seq_ids,
+                 const int32_t* n_new, const float* x_in, float* y_out);
+
+/* One decode step: one new token for each listed live sequence (a chunk of one row).
+ * x_in, y_out device float [n_seqs, H]. Errors as prefill; unknown id -> INVALID_ARG. */
+int dory_decode_step(dory_ctx* ctx, void* stream, int n_seqs, const int32_t* seq_ids,
+                     const float* x_in, float* y_out);
+
+int dory_release_seq(dory_ctx* ctx, int32_t seq_id); /* frees its pages */
+int dory_seq_len(const dory_ctx* ctx, int32_t seq_id, int64_t* len);
+int dory_live_seqs(const dory_ctx* ctx, int32_t* n);
+/* KV footprint: bytes of pages currently held by live sequences. */
+int dory_kv_bytes_in_use(const dory_ctx* ctx, size_t* bytes);
+/* Layer calls enqueued by the last prefill/decode call (host counter): E(k) =
+ * n_in + n_out + k * n_rec. */
+int dory_last_layer_calls(const dory_ctx* ctx, int64_t* n);
+
+/* ---- test and benchmark support: installing a seeded context without computing it */
+/* Extend sequence seq_id (created if new) by n_tokens positions and reserve their
+ * pages; the entries are undefined until written by dory_test_fill_kv. */
+int dory_test_reserve(dory_ctx* ctx, int32_t seq_id, int32_t n_tokens);
+/* Write entries pos0..pos0+n-1 of (layer, slot) of sequence seq_id from device arrays
+ * k, v [n, Hkv, d] in the act dtype. slot < k for recurrent layers in per_loop mode,
+ * else 0. Positions must be below the sequence length and, on sliding layers, inside
+ * the window ring. */
+int dory_test_fill_kv(dory_ctx* ctx, void* stream, int32_t seq_id, int layer, int slot,
+                      int32_t pos0, int32_t n, const void* k, const void* v);
+
+/* MXFP8 quantiser (arXiv §5.2: maximum scaling, group 32): w [rows, cols] device
+ * (w_dtype F32 or BF16), cols % 32 == 0 -> codes [rows, cols] E4M3 bytes and scales
+ * [rows, cols/32] E8M0 bytes (device). Scale 2^(floor(log2 amax) - 8), elements
+ * round-to-nearest-even with saturation at 448, all-zero group -> byte 0. */
+int dory_quantize_mxfp8(void* stream, const void* w, int w_dtype, int64_t rows,
+                        int64_t cols, uint8_t* codes, uint8_t* scales);
+
+/* Synchronise `stream` and report any pending HIP error (HIP). */
+int dory_sync(dory_ctx* ctx, void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* DORY_H */

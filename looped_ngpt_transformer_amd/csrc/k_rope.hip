@@ -1,0 +1,163 @@
+// RoPE + per-head QK normalisation + KV-cache write, and small page-table kernels.
+//
+// For each row (token at position p) of the fused [q | k | v | gate] projection:
+//  * q (Hq heads) and k (Hkv heads) are rotated: pairs (i, i + d/2) by the angle
+//    p * theta^(-2i/d), theta = 1e7 on full-attention layers and 1e4 on sliding ones
+//    (MXFP8 article, rope_parameters; arXiv §3.4);
+//  * with QK normalisation each rotated head is L2-normalised and scaled by s_qk
+//    (arXiv §2: query-key scale of the nGPT backbone);
+//  * k and v go to the row's page slot of the (layer, KV slot) stream; q and the gate
+//    pre-activation go to the attention's inputs.
+// The angle is formed and reduced modulo 2*pi in double precision (positions reach
+// 262144), then sin/cos are taken in float.
+#include "common.h"
+#include "kernels.h"
+
+namespace dory {
+
+template <typename KV>
+__device__ __forceinline__ KV* kv_page_ptr(const KVLayout& kv, int seq, int stream, int pos,
+                                           bool is_v, int head) {
+  const int lp = pos / PAGE;
+  const int32_t page =
+      kv.table[((size_t)seq * kv.n_streams + stream) * kv.tab_len + (lp % kv.ring)];
+  const size_t base = (size_t)page * kv.page_elems +
+                      (is_v ? (size_t)kv.Hkv * PAGE * kv.d : 0) +
+                      ((size_t)head * PAGE + (pos % PAGE)) * kv.d;
+  return (KV*)kv.pool + base;
+}
+
+template <typename IN, typename OUT>
+__global__ __launch_bounds__(256) void k_rope_kv(RopeArgs a) {
+  const int m = blockIdx.x;
+  const int lane = threadIdx.x & (WAVE - 1);
+  const int wave = threadIdx.x / WAVE;
+  const int d = a.d, half = d / 2;
+  const int p = a.pos[m];
+  const int seq = a.row_seq[m];
+  const size_t rowoff = (size_t)m * a.Nqkvg;
+  const size_t split_stride = (size_t)a.M * a.Nqkvg;
+  auto in = [&](int col) -> float {
+    if (a.in_f32) {
+      const float* f = (const float*)a.qkvg;
+      float t = 0.f;
+      for (int s = 0; s < a.splits; ++s) t += f[s * split_stride + rowoff + col];
+      return t;
+    }
+    return bf2f(((const bf16_t*)a.qkvg)[rowoff + col]);
+  };
+  const double ln_theta = log(a.theta);
+  OUT* qo = (OUT*)a.q_out;
+  // heads 0..Hq-1 are queries, Hq..Hq+Hkv-1 keys; one wave per head
+  for (int h = wave; h < a.Hq + a.Hkv; h += blockDim.x / WAVE) {
+    const bool is_q = h < a.Hq;
+    const int col0 = is_q ? h * d : a.Hq * d + (h - a.Hq) * d;
+    float r[4];
+    int idx[2];
+    float sq = 0.f;
+#pragma unroll
+    for (int j = 0; j < 2; ++j) {
+      const int i = lane + j * WAVE;
+      idx[j] = i;
+      if (i < half) {
+        const double freq = exp(-(2.0 * i / d) * ln_theta);
+        double ang = (double)p * freq;
+        ang -= 6.283185307179586 * rint(ang * 0.15915494309189535);
+        float sn, cs;
+        sincosf((float)ang, &sn, &cs);
+        const float x1 = in(col0 + i), x2 = in(col0 + i + half);
+        r[2 * j] = x1 * cs - x2 * sn;
+        r[2 * j + 1] = x1 * sn + x2 * cs;
+        sq += r[2 * j] * r[2 * j] + r[2 * j + 1] * r[2 * j + 1];
+      } else {
+        r[2 * j] = r[2 * j + 1] = 0.f;
+      }
+    }
+    float sc = 1.f;
+    if (a.qk_norm) sc = inv_norm(wave_sum(sq));
+#pragma unroll
+    for (int j = 0; j < 2; ++j) {
+      const int i = idx[j];
+      if (i >= half) continue;
+      float v1 = r[2 * j] * sc, v2 = r[2 * j + 1] * sc;
+      if (a.qk_norm) {
+        v1 *= a.s_qk[i];
+        v2 *= a.s_qk[i + half];
+      }
+      if (is_q) {
+        const size_t o = (size_t)m * a.Hq * d + (size_t)h * d;
+        st<OUT>(qo, o + i, v1);
+        st<OUT>(qo, o + i + half, v2);
+      } else {
+        OUT* kp = kv_page_ptr<OUT>(a.kv, seq, a.stream_idx, p, false, h - a.Hq);
+        st<OUT>(kp, i, v1);
+        st<OUT>(kp, i + half, v2);
+      }
+    }
+  }
+  // v -> V page (unrotated), gate pre-activation -> g_out
+  const int vcol0 = a.Hq * d + a.Hkv * d;
+  for (int c = threadIdx.x; c < a.Hkv * d; c += blockDim.x) {
+    const int hk = c / d, j = c % d;
+    OUT* vp = kv_page_ptr<OUT>(a.kv, seq, a.stream_idx, p, true, hk);
+    st<OUT>(vp, j, in(vcol0 + c));
+  }
+  if (a.gate) {
+    const int gcol0 = vcol0 + a.Hkv * d;
+    OUT* go = (OUT*)a.g_out;
+    for (int c = threadIdx.x; c < a.Hq * d; c += blockDim.x)
+      st<OUT>(go, (size_t)m * a.Hq * d + c, in(gcol0 + c));
+  }
+}
+
+hipError_t launch_rope_kv(const RopeArgs& a, hipStream_t st) {
+  if (a.M == 0) return hipSuccess;
+  if (a.kv.act == ACT_F32) {
+    if (!a.in_f32) return hipErrorInvalidValue;
+    hipLaunchKernelGGL((k_rope_kv<float, float>), dim3(a.M), dim3(256), 0, st, a);
+  } else {
+    hipLaunchKernelGGL((k_rope_kv<float, bf16_t>), dim3(a.M), dim3(256), 0, st, a);
+  }
+  return hipGetLastError();
+}
+
+// ------------------------------------------------------------------- page tables
+__global__ void k_apply_deltas(int32_t* table, const int32_t* deltas, int n) {
+  const int i = blockIdx.x * blockDim.x + threadIdx.x;
+  if (i < n) table[deltas[2 * i]] = deltas[2 * i + 1];
+}
+
+hipError_t launch_apply_deltas(int32_t* table, const int32_t* deltas, int n, hipStream_t st) {
+  if (n == 0) return hipSuccess;
+  hipLaunchKernelGGL(k_apply_deltas, dim3((n + 255) / 256), dim3(256), 0, st, table, deltas, n);
+  return hipGetLastError();
+}
+
+// Copy seeded K/V rows [n, Hkv, d] into the pages of one (sequence, stream).
+template <typename T>
+__global__ __launch_bounds__(256) void k_fill_kv(KVLayout kv, int seq, int stream, int pos0,
+                                                 int n, const T* k, const T* v) {
+  const int r = blockIdx.x;  // row
+  if (r >= n) return;
+  const int p = pos0 + r;
+  const int hd = kv.Hkv * kv.d;
+  for (int c = threadIdx.x; c < hd; c += blockDim.x) {
+    const int hk = c / kv.d, j = c % kv.d;
+    kv_page_ptr<T>(kv, seq, stream, p, false, hk)[j] = k[(size_t)r * hd + c];
+    kv_page_ptr<T>(kv, seq, stream, p, true, hk)[j] = v[(size_t)r * hd + c];
+  }
+}
+
+hipError_t launch_fill_kv(const KVLayout& kv, int seq_slot, int stream_idx, int pos0, int n,
+                          const void* k, const void* v, hipStream_t st) {
+  if (n == 0) return hipSuccess;
+  if (kv.act == ACT_F32)
+    hipLaunchKernelGGL(k_fill_kv<float>, dim3(n), dim3(256), 0, st, kv, seq_slot, stream_idx,
+                       pos0, n, (const float*)k, (const float*)v);
+  else
+    hipLaunchKernelGGL(k_fill_kv<bf16_t>, dim3(n), dim3(256), 0, st, kv, seq_slot, stream_idx,
+                       pos0, n, (const bf16_t*)k, (const bf16_t*)v);
+  return hipGetLastError();
+}
+
+}  // namespace dory

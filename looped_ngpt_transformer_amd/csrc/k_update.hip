@@ -1,0 +1,135 @@
+// Fused nGPT residual update and loop boundary (one work-group per row).
+//
+// s <- N((1 - a) * s + a * N(y))  — the nGPT update ("Dory1.0-4B" paper summary,
+// nGPT prerequisite; arXiv summary §2: normalised sublayer output blended with the
+// normalised residual by per-channel rates, then normalised). y arrives as split-K
+// partial sums and, when the producer did not apply it, with the pre-projection
+// L2 norm still to apply as a row scale (arXiv §2: L2 norm of the gated attention
+// output / SwiGLU activation before the output projection).
+// Loop boundaries (paper summary, core-method equation): at the end of the input block
+// x is saved and u_1 = N(x + x); at the end of loop t, s_t = N(.) and, unless t = k,
+// u_{t+1} = N(s_t + x).
+//
+// Each row's 2560-wide reductions are wave shuffles plus one LDS exchange across the
+// block's 4 waves; the row stays in registers between the reductions.
+#include "common.h"
+#include "kernels.h"
+
+namespace dory {
+
+constexpr int UPD_THREADS = 256;
+constexpr int UPD_MAXPER = 16;  // H <= 4096
+
+template <typename SB>
+__global__ __launch_bounds__(UPD_THREADS) void k_update(UpdateArgs u) {
+  __shared__ float red[UPD_THREADS / WAVE];
+  const int m = blockIdx.x;
+  const int H = u.H;
+  const size_t row = (size_t)m * H;
+  float v[UPD_MAXPER];
+  float rs = 1.f;
+  if (u.rs_ss) {
+    float t = 0.f;
+    for (int j = 0; j < u.rs_n; ++j) t += u.rs_ss[(size_t)m * u.rs_n + j];
+    rs = inv_norm(t);
+  }
+  float sq = 0.f;
+#pragma unroll
+  for (int k = 0; k < UPD_MAXPER; ++k) {
+    const int i = threadIdx.x + k * UPD_THREADS;
+    float y = 0.f;
+    if (i < H) {
+      for (int s = 0; s < u.splits; ++s) y += u.y[(size_t)s * u.M * H + row + i];
+      y *= rs;
+    }
+    v[k] = y;
+    sq += y * y;
+  }
+  const float ny = inv_norm(block_sum<UPD_THREADS / WAVE>(sq, red));
+  sq = 0.f;
+#pragma unroll
+  for (int k = 0; k < UPD_MAXPER; ++k) {
+    const int i = threadIdx.x + k * UPD_THREADS;
+    if (i < H) {
+      const float a = u.alpha[i];
+      const float t = (1.f - a) * u.s[row + i] + a * (v[k] * ny);
+      v[k] = t;
+      sq += t * t;
+    }
+  }
+  float n = inv_norm(block_sum<UPD_THREADS / WAVE>(sq, red));
+#pragma unroll
+  for (int k = 0; k < UPD_MAXPER; ++k) v[k] *= n;
+
+  if (u.bnd == BND_LOOP_CONTINUE || u.bnd == BND_LOOP_FINAL) {  // s_t = N(F(u_t))
+    sq = 0.f;
+#pragma unroll
+    for (int k = 0; k < UPD_MAXPER; ++k) sq += v[k] * v[k];
+    n = inv_norm(block_sum<UPD_THREADS / WAVE>(sq, red));
+#pragma unroll
+    for (int k = 0; k < UPD_MAXPER; ++k) v[k] *= n;
+  }
+  if (u.bnd == BND_SAVE_X || u.bnd == BND_LOOP_CONTINUE) {  // u = N(s + x)
+    sq = 0.f;
+#pragma unroll
+    for (int k = 0; k < UPD_MAXPER; ++k) {
+      const int i = threadIdx.x + k * UPD_THREADS;
+      if (i < H) {
+        float xv;
+        if (u.bnd == BND_SAVE_X) {
+          xv = v[k];
+          u.x[row + i] = xv;
+        } else {
+          xv = u.x[row + i];
+        }
+        v[k] += xv;
+        sq += v[k] * v[k];
+      }
+    }
+    n = inv_norm(block_sum<UPD_THREADS / WAVE>(sq, red));
+#pragma unroll
+    for (int k = 0; k < UPD_MAXPER; ++k) v[k] *= n;
+  }
+  SB* sb = (SB*)u.sb;
+#pragma unroll
+  for (int k = 0; k < UPD_MAXPER; ++k) {
+    const int i = threadIdx.x + k * UPD_THREADS;
+    if (i < H) {
+      u.s_out[row + i] = v[k];
+      if (sb) st<SB>(sb, row + i, v[k]);
+    }
+  }
+}
+
+template <typename SB>
+__global__ __launch_bounds__(256) void k_stage_input(const float* x, float* s, SB* sb, size_t n) {
+  for (size_t i = blockIdx.x * (size_t)blockDim.x + threadIdx.x; i < n;
+       i += (size_t)gridDim.x * blockDim.x) {
+    const float v = x[i];
+    s[i] = v;
+    st<SB>(sb, i, v);
+  }
+}
+
+hipError_t launch_update(const UpdateArgs& u, hipStream_t st) {
+  if (u.M == 0) return hipSuccess;
+  if (u.act == ACT_F32)
+    hipLaunchKernelGGL(k_update<float>, dim3(u.M), dim3(UPD_THREADS), 0, st, u);
+  else
+    hipLaunchKernelGGL(k_update<bf16_t>, dim3(u.M), dim3(UPD_THREADS), 0, st, u);
+  return hipGetLastError();
+}
+
+hipError_t launch_stage_input(const float* x_in, float* s, void* sb, int M, int H, int act,
+                              hipStream_t st) {
+  const size_t n = (size_t)M * H;
+  if (n == 0) return hipSuccess;
+  const int blocks = (int)((n + 255) / 256 < 4096 ? (n + 255) / 256 : 4096);
+  if (act == ACT_F32)
+    hipLaunchKernelGGL(k_stage_input<float>, dim3(blocks), dim3(256), 0, st, x_in, s, (float*)sb, n);
+  else
+    hipLaunchKernelGGL(k_stage_input<bf16_t>, dim3(blocks), dim3(256), 0, st, x_in, s, (bf16_t*)sb, n);
+  return hipGetLastError();
+}
+
+}  // namespace dory

@@ -1,0 +1,140 @@
+// Host-side launchers of the HIP kernels. Each returns the launch's hipError_t and
+// enqueues on `st`; argument shapes are checked by the caller (runtime.cpp) before
+// any launch.
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace dory {
+
+enum ActType { ACT_F32 = 0, ACT_BF16 = 1 };
+enum WFmt { W_F32 = 0, W_BF16 = 1, W_MXFP8 = 2 };
+
+// ---------------------------------------------------------------- GEMM  C = A B^T
+enum Epi {
+  EPI_F32 = 0,          // C float [M, N] (fp32 path; "partial" with one split)
+  EPI_PARTIAL = 1,      // C float [splits][M][N], split-K partial sums
+  EPI_STORE_ACT = 2,    // C bf16 [M, N]
+  EPI_F32_ROWSCALE = 3, // C float [M, N] scaled by 1/||row|| from sumsq partials rs_ss
+  EPI_SWIGLU = 4,       // rows [0, n_half) gate, [n_half, 2 n_half) up: C bf16 [M, n_half]
+                        // = SiLU(gate) * up, plus per-row sumsq partials into ss_out
+};
+
+struct GemmArgs {
+  const void* A = nullptr;  // [M, K] activations (act type), row stride lda
+  int lda = 0;
+  const void* B = nullptr;  // [N, K] weights (wfmt), row stride K
+  const uint8_t* Bs = nullptr;  // MXFP8 scales [N, K/32]
+  int M = 0, N = 0, K = 0;
+  int act = ACT_BF16;
+  int wfmt = W_BF16;
+  int epi = EPI_F32;
+  int splits = 1;
+  void* C = nullptr;
+  int ldc = 0;
+  const float* rs_ss = nullptr;  // [M, rs_n] sumsq partials of A's rows (ROWSCALE)
+  int rs_n = 0;
+  float* ss_out = nullptr;       // [M, ss_n] written by SWIGLU
+  int ss_n = 0;                  // set by the launcher: partial count per row
+  int n_half = 0;
+};
+// Number of sumsq partials per row the SWIGLU epilogue writes for this shape.
+int gemm_swiglu_ss_parts(const GemmArgs& g);
+// Split count the launcher would use for a decode-shaped GEMM (EPI_PARTIAL).
+int gemm_pick_splits(int M, int N, int K, int wfmt);
+hipError_t launch_gemm(const GemmArgs& g, hipStream_t st);
+
+// ------------------------------------------------------- nGPT update / loop boundary
+enum Boundary {
+  BND_NONE = 0,
+  BND_SAVE_X = 1,        // x <- s'; s <- N(s' + x)             (end of the input block)
+  BND_LOOP_CONTINUE = 2, // s_t = N(s'); s <- N(s_t + x)        (end of loop t < k)
+  BND_LOOP_FINAL = 3,    // s <- N(s')                          (end of loop k)
+};
+struct UpdateArgs {
+  const float* y = nullptr;  // [splits][M][H] raw sublayer output (partial sums)
+  int splits = 1;
+  const float* rs_ss = nullptr;  // optional [M, rs_n] sumsq partials (pre-projection norm)
+  int rs_n = 0;
+  float* s = nullptr;        // [M, H] state, updated in place
+  float* s_out = nullptr;    // where the new state goes (== s, or the caller's output)
+  void* sb = nullptr;        // [M, H] act-type copy of the new state (GEMM operand)
+  float* x = nullptr;        // [M, H] loop input x
+  const float* alpha = nullptr;  // [H]
+  int M = 0, H = 0;
+  int act = ACT_BF16;
+  int bnd = BND_NONE;
+};
+hipError_t launch_update(const UpdateArgs& u, hipStream_t st);
+// s = x_in; sb = act(x_in)
+hipError_t launch_stage_input(const float* x_in, float* s, void* sb, int M, int H, int act,
+                              hipStream_t st);
+
+// ------------------------------------------------------------ RoPE + QK norm + KV write
+struct KVLayout {
+  void* pool = nullptr;      // page pool base
+  int act = ACT_BF16;        // element type of K/V
+  int Hkv = 0, d = 0;
+  size_t page_elems = 0;     // elements per page (K and V)
+  const int32_t* table = nullptr;  // [max_seqs][n_streams][tab_len]
+  int n_streams = 0, tab_len = 0;
+  int ring = 0;              // ring length (pages) of this stream, tab_len for full layers
+};
+struct RopeArgs {
+  const void* qkvg = nullptr;  // bf16 [M, Nqkvg] or float [splits][M][Nqkvg]
+  int in_f32 = 0;
+  int splits = 1;
+  int M = 0, Hq = 0, Hkv = 0, d = 0, Nqkvg = 0, gate = 0;
+  const int32_t* pos = nullptr;      // [M]
+  const int32_t* row_seq = nullptr;  // [M] sequence slot
+  double theta = 1e4;
+  int qk_norm = 1;
+  const float* s_qk = nullptr;  // [d]
+  void* q_out = nullptr;        // act [M, Hq*d]
+  void* g_out = nullptr;        // act [M, Hq*d] (gate pre-activation)
+  KVLayout kv;
+  int stream_idx = 0;           // (layer, slot) stream within the sequence
+};
+hipError_t launch_rope_kv(const RopeArgs& a, hipStream_t st);
+
+// ------------------------------------------------------------------------ attention
+struct AttnArgs {
+  const void* q = nullptr;        // act [M, Hq*d] (rotated, normalised)
+  const void* g = nullptr;        // act [M, Hq*d] gate pre-activation (or null)
+  int M = 0, Hq = 0, Hkv = 0, d = 0;
+  const int32_t* pos = nullptr;
+  const int32_t* row_seq = nullptr;
+  int window = 0;                 // 0 = full attention
+  float scale = 1.f;
+  KVLayout kv;
+  int stream_idx = 0;
+  int max_pos = 0;                // largest position among the rows (host-known)
+  float* part = nullptr;          // [M][Hq][splits][d + 2] split partials (workspace)
+  int part_cap = 0;               // capacity of part in floats
+  void* o = nullptr;              // act [M, Hq*d]
+  float* ss = nullptr;            // [M, Hq] sumsq of the gated output, per head
+  // prefill tiles (chunks of consecutive rows of one sequence), MFMA path
+  const int32_t* tiles = nullptr; // [n_tiles][4]: row0, nrows, pos0, seq slot
+  int n_tiles = 0;
+  int max_tile_rows = 0;
+};
+// Row-wise paged attention (any row count; split over keys) + combine + gate.
+hipError_t launch_attn_rows(const AttnArgs& a, hipStream_t st);
+// Prefill attention on bf16 with MFMA (query tiles of 64 rows); writes o and ss.
+hipError_t launch_attn_prefill(const AttnArgs& a, hipStream_t st);
+size_t attn_rows_part_floats(int M, int Hq, int d, int max_pos, int window);
+
+// -------------------------------------------------------------------- SwiGLU reduce
+// h = SiLU(sum_s gate) * (sum_s up) from float partials [splits][M][2I]; h act [M, I];
+// ss [M, ss_n] per-row sumsq partials.
+hipError_t launch_swiglu(const float* gu, int splits, int M, int I, void* h, int act,
+                         float* ss, int ss_n, hipStream_t st);
+
+// ------------------------------------------------------------------ page table etc.
+hipError_t launch_apply_deltas(int32_t* table, const int32_t* deltas, int n, hipStream_t st);
+hipError_t launch_fill_kv(const KVLayout& kv, int seq_slot, int stream_idx, int pos0, int n,
+                          const void* k, const void* v, hipStream_t st);
+hipError_t launch_quantize_mxfp8(const void* w, int w_bf16, int64_t rows, int64_t cols,
+                                 uint8_t* codes, uint8_t* scales, hipStream_t st);
+
+}  // namespace dory

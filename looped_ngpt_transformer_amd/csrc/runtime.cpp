@@ -1,0 +1,927 @@
+// Host runtime behind include/dory.h: context, argument checks, the paged KV cache
+// (page allocator, per-(layer, slot) page tables, sliding-window rings) and the layer
+// schedule of the looped forward pass.
+//
+// Schedule ("Dory1.0-4B", paper summary core-method equation; arXiv §3.2): input block
+// layers once (KV slot 0); x saved at its end and u_1 = N(x + x); the recurrent block
+// k times with KV slot t-1 (per_loop) or 0 (last_loop), ending each loop with
+// s_t = N(.) and u_{t+1} = N(s_t + x); the output block once (slot 0).
+// KV slots (arXiv §6.1): per_loop keeps k slots per recurrent attention layer,
+// last_loop one slot that every loop overwrites.
+#include <hip/hip_runtime.h>
+
+#include <algorithm>
+#include <cmath>
+#include <cstdarg>
+#include <cstdio>
+#include <cstring>
+#include <map>
+#include <set>
+#include <string>
+#include <vector>
+
+#include "../../include/dory.h"
+#include "kernels.h"
+
+using namespace dory;
+
+namespace {
+
+constexpr int NSTAGE = 4;          // pinned staging buffers in rotation
+constexpr int DELTA_CAP = 65536;   // page-table updates per upload
+constexpr int SKINNY_M = 128;      // rows up to which projections use split-K tiles
+constexpr size_t ALIGN = 256;
+
+thread_local std::string g_create_err;
+
+size_t al(size_t x) { return (x + ALIGN - 1) / ALIGN * ALIGN; }
+
+struct Dims {
+  int H, Hq, Hkv, d, I, Nq, Nkv, Ng, Nqkvg, L;
+  int n_streams, tab_len, ring_swa;
+  size_t esz;          // act element size
+  size_t page_elems;   // elements per page (K and V)
+  size_t page_bytes;
+  int ss_h_n;          // sumsq partials per row of the SwiGLU activation
+  int max_tiles;
+};
+
+struct WsLayout {
+  size_t table, meta, s, x, sb, qkvg, q, g, o, h, part, ss_o, ss_h, apart, total;
+  size_t part_floats, apart_floats;
+  size_t meta_ints;
+};
+
+Dims dims_of(const dory_config& c) {
+  Dims D{};
+  D.H = c.hidden;
+  D.Hq = c.n_q_heads;
+  D.Hkv = c.n_kv_heads;
+  D.d = c.head_dim;
+  D.I = c.intermediate;
+  D.Nq = D.Hq * D.d;
+  D.Nkv = D.Hkv * D.d;
+  D.Ng = c.attn_gate == DORY_GATE_ELEMENTWISE ? D.Nq : 0;
+  D.Nqkvg = D.Nq + 2 * D.Nkv + D.Ng;
+  D.L = c.n_in + c.n_rec + c.n_out;
+  D.n_streams = c.n_in + c.n_rec * c.max_loops + c.n_out;
+  D.tab_len = (c.max_seq_len + DORY_PAGE_TOKENS - 1) / DORY_PAGE_TOKENS;
+  const int ring = (c.window + c.max_rows - 1 + DORY_PAGE_TOKENS - 1) / DORY_PAGE_TOKENS + 1;
+  D.ring_swa = std::min(ring, D.tab_len);
+  D.esz = c.act_dtype == DORY_DTYPE_F32 ? 4 : 2;
+  D.page_elems = (size_t)2 * D.Hkv * DORY_PAGE_TOKENS * D.d;
+  D.page_bytes = D.page_elems * D.esz;
+  D.ss_h_n = c.act_dtype == DORY_DTYPE_BF16 ? std::max(1, (D.I / 64) * 2) : 1;
+  D.max_tiles = (c.max_rows + 63) / 64 + c.max_seqs;
+  return D;
+}
+
+WsLayout layout_of(const dory_config& c, const Dims& D) {
+  WsLayout W{};
+  const size_t R = (size_t)c.max_rows;
+  size_t off = 0;
+  auto take = [&](size_t bytes) {
+    const size_t o = off;
+    off += al(bytes);
+    return o;
+  };
+  W.table = take((size_t)c.max_seqs * D.n_streams * D.tab_len * 4);
+  W.meta_ints = 2 * R + 4 * (size_t)D.max_tiles + 2 * (size_t)DELTA_CAP;
+  W.meta = take(W.meta_ints * 4);
+  W.s = take(R * D.H * 4);
+  W.x = take(R * D.H * 4);
+  W.sb = take(R * D.H * D.esz);
+  W.qkvg = take(R * D.Nqkvg * D.esz);
+  W.q = take(R * D.Nq * D.esz);
+  W.g = take(R * D.Nq * D.esz);
+  W.o = take(R * D.Nq * D.esz);
+  W.h = take(R * D.I * D.esz);
+  const size_t maxN = std::max({(size_t)D.Nqkvg, (size_t)2 * D.I, (size_t)D.H});
+  size_t pf = R * maxN;  // one split at max rows (fp32 path, prefill outputs)
+  if (c.act_dtype == DORY_DTYPE_BF16) pf = std::max(pf, (size_t)16 * std::min<size_t>(R, SKINNY_M) * maxN);
+  W.part_floats = pf;
+  W.part = take(pf * 4);
+  W.ss_o = take(R * D.Hq * 4);
+  W.ss_h = take(R * D.ss_h_n * 4);
+  W.apart_floats = std::max<size_t>(R, 256) * D.Hq * (D.d + 2) * 8;
+  W.apart = take(W.apart_floats * 4);
+  W.total = off;
+  return W;
+}
+
+struct Seq {
+  int32_t id = 0;
+  int slot = 0;
+  int64_t len = 0;
+  int k_built = 1;
+  int rec_slots = 1;
+  std::vector<std::vector<int32_t>> pages;  // per stream: table entries (-1 = none)
+};
+
+}  // namespace
+
+struct dory_ctx {
+  dory_config cfg{};
+  Dims D{};
+  WsLayout W{};
+  int k = 2;
+  int mode = DORY_KV_PER_LOOP;
+  std::vector<dory_layer_weights> lw;
+  std::vector<bool> lw_bound;
+  void* pool = nullptr;
+  size_t pool_bytes = 0;
+  int64_t n_pages = 0;
+  std::vector<int32_t> free_pages;
+  char* ws = nullptr;
+  size_t ws_bytes = 0;
+  std::map<int32_t, Seq> seqs;
+  std::vector<int> free_slots;
+  std::vector<int32_t> pending;  // (flat table index, page) pairs
+  std::string err;
+  int64_t last_calls = 0;
+  bool dev_ready = false;
+  int32_t* stage[NSTAGE] = {};
+  hipEvent_t ev[NSTAGE] = {};
+  int stage_i = 0;
+  std::vector<int32_t> scratch;
+
+  int fail(int code, const char* fmt, ...) {
+    char buf[512];
+    va_list ap;
+    va_start(ap, fmt);
+    vsnprintf(buf, sizeof buf, fmt, ap);
+    va_end(ap);
+    err = buf;
+    return code;
+  }
+  bool is_full(int l) const { return l % cfg.full_period == cfg.full_period - 1; }
+  int stream_of(int l, int slot) const {
+    if (l < cfg.n_in) return l;
+    if (l < cfg.n_in + cfg.n_rec) return cfg.n_in + (l - cfg.n_in) * cfg.max_loops + slot;
+    return cfg.n_in + cfg.n_rec * cfg.max_loops + (l - cfg.n_in - cfg.n_rec);
+  }
+  int ring_of(int l) const { return is_full(l) ? D.tab_len : D.ring_swa; }
+  int layer_of_stream(int s) const {
+    if (s < cfg.n_in) return s;
+    if (s < cfg.n_in + cfg.n_rec * cfg.max_loops) return cfg.n_in + (s - cfg.n_in) / cfg.max_loops;
+    return s - cfg.n_rec * cfg.max_loops + cfg.n_rec;
+  }
+  bool stream_used(const Seq& q, int s) const {
+    if (s < cfg.n_in || s >= cfg.n_in + cfg.n_rec * cfg.max_loops) return true;
+    return (s - cfg.n_in) % cfg.max_loops < q.rec_slots;
+  }
+};
+
+namespace {
+
+int hip_fail(dory_ctx* c, hipError_t e, const char* what) {
+  return c->fail(DORY_ERR_HIP, "%s: %s", what, hipGetErrorString(e));
+}
+
+#define HIPCHK(expr, what)                      \
+  do {                                          \
+    hipError_t e_ = (expr);                     \
+    if (e_ != hipSuccess) return hip_fail(ctx, e_, what); \
+  } while (0)
+
+int check_config(const dory_config* c, std::string& msg) {
+  auto bad = [&](const char* m) {
+    msg = m;
+    return DORY_ERR_INVALID_ARG;
+  };
+  auto uns = [&](const char* m) {
+    msg = m;
+    return DORY_ERR_UNSUPPORTED;
+  };
+  if (!c) return bad("null config");
+  if (c->hidden < 1 || c->n_q_heads < 1 || c->n_kv_heads < 1 || c->head_dim < 2 ||
+      c->intermediate < 1)
+    return bad("shape fields must be positive");
+  if (c->n_q_heads % c->n_kv_heads) return bad("n_q_heads must be a multiple of n_kv_heads");
+  if (c->head_dim % 2) return bad("head_dim must be even");
+  if (c->n_in < 1 || c->n_rec < 1 || c->n_out < 1) return bad("each block needs >= 1 layer");
+  if (c->window < 1 || c->full_period < 1) return bad("window and full_period must be >= 1");
+  if (!(c->theta_swa > 0) || !(c->theta_full > 0) || !std::isfinite(c->attn_scale))
+    return bad("RoPE bases must be > 0 and attn_scale finite");
+  if (c->qk_norm != 0 && c->qk_norm != 1) return bad("qk_norm must be 0 or 1");
+  if (c->attn_gate != DORY_GATE_NONE && c->attn_gate != DORY_GATE_ELEMENTWISE)
+    return bad("attn_gate must be DORY_GATE_NONE or DORY_GATE_ELEMENTWISE");
+  if (c->act_dtype != DORY_DTYPE_F32 && c->act_dtype != DORY_DTYPE_BF16) return bad("bad act_dtype");
+  if (c->weight_format < DORY_WFMT_F32 || c->weight_format > DORY_WFMT_MXFP8)
+    return bad("bad weight_format");
+  if ((c->weight_format == DORY_WFMT_F32) != (c->act_dtype == DORY_DTYPE_F32))
+    return bad("F32 weights go with F32 activations; BF16/MXFP8 weights with BF16");
+  if (c->max_loops < 1 || c->max_loops > DORY_MAX_LOOPS) return bad("max_loops must be 1..8");
+  if (c->max_seqs < 1 || c->max_rows < 1) return bad("max_seqs and max_rows must be >= 1");
+  if (c->max_seq_len < 1 || c->max_seq_len > DORY_MAX_POSITIONS)
+    return bad("max_seq_len must be 1..262144");
+  // what the kernels of this build run
+  const int G = c->n_q_heads / c->n_kv_heads;
+  if (G > 4) return uns("more than 4 query heads per KV head");
+  if (c->head_dim % 8 || c->head_dim > 256) return uns("head_dim must be a multiple of 8, <= 256");
+  if (c->hidden > 4096) return uns("hidden > 4096");
+  if (c->act_dtype == DORY_DTYPE_BF16) {
+    const int Nq = c->n_q_heads * c->head_dim;
+    const int Nqkvg = Nq + 2 * c->n_kv_heads * c->head_dim +
+                      (c->attn_gate == DORY_GATE_ELEMENTWISE ? Nq : 0);
+    if (c->hidden % 128 || Nq % 64 || c->intermediate % 64 || Nqkvg % 128)
+      return uns("bf16 shapes need hidden % 128, Hq*d % 64, I % 64, qkvg rows % 128 == 0");
+  }
+  if (c->act_dtype == DORY_DTYPE_F32 && c->head_dim * 4 * 2 * 64 > 49152)
+    return uns("fp32 head_dim too large for the attention tile");
+  const double tab = (double)c->max_seqs * (c->n_in + c->n_out + c->n_rec * c->max_loops) *
+                     ((c->max_seq_len + 63) / 64);
+  if (tab > 2e9) return uns("page table too large");
+  return DORY_OK;
+}
+
+int64_t pages_for_stream(int64_t len, bool full, int ring) {
+  const int64_t np = (len + DORY_PAGE_TOKENS - 1) / DORY_PAGE_TOKENS;
+  return full ? np : std::min<int64_t>(np, ring);
+}
+
+// Pages a sequence must newly allocate to grow from len0 to len1.
+int64_t pages_to_grow(const dory_ctx* c, const Seq& q, int64_t len1) {
+  int64_t need = 0;
+  for (int s = 0; s < c->D.n_streams; ++s) {
+    if (!c->stream_used(q, s)) continue;
+    const int l = c->layer_of_stream(s);
+    need += pages_for_stream(len1, c->is_full(l), c->ring_of(l)) -
+            pages_for_stream(q.len, c->is_full(l), c->ring_of(l));
+  }
+  return need;
+}
+
+void grow(dory_ctx* c, Seq& q, int64_t len1) {
+  const int64_t len0 = q.len;
+  for (int s = 0; s < c->D.n_streams; ++s) {
+    if (!c->stream_used(q, s)) continue;
+    const int l = c->layer_of_stream(s);
+    const int ring = c->ring_of(l);
+    auto& tab = q.pages[s];
+    const bool full = c->is_full(l);
+    if (!full && tab.empty()) tab.assign(ring, -1);
+    // logical pages [ceil(len0/64), ceil(len1/64)) are new; page lp lives in entry lp % ring
+    const int64_t lp0 = (len0 + DORY_PAGE_TOKENS - 1) / DORY_PAGE_TOKENS;
+    const int64_t lp1 = (len1 + DORY_PAGE_TOKENS - 1) / DORY_PAGE_TOKENS;
+    for (int64_t lp = lp0; lp < lp1; ++lp) {
+      const int idx = (int)(lp % ring);
+      if (full && (int64_t)tab.size() <= lp) tab.resize(lp + 1, -1);
+      if (tab[idx] < 0) {
+        tab[idx] = c->free_pages.back();
+        c->free_pages.pop_back();
+        const int64_t flat = ((int64_t)q.slot * c->D.n_streams + s) * c->D.tab_len + idx;
+        c->pending.push_back((int32_t)flat);
+        c->pending.push_back(tab[idx]);
+      }
+    }
+  }
+  q.len = len1;
+}
+
+void release(dory_ctx* c, Seq& q) {
+  for (auto& tab : q.pages)
+    for (int32_t p : tab)
+      if (p >= 0) c->free_pages.push_back(p);
+  c->free_slots.push_back(q.slot);
+}
+
+int dev_init(dory_ctx* ctx) {
+  if (ctx->dev_ready) return DORY_OK;
+  const size_t bytes = ctx->W.meta_ints * 4;
+  for (int i = 0; i < NSTAGE; ++i) {
+    HIPCHK(hipHostMalloc((void**)&ctx->stage[i], bytes, hipHostMallocDefault), "hipHostMalloc");
+    HIPCHK(hipEventCreateWithFlags(&ctx->ev[i], hipEventDisableTiming), "hipEventCreate");
+  }
+  ctx->dev_ready = true;
+  return DORY_OK;
+}
+
+// Copy n ints to the workspace's metadata area through a pinned staging buffer.
+int upload(dory_ctx* ctx, hipStream_t st, const int32_t* src, size_t n) {
+  if (n == 0) return DORY_OK;
+  const int i = ctx->stage_i++ % NSTAGE;
+  HIPCHK(hipEventSynchronize(ctx->ev[i]), "hipEventSynchronize");
+  memcpy(ctx->stage[i], src, n * 4);
+  HIPCHK(hipMemcpyAsync(ctx->ws + ctx->W.meta, ctx->stage[i], n * 4, hipMemcpyHostToDevice, st),
+         "hipMemcpyAsync");
+  HIPCHK(hipEventRecord(ctx->ev[i], st), "hipEventRecord");
+  return DORY_OK;
+}
+
+// Apply pending page-table updates beyond what fits with the call's own metadata.
+int flush_deltas(dory_ctx* ctx, hipStream_t st, size_t keep) {
+  while (ctx->pending.size() / 2 > keep) {
+    const size_t n = std::min<size_t>(ctx->pending.size() / 2, DELTA_CAP);
+    const size_t start = ctx->pending.size() - 2 * n;
+    int r = upload(ctx, st, ctx->pending.data() + start, 2 * n);
+    if (r) return r;
+    HIPCHK(launch_apply_deltas((int32_t*)(ctx->ws + ctx->W.table), (const int32_t*)(ctx->ws + ctx->W.meta),
+                               (int)n, st), "apply_deltas");
+    ctx->pending.resize(start);
+  }
+  return DORY_OK;
+}
+
+bool bound(dory_ctx* ctx) {
+  if (!ctx->pool || !ctx->ws) return false;
+  for (bool b : ctx->lw_bound)
+    if (!b) return false;
+  return true;
+}
+
+struct CallPlan {
+  int M = 0;
+  int max_pos = 0;
+  int n_tiles = 0;
+  int max_tile_rows = 0;
+};
+
+KVLayout kv_layout(dory_ctx* ctx, int l) {
+  KVLayout kv;
+  kv.pool = ctx->pool;
+  kv.act = ctx->cfg.act_dtype == DORY_DTYPE_F32 ? ACT_F32 : ACT_BF16;
+  kv.Hkv = ctx->D.Hkv;
+  kv.d = ctx->D.d;
+  kv.page_elems = ctx->D.page_elems;
+  kv.table = (const int32_t*)(ctx->ws + ctx->W.table);
+  kv.n_streams = ctx->D.n_streams;
+  kv.tab_len = ctx->D.tab_len;
+  kv.ring = ctx->ring_of(l);
+  return kv;
+}
+
+int run_layer(dory_ctx* ctx, hipStream_t st, const CallPlan& P, int l, int slot, int bnd,
+              float* out) {
+  const dory_config& c = ctx->cfg;
+  const Dims& D = ctx->D;
+  const WsLayout& W = ctx->W;
+  char* ws = ctx->ws;
+  const dory_layer_weights& w = ctx->lw[l];
+  const int M = P.M;
+  const int act = c.act_dtype == DORY_DTYPE_F32 ? ACT_F32 : ACT_BF16;
+  const int wf = c.weight_format == DORY_WFMT_F32 ? W_F32 : (c.weight_format == DORY_WFMT_BF16 ? W_BF16 : W_MXFP8);
+  const bool f32 = act == ACT_F32;
+  const bool skinny = !f32 && M <= SKINNY_M;
+  const int32_t* meta = (const int32_t*)(ws + W.meta);
+  float* part = (float*)(ws + W.part);
+  float* s = (float*)(ws + W.s);
+  float* ss_o = (float*)(ws + W.ss_o);
+  float* ss_h = (float*)(ws + W.ss_h);
+
+  auto gemm = [&](const void* A, int K, const void* B, const uint8_t* Bs, int N, int epi, void* C,
+                  int ldc, int splits) {
+    GemmArgs g;
+    g.A = A;
+    g.lda = K;
+    g.B = B;
+    g.Bs = Bs;
+    g.M = M;
+    g.N = N;
+    g.K = K;
+    g.act = act;
+    g.wfmt = wf;
+    g.epi = epi;
+    g.splits = splits;
+    g.C = C;
+    g.ldc = ldc;
+    return g;
+  };
+  auto update = [&](int splits, const float* rs, int rs_n, const float* alpha, int b, float* sout) {
+    UpdateArgs u;
+    u.y = part;
+    u.splits = splits;
+    u.rs_ss = rs;
+    u.rs_n = rs_n;
+    u.s = s;
+    u.s_out = sout ? sout : s;
+    u.sb = ws + W.sb;
+    u.x = (float*)(ws + W.x);
+    u.alpha = alpha;
+    u.M = M;
+    u.H = D.H;
+    u.act = act;
+    u.bnd = b;
+    return launch_update(u, st);
+  };
+
+  // ---- attention sublayer: [q|k|v|g] projection
+  int S = 1;
+  RopeArgs ra;
+  if (f32) {
+    HIPCHK(launch_gemm(gemm(ws + W.sb, D.H, w.w_qkvg, nullptr, D.Nqkvg, EPI_F32, part, D.Nqkvg, 1), st), "gemm qkvg");
+    ra.qkvg = part;
+    ra.in_f32 = 1;
+  } else if (skinny) {
+    S = gemm_pick_splits(M, D.Nqkvg, D.H, wf);
+    HIPCHK(launch_gemm(gemm(ws + W.sb, D.H, w.w_qkvg, w.s_qkvg, D.Nqkvg, EPI_PARTIAL, part, D.Nqkvg, S), st), "gemm qkvg");
+    ra.qkvg = part;
+    ra.in_f32 = 1;
+  } else {
+    HIPCHK(launch_gemm(gemm(ws + W.sb, D.H, w.w_qkvg, w.s_qkvg, D.Nqkvg, EPI_STORE_ACT, ws + W.qkvg, D.Nqkvg, 1), st), "gemm qkvg");
+    ra.qkvg = ws + W.qkvg;
+    ra.in_f32 = 0;
+  }
+  const bool full = ctx->is_full(l);
+  const int sidx = ctx->stream_of(l, slot);
+  ra.splits = S;
+  ra.M = M;
+  ra.Hq = D.Hq;
+  ra.Hkv = D.Hkv;
+  ra.d = D.d;
+  ra.Nqkvg = D.Nqkvg;
+  ra.gate = D.Ng > 0;
+  ra.pos = meta;
+  ra.row_seq = meta + c.max_rows;
+  ra.theta = full ? c.theta_full : c.theta_swa;
+  ra.qk_norm = c.qk_norm;
+  ra.s_qk = w.s_qk;
+  ra.q_out = ws + W.q;
+  ra.g_out = ws + W.g;
+  ra.kv = kv_layout(ctx, l);
+  ra.stream_idx = sidx;
+  HIPCHK(launch_rope_kv(ra, st), "rope_kv");
+
+  AttnArgs aa;
+  aa.q = ws + W.q;
+  aa.g = D.Ng ? ws + W.g : nullptr;
+  aa.M = M;
+  aa.Hq = D.Hq;
+  aa.Hkv = D.Hkv;
+  aa.d = D.d;
+  aa.pos = meta;
+  aa.row_seq = meta + c.max_rows;
+  aa.window = full ? 0 : c.window;
+  aa.scale = c.attn_scale;
+  aa.kv = ra.kv;
+  aa.stream_idx = sidx;
+  aa.max_pos = P.max_pos;
+  aa.part = (float*)(ws + W.apart);
+  aa.part_cap = (int)std::min<size_t>(W.apart_floats, 0x7fffffff);
+  aa.o = ws + W.o;
+  aa.ss = ss_o;
+  aa.tiles = meta + 2 * c.max_rows;
+  aa.n_tiles = P.n_tiles;
+  aa.max_tile_rows = P.max_tile_rows;
+  HIPCHK(launch_attn_rows(aa, st), "attention");
+
+  // ---- output projection + nGPT update (pre-projection norm as a row scale)
+  if (f32) {
+    HIPCHK(launch_gemm(gemm(ws + W.o, D.Nq, w.w_o, nullptr, D.H, EPI_F32, part, D.H, 1), st), "gemm o");
+    HIPCHK(update(1, ss_o, D.Hq, w.alpha_attn, BND_NONE, nullptr), "update attn");
+  } else if (skinny) {
+    S = gemm_pick_splits(M, D.H, D.Nq, wf);
+    HIPCHK(launch_gemm(gemm(ws + W.o, D.Nq, w.w_o, w.s_o, D.H, EPI_PARTIAL, part, D.H, S), st), "gemm o");
+    HIPCHK(update(S, ss_o, D.Hq, w.alpha_attn, BND_NONE, nullptr), "update attn");
+  } else {
+    GemmArgs g = gemm(ws + W.o, D.Nq, w.w_o, w.s_o, D.H, EPI_F32_ROWSCALE, part, D.H, 1);
+    g.rs_ss = ss_o;
+    g.rs_n = D.Hq;
+    HIPCHK(launch_gemm(g, st), "gemm o");
+    HIPCHK(update(1, nullptr, 0, w.alpha_attn, BND_NONE, nullptr), "update attn");
+  }
+
+  // ---- MLP sublayer
+  if (f32 || skinny) {
+    S = f32 ? 1 : gemm_pick_splits(M, 2 * D.I, D.H, wf);
+    HIPCHK(launch_gemm(gemm(ws + W.sb, D.H, w.w_gu, w.s_gu, 2 * D.I, f32 ? EPI_F32 : EPI_PARTIAL, part, 2 * D.I, S), st), "gemm gu");
+    HIPCHK(launch_swiglu(part, S, M, D.I, ws + W.h, act, ss_h, D.ss_h_n, st), "swiglu");
+    S = f32 ? 1 : gemm_pick_splits(M, D.H, D.I, wf);
+    HIPCHK(launch_gemm(gemm(ws + W.h, D.I, w.w_down, w.s_down, D.H, f32 ? EPI_F32 : EPI_PARTIAL, part, D.H, S), st), "gemm down");
+    HIPCHK(update(S, ss_h, D.ss_h_n, w.alpha_mlp, bnd, out), "update mlp");
+  } else {
+    GemmArgs g = gemm(ws + W.sb, D.H, w.w_gu, w.s_gu, 2 * D.I, EPI_SWIGLU, ws + W.h, D.I, 1);
+    g.n_half = D.I;
+    g.ss_out = ss_h;
+    if (gemm_swiglu_ss_parts(g) != D.ss_h_n) return ctx->fail(DORY_ERR_UNSUPPORTED, "swiglu partials");
+    HIPCHK(launch_gemm(g, st), "gemm gu");
+    GemmArgs g2 = gemm(ws + W.h, D.I, w.w_down, w.s_down, D.H, EPI_F32_ROWSCALE, part, D.H, 1);
+    g2.rs_ss = ss_h;
+    g2.rs_n = D.ss_h_n;
+    HIPCHK(launch_gemm(g2, st), "gemm down");
+    HIPCHK(update(1, nullptr, 0, w.alpha_mlp, bnd, out), "update mlp");
+  }
+  return DORY_OK;
+}
+
+int run_forward(dory_ctx* ctx, hipStream_t st, const CallPlan& P, const float* x_in, float* y_out) {
+  const dory_config& c = ctx->cfg;
+  char* ws = ctx->ws;
+  const int act = c.act_dtype == DORY_DTYPE_F32 ? ACT_F32 : ACT_BF16;
+  HIPCHK(launch_stage_input(x_in, (float*)(ws + ctx->W.s), ws + ctx->W.sb, P.M, ctx->D.H, act, st),
+         "stage_input");
+  int64_t calls = 0;
+  int r;
+  for (int l = 0; l < c.n_in; ++l) {
+    if ((r = run_layer(ctx, st, P, l, 0, l == c.n_in - 1 ? BND_SAVE_X : BND_NONE, nullptr))) return r;
+    ++calls;
+  }
+  for (int t = 1; t <= ctx->k; ++t) {
+    const int slot = ctx->mode == DORY_KV_PER_LOOP ? t - 1 : 0;
+    for (int l = c.n_in; l < c.n_in + c.n_rec; ++l) {
+      int b = BND_NONE;
+      if (l == c.n_in + c.n_rec - 1) b = t < ctx->k ? BND_LOOP_CONTINUE : BND_LOOP_FINAL;
+      if ((r = run_layer(ctx, st, P, l, slot, b, nullptr))) return r;
+      ++calls;
+    }
+  }
+  const int L = c.n_in + c.n_rec + c.n_out;
+  for (int l = c.n_in + c.n_rec; l < L; ++l) {
+    if ((r = run_layer(ctx, st, P, l, 0, BND_NONE, l == L - 1 ? y_out : nullptr))) return r;
+    ++calls;
+  }
+  ctx->last_calls = calls;
+  return DORY_OK;
+}
+
+// Shared body of prefill and decode: rows of each sequence, grown by n_new[i].
+int step(dory_ctx* ctx, hipStream_t st, int n, const int32_t* ids, const int32_t* n_new,
+         const float* x_in, float* y_out, bool decode) {
+  const dory_config& c = ctx->cfg;
+  if (!bound(ctx)) return ctx->fail(DORY_ERR_STATE, "weights, KV pool and workspace must be bound");
+  if (n < 1 || !ids || (!decode && !n_new) || !x_in || !y_out)
+    return ctx->fail(DORY_ERR_INVALID_ARG, "null argument or n_seqs < 1");
+  std::set<int32_t> seen;
+  int64_t rows = 0;
+  int n_newseq = 0;
+  for (int i = 0; i < n; ++i) {
+    if (!seen.insert(ids[i]).second) return ctx->fail(DORY_ERR_INVALID_ARG, "sequence id %d repeated", ids[i]);
+    const int64_t nn = decode ? 1 : n_new[i];
+    if (nn < 1) return ctx->fail(DORY_ERR_INVALID_ARG, "n_new[%d] < 1", i);
+    auto it = ctx->seqs.find(ids[i]);
+    const int64_t len = it == ctx->seqs.end() ? 0 : it->second.len;
+    if (it == ctx->seqs.end()) {
+      if (decode) return ctx->fail(DORY_ERR_INVALID_ARG, "decode of unknown sequence %d", ids[i]);
+      ++n_newseq;
+    }
+    if (len + nn > c.max_seq_len)
+      return ctx->fail(DORY_ERR_INVALID_ARG, "sequence %d would reach position %lld >= max_seq_len %d",
+                       ids[i], (long long)(len + nn - 1), c.max_seq_len);
+    rows += nn;
+  }
+  if (rows > c.max_rows) return ctx->fail(DORY_ERR_INVALID_ARG, "%lld rows > max_rows %d", (long long)rows, c.max_rows);
+  if ((int64_t)ctx->seqs.size() + n_newseq > c.max_seqs)
+    return ctx->fail(DORY_ERR_INVALID_ARG, "more than max_seqs %d live sequences", c.max_seqs);
+  // pages (transactional)
+  int64_t need = 0;
+  for (int i = 0; i < n; ++i) {
+    auto it = ctx->seqs.find(ids[i]);
+    Seq probe;
+    if (it != ctx->seqs.end()) probe = it->second;
+    else probe.rec_slots = ctx->mode == DORY_KV_PER_LOOP ? ctx->k : 1;
+    need += pages_to_grow(ctx, probe, probe.len + (decode ? 1 : n_new[i]));
+  }
+  if (need > (int64_t)ctx->free_pages.size())
+    return ctx->fail(DORY_ERR_OUT_OF_KV, "need %lld KV pages, %zu free", (long long)need, ctx->free_pages.size());
+  // per_loop sequences were built for one k
+  if (ctx->mode == DORY_KV_PER_LOOP)
+    for (int i = 0; i < n; ++i) {
+      auto it = ctx->seqs.find(ids[i]);
+      if (it != ctx->seqs.end() && it->second.k_built != ctx->k)
+        return ctx->fail(DORY_ERR_STATE, "sequence %d holds KV for k=%d", ids[i], it->second.k_built);
+    }
+  int r = dev_init(ctx);
+  if (r) return r;
+
+  // commit: create, grow, build row metadata
+  std::vector<int32_t>& meta = ctx->scratch;
+  const int R = c.max_rows;
+  meta.assign(2 * (size_t)R + 4 * (size_t)ctx->D.max_tiles, 0);
+  CallPlan P;
+  int row = 0;
+  for (int i = 0; i < n; ++i) {
+    auto it = ctx->seqs.find(ids[i]);
+    if (it == ctx->seqs.end()) {
+      Seq q;
+      q.id = ids[i];
+      q.slot = ctx->free_slots.back();
+      ctx->free_slots.pop_back();
+      q.k_built = ctx->k;
+      q.rec_slots = ctx->mode == DORY_KV_PER_LOOP ? ctx->k : 1;
+      q.pages.assign(ctx->D.n_streams, {});
+      it = ctx->seqs.emplace(ids[i], std::move(q)).first;
+    }
+    Seq& q = it->second;
+    const int nn = decode ? 1 : n_new[i];
+    const int64_t p0 = q.len;
+    grow(ctx, q, q.len + nn);
+    for (int j = 0; j < nn; ++j) {
+      meta[row + j] = (int32_t)(p0 + j);
+      meta[R + row + j] = q.slot;
+    }
+    for (int j = 0; j < nn; j += 64) {  // prefill tiles of <= 64 rows
+      int32_t* tl = &meta[2 * R + 4 * P.n_tiles];
+      tl[0] = row + j;
+      tl[1] = std::min(64, nn - j);
+      tl[2] = (int32_t)(p0 + j);
+      tl[3] = q.slot;
+      ++P.n_tiles;
+    }
+    P.max_tile_rows = std::min(64, std::max(P.max_tile_rows, nn));
+    P.max_pos = std::max<int>(P.max_pos, (int)(p0 + nn - 1));
+    row += nn;
+  }
+  P.M = row;
+  // deltas: whatever does not fit goes first in separate uploads
+  if ((r = flush_deltas(ctx, st, DELTA_CAP))) return r;
+  const size_t nd = ctx->pending.size() / 2;
+  meta.insert(meta.end(), ctx->pending.begin(), ctx->pending.end());
+  ctx->pending.clear();
+  if ((r = upload(ctx, st, meta.data(), meta.size()))) return r;
+  if (nd)
+    HIPCHK(launch_apply_deltas((int32_t*)(ctx->ws + ctx->W.table),
+                               (const int32_t*)(ctx->ws + ctx->W.meta) + 2 * R + 4 * ctx->D.max_tiles,
+                               (int)nd, st), "apply_deltas");
+  return run_forward(ctx, st, P, x_in, y_out);
+}
+
+}  // namespace
+
+// ============================================================================ C ABI
+extern "C" {
+
+int dory_create(const dory_config* cfg, dory_ctx** out) {
+  if (!out) {
+    g_create_err = "null output pointer";
+    return DORY_ERR_INVALID_ARG;
+  }
+  *out = nullptr;
+  std::string msg;
+  const int r = check_config(cfg, msg);
+  if (r) {
+    g_create_err = msg;
+    return r;
+  }
+  dory_ctx* c = new dory_ctx();
+  c->cfg = *cfg;
+  c->D = dims_of(*cfg);
+  c->W = layout_of(*cfg, c->D);
+  c->k = std::min(2, cfg->max_loops);
+  c->lw.assign(c->D.L, dory_layer_weights{});
+  c->lw_bound.assign(c->D.L, false);
+  for (int i = cfg->max_seqs - 1; i >= 0; --i) c->free_slots.push_back(i);
+  g_create_err.clear();
+  *out = c;
+  return DORY_OK;
+}
+
+int dory_destroy(dory_ctx* ctx) {
+  if (!ctx) return DORY_ERR_INVALID_ARG;
+  for (int i = 0; i < NSTAGE; ++i) {
+    if (ctx->ev[i]) {
+      (void)hipEventSynchronize(ctx->ev[i]);
+      (void)hipEventDestroy(ctx->ev[i]);
+    }
+    if (ctx->stage[i]) (void)hipHostFree(ctx->stage[i]);
+  }
+  delete ctx;
+  return DORY_OK;
+}
+
+const char* dory_last_error(const dory_ctx* ctx) {
+  return ctx ? ctx->err.c_str() : g_create_err.c_str();
+}
+
+int dory_query_sizes(const dory_config* cfg, size_t* page_bytes, size_t* workspace_bytes) {
+  std::string msg;
+  const int r = check_config(cfg, msg);
+  if (r) {
+    g_create_err = msg;
+    return r;
+  }
+  const Dims D = dims_of(*cfg);
+  if (page_bytes) *page_bytes = D.page_bytes;
+  if (workspace_bytes) *workspace_bytes = layout_of(*cfg, D).total;
+  return DORY_OK;
+}
+
+int dory_kv_pages_needed(const dory_config* cfg, int mode, int k, int64_t seq_len, int64_t n_seqs,
+                         int64_t* pages) {
+  std::string msg;
+  const int r = check_config(cfg, msg);
+  if (r) {
+    g_create_err = msg;
+    return r;
+  }
+  if (!pages || (mode != DORY_KV_PER_LOOP && mode != DORY_KV_LAST_LOOP) || k < 1 ||
+      k > cfg->max_loops || seq_len < 0 || n_seqs < 0) {
+    g_create_err = "bad argument";
+    return DORY_ERR_INVALID_ARG;
+  }
+  const Dims D = dims_of(*cfg);
+  int64_t per = 0;
+  const int L = D.L;
+  for (int l = 0; l < L; ++l) {
+    const bool full = l % cfg->full_period == cfg->full_period - 1;
+    const bool rec = l >= cfg->n_in && l < cfg->n_in + cfg->n_rec;
+    const int slots = rec && mode == DORY_KV_PER_LOOP ? k : 1;
+    per += slots * pages_for_stream(seq_len, full, full ? D.tab_len : D.ring_swa);
+  }
+  *pages = per * n_seqs;
+  return DORY_OK;
+}
+
+int dory_bind_weights(dory_ctx* ctx, int layer, const dory_layer_weights* w) {
+  if (!ctx) return DORY_ERR_INVALID_ARG;
+  if (layer < 0 || layer >= ctx->D.L) return ctx->fail(DORY_ERR_INVALID_ARG, "layer %d out of range", layer);
+  if (!w || !w->w_qkvg || !w->w_o || !w->w_gu || !w->w_down || !w->alpha_attn || !w->alpha_mlp || !w->s_qk)
+    return ctx->fail(DORY_ERR_INVALID_ARG, "null weight pointer");
+  if (ctx->cfg.weight_format == DORY_WFMT_MXFP8 && (!w->s_qkvg || !w->s_o || !w->s_gu || !w->s_down))
+    return ctx->fail(DORY_ERR_INVALID_ARG, "MXFP8 weights need scale arrays");
+  const uintptr_t mask = 15;
+  if (((uintptr_t)w->w_qkvg | (uintptr_t)w->w_o | (uintptr_t)w->w_gu | (uintptr_t)w->w_down) & mask)
+    return ctx->fail(DORY_ERR_INVALID_ARG, "weight matrices must be 16-byte aligned");
+  ctx->lw[layer] = *w;
+  ctx->lw_bound[layer] = true;
+  return DORY_OK;
+}
+
+int dory_bind_kv_pool(dory_ctx* ctx, void* pool, size_t bytes) {
+  if (!ctx) return DORY_ERR_INVALID_ARG;
+  if (!ctx->seqs.empty()) return ctx->fail(DORY_ERR_STATE, "sequences are live");
+  if (!pool || ((uintptr_t)pool & 255)) return ctx->fail(DORY_ERR_INVALID_ARG, "pool must be non-null, 256-byte aligned");
+  const int64_t n = (int64_t)(bytes / ctx->D.page_bytes);
+  if (n < 1) return ctx->fail(DORY_ERR_INVALID_ARG, "pool smaller than one page (%zu bytes)", ctx->D.page_bytes);
+  if (n > 0x7fffffff) return ctx->fail(DORY_ERR_INVALID_ARG, "too many pages");
+  ctx->pool = pool;
+  ctx->pool_bytes = bytes;
+  ctx->n_pages = n;
+  ctx->free_pages.clear();
+  for (int64_t i = n - 1; i >= 0; --i) ctx->free_pages.push_back((int32_t)i);
+  return DORY_OK;
+}
+
+int dory_bind_workspace(dory_ctx* ctx, void* ws, size_t bytes) {
+  if (!ctx) return DORY_ERR_INVALID_ARG;
+  if (!ctx->seqs.empty()) return ctx->fail(DORY_ERR_STATE, "sequences are live");
+  if (!ws || ((uintptr_t)ws & 255)) return ctx->fail(DORY_ERR_INVALID_ARG, "workspace must be non-null, 256-byte aligned");
+  if (bytes < ctx->W.total) return ctx->fail(DORY_ERR_INVALID_ARG, "workspace %zu < %zu bytes", bytes, ctx->W.total);
+  ctx->ws = (char*)ws;
+  ctx->ws_bytes = bytes;
+  return DORY_OK;
+}
+
+int dory_set_loops(dory_ctx* ctx, int k) {
+  if (!ctx) return DORY_ERR_INVALID_ARG;
+  if (k < 1 || k > ctx->cfg.max_loops) return ctx->fail(DORY_ERR_INVALID_ARG, "k=%d outside 1..%d", k, ctx->cfg.max_loops);
+  if (ctx->mode == DORY_KV_PER_LOOP)
+    for (auto& kv : ctx->seqs)
+      if (kv.second.k_built != k)
+        return ctx->fail(DORY_ERR_STATE, "per_loop sequence %d holds KV for k=%d", kv.first, kv.second.k_built);
+  ctx->k = k;
+  return DORY_OK;
+}
+
+int dory_get_loops(const dory_ctx* ctx, int* k) {
+  if (!ctx || !k) return DORY_ERR_INVALID_ARG;
+  *k = ctx->k;
+  return DORY_OK;
+}
+
+int dory_set_kv_mode(dory_ctx* ctx, int mode) {
+  if (!ctx) return DORY_ERR_INVALID_ARG;
+  if (mode != DORY_KV_PER_LOOP && mode != DORY_KV_LAST_LOOP) return ctx->fail(DORY_ERR_INVALID_ARG, "bad mode %d", mode);
+  if (!ctx->seqs.empty()) return ctx->fail(DORY_ERR_STATE, "sequences are live");
+  ctx->mode = mode;
+  return DORY_OK;
+}
+
+int dory_get_kv_mode(const dory_ctx* ctx, int* mode) {
+  if (!ctx || !mode) return DORY_ERR_INVALID_ARG;
+  *mode = ctx->mode;
+  return DORY_OK;
+}
+
+int dory_prefill(dory_ctx* ctx, void* stream, int n_seqs, const int32_t* seq_ids, const int32_t* n_new,
+                 const float* x_in, float* y_out) {
+  if (!ctx) return DORY_ERR_INVALID_ARG;
+  return step(ctx, (hipStream_t)stream, n_seqs, seq_ids, n_new, x_in, y_out, false);
+}
+
+int dory_decode_step(dory_ctx* ctx, void* stream, int n_seqs, const int32_t* seq_ids, const float* x_in,
+                     float* y_out) {
+  if (!ctx) return DORY_ERR_INVALID_ARG;
+  return step(ctx, (hipStream_t)stream, n_seqs, seq_ids, nullptr, x_in, y_out, true);
+}
+
+int dory_release_seq(dory_ctx* ctx, int32_t seq_id) {
+  if (!ctx) return DORY_ERR_INVALID_ARG;
+  auto it = ctx->seqs.find(seq_id);
+  if (it == ctx->seqs.end()) return ctx->fail(DORY_ERR_INVALID_ARG, "unknown sequence %d", seq_id);
+  release(ctx, it->second);
+  ctx->seqs.erase(it);
+  return DORY_OK;
+}
+
+int dory_seq_len(const dory_ctx* ctx, int32_t seq_id, int64_t* len) {
+  if (!ctx || !len) return DORY_ERR_INVALID_ARG;
+  auto it = ctx->seqs.find(seq_id);
+  if (it == ctx->seqs.end()) return DORY_ERR_INVALID_ARG;
+  *len = it->second.len;
+  return DORY_OK;
+}
+
+int dory_live_seqs(const dory_ctx* ctx, int32_t* n) {
+  if (!ctx || !n) return DORY_ERR_INVALID_ARG;
+  *n = (int32_t)ctx->seqs.size();
+  return DORY_OK;
+}
+
+int dory_kv_bytes_in_use(const dory_ctx* ctx, size_t* bytes) {
+  if (!ctx || !bytes) return DORY_ERR_INVALID_ARG;
+  *bytes = (size_t)(ctx->n_pages - (int64_t)ctx->free_pages.size()) * ctx->D.page_bytes;
+  return DORY_OK;
+}
+
+int dory_last_layer_calls(const dory_ctx* ctx, int64_t* n) {
+  if (!ctx || !n) return DORY_ERR_INVALID_ARG;
+  *n = ctx->last_calls;
+  return DORY_OK;
+}
+
+int dory_test_reserve(dory_ctx* ctx, int32_t seq_id, int32_t n_tokens) {
+  if (!ctx) return DORY_ERR_INVALID_ARG;
+  if (!ctx->pool || !ctx->ws) return ctx->fail(DORY_ERR_STATE, "KV pool and workspace must be bound");
+  if (n_tokens < 1) return ctx->fail(DORY_ERR_INVALID_ARG, "n_tokens < 1");
+  auto it = ctx->seqs.find(seq_id);
+  if (it == ctx->seqs.end() && (int)ctx->seqs.size() >= ctx->cfg.max_seqs)
+    return ctx->fail(DORY_ERR_INVALID_ARG, "more than max_seqs live sequences");
+  Seq probe;
+  if (it != ctx->seqs.end()) probe = it->second;
+  else probe.rec_slots = ctx->mode == DORY_KV_PER_LOOP ? ctx->k : 1;
+  if (it != ctx->seqs.end() && ctx->mode == DORY_KV_PER_LOOP && probe.k_built != ctx->k)
+    return ctx->fail(DORY_ERR_STATE, "sequence %d holds KV for k=%d", seq_id, probe.k_built);
+  if (probe.len + n_tokens > ctx->cfg.max_seq_len)
+    return ctx->fail(DORY_ERR_INVALID_ARG, "sequence would exceed max_seq_len");
+  const int64_t need = pages_to_grow(ctx, probe, probe.len + n_tokens);
+  if (need > (int64_t)ctx->free_pages.size())
+    return ctx->fail(DORY_ERR_OUT_OF_KV, "need %lld KV pages, %zu free", (long long)need, ctx->free_pages.size());
+  if (it == ctx->seqs.end()) {
+    Seq q;
+    q.id = seq_id;
+    q.slot = ctx->free_slots.back();
+    ctx->free_slots.pop_back();
+    q.k_built = ctx->k;
+    q.rec_slots = probe.rec_slots;
+    q.pages.assign(ctx->D.n_streams, {});
+    it = ctx->seqs.emplace(seq_id, std::move(q)).first;
+  }
+  grow(ctx, it->second, it->second.len + n_tokens);
+  return DORY_OK;
+}
+
+int dory_test_fill_kv(dory_ctx* ctx, void* stream, int32_t seq_id, int layer, int slot, int32_t pos0,
+                      int32_t n, const void* k, const void* v) {
+  if (!ctx) return DORY_ERR_INVALID_ARG;
+  auto it = ctx->seqs.find(seq_id);
+  if (it == ctx->seqs.end()) return ctx->fail(DORY_ERR_INVALID_ARG, "unknown sequence %d", seq_id);
+  const Seq& q = it->second;
+  if (layer < 0 || layer >= ctx->D.L) return ctx->fail(DORY_ERR_INVALID_ARG, "layer out of range");
+  const bool rec = layer >= ctx->cfg.n_in && layer < ctx->cfg.n_in + ctx->cfg.n_rec;
+  if (slot < 0 || slot >= (rec ? q.rec_slots : 1)) return ctx->fail(DORY_ERR_INVALID_ARG, "slot out of range");
+  if (!k || !v || n < 1 || pos0 < 0 || pos0 + (int64_t)n > q.len)
+    return ctx->fail(DORY_ERR_INVALID_ARG, "positions outside the sequence");
+  if (!ctx->is_full(layer)) {
+    const int64_t last_lp = (q.len - 1) / DORY_PAGE_TOKENS;
+    const int64_t first_ok = std::max<int64_t>(0, (last_lp - ctx->D.ring_swa + 1) * DORY_PAGE_TOKENS);
+    if (pos0 < first_ok) return ctx->fail(DORY_ERR_INVALID_ARG, "position %d left the sliding-window ring", pos0);
+  }
+  hipStream_t st = (hipStream_t)stream;
+  int r = dev_init(ctx);
+  if (r) return r;
+  if ((r = flush_deltas(ctx, st, 0))) return r;
+  HIPCHK(launch_fill_kv(kv_layout(ctx, layer), q.slot, ctx->stream_of(layer, slot), pos0, n, k, v, st),
+         "fill_kv");
+  return DORY_OK;
+}
+
+int dory_quantize_mxfp8(void* stream, const void* w, int w_dtype, int64_t rows, int64_t cols,
+                        uint8_t* codes, uint8_t* scales) {
+  if (!w || !codes || !scales || rows < 0 || cols < 0 || cols % 32 ||
+      (w_dtype != DORY_DTYPE_F32 && w_dtype != DORY_DTYPE_BF16)) {
+    g_create_err = "bad quantiser argument";
+    return DORY_ERR_INVALID_ARG;
+  }
+  if (rows * (cols / 32) > (int64_t)0x7fffffff * 8) {
+    g_create_err = "matrix too large";
+    return DORY_ERR_INVALID_ARG;
+  }
+  const hipError_t e = launch_quantize_mxfp8(w, w_dtype == DORY_DTYPE_BF16, rows, cols, codes, scales,
+                                             (hipStream_t)stream);
+  if (e != hipSuccess) {
+    g_create_err = hipGetErrorString(e);
+    return DORY_ERR_HIP;
+  }
+  return DORY_OK;
+}
+
+int dory_sync(dory_ctx* ctx, void* stream) {
+  const hipError_t e = hipStreamSynchronize((hipStream_t)stream);
+  if (e != hipSuccess) {
+    if (ctx) ctx->err = hipGetErrorString(e);
+    return DORY_ERR_HIP;
+  }
+  return DORY_OK;
+}
+
+}  // extern "C"

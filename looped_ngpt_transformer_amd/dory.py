@@ -1,0 +1,253 @@
+"""Thin ctypes binding of the C ABI in include/dory.h.
+
+Functions carry the C names and do argument marshalling only: torch tensors become
+device pointers, the current torch stream becomes the hipStream_t, python ints become
+host int32 arrays, and a non-zero status raises DoryError with the library's message.
+Every step of the forward pass runs in the HIP library; there is no other path, and
+loading fails loudly when the library has not been built.
+"""
+from __future__ import annotations
+
+import ctypes as C
+import os
+
+import numpy as np
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(HERE, "libdory.so")
+
+OK, ERR_INVALID_ARG, ERR_STATE, ERR_OUT_OF_KV, ERR_UNSUPPORTED, ERR_HIP = 0, -1, -2, -3, -4, -5
+DTYPE_F32, DTYPE_BF16 = 0, 1
+WFMT_F32, WFMT_BF16, WFMT_MXFP8 = 0, 1, 2
+KV_PER_LOOP, KV_LAST_LOOP = 0, 1
+GATE_NONE, GATE_ELEMENTWISE = 0, 1
+PAGE_TOKENS = 64
+MAX_POSITIONS = 262144
+MODES = {"per_loop": KV_PER_LOOP, "last_loop": KV_LAST_LOOP}
+
+
+class DoryError(RuntimeError):
+    def __init__(self, code: int, msg: str):
+        super().__init__(f"dory error {code}: {msg}")
+        self.code = code
+
+
+class dory_config(C.Structure):
+    _fields_ = [("hidden", C.c_int32), ("n_q_heads", C.c_int32), ("n_kv_heads", C.c_int32),
+                ("head_dim", C.c_int32), ("intermediate", C.c_int32), ("n_in", C.c_int32),
+                ("n_rec", C.c_int32), ("n_out", C.c_int32), ("window", C.c_int32),
+                ("full_period", C.c_int32), ("theta_swa", C.c_double),
+                ("theta_full", C.c_double), ("attn_scale", C.c_float), ("qk_norm", C.c_int32),
+                ("attn_gate", C.c_int32), ("act_dtype", C.c_int32), ("weight_format", C.c_int32),
+                ("max_loops", C.c_int32), ("max_seqs", C.c_int32), ("max_seq_len", C.c_int32),
+                ("max_rows", C.c_int32)]
+
+
+class dory_layer_weights(C.Structure):
+    _fields_ = [(n, C.c_void_p) for n in
+                ("w_qkvg", "w_o", "w_gu", "w_down", "s_qkvg", "s_o", "s_gu", "s_down",
+                 "alpha_attn", "alpha_mlp", "s_qk")]
+
+
+_P = C.c_void_p
+_I32P = C.POINTER(C.c_int32)
+_SIGS = {
+    "dory_create": (C.c_int, [C.POINTER(dory_config), C.POINTER(_P)]),
+    "dory_destroy": (C.c_int, [_P]),
+    "dory_last_error": (C.c_char_p, [_P]),
+    "dory_query_sizes": (C.c_int, [C.POINTER(dory_config), C.POINTER(C.c_size_t), C.POINTER(C.c_size_t)]),
+    "dory_kv_pages_needed": (C.c_int, [C.POINTER(dory_config), C.c_int, C.c_int, C.c_int64, C.c_int64,
+                                       C.POINTER(C.c_int64)]),
+    "dory_bind_weights": (C.c_int, [_P, C.c_int, C.POINTER(dory_layer_weights)]),
+    "dory_bind_kv_pool": (C.c_int, [_P, _P, C.c_size_t]),
+    "dory_bind_workspace": (C.c_int, [_P, _P, C.c_size_t]),
+    "dory_set_loops": (C.c_int, [_P, C.c_int]),
+    "dory_get_loops": (C.c_int, [_P, C.POINTER(C.c_int)]),
+    "dory_set_kv_mode": (C.c_int, [_P, C.c_int]),
+    "dory_get_kv_mode": (C.c_int, [_P, C.POINTER(C.c_int)]),
+    "dory_prefill": (C.c_int, [_P, _P, C.c_int, _I32P, _I32P, _P, _P]),
+    "dory_decode_step": (C.c_int, [_P, _P, C.c_int, _I32P, _P, _P]),
+    "dory_release_seq": (C.c_int, [_P, C.c_int32]),
+    "dory_seq_len": (C.c_int, [_P, C.c_int32, C.POINTER(C.c_int64)]),
+    "dory_live_seqs": (C.c_int, [_P, C.POINTER(C.c_int32)]),
+    "dory_kv_bytes_in_use": (C.c_int, [_P, C.POINTER(C.c_size_t)]),
+    "dory_last_layer_calls": (C.c_int, [_P, C.POINTER(C.c_int64)]),
+    "dory_test_reserve": (C.c_int, [_P, C.c_int32, C.c_int32]),
+    "dory_test_fill_kv": (C.c_int, [_P, _P, C.c_int32, C.c_int, C.c_int, C.c_int32, C.c_int32, _P, _P]),
+    "dory_quantize_mxfp8": (C.c_int, [_P, _P, C.c_int, C.c_int64, C.c_int64, _P, _P]),
+    "dory_sync": (C.c_int, [_P, _P]),
+}
+
+_lib = None
+
+
+def lib():
+    """The loaded libdory.so (raises if it has not been built)."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise ImportError(f"{LIB_PATH} is missing: run looped_ngpt_transformer_amd.build.build()")
+        L = C.CDLL(LIB_PATH)
+        for name, (res, args) in _SIGS.items():
+            f = getattr(L, name)
+            f.restype = res
+            f.argtypes = args
+        _lib = L
+    return _lib
+
+
+def _check(rc: int, ctx=None):
+    if rc != OK:
+        msg = lib().dory_last_error(ctx)
+        raise DoryError(rc, msg.decode() if msg else "")
+
+
+def _ptr(t):
+    return None if t is None else C.c_void_p(t.data_ptr())
+
+
+def _stream(stream):
+    if stream is not None:
+        return C.c_void_p(stream)
+    import torch
+    return C.c_void_p(torch.cuda.current_stream().cuda_stream)
+
+
+def _i32(values):
+    a = np.ascontiguousarray(np.asarray(values, dtype=np.int32))
+    return a, a.ctypes.data_as(_I32P)
+
+
+_ACT = {"f32": DTYPE_F32, "bf16": DTYPE_BF16}
+_WF = {"f32": WFMT_F32, "bf16": WFMT_BF16, "mxfp8": WFMT_MXFP8}
+
+
+def make_config(d: dict, max_loops=4, max_seqs=1, max_seq_len=4096, max_rows=4096) -> dory_config:
+    """dory_config from a shape dict (synth.CONFIGS entry) and runtime limits."""
+    return dory_config(
+        hidden=d["hidden"], n_q_heads=d["n_q_heads"], n_kv_heads=d["n_kv_heads"],
+        head_dim=d["head_dim"], intermediate=d["intermediate"], n_in=d["n_in"], n_rec=d["n_rec"],
+        n_out=d["n_out"], window=d["window"], full_period=d.get("full_period", 4),
+        theta_swa=d["theta_swa"], theta_full=d["theta_full"], attn_scale=d["attn_scale"],
+        qk_norm=d["qk_norm"], attn_gate=d["attn_gate"], act_dtype=_ACT[d["act_dtype"]],
+        weight_format=_WF[d["weight_format"]], max_loops=max_loops, max_seqs=max_seqs,
+        max_seq_len=max_seq_len, max_rows=max_rows)
+
+
+# ------------------------------------------------------------------ C-named wrappers
+def dory_create(cfg: dory_config):
+    h = C.c_void_p()
+    _check(lib().dory_create(C.byref(cfg), C.byref(h)))
+    return h
+
+
+def dory_destroy(ctx):
+    _check(lib().dory_destroy(ctx))
+
+
+def dory_last_error(ctx=None) -> str:
+    m = lib().dory_last_error(ctx)
+    return m.decode() if m else ""
+
+
+def dory_query_sizes(cfg: dory_config):
+    pb, wb = C.c_size_t(), C.c_size_t()
+    _check(lib().dory_query_sizes(C.byref(cfg), C.byref(pb), C.byref(wb)))
+    return pb.value, wb.value
+
+
+def dory_kv_pages_needed(cfg: dory_config, mode: int, k: int, seq_len: int, n_seqs: int) -> int:
+    p = C.c_int64()
+    _check(lib().dory_kv_pages_needed(C.byref(cfg), mode, k, seq_len, n_seqs, C.byref(p)))
+    return p.value
+
+
+def dory_bind_weights(ctx, layer: int, w: dory_layer_weights):
+    _check(lib().dory_bind_weights(ctx, layer, C.byref(w)), ctx)
+
+
+def dory_bind_kv_pool(ctx, pool_ptr: int, nbytes: int):
+    _check(lib().dory_bind_kv_pool(ctx, C.c_void_p(pool_ptr), nbytes), ctx)
+
+
+def dory_bind_workspace(ctx, ws_ptr: int, nbytes: int):
+    _check(lib().dory_bind_workspace(ctx, C.c_void_p(ws_ptr), nbytes), ctx)
+
+
+def dory_set_loops(ctx, k: int):
+    _check(lib().dory_set_loops(ctx, k), ctx)
+
+
+def dory_get_loops(ctx) -> int:
+    k = C.c_int()
+    _check(lib().dory_get_loops(ctx, C.byref(k)), ctx)
+    return k.value
+
+
+def dory_set_kv_mode(ctx, mode: int):
+    _check(lib().dory_set_kv_mode(ctx, mode), ctx)
+
+
+def dory_get_kv_mode(ctx) -> int:
+    m = C.c_int()
+    _check(lib().dory_get_kv_mode(ctx, C.byref(m)), ctx)
+    return m.value
+
+
+def dory_prefill(ctx, seq_ids, n_new, x_in, y_out, stream=None):
+    ids, idp = _i32(seq_ids)
+    nn, nnp = _i32(n_new)
+    _check(lib().dory_prefill(ctx, _stream(stream), len(ids), idp, nnp, _ptr(x_in), _ptr(y_out)), ctx)
+
+
+def dory_decode_step(ctx, seq_ids, x_in, y_out, stream=None):
+    ids, idp = _i32(seq_ids)
+    _check(lib().dory_decode_step(ctx, _stream(stream), len(ids), idp, _ptr(x_in), _ptr(y_out)), ctx)
+
+
+def dory_release_seq(ctx, seq_id: int):
+    _check(lib().dory_release_seq(ctx, seq_id), ctx)
+
+
+def dory_seq_len(ctx, seq_id: int) -> int:
+    n = C.c_int64()
+    _check(lib().dory_seq_len(ctx, seq_id, C.byref(n)), ctx)
+    return n.value
+
+
+def dory_live_seqs(ctx) -> int:
+    n = C.c_int32()
+    _check(lib().dory_live_seqs(ctx, C.byref(n)), ctx)
+    return n.value
+
+
+def dory_kv_bytes_in_use(ctx) -> int:
+    n = C.c_size_t()
+    _check(lib().dory_kv_bytes_in_use(ctx, C.byref(n)), ctx)
+    return n.value
+
+
+def dory_last_layer_calls(ctx) -> int:
+    n = C.c_int64()
+    _check(lib().dory_last_layer_calls(ctx, C.byref(n)), ctx)
+    return n.value
+
+
+def dory_test_reserve(ctx, seq_id: int, n_tokens: int):
+    _check(lib().dory_test_reserve(ctx, seq_id, n_tokens), ctx)
+
+
+def dory_test_fill_kv(ctx, seq_id, layer, slot, pos0, k, v, stream=None):
+    n = k.shape[0]
+    _check(lib().dory_test_fill_kv(ctx, _stream(stream), seq_id, layer, slot, pos0, n, _ptr(k), _ptr(v)), ctx)
+
+
+def dory_quantize_mxfp8(w, codes, scales, stream=None):
+    import torch
+    wd = DTYPE_BF16 if w.dtype == torch.bfloat16 else DTYPE_F32
+    rows, cols = w.shape
+    _check(lib().dory_quantize_mxfp8(_stream(stream), _ptr(w), wd, rows, cols, _ptr(codes), _ptr(scales)))
+
+
+def dory_sync(ctx=None, stream=None):
+    _check(lib().dory_sync(ctx, _stream(stream)), ctx)

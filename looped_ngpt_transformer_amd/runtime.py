@@ -1,0 +1,80 @@
+"""Device-memory plumbing around the C ABI: allocates the KV pool, workspace and MXFP8
+weight codes with torch, binds them to a context and keeps them alive. No arithmetic
+of the forward pass happens here (MXFP8 codes come from the library's quantiser)."""
+from __future__ import annotations
+
+import torch
+
+from . import dory as D
+
+
+class DoryRuntime:
+    def __init__(self, shape: dict, weights: list, *, max_loops=4, max_seqs=1,
+                 max_seq_len=4096, max_rows=4096, kv_pages: int | None = None,
+                 mode: str = "per_loop", loops: int = 2, device="cuda"):
+        self.shape = shape
+        self.device = torch.device(device)
+        self.cfg = D.make_config(shape, max_loops=max_loops, max_seqs=max_seqs,
+                                 max_seq_len=max_seq_len, max_rows=max_rows)
+        self.ctx = D.dory_create(self.cfg)
+        self.page_bytes, self.ws_bytes = D.dory_query_sizes(self.cfg)
+        if kv_pages is None:
+            kv_pages = D.dory_kv_pages_needed(self.cfg, D.KV_PER_LOOP, max_loops, max_seq_len, max_seqs)
+        self.kv_pages = kv_pages
+        self.ws = torch.empty(self.ws_bytes, dtype=torch.uint8, device=self.device)
+        self.pool = torch.empty(kv_pages * self.page_bytes, dtype=torch.uint8, device=self.device)
+        D.dory_bind_workspace(self.ctx, self.ws.data_ptr(), self.ws_bytes)
+        D.dory_bind_kv_pool(self.ctx, self.pool.data_ptr(), kv_pages * self.page_bytes)
+        self._keep = []
+        self.mx = {}  # (layer, matrix name) -> (E4M3 codes, E8M0 scales), MXFP8 only
+        self.bind_weights(weights)
+        D.dory_set_kv_mode(self.ctx, D.MODES[mode])
+        D.dory_set_loops(self.ctx, loops)
+
+    def bind_weights(self, weights: list):
+        mx = self.shape["weight_format"] == "mxfp8"
+        for l, w in enumerate(weights):
+            lw = D.dory_layer_weights()
+            for name in ("w_qkvg", "w_o", "w_gu", "w_down"):
+                t = w[name]
+                assert t.is_contiguous() and t.device.type == "cuda"
+                if mx:
+                    codes = torch.empty(t.shape, dtype=torch.uint8, device=t.device)
+                    scales = torch.empty((t.shape[0], t.shape[1] // 32), dtype=torch.uint8, device=t.device)
+                    D.dory_quantize_mxfp8(t, codes, scales)
+                    self.mx[(l, name)] = (codes, scales)
+                    setattr(lw, name, codes.data_ptr())
+                    setattr(lw, "s_" + name[2:], scales.data_ptr())
+                else:
+                    self._keep.append(t)
+                    setattr(lw, name, t.data_ptr())
+            for name in ("alpha_attn", "alpha_mlp", "s_qk"):
+                t = w[name].to(self.device, torch.float32).contiguous()
+                self._keep.append(t)
+                setattr(lw, name, t.data_ptr())
+            D.dory_bind_weights(self.ctx, l, lw)
+        torch.cuda.synchronize(self.device)
+
+    def prefill(self, seq_ids, n_new, x, y=None):
+        if y is None:
+            y = torch.empty((x.shape[0], self.shape["hidden"]), dtype=torch.float32, device=self.device)
+        D.dory_prefill(self.ctx, seq_ids, n_new, x, y)
+        return y
+
+    def decode(self, seq_ids, x, y=None):
+        if y is None:
+            y = torch.empty((x.shape[0], self.shape["hidden"]), dtype=torch.float32, device=self.device)
+        D.dory_decode_step(self.ctx, seq_ids, x, y)
+        return y
+
+    def close(self):
+        if self.ctx is not None:
+            torch.cuda.synchronize(self.device)
+            D.dory_destroy(self.ctx)
+            self.ctx = None
+
+    def __del__(self):
+        try:
+            self.close()
+        except Exception:
+            pass

@@ -16,8 +16,8 @@ Reading for the parts the pages leave open (OCP Microscaling formats v1.0):
   that rounds to zero encodes as 0x80).
 * groups run along the input (K) axis of each [N_out, K_in] matrix.
 
-The encoder below searches the table of all finite E4M3 values (brute force), which
-is slow and plainly correct.
+The encoder rounds by looking up the two neighbouring values in the table of all
+finite E4M3 values; the tests pin it against an exhaustive nearest-value search.
 """
 from __future__ import annotations
 
@@ -45,16 +45,21 @@ _POS_VALS = e4m3_decode(_POS_CODES)
 
 
 def e4m3_encode(x: np.ndarray) -> np.ndarray:
-    """Round to the nearest E4M3 value, ties to even code, saturate at 448."""
+    """Round to the nearest E4M3 value, ties to even code, saturate at 448.
+
+    The finite non-negative values increase strictly with the code, so the two
+    candidates for |x| are the table neighbours found by binary search.
+    """
     x = np.asarray(x, dtype=np.float64)
     a = np.minimum(np.abs(x), E4M3_MAX)
-    dist = np.abs(a[..., None] - _POS_VALS)                 # [..., 127]
-    best = dist.min(axis=-1, keepdims=True)
-    cand = dist == best
-    # among equidistant codes take the one with an even mantissa (code LSB 0)
-    even = cand & ((_POS_CODES & 1) == 0)
-    pick = np.where(even.any(axis=-1, keepdims=True), even, cand)
-    code = np.argmax(pick, axis=-1).astype(np.int64)
+    hi = np.clip(np.searchsorted(_POS_VALS, a, side="left"), 0, len(_POS_VALS) - 1)
+    lo = np.maximum(hi - 1, 0)
+    dlo = a - _POS_VALS[lo]
+    dhi = _POS_VALS[hi] - a
+    code = np.where(dhi < dlo, hi, lo)
+    tie = (dhi == dlo) & (hi != lo)
+    code = np.where(tie, np.where(hi % 2 == 0, hi, lo), code)   # ties: even mantissa
+    code = np.where(a == _POS_VALS[hi], hi, code)
     code = np.where(np.signbit(x), code | 0x80, code)
     return code.astype(np.uint8)
 

@@ -1,0 +1,76 @@
+"""Helpers for the GPU parity tests: run a schedule of prefill / decode calls through
+the C ABI and through the oracle on the same seeded inputs, and compare."""
+import math
+
+import numpy as np
+import torch
+
+import synth
+from oracle import dory_oracle as O
+from oracle import mxfp8 as MX
+from tests.helpers import oracle_weights, to_np
+
+BF16_COS = 0.9995
+BF16_MAXABS = 2e-2
+F32_MAXABS = 1e-4
+
+
+def gpu_weights(shape, seed, alpha="const"):
+    return synth.make_weights(shape, seed, "cuda", alpha=alpha)
+
+
+def oracle_model(shape, w_gpu, rt=None):
+    """Oracle weights: the same bf16/fp32 values, or dequantised MXFP8 codes produced by
+    the oracle's own quantiser from the same bf16 values."""
+    cfg = O.Config.from_dict(shape)
+    cpu = [{k: v.detach().cpu() for k, v in w.items()} for w in w_gpu]
+    if shape["weight_format"] == "mxfp8":
+        for w in cpu:
+            for name in ("w_qkvg", "w_o", "w_gu", "w_down"):
+                codes, scales = MX.quantize(to_np(w[name]))
+                w[name] = torch.from_numpy(MX.dequantize(codes, scales))
+    return cfg, oracle_weights(shape, cpu)
+
+
+def compare(y_gpu, y_ref, shape, what=""):
+    g = np.asarray(y_gpu, dtype=np.float64)
+    r = np.asarray(y_ref, dtype=np.float64)
+    assert g.shape == r.shape, (g.shape, r.shape)
+    assert np.all(np.isfinite(g)), f"{what}: non-finite GPU output"
+    maxabs = np.abs(g - r).max()
+    if shape["act_dtype"] == "f32":
+        assert maxabs <= F32_MAXABS, f"{what}: max|d| {maxabs:.3e} > {F32_MAXABS}"
+        return maxabs, 1.0
+    cos = np.sum(g * r, axis=1) / (np.linalg.norm(g, axis=1) * np.linalg.norm(r, axis=1))
+    assert cos.min() >= BF16_COS, f"{what}: min cosine {cos.min():.6f} < {BF16_COS}"
+    assert maxabs <= BF16_MAXABS, f"{what}: max|d| {maxabs:.3e} > {BF16_MAXABS}"
+    return maxabs, float(cos.min())
+
+
+def run_schedule(rt, schedule):
+    """schedule: list of (kind, [(seq_id, X float32 cuda [n, H])]). Returns the list of
+    outputs (numpy) per call."""
+    outs = []
+    for kind, items in schedule:
+        ids = [i for i, _ in items]
+        X = torch.cat([x for _, x in items]).contiguous()
+        if kind == "prefill":
+            y = rt.prefill(ids, [x.shape[0] for _, x in items], X)
+        else:
+            y = rt.decode(ids, X)
+        torch.cuda.synchronize()
+        outs.append(y.cpu().double().numpy())
+    return outs
+
+
+def oracle_schedule(cfg, W, schedule, k, mode, seqs=None):
+    seqs = {} if seqs is None else seqs
+    outs = []
+    for kind, items in schedule:
+        ys = []
+        for sid, x in items:
+            if sid not in seqs:
+                seqs[sid] = O.Sequence(cfg)
+            ys.append(O.prefill(cfg, W, seqs[sid], to_np(x), k, mode))
+        outs.append(np.concatenate(ys))
+    return outs

@@ -19,6 +19,29 @@ def test_decode_table_points():
     assert np.all(np.diff(vals) > 0)                  # codes 0..0x7E increase strictly
 
 
+def _encode_exhaustive(x):
+    """Nearest finite E4M3 value by exhaustive search, ties to the even code."""
+    vals = M.e4m3_decode(np.arange(0x7F))
+    out = []
+    for v in np.asarray(x, dtype=np.float64).ravel():
+        a = min(abs(v), 448.0)
+        dist = np.abs(vals - a)
+        cand = np.flatnonzero(dist == dist.min())
+        c = int(cand[0]) if len(cand) == 1 else int(cand[cand % 2 == 0][0])
+        out.append(c | (0x80 if np.signbit(v) else 0))
+    return np.array(out, dtype=np.uint8).reshape(np.shape(x))
+
+
+def test_encode_matches_exhaustive_search():
+    vals = M.e4m3_decode(np.arange(0x7F))
+    mids = (vals[1:] + vals[:-1]) / 2                 # every tie point
+    rng = np.random.default_rng(7)
+    x = np.concatenate([vals, mids, np.nextafter(mids, 0), np.nextafter(mids, 1e9),
+                        rng.uniform(0, 500, 2000), -rng.uniform(0, 500, 500),
+                        rng.uniform(0, 2 ** -6, 500), [0.0, -0.0, 448.0, 464.0, 1e30]])
+    np.testing.assert_array_equal(M.e4m3_encode(x), _encode_exhaustive(x))
+
+
 def test_encode_roundtrips_every_finite_code():
     codes = np.array([c for c in range(256) if (c & 0x7F) != 0x7F])
     np.testing.assert_array_equal(M.e4m3_encode(M.e4m3_decode(codes)), codes)
