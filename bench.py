@@ -1,0 +1,286 @@
+"""Throughput of the looped nGPT forward pass on one MI355X.
+
+Default workload (the one the metric is quoted on that fits one GPU): the Dory shape
+read as 8/20/8 blocks (36 layers, hidden 2560, 16/4 heads of 160, SwiGLU 4096, window
+1024, 3:1 sliding/full), bf16, batch 1, one 4096-token prefill at k = 2 (56 executed
+layers). One step = one whole prefill of a fresh sequence through the C ABI. Weights
+and inputs are seeded synthetic data resident in HBM before timing starts.
+
+Also: --workload D runs decode steps of the 72-layer shape (batch 32 over a seeded
+32768-token KV context) and --workload Q the MXFP8 decode (batch 128, 8192 context,
+k = 4, last_loop); --ks 1,2,4 measures several loop counts.
+
+Prints one JSON line. The roofline object covers the dominant kernel class (the
+projection GEMMs for prefill, attention for decode) from HIP events around each launch
+over the timed region; cpu_baseline times the float64 oracle on a bounded sample.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+PEAK_BF16_TFLOPS = 2500.0   # MI355X dense bf16 MFMA
+PEAK_HBM_GBS = 8000.0       # MI355X HBM3E
+
+WORKLOAD_TEXT = {
+    "P": "Dory-shape 8/20/8 (36 layers) bf16, batch 1, 4096-token prefill",
+    "D": "Full 16/40/16 (72 layers) bf16, decode batch 32 over a seeded 32768-token KV context",
+    "Q": "16/40/16 (72 layers) MXFP8 W8A16, decode batch 128 over a seeded 8192-token KV context",
+    "L": "16/40/16 (72 layers) bf16, batch 1, chunked prefill (chunks of 8192)",
+    "T": "tiny looped nGPT fp32, prefill 64",
+}
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=5)
+    ap.add_argument("--warmup", type=int, default=2)
+    ap.add_argument("--workload", default="P", choices=["P", "D", "Q", "L", "T"])
+    ap.add_argument("--k", type=int, default=None)
+    ap.add_argument("--ks", default=None, help="comma list of loop counts to measure too")
+    ap.add_argument("--mode", default=None, choices=["per_loop", "last_loop"])
+    ap.add_argument("--tokens", type=int, default=None, help="prefill length (P, L)")
+    ap.add_argument("--context", type=int, default=None, help="seeded KV context (D, Q)")
+    ap.add_argument("--batch", type=int, default=None, help="decode batch (D, Q)")
+    ap.add_argument("--cpu-rows", type=int, default=256)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    return ap.parse_args()
+
+
+def kernel_stats(rt, D):
+    return {D.KC_NAMES[k]: D.dory_profile_read(rt.ctx, k) for k in D.KC_NAMES}
+
+
+def roofline_of(stats, kind):
+    if kind == "mfma":
+        g = stats["gemm"]
+        ach = g["flops"] / (g["ms"] / 1e3) / 1e12
+        return {"bound": "mfma", "kernel": "gemm (bf16 MFMA projections)",
+                "achieved": round(ach, 1), "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
+                "frac": round(ach / PEAK_BF16_TFLOPS, 4), "traffic": None,
+                "launches": g["launches"], "avg_launch_us": round(1e3 * g["ms"] / g["launches"], 2)}
+    a = stats["attention"]
+    ach = a["bytes"] / (a["ms"] / 1e3) / 1e9
+    return {"bound": "hbm", "kernel": "attention (paged KV, split over keys)",
+            "achieved": round(ach, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
+            "frac": round(ach / PEAK_HBM_GBS, 4), "traffic": None,
+            "launches": a["launches"], "avg_launch_us": round(1e3 * a["ms"] / a["launches"], 2)}
+
+
+def time_prefill(rt, D, torch, X, tokens, steps, warmup, chunk=None):
+    """Each step: prefill a fresh sequence (in chunks if given), then release it."""
+    chunk = chunk or tokens
+    Y = torch.empty((chunk, X.shape[1]), dtype=torch.float32, device="cuda")
+
+    def one():
+        for c0 in range(0, tokens, chunk):
+            n = min(chunk, tokens - c0)
+            D.dory_prefill(rt.ctx, [0], [n], X[c0:c0 + n], Y[:n])
+        D.dory_release_seq(rt.ctx, 0)
+
+    for _ in range(warmup):
+        one()
+    torch.cuda.synchronize()
+    D.dory_profile_enable(rt.ctx, True)
+    t0 = time.perf_counter()
+    for _ in range(steps):
+        one()
+    torch.cuda.synchronize()
+    t1 = time.perf_counter()
+    D.dory_profile_enable(rt.ctx, False)
+    return (t1 - t0) / steps, kernel_stats(rt, D), Y
+
+
+def cpu_baseline_prefill(shape, weights, X, k, mode, rows, y_gpu):
+    """The float64 oracle on the first `rows` tokens of the prefill (a causal prefix,
+    so its outputs are exactly the first rows of the full prefill)."""
+    import numpy as np
+    from threadpoolctl import threadpool_info
+
+    from oracle import dory_oracle as O
+    cfg = O.Config.from_dict(shape)
+    W = [O.LayerWeights.from_packed(cfg, *(w[n].cpu().double().numpy() for n in
+                                          ("w_qkvg", "w_o", "w_gu", "w_down", "alpha_attn",
+                                           "alpha_mlp", "s_qk"))) for w in weights]
+    Xs = X[:rows].cpu().double().numpy()
+    t0 = time.perf_counter()
+    ref = O.prefill(cfg, W, O.Sequence(cfg), Xs, k, mode)
+    dt = time.perf_counter() - t0
+    g = y_gpu[:rows].cpu().double().numpy()
+    cos = np.sum(g * ref, 1) / (np.linalg.norm(g, axis=1) * np.linalg.norm(ref, axis=1))
+    threads = max([p.get("num_threads", 1) for p in threadpool_info()] + [1])
+    return ({"value": round(rows / dt, 3), "unit": "tokens/s", "cores": threads, "kind": "oracle",
+             "sample": f"first {rows} tokens of the prefill (causal prefix), all "
+                       f"{O.effective_depth(cfg, k)} layer calls, float64, {dt:.1f} s"},
+            {"rows": rows, "max_abs": float(np.abs(g - ref).max()), "min_cos": float(cos.min())})
+
+
+def bench_prefill(args, torch, synth, D, DoryRuntime):
+    wl = args.workload
+    shape = synth.config(wl)
+    k = args.k or 2
+    mode = args.mode or "per_loop"
+    tokens = args.tokens or (4096 if wl == "P" else 131072 if wl == "L" else 64)
+    chunk = 8192 if wl == "L" else None
+    ks = sorted({k} | ({int(x) for x in args.ks.split(",")} if args.ks else set()))
+    log(f"[bench] workload {wl}: generating weights")
+    weights = synth.make_weights(shape, 1234, "cuda")
+    max_rows = min(tokens, chunk or tokens)
+    rt = DoryRuntime(shape, weights, max_loops=max(ks + [2]), max_seqs=1, max_seq_len=tokens,
+                     max_rows=max_rows, mode=mode, loops=k)
+    X = synth.make_inputs(tokens, shape["hidden"], 99, device="cuda")
+    results = {}
+    for kk in ks:
+        D.dory_set_loops(rt.ctx, kk)
+        log(f"[bench] k={kk}: warmup {args.warmup}, steps {args.steps}")
+        dt, stats, Y = time_prefill(rt, D, torch, X, tokens, args.steps, args.warmup, chunk)
+        results[kk] = (dt, stats, Y)
+        log(f"[bench] k={kk}: {dt * 1e3:.2f} ms/step, {tokens / dt:.0f} tok/s, "
+            f"gemm {stats['gemm']['flops'] / stats['gemm']['ms'] / 1e9:.0f} TFLOP/s")
+    dt, stats, Y = results[k]
+    out = {
+        "metric": "prefill tokens/s (k=%d)" % k, "value": round(tokens / dt, 1),
+        "unit": "tokens/s", "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
+        "ms_per_step": round(dt * 1e3, 3), "higher_is_better": True, "scaling": "weak",
+        "vs_baseline": None, "dtype": "bf16" if shape["act_dtype"] == "bf16" else "f32",
+        "data": "synthetic (seeded random weights N(0,0.02) and unit-norm input states)",
+        "config": {"workload": WORKLOAD_TEXT[wl], "tokens": tokens, "loops": k, "kv_mode": mode,
+                   "executed_layers": shape["n_in"] + shape["n_out"] + k * shape["n_rec"],
+                   "chunk": chunk or tokens},
+        "roofline": roofline_of(stats, "mfma"),
+        "kernels": {n: {"launches": s["launches"], "ms_per_step": round(s["ms"] / args.steps, 3)}
+                    for n, s in stats.items()},
+    }
+    if len(ks) > 1:
+        out["by_loops"] = {str(kk): {"tokens_per_s": round(tokens / r[0], 1),
+                                     "ms_per_step": round(r[0] * 1e3, 3),
+                                     "gemm_tflops": round(r[1]["gemm"]["flops"] / r[1]["gemm"]["ms"] / 1e9, 1)}
+                           for kk, r in results.items()}
+    if not args.no_cpu_baseline and wl in ("P", "T"):
+        log(f"[bench] cpu baseline: oracle on the first {args.cpu_rows} tokens")
+        cb, par = cpu_baseline_prefill(shape, weights, X, k, mode, min(args.cpu_rows, tokens), Y)
+        out["cpu_baseline"] = cb
+        out["parity_prefix"] = par
+    rt.close()
+    return out
+
+
+def bench_decode(args, torch, synth, D, DoryRuntime):
+    wl = args.workload
+    shape = synth.config(wl)
+    batch = args.batch or (32 if wl == "D" else 128)
+    ctx_len = args.context or (32768 if wl == "D" else 8192)
+    k = args.k or (2 if wl == "D" else 4)
+    mode = args.mode or ("per_loop" if wl == "D" else "last_loop")
+    ks = sorted({k} | ({int(x) for x in args.ks.split(",")} if args.ks else set()))
+    log(f"[bench] workload {wl}: weights")
+    weights = synth.make_weights(shape, 1234, "cuda")
+    cfg_loops = max(ks)
+    steps = args.steps
+    results = {}
+    for kk in ks:
+        from looped_ngpt_transformer_amd import dory as DD
+        c = DD.make_config(shape, max_loops=cfg_loops, max_seqs=batch, max_seq_len=ctx_len + steps + args.warmup + 1,
+                           max_rows=batch)
+        pages = DD.dory_kv_pages_needed(c, DD.MODES[mode], kk, ctx_len + steps + args.warmup + 1, batch)
+        rt = DoryRuntime(shape, weights, max_loops=cfg_loops, max_seqs=batch,
+                         max_seq_len=ctx_len + steps + args.warmup + 1, max_rows=batch,
+                         kv_pages=pages, mode=mode, loops=kk)
+        log(f"[bench] k={kk} {mode}: KV pool {pages * rt.page_bytes / 1e9:.1f} GB; seeding {ctx_len} tokens x {batch}")
+        t0 = time.perf_counter()
+        seed_kv(rt, shape, synth, D, torch, batch, ctx_len, kk, mode)
+        torch.cuda.synchronize()
+        log(f"[bench] seeded in {time.perf_counter() - t0:.1f} s")
+        X = synth.make_inputs(batch * (steps + args.warmup), shape["hidden"], 77, device="cuda")
+        Y = torch.empty((batch, shape["hidden"]), dtype=torch.float32, device="cuda")
+        ids = list(range(batch))
+        for s in range(args.warmup):
+            D.dory_decode_step(rt.ctx, ids, X[s * batch:(s + 1) * batch], Y)
+        torch.cuda.synchronize()
+        D.dory_profile_enable(rt.ctx, True)
+        t0 = time.perf_counter()
+        for s in range(args.warmup, args.warmup + steps):
+            D.dory_decode_step(rt.ctx, ids, X[s * batch:(s + 1) * batch], Y)
+        torch.cuda.synchronize()
+        dt = (time.perf_counter() - t0) / steps
+        D.dory_profile_enable(rt.ctx, False)
+        stats = kernel_stats(rt, D)
+        kvb = D.dory_kv_bytes_in_use(rt.ctx)
+        results[kk] = (dt, stats, kvb)
+        log(f"[bench] k={kk}: {dt * 1e3:.2f} ms/step, {batch / dt:.1f} tok/s")
+        rt.close()
+        del rt
+        torch.cuda.empty_cache()
+    dt, stats, kvb = results[k]
+    tot_bytes = sum(s["bytes"] for s in stats.values()) / steps
+    out = {
+        "metric": "decode tokens/s (k=%d)" % k, "value": round(batch / dt, 2), "unit": "tokens/s",
+        "n_gpus": 1, "steps": steps, "warmup": args.warmup, "ms_per_step": round(dt * 1e3, 3),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "bf16",
+        "data": "synthetic (seeded random weights, seeded KV context, unit-norm inputs)",
+        "config": {"workload": WORKLOAD_TEXT[wl], "batch": batch, "context": ctx_len, "loops": k,
+                   "kv_mode": mode, "weights": shape["weight_format"],
+                   "executed_layers": shape["n_in"] + shape["n_out"] + k * shape["n_rec"]},
+        "roofline": roofline_of(stats, "hbm"),
+        "step_hbm_gbs": round(tot_bytes / dt / 1e9, 1),
+        "kv_bytes_in_use": kvb,
+        "kernels": {n: {"launches": s["launches"], "ms_per_step": round(s["ms"] / steps, 3),
+                        "gb_per_step": round(s["bytes"] / steps / 1e9, 3)} for n, s in stats.items()},
+    }
+    if len(ks) > 1:
+        out["by_loops"] = {str(kk): {"tokens_per_s": round(batch / r[0], 2), "ms_per_step": round(r[0] * 1e3, 3),
+                                     "kv_bytes_in_use": r[2]} for kk, r in results.items()}
+    return out
+
+
+def seed_kv(rt, shape, synth, D, torch, batch, ctx_len, k, mode):
+    """Reserve ctx_len positions per sequence and write seeded K/V into every cache slot
+    the sequence holds (sliding layers: the last window of positions)."""
+    L = shape["n_in"] + shape["n_rec"] + shape["n_out"]
+    W = shape["window"]
+    for b in range(batch):
+        D.dory_test_reserve(rt.ctx, b, ctx_len)
+        for l in range(L):
+            full = l % shape["full_period"] == shape["full_period"] - 1
+            rec = shape["n_in"] <= l < shape["n_in"] + shape["n_rec"]
+            slots = k if (rec and mode == "per_loop") else 1
+            p0 = 0 if full else max(0, ctx_len - W)
+            for s in range(slots):
+                kk, vv = synth.make_kv(shape, 555, b, l, s, p0, ctx_len - p0, device="cuda")
+                D.dory_test_fill_kv(rt.ctx, b, l, s, p0, kk, vv)
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(json.dumps({"error": "this build runs on one GPU; --gpus must be 1",
+                          "n_gpus": args.gpus}))
+        sys.exit(2)
+    import torch
+
+    import synth
+    from looped_ngpt_transformer_amd import dory as D
+    from looped_ngpt_transformer_amd.runtime import DoryRuntime
+    torch.cuda.set_device(0)
+    if args.workload in ("P", "L", "T"):
+        out = bench_prefill(args, torch, synth, D, DoryRuntime)
+    else:
+        out = bench_decode(args, torch, synth, D, DoryRuntime)
+    out["env"] = {"torch": torch.__version__, "hip": getattr(torch.version, "hip", None),
+                  "gpu": torch.cuda.get_device_name(0)}
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -202,6 +202,27 @@ int dory_test_fill_kv(dory_ctx* ctx, void* stream, int32_t seq_id, int layer, in
 int dory_quantize_mxfp8(void* stream, const void* w, int w_dtype, int64_t rows,
                         int64_t cols, uint8_t* codes, uint8_t* scales);
 
+/* ---- tracing: per-kernel-class launch timing with HIP events on the call's stream */
+#define DORY_KC_GEMM 0   /* projections: [q|k|v|gate], output, SwiGLU gate/up, down */
+#define DORY_KC_ATTN 1   /* attention over the KV cache (incl. split combine and gate) */
+#define DORY_KC_ROPE 2   /* RoPE + QK norm + KV-cache write */
+#define DORY_KC_UPDATE 3 /* nGPT update / loop boundary, input staging */
+#define DORY_KC_SWIGLU 4 /* SwiGLU from split-K partials */
+#define DORY_KC_COUNT 5
+typedef struct dory_kernel_stats {
+  int64_t launches; /* kernel launches recorded */
+  double ms;        /* summed event time of those launches */
+  double flops;     /* algorithmic FLOPs: GEMM 2*M*N*K; attention 4*Hq*d per visible
+                       (query, key) pair */
+  double bytes;     /* algorithmic HBM bytes: GEMM weights (+ scales) + activations in and
+                       out; attention K/V entries read (once per row) */
+} dory_kernel_stats;
+/* Start (on != 0: counters cleared) or stop recording. Recording brackets every launch
+ * with a pair of HIP events; it adds no device work beyond the event markers. */
+int dory_profile_enable(dory_ctx* ctx, int on);
+/* Totals for one class since enabling (waits for the recorded events). */
+int dory_profile_read(dory_ctx* ctx, int kclass, dory_kernel_stats* out);
+
 /* Synchronise `stream` and report any pending HIP error (HIP). */
 int dory_sync(dory_ctx* ctx, void* stream);
 

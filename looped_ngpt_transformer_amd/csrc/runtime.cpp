@@ -144,6 +144,12 @@ struct dory_ctx {
   hipEvent_t ev[NSTAGE] = {};
   int stage_i = 0;
   std::vector<int32_t> scratch;
+  // tracing
+  bool prof = false;
+  struct ProfRec { int kc; int ev; double flops, bytes; };
+  std::vector<hipEvent_t> pev;
+  int pev_used = 0;
+  std::vector<ProfRec> precs;
 
   int fail(int code, const char* fmt, ...) {
     char buf[512];
@@ -183,6 +189,32 @@ int hip_fail(dory_ctx* c, hipError_t e, const char* what) {
     hipError_t e_ = (expr);                     \
     if (e_ != hipSuccess) return hip_fail(ctx, e_, what); \
   } while (0)
+
+// Record a launch bracket: begin() before the launch, end() after it.
+int prof_event(dory_ctx* ctx, hipStream_t st) {
+  if (ctx->pev_used == (int)ctx->pev.size()) {
+    hipEvent_t e;
+    if (hipEventCreate(&e) != hipSuccess) return -1;
+    ctx->pev.push_back(e);
+  }
+  const int i = ctx->pev_used++;
+  if (hipEventRecord(ctx->pev[i], st) != hipSuccess) return -1;
+  return i;
+}
+
+struct Prof {
+  dory_ctx* ctx;
+  hipStream_t st;
+  int ev0 = -1;
+  Prof(dory_ctx* c, hipStream_t s) : ctx(c), st(s) {
+    if (ctx->prof) ev0 = prof_event(ctx, st);
+  }
+  void end(int kc, double flops, double bytes) {
+    if (!ctx->prof || ev0 < 0) return;
+    const int ev1 = prof_event(ctx, st);
+    if (ev1 == ev0 + 1) ctx->precs.push_back({kc, ev0, flops, bytes});
+  }
+};
 
 int check_config(const dory_config* c, std::string& msg) {
   auto bad = [&](const char* m) {
@@ -335,7 +367,25 @@ struct CallPlan {
   int max_pos = 0;
   int n_tiles = 0;
   int max_tile_rows = 0;
+  std::vector<std::pair<int64_t, int>> chunks;  // (first position, rows) per sequence
 };
+
+// Algorithmic attention work of one layer call: visible (query, key) pairs and the
+// distinct cached entries the call must read.
+void attn_work(const CallPlan& P, bool full, int W, double* pairs, double* keys) {
+  *pairs = 0;
+  *keys = 0;
+  for (auto& c : P.chunks) {
+    const int64_t p0 = c.first, n = c.second, p1 = p0 + n - 1;
+    if (full) {
+      *pairs += (double)n * (p0 + 1) + (double)n * (n - 1) / 2;
+      *keys += (double)(p1 + 1);
+    } else {
+      for (int64_t p = p0; p <= p1; ++p) *pairs += (double)std::min<int64_t>(p + 1, W);
+      *keys += (double)(p1 - std::max<int64_t>(0, p0 - W + 1) + 1);
+    }
+  }
+}
 
 KVLayout kv_layout(dory_ctx* ctx, int l) {
   KVLayout kv;
@@ -387,6 +437,16 @@ int run_layer(dory_ctx* ctx, hipStream_t st, const CallPlan& P, int l, int slot,
     g.ldc = ldc;
     return g;
   };
+  const double wbytes = wf == W_F32 ? 4.0 : (wf == W_BF16 ? 2.0 : 1.0 + 1.0 / 32);
+  auto run_gemm = [&](const GemmArgs& g) -> hipError_t {
+    Prof pr(ctx, st);
+    const hipError_t e = launch_gemm(g, st);
+    const double outb = g.epi == EPI_STORE_ACT || g.epi == EPI_SWIGLU ? 2.0 : 4.0 * g.splits;
+    const double ncols = g.epi == EPI_SWIGLU ? g.n_half : g.N;
+    pr.end(DORY_KC_GEMM, 2.0 * g.M * g.N * (double)g.K,
+           (double)g.N * g.K * wbytes + (double)g.M * g.K * D.esz + (double)g.M * ncols * outb);
+    return e;
+  };
   auto update = [&](int splits, const float* rs, int rs_n, const float* alpha, int b, float* sout) {
     UpdateArgs u;
     u.y = part;
@@ -402,23 +462,26 @@ int run_layer(dory_ctx* ctx, hipStream_t st, const CallPlan& P, int l, int slot,
     u.H = D.H;
     u.act = act;
     u.bnd = b;
-    return launch_update(u, st);
+    Prof pr(ctx, st);
+    const hipError_t e = launch_update(u, st);
+    pr.end(DORY_KC_UPDATE, 0, (double)M * D.H * (4.0 * splits + 4 + 4 + D.esz));
+    return e;
   };
 
   // ---- attention sublayer: [q|k|v|g] projection
   int S = 1;
   RopeArgs ra;
   if (f32) {
-    HIPCHK(launch_gemm(gemm(ws + W.sb, D.H, w.w_qkvg, nullptr, D.Nqkvg, EPI_F32, part, D.Nqkvg, 1), st), "gemm qkvg");
+    HIPCHK(run_gemm(gemm(ws + W.sb, D.H, w.w_qkvg, nullptr, D.Nqkvg, EPI_F32, part, D.Nqkvg, 1)), "gemm qkvg");
     ra.qkvg = part;
     ra.in_f32 = 1;
   } else if (skinny) {
     S = gemm_pick_splits(M, D.Nqkvg, D.H, wf);
-    HIPCHK(launch_gemm(gemm(ws + W.sb, D.H, w.w_qkvg, w.s_qkvg, D.Nqkvg, EPI_PARTIAL, part, D.Nqkvg, S), st), "gemm qkvg");
+    HIPCHK(run_gemm(gemm(ws + W.sb, D.H, w.w_qkvg, w.s_qkvg, D.Nqkvg, EPI_PARTIAL, part, D.Nqkvg, S)), "gemm qkvg");
     ra.qkvg = part;
     ra.in_f32 = 1;
   } else {
-    HIPCHK(launch_gemm(gemm(ws + W.sb, D.H, w.w_qkvg, w.s_qkvg, D.Nqkvg, EPI_STORE_ACT, ws + W.qkvg, D.Nqkvg, 1), st), "gemm qkvg");
+    HIPCHK(run_gemm(gemm(ws + W.sb, D.H, w.w_qkvg, w.s_qkvg, D.Nqkvg, EPI_STORE_ACT, ws + W.qkvg, D.Nqkvg, 1)), "gemm qkvg");
     ra.qkvg = ws + W.qkvg;
     ra.in_f32 = 0;
   }
@@ -440,7 +503,11 @@ int run_layer(dory_ctx* ctx, hipStream_t st, const CallPlan& P, int l, int slot,
   ra.g_out = ws + W.g;
   ra.kv = kv_layout(ctx, l);
   ra.stream_idx = sidx;
-  HIPCHK(launch_rope_kv(ra, st), "rope_kv");
+  {
+    Prof pr(ctx, st);
+    HIPCHK(launch_rope_kv(ra, st), "rope_kv");
+    pr.end(DORY_KC_ROPE, 0, (double)M * (D.Nqkvg * (ra.in_f32 ? 4.0 * S : D.esz) + (2 * D.Nq + 2 * D.Nkv) * D.esz));
+  }
 
   AttnArgs aa;
   aa.q = ws + W.q;
@@ -463,42 +530,53 @@ int run_layer(dory_ctx* ctx, hipStream_t st, const CallPlan& P, int l, int slot,
   aa.tiles = meta + 2 * c.max_rows;
   aa.n_tiles = P.n_tiles;
   aa.max_tile_rows = P.max_tile_rows;
-  HIPCHK(launch_attn_rows(aa, st), "attention");
+  {
+    double pairs, keys;
+    attn_work(P, full, c.window, &pairs, &keys);
+    Prof pr(ctx, st);
+    HIPCHK(launch_attn_rows(aa, st), "attention");
+    pr.end(DORY_KC_ATTN, 4.0 * D.Hq * D.d * pairs,
+           keys * 2.0 * D.Nkv * D.esz + (double)M * 3 * D.Nq * D.esz);
+  }
 
   // ---- output projection + nGPT update (pre-projection norm as a row scale)
   if (f32) {
-    HIPCHK(launch_gemm(gemm(ws + W.o, D.Nq, w.w_o, nullptr, D.H, EPI_F32, part, D.H, 1), st), "gemm o");
+    HIPCHK(run_gemm(gemm(ws + W.o, D.Nq, w.w_o, nullptr, D.H, EPI_F32, part, D.H, 1)), "gemm o");
     HIPCHK(update(1, ss_o, D.Hq, w.alpha_attn, BND_NONE, nullptr), "update attn");
   } else if (skinny) {
     S = gemm_pick_splits(M, D.H, D.Nq, wf);
-    HIPCHK(launch_gemm(gemm(ws + W.o, D.Nq, w.w_o, w.s_o, D.H, EPI_PARTIAL, part, D.H, S), st), "gemm o");
+    HIPCHK(run_gemm(gemm(ws + W.o, D.Nq, w.w_o, w.s_o, D.H, EPI_PARTIAL, part, D.H, S)), "gemm o");
     HIPCHK(update(S, ss_o, D.Hq, w.alpha_attn, BND_NONE, nullptr), "update attn");
   } else {
     GemmArgs g = gemm(ws + W.o, D.Nq, w.w_o, w.s_o, D.H, EPI_F32_ROWSCALE, part, D.H, 1);
     g.rs_ss = ss_o;
     g.rs_n = D.Hq;
-    HIPCHK(launch_gemm(g, st), "gemm o");
+    HIPCHK(run_gemm(g), "gemm o");
     HIPCHK(update(1, nullptr, 0, w.alpha_attn, BND_NONE, nullptr), "update attn");
   }
 
   // ---- MLP sublayer
   if (f32 || skinny) {
     S = f32 ? 1 : gemm_pick_splits(M, 2 * D.I, D.H, wf);
-    HIPCHK(launch_gemm(gemm(ws + W.sb, D.H, w.w_gu, w.s_gu, 2 * D.I, f32 ? EPI_F32 : EPI_PARTIAL, part, 2 * D.I, S), st), "gemm gu");
-    HIPCHK(launch_swiglu(part, S, M, D.I, ws + W.h, act, ss_h, D.ss_h_n, st), "swiglu");
+    HIPCHK(run_gemm(gemm(ws + W.sb, D.H, w.w_gu, w.s_gu, 2 * D.I, f32 ? EPI_F32 : EPI_PARTIAL, part, 2 * D.I, S)), "gemm gu");
+    {
+      Prof pr(ctx, st);
+      HIPCHK(launch_swiglu(part, S, M, D.I, ws + W.h, act, ss_h, D.ss_h_n, st), "swiglu");
+      pr.end(DORY_KC_SWIGLU, 0, (double)M * (2.0 * D.I * 4 * S + D.I * D.esz));
+    }
     S = f32 ? 1 : gemm_pick_splits(M, D.H, D.I, wf);
-    HIPCHK(launch_gemm(gemm(ws + W.h, D.I, w.w_down, w.s_down, D.H, f32 ? EPI_F32 : EPI_PARTIAL, part, D.H, S), st), "gemm down");
+    HIPCHK(run_gemm(gemm(ws + W.h, D.I, w.w_down, w.s_down, D.H, f32 ? EPI_F32 : EPI_PARTIAL, part, D.H, S)), "gemm down");
     HIPCHK(update(S, ss_h, D.ss_h_n, w.alpha_mlp, bnd, out), "update mlp");
   } else {
     GemmArgs g = gemm(ws + W.sb, D.H, w.w_gu, w.s_gu, 2 * D.I, EPI_SWIGLU, ws + W.h, D.I, 1);
     g.n_half = D.I;
     g.ss_out = ss_h;
     if (gemm_swiglu_ss_parts(g) != D.ss_h_n) return ctx->fail(DORY_ERR_UNSUPPORTED, "swiglu partials");
-    HIPCHK(launch_gemm(g, st), "gemm gu");
+    HIPCHK(run_gemm(g), "gemm gu");
     GemmArgs g2 = gemm(ws + W.h, D.I, w.w_down, w.s_down, D.H, EPI_F32_ROWSCALE, part, D.H, 1);
     g2.rs_ss = ss_h;
     g2.rs_n = D.ss_h_n;
-    HIPCHK(launch_gemm(g2, st), "gemm down");
+    HIPCHK(run_gemm(g2), "gemm down");
     HIPCHK(update(1, nullptr, 0, w.alpha_mlp, bnd, out), "update mlp");
   }
   return DORY_OK;
@@ -508,8 +586,12 @@ int run_forward(dory_ctx* ctx, hipStream_t st, const CallPlan& P, const float* x
   const dory_config& c = ctx->cfg;
   char* ws = ctx->ws;
   const int act = c.act_dtype == DORY_DTYPE_F32 ? ACT_F32 : ACT_BF16;
-  HIPCHK(launch_stage_input(x_in, (float*)(ws + ctx->W.s), ws + ctx->W.sb, P.M, ctx->D.H, act, st),
-         "stage_input");
+  {
+    Prof pr(ctx, st);
+    HIPCHK(launch_stage_input(x_in, (float*)(ws + ctx->W.s), ws + ctx->W.sb, P.M, ctx->D.H, act, st),
+           "stage_input");
+    pr.end(DORY_KC_UPDATE, 0, (double)P.M * ctx->D.H * (8.0 + ctx->D.esz));
+  }
   int64_t calls = 0;
   int r;
   for (int l = 0; l < c.n_in; ++l) {
@@ -618,6 +700,7 @@ int step(dory_ctx* ctx, hipStream_t st, int n, const int32_t* ids, const int32_t
       ++P.n_tiles;
     }
     P.max_tile_rows = std::min(64, std::max(P.max_tile_rows, nn));
+    P.chunks.emplace_back(p0, nn);
     P.max_pos = std::max<int>(P.max_pos, (int)(p0 + nn - 1));
     row += nn;
   }
@@ -667,6 +750,10 @@ int dory_create(const dory_config* cfg, dory_ctx** out) {
 
 int dory_destroy(dory_ctx* ctx) {
   if (!ctx) return DORY_ERR_INVALID_ARG;
+  for (auto e : ctx->pev) {
+    (void)hipEventSynchronize(e);
+    (void)hipEventDestroy(e);
+  }
   for (int i = 0; i < NSTAGE; ++i) {
     if (ctx->ev[i]) {
       (void)hipEventSynchronize(ctx->ev[i]);
@@ -912,6 +999,34 @@ int dory_quantize_mxfp8(void* stream, const void* w, int w_dtype, int64_t rows, 
     g_create_err = hipGetErrorString(e);
     return DORY_ERR_HIP;
   }
+  return DORY_OK;
+}
+
+int dory_profile_enable(dory_ctx* ctx, int on) {
+  if (!ctx) return DORY_ERR_INVALID_ARG;
+  if (on) {
+    for (int i = 0; i < ctx->pev_used; ++i) (void)hipEventSynchronize(ctx->pev[i]);
+    ctx->precs.clear();
+    ctx->pev_used = 0;
+  }
+  ctx->prof = on != 0;
+  return DORY_OK;
+}
+
+int dory_profile_read(dory_ctx* ctx, int kclass, dory_kernel_stats* out) {
+  if (!ctx || !out || kclass < 0 || kclass >= DORY_KC_COUNT) return DORY_ERR_INVALID_ARG;
+  dory_kernel_stats r{0, 0.0, 0.0, 0.0};
+  for (auto& p : ctx->precs) {
+    if (p.kc != kclass) continue;
+    float ms = 0.f;
+    HIPCHK(hipEventSynchronize(ctx->pev[p.ev + 1]), "hipEventSynchronize");
+    HIPCHK(hipEventElapsedTime(&ms, ctx->pev[p.ev], ctx->pev[p.ev + 1]), "hipEventElapsedTime");
+    r.launches += 1;
+    r.ms += ms;
+    r.flops += p.flops;
+    r.bytes += p.bytes;
+  }
+  *out = r;
   return DORY_OK;
 }
 

@@ -49,6 +49,15 @@ class dory_layer_weights(C.Structure):
                  "alpha_attn", "alpha_mlp", "s_qk")]
 
 
+class dory_kernel_stats(C.Structure):
+    _fields_ = [("launches", C.c_int64), ("ms", C.c_double), ("flops", C.c_double),
+                ("bytes", C.c_double)]
+
+
+KC_GEMM, KC_ATTN, KC_ROPE, KC_UPDATE, KC_SWIGLU = range(5)
+KC_NAMES = {KC_GEMM: "gemm", KC_ATTN: "attention", KC_ROPE: "rope_kv", KC_UPDATE: "update",
+            KC_SWIGLU: "swiglu"}
+
 _P = C.c_void_p
 _I32P = C.POINTER(C.c_int32)
 _SIGS = {
@@ -75,6 +84,8 @@ _SIGS = {
     "dory_test_reserve": (C.c_int, [_P, C.c_int32, C.c_int32]),
     "dory_test_fill_kv": (C.c_int, [_P, _P, C.c_int32, C.c_int, C.c_int, C.c_int32, C.c_int32, _P, _P]),
     "dory_quantize_mxfp8": (C.c_int, [_P, _P, C.c_int, C.c_int64, C.c_int64, _P, _P]),
+    "dory_profile_enable": (C.c_int, [_P, C.c_int]),
+    "dory_profile_read": (C.c_int, [_P, C.c_int, C.POINTER(dory_kernel_stats)]),
     "dory_sync": (C.c_int, [_P, _P]),
 }
 
@@ -251,3 +262,13 @@ def dory_quantize_mxfp8(w, codes, scales, stream=None):
 
 def dory_sync(ctx=None, stream=None):
     _check(lib().dory_sync(ctx, _stream(stream)), ctx)
+
+
+def dory_profile_enable(ctx, on: bool):
+    _check(lib().dory_profile_enable(ctx, 1 if on else 0), ctx)
+
+
+def dory_profile_read(ctx, kclass: int) -> dict:
+    r = dory_kernel_stats()
+    _check(lib().dory_profile_read(ctx, kclass, C.byref(r)), ctx)
+    return {"launches": r.launches, "ms": r.ms, "flops": r.flops, "bytes": r.bytes}
