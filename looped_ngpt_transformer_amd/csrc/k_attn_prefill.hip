@@ -1,0 +1,249 @@
+// Prefill attention on bf16 with MFMA (flash-style online softmax over KV pages).
+//
+// Same maths as the row kernel: GQA (4 query heads per KV head), causal, sliding
+// window W on sliding layers, softmax(scale * q.k) v, then the sigmoid output gate and
+// the per-head sum of squares for the pre-projection norm ("Dory1.0-4B": paper summary
+// "technical novelty"; arXiv §2; MXFP8 article "hybrid attention").
+//
+// Work-group = (tile of <= 64 consecutive query rows of one sequence, KV head): 8 waves,
+// wave = (query head g of the group, half of the tile's rows). Per KV page (64 keys):
+//   S^T = K Q^T   with v_mfma_f32_16x16x32_bf16 (A = K rows from LDS, B = Q in registers),
+//   online softmax per query in registers (lane's query is lane % 16),
+//   O^T += V^T P^T (A = V^T from LDS, B = P straight from the S^T accumulators: the lane
+//   already holds 2x4 keys of its query, which is a valid k-ordering of the MFMA when
+//   V^T is read with the same key permutation).
+// K is staged row-major (padded rows), V transposed into LDS (padded rows); the next
+// page is prefetched into registers while the current one is consumed. Entries of the
+// last page beyond the chunk's last position are zeroed, so unwritten cache memory can
+// never reach the sums.
+#include "common.h"
+#include "kernels.h"
+
+namespace dory {
+
+template <int D>
+__global__ __launch_bounds__(512) void k_attn_prefill(AttnArgs a) {
+  constexpr int G = 4;
+  constexpr int DC = D / 32;       // 32-wide chunks of the head dim (QK contraction)
+  constexpr int CB = D / 16;       // 16-channel blocks of the output
+  constexpr int KCH = D / 8 + 1;   // 16-byte chunks per padded K row
+  constexpr int VTR = 64 + 4;      // bf16 per padded V^T row
+  constexpr int NCH = 2 * 64 * D / 8;  // 16-byte chunks of K and V per page and head
+  constexpr int CPT = NCH / 512;       // chunks per thread
+  static_assert(D % 32 == 0 && NCH % 512 == 0, "head dim");
+
+  __shared__ uint4 Ks[64 * KCH];
+  __shared__ __align__(16) bf16_t Vt[D * VTR];
+
+  const int tile = a.n_tiles - 1 - blockIdx.x;  // longest (latest) tiles first
+  const int hk = blockIdx.y;
+  const int32_t* tl = a.tiles + 4 * tile;
+  const int row0 = tl[0], nrows = tl[1], pos0 = tl[2], seq = tl[3];
+  const int t = threadIdx.x, lane = t & 63, w = t >> 6;
+  const int g = w >> 1, qh = w & 1;
+  const int h = hk * G + g;
+  const int HqD = a.Hq * D;
+  const int lq = lane & 15, lk = lane >> 4;
+
+  const int kmax = pos0 + nrows - 1;
+  const bool full = a.window == 0;
+  const int klo = full ? 0 : max(0, pos0 - a.window + 1);
+  const int pg_lo = klo / PAGE, pg_hi = kmax / PAGE;
+  const int32_t* trow = a.kv.table + ((size_t)seq * a.kv.n_streams + a.stream_idx) * a.kv.tab_len;
+  const bf16_t* pool = (const bf16_t*)a.kv.pool;
+
+  // Q fragments (B operand): query 16 qb + lq of this wave's half, dims 32 c + 8 lk + e
+  bf16x8 qf[2][DC];
+#pragma unroll
+  for (int qb = 0; qb < 2; ++qb) {
+    const int i = 32 * qh + 16 * qb + lq;
+#pragma unroll
+    for (int c = 0; c < DC; ++c) {
+      uint4 v = make_uint4(0, 0, 0, 0);
+      if (i < nrows)
+        v = *(const uint4*)((const bf16_t*)a.q + (size_t)(row0 + i) * HqD + (size_t)h * D + 32 * c + 8 * lk);
+      qf[qb][c] = __builtin_bit_cast(bf16x8, v);
+    }
+  }
+
+  uint4 pre[CPT];
+  auto gload = [&](int pg) {
+    const int32_t page = trow[pg % a.kv.ring];
+    const bf16_t* kp = pool + (size_t)page * a.kv.page_elems + (size_t)hk * 64 * D;
+    const bf16_t* vp = kp + (size_t)a.kv.Hkv * 64 * D;
+#pragma unroll
+    for (int i = 0; i < CPT; ++i) {
+      const int s = t + 512 * i;
+      pre[i] = s < NCH / 2 ? ((const uint4*)kp)[s] : ((const uint4*)vp)[s - NCH / 2];
+    }
+  };
+  auto sstore = [&](int pg) {
+#pragma unroll
+    for (int i = 0; i < CPT; ++i) {
+      const int s = t + 512 * i;
+      const bool isv = s >= NCH / 2;
+      const int s2 = isv ? s - NCH / 2 : s;
+      const int j = s2 / (D / 8), ch = s2 % (D / 8);
+      const uint4 v = (pg * PAGE + j > kmax) ? make_uint4(0, 0, 0, 0) : pre[i];
+      if (!isv) {
+        Ks[j * KCH + ch] = v;
+      } else {
+        const uint32_t wv[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          Vt[(8 * ch + 2 * e) * VTR + j] = (bf16_t)(wv[e] & 0xFFFF);
+          Vt[(8 * ch + 2 * e + 1) * VTR + j] = (bf16_t)(wv[e] >> 16);
+        }
+      }
+    }
+  };
+
+  const float sl2 = a.scale * 1.4426950408889634f;  // logits in log2 units
+  float m_run[2] = {-INFINITY, -INFINITY}, l_run[2] = {0.f, 0.f};
+  f32x4 o[CB][2];
+#pragma unroll
+  for (int cb = 0; cb < CB; ++cb) o[cb][0] = o[cb][1] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+  gload(pg_lo);
+  for (int pg = pg_lo; pg <= pg_hi; ++pg) {
+    __syncthreads();
+    sstore(pg);
+    __syncthreads();
+    if (pg < pg_hi) gload(pg + 1);
+
+    // S^T[key 16 kb + 4 lk + r][query 16 qb + lq]
+    f32x4 st[4][2];
+#pragma unroll
+    for (int kb = 0; kb < 4; ++kb) {
+      st[kb][0] = st[kb][1] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int c = 0; c < DC; ++c) {
+        const bf16x8 kf = __builtin_bit_cast(bf16x8, Ks[(16 * kb + lq) * KCH + 4 * c + lk]);
+        st[kb][0] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kf, qf[0][c], st[kb][0], 0, 0, 0);
+        st[kb][1] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kf, qf[1][c], st[kb][1], 0, 0, 0);
+      }
+    }
+    // online softmax; probabilities packed as the PV B operand
+    bf16x8 pf[2][2];
+#pragma unroll
+    for (int qb = 0; qb < 2; ++qb) {
+      const int i = 32 * qh + 16 * qb + lq;
+      const int qpos = pos0 + i;
+      const bool qv = i < nrows;
+      float sv[4][4];
+      float mt = -INFINITY;
+#pragma unroll
+      for (int kb = 0; kb < 4; ++kb)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          const int kpos = pg * PAGE + 16 * kb + 4 * lk + r;
+          const bool vis = qv && kpos <= qpos && (full || qpos - kpos < a.window);
+          sv[kb][r] = vis ? st[kb][qb][r] * sl2 : -INFINITY;
+          mt = fmaxf(mt, sv[kb][r]);
+        }
+      mt = fmaxf(mt, __shfl_xor(mt, 16, 64));
+      mt = fmaxf(mt, __shfl_xor(mt, 32, 64));
+      const float m_new = fmaxf(m_run[qb], mt);
+      const float corr = m_run[qb] == -INFINITY ? 0.f : exp2f(m_run[qb] - m_new);
+      float ps = 0.f;
+      uint32_t pk[2][2];  // [kc][pair]: packed bf16 pairs
+      float pv[4][4];
+#pragma unroll
+      for (int kb = 0; kb < 4; ++kb)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          const float p = sv[kb][r] == -INFINITY ? 0.f : exp2f(sv[kb][r] - m_new);
+          pv[kb][r] = p;
+          ps += p;
+        }
+      ps += __shfl_xor(ps, 16, 64);
+      ps += __shfl_xor(ps, 32, 64);
+      l_run[qb] = l_run[qb] * corr + ps;
+      m_run[qb] = m_new;
+#pragma unroll
+      for (int cb = 0; cb < CB; ++cb) o[cb][qb] *= corr;
+#pragma unroll
+      for (int kc = 0; kc < 2; ++kc) {
+        uint32_t u[4];
+#pragma unroll
+        for (int e = 0; e < 4; e += 2) {
+          u[e / 2] = (uint32_t)f2bf(pv[2 * kc][e]) | ((uint32_t)f2bf(pv[2 * kc][e + 1]) << 16);
+          u[2 + e / 2] = (uint32_t)f2bf(pv[2 * kc + 1][e]) | ((uint32_t)f2bf(pv[2 * kc + 1][e + 1]) << 16);
+        }
+        pf[qb][kc] = __builtin_bit_cast(bf16x8, make_uint4(u[0], u[1], u[2], u[3]));
+      }
+    }
+    // O^T[channel 16 cb + 4 lk + r][query 16 qb + lq] += V^T P^T
+#pragma unroll
+    for (int cb = 0; cb < CB; ++cb) {
+#pragma unroll
+      for (int kc = 0; kc < 2; ++kc) {
+        const bf16_t* vr = Vt + (16 * cb + lq) * VTR + 32 * kc + 4 * lk;
+        const uint2 lo = *(const uint2*)vr;
+        const uint2 hi = *(const uint2*)(vr + 16);
+        const bf16x8 vf = __builtin_bit_cast(bf16x8, make_uint4(lo.x, lo.y, hi.x, hi.y));
+        o[cb][0] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vf, pf[0][kc], o[cb][0], 0, 0, 0);
+        o[cb][1] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vf, pf[1][kc], o[cb][1], 0, 0, 0);
+      }
+    }
+  }
+
+  // epilogue: normalise, gate, store, per-head sum of squares
+#pragma unroll
+  for (int qb = 0; qb < 2; ++qb) {
+    const int i = 32 * qh + 16 * qb + lq;
+    const bool qv = i < nrows;
+    const float invl = qv ? 1.f / l_run[qb] : 0.f;
+    const size_t base = (size_t)(row0 + (qv ? i : 0)) * HqD + (size_t)h * D;
+    float sq = 0.f;
+#pragma unroll
+    for (int cb = 0; cb < CB; ++cb) {
+      const int c = 16 * cb + 4 * lk;
+      float v[4];
+#pragma unroll
+      for (int r = 0; r < 4; ++r) v[r] = o[cb][qb][r] * invl;
+      if (qv) {
+        if (a.g) {
+          const uint2 gg = *(const uint2*)((const bf16_t*)a.g + base + c);
+          const uint32_t gw[2] = {gg.x, gg.y};
+#pragma unroll
+          for (int r = 0; r < 4; ++r) {
+            const float gv = bf2f((bf16_t)((gw[r / 2] >> (16 * (r & 1))) & 0xFFFF));
+            v[r] *= 1.f / (1.f + __expf(-gv));
+          }
+        }
+        uint2 ov;
+        ov.x = (uint32_t)f2bf(v[0]) | ((uint32_t)f2bf(v[1]) << 16);
+        ov.y = (uint32_t)f2bf(v[2]) | ((uint32_t)f2bf(v[3]) << 16);
+        *(uint2*)((bf16_t*)a.o + base + c) = ov;
+#pragma unroll
+        for (int r = 0; r < 4; ++r) sq += v[r] * v[r];
+      }
+    }
+    sq += __shfl_xor(sq, 16, 64);
+    sq += __shfl_xor(sq, 32, 64);
+    if (qv && lk == 0) a.ss[(size_t)(row0 + i) * a.Hq + h] = sq;
+  }
+}
+
+hipError_t launch_attn_prefill(const AttnArgs& a, hipStream_t st) {
+  if (a.n_tiles == 0) return hipSuccess;
+  if (a.kv.act != ACT_BF16 || a.Hq != 4 * a.Hkv) return hipErrorInvalidValue;
+  dim3 grid(a.n_tiles, a.Hkv);
+  switch (a.d) {
+    case 64:
+      hipLaunchKernelGGL(k_attn_prefill<64>, grid, dim3(512), 0, st, a);
+      break;
+    case 128:
+      hipLaunchKernelGGL(k_attn_prefill<128>, grid, dim3(512), 0, st, a);
+      break;
+    case 160:
+      hipLaunchKernelGGL(k_attn_prefill<160>, grid, dim3(512), 0, st, a);
+      break;
+    default:
+      return hipErrorInvalidValue;
+  }
+  return hipGetLastError();
+}
+
+}  // namespace dory

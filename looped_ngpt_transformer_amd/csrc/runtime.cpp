@@ -534,7 +534,12 @@ int run_layer(dory_ctx* ctx, hipStream_t st, const CallPlan& P, int l, int slot,
     double pairs, keys;
     attn_work(P, full, c.window, &pairs, &keys);
     Prof pr(ctx, st);
-    HIPCHK(launch_attn_rows(aa, st), "attention");
+    const bool mfma_attn = !f32 && P.max_tile_rows > 1 && D.Hq == 4 * D.Hkv &&
+                           (D.d == 64 || D.d == 128 || D.d == 160);
+    if (mfma_attn)
+      HIPCHK(launch_attn_prefill(aa, st), "attention (prefill)");
+    else
+      HIPCHK(launch_attn_rows(aa, st), "attention");
     pr.end(DORY_KC_ATTN, 4.0 * D.Hq * D.d * pairs,
            keys * 2.0 * D.Nkv * D.esz + (double)M * 3 * D.Nq * D.esz);
   }
