@@ -34,148 +34,13 @@ __device__ __forceinline__ void dq4(uint32_t word, float sc, uint32_t* out) {
   out[1] = (uint32_t)f2bf(hi.x * sc) | ((uint32_t)f2bf(hi.y * sc) << 16);
 }
 
-template <int BM, int BN, int WMW, int WNW, int EPI, int WF>
-__global__ __launch_bounds__(GT) void k_gemm_mfma(GemmArgs g) {
+// Epilogue: lane holds C[m = i*16 + 4*(lane>>4) + r][n = j*16 + (lane&15)] of its wave tile.
+template <int BM, int BN, int WMW, int WNW, int EPI>
+__device__ __forceinline__ void gemm_epilogue(const GemmArgs& g, f32x4 (&acc)[BM / WMW / 16][BN / WNW / 16],
+                                              int n_tile, int m0, int split, int wm, int wn, int lane,
+                                              const float* rowscale) {
   constexpr int TM = BM / WMW, TN = BN / WNW;
   constexpr int FM = TM / 16, FN = TN / 16;
-  constexpr int A_CH = BM * 8 / GT;                         // 16B chunks of A per thread
-  constexpr int B_CH = WF == W_MXFP8 ? BN * 4 / GT : BN * 8 / GT;  // MXFP8: 16 codes each
-  static_assert(A_CH >= 1 && B_CH >= 1, "tile too small");
-  static_assert(EPI != EPI_SWIGLU || FN % 2 == 0, "SwiGLU needs gate/up pairs per wave");
-
-  __shared__ __align__(16) uint4 As[BM * 8];
-  __shared__ __align__(16) uint4 Bs[BN * 8];
-  __shared__ float rowscale[EPI == EPI_F32_ROWSCALE ? BM : 1];
-
-  const int t = threadIdx.x, lane = t & 63, wave = t >> 6;
-  const int wm = wave / WNW, wn = wave % WNW;
-  const int n_tile = blockIdx.x, m0 = blockIdx.y * BM;
-  const int split = blockIdx.z;
-  const int Ks = g.K / g.splits;
-  const int kbeg = split * Ks, kend = kbeg + Ks;
-
-  const bf16_t* A = (const bf16_t*)g.A;
-  // B tile row r -> weight row
-  auto brow = [&](int r) -> int {
-    if (EPI == EPI_SWIGLU) {
-      const int c0 = n_tile * (BN / 2);
-      return r < BN / 2 ? c0 + r : g.n_half + c0 + (r - BN / 2);
-    }
-    return n_tile * BN + r;
-  };
-
-  uint4 ra[A_CH];
-  uint4 rb[B_CH];
-  uint32_t rsc[WF == W_MXFP8 ? B_CH : 1];
-
-  auto gload = [&](int k0) {
-#pragma unroll
-    for (int i = 0; i < A_CH; ++i) {
-      const int c = t & 7, r = (t >> 3) + i * (GT / 8);
-      const int m = m0 + r;
-      ra[i] = m < g.M ? *(const uint4*)(A + (size_t)m * g.lda + k0 + c * 8) : make_uint4(0, 0, 0, 0);
-    }
-    if (WF == W_MXFP8) {
-      const uint8_t* B8 = (const uint8_t*)g.B;
-#pragma unroll
-      for (int i = 0; i < B_CH; ++i) {
-        const int c = t & 3, r = (t >> 2) + i * (GT / 4);
-        const int n = brow(r);
-        rb[i] = *(const uint4*)(B8 + (size_t)n * g.K + k0 + c * 16);
-        rsc[i] = g.Bs[(size_t)n * (g.K / 32) + (k0 + c * 16) / 32];
-      }
-    } else {
-      const bf16_t* B = (const bf16_t*)g.B;
-#pragma unroll
-      for (int i = 0; i < B_CH; ++i) {
-        const int c = t & 7, r = (t >> 3) + i * (GT / 8);
-        rb[i] = *(const uint4*)(B + (size_t)brow(r) * g.K + k0 + c * 8);
-      }
-    }
-  };
-  auto sstore = [&]() {
-#pragma unroll
-    for (int i = 0; i < A_CH; ++i) {
-      const int c = t & 7, r = (t >> 3) + i * (GT / 8);
-      As[swz(r, c)] = ra[i];
-    }
-    if (WF == W_MXFP8) {
-#pragma unroll
-      for (int i = 0; i < B_CH; ++i) {
-        const int c = t & 3, r = (t >> 2) + i * (GT / 4);
-        const float sc = e8m0_to_f32(rsc[i]);
-        uint32_t v[8];
-        dq4(rb[i].x, sc, v);
-        dq4(rb[i].y, sc, v + 2);
-        dq4(rb[i].z, sc, v + 4);
-        dq4(rb[i].w, sc, v + 6);
-        Bs[swz(r, 2 * c)] = make_uint4(v[0], v[1], v[2], v[3]);
-        Bs[swz(r, 2 * c + 1)] = make_uint4(v[4], v[5], v[6], v[7]);
-      }
-    } else {
-#pragma unroll
-      for (int i = 0; i < B_CH; ++i) {
-        const int c = t & 7, r = (t >> 3) + i * (GT / 8);
-        Bs[swz(r, c)] = rb[i];
-      }
-    }
-  };
-
-  if (EPI == EPI_F32_ROWSCALE) {
-    for (int r = t; r < BM; r += GT) {
-      const int m = m0 + r;
-      float s = 0.f;
-      if (m < g.M)
-        for (int j = 0; j < g.rs_n; ++j) s += g.rs_ss[(size_t)m * g.rs_n + j];
-      rowscale[r] = inv_norm(s);
-    }
-  }
-
-  f32x4 acc[FM][FN];
-#pragma unroll
-  for (int i = 0; i < FM; ++i)
-#pragma unroll
-    for (int j = 0; j < FN; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
-
-  // wave's B-tile row for its j-th 16-column block
-  auto bblock = [&](int j) -> int {
-    if (EPI == EPI_SWIGLU) {
-      constexpr int TNh = TN / 2;
-      return j < FN / 2 ? wn * TNh + j * 16 : BN / 2 + wn * TNh + (j - FN / 2) * 16;
-    }
-    return wn * TN + j * 16;
-  };
-
-  gload(kbeg);
-  sstore();
-  __syncthreads();
-  for (int k0 = kbeg; k0 < kend; k0 += BK) {
-    const bool more = k0 + BK < kend;
-    if (more) gload(k0 + BK);
-#pragma unroll
-    for (int kk = 0; kk < 2; ++kk) {
-      const int ch = kk * 4 + (lane >> 4);
-      bf16x8 af[FM], bfr[FN];
-#pragma unroll
-      for (int i = 0; i < FM; ++i)
-        af[i] = __builtin_bit_cast(bf16x8, As[swz(wm * TM + i * 16 + (lane & 15), ch)]);
-#pragma unroll
-      for (int j = 0; j < FN; ++j)
-        bfr[j] = __builtin_bit_cast(bf16x8, Bs[swz(bblock(j) + (lane & 15), ch)]);
-#pragma unroll
-      for (int i = 0; i < FM; ++i)
-#pragma unroll
-        for (int j = 0; j < FN; ++j)
-          acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(af[i], bfr[j], acc[i][j], 0, 0, 0);
-    }
-    __syncthreads();
-    if (more) {
-      sstore();
-      __syncthreads();
-    }
-  }
-
-  // ---- epilogue: lane holds C[m = i*16 + 4*(lane>>4) + r][n = j*16 + (lane&15)]
   const int mrow0 = m0 + wm * TM + 4 * (lane >> 4);
   if (EPI == EPI_SWIGLU) {
     constexpr int TNh = TN / 2;
@@ -223,6 +88,312 @@ __global__ __launch_bounds__(GT) void k_gemm_mfma(GemmArgs g) {
       }
     }
   }
+}
+
+// XCD-aware tile order. Work-groups are dispatched round-robin over the 8 XCDs (each
+// with its own L2); give each XCD a contiguous share of the tiles, ordered in groups of
+// GM m-tiles (m fastest) so the tiles resident on one XCD share A rows and B columns.
+template <int GM>
+__device__ __forceinline__ void tile_coords(int* n_tile, int* m_tile) {
+  const int nx = gridDim.x, ny = gridDim.y, total = nx * ny;
+  const int bid = blockIdx.x + blockIdx.y * nx;
+  const int L = (total % 8 == 0) ? (bid % 8) * (total / 8) + bid / 8 : bid;
+  const int per_group = GM * nx;
+  const int first_m = (L / per_group) * GM;
+  const int gm = min(ny - first_m, GM);
+  const int r = L % per_group;
+  *m_tile = first_m + r % gm;
+  *n_tile = r / gm;
+}
+
+template <int BM, int BN, int WMW, int WNW, int EPI, int WF>
+__global__ __launch_bounds__(GT) void k_gemm_mfma(GemmArgs g) {
+  constexpr int TM = BM / WMW, TN = BN / WNW;
+  constexpr int FM = TM / 16, FN = TN / 16;
+  constexpr int A_CH = BM * 8 / GT;                         // 16B chunks of A per thread
+  constexpr int B_CH = WF == W_MXFP8 ? BN * 4 / GT : BN * 8 / GT;  // MXFP8: 16 codes each
+  static_assert(A_CH >= 1 && B_CH >= 1, "tile too small");
+  static_assert(EPI != EPI_SWIGLU || FN % 2 == 0, "SwiGLU needs gate/up pairs per wave");
+
+  __shared__ __align__(16) uint4 As[2][BM * 8];  // double-buffered K-tiles
+  __shared__ __align__(16) uint4 Bs[2][BN * 8];
+  __shared__ float rowscale[EPI == EPI_F32_ROWSCALE ? BM : 1];
+
+  const int t = threadIdx.x, lane = t & 63, wave = t >> 6;
+  const int wm = wave / WNW, wn = wave % WNW;
+  int n_tile, m_tile;
+  tile_coords<8>(&n_tile, &m_tile);
+  const int m0 = m_tile * BM;
+  const int split = blockIdx.z;
+  const int Ks = g.K / g.splits;
+  const int kbeg = split * Ks, kend = kbeg + Ks;
+
+  const bf16_t* A = (const bf16_t*)g.A;
+  // B tile row r -> weight row
+  auto brow = [&](int r) -> int {
+    if (EPI == EPI_SWIGLU) {
+      const int c0 = n_tile * (BN / 2);
+      return r < BN / 2 ? c0 + r : g.n_half + c0 + (r - BN / 2);
+    }
+    return n_tile * BN + r;
+  };
+
+  uint4 ra[A_CH];
+  uint4 rb[B_CH];
+  uint32_t rsc[WF == W_MXFP8 ? B_CH : 1];
+
+  auto gload = [&](int k0) {
+#pragma unroll
+    for (int i = 0; i < A_CH; ++i) {
+      const int c = t & 7, r = (t >> 3) + i * (GT / 8);
+      const int m = m0 + r;
+      ra[i] = m < g.M ? *(const uint4*)(A + (size_t)m * g.lda + k0 + c * 8) : make_uint4(0, 0, 0, 0);
+    }
+    if (WF == W_MXFP8) {
+      const uint8_t* B8 = (const uint8_t*)g.B;
+#pragma unroll
+      for (int i = 0; i < B_CH; ++i) {
+        const int c = t & 3, r = (t >> 2) + i * (GT / 4);
+        const int n = brow(r);
+        rb[i] = *(const uint4*)(B8 + (size_t)n * g.K + k0 + c * 16);
+        rsc[i] = g.Bs[(size_t)n * (g.K / 32) + (k0 + c * 16) / 32];
+      }
+    } else {
+      const bf16_t* B = (const bf16_t*)g.B;
+#pragma unroll
+      for (int i = 0; i < B_CH; ++i) {
+        const int c = t & 7, r = (t >> 3) + i * (GT / 8);
+        rb[i] = *(const uint4*)(B + (size_t)brow(r) * g.K + k0 + c * 8);
+      }
+    }
+  };
+  auto sstore = [&](int buf) {
+#pragma unroll
+    for (int i = 0; i < A_CH; ++i) {
+      const int c = t & 7, r = (t >> 3) + i * (GT / 8);
+      As[buf][swz(r, c)] = ra[i];
+    }
+    if (WF == W_MXFP8) {
+#pragma unroll
+      for (int i = 0; i < B_CH; ++i) {
+        const int c = t & 3, r = (t >> 2) + i * (GT / 4);
+        const float sc = e8m0_to_f32(rsc[i]);
+        uint32_t v[8];
+        dq4(rb[i].x, sc, v);
+        dq4(rb[i].y, sc, v + 2);
+        dq4(rb[i].z, sc, v + 4);
+        dq4(rb[i].w, sc, v + 6);
+        Bs[buf][swz(r, 2 * c)] = make_uint4(v[0], v[1], v[2], v[3]);
+        Bs[buf][swz(r, 2 * c + 1)] = make_uint4(v[4], v[5], v[6], v[7]);
+      }
+    } else {
+#pragma unroll
+      for (int i = 0; i < B_CH; ++i) {
+        const int c = t & 7, r = (t >> 3) + i * (GT / 8);
+        Bs[buf][swz(r, c)] = rb[i];
+      }
+    }
+  };
+
+  if (EPI == EPI_F32_ROWSCALE) {
+    for (int r = t; r < BM; r += GT) {
+      const int m = m0 + r;
+      float s = 0.f;
+      if (m < g.M)
+        for (int j = 0; j < g.rs_n; ++j) s += g.rs_ss[(size_t)m * g.rs_n + j];
+      rowscale[r] = inv_norm(s);
+    }
+  }
+
+  f32x4 acc[FM][FN];
+#pragma unroll
+  for (int i = 0; i < FM; ++i)
+#pragma unroll
+    for (int j = 0; j < FN; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+  // wave's B-tile row for its j-th 16-column block
+  auto bblock = [&](int j) -> int {
+    if (EPI == EPI_SWIGLU) {
+      constexpr int TNh = TN / 2;
+      return j < FN / 2 ? wn * TNh + j * 16 : BN / 2 + wn * TNh + (j - FN / 2) * 16;
+    }
+    return wn * TN + j * 16;
+  };
+
+  // one barrier per K-tile: tile i+1 is loaded into registers during tile i's MFMAs
+  // and stored to the other LDS buffer, whose readers all passed the previous barrier
+  gload(kbeg);
+  sstore(0);
+  __syncthreads();
+  const int nk = (kend - kbeg) / BK;
+  for (int it = 0; it < nk; ++it) {
+    const int cur = it & 1;
+    const bool more = it + 1 < nk;
+    if (more) gload(kbeg + (it + 1) * BK);
+#pragma unroll
+    for (int kk = 0; kk < 2; ++kk) {
+      const int ch = kk * 4 + (lane >> 4);
+      bf16x8 af[FM], bfr[FN];
+#pragma unroll
+      for (int i = 0; i < FM; ++i)
+        af[i] = __builtin_bit_cast(bf16x8, As[cur][swz(wm * TM + i * 16 + (lane & 15), ch)]);
+#pragma unroll
+      for (int j = 0; j < FN; ++j)
+        bfr[j] = __builtin_bit_cast(bf16x8, Bs[cur][swz(bblock(j) + (lane & 15), ch)]);
+#pragma unroll
+      for (int i = 0; i < FM; ++i)
+#pragma unroll
+        for (int j = 0; j < FN; ++j)
+          acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(af[i], bfr[j], acc[i][j], 0, 0, 0);
+    }
+    if (more) sstore(cur ^ 1);
+    __syncthreads();
+  }
+
+  gemm_epilogue<BM, BN, WMW, WNW, EPI>(g, acc, n_tile, m0, split, wm, wn, lane, rowscale);
+}
+
+// ------------------------------------------------------- bf16 GEMM, direct-to-LDS pipeline
+// The same product for bf16 weights with a deeper pipeline: K-tiles of 32 staged in a
+// ring of STAGES LDS buffers by global_load_lds_dwordx4 (each lane's 16 bytes land at
+// the wave's LDS base + 16 * lane, so the XOR swizzle is applied on the source side).
+// Loads for tile i + STAGES - 1 are issued while tile i is multiplied; one barrier per
+// tile. Rows of A beyond M are loaded from row M - 1 (valid memory) and never stored.
+typedef __attribute__((address_space(3))) void* lds_void_t;
+typedef __attribute__((address_space(1))) void* gbl_void_t;
+
+// LDS position of 16-byte chunk `chunk` of tile row `row` (CPR chunks per row): XOR
+// swizzle so the 16 rows an MFMA fragment read touches fall in distinct banks.
+template <int CPR>
+__device__ __forceinline__ int swzc(int row, int chunk) {
+  return row * CPR + (chunk ^ (CPR == 8 ? (row & 7) : ((row >> 1) & 3)));
+}
+
+// s_waitcnt vmcnt(n) for a run-time n <= 31 (other counters untouched)
+__device__ __forceinline__ void wait_vmcnt(int n) {
+  switch (n) {
+#define DORY_WVM(N) case N: asm volatile("s_waitcnt vmcnt(" #N ")" ::: "memory"); break;
+    DORY_WVM(0) DORY_WVM(1) DORY_WVM(2) DORY_WVM(3) DORY_WVM(4) DORY_WVM(5) DORY_WVM(6)
+    DORY_WVM(7) DORY_WVM(8) DORY_WVM(9) DORY_WVM(10) DORY_WVM(11) DORY_WVM(12) DORY_WVM(13)
+    DORY_WVM(14) DORY_WVM(15) DORY_WVM(16) DORY_WVM(17) DORY_WVM(18) DORY_WVM(19) DORY_WVM(20)
+    DORY_WVM(21) DORY_WVM(22) DORY_WVM(23) DORY_WVM(24) DORY_WVM(25) DORY_WVM(26) DORY_WVM(27)
+    DORY_WVM(28) DORY_WVM(29) DORY_WVM(30) DORY_WVM(31)
+#undef DORY_WVM
+    default: asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); break;
+  }
+}
+
+template <int BM, int BN, int WMW, int WNW, int EPI, int STAGES, int PBK = 32>
+__global__ __launch_bounds__(GT) void k_gemm_pipe(GemmArgs g) {
+  constexpr int TM = BM / WMW, TN = BN / WNW;
+  constexpr int FM = TM / 16, FN = TN / 16;
+  constexpr int CPR = PBK / 8;                     // 16-byte chunks per tile row
+  constexpr int ACH = BM * CPR, BCH = BN * CPR;    // chunks per K-tile
+  constexpr int NINST = (ACH + BCH) / 64;         // wave load instructions per K-tile
+  constexpr int MAXI = (NINST + 3) / 4;
+  static_assert(ACH % 64 == 0 && BCH % 64 == 0, "tile rows must be multiples of 16");
+  static_assert(EPI != EPI_SWIGLU || FN % 2 == 0, "SwiGLU needs gate/up pairs per wave");
+  static_assert((STAGES - 2) * MAXI <= 31, "vmcnt range");
+  static_assert(PBK == 32 || PBK == 64, "K-tile of 32 or 64");
+  static_assert(STAGES >= 2, "at least double buffering");
+
+  __shared__ __align__(16) uint4 sm[STAGES][ACH + BCH];
+  __shared__ float rowscale[EPI == EPI_F32_ROWSCALE ? BM : 1];
+
+  const int t = threadIdx.x, lane = t & 63, wave = t >> 6;
+  const int wm = wave / WNW, wn = wave % WNW;
+  int n_tile, m_tile;
+  tile_coords<8>(&n_tile, &m_tile);
+  const int m0 = m_tile * BM;
+  const int split = blockIdx.z;
+  const int Ks = g.K / g.splits;
+  const int kbeg = split * Ks;
+  const int nk = Ks / PBK;
+  const bf16_t* A = (const bf16_t*)g.A;
+  const bf16_t* B = (const bf16_t*)g.B;
+  const int my_inst = (NINST - wave + 3) / 4;  // instructions this wave issues per K-tile
+
+  auto brow = [&](int r) -> int {
+    if (EPI == EPI_SWIGLU) {
+      const int c0 = n_tile * (BN / 2);
+      return r < BN / 2 ? c0 + r : g.n_half + c0 + (r - BN / 2);
+    }
+    return n_tile * BN + r;
+  };
+  auto issue = [&](int slot, int k0) {
+#pragma unroll
+    for (int q = 0; q < MAXI; ++q) {
+      const int inst = wave + 4 * q;
+      if (inst < NINST) {
+        const int sidx = inst * 64 + lane;
+        const bf16_t* src;
+        if (sidx < ACH) {
+          const int r = sidx / CPR, c = swzc<CPR>(r, sidx % CPR) - r * CPR;
+          const int m = min(m0 + r, g.M - 1);
+          src = A + (size_t)m * g.lda + k0 + 8 * c;
+        } else {
+          const int s2 = sidx - ACH;
+          const int r = s2 / CPR, c = swzc<CPR>(r, s2 % CPR) - r * CPR;
+          src = B + (size_t)brow(r) * g.K + k0 + 8 * c;
+        }
+        __builtin_amdgcn_global_load_lds((gbl_void_t)src, (lds_void_t)(&sm[slot][inst * 64]), 16, 0, 0);
+      }
+    }
+  };
+
+  if (EPI == EPI_F32_ROWSCALE) {
+    for (int r = t; r < BM; r += GT) {
+      const int m = m0 + r;
+      float sacc = 0.f;
+      if (m < g.M)
+        for (int j = 0; j < g.rs_n; ++j) sacc += g.rs_ss[(size_t)m * g.rs_n + j];
+      rowscale[r] = inv_norm(sacc);
+    }
+  }
+
+  f32x4 acc[FM][FN];
+#pragma unroll
+  for (int i = 0; i < FM; ++i)
+#pragma unroll
+    for (int j = 0; j < FN; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+  auto bblock = [&](int j) -> int {
+    if (EPI == EPI_SWIGLU) {
+      constexpr int TNh = TN / 2;
+      return j < FN / 2 ? wn * TNh + j * 16 : BN / 2 + wn * TNh + (j - FN / 2) * 16;
+    }
+    return wn * TN + j * 16;
+  };
+
+#pragma unroll
+  for (int st = 0; st < STAGES - 1; ++st)
+    if (st < nk) issue(st, kbeg + PBK * st);
+
+  for (int it = 0; it < nk; ++it) {
+    const int ahead = min(STAGES - 2, nk - 1 - it);  // later tiles already in flight
+    wait_vmcnt(ahead * my_inst);
+    __syncthreads();
+    if (it + STAGES - 1 < nk) issue((it + STAGES - 1) % STAGES, kbeg + PBK * (it + STAGES - 1));
+    const uint4* As = sm[it % STAGES];
+    const uint4* Bs = As + ACH;
+#pragma unroll
+    for (int kk = 0; kk < PBK / 32; ++kk) {
+      const int ch = kk * 4 + (lane >> 4);
+      bf16x8 af[FM], bfr[FN];
+#pragma unroll
+      for (int i = 0; i < FM; ++i)
+        af[i] = __builtin_bit_cast(bf16x8, As[swzc<CPR>(wm * TM + i * 16 + (lane & 15), ch)]);
+#pragma unroll
+      for (int j = 0; j < FN; ++j)
+        bfr[j] = __builtin_bit_cast(bf16x8, Bs[swzc<CPR>(bblock(j) + (lane & 15), ch)]);
+#pragma unroll
+      for (int i = 0; i < FM; ++i)
+#pragma unroll
+        for (int j = 0; j < FN; ++j)
+          acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(af[i], bfr[j], acc[i][j], 0, 0, 0);
+    }
+  }
+  gemm_epilogue<BM, BN, WMW, WNW, EPI>(g, acc, n_tile, m0, split, wm, wn, lane, rowscale);
 }
 
 // ------------------------------------------------------------------ fp32 GEMM (T)
@@ -276,9 +447,21 @@ int gemm_pick_splits(int M, int N, int K, int wfmt) {
   return s;
 }
 
-int gemm_swiglu_ss_parts(const GemmArgs& g) {
-  // prefill SwiGLU tile: BN = 128 (64 gate + 64 up columns), 2 waves along N
-  return (g.n_half / 64) * 2;
+// SwiGLU epilogue tiles: bf16 weights use 256x256 tiles (128 h columns, 2 waves along N)
+// when n_half allows, otherwise (and for MXFP8) 128x128 tiles (64 h columns).
+static bool swiglu_big(int n_half, int wfmt) { return wfmt == W_BF16 && n_half % 128 == 0; }
+
+int gemm_swiglu_parts(int n_half, int wfmt) {
+  return swiglu_big(n_half, wfmt) ? (n_half / 128) * 2 : (n_half / 64) * 2;
+}
+
+int gemm_swiglu_ss_parts(const GemmArgs& g) { return gemm_swiglu_parts(g.n_half, g.wfmt); }
+
+template <int BM, int BN, int WMW, int WNW, int EPI, int STAGES, int PBK = 32>
+static hipError_t go_pipe(const GemmArgs& g, hipStream_t st, int ntiles_n) {
+  dim3 grid(ntiles_n, (g.M + BM - 1) / BM, g.splits);
+  hipLaunchKernelGGL((k_gemm_pipe<BM, BN, WMW, WNW, EPI, STAGES, PBK>), grid, dim3(GT), 0, st, g);
+  return hipGetLastError();
 }
 
 template <int BM, int BN, int WMW, int WNW, int EPI>
@@ -301,21 +484,34 @@ hipError_t launch_gemm(const GemmArgs& gin, hipStream_t st) {
     return hipGetLastError();
   }
   if (g.act != ACT_BF16 || g.K % BK != 0 || g.K % (g.splits * BK) != 0) return hipErrorInvalidValue;
+  const bool bf = g.wfmt == W_BF16;  // bf16 weights: direct-to-LDS pipeline
   switch (g.epi) {
-    case EPI_PARTIAL:
+    case EPI_PARTIAL:  // small M (decode): stream the weights, split K
       if (g.N % 64) return hipErrorInvalidValue;
+      if (bf) {
+        if (g.M <= 32) return go_pipe<32, 64, 1, 4, EPI_PARTIAL, 4, 32>(g, st, g.N / 64);
+        if (g.M <= 64) return go_pipe<64, 64, 1, 4, EPI_PARTIAL, 4, 32>(g, st, g.N / 64);
+        return go_pipe<128, 64, 1, 4, EPI_PARTIAL, 4, 32>(g, st, g.N / 64);
+      }
       if (g.M <= 32) return go<32, 64, 1, 4, EPI_PARTIAL>(g, st, g.N / 64);
       if (g.M <= 64) return go<64, 64, 1, 4, EPI_PARTIAL>(g, st, g.N / 64);
       return go<128, 64, 1, 4, EPI_PARTIAL>(g, st, g.N / 64);
     case EPI_STORE_ACT:
-      if (g.N % 128 || g.splits != 1) return hipErrorInvalidValue;
+      if (g.splits != 1) return hipErrorInvalidValue;
+      if (bf && g.N % 256 == 0) return go_pipe<256, 256, 2, 2, EPI_STORE_ACT, 2, 64>(g, st, g.N / 256);
+      if (bf && g.N % 160 == 0) return go_pipe<256, 160, 2, 2, EPI_STORE_ACT, 2, 64>(g, st, g.N / 160);
+      if (g.N % 128) return hipErrorInvalidValue;
       return go<128, 128, 2, 2, EPI_STORE_ACT>(g, st, g.N / 128);
     case EPI_F32_ROWSCALE:
-      if (g.N % 128 || g.splits != 1) return hipErrorInvalidValue;
+      if (g.splits != 1) return hipErrorInvalidValue;
+      if (bf && g.N % 160 == 0) return go_pipe<256, 160, 2, 2, EPI_F32_ROWSCALE, 2, 64>(g, st, g.N / 160);
+      if (bf && g.N % 256 == 0) return go_pipe<256, 256, 2, 2, EPI_F32_ROWSCALE, 2, 64>(g, st, g.N / 256);
+      if (g.N % 128) return hipErrorInvalidValue;
       return go<128, 128, 2, 2, EPI_F32_ROWSCALE>(g, st, g.N / 128);
     case EPI_SWIGLU:
       if (g.n_half % 64 || g.splits != 1) return hipErrorInvalidValue;
       g.ss_n = gemm_swiglu_ss_parts(g);
+      if (swiglu_big(g.n_half, g.wfmt)) return go_pipe<256, 256, 2, 2, EPI_SWIGLU, 2, 64>(g, st, g.n_half / 128);
       return go<128, 128, 2, 2, EPI_SWIGLU>(g, st, g.n_half / 64);
     default:
       return hipErrorInvalidValue;

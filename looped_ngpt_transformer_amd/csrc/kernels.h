@@ -40,6 +40,7 @@ struct GemmArgs {
 };
 // Number of sumsq partials per row the SWIGLU epilogue writes for this shape.
 int gemm_swiglu_ss_parts(const GemmArgs& g);
+int gemm_swiglu_parts(int n_half, int wfmt);
 // Split count the launcher would use for a decode-shaped GEMM (EPI_PARTIAL).
 int gemm_pick_splits(int M, int N, int K, int wfmt);
 hipError_t launch_gemm(const GemmArgs& g, hipStream_t st);

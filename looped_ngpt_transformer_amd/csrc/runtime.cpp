@@ -71,7 +71,9 @@ Dims dims_of(const dory_config& c) {
   D.esz = c.act_dtype == DORY_DTYPE_F32 ? 4 : 2;
   D.page_elems = (size_t)2 * D.Hkv * DORY_PAGE_TOKENS * D.d;
   D.page_bytes = D.page_elems * D.esz;
-  D.ss_h_n = c.act_dtype == DORY_DTYPE_BF16 ? std::max(1, (D.I / 64) * 2) : 1;
+  D.ss_h_n = c.act_dtype == DORY_DTYPE_BF16
+                 ? std::max(1, gemm_swiglu_parts(D.I, c.weight_format == DORY_WFMT_MXFP8 ? W_MXFP8 : W_BF16))
+                 : 1;
   D.max_tiles = (c.max_rows + 63) / 64 + c.max_seqs;
   return D;
 }
