@@ -61,4 +61,19 @@ __device__ __forceinline__ float block_sum(float v, float* red) {
 
 __device__ __forceinline__ float inv_norm(float sumsq) { return 1.0f / fmaxf(sqrtf(sumsq), NORM_EPS); }
 
+// sigmoid gate value for (row m, channel c) from the projection output (bf16 [M, ld]
+// or float split partials [splits][M][ld])
+__device__ __forceinline__ float gate_at(const void* g, int f32, int ld, int splits, size_t sstride,
+                                         int m, int c) {
+  float x;
+  if (f32) {
+    const float* f = (const float*)g + (size_t)m * ld + c;
+    x = 0.f;
+    for (int s = 0; s < splits; ++s) x += f[(size_t)s * sstride];
+  } else {
+    x = bf2f(((const bf16_t*)g)[(size_t)m * ld + c]);
+  }
+  return 1.f / (1.f + __expf(-x));
+}
+
 }  // namespace dory

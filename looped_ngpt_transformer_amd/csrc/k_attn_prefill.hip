@@ -12,10 +12,10 @@
 //   O^T += V^T P^T (A = V^T from LDS, B = P straight from the S^T accumulators: the lane
 //   already holds 2x4 keys of its query, which is a valid k-ordering of the MFMA when
 //   V^T is read with the same key permutation).
-// K is staged row-major (padded rows), V transposed into LDS (padded rows); the next
-// page is prefetched into registers while the current one is consumed. Entries of the
-// last page beyond the chunk's last position are zeroed, so unwritten cache memory can
-// never reach the sums.
+// K is staged row-major (padded rows) and V^T (the page stores V channel-major) into
+// padded LDS rows; the next page is prefetched into registers while the current one is
+// consumed. Entries of the last page beyond the chunk's last position are zeroed, so
+// unwritten cache memory can never reach the sums.
 #include "common.h"
 #include "kernels.h"
 
@@ -27,7 +27,7 @@ __global__ __launch_bounds__(512) void k_attn_prefill(AttnArgs a) {
   constexpr int DC = D / 32;       // 32-wide chunks of the head dim (QK contraction)
   constexpr int CB = D / 16;       // 16-channel blocks of the output
   constexpr int KCH = D / 8 + 1;   // 16-byte chunks per padded K row
-  constexpr int VTR = 64 + 4;      // bf16 per padded V^T row
+  constexpr int VTR = 64 + 8;      // bf16 per padded V^T row (144 B: 16-byte aligned)
   constexpr int NCH = 2 * 64 * D / 8;  // 16-byte chunks of K and V per page and head
   constexpr int CPT = NCH / 512;       // chunks per thread
   static_assert(D % 32 == 0 && NCH % 512 == 0, "head dim");
@@ -83,17 +83,21 @@ __global__ __launch_bounds__(512) void k_attn_prefill(AttnArgs a) {
       const int s = t + 512 * i;
       const bool isv = s >= NCH / 2;
       const int s2 = isv ? s - NCH / 2 : s;
-      const int j = s2 / (D / 8), ch = s2 % (D / 8);
-      const uint4 v = (pg * PAGE + j > kmax) ? make_uint4(0, 0, 0, 0) : pre[i];
-      if (!isv) {
-        Ks[j * KCH + ch] = v;
-      } else {
-        const uint32_t wv[4] = {v.x, v.y, v.z, v.w};
+      if (!isv) {  // K chunk: token j, channels 8 ch .. 8 ch + 7
+        const int j = s2 / (D / 8), ch = s2 % (D / 8);
+        Ks[j * KCH + ch] = (pg * PAGE + j > kmax) ? make_uint4(0, 0, 0, 0) : pre[i];
+      } else {     // V^T chunk: channel c, tokens 8 kc .. 8 kc + 7
+        const int c = s2 / 8, kc = s2 % 8;
+        uint4 v = pre[i];
+        const int over = pg * PAGE + 8 * kc + 7 - kmax;  // tokens past the chunk's last
+        if (over > 0) {
+          uint32_t wv[4] = {v.x, v.y, v.z, v.w};
 #pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          Vt[(8 * ch + 2 * e) * VTR + j] = (bf16_t)(wv[e] & 0xFFFF);
-          Vt[(8 * ch + 2 * e + 1) * VTR + j] = (bf16_t)(wv[e] >> 16);
+          for (int e = 0; e < 8; ++e)
+            if (8 * kc + e > kmax - pg * PAGE) wv[e / 2] &= (e & 1) ? 0x0000FFFFu : 0xFFFF0000u;
+          v = make_uint4(wv[0], wv[1], wv[2], wv[3]);
         }
+        *(uint4*)(Vt + c * VTR + 8 * kc) = v;
       }
     }
   };
@@ -204,13 +208,9 @@ __global__ __launch_bounds__(512) void k_attn_prefill(AttnArgs a) {
       for (int r = 0; r < 4; ++r) v[r] = o[cb][qb][r] * invl;
       if (qv) {
         if (a.g) {
-          const uint2 gg = *(const uint2*)((const bf16_t*)a.g + base + c);
-          const uint32_t gw[2] = {gg.x, gg.y};
 #pragma unroll
-          for (int r = 0; r < 4; ++r) {
-            const float gv = bf2f((bf16_t)((gw[r / 2] >> (16 * (r & 1))) & 0xFFFF));
-            v[r] *= 1.f / (1.f + __expf(-gv));
-          }
+          for (int r = 0; r < 4; ++r)
+            v[r] *= gate_at(a.g, a.g_f32, a.g_ld, a.g_splits, a.g_sstride, row0 + i, h * D + c + r);
         }
         uint2 ov;
         ov.x = (uint32_t)f2bf(v[0]) | ((uint32_t)f2bf(v[1]) << 16);

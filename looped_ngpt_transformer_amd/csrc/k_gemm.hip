@@ -90,6 +90,22 @@ __device__ __forceinline__ void gemm_epilogue(const GemmArgs& g, f32x4 (&acc)[BM
   }
 }
 
+// Row scales 1/||row|| of the tile's BM rows from the producer's sum-of-squares
+// partials: the [BM, rs_n] block is contiguous, read coalesced and summed per row with
+// LDS atomics. Ends with a barrier.
+template <int BM>
+__device__ __forceinline__ void load_rowscale(const GemmArgs& g, int m0, float* rowscale) {
+  for (int r = threadIdx.x; r < BM; r += GT) rowscale[r] = 0.f;
+  __syncthreads();
+  const int rows = min(BM, g.M - m0);
+  const int n = rows * g.rs_n;
+  const float* src = g.rs_ss + (size_t)m0 * g.rs_n;
+  for (int e = threadIdx.x; e < n; e += GT) atomicAdd(&rowscale[e / g.rs_n], src[e]);
+  __syncthreads();
+  for (int r = threadIdx.x; r < BM; r += GT) rowscale[r] = inv_norm(rowscale[r]);
+  __syncthreads();
+}
+
 // XCD-aware tile order. Work-groups are dispatched round-robin over the 8 XCDs (each
 // with its own L2); give each XCD a contiguous share of the tiles, ordered in groups of
 // GM m-tiles (m fastest) so the tiles resident on one XCD share A rows and B columns.
@@ -195,15 +211,7 @@ __global__ __launch_bounds__(GT) void k_gemm_mfma(GemmArgs g) {
     }
   };
 
-  if (EPI == EPI_F32_ROWSCALE) {
-    for (int r = t; r < BM; r += GT) {
-      const int m = m0 + r;
-      float s = 0.f;
-      if (m < g.M)
-        for (int j = 0; j < g.rs_n; ++j) s += g.rs_ss[(size_t)m * g.rs_n + j];
-      rowscale[r] = inv_norm(s);
-    }
-  }
+  if (EPI == EPI_F32_ROWSCALE) load_rowscale<BM>(g, m0, rowscale);
 
   f32x4 acc[FM][FN];
 #pragma unroll
@@ -341,15 +349,7 @@ __global__ __launch_bounds__(GT) void k_gemm_pipe(GemmArgs g) {
     }
   };
 
-  if (EPI == EPI_F32_ROWSCALE) {
-    for (int r = t; r < BM; r += GT) {
-      const int m = m0 + r;
-      float sacc = 0.f;
-      if (m < g.M)
-        for (int j = 0; j < g.rs_n; ++j) sacc += g.rs_ss[(size_t)m * g.rs_n + j];
-      rowscale[r] = inv_norm(sacc);
-    }
-  }
+  if (EPI == EPI_F32_ROWSCALE) load_rowscale<BM>(g, m0, rowscale);
 
   f32x4 acc[FM][FN];
 #pragma unroll
@@ -440,10 +440,11 @@ __global__ __launch_bounds__(256) void k_gemm_f32(GemmArgs g) {
 
 // ------------------------------------------------------------------------ dispatch
 int gemm_pick_splits(int M, int N, int K, int wfmt) {
-  // small-M (decode) tiles are BN = 64 wide; aim for >= 512 work-groups
+  // small-M (decode) tiles are BN = 64 wide; split K until there are >= 400 work-groups
+  // (each split a multiple of 64 and at least 128 long)
   const int tiles = (N / 64) * ((M + 127) / 128);
   int s = 1;
-  while (s < 16 && tiles * s < 512 && (K / BK) % (2 * s) == 0 && K / (2 * s) >= 2 * BK) s *= 2;
+  while (s < 16 && tiles * s < 400 && (K / BK) % (2 * s) == 0 && K / (2 * s) >= 2 * BK) s *= 2;
   return s;
 }
 
@@ -489,9 +490,9 @@ hipError_t launch_gemm(const GemmArgs& gin, hipStream_t st) {
     case EPI_PARTIAL:  // small M (decode): stream the weights, split K
       if (g.N % 64) return hipErrorInvalidValue;
       if (bf) {
-        if (g.M <= 32) return go_pipe<32, 64, 1, 4, EPI_PARTIAL, 4, 32>(g, st, g.N / 64);
-        if (g.M <= 64) return go_pipe<64, 64, 1, 4, EPI_PARTIAL, 4, 32>(g, st, g.N / 64);
-        return go_pipe<128, 64, 1, 4, EPI_PARTIAL, 4, 32>(g, st, g.N / 64);
+        if (g.M <= 32) return go_pipe<32, 64, 1, 4, EPI_PARTIAL, 4, 64>(g, st, g.N / 64);
+        if (g.M <= 64) return go_pipe<64, 64, 1, 4, EPI_PARTIAL, 4, 64>(g, st, g.N / 64);
+        return go_pipe<128, 64, 1, 4, EPI_PARTIAL, 3, 64>(g, st, g.N / 64);
       }
       if (g.M <= 32) return go<32, 64, 1, 4, EPI_PARTIAL>(g, st, g.N / 64);
       if (g.M <= 64) return go<64, 64, 1, 4, EPI_PARTIAL>(g, st, g.N / 64);

@@ -1,4 +1,6 @@
 // SwiGLU activation from split-K partial sums, and the MXFP8 weight quantiser.
+#include <algorithm>
+
 #include "common.h"
 #include "kernels.h"
 
@@ -8,15 +10,18 @@ namespace dory {
 // [splits][M][2I] (gate columns [0, I), up columns [I, 2I)). Also writes the row's
 // sum of squares of h in ss_n partials (the L2 norm before the down projection,
 // arXiv §2, is applied by the consumer as a row scale).
+// grid (M, blocks per row): block b of a row covers columns [b*1024, (b+1)*1024) and
+// writes its sum of squares to ss[m][b]; block 0 also clears ss[m][nb .. ss_n).
 template <typename T>
 __global__ __launch_bounds__(256) void k_swiglu(const float* gu, int splits, int M, int I,
                                                 T* h, float* ss, int ss_n) {
   __shared__ float red[4];
-  const int m = blockIdx.x;
+  const int m = blockIdx.x, b = blockIdx.y, nb = gridDim.y;
   const size_t sstride = (size_t)M * 2 * I;
   const size_t row = (size_t)m * 2 * I;
   float sq = 0.f;
-  for (int i = threadIdx.x; i < I; i += blockDim.x) {
+  const int i1 = min(I, (b + 1) * 1024);
+  for (int i = b * 1024 + threadIdx.x; i < i1; i += blockDim.x) {
     float g = 0.f, u = 0.f;
     for (int s = 0; s < splits; ++s) {
       g += gu[s * sstride + row + i];
@@ -27,19 +32,21 @@ __global__ __launch_bounds__(256) void k_swiglu(const float* gu, int splits, int
     sq += v * v;
   }
   sq = block_sum<4>(sq, red);
-  if (threadIdx.x == 0) {
-    ss[(size_t)m * ss_n] = sq;
-    for (int j = 1; j < ss_n; ++j) ss[(size_t)m * ss_n + j] = 0.f;
-  }
+  if (threadIdx.x == 0) ss[(size_t)m * ss_n + b] = sq;
+  if (b == 0)
+    for (int j = nb + threadIdx.x; j < ss_n; j += blockDim.x) ss[(size_t)m * ss_n + j] = 0.f;
 }
 
 hipError_t launch_swiglu(const float* gu, int splits, int M, int I, void* h, int act,
                          float* ss, int ss_n, hipStream_t st) {
   if (M == 0) return hipSuccess;
+  const int nb = std::min((I + 1023) / 1024, ss_n);
+  if (nb < 1 || (I + 1023) / 1024 > ss_n) return hipErrorInvalidValue;
+  const dim3 grid(M, nb);
   if (act == ACT_F32)
-    hipLaunchKernelGGL(k_swiglu<float>, dim3(M), dim3(256), 0, st, gu, splits, M, I, (float*)h, ss, ss_n);
+    hipLaunchKernelGGL(k_swiglu<float>, grid, dim3(256), 0, st, gu, splits, M, I, (float*)h, ss, ss_n);
   else
-    hipLaunchKernelGGL(k_swiglu<bf16_t>, dim3(M), dim3(256), 0, st, gu, splits, M, I, (bf16_t*)h, ss, ss_n);
+    hipLaunchKernelGGL(k_swiglu<bf16_t>, grid, dim3(256), 0, st, gu, splits, M, I, (bf16_t*)h, ss, ss_n);
   return hipGetLastError();
 }
 

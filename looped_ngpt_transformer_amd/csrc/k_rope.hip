@@ -6,28 +6,38 @@
 //    (MXFP8 article, rope_parameters; arXiv §3.4);
 //  * with QK normalisation each rotated head is L2-normalised and scaled by s_qk
 //    (arXiv §2: query-key scale of the nGPT backbone);
-//  * k and v go to the row's page slot of the (layer, KV slot) stream; q and the gate
-//    pre-activation go to the attention's inputs.
-// The angle is formed and reduced modulo 2*pi in double precision (positions reach
-// 262144), then sin/cos are taken in float.
+//  * k and v go to the row's page slot of the (layer, KV slot) stream; q goes to the
+//    attention's input (the gate pre-activation is read in place by the attention).
+// The frequencies theta^(-2i/d) come from a table computed on the host in double; the
+// angle is formed and reduced modulo 2*pi in double precision (positions reach 262144),
+// then sin/cos are taken in float.
 #include "common.h"
 #include "kernels.h"
 
 namespace dory {
 
+// Page layout (per KV head): K row-major [64 tokens][d], V channel-major [d][64 tokens].
+// kv_k_ptr: the token's K row (d contiguous elements).
 template <typename KV>
-__device__ __forceinline__ KV* kv_page_ptr(const KVLayout& kv, int seq, int stream, int pos,
-                                           bool is_v, int head) {
+__device__ __forceinline__ KV* kv_k_ptr(const KVLayout& kv, int seq, int stream, int pos, int head) {
   const int lp = pos / PAGE;
   const int32_t page =
       kv.table[((size_t)seq * kv.n_streams + stream) * kv.tab_len + (lp % kv.ring)];
-  const size_t base = (size_t)page * kv.page_elems +
-                      (is_v ? (size_t)kv.Hkv * PAGE * kv.d : 0) +
-                      ((size_t)head * PAGE + (pos % PAGE)) * kv.d;
-  return (KV*)kv.pool + base;
+  return (KV*)kv.pool + (size_t)page * kv.page_elems + ((size_t)head * PAGE + (pos % PAGE)) * kv.d;
+}
+// kv_v_ptr: channel 0 of the token's V column; channel j is at [j * 64].
+template <typename KV>
+__device__ __forceinline__ KV* kv_v_ptr(const KVLayout& kv, int seq, int stream, int pos, int head) {
+  const int lp = pos / PAGE;
+  const int32_t page =
+      kv.table[((size_t)seq * kv.n_streams + stream) * kv.tab_len + (lp % kv.ring)];
+  return (KV*)kv.pool + (size_t)page * kv.page_elems + (size_t)kv.Hkv * PAGE * kv.d +
+         (size_t)head * kv.d * PAGE + (pos % PAGE);
 }
 
-template <typename IN, typename OUT>
+// grid (M rows, head groups + 1): block y < n_hb rotates heads 4y .. 4y+3 (one per wave,
+// queries then keys); the last block copies v to the cache.
+template <typename OUT>
 __global__ __launch_bounds__(256) void k_rope_kv(RopeArgs a) {
   const int m = blockIdx.x;
   const int lane = threadIdx.x & (WAVE - 1);
@@ -46,22 +56,21 @@ __global__ __launch_bounds__(256) void k_rope_kv(RopeArgs a) {
     }
     return bf2f(((const bf16_t*)a.qkvg)[rowoff + col]);
   };
-  const double ln_theta = log(a.theta);
-  OUT* qo = (OUT*)a.q_out;
-  // heads 0..Hq-1 are queries, Hq..Hq+Hkv-1 keys; one wave per head
-  for (int h = wave; h < a.Hq + a.Hkv; h += blockDim.x / WAVE) {
+  const int n_heads = a.Hq + a.Hkv;
+  const int n_hb = (n_heads + 3) / 4;
+  if ((int)blockIdx.y < n_hb) {
+    const int h = blockIdx.y * 4 + wave;
+    if (h >= n_heads) return;
     const bool is_q = h < a.Hq;
     const int col0 = is_q ? h * d : a.Hq * d + (h - a.Hq) * d;
     float r[4];
-    int idx[2];
     float sq = 0.f;
 #pragma unroll
     for (int j = 0; j < 2; ++j) {
       const int i = lane + j * WAVE;
-      idx[j] = i;
       if (i < half) {
-        const double freq = exp(-(2.0 * i / d) * ln_theta);
-        double ang = (double)p * freq;
+        // angle p * theta^(-2i/d) in double, reduced modulo 2*pi before the float sin/cos
+        double ang = (double)p * a.freq[i];
         ang -= 6.283185307179586 * rint(ang * 0.15915494309189535);
         float sn, cs;
         sincosf((float)ang, &sn, &cs);
@@ -75,9 +84,10 @@ __global__ __launch_bounds__(256) void k_rope_kv(RopeArgs a) {
     }
     float sc = 1.f;
     if (a.qk_norm) sc = inv_norm(wave_sum(sq));
+    OUT* qo = (OUT*)a.q_out;
 #pragma unroll
     for (int j = 0; j < 2; ++j) {
-      const int i = idx[j];
+      const int i = lane + j * WAVE;
       if (i >= half) continue;
       float v1 = r[2 * j] * sc, v2 = r[2 * j + 1] * sc;
       if (a.qk_norm) {
@@ -89,34 +99,31 @@ __global__ __launch_bounds__(256) void k_rope_kv(RopeArgs a) {
         st<OUT>(qo, o + i, v1);
         st<OUT>(qo, o + i + half, v2);
       } else {
-        OUT* kp = kv_page_ptr<OUT>(a.kv, seq, a.stream_idx, p, false, h - a.Hq);
+        OUT* kp = kv_k_ptr<OUT>(a.kv, seq, a.stream_idx, p, h - a.Hq);
         st<OUT>(kp, i, v1);
         st<OUT>(kp, i + half, v2);
       }
     }
+    return;
   }
-  // v -> V page (unrotated), gate pre-activation -> g_out
+  // v -> V page (unrotated); the gate stays in the projection output
   const int vcol0 = a.Hq * d + a.Hkv * d;
   for (int c = threadIdx.x; c < a.Hkv * d; c += blockDim.x) {
     const int hk = c / d, j = c % d;
-    OUT* vp = kv_page_ptr<OUT>(a.kv, seq, a.stream_idx, p, true, hk);
-    st<OUT>(vp, j, in(vcol0 + c));
-  }
-  if (a.gate) {
-    const int gcol0 = vcol0 + a.Hkv * d;
-    OUT* go = (OUT*)a.g_out;
-    for (int c = threadIdx.x; c < a.Hq * d; c += blockDim.x)
-      st<OUT>(go, (size_t)m * a.Hq * d + c, in(gcol0 + c));
+    OUT* vp = kv_v_ptr<OUT>(a.kv, seq, a.stream_idx, p, hk);
+    st<OUT>(vp, (size_t)j * PAGE, in(vcol0 + c));
   }
 }
 
 hipError_t launch_rope_kv(const RopeArgs& a, hipStream_t st) {
   if (a.M == 0) return hipSuccess;
+  if (a.d > 256 || !a.freq) return hipErrorInvalidValue;
+  dim3 grid(a.M, (a.Hq + a.Hkv + 3) / 4 + 1);
   if (a.kv.act == ACT_F32) {
     if (!a.in_f32) return hipErrorInvalidValue;
-    hipLaunchKernelGGL((k_rope_kv<float, float>), dim3(a.M), dim3(256), 0, st, a);
+    hipLaunchKernelGGL(k_rope_kv<float>, grid, dim3(256), 0, st, a);
   } else {
-    hipLaunchKernelGGL((k_rope_kv<float, bf16_t>), dim3(a.M), dim3(256), 0, st, a);
+    hipLaunchKernelGGL(k_rope_kv<bf16_t>, grid, dim3(256), 0, st, a);
   }
   return hipGetLastError();
 }
@@ -143,8 +150,8 @@ __global__ __launch_bounds__(256) void k_fill_kv(KVLayout kv, int seq, int strea
   const int hd = kv.Hkv * kv.d;
   for (int c = threadIdx.x; c < hd; c += blockDim.x) {
     const int hk = c / kv.d, j = c % kv.d;
-    kv_page_ptr<T>(kv, seq, stream, p, false, hk)[j] = k[(size_t)r * hd + c];
-    kv_page_ptr<T>(kv, seq, stream, p, true, hk)[j] = v[(size_t)r * hd + c];
+    kv_k_ptr<T>(kv, seq, stream, p, hk)[j] = k[(size_t)r * hd + c];
+    kv_v_ptr<T>(kv, seq, stream, p, hk)[(size_t)j * PAGE] = v[(size_t)r * hd + c];
   }
 }
 

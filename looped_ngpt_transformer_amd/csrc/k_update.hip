@@ -17,21 +17,21 @@
 
 namespace dory {
 
-constexpr int UPD_THREADS = 256;
-constexpr int UPD_MAXPER = 16;  // H <= 4096
-
-template <typename SB>
+// THREADS per row: 256 for many rows, 1024 for few rows (decode) so that each row's
+// loads are spread over more waves.
+template <typename SB, int UPD_THREADS>
 __global__ __launch_bounds__(UPD_THREADS) void k_update(UpdateArgs u) {
+  constexpr int UPD_MAXPER = 4096 / UPD_THREADS;  // H <= 4096
   __shared__ float red[UPD_THREADS / WAVE];
   const int m = blockIdx.x;
   const int H = u.H;
   const size_t row = (size_t)m * H;
   float v[UPD_MAXPER];
   float rs = 1.f;
-  if (u.rs_ss) {
+  if (u.rs_ss) {  // row scale 1/||row|| from the producer's sum-of-squares partials
     float t = 0.f;
-    for (int j = 0; j < u.rs_n; ++j) t += u.rs_ss[(size_t)m * u.rs_n + j];
-    rs = inv_norm(t);
+    for (int j = threadIdx.x; j < u.rs_n; j += UPD_THREADS) t += u.rs_ss[(size_t)m * u.rs_n + j];
+    rs = inv_norm(block_sum<UPD_THREADS / WAVE>(t, red));
   }
   float sq = 0.f;
 #pragma unroll
@@ -113,10 +113,14 @@ __global__ __launch_bounds__(256) void k_stage_input(const float* x, float* s, S
 
 hipError_t launch_update(const UpdateArgs& u, hipStream_t st) {
   if (u.M == 0) return hipSuccess;
-  if (u.act == ACT_F32)
-    hipLaunchKernelGGL(k_update<float>, dim3(u.M), dim3(UPD_THREADS), 0, st, u);
-  else
-    hipLaunchKernelGGL(k_update<bf16_t>, dim3(u.M), dim3(UPD_THREADS), 0, st, u);
+  const bool few = u.M < 512;
+  if (u.act == ACT_F32) {
+    if (few) hipLaunchKernelGGL((k_update<float, 1024>), dim3(u.M), dim3(1024), 0, st, u);
+    else hipLaunchKernelGGL((k_update<float, 256>), dim3(u.M), dim3(256), 0, st, u);
+  } else {
+    if (few) hipLaunchKernelGGL((k_update<bf16_t, 1024>), dim3(u.M), dim3(1024), 0, st, u);
+    else hipLaunchKernelGGL((k_update<bf16_t, 256>), dim3(u.M), dim3(256), 0, st, u);
+  }
   return hipGetLastError();
 }
 

@@ -88,11 +88,10 @@ struct RopeArgs {
   int M = 0, Hq = 0, Hkv = 0, d = 0, Nqkvg = 0, gate = 0;
   const int32_t* pos = nullptr;      // [M]
   const int32_t* row_seq = nullptr;  // [M] sequence slot
-  double theta = 1e4;
+  const double* freq = nullptr;  // [d/2] theta^(-2i/d) for this layer's base
   int qk_norm = 1;
   const float* s_qk = nullptr;  // [d]
   void* q_out = nullptr;        // act [M, Hq*d]
-  void* g_out = nullptr;        // act [M, Hq*d] (gate pre-activation)
   KVLayout kv;
   int stream_idx = 0;           // (layer, slot) stream within the sequence
 };
@@ -101,7 +100,11 @@ hipError_t launch_rope_kv(const RopeArgs& a, hipStream_t st);
 // ------------------------------------------------------------------------ attention
 struct AttnArgs {
   const void* q = nullptr;        // act [M, Hq*d] (rotated, normalised)
-  const void* g = nullptr;        // act [M, Hq*d] gate pre-activation (or null)
+  // gate pre-activation, read where the projection left it: row m, channel c at
+  // g[m * g_ld + c] (+ split s at s * g_sstride for float partials, summed over g_splits)
+  const void* g = nullptr;        // null: no gate
+  int g_f32 = 0, g_ld = 0, g_splits = 1;
+  size_t g_sstride = 0;
   int M = 0, Hq = 0, Hkv = 0, d = 0;
   const int32_t* pos = nullptr;
   const int32_t* row_seq = nullptr;

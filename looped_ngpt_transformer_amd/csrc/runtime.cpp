@@ -31,6 +31,7 @@ constexpr int NSTAGE = 4;          // pinned staging buffers in rotation
 constexpr int DELTA_CAP = 65536;   // page-table updates per upload
 constexpr int SKINNY_M = 128;      // rows up to which projections use split-K tiles
 constexpr size_t ALIGN = 256;
+constexpr int ROPE_INTS = 2 * 128 * 2;  // two tables of up to 128 doubles
 
 thread_local std::string g_create_err;
 
@@ -47,7 +48,7 @@ struct Dims {
 };
 
 struct WsLayout {
-  size_t table, meta, s, x, sb, qkvg, q, g, o, h, part, ss_o, ss_h, apart, total;
+  size_t table, meta, s, x, sb, qkvg, q, o, h, part, ss_o, ss_h, apart, total;
   size_t part_floats, apart_floats;
   size_t meta_ints;
 };
@@ -71,9 +72,10 @@ Dims dims_of(const dory_config& c) {
   D.esz = c.act_dtype == DORY_DTYPE_F32 ? 4 : 2;
   D.page_elems = (size_t)2 * D.Hkv * DORY_PAGE_TOKENS * D.d;
   D.page_bytes = D.page_elems * D.esz;
-  D.ss_h_n = c.act_dtype == DORY_DTYPE_BF16
-                 ? std::max(1, gemm_swiglu_parts(D.I, c.weight_format == DORY_WFMT_MXFP8 ? W_MXFP8 : W_BF16))
-                 : 1;
+  D.ss_h_n = std::max((D.I + 1023) / 1024,  // SwiGLU-reduce blocks per row
+                      c.act_dtype == DORY_DTYPE_BF16
+                          ? gemm_swiglu_parts(D.I, c.weight_format == DORY_WFMT_MXFP8 ? W_MXFP8 : W_BF16)
+                          : 1);
   D.max_tiles = (c.max_rows + 63) / 64 + c.max_seqs;
   return D;
 }
@@ -88,14 +90,15 @@ WsLayout layout_of(const dory_config& c, const Dims& D) {
     return o;
   };
   W.table = take((size_t)c.max_seqs * D.n_streams * D.tab_len * 4);
-  W.meta_ints = 2 * R + 4 * (size_t)D.max_tiles + 2 * (size_t)DELTA_CAP;
+  // metadata per call: positions, row -> sequence slot, prefill tiles, RoPE frequency
+  // tables (2 bases x 128 doubles), page-table updates
+  W.meta_ints = 2 * R + 4 * (size_t)D.max_tiles + ROPE_INTS + 2 * (size_t)DELTA_CAP;
   W.meta = take(W.meta_ints * 4);
   W.s = take(R * D.H * 4);
   W.x = take(R * D.H * 4);
   W.sb = take(R * D.H * D.esz);
   W.qkvg = take(R * D.Nqkvg * D.esz);
   W.q = take(R * D.Nq * D.esz);
-  W.g = take(R * D.Nq * D.esz);
   W.o = take(R * D.Nq * D.esz);
   W.h = take(R * D.I * D.esz);
   const size_t maxN = std::max({(size_t)D.Nqkvg, (size_t)2 * D.I, (size_t)D.H});
@@ -498,11 +501,10 @@ int run_layer(dory_ctx* ctx, hipStream_t st, const CallPlan& P, int l, int slot,
   ra.gate = D.Ng > 0;
   ra.pos = meta;
   ra.row_seq = meta + c.max_rows;
-  ra.theta = full ? c.theta_full : c.theta_swa;
+  ra.freq = (const double*)(meta + 2 * c.max_rows + 4 * D.max_tiles) + (full ? 128 : 0);
   ra.qk_norm = c.qk_norm;
   ra.s_qk = w.s_qk;
   ra.q_out = ws + W.q;
-  ra.g_out = ws + W.g;
   ra.kv = kv_layout(ctx, l);
   ra.stream_idx = sidx;
   {
@@ -513,7 +515,18 @@ int run_layer(dory_ctx* ctx, hipStream_t st, const CallPlan& P, int l, int slot,
 
   AttnArgs aa;
   aa.q = ws + W.q;
-  aa.g = D.Ng ? ws + W.g : nullptr;
+  if (D.Ng) {  // the gate columns of the [q|k|v|gate] projection output
+    const int gcol = D.Nq + 2 * D.Nkv;
+    aa.g_ld = D.Nqkvg;
+    if (ra.in_f32) {
+      aa.g = (const float*)ra.qkvg + gcol;
+      aa.g_f32 = 1;
+      aa.g_splits = S;
+      aa.g_sstride = (size_t)M * D.Nqkvg;
+    } else {
+      aa.g = (const uint16_t*)ra.qkvg + gcol;  // bf16 elements
+    }
+  }
   aa.M = M;
   aa.Hq = D.Hq;
   aa.Hkv = D.Hkv;
@@ -675,7 +688,15 @@ int step(dory_ctx* ctx, hipStream_t st, int n, const int32_t* ids, const int32_t
   // commit: create, grow, build row metadata
   std::vector<int32_t>& meta = ctx->scratch;
   const int R = c.max_rows;
-  meta.assign(2 * (size_t)R + 4 * (size_t)ctx->D.max_tiles, 0);
+  meta.assign(2 * (size_t)R + 4 * (size_t)ctx->D.max_tiles + ROPE_INTS, 0);
+  {  // RoPE frequencies theta^(-2i/d), sliding base then full base
+    double* fr = (double*)(meta.data() + 2 * (size_t)R + 4 * (size_t)ctx->D.max_tiles);
+    const int d = ctx->D.d;
+    for (int i = 0; i < d / 2; ++i) {
+      fr[i] = std::pow(c.theta_swa, -2.0 * i / d);
+      fr[128 + i] = std::pow(c.theta_full, -2.0 * i / d);
+    }
+  }
   CallPlan P;
   int row = 0;
   for (int i = 0; i < n; ++i) {
@@ -720,7 +741,7 @@ int step(dory_ctx* ctx, hipStream_t st, int n, const int32_t* ids, const int32_t
   if ((r = upload(ctx, st, meta.data(), meta.size()))) return r;
   if (nd)
     HIPCHK(launch_apply_deltas((int32_t*)(ctx->ws + ctx->W.table),
-                               (const int32_t*)(ctx->ws + ctx->W.meta) + 2 * R + 4 * ctx->D.max_tiles,
+                               (const int32_t*)(ctx->ws + ctx->W.meta) + 2 * R + 4 * ctx->D.max_tiles + ROPE_INTS,
                                (int)nd, st), "apply_deltas");
   return run_forward(ctx, st, P, x_in, y_out);
 }

@@ -116,3 +116,51 @@ def test_bitwise_deterministic_and_batch_permutation():
     for i in range(3):
         assert torch.equal(outs[0][i], outs[1][i])     # run to run: bitwise
         assert torch.equal(outs[0][i], outs[2][i])     # row order does not matter
+
+
+def _seed_kv(rt, shape, seqs, k, mode, seed=9):
+    """Reserve each sequence's context and write seeded K/V into every cache slot it
+    holds (sliding layers: the last 128 positions). Returns the oracle's stores."""
+    from oracle import dory_oracle as O
+    from tests.helpers import to_np
+    cfg = O.Config.from_dict(shape)
+    L = shape["n_in"] + shape["n_rec"] + shape["n_out"]
+    stores = {}
+    for sid, C in seqs.items():
+        D.dory_test_reserve(rt.ctx, sid, C)
+        seq = O.Sequence(cfg)
+        seq.length = C
+        for l in range(L):
+            rec = shape["n_in"] <= l < shape["n_in"] + shape["n_rec"]
+            slots = k if (rec and mode == "per_loop") else 1
+            p0 = 0 if O.layer_is_full(cfg, l) else max(0, C - 128)
+            for s in range(slots):
+                kk, vv = synth.make_kv(shape, seed, sid, l, s, p0, C - p0, device="cuda")
+                D.dory_test_fill_kv(rt.ctx, sid, l, s, p0, kk, vv)
+                seq.kv.write(l, s, np.arange(p0, C), to_np(kk), to_np(vv))
+        stores[sid] = seq
+    torch.cuda.synchronize()
+    return stores
+
+
+@pytest.mark.parametrize("mode", ["per_loop", "last_loop"])
+def test_bf16_decode_over_seeded_context(mode):
+    """Decode steps of two sequences over seeded 1500- and 900-token contexts: many KV
+    pages per row (split over waves), partial pages and sliding-window rings."""
+    from oracle import dory_oracle as O
+    from tests.helpers import to_np
+    S = PSMALL
+    k = 2
+    w = gpu_weights(S, 8)
+    rt = DoryRuntime(S, w, max_loops=2, max_seqs=2, max_seq_len=1600, max_rows=256, mode=mode, loops=k)
+    stores = _seed_kv(rt, S, {0: 1500, 1: 900}, k, mode)
+    cfg, W = oracle_model(S, w)
+    for step in range(3):
+        X = xin(S, 2, 60 + step)
+        y = rt.decode([1, 0], X)
+        torch.cuda.synchronize()
+        got = y.cpu().double().numpy()
+        for j, sid in enumerate([1, 0]):
+            ref = O.prefill(cfg, W, stores[sid], to_np(X[j:j + 1]), k, mode)
+            compare(got[j:j + 1], ref, S, f"step {step} seq {sid}")
+    rt.close()
