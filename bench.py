@@ -55,7 +55,35 @@ def parse():
     ap.add_argument("--batch", type=int, default=None, help="decode batch (D, Q)")
     ap.add_argument("--cpu-rows", type=int, default=256)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--copy-probe", action="store_true",
+                    help="run out = src * 1 over 1 GiB first (counter calibration for rocprofv3 --pmc)")
     return ap.parse_args()
+
+
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic.json")
+
+
+def source_digest(*names):
+    """Digest of kernel sources: measured traffic applies only to the code it came from."""
+    import hashlib
+    h = hashlib.sha256()
+    for n in names:
+        with open(os.path.join(ROOT, "looped_ngpt_transformer_amd", "csrc", n), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+def measured_traffic(key, sources):
+    """HBM bytes per launch from the committed counter summary (FETCH_SIZE + WRITE_SIZE,
+    scaled by the copy-probe calibration), or None when absent or taken on other code."""
+    try:
+        with open(TRAFFIC_FILE) as f:
+            t = json.load(f)[key]
+    except (OSError, KeyError, ValueError):
+        return None
+    if t.get("source_digest") != source_digest(*sources):
+        return None
+    return t.get("bytes_per_launch")
 
 
 def kernel_stats(rt, D):
@@ -68,13 +96,15 @@ def roofline_of(stats, kind):
         ach = g["flops"] / (g["ms"] / 1e3) / 1e12
         return {"bound": "mfma", "kernel": "gemm (bf16 MFMA projections)",
                 "achieved": round(ach, 1), "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
-                "frac": round(ach / PEAK_BF16_TFLOPS, 4), "traffic": None,
+                "frac": round(ach / PEAK_BF16_TFLOPS, 4),
+                "traffic": measured_traffic("prefill_gemm", ["k_gemm.hip", "common.h", "kernels.h"]),
                 "launches": g["launches"], "avg_launch_us": round(1e3 * g["ms"] / g["launches"], 2)}
     a = stats["attention"]
     ach = a["bytes"] / (a["ms"] / 1e3) / 1e9
     return {"bound": "hbm", "kernel": "attention (paged KV, split over keys)",
             "achieved": round(ach, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
-            "frac": round(ach / PEAK_HBM_GBS, 4), "traffic": None,
+            "frac": round(ach / PEAK_HBM_GBS, 4),
+            "traffic": measured_traffic("decode_attention", ["k_attn.hip", "common.h", "kernels.h"]),
             "launches": a["launches"], "avg_launch_us": round(1e3 * a["ms"] / a["launches"], 2)}
 
 
@@ -273,6 +303,12 @@ def main():
     from looped_ngpt_transformer_amd import dory as D
     from looped_ngpt_transformer_amd.runtime import DoryRuntime
     torch.cuda.set_device(0)
+    if args.copy_probe:  # a plain copy kernel of known size: 1 GiB read, 1 GiB written
+        src = torch.ones(2 ** 28, dtype=torch.float32, device="cuda")
+        dst = torch.empty_like(src)
+        torch.mul(src, 1.0, out=dst)
+        torch.cuda.synchronize()
+        del src, dst
     if args.workload in ("P", "L", "T"):
         out = bench_prefill(args, torch, synth, D, DoryRuntime)
     else:
