@@ -109,7 +109,9 @@ def roofline_of(stats, kind):
 
 
 def time_prefill(rt, D, torch, X, tokens, steps, warmup, chunk=None):
-    """Each step: prefill a fresh sequence (in chunks if given), then release it."""
+    """Each step: prefill a fresh sequence (in chunks if given), then release it. The
+    timed steps carry HIP events around the GEMM launches only; one more untimed step
+    records every kernel class for the per-class breakdown."""
     chunk = chunk or tokens
     Y = torch.empty((chunk, X.shape[1]), dtype=torch.float32, device="cuda")
 
@@ -122,14 +124,19 @@ def time_prefill(rt, D, torch, X, tokens, steps, warmup, chunk=None):
     for _ in range(warmup):
         one()
     torch.cuda.synchronize()
-    D.dory_profile_enable(rt.ctx, True)
+    D.dory_profile_enable(rt.ctx, [D.KC_GEMM])
     t0 = time.perf_counter()
     for _ in range(steps):
         one()
     torch.cuda.synchronize()
     t1 = time.perf_counter()
     D.dory_profile_enable(rt.ctx, False)
-    return (t1 - t0) / steps, kernel_stats(rt, D), Y
+    timed = kernel_stats(rt, D)
+    D.dory_profile_enable(rt.ctx, True)
+    one()
+    torch.cuda.synchronize()
+    D.dory_profile_enable(rt.ctx, False)
+    return (t1 - t0) / steps, timed, kernel_stats(rt, D), Y
 
 
 def cpu_baseline_prefill(shape, weights, X, k, mode, rows, y_gpu):
@@ -174,11 +181,11 @@ def bench_prefill(args, torch, synth, D, DoryRuntime):
     for kk in ks:
         D.dory_set_loops(rt.ctx, kk)
         log(f"[bench] k={kk}: warmup {args.warmup}, steps {args.steps}")
-        dt, stats, Y = time_prefill(rt, D, torch, X, tokens, args.steps, args.warmup, chunk)
-        results[kk] = (dt, stats, Y)
+        dt, stats, brk, Y = time_prefill(rt, D, torch, X, tokens, args.steps, args.warmup, chunk)
+        results[kk] = (dt, stats, Y, brk)
         log(f"[bench] k={kk}: {dt * 1e3:.2f} ms/step, {tokens / dt:.0f} tok/s, "
             f"gemm {stats['gemm']['flops'] / stats['gemm']['ms'] / 1e9:.0f} TFLOP/s")
-    dt, stats, Y = results[k]
+    dt, stats, Y, brk = results[k]
     out = {
         "metric": "prefill tokens/s (k=%d)" % k, "value": round(tokens / dt, 1),
         "unit": "tokens/s", "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
@@ -189,8 +196,7 @@ def bench_prefill(args, torch, synth, D, DoryRuntime):
                    "executed_layers": shape["n_in"] + shape["n_out"] + k * shape["n_rec"],
                    "chunk": chunk or tokens},
         "roofline": roofline_of(stats, "mfma"),
-        "kernels": {n: {"launches": s["launches"], "ms_per_step": round(s["ms"] / args.steps, 3)}
-                    for n, s in stats.items()},
+        "kernels": {n: {"launches": s["launches"], "ms": round(s["ms"], 3)} for n, s in brk.items()},
     }
     if len(ks) > 1:
         out["by_loops"] = {str(kk): {"tokens_per_s": round(tokens / r[0], 1),
@@ -238,7 +244,8 @@ def bench_decode(args, torch, synth, D, DoryRuntime):
         for s in range(args.warmup):
             D.dory_decode_step(rt.ctx, ids, X[s * batch:(s + 1) * batch], Y)
         torch.cuda.synchronize()
-        D.dory_profile_enable(rt.ctx, True)
+        # timed steps: HIP events around the attention launches only
+        D.dory_profile_enable(rt.ctx, [D.KC_ATTN])
         t0 = time.perf_counter()
         for s in range(args.warmup, args.warmup + steps):
             D.dory_decode_step(rt.ctx, ids, X[s * batch:(s + 1) * batch], Y)
@@ -247,13 +254,19 @@ def bench_decode(args, torch, synth, D, DoryRuntime):
         D.dory_profile_enable(rt.ctx, False)
         stats = kernel_stats(rt, D)
         kvb = D.dory_kv_bytes_in_use(rt.ctx)
-        results[kk] = (dt, stats, kvb)
+        # one more (untimed) step with every kernel class recorded, for the breakdown
+        D.dory_profile_enable(rt.ctx, True)
+        D.dory_decode_step(rt.ctx, ids, X[:batch], Y)
+        torch.cuda.synchronize()
+        D.dory_profile_enable(rt.ctx, False)
+        brk = kernel_stats(rt, D)
+        results[kk] = (dt, stats, kvb, brk)
         log(f"[bench] k={kk}: {dt * 1e3:.2f} ms/step, {batch / dt:.1f} tok/s")
         rt.close()
         del rt
         torch.cuda.empty_cache()
-    dt, stats, kvb = results[k]
-    tot_bytes = sum(s["bytes"] for s in stats.values()) / steps
+    dt, stats, kvb, brk = results[k]
+    tot_bytes = sum(s["bytes"] for s in brk.values())
     out = {
         "metric": "decode tokens/s (k=%d)" % k, "value": round(batch / dt, 2), "unit": "tokens/s",
         "n_gpus": 1, "steps": steps, "warmup": args.warmup, "ms_per_step": round(dt * 1e3, 3),
@@ -265,8 +278,8 @@ def bench_decode(args, torch, synth, D, DoryRuntime):
         "roofline": roofline_of(stats, "hbm"),
         "step_hbm_gbs": round(tot_bytes / dt / 1e9, 1),
         "kv_bytes_in_use": kvb,
-        "kernels": {n: {"launches": s["launches"], "ms_per_step": round(s["ms"] / steps, 3),
-                        "gb_per_step": round(s["bytes"] / steps / 1e9, 3)} for n, s in stats.items()},
+        "kernels": {n: {"launches": s["launches"], "ms": round(s["ms"], 3),
+                        "gb": round(s["bytes"] / 1e9, 3)} for n, s in brk.items()},
     }
     if len(ks) > 1:
         out["by_loops"] = {str(kk): {"tokens_per_s": round(batch / r[0], 2), "ms_per_step": round(r[0] * 1e3, 3),

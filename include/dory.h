@@ -217,9 +217,13 @@ typedef struct dory_kernel_stats {
   double bytes;     /* algorithmic HBM bytes: GEMM weights (+ scales) + activations in and
                        out; attention K/V entries read (once per row) */
 } dory_kernel_stats;
-/* Start (on != 0: counters cleared) or stop recording. Recording brackets every launch
- * with a pair of HIP events; it adds no device work beyond the event markers. */
-int dory_profile_enable(dory_ctx* ctx, int on);
+#define DORY_KC_ALL ((1 << DORY_KC_COUNT) - 1)
+/* Start recording the classes in class_mask (bit 1 << DORY_KC_*; counters cleared), or
+ * stop (class_mask 0). Recording brackets each launch of a selected class with a pair of
+ * HIP events on the call's stream; it adds no device work beyond the event markers, but
+ * each marker costs some launch latency, so time a step with only the classes needed.
+ * INVALID_ARG for bits outside DORY_KC_ALL. */
+int dory_profile_enable(dory_ctx* ctx, int class_mask);
 /* Totals for one class since enabling (waits for the recorded events). */
 int dory_profile_read(dory_ctx* ctx, int kclass, dory_kernel_stats* out);
 

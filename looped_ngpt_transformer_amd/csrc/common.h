@@ -59,6 +59,46 @@ __device__ __forceinline__ float block_sum(float v, float* red) {
   return t;
 }
 
+// ---------------------------------------------------------------- KV page layout
+// A page holds 64 tokens of one (sequence, layer, slot) stream: for each KV head a K
+// block of 64 x d elements, then for each KV head a V block of d x 64 elements. Both
+// blocks are stored as 8-element chunks in the order the attention MFMAs consume them,
+// so that every 16 x 32 operand fragment is 64 consecutive chunks (1 KiB in bf16):
+//  * K chunk (token t, channels 8 cc .. + 7): half hf = t / 32, u = t % 32, fragment
+//    (kb = (u / 4) % 2, c = cc / 4), lane (lk = cc % 4, lq = 4 (u / 8) + u % 4).
+//    The rows of a 16-key fragment are tokens 8 (lq / 4) + 4 kb + lq % 4, so the S^T
+//    accumulators of lane (lq, lk) cover the 8 consecutive tokens 8 lk .. + 7.
+//  * V chunk (channel ch, tokens 32 hf + 8 lk .. + 7): fragment (hf, cb = ch / 16),
+//    lane (lk, lq = ch % 16), the 8 tokens in order.
+// d must be a multiple of 32. Offsets are in elements within the head's block.
+__device__ __forceinline__ int kv_k_off(int t, int ch, int d) {
+  const int hf = t >> 5, u = t & 31;
+  const int lq = ((u >> 3) << 2) | (u & 3), kb = (u >> 2) & 1;
+  const int cc = ch >> 3;
+  const int chunk = (((hf * 2 + kb) * (d >> 5) + (cc >> 2)) * 4 + (cc & 3)) * 16 + lq;
+  return chunk * 8 + (ch & 7);
+}
+__device__ __forceinline__ int kv_v_off(int t, int ch, int d) {
+  const int hf = t >> 5, u = t & 31;
+  const int chunk = ((hf * (d >> 4) + (ch >> 4)) * 4 + (u >> 3)) * 16 + (ch & 15);
+  return chunk * 8 + (u & 7);
+}
+// Inverses for whole chunks q: K chunk -> (token, first channel); V chunk -> (channel,
+// first token).
+__device__ __forceinline__ void kv_k_chunk(int q, int d, int& t, int& ch) {
+  const int DC = d >> 5;
+  const int lq = q & 15, lk = (q >> 4) & 3, c = (q >> 6) % DC, kb = (q / (64 * DC)) & 1,
+            hf = q / (128 * DC);
+  t = 32 * hf + 8 * (lq >> 2) + 4 * kb + (lq & 3);
+  ch = 8 * (4 * c + lk);
+}
+__device__ __forceinline__ void kv_v_chunk(int q, int d, int& ch, int& t) {
+  const int CB = d >> 4;
+  const int lq = q & 15, lk = (q >> 4) & 3, cb = (q >> 6) % CB, hf = q / (64 * CB);
+  ch = 16 * cb + lq;
+  t = 32 * hf + 8 * lk;
+}
+
 __device__ __forceinline__ float inv_norm(float sumsq) { return 1.0f / fmaxf(sqrtf(sumsq), NORM_EPS); }
 
 // sigmoid gate value for (row m, channel c) from the projection output (bf16 [M, ld]

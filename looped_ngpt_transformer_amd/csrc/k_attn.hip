@@ -10,9 +10,9 @@
 // which the consumer forms the L2 norm before the output projection (arXiv §2).
 //
 // Work-group = (row, KV head, split); its 4 waves are the group's query heads, so
-// each K/V page is read once for all of them. A page tile (64 keys of one KV head:
-// K row-major and V channel-major, each contiguous in the page) is staged in LDS with
-// coalesced 16-byte loads.
+// each K/V page is read once for all of them. A page's K and V blocks of one KV head
+// (each contiguous in the page) are staged in LDS as a row-major K tile and a
+// channel-major V tile.
 #include <algorithm>
 
 #include "common.h"
@@ -31,7 +31,7 @@ __global__ __launch_bounds__(ATT_THREADS) void k_attn_rows(AttnArgs a, int split
   const int d = a.d;
   const int G = a.Hq / a.Hkv;
   T* Ks = (T*)smem;                              // [64][d]
-  T* Vs = Ks + PAGE * d;                         // [d][64] (channel-major, as in the page)
+  T* Vs = Ks + PAGE * d;                         // [d][64] (channel-major)
   float* qs = (float*)(Vs + PAGE * d);           // [G][d]
   float* part = qs + ATT_MAXG * d;               // [4][G][64] partial dots
   float* P = part + 4 * ATT_MAXG * PAGE;         // [G][64] probabilities
@@ -52,7 +52,7 @@ __global__ __launch_bounds__(ATT_THREADS) void k_attn_rows(AttnArgs a, int split
   float m_run = -INFINITY, l_run = 0.f;
   float o[4] = {0.f, 0.f, 0.f, 0.f};  // dims lane + 64 c, c < 4 (d <= 256)
   const int dq = d / 4;               // dims per QK quarter
-  const int chunks = PAGE * d * (int)sizeof(T) / 16;  // 16-byte chunks per K (or V) page
+  const int chunks = PAGE * d / 8;    // 8-element chunks per K (or V) block
   const int32_t* trow = a.kv.table + ((size_t)seq * a.kv.n_streams + a.stream_idx) * a.kv.tab_len;
 
   for (int pg = pa; pg <= pb; ++pg) {
@@ -60,9 +60,14 @@ __global__ __launch_bounds__(ATT_THREADS) void k_attn_rows(AttnArgs a, int split
     const T* kp = (const T*)a.kv.pool + (size_t)page * a.kv.page_elems + (size_t)hk * PAGE * d;
     const T* vp = kp + (size_t)a.Hkv * PAGE * d;
     __syncthreads();  // previous tile fully consumed
-    for (int c = t; c < chunks; c += ATT_THREADS) {
-      ((uint4*)Ks)[c] = ((const uint4*)kp)[c];
-      ((uint4*)Vs)[c] = ((const uint4*)vp)[c];
+    for (int q8 = t; q8 < chunks; q8 += ATT_THREADS) {  // 8-element chunks, page order -> tiles
+      int tok, ch;
+      kv_k_chunk(q8, d, tok, ch);
+#pragma unroll
+      for (int e = 0; e < 8; ++e) Ks[tok * d + ch + e] = kp[q8 * 8 + e];
+      kv_v_chunk(q8, d, ch, tok);
+#pragma unroll
+      for (int e = 0; e < 8; ++e) Vs[ch * PAGE + tok + e] = vp[q8 * 8 + e];
     }
     __syncthreads();
     {  // partial dots: key j = lane, dims [w*dq, (w+1)*dq) for every query head
@@ -191,19 +196,29 @@ __global__ __launch_bounds__(256) void k_attn_combine(AttnArgs a, int splits) {
 // ------------------------------------------------------------- decode attention, MFMA
 // One wave per (row, KV head, sub-split of the row's pages); no LDS and no barriers.
 // The wave streams its pages straight from HBM, 32 keys at a time with the next 32
-// in flight: K rows as MFMA A fragments (16 keys x 32 channels), V^T fragments from the
-// channel-major V half of the page. S^T = K Q^T
-// puts the 4 grouped query heads in the B operand (columns 4..15 are zero), and the
-// probabilities feed O^T += V^T P^T from the S^T accumulators as in the prefill kernel.
-// Keys outside [lo, p] get -inf logits and, on partial pages, zeroed V entries.
-template <int D>
-__global__ __launch_bounds__(256) void k_attn_decode(AttnArgs a, int nsub, int pps) {
+// in flight. S^T = K Q^T puts the 4 grouped query heads in the B operand (columns
+// 4..15 are zero) and O^T += V^T P^T takes P^T from the S^T accumulators. The page
+// stores the rows of a 16-key K fragment in the order 8 (i / 4) + 4 kb + i % 4, so each
+// lane's accumulators hold 8 consecutive keys, which is exactly the lane's part of the
+// matching V^T fragment. Keys outside [lo, p] get -inf logits and, on partial pages,
+// zeroed V entries.
+//
+// The split partials (max in log2 units, sum, unnormalised output per head) go to the
+// workspace; k_decode_merge combines them.
+constexpr int BUF_RSRC_WORD3 = 0x00020000;  // buffer resource flags: raw 32-bit dwords
+
+// NBUF: register sets of K/V fragments per wave (2: the next half-page is in flight
+// while the current one is computed); WPE: waves per SIMD the registers are cut for.
+template <int D, int NBUF, int WPE>
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(WPE))) void k_attn_decode(AttnArgs a, int nsub, int pps) {
   constexpr int G = 4, DC = D / 32, CB = D / 16;
+  constexpr int PSTRIDE = 2 * G + G * D;  // floats per partial: m[G], l[G], o[G][D]
   const int lane = threadIdx.x & 63;
-  const int wid = blockIdx.x * 4 + (threadIdx.x >> 6);
+  // wave-uniform indices in scalar registers: page addresses become scalar bases
+  const int wid = __builtin_amdgcn_readfirstlane(blockIdx.x * 4 + (threadIdx.x >> 6));
   if (wid >= a.M * a.Hkv * nsub) return;
-  const int sub = wid % nsub, mh = wid / nsub;
-  const int hk = mh % a.Hkv, m = mh / a.Hkv;
+  const int sub = wid % nsub, grp = wid / nsub;
+  const int hk = grp % a.Hkv, m = grp / a.Hkv;
   const int lq = lane & 15, lk = lane >> 4;
   const int p = a.pos[m];
   const int seq = a.row_seq[m];
@@ -227,33 +242,38 @@ __global__ __launch_bounds__(256) void k_attn_decode(AttnArgs a, int nsub, int p
 #pragma unroll
   for (int cb = 0; cb < CB; ++cb) o[cb] = f32x4{0.f, 0.f, 0.f, 0.f};
 
-  // Half-pages (32 keys) hp = 2 * page + hf. The fragments of half-page hp + 1 are
-  // loaded into the second register set while hp is computed.
+  // Half-pages (32 keys) hp = 2 * page + hf; lane (lq, lk) owns keys 32 hf + 8 lk .. + 7.
+  // Every fragment is 1 KiB contiguous in the page (fragment-order layout), read with
+  // one 16-byte load per lane through a buffer resource on the page (scalar base,
+  // bounds = the page): the per-lane offset is 16 * lane, the rest scalar.
   struct Half {
-    uint4 k[2][DC];   // K rows 32 hf + 16 kb + lq, channels 32 c + 8 lk .. + 7
-    uint2 v[CB][2];   // V^T channel 16 cb + lq, keys 32 hf + 4 lk (+16) .. + 3
+    uint4 k[2][DC];  // K fragment (kb, c): tokens 8 (lq / 4) + 4 kb + lq % 4, channels 32 c + 8 lk ..
+    uint4 v[CB];     // V^T fragment cb: channel 16 cb + lq, tokens 8 lk .. + 7 of the half
   };
+  const int voff = 16 * lane;
+  const int kofs = hk * PAGE * D * 2;
+  const int vofs = (a.Hkv + hk) * PAGE * D * 2;
+  const int page_bytes = (int)(a.kv.page_elems * 2);
   auto load = [&](int hp, Half& H) {
     const int pg = hp >> 1, hf = hp & 1;
     const int32_t page = trow[pg % a.kv.ring];
-    const bf16_t* kp = pool + (size_t)page * a.kv.page_elems + (size_t)hk * PAGE * D;
-    const bf16_t* vp = pool + (size_t)page * a.kv.page_elems + (size_t)a.Hkv * PAGE * D + (size_t)hk * D * PAGE;
+    const __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc(
+        (void*)(pool + (size_t)page * a.kv.page_elems), 0, page_bytes, BUF_RSRC_WORD3);
 #pragma unroll
     for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
       for (int c = 0; c < DC; ++c)
-        H.k[kb][c] = *(const uint4*)(kp + (size_t)(32 * hf + 16 * kb + lq) * D + 32 * c + 8 * lk);
+        H.k[kb][c] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(
+                         rs, voff, kofs + ((hf * 2 + kb) * DC + c) * 1024, 0));
 #pragma unroll
-    for (int cb = 0; cb < CB; ++cb) {
-      const bf16_t* vr = vp + (size_t)(16 * cb + lq) * PAGE + 32 * hf + 4 * lk;
-      H.v[cb][0] = *(const uint2*)vr;
-      H.v[cb][1] = *(const uint2*)(vr + 16);
-    }
+    for (int cb = 0; cb < CB; ++cb)
+      H.v[cb] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(
+                    rs, voff, vofs + (hf * CB + cb) * 1024, 0));
   };
   auto compute = [&](int hp, const Half& H) {
     const int pg = hp >> 1, hf = hp & 1;
-    const int kbase = pg * PAGE + 32 * hf;
-    const bool whole = kbase >= lo && kbase + 31 <= p;
+    const int kbase = pg * PAGE + 32 * hf + 8 * lk;  // this lane's first key
+    const bool whole = pg * PAGE + 32 * hf >= lo && pg * PAGE + 32 * hf + 31 <= p;
     f32x4 st[2];
 #pragma unroll
     for (int kb = 0; kb < 2; ++kb) {
@@ -262,83 +282,189 @@ __global__ __launch_bounds__(256) void k_attn_decode(AttnArgs a, int nsub, int p
       for (int c = 0; c < DC; ++c)
         st[kb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, H.k[kb][c]), qf[c], st[kb], 0, 0, 0);
     }
-    // S^T[key kbase + 16 kb + 4 lk + r][head lq]: online softmax for head lq
-    float sv[2][4];
+    // st[kb][r] = S^T[key kbase + 4 kb + r][head lq]: online softmax for head lq
+    float sv[8];
     float mt = -INFINITY;
 #pragma unroll
-    for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        const int key = kbase + 16 * kb + 4 * lk + r;
-        const bool vis = key >= lo && key <= p;
-        sv[kb][r] = vis ? st[kb][r] * sl2 : -INFINITY;
-        mt = fmaxf(mt, sv[kb][r]);
-      }
+    for (int e = 0; e < 8; ++e) {
+      const int key = kbase + e;
+      const bool vis = key >= lo && key <= p;
+      sv[e] = vis ? st[e >> 2][e & 3] * sl2 : -INFINITY;
+      mt = fmaxf(mt, sv[e]);
+    }
     mt = fmaxf(mt, __shfl_xor(mt, 16, 64));
     mt = fmaxf(mt, __shfl_xor(mt, 32, 64));
     const float m_new = fmaxf(m_run, mt);
     const float corr = m_run == -INFINITY ? 0.f : exp2f(m_run - m_new);
-    float pe[2][4];
+    float pe[8];
     float ps = 0.f;
 #pragma unroll
-    for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        pe[kb][r] = sv[kb][r] == -INFINITY ? 0.f : exp2f(sv[kb][r] - m_new);
-        ps += pe[kb][r];
-      }
+    for (int e = 0; e < 8; ++e) {
+      pe[e] = sv[e] == -INFINITY ? 0.f : exp2f(sv[e] - m_new);
+      ps += pe[e];
+    }
     ps += __shfl_xor(ps, 16, 64);
     ps += __shfl_xor(ps, 32, 64);
     l_run = l_run * corr + ps;
     m_run = m_new;
     uint32_t u[4];
-    u[0] = (uint32_t)f2bf(pe[0][0]) | ((uint32_t)f2bf(pe[0][1]) << 16);
-    u[1] = (uint32_t)f2bf(pe[0][2]) | ((uint32_t)f2bf(pe[0][3]) << 16);
-    u[2] = (uint32_t)f2bf(pe[1][0]) | ((uint32_t)f2bf(pe[1][1]) << 16);
-    u[3] = (uint32_t)f2bf(pe[1][2]) | ((uint32_t)f2bf(pe[1][3]) << 16);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) u[i] = (uint32_t)f2bf(pe[2 * i]) | ((uint32_t)f2bf(pe[2 * i + 1]) << 16);
     const bf16x8 pf = __builtin_bit_cast(bf16x8, make_uint4(u[0], u[1], u[2], u[3]));
+    if (whole) {
 #pragma unroll
-    for (int cb = 0; cb < CB; ++cb) {
-      uint2 v0 = H.v[cb][0], v1 = H.v[cb][1];
-      if (!whole) {  // zero entries of keys outside [lo, p]
-        uint32_t w4[4] = {v0.x, v0.y, v1.x, v1.y};
-#pragma unroll
-        for (int e = 0; e < 8; ++e) {
-          const int key = kbase + (e < 4 ? 4 * lk + e : 16 + 4 * lk + e - 4);
-          if (key < lo || key > p) w4[e / 2] &= (e & 1) ? 0x0000FFFFu : 0xFFFF0000u;
-        }
-        v0 = make_uint2(w4[0], w4[1]);
-        v1 = make_uint2(w4[2], w4[3]);
+      for (int cb = 0; cb < CB; ++cb) {
+        o[cb] *= corr;
+        o[cb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, H.v[cb]), pf, o[cb], 0, 0, 0);
       }
-      o[cb] *= corr;
-      o[cb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
-          __builtin_bit_cast(bf16x8, make_uint4(v0.x, v0.y, v1.x, v1.y)), pf, o[cb], 0, 0, 0);
+    } else {  // zero V entries of keys outside [lo, p] (may be unwritten)
+      uint32_t vmask[4] = {0xFFFFFFFFu, 0xFFFFFFFFu, 0xFFFFFFFFu, 0xFFFFFFFFu};
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        const int key = kbase + e;
+        if (key < lo || key > p) vmask[e >> 1] &= (e & 1) ? 0x0000FFFFu : 0xFFFF0000u;
+      }
+#pragma unroll
+      for (int cb = 0; cb < CB; ++cb) {
+        const uint4 v = H.v[cb];
+        const uint4 vm = make_uint4(v.x & vmask[0], v.y & vmask[1], v.z & vmask[2], v.w & vmask[3]);
+        o[cb] *= corr;
+        o[cb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, vm), pf, o[cb], 0, 0, 0);
+      }
     }
   };
 
   const int h0 = 2 * pa, h1 = 2 * pb + 1;  // empty when pa > pb
-  if (h0 <= h1) {
-    Half A, B;
-    load(h0, A);
-    for (int hp = h0; hp <= h1; hp += 2) {
-      if (hp + 1 <= h1) load(hp + 1, B);
+  if constexpr (NBUF == 2) {  // next half-page in flight while this one is computed
+    if (h0 <= h1) {
+      Half A, B;
+      load(h0, A);
+      for (int hp = h0; hp <= h1; hp += 2) {
+        if (hp + 1 <= h1) load(hp + 1, B);
+        compute(hp, A);
+        if (hp + 2 <= h1) load(hp + 2, A);
+        if (hp + 1 <= h1) compute(hp + 1, B);
+      }
+    }
+  } else {  // one half-page per wave in flight; latency hidden by resident waves
+    for (int hp = h0; hp <= h1; ++hp) {
+      Half A;
+      load(hp, A);
       compute(hp, A);
-      if (hp + 2 <= h1) load(hp + 2, A);
-      if (hp + 1 <= h1) compute(hp + 1, B);
     }
   }
+
+  // ---- publish this split's partial: O^T[channel 16 cb + 4 lk + r][head lq]
+  float* const gbase = a.part + (size_t)grp * nsub * PSTRIDE;
   if (lq < G) {
-    const int h = hk * G + lq;
-    float* dst = a.part + (((size_t)m * a.Hq + h) * nsub + sub) * (D + 2);
+    float* mine = gbase + (size_t)sub * PSTRIDE;
     if (lk == 0) {
-      dst[0] = m_run;
-      dst[1] = l_run;
+      mine[lq] = m_run;
+      mine[G + lq] = l_run;
     }
 #pragma unroll
-    for (int cb = 0; cb < CB; ++cb)
-#pragma unroll
-      for (int r = 0; r < 4; ++r) dst[2 + 16 * cb + 4 * lk + r] = o[cb][r];
+    for (int cb = 0; cb < CB; ++cb) *(f32x4*)(mine + 2 * G + lq * D + 16 * cb + 4 * lk) = o[cb];
   }
+}
+
+// Merge of the decode splits, sigmoid gate, output and per-head sum of squares. One
+// wave per (row, query head): lane s < nsub weighs split s, then the lanes take channel
+// pairs and accumulate the splits 8 at a time (their loads in flight together; empty
+// splits hold zeros and weigh 0).
+template <int D>
+__global__ __launch_bounds__(64) void k_decode_merge(AttnArgs a, int nsub) {
+  constexpr int G = 4;
+  constexpr int PSTRIDE = 2 * G + G * D;
+  constexpr int NP = D / 2;                 // channel pairs
+  constexpr int PPL = (NP + 63) / 64;       // pairs per lane
+  const int lane = threadIdx.x;
+  const int m = blockIdx.x / a.Hq, h = blockIdx.x % a.Hq;
+  const int hk = h / G, g = h % G;
+  const float* gbase = a.part + (size_t)(m * a.Hkv + hk) * nsub * PSTRIDE;
+  const float ms = lane < nsub ? gbase[(size_t)lane * PSTRIDE + g] : -INFINITY;
+  const float ls = lane < nsub ? gbase[(size_t)lane * PSTRIDE + G + g] : 0.f;
+  const float mx = wave_max(ms);
+  const float wgt = ms == -INFINITY ? 0.f : exp2f(ms - mx);
+  const float L = wave_sum(wgt * ls);
+  const float* ob = gbase + 2 * G + g * D;
+  f32x2 acc[PPL];
+#pragma unroll
+  for (int i = 0; i < PPL; ++i) acc[i] = f32x2{0.f, 0.f};
+  for (int s0 = 0; s0 < nsub; s0 += 8) {
+    f32x2 v[8][PPL];
+    float w[8];
+#pragma unroll
+    for (int u = 0; u < 8; ++u) {
+      const int s = min(s0 + u, nsub - 1);
+      w[u] = s0 + u < nsub ? __shfl(wgt, s, 64) : 0.f;
+#pragma unroll
+      for (int i = 0; i < PPL; ++i) {
+        const int pr = lane + 64 * i;
+        v[u][i] = pr < NP ? *(const f32x2*)(ob + (size_t)s * PSTRIDE + 2 * pr) : f32x2{0.f, 0.f};
+      }
+    }
+#pragma unroll
+    for (int u = 0; u < 8; ++u)
+#pragma unroll
+      for (int i = 0; i < PPL; ++i) acc[i] += w[u] * v[u][i];
+  }
+  const float invL = 1.f / L;
+  bf16_t* out = (bf16_t*)a.o + (size_t)m * a.Hq * D + (size_t)h * D;
+  float sq = 0.f;
+#pragma unroll
+  for (int i = 0; i < PPL; ++i) {
+    const int pr = lane + 64 * i;
+    if (pr >= NP) continue;
+    const int c = 2 * pr;
+    float v0 = acc[i][0] * invL, v1 = acc[i][1] * invL;
+    if (a.g) {
+      v0 *= gate_at(a.g, a.g_f32, a.g_ld, a.g_splits, a.g_sstride, m, h * D + c);
+      v1 *= gate_at(a.g, a.g_f32, a.g_ld, a.g_splits, a.g_sstride, m, h * D + c + 1);
+    }
+    *(uint32_t*)(out + c) = (uint32_t)f2bf(v0) | ((uint32_t)f2bf(v1) << 16);
+    sq += v0 * v0 + v1 * v1;
+  }
+  sq = wave_sum(sq);
+  if (lane == 0) a.ss[(size_t)m * a.Hq + h] = sq;
+}
+
+// One launch of the decode kernel: (row, KV head) groups split over keys so that the
+// waves fill the device once (the resident count comes from the occupancy query); at
+// most max_sub splits per group (the merge weighs one split per lane: <= 64).
+template <int D, int NBUF, int WPE>
+static hipError_t launch_decode(const AttnArgs& a, int n_pages, int max_sub, hipStream_t st) {
+  static int slots = 0;
+  if (!slots) {
+    int dev = 0, cus = 0, blocks = 0;
+    if (hipGetDevice(&dev) != hipSuccess ||
+        hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
+        hipOccupancyMaxActiveBlocksPerMultiprocessor(&blocks, k_attn_decode<D, NBUF, WPE>, 256, 0) != hipSuccess ||
+        cus <= 0 || blocks <= 0)
+      return hipErrorInvalidValue;
+    slots = cus * blocks * 4;
+  }
+  const int groups = a.M * a.Hkv;
+  int nsub = std::max(1, slots / groups);
+  nsub = std::min({nsub, n_pages, max_sub, 64});
+  while (nsub > 1 && (size_t)a.M * a.Hq * nsub * (a.d + 2) > (size_t)a.part_cap) nsub = (nsub + 1) / 2;
+  const int pps = (n_pages + nsub - 1) / nsub;
+  nsub = (n_pages + pps - 1) / pps;
+  const int waves = groups * nsub;
+  hipLaunchKernelGGL((k_attn_decode<D, NBUF, WPE>), dim3((waves + 3) / 4), dim3(256), 0, st, a, nsub, pps);
+  hipLaunchKernelGGL(k_decode_merge<D>, dim3(a.M * a.Hq), dim3(64), 0, st, a, nsub);
+  return hipGetLastError();
+}
+
+// Long key ranges: two register sets per wave, one wave per SIMD, up to 16 splits.
+// Short ranges (sliding windows, short contexts): one register set, three waves per SIMD,
+// a page per split, so that the whole range is requested at once.
+#ifndef DORY_DECODE_SHORT_PAGES
+#define DORY_DECODE_SHORT_PAGES 32
+#endif
+template <int D>
+static hipError_t launch_decode_d(const AttnArgs& a, int n_pages, hipStream_t st) {
+  if (n_pages > DORY_DECODE_SHORT_PAGES) return launch_decode<D, 2, 1>(a, n_pages, 16, st);
+  return launch_decode<D, 1, 3>(a, n_pages, 64, st);
 }
 
 static int attn_pages_max(int max_pos, int window) {
@@ -366,20 +492,11 @@ hipError_t launch_attn_rows(const AttnArgs& a, hipStream_t st) {
   if (a.M == 0) return hipSuccess;
   const int G = a.Hq / a.Hkv;
   if (a.kv.act == ACT_BF16 && G == 4 && (a.d == 64 || a.d == 128 || a.d == 160)) {
-    // MFMA decode kernel: ~4096 waves over (row, KV head, sub-split)
+    // MFMA decode kernel + split merge
     const int n_pages = attn_pages_max(a.max_pos, a.window);
-    int nsub = (4096 + a.M * a.Hkv - 1) / (a.M * a.Hkv);
-    nsub = std::max(1, std::min(nsub, n_pages));
-    while (nsub > 1 && (size_t)a.M * a.Hq * nsub * (a.d + 2) > (size_t)a.part_cap) nsub = (nsub + 1) / 2;
-    const int pps = (n_pages + nsub - 1) / nsub;
-    nsub = (n_pages + pps - 1) / pps;
-    const int waves = a.M * a.Hkv * nsub;
-    const dim3 grid((waves + 3) / 4);
-    if (a.d == 64) hipLaunchKernelGGL(k_attn_decode<64>, grid, dim3(256), 0, st, a, nsub, pps);
-    else if (a.d == 128) hipLaunchKernelGGL(k_attn_decode<128>, grid, dim3(256), 0, st, a, nsub, pps);
-    else hipLaunchKernelGGL(k_attn_decode<160>, grid, dim3(256), 0, st, a, nsub, pps);
-    hipLaunchKernelGGL(k_attn_combine<bf16_t>, dim3((a.M * a.Hq + 3) / 4), dim3(256), 0, st, a, nsub);
-    return hipGetLastError();
+    if (a.d == 64) return launch_decode_d<64>(a, n_pages, st);
+    if (a.d == 128) return launch_decode_d<128>(a, n_pages, st);
+    return launch_decode_d<160>(a, n_pages, st);
   }
   if (G > ATT_MAXG || a.d > ATT_MAXD || a.d % 8 != 0) return hipErrorInvalidValue;
   const int n_pages = attn_pages_max(a.max_pos, a.window);

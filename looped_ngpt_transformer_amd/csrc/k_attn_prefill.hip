@@ -12,9 +12,9 @@
 //   O^T += V^T P^T (A = V^T from LDS, B = P straight from the S^T accumulators: the lane
 //   already holds 2x4 keys of its query, which is a valid k-ordering of the MFMA when
 //   V^T is read with the same key permutation).
-// K is staged row-major (padded rows) and V^T (the page stores V channel-major) into
-// padded LDS rows; the next page is prefetched into registers while the current one is
-// consumed. Entries of the last page beyond the chunk's last position are zeroed, so
+// The page's K and V blocks (8-element chunks in MFMA fragment order) are staged as a
+// row-major K tile and a V^T tile in padded LDS rows; the next page is prefetched into
+// registers while the current one is consumed. Entries of the last page beyond the chunk's last position are zeroed, so
 // unwritten cache memory can never reach the sums.
 #include "common.h"
 #include "kernels.h"
@@ -94,10 +94,14 @@ __global__ __launch_bounds__(PF_THREADS) void k_attn_prefill(AttnArgs a) {
       const bool isv = s >= NCH / 2;
       const int s2 = isv ? s - NCH / 2 : s;
       if (!isv) {  // K chunk: token j, channels 8 ch .. 8 ch + 7
-        const int j = s2 / (D / 8), ch = s2 % (D / 8);
+        int j, c8;
+        kv_k_chunk(s2, D, j, c8);
+        const int ch = c8 >> 3;
         Ks[buf][j * KCH + ch] = (pg * PAGE + j > kmax) ? make_uint4(0, 0, 0, 0) : pre[i];
       } else {     // V^T chunk: channel c, tokens 8 kc .. 8 kc + 7
-        const int c = s2 / 8, kc = s2 % 8;
+        int c, t8;
+        kv_v_chunk(s2, D, c, t8);
+        const int kc = t8 >> 3;
         uint4 v = pre[i];
         const int over = pg * PAGE + 8 * kc + 7 - kmax;  // tokens past the chunk's last
         if (over > 0) {

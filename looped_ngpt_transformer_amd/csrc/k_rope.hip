@@ -16,23 +16,21 @@
 
 namespace dory {
 
-// Page layout (per KV head): K row-major [64 tokens][d], V channel-major [d][64 tokens].
-// kv_k_ptr: the token's K row (d contiguous elements).
+// The page slot of token pos in a (sequence, stream), and its K / V blocks of one head.
 template <typename KV>
-__device__ __forceinline__ KV* kv_k_ptr(const KVLayout& kv, int seq, int stream, int pos, int head) {
+__device__ __forceinline__ KV* kv_page(const KVLayout& kv, int seq, int stream, int pos) {
   const int lp = pos / PAGE;
   const int32_t page =
       kv.table[((size_t)seq * kv.n_streams + stream) * kv.tab_len + (lp % kv.ring)];
-  return (KV*)kv.pool + (size_t)page * kv.page_elems + ((size_t)head * PAGE + (pos % PAGE)) * kv.d;
+  return (KV*)kv.pool + (size_t)page * kv.page_elems;
 }
-// kv_v_ptr: channel 0 of the token's V column; channel j is at [j * 64].
 template <typename KV>
-__device__ __forceinline__ KV* kv_v_ptr(const KVLayout& kv, int seq, int stream, int pos, int head) {
-  const int lp = pos / PAGE;
-  const int32_t page =
-      kv.table[((size_t)seq * kv.n_streams + stream) * kv.tab_len + (lp % kv.ring)];
-  return (KV*)kv.pool + (size_t)page * kv.page_elems + (size_t)kv.Hkv * PAGE * kv.d +
-         (size_t)head * kv.d * PAGE + (pos % PAGE);
+__device__ __forceinline__ KV* kv_kblock(KV* page, const KVLayout& kv, int head) {
+  return page + (size_t)head * PAGE * kv.d;
+}
+template <typename KV>
+__device__ __forceinline__ KV* kv_vblock(KV* page, const KVLayout& kv, int head) {
+  return page + (size_t)(kv.Hkv + head) * PAGE * kv.d;
 }
 
 // grid (M rows, head groups + 1): block y < n_hb rotates heads 4y .. 4y+3 (one per wave,
@@ -99,19 +97,19 @@ __global__ __launch_bounds__(256) void k_rope_kv(RopeArgs a) {
         st<OUT>(qo, o + i, v1);
         st<OUT>(qo, o + i + half, v2);
       } else {
-        OUT* kp = kv_k_ptr<OUT>(a.kv, seq, a.stream_idx, p, h - a.Hq);
-        st<OUT>(kp, i, v1);
-        st<OUT>(kp, i + half, v2);
+        OUT* kb = kv_kblock(kv_page<OUT>(a.kv, seq, a.stream_idx, p), a.kv, h - a.Hq);
+        st<OUT>(kb, kv_k_off(p % PAGE, i, d), v1);
+        st<OUT>(kb, kv_k_off(p % PAGE, i + half, d), v2);
       }
     }
     return;
   }
   // v -> V page (unrotated); the gate stays in the projection output
   const int vcol0 = a.Hq * d + a.Hkv * d;
+  OUT* pgp = kv_page<OUT>(a.kv, seq, a.stream_idx, p);
   for (int c = threadIdx.x; c < a.Hkv * d; c += blockDim.x) {
     const int hk = c / d, j = c % d;
-    OUT* vp = kv_v_ptr<OUT>(a.kv, seq, a.stream_idx, p, hk);
-    st<OUT>(vp, (size_t)j * PAGE, in(vcol0 + c));
+    st<OUT>(kv_vblock(pgp, a.kv, hk), kv_v_off(p % PAGE, j, d), in(vcol0 + c));
   }
 }
 
@@ -148,10 +146,11 @@ __global__ __launch_bounds__(256) void k_fill_kv(KVLayout kv, int seq, int strea
   if (r >= n) return;
   const int p = pos0 + r;
   const int hd = kv.Hkv * kv.d;
+  T* pgp = kv_page<T>(kv, seq, stream, p);
   for (int c = threadIdx.x; c < hd; c += blockDim.x) {
     const int hk = c / kv.d, j = c % kv.d;
-    kv_k_ptr<T>(kv, seq, stream, p, hk)[j] = k[(size_t)r * hd + c];
-    kv_v_ptr<T>(kv, seq, stream, p, hk)[(size_t)j * PAGE] = v[(size_t)r * hd + c];
+    kv_kblock(pgp, kv, hk)[kv_k_off(p % PAGE, j, kv.d)] = k[(size_t)r * hd + c];
+    kv_vblock(pgp, kv, hk)[kv_v_off(p % PAGE, j, kv.d)] = v[(size_t)r * hd + c];
   }
 }
 

@@ -150,7 +150,7 @@ struct dory_ctx {
   int stage_i = 0;
   std::vector<int32_t> scratch;
   // tracing
-  bool prof = false;
+  int prof = 0;  // bit mask of kernel classes being timed
   struct ProfRec { int kc; int ev; double flops, bytes; };
   std::vector<hipEvent_t> pev;
   int pev_used = 0;
@@ -210,12 +210,13 @@ int prof_event(dory_ctx* ctx, hipStream_t st) {
 struct Prof {
   dory_ctx* ctx;
   hipStream_t st;
+  int kc;
   int ev0 = -1;
-  Prof(dory_ctx* c, hipStream_t s) : ctx(c), st(s) {
-    if (ctx->prof) ev0 = prof_event(ctx, st);
+  Prof(dory_ctx* c, hipStream_t s, int k) : ctx(c), st(s), kc(k) {
+    if (ctx->prof & (1 << kc)) ev0 = prof_event(ctx, st);
   }
-  void end(int kc, double flops, double bytes) {
-    if (!ctx->prof || ev0 < 0) return;
+  void end(double flops, double bytes) {
+    if (ev0 < 0) return;
     const int ev1 = prof_event(ctx, st);
     if (ev1 == ev0 + 1) ctx->precs.push_back({kc, ev0, flops, bytes});
   }
@@ -255,7 +256,7 @@ int check_config(const dory_config* c, std::string& msg) {
   // what the kernels of this build run
   const int G = c->n_q_heads / c->n_kv_heads;
   if (G > 4) return uns("more than 4 query heads per KV head");
-  if (c->head_dim % 8 || c->head_dim > 256) return uns("head_dim must be a multiple of 8, <= 256");
+  if (c->head_dim % 32 || c->head_dim > 256) return uns("head_dim must be a multiple of 32, <= 256 (KV page fragments)");
   if (c->hidden > 4096) return uns("hidden > 4096");
   if (c->act_dtype == DORY_DTYPE_BF16) {
     const int Nq = c->n_q_heads * c->head_dim;
@@ -444,11 +445,11 @@ int run_layer(dory_ctx* ctx, hipStream_t st, const CallPlan& P, int l, int slot,
   };
   const double wbytes = wf == W_F32 ? 4.0 : (wf == W_BF16 ? 2.0 : 1.0 + 1.0 / 32);
   auto run_gemm = [&](const GemmArgs& g) -> hipError_t {
-    Prof pr(ctx, st);
+    Prof pr(ctx, st, DORY_KC_GEMM);
     const hipError_t e = launch_gemm(g, st);
     const double outb = g.epi == EPI_STORE_ACT || g.epi == EPI_SWIGLU ? 2.0 : 4.0 * g.splits;
     const double ncols = g.epi == EPI_SWIGLU ? g.n_half : g.N;
-    pr.end(DORY_KC_GEMM, 2.0 * g.M * g.N * (double)g.K,
+    pr.end(2.0 * g.M * g.N * (double)g.K,
            (double)g.N * g.K * wbytes + (double)g.M * g.K * D.esz + (double)g.M * ncols * outb);
     return e;
   };
@@ -467,9 +468,9 @@ int run_layer(dory_ctx* ctx, hipStream_t st, const CallPlan& P, int l, int slot,
     u.H = D.H;
     u.act = act;
     u.bnd = b;
-    Prof pr(ctx, st);
+    Prof pr(ctx, st, DORY_KC_UPDATE);
     const hipError_t e = launch_update(u, st);
-    pr.end(DORY_KC_UPDATE, 0, (double)M * D.H * (4.0 * splits + 4 + 4 + D.esz));
+    pr.end(0, (double)M * D.H * (4.0 * splits + 4 + 4 + D.esz));
     return e;
   };
 
@@ -508,9 +509,9 @@ int run_layer(dory_ctx* ctx, hipStream_t st, const CallPlan& P, int l, int slot,
   ra.kv = kv_layout(ctx, l);
   ra.stream_idx = sidx;
   {
-    Prof pr(ctx, st);
+    Prof pr(ctx, st, DORY_KC_ROPE);
     HIPCHK(launch_rope_kv(ra, st), "rope_kv");
-    pr.end(DORY_KC_ROPE, 0, (double)M * (D.Nqkvg * (ra.in_f32 ? 4.0 * S : D.esz) + (2 * D.Nq + 2 * D.Nkv) * D.esz));
+    pr.end(0, (double)M * (D.Nqkvg * (ra.in_f32 ? 4.0 * S : D.esz) + (2 * D.Nq + 2 * D.Nkv) * D.esz));
   }
 
   AttnArgs aa;
@@ -548,14 +549,14 @@ int run_layer(dory_ctx* ctx, hipStream_t st, const CallPlan& P, int l, int slot,
   {
     double pairs, keys;
     attn_work(P, full, c.window, &pairs, &keys);
-    Prof pr(ctx, st);
+    Prof pr(ctx, st, DORY_KC_ATTN);
     const bool mfma_attn = !f32 && P.max_tile_rows > 1 && D.Hq == 4 * D.Hkv &&
                            (D.d == 64 || D.d == 128 || D.d == 160);
     if (mfma_attn)
       HIPCHK(launch_attn_prefill(aa, st), "attention (prefill)");
     else
       HIPCHK(launch_attn_rows(aa, st), "attention");
-    pr.end(DORY_KC_ATTN, 4.0 * D.Hq * D.d * pairs,
+    pr.end(4.0 * D.Hq * D.d * pairs,
            keys * 2.0 * D.Nkv * D.esz + (double)M * 3 * D.Nq * D.esz);
   }
 
@@ -580,9 +581,9 @@ int run_layer(dory_ctx* ctx, hipStream_t st, const CallPlan& P, int l, int slot,
     S = f32 ? 1 : gemm_pick_splits(M, 2 * D.I, D.H, wf);
     HIPCHK(run_gemm(gemm(ws + W.sb, D.H, w.w_gu, w.s_gu, 2 * D.I, f32 ? EPI_F32 : EPI_PARTIAL, part, 2 * D.I, S)), "gemm gu");
     {
-      Prof pr(ctx, st);
+      Prof pr(ctx, st, DORY_KC_SWIGLU);
       HIPCHK(launch_swiglu(part, S, M, D.I, ws + W.h, act, ss_h, D.ss_h_n, st), "swiglu");
-      pr.end(DORY_KC_SWIGLU, 0, (double)M * (2.0 * D.I * 4 * S + D.I * D.esz));
+      pr.end(0, (double)M * (2.0 * D.I * 4 * S + D.I * D.esz));
     }
     S = f32 ? 1 : gemm_pick_splits(M, D.H, D.I, wf);
     HIPCHK(run_gemm(gemm(ws + W.h, D.I, w.w_down, w.s_down, D.H, f32 ? EPI_F32 : EPI_PARTIAL, part, D.H, S)), "gemm down");
@@ -607,10 +608,10 @@ int run_forward(dory_ctx* ctx, hipStream_t st, const CallPlan& P, const float* x
   char* ws = ctx->ws;
   const int act = c.act_dtype == DORY_DTYPE_F32 ? ACT_F32 : ACT_BF16;
   {
-    Prof pr(ctx, st);
+    Prof pr(ctx, st, DORY_KC_UPDATE);
     HIPCHK(launch_stage_input(x_in, (float*)(ws + ctx->W.s), ws + ctx->W.sb, P.M, ctx->D.H, act, st),
            "stage_input");
-    pr.end(DORY_KC_UPDATE, 0, (double)P.M * ctx->D.H * (8.0 + ctx->D.esz));
+    pr.end(0, (double)P.M * ctx->D.H * (8.0 + ctx->D.esz));
   }
   int64_t calls = 0;
   int r;
@@ -1030,14 +1031,14 @@ int dory_quantize_mxfp8(void* stream, const void* w, int w_dtype, int64_t rows, 
   return DORY_OK;
 }
 
-int dory_profile_enable(dory_ctx* ctx, int on) {
-  if (!ctx) return DORY_ERR_INVALID_ARG;
-  if (on) {
+int dory_profile_enable(dory_ctx* ctx, int class_mask) {
+  if (!ctx || class_mask < 0 || class_mask >= (1 << DORY_KC_COUNT)) return DORY_ERR_INVALID_ARG;
+  if (class_mask) {
     for (int i = 0; i < ctx->pev_used; ++i) (void)hipEventSynchronize(ctx->pev[i]);
     ctx->precs.clear();
     ctx->pev_used = 0;
   }
-  ctx->prof = on != 0;
+  ctx->prof = class_mask;
   return DORY_OK;
 }
 

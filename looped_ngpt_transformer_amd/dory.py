@@ -264,8 +264,17 @@ def dory_sync(ctx=None, stream=None):
     _check(lib().dory_sync(ctx, _stream(stream)), ctx)
 
 
-def dory_profile_enable(ctx, on: bool):
-    _check(lib().dory_profile_enable(ctx, 1 if on else 0), ctx)
+def dory_profile_enable(ctx, classes):
+    """classes: True (all), False/None (stop), or an iterable of KC_* class ids."""
+    if classes is True:
+        mask = (1 << len(KC_NAMES)) - 1
+    elif not classes:
+        mask = 0
+    else:
+        mask = 0
+        for k in classes:
+            mask |= 1 << k
+    _check(lib().dory_profile_enable(ctx, mask), ctx)
 
 
 def dory_profile_read(ctx, kclass: int) -> dict:

@@ -57,7 +57,7 @@ def test_create_validation():
                              ("head_dim", 63, D.ERR_INVALID_ARG), ("n_rec", 0, D.ERR_INVALID_ARG),
                              ("max_loops", 9, D.ERR_INVALID_ARG), ("max_seq_len", 262145, D.ERR_INVALID_ARG),
                              ("weight_format", D.WFMT_BF16, D.ERR_INVALID_ARG),
-                             ("head_dim", 264, D.ERR_UNSUPPORTED)]:
+                             ("head_dim", 264, D.ERR_UNSUPPORTED), ("head_dim", 48, D.ERR_UNSUPPORTED)]:
         c = cfg()
         setattr(c, field, val)
         with pytest.raises(D.DoryError) as e:

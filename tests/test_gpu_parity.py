@@ -21,8 +21,21 @@ def xin(shape, n, seed, stream=0):
     return synth.make_inputs(n, shape["hidden"], seed, stream, device="cuda")
 
 
-def _run_case(shape, k, mode, schedule, max_rows=256, max_seq_len=512, max_seqs=4, wseed=7):
+def sharpen(w, a_attn=1.0, a_mlp=0.5):
+    """Rates that let each sublayer's output through undamped: with a = 1 the state after
+    an attention sublayer is N(its output), so attention errors reach the final states
+    at full size instead of scaled by 0.05."""
+    for lw in w:
+        lw["alpha_attn"].fill_(a_attn)
+        lw["alpha_mlp"].fill_(a_mlp)
+    return w
+
+
+def _run_case(shape, k, mode, schedule, max_rows=256, max_seq_len=512, max_seqs=4, wseed=7,
+              sharp=False):
     w = gpu_weights(shape, wseed)
+    if sharp:
+        sharpen(w)
     rt = DoryRuntime(shape, w, max_loops=4, max_seqs=max_seqs, max_seq_len=max_seq_len,
                      max_rows=max_rows, mode=mode, loops=k)
     got = run_schedule(rt, schedule)
@@ -69,6 +82,25 @@ def test_bf16_small_prefill_then_decode(k, mode):
              ("decode", [(1, xin(S, 1, 15)), (0, xin(S, 1, 16))]),
              ("prefill", [(1, xin(S, 140, 17))])]
     _run_case(S, k, mode, sched, max_rows=256, max_seq_len=512, max_seqs=2)
+
+
+@pytest.mark.parametrize("mode", ["per_loop", "last_loop"])
+def test_bf16_small_sharp_rates(mode):
+    """As above with a_attn = 1, a_mlp = 0.5 (attention and MLP outputs undamped)."""
+    S = PSMALL
+    sched = [("prefill", [(0, xin(S, 150, 71))]),
+             ("decode", [(0, xin(S, 1, 72))]),
+             ("prefill", [(0, xin(S, 90, 73)), (1, xin(S, 20, 74))]),
+             ("decode", [(1, xin(S, 1, 75)), (0, xin(S, 1, 76))])]
+    _run_case(S, 2, mode, sched, max_rows=256, max_seq_len=512, max_seqs=2, sharp=True)
+
+
+def test_tiny_fp32_sharp_rates():
+    T = synth.config("T")
+    sched = [("prefill", [(0, xin(T, 50, 81))])]
+    for s in range(6):
+        sched.append(("decode", [(0, xin(T, 1, 82, stream=s))]))
+    _run_case(T, 2, "per_loop", sched, max_rows=64, max_seq_len=128, max_seqs=1, sharp=True)
 
 
 def test_bf16_k4_last_loop():
@@ -143,15 +175,19 @@ def _seed_kv(rt, shape, seqs, k, mode, seed=9):
     return stores
 
 
+@pytest.mark.parametrize("sharp", [False, True])
 @pytest.mark.parametrize("mode", ["per_loop", "last_loop"])
-def test_bf16_decode_over_seeded_context(mode):
+def test_bf16_decode_over_seeded_context(mode, sharp):
     """Decode steps of two sequences over seeded 1500- and 900-token contexts: many KV
-    pages per row (split over waves), partial pages and sliding-window rings."""
+    pages per row (split over waves and merged), partial pages and sliding-window rings;
+    also with undamped rates so the split merge is checked at full size."""
     from oracle import dory_oracle as O
     from tests.helpers import to_np
     S = PSMALL
     k = 2
     w = gpu_weights(S, 8)
+    if sharp:
+        sharpen(w)
     rt = DoryRuntime(S, w, max_loops=2, max_seqs=2, max_seq_len=1600, max_rows=256, mode=mode, loops=k)
     stores = _seed_kv(rt, S, {0: 1500, 1: 900}, k, mode)
     cfg, W = oracle_model(S, w)
