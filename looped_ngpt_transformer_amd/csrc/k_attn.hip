@@ -5,9 +5,9 @@
 // output is softmax_j(scale * q.k_j) weighted sum of v_j ("Dory1.0-4B": GQA with 16
 // query / 4 KV heads, 3:1 sliding (W = 1024) / full attention — paper summary
 // "technical novelty", MXFP8 article "hybrid attention").
-// The combine step merges the per-split softmax partials, applies the sigmoid output
-// gate elementwise and writes the per-head sum of squares of the gated output, from
-// which the consumer forms the L2 norm before the output projection (arXiv §2).
+// The combine step merges the per-split softmax partials and applies the sigmoid
+// output gate elementwise. (The L2 norm before the output projection, arXiv §2, only
+// scales the row, which the nGPT update's N(.) removes.)
 //
 // Work-group = (row, KV head, split); its 4 waves are the group's query heads, so
 // each K/V page is read once for all of them. A page's K and V blocks of one KV head
@@ -135,7 +135,7 @@ __global__ __launch_bounds__(ATT_THREADS) void k_attn_rows(AttnArgs a, int split
   }
 }
 
-// Merge splits, apply the sigmoid gate, write o (act) and per-head sum of squares.
+// Merge splits, apply the sigmoid gate, write o (act).
 // One wave per (row, head): lane s < splits holds split s's weight exp(m_s - max) and
 // l_s; the weights reach the other lanes by shuffles while each lane merges its channels.
 template <typename T>
@@ -177,7 +177,6 @@ __global__ __launch_bounds__(256) void k_attn_combine(AttnArgs a, int splits) {
     }
   }
   const float invL = 1.f / L;
-  float sq = 0.f;
 #pragma unroll
   for (int c = 0; c < 4; ++c) {
     const int i = lane + 64 * c;
@@ -186,11 +185,8 @@ __global__ __launch_bounds__(256) void k_attn_combine(AttnArgs a, int splits) {
       const size_t e = (size_t)m * a.Hq * d + (size_t)h * d + i;
       if (a.g) ov *= gate_at(a.g, a.g_f32, a.g_ld, a.g_splits, a.g_sstride, m, h * d + i);
       st<T>((T*)a.o, e, ov);
-      sq += ov * ov;
     }
   }
-  sq = wave_sum(sq);
-  if (lane == 0) a.ss[(size_t)m * a.Hq + h] = sq;
 }
 
 // ------------------------------------------------------------- decode attention, MFMA
@@ -367,7 +363,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(WPE))) void
   }
 }
 
-// Merge of the decode splits, sigmoid gate, output and per-head sum of squares. One
+// Merge of the decode splits, sigmoid gate and output. One
 // wave per (row, query head): lane s < nsub weighs split s, then the lanes take channel
 // pairs and accumulate the splits 8 at a time (their loads in flight together; empty
 // splits hold zeros and weigh 0).
@@ -410,7 +406,6 @@ __global__ __launch_bounds__(64) void k_decode_merge(AttnArgs a, int nsub) {
   }
   const float invL = 1.f / L;
   bf16_t* out = (bf16_t*)a.o + (size_t)m * a.Hq * D + (size_t)h * D;
-  float sq = 0.f;
 #pragma unroll
   for (int i = 0; i < PPL; ++i) {
     const int pr = lane + 64 * i;
@@ -422,10 +417,7 @@ __global__ __launch_bounds__(64) void k_decode_merge(AttnArgs a, int nsub) {
       v1 *= gate_at(a.g, a.g_f32, a.g_ld, a.g_splits, a.g_sstride, m, h * D + c + 1);
     }
     *(uint32_t*)(out + c) = (uint32_t)f2bf(v0) | ((uint32_t)f2bf(v1) << 16);
-    sq += v0 * v0 + v1 * v1;
   }
-  sq = wave_sum(sq);
-  if (lane == 0) a.ss[(size_t)m * a.Hq + h] = sq;
 }
 
 // One launch of the decode kernel: (row, KV head) groups split over keys so that the

@@ -1,9 +1,9 @@
 // Prefill attention on bf16 with MFMA (flash-style online softmax over KV pages).
 //
 // Same maths as the row kernel: GQA (4 query heads per KV head), causal, sliding
-// window W on sliding layers, softmax(scale * q.k) v, then the sigmoid output gate and
-// the per-head sum of squares for the pre-projection norm ("Dory1.0-4B": paper summary
-// "technical novelty"; arXiv §2; MXFP8 article "hybrid attention").
+// window W on sliding layers, softmax(scale * q.k) v, then the sigmoid output gate
+// ("Dory1.0-4B": paper summary "technical novelty"; arXiv §2; MXFP8 article "hybrid
+// attention").
 //
 // Work-group = (tile of <= 64 consecutive query rows of one sequence, KV head): 16
 // waves, wave = (query head g of the group, 16-row quarter of the tile). Per KV page:
@@ -215,14 +215,13 @@ __global__ __launch_bounds__(PF_THREADS) void k_attn_prefill(AttnArgs a) {
     __syncthreads();
   }
 
-  // epilogue: normalise, gate, store, per-head sum of squares
+  // epilogue: normalise, gate, store
 #pragma unroll
   for (int qb = 0; qb < 1; ++qb) {
     const int i = 16 * qq + lq;
     const bool qv = i < nrows;
     const float invl = qv ? 1.f / l_run[qb] : 0.f;
     const size_t base = (size_t)(row0 + (qv ? i : 0)) * HqD + (size_t)h * D;
-    float sq = 0.f;
 #pragma unroll
     for (int cb = 0; cb < CB; ++cb) {
       const int c = 16 * cb + 4 * lk;
@@ -239,13 +238,8 @@ __global__ __launch_bounds__(PF_THREADS) void k_attn_prefill(AttnArgs a) {
         ov.x = (uint32_t)f2bf(v[0]) | ((uint32_t)f2bf(v[1]) << 16);
         ov.y = (uint32_t)f2bf(v[2]) | ((uint32_t)f2bf(v[3]) << 16);
         *(uint2*)((bf16_t*)a.o + base + c) = ov;
-#pragma unroll
-        for (int r = 0; r < 4; ++r) sq += v[r] * v[r];
       }
     }
-    sq += __shfl_xor(sq, 16, 64);
-    sq += __shfl_xor(sq, 32, 64);
-    if (qv && lk == 0) a.ss[(size_t)(row0 + i) * a.Hq + h] = sq;
   }
 }
 

@@ -8,9 +8,10 @@
 // MXFP8 weights (E4M3 + one E8M0 scale per 32 along K, W8A16: arXiv §5, MXFP8 article)
 // are dequantised to bf16 exactly while staged into LDS, so the MFMAs are bf16 x bf16
 // with fp32 accumulation.
-// Epilogues fuse what follows each projection: bf16 store; fp32 store scaled by the
-// pre-projection row norm; SwiGLU with the sum of squares the down projection's norm
-// needs; or fp32 split-K partials for small-M (decode) shapes.
+// Epilogues fuse what follows each projection: bf16 store; fp32 store; SwiGLU; or fp32
+// split-K partials for small-M (decode) shapes. The L2 norms before the output and down
+// projections only scale a row, and the nGPT update normalises the projection's output,
+// so they need no work here.
 #include "common.h"
 #include "kernels.h"
 
@@ -37,8 +38,7 @@ __device__ __forceinline__ void dq4(uint32_t word, float sc, uint32_t* out) {
 // Epilogue: lane holds C[m = i*16 + 4*(lane>>4) + r][n = j*16 + (lane&15)] of its wave tile.
 template <int BM, int BN, int WMW, int WNW, int EPI>
 __device__ __forceinline__ void gemm_epilogue(const GemmArgs& g, f32x4 (&acc)[BM / WMW / 16][BN / WNW / 16],
-                                              int n_tile, int m0, int split, int wm, int wn, int lane,
-                                              const float* rowscale) {
+                                              int n_tile, int m0, int split, int wm, int wn, int lane) {
   constexpr int TM = BM / WMW, TN = BN / WNW;
   constexpr int FM = TM / 16, FN = TN / 16;
   const int mrow0 = m0 + wm * TM + 4 * (lane >> 4);
@@ -46,23 +46,17 @@ __device__ __forceinline__ void gemm_epilogue(const GemmArgs& g, f32x4 (&acc)[BM
     constexpr int TNh = TN / 2;
     bf16_t* H = (bf16_t*)g.C;
     const int c0 = n_tile * (BN / 2) + wn * TNh + (lane & 15);
-    const int part = n_tile * WNW + wn;
 #pragma unroll
     for (int i = 0; i < FM; ++i) {
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
         const int m = mrow0 + i * 16 + r;
-        float sq = 0.f;
+        if (m >= g.M) continue;
 #pragma unroll
         for (int j = 0; j < FN / 2; ++j) {
           const float gt = acc[i][j][r], up = acc[i][j + FN / 2][r];
-          const float hv = gt / (1.f + __expf(-gt)) * up;
-          if (m < g.M) H[(size_t)m * g.ldc + c0 + j * 16] = f2bf(hv);
-          sq += hv * hv;
+          H[(size_t)m * g.ldc + c0 + j * 16] = f2bf(gt / (1.f + __expf(-gt)) * up);
         }
-#pragma unroll
-        for (int msk = 1; msk < 16; msk <<= 1) sq += __shfl_xor(sq, msk, 64);
-        if ((lane & 15) == 0 && m < g.M) g.ss_out[(size_t)m * g.ss_n + part] = sq;
       }
     }
     return;
@@ -80,30 +74,12 @@ __device__ __forceinline__ void gemm_epilogue(const GemmArgs& g, f32x4 (&acc)[BM
         const float v = acc[i][j][r];
         if (EPI == EPI_STORE_ACT) {
           ((bf16_t*)g.C)[(size_t)m * g.ldc + n] = f2bf(v);
-        } else if (EPI == EPI_F32_ROWSCALE) {
-          ((float*)g.C)[(size_t)m * g.ldc + n] = v * rowscale[m - m0];
         } else {  // EPI_PARTIAL / EPI_F32
           ((float*)g.C)[(size_t)split * g.M * g.ldc + (size_t)m * g.ldc + n] = v;
         }
       }
     }
   }
-}
-
-// Row scales 1/||row|| of the tile's BM rows from the producer's sum-of-squares
-// partials: the [BM, rs_n] block is contiguous, read coalesced and summed per row with
-// LDS atomics. Ends with a barrier.
-template <int BM>
-__device__ __forceinline__ void load_rowscale(const GemmArgs& g, int m0, float* rowscale) {
-  for (int r = threadIdx.x; r < BM; r += GT) rowscale[r] = 0.f;
-  __syncthreads();
-  const int rows = min(BM, g.M - m0);
-  const int n = rows * g.rs_n;
-  const float* src = g.rs_ss + (size_t)m0 * g.rs_n;
-  for (int e = threadIdx.x; e < n; e += GT) atomicAdd(&rowscale[e / g.rs_n], src[e]);
-  __syncthreads();
-  for (int r = threadIdx.x; r < BM; r += GT) rowscale[r] = inv_norm(rowscale[r]);
-  __syncthreads();
 }
 
 // XCD-aware tile order. Work-groups are dispatched round-robin over the 8 XCDs (each
@@ -133,7 +109,6 @@ __global__ __launch_bounds__(GT) void k_gemm_mfma(GemmArgs g) {
 
   __shared__ __align__(16) uint4 As[2][BM * 8];  // double-buffered K-tiles
   __shared__ __align__(16) uint4 Bs[2][BN * 8];
-  __shared__ float rowscale[EPI == EPI_F32_ROWSCALE ? BM : 1];
 
   const int t = threadIdx.x, lane = t & 63, wave = t >> 6;
   const int wm = wave / WNW, wn = wave % WNW;
@@ -211,7 +186,6 @@ __global__ __launch_bounds__(GT) void k_gemm_mfma(GemmArgs g) {
     }
   };
 
-  if (EPI == EPI_F32_ROWSCALE) load_rowscale<BM>(g, m0, rowscale);
 
   f32x4 acc[FM][FN];
 #pragma unroll
@@ -258,7 +232,7 @@ __global__ __launch_bounds__(GT) void k_gemm_mfma(GemmArgs g) {
     __syncthreads();
   }
 
-  gemm_epilogue<BM, BN, WMW, WNW, EPI>(g, acc, n_tile, m0, split, wm, wn, lane, rowscale);
+  gemm_epilogue<BM, BN, WMW, WNW, EPI>(g, acc, n_tile, m0, split, wm, wn, lane);
 }
 
 // ------------------------------------------------------- bf16 GEMM, direct-to-LDS pipeline
@@ -306,7 +280,6 @@ __global__ __launch_bounds__(GT) void k_gemm_pipe(GemmArgs g) {
   static_assert(STAGES >= 2, "at least double buffering");
 
   __shared__ __align__(16) uint4 sm[STAGES][ACH + BCH];
-  __shared__ float rowscale[EPI == EPI_F32_ROWSCALE ? BM : 1];
 
   const int t = threadIdx.x, lane = t & 63, wave = t >> 6;
   const int wm = wave / WNW, wn = wave % WNW;
@@ -349,7 +322,6 @@ __global__ __launch_bounds__(GT) void k_gemm_pipe(GemmArgs g) {
     }
   };
 
-  if (EPI == EPI_F32_ROWSCALE) load_rowscale<BM>(g, m0, rowscale);
 
   f32x4 acc[FM][FN];
 #pragma unroll
@@ -393,7 +365,7 @@ __global__ __launch_bounds__(GT) void k_gemm_pipe(GemmArgs g) {
           acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(af[i], bfr[j], acc[i][j], 0, 0, 0);
     }
   }
-  gemm_epilogue<BM, BN, WMW, WNW, EPI>(g, acc, n_tile, m0, split, wm, wn, lane, rowscale);
+  gemm_epilogue<BM, BN, WMW, WNW, EPI>(g, acc, n_tile, m0, split, wm, wn, lane);
 }
 
 // ------------------------------------------------------------------ fp32 GEMM (T)
@@ -439,24 +411,24 @@ __global__ __launch_bounds__(256) void k_gemm_f32(GemmArgs g) {
 }
 
 // ------------------------------------------------------------------------ dispatch
+#ifndef DORY_SPLITK_WG
+#define DORY_SPLITK_WG 400
+#endif
+#ifndef DORY_SPLITK_MINK
+#define DORY_SPLITK_MINK 128
+#endif
 int gemm_pick_splits(int M, int N, int K, int wfmt) {
-  // small-M (decode) tiles are BN = 64 wide; split K until there are >= 400 work-groups
-  // (each split a multiple of 64 and at least 128 long)
+  // small-M (decode) tiles are BN = 64 wide; split K until there are enough work-groups
+  // to keep the weight stream in flight (each split a multiple of 64, not too short)
   const int tiles = (N / 64) * ((M + 127) / 128);
   int s = 1;
-  while (s < 16 && tiles * s < 400 && (K / BK) % (2 * s) == 0 && K / (2 * s) >= 2 * BK) s *= 2;
+  while (s < 32 && tiles * s < DORY_SPLITK_WG && (K / BK) % (2 * s) == 0 && K / (2 * s) >= DORY_SPLITK_MINK) s *= 2;
   return s;
 }
 
 // SwiGLU epilogue tiles: bf16 weights use 256x256 tiles (128 h columns, 2 waves along N)
 // when n_half allows, otherwise (and for MXFP8) 128x128 tiles (64 h columns).
 static bool swiglu_big(int n_half, int wfmt) { return wfmt == W_BF16 && n_half % 128 == 0; }
-
-int gemm_swiglu_parts(int n_half, int wfmt) {
-  return swiglu_big(n_half, wfmt) ? (n_half / 128) * 2 : (n_half / 64) * 2;
-}
-
-int gemm_swiglu_ss_parts(const GemmArgs& g) { return gemm_swiglu_parts(g.n_half, g.wfmt); }
 
 template <int BM, int BN, int WMW, int WNW, int EPI, int STAGES, int PBK = 32>
 static hipError_t go_pipe(const GemmArgs& g, hipStream_t st, int ntiles_n) {
@@ -503,15 +475,14 @@ hipError_t launch_gemm(const GemmArgs& gin, hipStream_t st) {
       if (bf && g.N % 160 == 0) return go_pipe<256, 160, 2, 2, EPI_STORE_ACT, 2, 64>(g, st, g.N / 160);
       if (g.N % 128) return hipErrorInvalidValue;
       return go<128, 128, 2, 2, EPI_STORE_ACT>(g, st, g.N / 128);
-    case EPI_F32_ROWSCALE:
+    case EPI_F32:  // large M: fp32 output for the nGPT update
       if (g.splits != 1) return hipErrorInvalidValue;
-      if (bf && g.N % 160 == 0) return go_pipe<256, 160, 2, 2, EPI_F32_ROWSCALE, 2, 64>(g, st, g.N / 160);
-      if (bf && g.N % 256 == 0) return go_pipe<256, 256, 2, 2, EPI_F32_ROWSCALE, 2, 64>(g, st, g.N / 256);
+      if (bf && g.N % 160 == 0) return go_pipe<256, 160, 2, 2, EPI_F32, 2, 64>(g, st, g.N / 160);
+      if (bf && g.N % 256 == 0) return go_pipe<256, 256, 2, 2, EPI_F32, 2, 64>(g, st, g.N / 256);
       if (g.N % 128) return hipErrorInvalidValue;
-      return go<128, 128, 2, 2, EPI_F32_ROWSCALE>(g, st, g.N / 128);
+      return go<128, 128, 2, 2, EPI_F32>(g, st, g.N / 128);
     case EPI_SWIGLU:
       if (g.n_half % 64 || g.splits != 1) return hipErrorInvalidValue;
-      g.ss_n = gemm_swiglu_ss_parts(g);
       if (swiglu_big(g.n_half, g.wfmt)) return go_pipe<256, 256, 2, 2, EPI_SWIGLU, 2, 64>(g, st, g.n_half / 128);
       return go<128, 128, 2, 2, EPI_SWIGLU>(g, st, g.n_half / 64);
     default:

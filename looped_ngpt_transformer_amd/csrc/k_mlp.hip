@@ -7,19 +7,14 @@
 namespace dory {
 
 // h = SiLU(gate) * up ("Dory1.0-4B" paper summary: SwiGLU MLP), from float partials
-// [splits][M][2I] (gate columns [0, I), up columns [I, 2I)). Also writes the row's
-// sum of squares of h in ss_n partials (the L2 norm before the down projection,
-// arXiv §2, is applied by the consumer as a row scale).
-// grid (M, blocks per row): block b of a row covers columns [b*1024, (b+1)*1024) and
-// writes its sum of squares to ss[m][b]; block 0 also clears ss[m][nb .. ss_n).
+// [splits][M][2I] (gate columns [0, I), up columns [I, 2I)). The L2 norm before the down
+// projection (arXiv §2) only scales the row, which the nGPT update's N(.) removes.
+// grid (M, blocks per row): block b of a row covers columns [b*1024, (b+1)*1024).
 template <typename T>
-__global__ __launch_bounds__(256) void k_swiglu(const float* gu, int splits, int M, int I,
-                                                T* h, float* ss, int ss_n) {
-  __shared__ float red[4];
-  const int m = blockIdx.x, b = blockIdx.y, nb = gridDim.y;
+__global__ __launch_bounds__(256) void k_swiglu(const float* gu, int splits, int M, int I, T* h) {
+  const int m = blockIdx.x, b = blockIdx.y;
   const size_t sstride = (size_t)M * 2 * I;
   const size_t row = (size_t)m * 2 * I;
-  float sq = 0.f;
   const int i1 = min(I, (b + 1) * 1024);
   for (int i = b * 1024 + threadIdx.x; i < i1; i += blockDim.x) {
     float g = 0.f, u = 0.f;
@@ -27,26 +22,18 @@ __global__ __launch_bounds__(256) void k_swiglu(const float* gu, int splits, int
       g += gu[s * sstride + row + i];
       u += gu[s * sstride + row + I + i];
     }
-    const float v = g / (1.f + __expf(-g)) * u;
-    st<T>(h, (size_t)m * I + i, v);
-    sq += v * v;
+    st<T>(h, (size_t)m * I + i, g / (1.f + __expf(-g)) * u);
   }
-  sq = block_sum<4>(sq, red);
-  if (threadIdx.x == 0) ss[(size_t)m * ss_n + b] = sq;
-  if (b == 0)
-    for (int j = nb + threadIdx.x; j < ss_n; j += blockDim.x) ss[(size_t)m * ss_n + j] = 0.f;
 }
 
 hipError_t launch_swiglu(const float* gu, int splits, int M, int I, void* h, int act,
-                         float* ss, int ss_n, hipStream_t st) {
+                         hipStream_t st) {
   if (M == 0) return hipSuccess;
-  const int nb = std::min((I + 1023) / 1024, ss_n);
-  if (nb < 1 || (I + 1023) / 1024 > ss_n) return hipErrorInvalidValue;
-  const dim3 grid(M, nb);
+  const dim3 grid(M, (I + 1023) / 1024);
   if (act == ACT_F32)
-    hipLaunchKernelGGL(k_swiglu<float>, grid, dim3(256), 0, st, gu, splits, M, I, (float*)h, ss, ss_n);
+    hipLaunchKernelGGL(k_swiglu<float>, grid, dim3(256), 0, st, gu, splits, M, I, (float*)h);
   else
-    hipLaunchKernelGGL(k_swiglu<bf16_t>, grid, dim3(256), 0, st, gu, splits, M, I, (bf16_t*)h, ss, ss_n);
+    hipLaunchKernelGGL(k_swiglu<bf16_t>, grid, dim3(256), 0, st, gu, splits, M, I, (bf16_t*)h);
   return hipGetLastError();
 }
 

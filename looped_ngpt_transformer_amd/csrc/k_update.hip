@@ -3,15 +3,14 @@
 // s <- N((1 - a) * s + a * N(y))  — the nGPT update ("Dory1.0-4B" paper summary,
 // nGPT prerequisite; arXiv summary §2: normalised sublayer output blended with the
 // normalised residual by per-channel rates, then normalised). y arrives as split-K
-// partial sums and, when the producer did not apply it, with the pre-projection
-// L2 norm still to apply as a row scale (arXiv §2: L2 norm of the gated attention
-// output / SwiGLU activation before the output projection).
+// partial sums. The L2 norm the pages put before the output and down projections (arXiv
+// §2) scales y's row by a positive factor, which N(y) removes, so it needs no work.
 // Loop boundaries (paper summary, core-method equation): at the end of the input block
 // x is saved and u_1 = N(x + x); at the end of loop t, s_t = N(.) and, unless t = k,
 // u_{t+1} = N(s_t + x).
 //
-// Each row's 2560-wide reductions are wave shuffles plus one LDS exchange across the
-// block's 4 waves; the row stays in registers between the reductions.
+// All of the row's loads (partials, state, rates, x) are issued first; the 2560-wide
+// reductions are wave shuffles plus one LDS exchange, the row stays in registers.
 #include "common.h"
 #include "kernels.h"
 
@@ -26,21 +25,19 @@ __global__ __launch_bounds__(UPD_THREADS) void k_update(UpdateArgs u) {
   const int m = blockIdx.x;
   const int H = u.H;
   const size_t row = (size_t)m * H;
-  float v[UPD_MAXPER];
-  float rs = 1.f;
-  if (u.rs_ss) {  // row scale 1/||row|| from the producer's sum-of-squares partials
-    float t = 0.f;
-    for (int j = threadIdx.x; j < u.rs_n; j += UPD_THREADS) t += u.rs_ss[(size_t)m * u.rs_n + j];
-    rs = inv_norm(block_sum<UPD_THREADS / WAVE>(t, red));
-  }
+  const bool need_x = u.bnd == BND_LOOP_CONTINUE;
+  float v[UPD_MAXPER], sv[UPD_MAXPER], av[UPD_MAXPER], xv[UPD_MAXPER];
   float sq = 0.f;
 #pragma unroll
   for (int k = 0; k < UPD_MAXPER; ++k) {
     const int i = threadIdx.x + k * UPD_THREADS;
     float y = 0.f;
+    sv[k] = av[k] = xv[k] = 0.f;
     if (i < H) {
       for (int s = 0; s < u.splits; ++s) y += u.y[(size_t)s * u.M * H + row + i];
-      y *= rs;
+      sv[k] = u.s[row + i];
+      av[k] = u.alpha[i];
+      if (need_x) xv[k] = u.x[row + i];
     }
     v[k] = y;
     sq += y * y;
@@ -49,13 +46,9 @@ __global__ __launch_bounds__(UPD_THREADS) void k_update(UpdateArgs u) {
   sq = 0.f;
 #pragma unroll
   for (int k = 0; k < UPD_MAXPER; ++k) {
-    const int i = threadIdx.x + k * UPD_THREADS;
-    if (i < H) {
-      const float a = u.alpha[i];
-      const float t = (1.f - a) * u.s[row + i] + a * (v[k] * ny);
-      v[k] = t;
-      sq += t * t;
-    }
+    const float t = (1.f - av[k]) * sv[k] + av[k] * (v[k] * ny);  // zero beyond H
+    v[k] = t;
+    sq += t * t;
   }
   float n = inv_norm(block_sum<UPD_THREADS / WAVE>(sq, red));
 #pragma unroll
@@ -75,14 +68,14 @@ __global__ __launch_bounds__(UPD_THREADS) void k_update(UpdateArgs u) {
     for (int k = 0; k < UPD_MAXPER; ++k) {
       const int i = threadIdx.x + k * UPD_THREADS;
       if (i < H) {
-        float xv;
+        float x;
         if (u.bnd == BND_SAVE_X) {
-          xv = v[k];
-          u.x[row + i] = xv;
+          x = v[k];
+          u.x[row + i] = x;
         } else {
-          xv = u.x[row + i];
+          x = xv[k];
         }
-        v[k] += xv;
+        v[k] += x;
         sq += v[k] * v[k];
       }
     }

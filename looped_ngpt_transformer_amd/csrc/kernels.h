@@ -12,12 +12,11 @@ enum WFmt { W_F32 = 0, W_BF16 = 1, W_MXFP8 = 2 };
 
 // ---------------------------------------------------------------- GEMM  C = A B^T
 enum Epi {
-  EPI_F32 = 0,          // C float [M, N] (fp32 path; "partial" with one split)
+  EPI_F32 = 0,          // C float [M, N] ("partial" with one split)
   EPI_PARTIAL = 1,      // C float [splits][M][N], split-K partial sums
   EPI_STORE_ACT = 2,    // C bf16 [M, N]
-  EPI_F32_ROWSCALE = 3, // C float [M, N] scaled by 1/||row|| from sumsq partials rs_ss
   EPI_SWIGLU = 4,       // rows [0, n_half) gate, [n_half, 2 n_half) up: C bf16 [M, n_half]
-                        // = SiLU(gate) * up, plus per-row sumsq partials into ss_out
+                        // = SiLU(gate) * up
 };
 
 struct GemmArgs {
@@ -32,15 +31,8 @@ struct GemmArgs {
   int splits = 1;
   void* C = nullptr;
   int ldc = 0;
-  const float* rs_ss = nullptr;  // [M, rs_n] sumsq partials of A's rows (ROWSCALE)
-  int rs_n = 0;
-  float* ss_out = nullptr;       // [M, ss_n] written by SWIGLU
-  int ss_n = 0;                  // set by the launcher: partial count per row
   int n_half = 0;
 };
-// Number of sumsq partials per row the SWIGLU epilogue writes for this shape.
-int gemm_swiglu_ss_parts(const GemmArgs& g);
-int gemm_swiglu_parts(int n_half, int wfmt);
 // Split count the launcher would use for a decode-shaped GEMM (EPI_PARTIAL).
 int gemm_pick_splits(int M, int N, int K, int wfmt);
 hipError_t launch_gemm(const GemmArgs& g, hipStream_t st);
@@ -53,10 +45,9 @@ enum Boundary {
   BND_LOOP_FINAL = 3,    // s <- N(s')                          (end of loop k)
 };
 struct UpdateArgs {
-  const float* y = nullptr;  // [splits][M][H] raw sublayer output (partial sums)
+  const float* y = nullptr;  // [splits][M][H] raw sublayer output (partial sums); any
+                             // positive row scale (the pre-projection norms) cancels in N(y)
   int splits = 1;
-  const float* rs_ss = nullptr;  // optional [M, rs_n] sumsq partials (pre-projection norm)
-  int rs_n = 0;
   float* s = nullptr;        // [M, H] state, updated in place
   float* s_out = nullptr;    // where the new state goes (== s, or the caller's output)
   void* sb = nullptr;        // [M, H] act-type copy of the new state (GEMM operand)
@@ -116,7 +107,6 @@ struct AttnArgs {
   float* part = nullptr;          // [M][Hq][splits][d + 2] split partials (workspace)
   int part_cap = 0;               // capacity of part in floats
   void* o = nullptr;              // act [M, Hq*d]
-  float* ss = nullptr;            // [M, Hq] sumsq of the gated output, per head
   // prefill tiles (chunks of consecutive rows of one sequence), MFMA path
   const int32_t* tiles = nullptr; // [n_tiles][4]: row0, nrows, pos0, seq slot
   int n_tiles = 0;
@@ -124,15 +114,14 @@ struct AttnArgs {
 };
 // Row-wise paged attention (any row count; split over keys) + combine + gate.
 hipError_t launch_attn_rows(const AttnArgs& a, hipStream_t st);
-// Prefill attention on bf16 with MFMA (query tiles of 64 rows); writes o and ss.
+// Prefill attention on bf16 with MFMA (query tiles of 64 rows); writes o.
 hipError_t launch_attn_prefill(const AttnArgs& a, hipStream_t st);
 size_t attn_rows_part_floats(int M, int Hq, int d, int max_pos, int window);
 
 // -------------------------------------------------------------------- SwiGLU reduce
 // h = SiLU(sum_s gate) * (sum_s up) from float partials [splits][M][2I]; h act [M, I];
-// ss [M, ss_n] per-row sumsq partials.
 hipError_t launch_swiglu(const float* gu, int splits, int M, int I, void* h, int act,
-                         float* ss, int ss_n, hipStream_t st);
+                         hipStream_t st);
 
 // ------------------------------------------------------------------ page table etc.
 hipError_t launch_apply_deltas(int32_t* table, const int32_t* deltas, int n, hipStream_t st);

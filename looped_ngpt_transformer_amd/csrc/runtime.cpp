@@ -43,12 +43,11 @@ struct Dims {
   size_t esz;          // act element size
   size_t page_elems;   // elements per page (K and V)
   size_t page_bytes;
-  int ss_h_n;          // sumsq partials per row of the SwiGLU activation
   int max_tiles;
 };
 
 struct WsLayout {
-  size_t table, meta, s, x, sb, qkvg, q, o, h, part, ss_o, ss_h, apart, total;
+  size_t table, meta, s, x, sb, qkvg, q, o, h, part, apart, total;
   size_t part_floats, apart_floats;
   size_t meta_ints;
 };
@@ -72,10 +71,6 @@ Dims dims_of(const dory_config& c) {
   D.esz = c.act_dtype == DORY_DTYPE_F32 ? 4 : 2;
   D.page_elems = (size_t)2 * D.Hkv * DORY_PAGE_TOKENS * D.d;
   D.page_bytes = D.page_elems * D.esz;
-  D.ss_h_n = std::max((D.I + 1023) / 1024,  // SwiGLU-reduce blocks per row
-                      c.act_dtype == DORY_DTYPE_BF16
-                          ? gemm_swiglu_parts(D.I, c.weight_format == DORY_WFMT_MXFP8 ? W_MXFP8 : W_BF16)
-                          : 1);
   D.max_tiles = (c.max_rows + 63) / 64 + c.max_seqs;
   return D;
 }
@@ -103,11 +98,9 @@ WsLayout layout_of(const dory_config& c, const Dims& D) {
   W.h = take(R * D.I * D.esz);
   const size_t maxN = std::max({(size_t)D.Nqkvg, (size_t)2 * D.I, (size_t)D.H});
   size_t pf = R * maxN;  // one split at max rows (fp32 path, prefill outputs)
-  if (c.act_dtype == DORY_DTYPE_BF16) pf = std::max(pf, (size_t)16 * std::min<size_t>(R, SKINNY_M) * maxN);
+  if (c.act_dtype == DORY_DTYPE_BF16) pf = std::max(pf, (size_t)32 * std::min<size_t>(R, SKINNY_M) * maxN);  // <= 32 splits
   W.part_floats = pf;
   W.part = take(pf * 4);
-  W.ss_o = take(R * D.Hq * 4);
-  W.ss_h = take(R * D.ss_h_n * 4);
   W.apart_floats = std::max<size_t>(R, 256) * D.Hq * (D.d + 2) * 8;
   W.apart = take(W.apart_floats * 4);
   W.total = off;
@@ -422,8 +415,6 @@ int run_layer(dory_ctx* ctx, hipStream_t st, const CallPlan& P, int l, int slot,
   const int32_t* meta = (const int32_t*)(ws + W.meta);
   float* part = (float*)(ws + W.part);
   float* s = (float*)(ws + W.s);
-  float* ss_o = (float*)(ws + W.ss_o);
-  float* ss_h = (float*)(ws + W.ss_h);
 
   auto gemm = [&](const void* A, int K, const void* B, const uint8_t* Bs, int N, int epi, void* C,
                   int ldc, int splits) {
@@ -453,12 +444,10 @@ int run_layer(dory_ctx* ctx, hipStream_t st, const CallPlan& P, int l, int slot,
            (double)g.N * g.K * wbytes + (double)g.M * g.K * D.esz + (double)g.M * ncols * outb);
     return e;
   };
-  auto update = [&](int splits, const float* rs, int rs_n, const float* alpha, int b, float* sout) {
+  auto update = [&](int splits, const float* alpha, int b, float* sout) {
     UpdateArgs u;
     u.y = part;
     u.splits = splits;
-    u.rs_ss = rs;
-    u.rs_n = rs_n;
     u.s = s;
     u.s_out = sout ? sout : s;
     u.sb = ws + W.sb;
@@ -542,7 +531,6 @@ int run_layer(dory_ctx* ctx, hipStream_t st, const CallPlan& P, int l, int slot,
   aa.part = (float*)(ws + W.apart);
   aa.part_cap = (int)std::min<size_t>(W.apart_floats, 0x7fffffff);
   aa.o = ws + W.o;
-  aa.ss = ss_o;
   aa.tiles = meta + 2 * c.max_rows;
   aa.n_tiles = P.n_tiles;
   aa.max_tile_rows = P.max_tile_rows;
@@ -563,17 +551,14 @@ int run_layer(dory_ctx* ctx, hipStream_t st, const CallPlan& P, int l, int slot,
   // ---- output projection + nGPT update (pre-projection norm as a row scale)
   if (f32) {
     HIPCHK(run_gemm(gemm(ws + W.o, D.Nq, w.w_o, nullptr, D.H, EPI_F32, part, D.H, 1)), "gemm o");
-    HIPCHK(update(1, ss_o, D.Hq, w.alpha_attn, BND_NONE, nullptr), "update attn");
+    HIPCHK(update(1, w.alpha_attn, BND_NONE, nullptr), "update attn");
   } else if (skinny) {
     S = gemm_pick_splits(M, D.H, D.Nq, wf);
     HIPCHK(run_gemm(gemm(ws + W.o, D.Nq, w.w_o, w.s_o, D.H, EPI_PARTIAL, part, D.H, S)), "gemm o");
-    HIPCHK(update(S, ss_o, D.Hq, w.alpha_attn, BND_NONE, nullptr), "update attn");
+    HIPCHK(update(S, w.alpha_attn, BND_NONE, nullptr), "update attn");
   } else {
-    GemmArgs g = gemm(ws + W.o, D.Nq, w.w_o, w.s_o, D.H, EPI_F32_ROWSCALE, part, D.H, 1);
-    g.rs_ss = ss_o;
-    g.rs_n = D.Hq;
-    HIPCHK(run_gemm(g), "gemm o");
-    HIPCHK(update(1, nullptr, 0, w.alpha_attn, BND_NONE, nullptr), "update attn");
+    HIPCHK(run_gemm(gemm(ws + W.o, D.Nq, w.w_o, w.s_o, D.H, EPI_F32, part, D.H, 1)), "gemm o");
+    HIPCHK(update(1, w.alpha_attn, BND_NONE, nullptr), "update attn");
   }
 
   // ---- MLP sublayer
@@ -582,23 +567,18 @@ int run_layer(dory_ctx* ctx, hipStream_t st, const CallPlan& P, int l, int slot,
     HIPCHK(run_gemm(gemm(ws + W.sb, D.H, w.w_gu, w.s_gu, 2 * D.I, f32 ? EPI_F32 : EPI_PARTIAL, part, 2 * D.I, S)), "gemm gu");
     {
       Prof pr(ctx, st, DORY_KC_SWIGLU);
-      HIPCHK(launch_swiglu(part, S, M, D.I, ws + W.h, act, ss_h, D.ss_h_n, st), "swiglu");
+      HIPCHK(launch_swiglu(part, S, M, D.I, ws + W.h, act, st), "swiglu");
       pr.end(0, (double)M * (2.0 * D.I * 4 * S + D.I * D.esz));
     }
     S = f32 ? 1 : gemm_pick_splits(M, D.H, D.I, wf);
     HIPCHK(run_gemm(gemm(ws + W.h, D.I, w.w_down, w.s_down, D.H, f32 ? EPI_F32 : EPI_PARTIAL, part, D.H, S)), "gemm down");
-    HIPCHK(update(S, ss_h, D.ss_h_n, w.alpha_mlp, bnd, out), "update mlp");
+    HIPCHK(update(S, w.alpha_mlp, bnd, out), "update mlp");
   } else {
     GemmArgs g = gemm(ws + W.sb, D.H, w.w_gu, w.s_gu, 2 * D.I, EPI_SWIGLU, ws + W.h, D.I, 1);
     g.n_half = D.I;
-    g.ss_out = ss_h;
-    if (gemm_swiglu_ss_parts(g) != D.ss_h_n) return ctx->fail(DORY_ERR_UNSUPPORTED, "swiglu partials");
     HIPCHK(run_gemm(g), "gemm gu");
-    GemmArgs g2 = gemm(ws + W.h, D.I, w.w_down, w.s_down, D.H, EPI_F32_ROWSCALE, part, D.H, 1);
-    g2.rs_ss = ss_h;
-    g2.rs_n = D.ss_h_n;
-    HIPCHK(run_gemm(g2), "gemm down");
-    HIPCHK(update(1, nullptr, 0, w.alpha_mlp, bnd, out), "update mlp");
+    HIPCHK(run_gemm(gemm(ws + W.h, D.I, w.w_down, w.s_down, D.H, EPI_F32, part, D.H, 1)), "gemm down");
+    HIPCHK(update(1, w.alpha_mlp, bnd, out), "update mlp");
   }
   return DORY_OK;
 }
