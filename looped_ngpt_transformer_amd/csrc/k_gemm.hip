@@ -82,6 +82,49 @@ __device__ __forceinline__ void gemm_epilogue(const GemmArgs& g, f32x4 (&acc)[BM
   }
 }
 
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+
+// Epilogue of the 32x32 MFMA tiles: register r of lane l holds
+// C[m = i*32 + 8*(r/4) + 4*(l/32) + r%4][n = j*32 + l%32] of the wave tile.
+template <int BM, int BN, int WMW, int WNW, int EPI>
+__device__ __forceinline__ void gemm_epilogue32(const GemmArgs& g, f32x16 (&acc)[BM / WMW / 32][BN / WNW / 32],
+                                                int n_tile, int m0, int wm, int wn, int lane) {
+  constexpr int TM = BM / WMW, TN = BN / WNW;
+  constexpr int FM = TM / 32, FN = TN / 32;
+  const int mrow0 = m0 + wm * TM + 4 * (lane >> 5);
+  if (EPI == EPI_SWIGLU) {
+    bf16_t* H = (bf16_t*)g.C;
+    const int c0 = n_tile * (BN / 2) + wn * (TN / 2) + (lane & 31);
+#pragma unroll
+    for (int i = 0; i < FM; ++i)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const int m = mrow0 + i * 32 + 8 * (r >> 2) + (r & 3);
+        if (m >= g.M) continue;
+#pragma unroll
+        for (int j = 0; j < FN / 2; ++j) {
+          const float gt = acc[i][j][r], up = acc[i][j + FN / 2][r];
+          H[(size_t)m * g.ldc + c0 + j * 32] = f2bf(gt / (1.f + __expf(-gt)) * up);
+        }
+      }
+    return;
+  }
+  const int ncol0 = n_tile * BN + wn * TN + (lane & 31);
+#pragma unroll
+  for (int i = 0; i < FM; ++i)
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+      const int m = mrow0 + i * 32 + 8 * (r >> 2) + (r & 3);
+      if (m >= g.M) continue;
+#pragma unroll
+      for (int j = 0; j < FN; ++j) {
+        const int n = ncol0 + j * 32;
+        if (EPI == EPI_STORE_ACT) ((bf16_t*)g.C)[(size_t)m * g.ldc + n] = f2bf(acc[i][j][r]);
+        else ((float*)g.C)[(size_t)m * g.ldc + n] = acc[i][j][r];  // EPI_F32, one split
+      }
+    }
+}
+
 // XCD-aware tile order. Work-groups are dispatched round-robin over the 8 XCDs (each
 // with its own L2); give each XCD a contiguous share of the tiles, ordered in groups of
 // GM m-tiles (m fastest) so the tiles resident on one XCD share A rows and B columns.
@@ -426,15 +469,160 @@ int gemm_pick_splits(int M, int N, int K, int wfmt) {
   return s;
 }
 
-// SwiGLU epilogue tiles: bf16 weights use 256x256 tiles (128 h columns, 2 waves along N)
-// when n_half allows, otherwise (and for MXFP8) 128x128 tiles (64 h columns).
-static bool swiglu_big(int n_half, int wfmt) { return wfmt == W_BF16 && n_half % 128 == 0; }
+
+// Large-M tiles on v_mfma_f32_32x32x16_bf16 (on gfx950 it sustains about 1.5x the
+// rate of the 16x16x32 form). Same direct-to-LDS K-slice ring of 64-wide slices as
+// k_gemm_pipe; each wave owns (BM/WMW) x (BN/WNW) outputs as 32x32 blocks. A fragment
+// (lane l): row l % 32 of the block, K elements 8 (l / 32) .. + 7 of the 16-wide step,
+// one swizzled 16-byte LDS chunk.
+template <int BM, int BN, int WMW, int WNW, int EPI, int STAGES>
+__global__ __launch_bounds__(WMW * WNW * 64) void k_gemm_pipe32(GemmArgs g) {
+  constexpr int PBK = 64;
+  constexpr int NW = WMW * WNW;  // 4 waves (one per SIMD) or 8 (two per SIMD)
+  constexpr int TM = BM / WMW, TN = BN / WNW;
+  constexpr int FM = TM / 32, FN = TN / 32;
+  constexpr int CPR = PBK / 8;
+  constexpr int ACH = BM * CPR, BCH = BN * CPR;
+  constexpr int NINST = (ACH + BCH) / 64;
+  constexpr int MAXI = (NINST + NW - 1) / NW;
+  static_assert(TM % 32 == 0 && TN % 32 == 0, "32x32 blocks per wave");
+  static_assert(NW == 4 || NW == 8, "4 or 8 waves");
+  static_assert(ACH % 64 == 0 && BCH % 64 == 0, "tile rows must be multiples of 8");
+  static_assert(EPI != EPI_SWIGLU || FN % 2 == 0, "SwiGLU needs gate/up pairs per wave");
+  static_assert((STAGES - 2) * MAXI <= 31, "vmcnt range");
+  static_assert(STAGES >= 2, "at least double buffering");
+
+  __shared__ __align__(16) uint4 sm[STAGES][ACH + BCH];
+
+  const int t = threadIdx.x, lane = t & 63, wave = t >> 6;
+  const int wm = wave / WNW, wn = wave % WNW;
+  int n_tile, m_tile;
+  tile_coords<8>(&n_tile, &m_tile);
+  const int m0 = m_tile * BM;
+  const int nk = g.K / PBK;
+  const bf16_t* A = (const bf16_t*)g.A;
+  const bf16_t* B = (const bf16_t*)g.B;
+  const int my_inst = (NINST - wave + NW - 1) / NW;
+
+  auto brow = [&](int r) -> int {
+    if (EPI == EPI_SWIGLU) {
+      const int c0 = n_tile * (BN / 2);
+      return r < BN / 2 ? c0 + r : g.n_half + c0 + (r - BN / 2);
+    }
+    return n_tile * BN + r;
+  };
+  auto issue = [&](int slot, int k0) {
+#pragma unroll
+    for (int q = 0; q < MAXI; ++q) {
+      const int inst = wave + NW * q;
+      if (inst < NINST) {
+        const int sidx = inst * 64 + lane;
+        const bf16_t* src;
+        if (sidx < ACH) {
+          const int r = sidx / CPR, c = swzc<CPR>(r, sidx % CPR) - r * CPR;
+          const int m = min(m0 + r, g.M - 1);
+          src = A + (size_t)m * g.lda + k0 + 8 * c;
+        } else {
+          const int s2 = sidx - ACH;
+          const int r = s2 / CPR, c = swzc<CPR>(r, s2 % CPR) - r * CPR;
+          src = B + (size_t)brow(r) * g.K + k0 + 8 * c;
+        }
+        __builtin_amdgcn_global_load_lds((gbl_void_t)src, (lds_void_t)(&sm[slot][inst * 64]), 16, 0, 0);
+      }
+    }
+  };
+  auto bblock = [&](int j) -> int {
+    if (EPI == EPI_SWIGLU) {
+      constexpr int TNh = TN / 2;
+      return j < FN / 2 ? wn * TNh + j * 32 : BN / 2 + wn * TNh + (j - FN / 2) * 32;
+    }
+    return wn * TN + j * 32;
+  };
+
+  f32x16 acc[FM][FN];
+#pragma unroll
+  for (int i = 0; i < FM; ++i)
+#pragma unroll
+    for (int j = 0; j < FN; ++j)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.f;
+
+#pragma unroll
+  for (int st = 0; st < STAGES - 1; ++st)
+    if (st < nk) issue(st, PBK * st);
+
+  for (int it = 0; it < nk; ++it) {
+    const int ahead = min(STAGES - 2, nk - 1 - it);  // later tiles already in flight
+    wait_vmcnt(ahead * my_inst);
+    __syncthreads();
+    if (it + STAGES - 1 < nk) issue((it + STAGES - 1) % STAGES, PBK * (it + STAGES - 1));
+    const uint4* As = sm[it % STAGES];
+    const uint4* Bs = As + ACH;
+    // 16-wide K steps with two fragment sets: the reads of step ks+1 are interleaved with
+    // the MFMAs of step ks (one read after each MFMA), so LDS latency stays hidden
+    bf16x8 af[2][FM], bfr[2][FN];
+    auto ldfrag = [&](int ks, bf16x8 (&a)[FM], bf16x8 (&b)[FN]) {
+      const int ch = ks * 2 + (lane >> 5);
+#pragma unroll
+      for (int i = 0; i < FM; ++i)
+        a[i] = __builtin_bit_cast(bf16x8, As[swzc<CPR>(wm * TM + i * 32 + (lane & 31), ch)]);
+#pragma unroll
+      for (int j = 0; j < FN; ++j)
+        b[j] = __builtin_bit_cast(bf16x8, Bs[swzc<CPR>(bblock(j) + (lane & 31), ch)]);
+    };
+    ldfrag(0, af[0], bfr[0]);
+#pragma unroll
+    for (int ks = 0; ks < PBK / 16; ++ks) {
+      const int cur = ks & 1;
+      if (ks + 1 < PBK / 16) ldfrag(ks + 1, af[cur ^ 1], bfr[cur ^ 1]);
+#pragma unroll
+      for (int i = 0; i < FM; ++i)
+#pragma unroll
+        for (int j = 0; j < FN; ++j)
+          acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[cur][i], bfr[cur][j], acc[i][j], 0, 0, 0);
+      if (ks + 1 < PBK / 16) {
+#pragma unroll
+        for (int q = 0; q < FM + FN; ++q) {
+          __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // one MFMA
+          __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);  // one LDS read
+        }
+        __builtin_amdgcn_sched_group_barrier(0x008, FM * FN - (FM + FN), 0);
+      }
+    }
+  }
+  gemm_epilogue32<BM, BN, WMW, WNW, EPI>(g, acc, n_tile, m0, wm, wn, lane);
+}
 
 template <int BM, int BN, int WMW, int WNW, int EPI, int STAGES, int PBK = 32>
 static hipError_t go_pipe(const GemmArgs& g, hipStream_t st, int ntiles_n) {
   dim3 grid(ntiles_n, (g.M + BM - 1) / BM, g.splits);
   hipLaunchKernelGGL((k_gemm_pipe<BM, BN, WMW, WNW, EPI, STAGES, PBK>), grid, dim3(GT), 0, st, g);
   return hipGetLastError();
+}
+
+// Large-M (prefill) tiles for bf16 weights over n output columns (for SwiGLU, gate and
+// up columns together): 256x256 tiles when they fill the device, else 256x160 (waves
+// stacked along M) when n allows; hipErrorNotSupported when no tile shape divides n.
+template <int BM, int BN, int WMW, int WNW, int EPI, int STAGES>
+static hipError_t go_pipe32(const GemmArgs& g, hipStream_t st, int ntiles_n) {
+  dim3 grid(ntiles_n, (g.M + BM - 1) / BM);
+  hipLaunchKernelGGL((k_gemm_pipe32<BM, BN, WMW, WNW, EPI, STAGES>), grid, dim3(WMW * WNW * 64), 0, st, g);
+  return hipGetLastError();
+}
+
+template <int EPI>
+static hipError_t go_big(const GemmArgs& g, hipStream_t st, int n) {
+#ifndef DORY_BIG_WAVES
+#define DORY_BIG_WAVES 8
+#endif
+  if (n % 256 == 0 && (EPI == EPI_SWIGLU || n / 256 * ((g.M + 255) / 256) >= 256)) {
+    if (DORY_BIG_WAVES == 8) return go_pipe32<256, 256, 2, 4, EPI, 2>(g, st, n / 256);
+    return go_pipe32<256, 256, 2, 2, EPI, 2>(g, st, n / 256);
+  }
+  if constexpr (EPI != EPI_SWIGLU)
+    if (n % 160 == 0) return go_pipe32<256, 160, 4, 1, EPI, 2>(g, st, n / 160);
+  if (n % 256 == 0) return go_pipe32<256, 256, 2, 2, EPI, 2>(g, st, n / 256);
+  return hipErrorNotSupported;
 }
 
 template <int BM, int BN, int WMW, int WNW, int EPI>
@@ -471,19 +659,26 @@ hipError_t launch_gemm(const GemmArgs& gin, hipStream_t st) {
       return go<128, 64, 1, 4, EPI_PARTIAL>(g, st, g.N / 64);
     case EPI_STORE_ACT:
       if (g.splits != 1) return hipErrorInvalidValue;
-      if (bf && g.N % 256 == 0) return go_pipe<256, 256, 2, 2, EPI_STORE_ACT, 2, 64>(g, st, g.N / 256);
-      if (bf && g.N % 160 == 0) return go_pipe<256, 160, 2, 2, EPI_STORE_ACT, 2, 64>(g, st, g.N / 160);
+      if (bf) {
+        const hipError_t e = go_big<EPI_STORE_ACT>(g, st, g.N);
+        if (e != hipErrorNotSupported) return e;
+      }
       if (g.N % 128) return hipErrorInvalidValue;
       return go<128, 128, 2, 2, EPI_STORE_ACT>(g, st, g.N / 128);
     case EPI_F32:  // large M: fp32 output for the nGPT update
       if (g.splits != 1) return hipErrorInvalidValue;
-      if (bf && g.N % 160 == 0) return go_pipe<256, 160, 2, 2, EPI_F32, 2, 64>(g, st, g.N / 160);
-      if (bf && g.N % 256 == 0) return go_pipe<256, 256, 2, 2, EPI_F32, 2, 64>(g, st, g.N / 256);
+      if (bf) {
+        const hipError_t e = go_big<EPI_F32>(g, st, g.N);
+        if (e != hipErrorNotSupported) return e;
+      }
       if (g.N % 128) return hipErrorInvalidValue;
       return go<128, 128, 2, 2, EPI_F32>(g, st, g.N / 128);
     case EPI_SWIGLU:
       if (g.n_half % 64 || g.splits != 1) return hipErrorInvalidValue;
-      if (swiglu_big(g.n_half, g.wfmt)) return go_pipe<256, 256, 2, 2, EPI_SWIGLU, 2, 64>(g, st, g.n_half / 128);
+      if (g.wfmt == W_BF16) {  // tiles interleave gate and up halves
+        const hipError_t e = go_big<EPI_SWIGLU>(g, st, 2 * g.n_half);
+        if (e != hipErrorNotSupported) return e;
+      }
       return go<128, 128, 2, 2, EPI_SWIGLU>(g, st, g.n_half / 64);
     default:
       return hipErrorInvalidValue;
