@@ -25,6 +25,14 @@ __device__ __forceinline__ bf16_t f2bf(float f) {
   return (bf16_t)(u >> 16);
 }
 
+// two floats -> packed bf16 pair (a in the low half), round to nearest even, with the
+// hardware conversion (v_cvt_pk_bf16_f32)
+__device__ __forceinline__ uint32_t pack_bf16x2(float a, float b) {
+  typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+  const bf16x2_t v = {(__bf16)a, (__bf16)b};
+  return __builtin_bit_cast(uint32_t, v);
+}
+
 template <typename T> __device__ __forceinline__ float ld(const T* p, size_t i);
 template <> __device__ __forceinline__ float ld<float>(const float* p, size_t i) { return p[i]; }
 template <> __device__ __forceinline__ float ld<bf16_t>(const bf16_t* p, size_t i) { return bf2f(p[i]); }

@@ -5,51 +5,90 @@
 // ("Dory1.0-4B": paper summary "technical novelty"; arXiv §2; MXFP8 article "hybrid
 // attention").
 //
-// Work-group = (tile of <= 64 consecutive query rows of one sequence, KV head): 16
-// waves, wave = (query head g of the group, 16-row quarter of the tile). Per KV page:
-//   S^T = K Q^T   with v_mfma_f32_16x16x32_bf16 (A = K rows from LDS, B = Q in registers),
-//   online softmax per query in registers (lane's query is lane % 16),
-//   O^T += V^T P^T (A = V^T from LDS, B = P straight from the S^T accumulators: the lane
-//   already holds 2x4 keys of its query, which is a valid k-ordering of the MFMA when
-//   V^T is read with the same key permutation).
-// The page's K and V blocks (8-element chunks in MFMA fragment order) are staged as a
-// row-major K tile and a V^T tile in padded LDS rows; the next page is prefetched into
-// registers while the current one is consumed. Entries of the last page beyond the chunk's last position are zeroed, so
-// unwritten cache memory can never reach the sums.
+// Work-group = (tile of <= 64 consecutive query rows of one sequence, KV head): 8
+// waves, wave = (query head g of the group, 32-row half of the tile), two waves per
+// SIMD. Per 64-key KV page, with v_mfma_f32_32x32x16_bf16 (on gfx950 about 1.5x the
+// rate of the 16x16x32 form):
+//   S^T = K Q^T   (A = K rows from LDS, B = Q in registers): two 32-key blocks,
+//   online softmax per query in registers (lanes l and l + 32 share query l % 32),
+//   O^T += V^T P^T (A = V^T from LDS, B = P straight from the S^T accumulators: lane
+//   half h holds keys 4h..4h+3 and 8+4h..8+4h+3 of each 16-key group, which is a valid
+//   k-ordering of the MFMA when V^T is read with the same key permutation).
+// The page's K and V blocks are stored as 1 KiB groups of 16-byte chunks in MFMA
+// fragment order; they go straight from HBM into LDS (global_load_lds, three stages:
+// two pages in flight while one is consumed), each group at a padded stride so that the
+// 32x32 fragment reads are free of bank conflicts. Keys beyond the chunk's last position
+// are masked out of the softmax; their V entries are multiplied by zero probabilities
+// and hold zeros or stale finite values (pages are cleared when first allocated).
+#include <type_traits>
+
 #include "common.h"
 #include "kernels.h"
 
 namespace dory {
 
-constexpr int PF_THREADS = 1024;
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+
+constexpr int PF_WAVES = 8;
+constexpr int PF_THREADS = PF_WAVES * 64;
 constexpr int PF_MAX_PAGES = 4096;  // positions up to 262144
+
+typedef __attribute__((address_space(3))) void* pf_lds_t;
+typedef __attribute__((address_space(1))) void* pf_gbl_t;
+
+// s_waitcnt vmcnt(n) for the few run-time values the page pipeline needs
+__device__ __forceinline__ void pf_wait_vmcnt(int n) {
+  switch (n) {
+    case 0: asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); break;
+    case 1: asm volatile("s_waitcnt vmcnt(1)" ::: "memory"); break;
+    case 2: asm volatile("s_waitcnt vmcnt(2)" ::: "memory"); break;
+    case 3: asm volatile("s_waitcnt vmcnt(3)" ::: "memory"); break;
+    case 4: asm volatile("s_waitcnt vmcnt(4)" ::: "memory"); break;
+    case 5: asm volatile("s_waitcnt vmcnt(5)" ::: "memory"); break;
+    case 6: asm volatile("s_waitcnt vmcnt(6)" ::: "memory"); break;
+    default: asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); break;
+  }
+}
 
 template <int D>
 __global__ __launch_bounds__(PF_THREADS) void k_attn_prefill(AttnArgs a) {
   constexpr int G = 4;
-  constexpr int DC = D / 32;       // 32-wide chunks of the head dim (QK contraction)
-  constexpr int CB = D / 16;       // 16-channel blocks of the output
-  constexpr int KCH = D / 8 + 1;   // 16-byte chunks per padded K row
-  // bf16 per padded V^T row: a 136-byte stride puts the 16 rows of an 8-byte fragment
-  // read in distinct banks (row r at 8r mod 128 bytes)
-  constexpr int VTR = 64 + 4;
-  constexpr int NCH = 2 * 64 * D / 8;  // 16-byte chunks of K and V per page and head
-  constexpr int CPT = (NCH + PF_THREADS - 1) / PF_THREADS;  // chunks per thread (last partial)
-  static_assert(D % 32 == 0, "head dim");
+  constexpr int KS = D / 16;       // 16-wide steps of the head dim (QK contraction)
+  constexpr int CB = D / 32;       // 32-channel blocks of the output
+  constexpr int DC = D / 32;       // 32-channel chunks of a K fragment group
+  constexpr int CB16 = D / 16;     // 16-channel blocks of V
+  constexpr int NG = D / 8;        // 1 KiB groups per K (or V) block of one head
+  // padded group strides: K fragments read two groups DC apart, V fragments two groups
+  // 1 apart, in the same LDS cycle
+  constexpr int KGS = 1024 + (DC == 5 ? 128 : 128 / DC);
+  constexpr int VGS = 1024 + 8;
+  constexpr int STAGE = NG * (KGS + VGS);  // bytes per page stage
+  constexpr int NSTAGE = 3;
+  constexpr int GPW = (2 * NG + PF_WAVES - 1) / PF_WAVES;  // load instructions per wave per page
+  static_assert(D % 32 == 0 && DC >= 1 && (DC == 5 || 128 % DC == 0), "head dim");
+  static_assert(GPW <= 6, "vmcnt range of the page pipeline");
 
-  __shared__ uint4 Ks[2][64 * KCH];                  // double-buffered page tiles
-  __shared__ __align__(16) bf16_t Vt[2][D * VTR];
-  __shared__ int32_t pages[PF_MAX_PAGES];            // the tile's page ids
+  // one array per stage: LDS reads of one stage are then known not to alias the
+  // direct-to-LDS loads in flight into the others, so they need not wait for them
+  __shared__ __align__(16) unsigned char sm0[STAGE];
+  __shared__ __align__(16) unsigned char sm1[STAGE];
+  __shared__ __align__(16) unsigned char sm2[STAGE];
+  __shared__ int32_t pages[PF_MAX_PAGES];  // the tile's page ids
+  auto stage_ptr = [&](auto S) -> unsigned char* {
+    if constexpr (decltype(S)::value == 0) return sm0;
+    else if constexpr (decltype(S)::value == 1) return sm1;
+    else return sm2;
+  };
 
   const int tile = a.n_tiles - 1 - blockIdx.x;  // longest (latest) tiles first
   const int hk = blockIdx.y;
   const int32_t* tl = a.tiles + 4 * tile;
   const int row0 = tl[0], nrows = tl[1], pos0 = tl[2], seq = tl[3];
   const int t = threadIdx.x, lane = t & 63, w = t >> 6;
-  const int g = w >> 2, qq = w & 3;  // query head, 16-row quarter
+  const int g = w >> 1, hh = w & 1;  // query head, 32-row half
   const int h = hk * G + g;
   const int HqD = a.Hq * D;
-  const int lq = lane & 15, lk = lane >> 4;
+  const int l32 = lane & 31, lh = lane >> 5;
 
   const int kmax = pos0 + nrows - 1;
   const bool full = a.window == 0;
@@ -58,181 +97,179 @@ __global__ __launch_bounds__(PF_THREADS) void k_attn_prefill(AttnArgs a) {
   const int32_t* trow = a.kv.table + ((size_t)seq * a.kv.n_streams + a.stream_idx) * a.kv.tab_len;
   const bf16_t* pool = (const bf16_t*)a.kv.pool;
 
-  // Q fragments (B operand): query 16 qq + lq, dims 32 c + 8 lk + e
-  bf16x8 qf[1][DC];
+  // Q fragments (B operand): query 32 hh + l32, channels 16 c + 8 lh .. + 7
+  const int qi = 32 * hh + l32;
+  const bool qv = qi < nrows;
+  const int qpos = pos0 + qi;
+  bf16x8 qf[KS];
 #pragma unroll
-  for (int qb = 0; qb < 1; ++qb) {
-    const int i = 16 * qq + lq;
-#pragma unroll
-    for (int c = 0; c < DC; ++c) {
-      uint4 v = make_uint4(0, 0, 0, 0);
-      if (i < nrows)
-        v = *(const uint4*)((const bf16_t*)a.q + (size_t)(row0 + i) * HqD + (size_t)h * D + 32 * c + 8 * lk);
-      qf[qb][c] = __builtin_bit_cast(bf16x8, v);
-    }
+  for (int c = 0; c < KS; ++c) {
+    uint4 v = make_uint4(0, 0, 0, 0);
+    if (qv) v = *(const uint4*)((const bf16_t*)a.q + (size_t)(row0 + qi) * HqD + (size_t)h * D + 16 * c + 8 * lh);
+    qf[c] = __builtin_bit_cast(bf16x8, v);
   }
 
   for (int i = t; i <= pg_hi - pg_lo; i += PF_THREADS) pages[i] = trow[(pg_lo + i) % a.kv.ring];
   __syncthreads();
 
-  // K/V of page pg into registers
-  auto gload = [&](int pg, uint4 (&pre)[CPT]) {
+  // page pg -> stage: wave w loads groups w, w + 8, ... (K groups 0..NG-1, then V)
+  auto issue = [&](int pg, auto S) {
     const int32_t page = pages[pg - pg_lo];
-    const bf16_t* kp = pool + (size_t)page * a.kv.page_elems + (size_t)hk * 64 * D;
-    const bf16_t* vp = kp + (size_t)a.kv.Hkv * 64 * D;
+    const unsigned char* kb = (const unsigned char*)(pool + (size_t)page * a.kv.page_elems + (size_t)hk * 64 * D);
+    const unsigned char* vb = (const unsigned char*)(pool + (size_t)page * a.kv.page_elems + (size_t)(a.kv.Hkv + hk) * 64 * D);
+    unsigned char* st0 = stage_ptr(S);
 #pragma unroll
-    for (int i = 0; i < CPT; ++i) {
-      const int s = t + PF_THREADS * i;
-      if (s < NCH) pre[i] = s < NCH / 2 ? ((const uint4*)kp)[s] : ((const uint4*)vp)[s - NCH / 2];
-    }
-  };
-  auto sstore = [&](int pg, const uint4 (&pre)[CPT], int buf) {
-#pragma unroll
-    for (int i = 0; i < CPT; ++i) {
-      const int s = t + PF_THREADS * i;
-      if (s >= NCH) break;
-      const bool isv = s >= NCH / 2;
-      const int s2 = isv ? s - NCH / 2 : s;
-      if (!isv) {  // K chunk: token j, channels 8 ch .. 8 ch + 7
-        int j, c8;
-        kv_k_chunk(s2, D, j, c8);
-        const int ch = c8 >> 3;
-        Ks[buf][j * KCH + ch] = (pg * PAGE + j > kmax) ? make_uint4(0, 0, 0, 0) : pre[i];
-      } else {     // V^T chunk: channel c, tokens 8 kc .. 8 kc + 7
-        int c, t8;
-        kv_v_chunk(s2, D, c, t8);
-        const int kc = t8 >> 3;
-        uint4 v = pre[i];
-        const int over = pg * PAGE + 8 * kc + 7 - kmax;  // tokens past the chunk's last
-        if (over > 0) {
-          uint32_t wv[4] = {v.x, v.y, v.z, v.w};
-#pragma unroll
-          for (int e = 0; e < 8; ++e)
-            if (8 * kc + e > kmax - pg * PAGE) wv[e / 2] &= (e & 1) ? 0x0000FFFFu : 0xFFFF0000u;
-          v = make_uint4(wv[0], wv[1], wv[2], wv[3]);
-        }
-        uint2* dst = (uint2*)(Vt[buf] + c * VTR + 8 * kc);  // 8-byte aligned rows
-        dst[0] = make_uint2(v.x, v.y);
-        dst[1] = make_uint2(v.z, v.w);
+    for (int q = 0; q < GPW; ++q) {
+      const int grp = w + PF_WAVES * q;
+      if (grp < 2 * NG) {
+        const bool isv = grp >= NG;
+        const int gi = isv ? grp - NG : grp;
+        const unsigned char* src = (isv ? vb : kb) + gi * 1024 + lane * 16;
+        unsigned char* dst = st0 + (isv ? NG * KGS + gi * VGS : gi * KGS);
+        __builtin_amdgcn_global_load_lds((pf_gbl_t)src, (pf_lds_t)dst, 16, 0, 0);
       }
     }
   };
+  const int my_inst = __builtin_amdgcn_readfirstlane((2 * NG - w + PF_WAVES - 1) / PF_WAVES);
 
+  // per-lane parts of the fragment addresses (bytes within a stage)
+  //   K fragment (key block hf, 16-channel step c): group (2 hf + kb16) DC + c / 2,
+  //   chunk ((c % 2) 2 + lh) 16 + lq with kb16 = (l32 / 4) % 2, lq = 4 (l32 / 8) + l32 % 4
+  const int koff = ((l32 >> 2) & 1) * DC * KGS + (lh * 16 + (((l32 >> 3) << 2) | (l32 & 3))) * 16;
+  //   V fragment (channel block cb, key step s): group (s / 2) CB16 + 2 cb + l32 / 16,
+  //   chunk (2 (s % 2) + half) 16 + l32 % 16, plus 8 bytes for lane half lh
+  const int voff = NG * KGS + (l32 >> 4) * VGS + (l32 & 15) * 16 + 8 * lh;
   const float sl2 = a.scale * 1.4426950408889634f;  // logits in log2 units
-  float m_run[1] = {-INFINITY}, l_run[1] = {0.f};
-  f32x4 o[CB][1];
+  float m_run = -INFINITY, l_run = 0.f;
+  f32x16 o[CB];
 #pragma unroll
-  for (int cb = 0; cb < CB; ++cb) o[cb][0] = f32x4{0.f, 0.f, 0.f, 0.f};
+  for (int cb = 0; cb < CB; ++cb)
+#pragma unroll
+    for (int r = 0; r < 16; ++r) o[cb][r] = 0.f;
 
   // one page per step from LDS buffer (pg - pg_lo) & 1; the next page's tiles go to the
   // other buffer (its readers passed the previous barrier) while the page after that is
   // loaded into registers
-  auto compute = [&](int pg, int buf) {
-    // S^T[key 16 kb + 4 lk + r][query 16 qb + lq]
-    f32x4 st[4][1];
+  auto compute = [&](int pg, auto S) {
+    const unsigned char* st0 = stage_ptr(S);
+    // S^T[key 32 kb + 8 (r / 4) + 4 lh + r % 4][query l32]
+    f32x16 st[2];
 #pragma unroll
-    for (int kb = 0; kb < 4; ++kb) {
-      st[kb][0] = f32x4{0.f, 0.f, 0.f, 0.f};
+    for (int kb = 0; kb < 2; ++kb) {
 #pragma unroll
-      for (int c = 0; c < DC; ++c) {
-        const bf16x8 kf = __builtin_bit_cast(bf16x8, Ks[buf][(16 * kb + lq) * KCH + 4 * c + lk]);
-        st[kb][0] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kf, qf[0][c], st[kb][0], 0, 0, 0);
+      for (int r = 0; r < 16; ++r) st[kb][r] = 0.f;
+#pragma unroll
+      for (int c = 0; c < KS; ++c) {
+        const int off = (2 * kb * DC + (c >> 1)) * KGS + (c & 1) * 32 * 16;
+        const bf16x8 kf = *(const bf16x8*)(st0 + koff + off);
+        st[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf, qf[c], st[kb], 0, 0, 0);
       }
     }
-    // online softmax; probabilities packed as the PV B operand
-    bf16x8 pf[1][2];
+    // online softmax for query l32 over this lane's 32 keys and the partner lane's 32.
+    // Pages every query of the tile sees in full skip the per-key masks.
+    const bool all_vis = pg * PAGE + PAGE - 1 <= pos0 && (full || pos0 + nrows - 1 - pg * PAGE < a.window);
+    float mt = -INFINITY;
+    if (all_vis) {
 #pragma unroll
-    for (int qb = 0; qb < 1; ++qb) {
-      const int i = 16 * qq + lq;
-      const int qpos = pos0 + i;
-      const bool qv = i < nrows;
-      float sv[4][4];
-      float mt = -INFINITY;
+      for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
-      for (int kb = 0; kb < 4; ++kb)
+        for (int r = 0; r < 16; ++r) {
+          st[kb][r] *= sl2;
+          mt = fmaxf(mt, st[kb][r]);
+        }
+    } else {
 #pragma unroll
-        for (int r = 0; r < 4; ++r) {
-          const int kpos = pg * PAGE + 16 * kb + 4 * lk + r;
+      for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const int kpos = pg * PAGE + 32 * kb + 8 * (r >> 2) + 4 * lh + (r & 3);
           const bool vis = qv && kpos <= qpos && (full || qpos - kpos < a.window);
-          sv[kb][r] = vis ? st[kb][qb][r] * sl2 : -INFINITY;
-          mt = fmaxf(mt, sv[kb][r]);
+          st[kb][r] = vis ? st[kb][r] * sl2 : -INFINITY;
+          mt = fmaxf(mt, st[kb][r]);
         }
-      mt = fmaxf(mt, __shfl_xor(mt, 16, 64));
-      mt = fmaxf(mt, __shfl_xor(mt, 32, 64));
-      const float m_new = fmaxf(m_run[qb], mt);
-      const float corr = m_run[qb] == -INFINITY ? 0.f : exp2f(m_run[qb] - m_new);
-      float ps = 0.f;
-      float pv[4][4];
-#pragma unroll
-      for (int kb = 0; kb < 4; ++kb)
-#pragma unroll
-        for (int r = 0; r < 4; ++r) {
-          const float p = sv[kb][r] == -INFINITY ? 0.f : exp2f(sv[kb][r] - m_new);
-          pv[kb][r] = p;
-          ps += p;
-        }
-      ps += __shfl_xor(ps, 16, 64);
-      ps += __shfl_xor(ps, 32, 64);
-      l_run[qb] = l_run[qb] * corr + ps;
-      m_run[qb] = m_new;
-#pragma unroll
-      for (int cb = 0; cb < CB; ++cb) o[cb][qb] *= corr;
-#pragma unroll
-      for (int kc = 0; kc < 2; ++kc) {
-        uint32_t u[4];
-#pragma unroll
-        for (int e = 0; e < 4; e += 2) {
-          u[e / 2] = (uint32_t)f2bf(pv[2 * kc][e]) | ((uint32_t)f2bf(pv[2 * kc][e + 1]) << 16);
-          u[2 + e / 2] = (uint32_t)f2bf(pv[2 * kc + 1][e]) | ((uint32_t)f2bf(pv[2 * kc + 1][e + 1]) << 16);
-        }
-        pf[qb][kc] = __builtin_bit_cast(bf16x8, make_uint4(u[0], u[1], u[2], u[3]));
-      }
     }
-    // O^T[channel 16 cb + 4 lk + r][query 16 qb + lq] += V^T P^T
+    mt = fmaxf(mt, __shfl_xor(mt, 32, 64));
+    const float m_new = fmaxf(m_run, mt);
+    // a query that has seen no visible key yet keeps m = -inf; its (all -inf) logits
+    // give p = exp2(-inf) = 0 against a finite reference instead of NaN
+    const float m_ref = m_new == -INFINITY ? 0.f : m_new;
+    float ps = 0.f;
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const float p = exp2f(st[kb][r] - m_ref);
+        st[kb][r] = p;
+        ps += p;
+      }
+    ps += __shfl_xor(ps, 32, 64);
+    if (!__all(m_new == m_run)) {  // rescale only when some query's maximum moved
+      const float corr = m_run == -INFINITY ? 0.f : exp2f(m_run - m_new);
+      l_run *= corr;
+#pragma unroll
+      for (int cb = 0; cb < CB; ++cb) o[cb] *= corr;
+    }
+    l_run += ps;
+    m_run = m_new;
+    // P^T fragment of 16-key step s: slots e < 4 are keys 16 s + 4 lh + e, slots e >= 4
+    // keys 16 s + 8 + 4 lh + e - 4 (accumulator rows 8 (s % 2) + e of block s / 2)
+    bf16x8 pf[4];
+#pragma unroll
+    for (int s = 0; s < 4; ++s) {
+      uint32_t u[4];
+#pragma unroll
+      for (int e = 0; e < 8; e += 2) u[e / 2] = pack_bf16x2(st[s >> 1][8 * (s & 1) + e], st[s >> 1][8 * (s & 1) + e + 1]);
+      pf[s] = __builtin_bit_cast(bf16x8, make_uint4(u[0], u[1], u[2], u[3]));
+    }
+    // O^T[channel 32 cb + 8 (r / 4) + 4 lh + r % 4][query l32] += V^T P^T
 #pragma unroll
     for (int cb = 0; cb < CB; ++cb) {
 #pragma unroll
-      for (int kc = 0; kc < 2; ++kc) {
-        const bf16_t* vr = Vt[buf] + (16 * cb + lq) * VTR + 32 * kc + 4 * lk;
+      for (int s = 0; s < 4; ++s) {
+        const unsigned char* vr = st0 + voff + ((s >> 1) * CB16 + 2 * cb) * VGS + (2 * (s & 1)) * 16 * 16;
         const uint2 lo = *(const uint2*)vr;
-        const uint2 hi = *(const uint2*)(vr + 16);
+        const uint2 hi = *(const uint2*)(vr + 16 * 16);
         const bf16x8 vf = __builtin_bit_cast(bf16x8, make_uint4(lo.x, lo.y, hi.x, hi.y));
-        o[cb][0] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vf, pf[0][kc], o[cb][0], 0, 0, 0);
+        o[cb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf, pf[s], o[cb], 0, 0, 0);
       }
     }
   };
 
-  uint4 pre[CPT];
-  gload(pg_lo, pre);
-  sstore(pg_lo, pre, 0);
-  if (pg_lo + 1 <= pg_hi) gload(pg_lo + 1, pre);
-  __syncthreads();
-  for (int pg = pg_lo; pg <= pg_hi; ++pg) {
-    const int buf = (pg - pg_lo) & 1;
-    if (pg + 1 <= pg_hi) sstore(pg + 1, pre, buf ^ 1);
-    if (pg + 2 <= pg_hi) gload(pg + 2, pre);
-    compute(pg, buf);
-    __syncthreads();
+  // three-stage page pipeline: pages pg+1 and pg+2 load while pg is consumed; the loop
+  // is unrolled by the stage count so every stage index is a compile-time constant
+  using S0 = std::integral_constant<int, 0>;
+  using S1 = std::integral_constant<int, 1>;
+  using S2 = std::integral_constant<int, 2>;
+  auto step = [&](int pg, auto S, auto S_next2) {
+    pf_wait_vmcnt(pg + 1 <= pg_hi ? my_inst : 0);  // page pg has landed (this wave's part)
+    __syncthreads();                                // ... and every wave's; stage of pg-1 free
+    if (pg + 2 <= pg_hi) issue(pg + 2, S_next2);
+    compute(pg, S);
+  };
+  issue(pg_lo, S0{});
+  if (pg_lo + 1 <= pg_hi) issue(pg_lo + 1, S1{});
+  for (int pg = pg_lo; pg <= pg_hi; pg += 3) {
+    step(pg, S0{}, S2{});
+    if (pg + 1 <= pg_hi) step(pg + 1, S1{}, S0{});
+    if (pg + 2 <= pg_hi) step(pg + 2, S2{}, S1{});
   }
 
-  // epilogue: normalise, gate, store
-#pragma unroll
-  for (int qb = 0; qb < 1; ++qb) {
-    const int i = 16 * qq + lq;
-    const bool qv = i < nrows;
-    const float invl = qv ? 1.f / l_run[qb] : 0.f;
-    const size_t base = (size_t)(row0 + (qv ? i : 0)) * HqD + (size_t)h * D;
+  // epilogue: normalise, gate, store; lane holds 4 consecutive channels per (cb, r / 4)
+  if (qv) {
+    const float invl = 1.f / l_run;
+    const size_t base = (size_t)(row0 + qi) * HqD + (size_t)h * D;
 #pragma unroll
     for (int cb = 0; cb < CB; ++cb) {
-      const int c = 16 * cb + 4 * lk;
-      float v[4];
 #pragma unroll
-      for (int r = 0; r < 4; ++r) v[r] = o[cb][qb][r] * invl;
-      if (qv) {
+      for (int rb = 0; rb < 4; ++rb) {
+        const int c = 32 * cb + 8 * rb + 4 * lh;
+        float v[4];
+#pragma unroll
+        for (int r = 0; r < 4; ++r) v[r] = o[cb][4 * rb + r] * invl;
         if (a.g) {
 #pragma unroll
           for (int r = 0; r < 4; ++r)
-            v[r] *= gate_at(a.g, a.g_f32, a.g_ld, a.g_splits, a.g_sstride, row0 + i, h * D + c + r);
+            v[r] *= gate_at(a.g, a.g_f32, a.g_ld, a.g_splits, a.g_sstride, row0 + qi, h * D + c + r);
         }
         uint2 ov;
         ov.x = (uint32_t)f2bf(v[0]) | ((uint32_t)f2bf(v[1]) << 16);
@@ -246,6 +283,7 @@ __global__ __launch_bounds__(PF_THREADS) void k_attn_prefill(AttnArgs a) {
 hipError_t launch_attn_prefill(const AttnArgs& a, hipStream_t st) {
   if (a.n_tiles == 0) return hipSuccess;
   if (a.kv.act != ACT_BF16 || a.Hq != 4 * a.Hkv) return hipErrorInvalidValue;
+  if (a.max_pos / PAGE + 1 > PF_MAX_PAGES) return hipErrorInvalidValue;
   dim3 grid(a.n_tiles, a.Hkv);
   switch (a.d) {
     case 64:

@@ -113,6 +113,143 @@ __global__ __launch_bounds__(256) void k_rope_kv(RopeArgs a) {
   }
 }
 
+// Prefill form: one work-group per (16-row quarter of a tile of <= 64 consecutive rows
+// of one sequence, KV head), bf16 projection output. The rotation angles of the rows
+// are computed once into LDS; a 16-lane group then rotates one (row, head) with each
+// lane holding 8 consecutive channels of both halves of the RoPE pairs, so q and K are
+// read and written as 16-byte chunks (a K chunk of the page is 8 channels of one
+// token). V is transposed through LDS so that its page chunks (8 tokens of one
+// channel) are written whole; chunks the quarter covers only in part are written
+// element by element.
+constexpr int RT_ROWS = 16;
+
+template <int D>
+__global__ __launch_bounds__(256) void k_rope_tile(RopeArgs a) {
+  constexpr int HALF = D / 2, HC = HALF / 8;  // 16-byte chunks per half head
+  constexpr int VR = D + 8;                   // padded bf16 row of the V tile
+  static_assert(D % 16 == 0 && HC <= 16, "head dim");
+  __shared__ __align__(16) bf16_t Vs[RT_ROWS * VR];
+  __shared__ __align__(16) float2 CS[RT_ROWS * HALF];  // (cos, sin) per row and pair
+  const int hk = blockIdx.y;
+  const int32_t* tl = a.tiles + 4 * blockIdx.x;
+  const int seq = tl[3];
+  const int r0 = RT_ROWS * blockIdx.z;
+  if (r0 >= tl[1]) return;
+  const int nrows = min(RT_ROWS, tl[1] - r0);
+  const int row0 = tl[0] + r0, pos0 = tl[2] + r0;
+  const int G = a.Hq / a.Hkv;
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int grp = lane >> 4, j = lane & 15;  // 16-lane group, chunk within the half
+  const bf16_t* X = (const bf16_t*)a.qkvg;
+  bf16_t* Q = (bf16_t*)a.q_out;
+
+  // angles p * theta^(-2i/d) in double, reduced modulo 2*pi before the float sin/cos
+  for (int c = threadIdx.x; c < nrows * HALF; c += 256) {
+    const int i = c / HALF, k = c % HALF;
+    double ang = (double)(pos0 + i) * a.freq[k];
+    ang -= 6.283185307179586 * rint(ang * 0.15915494309189535);
+    float sn, cs;
+    sincosf((float)ang, &sn, &cs);
+    CS[c] = make_float2(cs, sn);
+  }
+  // V rows -> LDS (16-byte chunks)
+  const int vcol0 = a.Hq * D + a.Hkv * D + hk * D;
+  for (int c = threadIdx.x; c < nrows * (D / 8); c += 256) {
+    const int i = c / (D / 8), k8 = c % (D / 8);
+    *(uint4*)(Vs + i * VR + 8 * k8) = *(const uint4*)(X + (size_t)(row0 + i) * a.Nqkvg + vcol0 + 8 * k8);
+  }
+  __syncthreads();
+
+  // rotation + norm of the q heads hk*G .. hk*G+G-1 and of K head hk, one item per group
+  const int items = nrows * (G + 1);
+  for (int it0 = wave * 4; it0 < items; it0 += 16) {
+    const int item = it0 + grp;
+    const bool act = item < items && j < HC;
+    const int i = act ? item / (G + 1) : 0, hi = act ? item % (G + 1) : 0;
+    const bool is_k = hi == G;
+    const int p = pos0 + i;
+    const int col0 = is_k ? a.Hq * D + hk * D : (hk * G + hi) * D;
+    float r1[8], r2[8];
+    float sq = 0.f;
+    if (act) {
+      const uint4 u1 = *(const uint4*)(X + (size_t)(row0 + i) * a.Nqkvg + col0 + 8 * j);
+      const uint4 u2 = *(const uint4*)(X + (size_t)(row0 + i) * a.Nqkvg + col0 + HALF + 8 * j);
+      const uint32_t w1[4] = {u1.x, u1.y, u1.z, u1.w}, w2[4] = {u2.x, u2.y, u2.z, u2.w};
+      const float2* cs = CS + i * HALF + 8 * j;
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        const float x1 = __uint_as_float((e & 1) ? (w1[e / 2] & 0xFFFF0000u) : (w1[e / 2] << 16));
+        const float x2 = __uint_as_float((e & 1) ? (w2[e / 2] & 0xFFFF0000u) : (w2[e / 2] << 16));
+        const float2 t = cs[e];
+        r1[e] = x1 * t.x - x2 * t.y;
+        r2[e] = x1 * t.y + x2 * t.x;
+        sq += r1[e] * r1[e] + r2[e] * r2[e];
+      }
+    }
+#pragma unroll
+    for (int m = 8; m >= 1; m >>= 1) sq += __shfl_xor(sq, m, 64);  // within the 16-lane group
+    if (!act) continue;
+    float sc = 1.f;
+    if (a.qk_norm) sc = inv_norm(sq);
+    uint32_t o1[4], o2[4];
+#pragma unroll
+    for (int e = 0; e < 8; e += 2) {
+      float a0 = r1[e] * sc, a1 = r1[e + 1] * sc, b0 = r2[e] * sc, b1 = r2[e + 1] * sc;
+      if (a.qk_norm) {
+        a0 *= a.s_qk[8 * j + e];
+        a1 *= a.s_qk[8 * j + e + 1];
+        b0 *= a.s_qk[HALF + 8 * j + e];
+        b1 *= a.s_qk[HALF + 8 * j + e + 1];
+      }
+      o1[e / 2] = pack_bf16x2(a0, a1);
+      o2[e / 2] = pack_bf16x2(b0, b1);
+    }
+    if (!is_k) {
+      bf16_t* q = Q + (size_t)(row0 + i) * a.Hq * D + (hk * G + hi) * D;
+      *(uint4*)(q + 8 * j) = make_uint4(o1[0], o1[1], o1[2], o1[3]);
+      *(uint4*)(q + HALF + 8 * j) = make_uint4(o2[0], o2[1], o2[2], o2[3]);
+    } else {
+      bf16_t* kb = kv_kblock(kv_page<bf16_t>(a.kv, seq, a.stream_idx, p), a.kv, hk);
+      *(uint4*)(kb + kv_k_off(p % PAGE, 8 * j, D)) = make_uint4(o1[0], o1[1], o1[2], o1[3]);
+      *(uint4*)(kb + kv_k_off(p % PAGE, HALF + 8 * j, D)) = make_uint4(o2[0], o2[1], o2[2], o2[3]);
+    }
+  }
+
+  // V chunks: (group of 8 positions, channel); whole chunks when the quarter holds all 8
+  const int g_lo = pos0 / 8, g_hi = (pos0 + nrows - 1) / 8;
+  for (int c = threadIdx.x; c < (g_hi - g_lo + 1) * D; c += 256) {
+    const int g8 = g_lo + c / D, ch = c % D;
+    const int p0 = 8 * g8;
+    bf16_t* vb = kv_vblock(kv_page<bf16_t>(a.kv, seq, a.stream_idx, p0), a.kv, hk);
+    bf16_t* dst = vb + kv_v_off(p0 % PAGE, ch, D);
+    if (p0 >= pos0 && p0 + 7 <= pos0 + nrows - 1) {
+      uint32_t u[4];
+#pragma unroll
+      for (int e = 0; e < 8; e += 2)
+        u[e / 2] = (uint32_t)Vs[(p0 + e - pos0) * VR + ch] | ((uint32_t)Vs[(p0 + e + 1 - pos0) * VR + ch] << 16);
+      *(uint4*)dst = make_uint4(u[0], u[1], u[2], u[3]);
+    } else {
+      for (int e = 0; e < 8; ++e) {
+        const int pp = p0 + e;
+        if (pp >= pos0 && pp < pos0 + nrows) dst[e] = Vs[(pp - pos0) * VR + ch];
+      }
+    }
+  }
+}
+
+hipError_t launch_rope_kv_tiles(const RopeArgs& a, hipStream_t st) {
+  if (a.n_tiles == 0) return hipSuccess;
+  if (a.in_f32 || a.kv.act != ACT_BF16 || !a.freq || !a.tiles || a.Hq % a.Hkv) return hipErrorInvalidValue;
+  dim3 grid(a.n_tiles, a.Hkv, 64 / RT_ROWS);
+  switch (a.d) {
+    case 64: hipLaunchKernelGGL(k_rope_tile<64>, grid, dim3(256), 0, st, a); break;
+    case 128: hipLaunchKernelGGL(k_rope_tile<128>, grid, dim3(256), 0, st, a); break;
+    case 160: hipLaunchKernelGGL(k_rope_tile<160>, grid, dim3(256), 0, st, a); break;
+    default: return hipErrorInvalidValue;
+  }
+  return hipGetLastError();
+}
+
 hipError_t launch_rope_kv(const RopeArgs& a, hipStream_t st) {
   if (a.M == 0) return hipSuccess;
   if (a.d > 256 || !a.freq) return hipErrorInvalidValue;
@@ -127,14 +264,25 @@ hipError_t launch_rope_kv(const RopeArgs& a, hipStream_t st) {
 }
 
 // ------------------------------------------------------------------- page tables
-__global__ void k_apply_deltas(int32_t* table, const int32_t* deltas, int n) {
-  const int i = blockIdx.x * blockDim.x + threadIdx.x;
-  if (i < n) table[deltas[2 * i]] = deltas[2 * i + 1];
+// One work-group per (table index, page) pair: install the entry and clear the newly
+// allocated page, so that cache entries no token has written yet hold zeros (kernels
+// may read them as MFMA operands with a zero weight; they must not be NaN or Inf).
+__global__ __launch_bounds__(256) void k_apply_deltas(int32_t* table, const int32_t* deltas, int n,
+                                                      uint4* pool, size_t page_chunks) {
+  const int i = blockIdx.x;
+  if (i >= n) return;
+  const int32_t page = deltas[2 * i + 1];
+  if (threadIdx.x == 0) table[deltas[2 * i]] = page;
+  uint4* p = pool + (size_t)page * page_chunks;
+  for (size_t c = threadIdx.x; c < page_chunks; c += 256) p[c] = make_uint4(0, 0, 0, 0);
 }
 
-hipError_t launch_apply_deltas(int32_t* table, const int32_t* deltas, int n, hipStream_t st) {
+hipError_t launch_apply_deltas(int32_t* table, const int32_t* deltas, int n, void* pool,
+                               size_t page_bytes, hipStream_t st) {
   if (n == 0) return hipSuccess;
-  hipLaunchKernelGGL(k_apply_deltas, dim3((n + 255) / 256), dim3(256), 0, st, table, deltas, n);
+  if (page_bytes % 16) return hipErrorInvalidValue;
+  hipLaunchKernelGGL(k_apply_deltas, dim3(n), dim3(256), 0, st, table, deltas, n, (uint4*)pool,
+                     page_bytes / 16);
   return hipGetLastError();
 }
 

@@ -85,8 +85,12 @@ struct RopeArgs {
   void* q_out = nullptr;        // act [M, Hq*d]
   KVLayout kv;
   int stream_idx = 0;           // (layer, slot) stream within the sequence
+  const int32_t* tiles = nullptr;  // prefill tiles [n_tiles][4]: row0, nrows, pos0, seq slot
+  int n_tiles = 0;
 };
 hipError_t launch_rope_kv(const RopeArgs& a, hipStream_t st);
+// Prefill form over the tiles (bf16 projection output, d in {64, 128, 160}).
+hipError_t launch_rope_kv_tiles(const RopeArgs& a, hipStream_t st);
 
 // ------------------------------------------------------------------------ attention
 struct AttnArgs {
@@ -124,7 +128,9 @@ hipError_t launch_swiglu(const float* gu, int splits, int M, int I, void* h, int
                          hipStream_t st);
 
 // ------------------------------------------------------------------ page table etc.
-hipError_t launch_apply_deltas(int32_t* table, const int32_t* deltas, int n, hipStream_t st);
+// Install page-table entries (pairs of flat table index, page) and zero those pages.
+hipError_t launch_apply_deltas(int32_t* table, const int32_t* deltas, int n, void* pool,
+                               size_t page_bytes, hipStream_t st);
 hipError_t launch_fill_kv(const KVLayout& kv, int seq_slot, int stream_idx, int pos0, int n,
                           const void* k, const void* v, hipStream_t st);
 hipError_t launch_quantize_mxfp8(const void* w, int w_bf16, int64_t rows, int64_t cols,

@@ -348,7 +348,7 @@ int flush_deltas(dory_ctx* ctx, hipStream_t st, size_t keep) {
     int r = upload(ctx, st, ctx->pending.data() + start, 2 * n);
     if (r) return r;
     HIPCHK(launch_apply_deltas((int32_t*)(ctx->ws + ctx->W.table), (const int32_t*)(ctx->ws + ctx->W.meta),
-                               (int)n, st), "apply_deltas");
+                               (int)n, ctx->pool, ctx->D.page_bytes, st), "apply_deltas");
     ctx->pending.resize(start);
   }
   return DORY_OK;
@@ -497,9 +497,12 @@ int run_layer(dory_ctx* ctx, hipStream_t st, const CallPlan& P, int l, int slot,
   ra.q_out = ws + W.q;
   ra.kv = kv_layout(ctx, l);
   ra.stream_idx = sidx;
+  ra.tiles = meta + 2 * c.max_rows;
+  ra.n_tiles = P.n_tiles;
   {
     Prof pr(ctx, st, DORY_KC_ROPE);
-    HIPCHK(launch_rope_kv(ra, st), "rope_kv");
+    const bool tiled = !ra.in_f32 && P.max_tile_rows > 1 && (D.d == 64 || D.d == 128 || D.d == 160);
+    HIPCHK(tiled ? launch_rope_kv_tiles(ra, st) : launch_rope_kv(ra, st), "rope_kv");
     pr.end(0, (double)M * (D.Nqkvg * (ra.in_f32 ? 4.0 * S : D.esz) + (2 * D.Nq + 2 * D.Nkv) * D.esz));
   }
 
@@ -723,7 +726,7 @@ int step(dory_ctx* ctx, hipStream_t st, int n, const int32_t* ids, const int32_t
   if (nd)
     HIPCHK(launch_apply_deltas((int32_t*)(ctx->ws + ctx->W.table),
                                (const int32_t*)(ctx->ws + ctx->W.meta) + 2 * R + 4 * ctx->D.max_tiles + ROPE_INTS,
-                               (int)nd, st), "apply_deltas");
+                               (int)nd, ctx->pool, ctx->D.page_bytes, st), "apply_deltas");
   return run_forward(ctx, st, P, x_in, y_out);
 }
 
