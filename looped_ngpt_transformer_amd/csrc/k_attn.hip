@@ -450,12 +450,10 @@ static hipError_t launch_decode(const AttnArgs& a, int n_pages, int max_sub, hip
 // Long key ranges: two register sets per wave, one wave per SIMD, up to 16 splits.
 // Short ranges (sliding windows, short contexts): one register set, three waves per SIMD,
 // a page per split, so that the whole range is requested at once.
-#ifndef DORY_DECODE_SHORT_PAGES
-#define DORY_DECODE_SHORT_PAGES 32
-#endif
+constexpr int DECODE_SHORT_PAGES = 32;
 template <int D>
 static hipError_t launch_decode_d(const AttnArgs& a, int n_pages, hipStream_t st) {
-  if (n_pages > DORY_DECODE_SHORT_PAGES) return launch_decode<D, 2, 1>(a, n_pages, 16, st);
+  if (n_pages > DECODE_SHORT_PAGES) return launch_decode<D, 2, 1>(a, n_pages, 16, st);
   return launch_decode<D, 1, 3>(a, n_pages, 64, st);
 }
 

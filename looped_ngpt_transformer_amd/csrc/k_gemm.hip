@@ -27,12 +27,12 @@ __device__ __forceinline__ float e8m0_to_f32(uint32_t e) {
 }
 
 // 4 E4M3 bytes of `word` times the group scale -> 4 bf16 packed in 2 words (byte i
-// of the word is element i). Exact whenever the product is a bf16 value.
+// of the word is element i), with gfx950's scaled conversion (two codes per
+// instruction). Exact whenever the product is a bf16 value, which holds for every
+// code times a power-of-two group scale outside the extreme E8M0 range.
 __device__ __forceinline__ void dq4(uint32_t word, float sc, uint32_t* out) {
-  const f32x2 lo = __builtin_amdgcn_cvt_pk_f32_fp8((int)word, false);
-  const f32x2 hi = __builtin_amdgcn_cvt_pk_f32_fp8((int)word, true);
-  out[0] = (uint32_t)f2bf(lo.x * sc) | ((uint32_t)f2bf(lo.y * sc) << 16);
-  out[1] = (uint32_t)f2bf(hi.x * sc) | ((uint32_t)f2bf(hi.y * sc) << 16);
+  out[0] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8((int)word, sc, false));
+  out[1] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8((int)word, sc, true));
 }
 
 // Epilogue: lane holds C[m = i*16 + 4*(lane>>4) + r][n = j*16 + (lane&15)] of its wave tile.
@@ -288,10 +288,12 @@ typedef __attribute__((address_space(3))) void* lds_void_t;
 typedef __attribute__((address_space(1))) void* gbl_void_t;
 
 // LDS position of 16-byte chunk `chunk` of tile row `row` (CPR chunks per row): XOR
-// swizzle so the 16 rows an MFMA fragment read touches fall in distinct banks.
+// swizzle so that the 16 consecutive rows one LDS cycle serves for a fragment read
+// (same logical chunk) land in 16 distinct 16-byte bank groups: with 128-byte rows, row
+// parity picks the half of the 64 banks and (row / 2) % 8 the group within it.
 template <int CPR>
 __device__ __forceinline__ int swzc(int row, int chunk) {
-  return row * CPR + (chunk ^ (CPR == 8 ? (row & 7) : ((row >> 1) & 3)));
+  return row * CPR + (chunk ^ (CPR == 8 ? ((row >> 1) & 7) : ((row >> 1) & 3)));
 }
 
 // s_waitcnt vmcnt(n) for a run-time n <= 31 (other counters untouched)
@@ -454,18 +456,19 @@ __global__ __launch_bounds__(256) void k_gemm_f32(GemmArgs g) {
 }
 
 // ------------------------------------------------------------------------ dispatch
-#ifndef DORY_SPLITK_WG
-#define DORY_SPLITK_WG 400
-#endif
-#ifndef DORY_SPLITK_MINK
-#define DORY_SPLITK_MINK 128
-#endif
+constexpr int SPLITK_WG = 400;    // work-groups a decode GEMM aims for
+constexpr int SPLITK_MINK = 128;  // shortest K range of one split
 int gemm_pick_splits(int M, int N, int K, int wfmt) {
-  // small-M (decode) tiles are BN = 64 wide; split K until there are enough work-groups
-  // to keep the weight stream in flight (each split a multiple of 64, not too short)
-  const int tiles = (N / 64) * ((M + 127) / 128);
+  // small-M (decode) tiles are BN = 64 wide (128 for MXFP8); split K until there are
+  // enough work-groups to keep the weight stream in flight (each split a multiple of 64,
+  // not too short)
+  int tiles = (N / 64) * ((M + 127) / 128), cap = 32;
+  if (wfmt == W_MXFP8 && N % 128 == 0) {  // 32 or 64 activation rows per tile, <= 8 splits
+    tiles = (N / 128) * ((M + (M <= 32 ? 31 : 63)) / (M <= 32 ? 32 : 64));
+    cap = 8;
+  }
   int s = 1;
-  while (s < 32 && tiles * s < DORY_SPLITK_WG && (K / BK) % (2 * s) == 0 && K / (2 * s) >= DORY_SPLITK_MINK) s *= 2;
+  while (s < cap && tiles * s < SPLITK_WG && (K / BK) % (2 * s) == 0 && K / (2 * s) >= SPLITK_MINK) s *= 2;
   return s;
 }
 
@@ -593,6 +596,132 @@ __global__ __launch_bounds__(WMW * WNW * 64) void k_gemm_pipe32(GemmArgs g) {
   gemm_epilogue32<BM, BN, WMW, WNW, EPI>(g, acc, n_tile, m0, wm, wn, lane);
 }
 
+// MXFP8 (W8A16) split-K tiles for decode-sized M, on v_mfma_f32_32x32x16_bf16. The
+// bf16 activations and the E4M3 weight codes stream straight into an LDS ring of
+// 64-wide K slices; each lane turns its 8 codes of a B fragment into bf16 just before
+// the MFMA (scaled fp8 -> bf16 conversion by the group's 2^e, exact), so the weights cross HBM
+// once at one byte each. The E8M0 scales of the next slice are loaded into registers a
+// slice ahead. Output: fp32 split-K partials (EPI_PARTIAL).
+template <int BM, int BN, int WMW, int WNW, int STAGES>
+__global__ __launch_bounds__(GT) void k_gemm_mx32(GemmArgs g) {
+  constexpr int PBK = 64;
+  constexpr int TM = BM / WMW, TN = BN / WNW;
+  constexpr int FM = TM / 32, FN = TN / 32;
+  constexpr int ACH = BM * 8, BCH = BN * 4;   // 16-byte chunks of A (bf16) / B (codes)
+  constexpr int NINST = (ACH + BCH) / 64;
+  constexpr int MAXI = (NINST + 3) / 4;
+  static_assert(WMW * WNW == 4 && TM % 32 == 0 && TN % 32 == 0, "tile");
+  static_assert(ACH % 64 == 0 && BCH % 64 == 0, "tile rows");
+  static_assert((STAGES - 2) * MAXI <= 31 && STAGES >= 2, "pipeline");
+  __shared__ __align__(16) uint4 sm[STAGES][ACH + BCH];
+
+  const int t = threadIdx.x, lane = t & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(t >> 6);
+  const int wm = wave / WNW, wn = wave % WNW;
+  const int n_tile = blockIdx.x, m0 = blockIdx.y * BM, split = blockIdx.z;
+  const int Ks = g.K / g.splits, kbeg = split * Ks, nk = Ks / PBK;
+  const bf16_t* A = (const bf16_t*)g.A;
+  const uint8_t* B = (const uint8_t*)g.B;
+  const int my_inst = (NINST - wave + 3) / 4;
+  const int l32 = lane & 31, lh = lane >> 5;
+
+  auto issue = [&](int slot, int k0) {
+#pragma unroll
+    for (int q = 0; q < MAXI; ++q) {
+      const int inst = wave + 4 * q;
+      if (inst < NINST) {
+        const int sidx = inst * 64 + lane;
+        const void* src;
+        if (sidx < ACH) {  // A row r, chunk c (8 bf16)
+          const int r = sidx >> 3, c = swzc<8>(r, sidx & 7) - r * 8;
+          src = A + (size_t)min(m0 + r, g.M - 1) * g.lda + k0 + 8 * c;
+        } else {           // B row r, chunk c (16 codes); chunk slot c ^ ((r >> 2) & 3)
+          const int s2 = sidx - ACH, r = s2 >> 2, c = (s2 & 3) ^ ((r >> 2) & 3);
+          src = B + (size_t)(n_tile * BN + r) * g.K + k0 + 16 * c;
+        }
+        __builtin_amdgcn_global_load_lds((gbl_void_t)src, (lds_void_t)(&sm[slot][inst * 64]), 16, 0, 0);
+      }
+    }
+  };
+  // E8M0 scales of B fragment j for the two 32-groups of slice k0
+  auto ldscale = [&](int k0, uint32_t (&sc)[FN][2]) {
+#pragma unroll
+    for (int j = 0; j < FN; ++j) {
+      const int n = n_tile * BN + wn * TN + j * 32 + l32;
+      const uint8_t* p = g.Bs + (size_t)n * (g.K / 32) + k0 / 32;
+      sc[j][0] = p[0];
+      sc[j][1] = p[1];
+    }
+  };
+
+  f32x16 acc[FM][FN];
+#pragma unroll
+  for (int i = 0; i < FM; ++i)
+#pragma unroll
+    for (int j = 0; j < FN; ++j)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.f;
+
+  // The scale loads of slice it+1 are issued after the tile loads of this step, so the
+  // wait below (which counts only tile loads as newer than tile it) is conservative.
+  uint32_t scn[FN][2];
+#pragma unroll
+  for (int st = 0; st < STAGES - 1; ++st)
+    if (st < nk) issue(st, kbeg + PBK * st);
+  ldscale(kbeg, scn);
+  for (int it = 0; it < nk; ++it) {
+    wait_vmcnt(min(STAGES - 2, nk - 1 - it) * my_inst);
+    __syncthreads();
+    if (it + STAGES - 1 < nk) issue((it + STAGES - 1) % STAGES, kbeg + PBK * (it + STAGES - 1));
+    uint32_t sc[FN][2];
+#pragma unroll
+    for (int j = 0; j < FN; ++j) sc[j][0] = scn[j][0], sc[j][1] = scn[j][1];
+    if (it + 1 < nk) ldscale(kbeg + PBK * (it + 1), scn);
+    const uint4* As = sm[it % STAGES];
+    const unsigned char* Bb = (const unsigned char*)(As + ACH);
+#pragma unroll
+    for (int ks = 0; ks < PBK / 16; ++ks) {
+      bf16x8 af[FM], bfr[FN];
+#pragma unroll
+      for (int i = 0; i < FM; ++i)
+        af[i] = __builtin_bit_cast(bf16x8, As[swzc<8>(wm * TM + i * 32 + l32, 2 * ks + lh)]);
+#pragma unroll
+      for (int j = 0; j < FN; ++j) {
+        const int r = wn * TN + j * 32 + l32;
+        const uint2 cw = *(const uint2*)(Bb + (r * 4 + (ks ^ ((r >> 2) & 3))) * 16 + 8 * lh);
+        const float scf = e8m0_to_f32(sc[j][ks >> 1]);
+        uint32_t v[4];
+        dq4(cw.x, scf, v);
+        dq4(cw.y, scf, v + 2);
+        bfr[j] = __builtin_bit_cast(bf16x8, make_uint4(v[0], v[1], v[2], v[3]));
+      }
+#pragma unroll
+      for (int i = 0; i < FM; ++i)
+#pragma unroll
+        for (int j = 0; j < FN; ++j)
+          acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[i], bfr[j], acc[i][j], 0, 0, 0);
+    }
+  }
+  // split-K partials: register r of lane l = C[8 (r / 4) + 4 (l / 32) + r % 4][l % 32]
+  float* C = (float*)g.C + (size_t)split * g.M * g.ldc;
+#pragma unroll
+  for (int i = 0; i < FM; ++i)
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+      const int m = m0 + wm * TM + i * 32 + 8 * (r >> 2) + 4 * lh + (r & 3);
+      if (m >= g.M) continue;
+#pragma unroll
+      for (int j = 0; j < FN; ++j) C[(size_t)m * g.ldc + n_tile * BN + wn * TN + j * 32 + l32] = acc[i][j][r];
+    }
+}
+
+template <int BM, int BN, int WMW, int WNW, int STAGES>
+static hipError_t go_mx(const GemmArgs& g, hipStream_t st) {
+  dim3 grid(g.N / BN, (g.M + BM - 1) / BM, g.splits);
+  hipLaunchKernelGGL((k_gemm_mx32<BM, BN, WMW, WNW, STAGES>), grid, dim3(GT), 0, st, g);
+  return hipGetLastError();
+}
+
 template <int BM, int BN, int WMW, int WNW, int EPI, int STAGES, int PBK = 32>
 static hipError_t go_pipe(const GemmArgs& g, hipStream_t st, int ntiles_n) {
   dim3 grid(ntiles_n, (g.M + BM - 1) / BM, g.splits);
@@ -612,16 +741,12 @@ static hipError_t go_pipe32(const GemmArgs& g, hipStream_t st, int ntiles_n) {
 
 template <int EPI>
 static hipError_t go_big(const GemmArgs& g, hipStream_t st, int n) {
-#ifndef DORY_BIG_WAVES
-#define DORY_BIG_WAVES 8
-#endif
   if (n % 256 == 0 && (EPI == EPI_SWIGLU || n / 256 * ((g.M + 255) / 256) >= 256)) {
-    if (DORY_BIG_WAVES == 8) return go_pipe32<256, 256, 2, 4, EPI, 2>(g, st, n / 256);
-    return go_pipe32<256, 256, 2, 2, EPI, 2>(g, st, n / 256);
+    return go_pipe32<256, 256, 2, 4, EPI, 2>(g, st, n / 256);
   }
   if constexpr (EPI != EPI_SWIGLU)
     if (n % 160 == 0) return go_pipe32<256, 160, 4, 1, EPI, 2>(g, st, n / 160);
-  if (n % 256 == 0) return go_pipe32<256, 256, 2, 2, EPI, 2>(g, st, n / 256);
+  if (n % 256 == 0) return go_pipe32<256, 256, 2, 4, EPI, 2>(g, st, n / 256);
   return hipErrorNotSupported;
 }
 
@@ -653,6 +778,10 @@ hipError_t launch_gemm(const GemmArgs& gin, hipStream_t st) {
         if (g.M <= 32) return go_pipe<32, 64, 1, 4, EPI_PARTIAL, 4, 64>(g, st, g.N / 64);
         if (g.M <= 64) return go_pipe<64, 64, 1, 4, EPI_PARTIAL, 4, 64>(g, st, g.N / 64);
         return go_pipe<128, 64, 1, 4, EPI_PARTIAL, 3, 64>(g, st, g.N / 64);
+      }
+      if (g.N % 128 == 0) {  // MXFP8: 128 weight rows per tile
+        if (g.M <= 32) return go_mx<32, 128, 1, 4, 4>(g, st);
+        return go_mx<64, 128, 1, 4, 4>(g, st);
       }
       if (g.M <= 32) return go<32, 64, 1, 4, EPI_PARTIAL>(g, st, g.N / 64);
       if (g.M <= 64) return go<64, 64, 1, 4, EPI_PARTIAL>(g, st, g.N / 64);

@@ -132,6 +132,16 @@ def test_mxfp8_small_forward():
     _run_case(S, 2, "last_loop", sched, max_rows=256, max_seq_len=256, max_seqs=1)
 
 
+@pytest.mark.parametrize("batch", [40, 128])
+def test_mxfp8_decode_batches(batch):
+    """MXFP8 weights at decode batch sizes (split-K tiles of 64 and 128 rows): prefill
+    `batch` short sequences in one call, then one decode step for all of them."""
+    S = dict(PSMALL, weight_format="mxfp8")
+    sched = [("prefill", [(i, xin(S, 2 + i % 3, 300 + i)) for i in range(batch)]),
+             ("decode", [(i, xin(S, 1, 600 + i)) for i in range(batch)])]
+    _run_case(S, 2, "last_loop", sched, max_rows=512, max_seq_len=16, max_seqs=batch, sharp=True)
+
+
 def test_bitwise_deterministic_and_batch_permutation():
     S = PSMALL
     w = gpu_weights(S, 3)
