@@ -9,8 +9,12 @@
 // x is saved and u_1 = N(x + x); at the end of loop t, s_t = N(.) and, unless t = k,
 // u_{t+1} = N(s_t + x).
 //
-// All of the row's loads (partials, state, rates, x) are issued first; the 2560-wide
-// reductions are wave shuffles plus one LDS exchange, the row stays in registers.
+// All of the row's loads (partials, state, rates, x) are issued first. Every norm the
+// update and the boundary need follows from sums over the row taken in one pass
+// (wave shuffles plus one LDS exchange): with t = (1 - a) s + a y / ||y||,
+//   ||t||^2 = sum((1-a)s)^2 + 2 sum((1-a)s a y) / ||y|| + sum(a y)^2 / ||y||^2,
+// and for u = N(s_t + x), s_t . x = (sum((1-a)s x) + sum(a y x) / ||y||) / ||t||. The row
+// stays in registers.
 #include "common.h"
 #include "kernels.h"
 
@@ -21,75 +25,84 @@ namespace dory {
 template <typename SB, int UPD_THREADS>
 __global__ __launch_bounds__(UPD_THREADS) void k_update(UpdateArgs u) {
   constexpr int UPD_MAXPER = 4096 / UPD_THREADS;  // H <= 4096
-  __shared__ float red[UPD_THREADS / WAVE];
+  constexpr int NW = UPD_THREADS / WAVE;
+  constexpr int NS = 7;  // sums: yy, A, B, C, (1-a)s.x, a y.x, x.x
+  __shared__ float red[NW][NS];
   const int m = blockIdx.x;
   const int H = u.H;
   const size_t row = (size_t)m * H;
   const bool need_x = u.bnd == BND_LOOP_CONTINUE;
-  float v[UPD_MAXPER], sv[UPD_MAXPER], av[UPD_MAXPER], xv[UPD_MAXPER];
-  float sq = 0.f;
+  float yv[UPD_MAXPER], sv[UPD_MAXPER], av[UPD_MAXPER], xv[UPD_MAXPER];
+  float acc[NS] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
 #pragma unroll
   for (int k = 0; k < UPD_MAXPER; ++k) {
     const int i = threadIdx.x + k * UPD_THREADS;
     float y = 0.f;
     sv[k] = av[k] = xv[k] = 0.f;
     if (i < H) {
-      for (int s = 0; s < u.splits; ++s) y += u.y[(size_t)s * u.M * H + row + i];
+      for (int sp = 0; sp < u.splits; ++sp) y += u.y[(size_t)sp * u.M * H + row + i];
       sv[k] = u.s[row + i];
       av[k] = u.alpha[i];
       if (need_x) xv[k] = u.x[row + i];
     }
-    v[k] = y;
-    sq += y * y;
+    yv[k] = y;
+    const float bs = (1.f - av[k]) * sv[k], ay = av[k] * y;
+    acc[0] += y * y;
+    acc[1] += bs * bs;
+    acc[2] += bs * ay;
+    acc[3] += ay * ay;
+    acc[4] += bs * xv[k];
+    acc[5] += ay * xv[k];
+    acc[6] += xv[k] * xv[k];
   }
-  const float ny = inv_norm(block_sum<UPD_THREADS / WAVE>(sq, red));
-  sq = 0.f;
 #pragma unroll
-  for (int k = 0; k < UPD_MAXPER; ++k) {
-    const float t = (1.f - av[k]) * sv[k] + av[k] * (v[k] * ny);  // zero beyond H
-    v[k] = t;
-    sq += t * t;
+  for (int q = 0; q < NS; ++q) acc[q] = wave_sum(acc[q]);
+  if ((threadIdx.x & (WAVE - 1)) == 0)
+#pragma unroll
+    for (int q = 0; q < NS; ++q) red[threadIdx.x / WAVE][q] = acc[q];
+  __syncthreads();
+  float tot[NS];
+#pragma unroll
+  for (int q = 0; q < NS; ++q) {
+    tot[q] = 0.f;
+#pragma unroll
+    for (int w = 0; w < NW; ++w) tot[q] += red[w][q];
   }
-  float n = inv_norm(block_sum<UPD_THREADS / WAVE>(sq, red));
-#pragma unroll
-  for (int k = 0; k < UPD_MAXPER; ++k) v[k] *= n;
-
+  const float ny = inv_norm(tot[0]);
+  const float tt = fmaxf(tot[1] + 2.f * tot[2] * ny + tot[3] * ny * ny, 0.f);  // ||t||^2
+  const float nt = inv_norm(tt);
+  float scale = nt;          // s' = t * nt
+  float norm_sp = sqrtf(tt) * nt;  // ||s'||
+  float add_x = 0.f;         // coefficient of x in the result
   if (u.bnd == BND_LOOP_CONTINUE || u.bnd == BND_LOOP_FINAL) {  // s_t = N(F(u_t))
-    sq = 0.f;
-#pragma unroll
-    for (int k = 0; k < UPD_MAXPER; ++k) sq += v[k] * v[k];
-    n = inv_norm(block_sum<UPD_THREADS / WAVE>(sq, red));
-#pragma unroll
-    for (int k = 0; k < UPD_MAXPER; ++k) v[k] *= n;
+    const float n2 = inv_norm(norm_sp * norm_sp);
+    scale *= n2;
+    norm_sp *= n2;
   }
-  if (u.bnd == BND_SAVE_X || u.bnd == BND_LOOP_CONTINUE) {  // u = N(s + x)
-    sq = 0.f;
+  if (u.bnd == BND_LOOP_CONTINUE) {  // u = N(s_t + x)
+    const float dot = (tot[4] + tot[5] * ny) * scale;  // s_t . x
+    const float n3 = inv_norm(norm_sp * norm_sp + 2.f * dot + tot[6]);
+    scale *= n3;
+    add_x = n3;
+  } else if (u.bnd == BND_SAVE_X) {  // x = s'; u = N(s' + s')
+    const float n3 = inv_norm(4.f * norm_sp * norm_sp);
+    float* X = u.x;
 #pragma unroll
     for (int k = 0; k < UPD_MAXPER; ++k) {
       const int i = threadIdx.x + k * UPD_THREADS;
-      if (i < H) {
-        float x;
-        if (u.bnd == BND_SAVE_X) {
-          x = v[k];
-          u.x[row + i] = x;
-        } else {
-          x = xv[k];
-        }
-        v[k] += x;
-        sq += v[k] * v[k];
-      }
+      if (i < H) X[row + i] = ((1.f - av[k]) * sv[k] + av[k] * yv[k] * ny) * nt;
     }
-    n = inv_norm(block_sum<UPD_THREADS / WAVE>(sq, red));
-#pragma unroll
-    for (int k = 0; k < UPD_MAXPER; ++k) v[k] *= n;
+    scale *= 2.f * n3;
   }
   SB* sb = (SB*)u.sb;
 #pragma unroll
   for (int k = 0; k < UPD_MAXPER; ++k) {
     const int i = threadIdx.x + k * UPD_THREADS;
     if (i < H) {
-      u.s_out[row + i] = v[k];
-      if (sb) st<SB>(sb, row + i, v[k]);
+      const float t = (1.f - av[k]) * sv[k] + av[k] * yv[k] * ny;
+      const float v = t * scale + add_x * xv[k];
+      u.s_out[row + i] = v;
+      if (sb) st<SB>(sb, row + i, v);
     }
   }
 }
