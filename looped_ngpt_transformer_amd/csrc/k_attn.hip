@@ -291,12 +291,13 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(WPE))) void
     mt = fmaxf(mt, __shfl_xor(mt, 16, 64));
     mt = fmaxf(mt, __shfl_xor(mt, 32, 64));
     const float m_new = fmaxf(m_run, mt);
-    const float corr = m_run == -INFINITY ? 0.f : exp2f(m_run - m_new);
+    const float corr = m_run == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(m_run - m_new);
+    const float m_ref = m_new == -INFINITY ? 0.f : m_new;  // no key seen yet: p = exp2(-inf) = 0
     float pe[8];
     float ps = 0.f;
 #pragma unroll
     for (int e = 0; e < 8; ++e) {
-      pe[e] = sv[e] == -INFINITY ? 0.f : exp2f(sv[e] - m_new);
+      pe[e] = __builtin_amdgcn_exp2f(sv[e] - m_ref);
       ps += pe[e];
     }
     ps += __shfl_xor(ps, 16, 64);

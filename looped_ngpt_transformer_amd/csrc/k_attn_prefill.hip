@@ -155,11 +155,13 @@ __global__ __launch_bounds__(PF_THREADS) void k_attn_prefill(AttnArgs a) {
     // S^T[key 32 kb + 8 (r / 4) + 4 lh + r % 4][query l32]
     f32x16 st[2];
 #pragma unroll
-    for (int kb = 0; kb < 2; ++kb) {
+    for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
       for (int r = 0; r < 16; ++r) st[kb][r] = 0.f;
 #pragma unroll
-      for (int c = 0; c < KS; ++c) {
+    for (int c = 0; c < KS; ++c) {  // the two key blocks interleaved: independent chains
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb) {
         const int off = (2 * kb * DC + (c >> 1)) * KGS + (c & 1) * 32 * 16;
         const bf16x8 kf = *(const bf16x8*)(st0 + koff + off);
         st[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf, qf[c], st[kb], 0, 0, 0);
@@ -173,22 +175,23 @@ __global__ __launch_bounds__(PF_THREADS) void k_attn_prefill(AttnArgs a) {
 #pragma unroll
       for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          st[kb][r] *= sl2;
-          mt = fmaxf(mt, st[kb][r]);
-        }
+        for (int r = 0; r < 16; ++r) mt = fmaxf(mt, st[kb][r]);
     } else {
+      const int wlim = full ? 0x7fffffff : a.window;  // keys visible at 0 <= qpos - kpos < wlim
+      const int d0 = qv ? qpos - pg * PAGE - 4 * lh : -1;
 #pragma unroll
       for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
-          const int kpos = pg * PAGE + 32 * kb + 8 * (r >> 2) + 4 * lh + (r & 3);
-          const bool vis = qv && kpos <= qpos && (full || qpos - kpos < a.window);
-          st[kb][r] = vis ? st[kb][r] * sl2 : -INFINITY;
+          const int dlt = d0 - (32 * kb + 8 * (r >> 2) + (r & 3));  // qpos - kpos
+          const bool vis = (dlt >= 0) & (dlt < wlim);
+          st[kb][r] = vis ? st[kb][r] : -INFINITY;
           mt = fmaxf(mt, st[kb][r]);
         }
     }
-    mt = fmaxf(mt, __shfl_xor(mt, 32, 64));
+    // raw logits so far: the running maximum is kept in scaled (log2) units, the scale
+    // being positive, and the scale is applied inside the exponent's FMA
+    mt = fmaxf(mt, __shfl_xor(mt, 32, 64)) * sl2;
     const float m_new = fmaxf(m_run, mt);
     // a query that has seen no visible key yet keeps m = -inf; its (all -inf) logits
     // give p = exp2(-inf) = 0 against a finite reference instead of NaN
@@ -198,13 +201,13 @@ __global__ __launch_bounds__(PF_THREADS) void k_attn_prefill(AttnArgs a) {
     for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
-        const float p = exp2f(st[kb][r] - m_ref);
+        const float p = __builtin_amdgcn_exp2f(fmaf(st[kb][r], sl2, -m_ref));  // exp2(-inf) = 0
         st[kb][r] = p;
         ps += p;
       }
     ps += __shfl_xor(ps, 32, 64);
     if (!__all(m_new == m_run)) {  // rescale only when some query's maximum moved
-      const float corr = m_run == -INFINITY ? 0.f : exp2f(m_run - m_new);
+      const float corr = m_run == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(m_run - m_new);
       l_run *= corr;
 #pragma unroll
       for (int cb = 0; cb < CB; ++cb) o[cb] *= corr;
@@ -223,9 +226,9 @@ __global__ __launch_bounds__(PF_THREADS) void k_attn_prefill(AttnArgs a) {
     }
     // O^T[channel 32 cb + 8 (r / 4) + 4 lh + r % 4][query l32] += V^T P^T
 #pragma unroll
-    for (int cb = 0; cb < CB; ++cb) {
+    for (int s = 0; s < 4; ++s) {  // the CB output blocks interleaved: independent chains
 #pragma unroll
-      for (int s = 0; s < 4; ++s) {
+      for (int cb = 0; cb < CB; ++cb) {
         const unsigned char* vr = st0 + voff + ((s >> 1) * CB16 + 2 * cb) * VGS + (2 * (s & 1)) * 16 * 16;
         const uint2 lo = *(const uint2*)vr;
         const uint2 hi = *(const uint2*)(vr + 16 * 16);
