@@ -53,7 +53,7 @@ def parse():
     ap.add_argument("--tokens", type=int, default=None, help="prefill length (P, L)")
     ap.add_argument("--context", type=int, default=None, help="seeded KV context (D, Q)")
     ap.add_argument("--batch", type=int, default=None, help="decode batch (D, Q)")
-    ap.add_argument("--cpu-rows", type=int, default=256)
+    ap.add_argument("--cpu-rows", type=int, default=768)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--copy-probe", action="store_true",
                     help="run out = src * 1 over 1 GiB first (counter calibration for rocprofv3 --pmc)")
@@ -73,15 +73,16 @@ def source_digest(*names):
     return h.hexdigest()[:16]
 
 
-def measured_traffic(key, sources):
+def measured_traffic(key, workload, sources):
     """HBM bytes per launch from the committed counter summary (FETCH_SIZE + WRITE_SIZE,
-    scaled by the copy-probe calibration), or None when absent or taken on other code."""
+    scaled by the copy-probe calibration), or None when absent, taken on another
+    workload or taken on other code."""
     try:
         with open(TRAFFIC_FILE) as f:
             t = json.load(f)[key]
     except (OSError, KeyError, ValueError):
         return None
-    if t.get("source_digest") != source_digest(*sources):
+    if t.get("bench_workload") != workload or t.get("source_digest") != source_digest(*sources):
         return None
     return t.get("bytes_per_launch")
 
@@ -90,21 +91,21 @@ def kernel_stats(rt, D):
     return {D.KC_NAMES[k]: D.dory_profile_read(rt.ctx, k) for k in D.KC_NAMES}
 
 
-def roofline_of(stats, kind):
+def roofline_of(stats, kind, workload):
     if kind == "mfma":
         g = stats["gemm"]
         ach = g["flops"] / (g["ms"] / 1e3) / 1e12
         return {"bound": "mfma", "kernel": "gemm (bf16 MFMA projections)",
                 "achieved": round(ach, 1), "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
                 "frac": round(ach / PEAK_BF16_TFLOPS, 4),
-                "traffic": measured_traffic("prefill_gemm", ["k_gemm.hip", "common.h", "kernels.h"]),
+                "traffic": measured_traffic("prefill_gemm", workload, ["k_gemm.hip", "common.h", "kernels.h"]),
                 "launches": g["launches"], "avg_launch_us": round(1e3 * g["ms"] / g["launches"], 2)}
     a = stats["attention"]
     ach = a["bytes"] / (a["ms"] / 1e3) / 1e9
     return {"bound": "hbm", "kernel": "attention (paged KV, split over keys)",
             "achieved": round(ach, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
             "frac": round(ach / PEAK_HBM_GBS, 4),
-            "traffic": measured_traffic("decode_attention", ["k_attn.hip", "common.h", "kernels.h"]),
+            "traffic": measured_traffic("decode_attention", workload, ["k_attn.hip", "common.h", "kernels.h"]),
             "launches": a["launches"], "avg_launch_us": round(1e3 * a["ms"] / a["launches"], 2)}
 
 
@@ -195,7 +196,7 @@ def bench_prefill(args, torch, synth, D, DoryRuntime):
         "config": {"workload": WORKLOAD_TEXT[wl], "tokens": tokens, "loops": k, "kv_mode": mode,
                    "executed_layers": shape["n_in"] + shape["n_out"] + k * shape["n_rec"],
                    "chunk": chunk or tokens},
-        "roofline": roofline_of(stats, "mfma"),
+        "roofline": roofline_of(stats, "mfma", wl),
         "kernels": {n: {"launches": s["launches"], "ms": round(s["ms"], 3)} for n, s in brk.items()},
     }
     if len(ks) > 1:
@@ -275,7 +276,7 @@ def bench_decode(args, torch, synth, D, DoryRuntime):
         "config": {"workload": WORKLOAD_TEXT[wl], "batch": batch, "context": ctx_len, "loops": k,
                    "kv_mode": mode, "weights": shape["weight_format"],
                    "executed_layers": shape["n_in"] + shape["n_out"] + k * shape["n_rec"]},
-        "roofline": roofline_of(stats, "hbm"),
+        "roofline": roofline_of(stats, "hbm", wl),
         "step_hbm_gbs": round(tot_bytes / dt / 1e9, 1),
         "kv_bytes_in_use": kvb,
         "kernels": {n: {"launches": s["launches"], "ms": round(s["ms"], 3),

@@ -9,15 +9,16 @@
 // waves, wave = (query head g of the group, 32-row half of the tile), two waves per
 // SIMD. Per 64-key KV page, with v_mfma_f32_32x32x16_bf16 (on gfx950 about 1.5x the
 // rate of the 16x16x32 form):
-//   S^T = K Q^T   (A = K rows from LDS, B = Q in registers): two 32-key blocks,
+//   S^T = K Q^T   (A = K rows from LDS, B = Q in registers): two 32-key blocks whose
+//   rows are read in the key order 16 (r / 16) + 8 ((r / 4) % 2) + 4 ((r / 8) % 2) + r % 4,
+//   so that each lane's eight accumulators of a 16-key step hold 8 consecutive keys;
 //   online softmax per query in registers (lanes l and l + 32 share query l % 32),
-//   O^T += V^T P^T (A = V^T from LDS, B = P straight from the S^T accumulators: lane
-//   half h holds keys 4h..4h+3 and 8+4h..8+4h+3 of each 16-key group, which is a valid
-//   k-ordering of the MFMA when V^T is read with the same key permutation).
+//   O^T += V^T P^T (A = V^T from LDS, one 16-byte chunk of 8 consecutive keys per lane;
+//   B = P straight from the S^T accumulators).
 // The page's K and V blocks are stored as 1 KiB groups of 16-byte chunks in MFMA
 // fragment order; they go straight from HBM into LDS (global_load_lds, three stages:
-// two pages in flight while one is consumed), each group at a padded stride so that the
-// 32x32 fragment reads are free of bank conflicts. Keys beyond the chunk's last position
+// two pages in flight while one is consumed), the K groups at a padded stride so that
+// the 32x32 fragment reads are free of bank conflicts. Keys beyond the chunk's last position
 // are masked out of the softmax; their V entries are multiplied by zero probabilities
 // and hold zeros or stale finite values (pages are cleared when first allocated).
 #include <type_traits>
@@ -58,10 +59,11 @@ __global__ __launch_bounds__(PF_THREADS) void k_attn_prefill(AttnArgs a) {
   constexpr int DC = D / 32;       // 32-channel chunks of a K fragment group
   constexpr int CB16 = D / 16;     // 16-channel blocks of V
   constexpr int NG = D / 8;        // 1 KiB groups per K (or V) block of one head
-  // padded group strides: K fragments read two groups DC apart, V fragments two groups
-  // 1 apart, in the same LDS cycle
+  // K fragments read two groups DC apart in the same LDS cycle: pad their stride so the
+  // two land on opposite halves of the banks. V fragments read 256 contiguous bytes per
+  // 16 lanes.
   constexpr int KGS = 1024 + (DC == 5 ? 128 : 128 / DC);
-  constexpr int VGS = 1024 + 8;
+  constexpr int VGS = 1024;
   constexpr int STAGE = NG * (KGS + VGS);  // bytes per page stage
   constexpr int NSTAGE = 3;
   constexpr int GPW = (2 * NG + PF_WAVES - 1) / PF_WAVES;  // load instructions per wave per page
@@ -133,12 +135,14 @@ __global__ __launch_bounds__(PF_THREADS) void k_attn_prefill(AttnArgs a) {
   const int my_inst = __builtin_amdgcn_readfirstlane((2 * NG - w + PF_WAVES - 1) / PF_WAVES);
 
   // per-lane parts of the fragment addresses (bytes within a stage)
-  //   K fragment (key block hf, 16-channel step c): group (2 hf + kb16) DC + c / 2,
-  //   chunk ((c % 2) 2 + lh) 16 + lq with kb16 = (l32 / 4) % 2, lq = 4 (l32 / 8) + l32 % 4
-  const int koff = ((l32 >> 2) & 1) * DC * KGS + (lh * 16 + (((l32 >> 3) << 2) | (l32 & 3))) * 16;
+  //   K fragment (key block hf, 16-channel step c), A row l32 = key
+  //   u = 16 (l32 / 16) + 8 ((l32 / 4) % 2) + 4 ((l32 / 8) % 2) + l32 % 4 of the block:
+  //   group (2 hf + (u / 4) % 2) DC + c / 2, chunk (2 (c % 2) + lh) 16 + 4 (u / 8) + u % 4
+  const int koff = ((l32 >> 3) & 1) * DC * KGS +
+                   (lh * 16 + ((l32 >> 4) << 3) + (((l32 >> 2) & 1) << 2) + (l32 & 3)) * 16;
   //   V fragment (channel block cb, key step s): group (s / 2) CB16 + 2 cb + l32 / 16,
-  //   chunk (2 (s % 2) + half) 16 + l32 % 16, plus 8 bytes for lane half lh
-  const int voff = NG * KGS + (l32 >> 4) * VGS + (l32 & 15) * 16 + 8 * lh;
+  //   chunk (2 (s % 2) + lh) 16 + l32 % 16 (keys 16 s + 8 lh .. + 7 of channel l32)
+  const int voff = NG * KGS + (l32 >> 4) * VGS + (lh * 16 + (l32 & 15)) * 16;
   const float sl2 = a.scale * 1.4426950408889634f;  // logits in log2 units
   float m_run = -INFINITY, l_run = 0.f;
   f32x16 o[CB];
@@ -152,7 +156,7 @@ __global__ __launch_bounds__(PF_THREADS) void k_attn_prefill(AttnArgs a) {
   // loaded into registers
   auto compute = [&](int pg, auto S) {
     const unsigned char* st0 = stage_ptr(S);
-    // S^T[key 32 kb + 8 (r / 4) + 4 lh + r % 4][query l32]
+    // S^T[key 32 kb + 16 (r / 8) + 8 lh + r % 8][query l32]
     f32x16 st[2];
 #pragma unroll
     for (int kb = 0; kb < 2; ++kb)
@@ -178,12 +182,12 @@ __global__ __launch_bounds__(PF_THREADS) void k_attn_prefill(AttnArgs a) {
         for (int r = 0; r < 16; ++r) mt = fmaxf(mt, st[kb][r]);
     } else {
       const int wlim = full ? 0x7fffffff : a.window;  // keys visible at 0 <= qpos - kpos < wlim
-      const int d0 = qv ? qpos - pg * PAGE - 4 * lh : -1;
+      const int d0 = qv ? qpos - pg * PAGE - 8 * lh : -1;
 #pragma unroll
       for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
-          const int dlt = d0 - (32 * kb + 8 * (r >> 2) + (r & 3));  // qpos - kpos
+          const int dlt = d0 - (32 * kb + 16 * (r >> 3) + (r & 7));  // qpos - kpos
           const bool vis = (dlt >= 0) & (dlt < wlim);
           st[kb][r] = vis ? st[kb][r] : -INFINITY;
           mt = fmaxf(mt, st[kb][r]);
@@ -214,8 +218,8 @@ __global__ __launch_bounds__(PF_THREADS) void k_attn_prefill(AttnArgs a) {
     }
     l_run += ps;
     m_run = m_new;
-    // P^T fragment of 16-key step s: slots e < 4 are keys 16 s + 4 lh + e, slots e >= 4
-    // keys 16 s + 8 + 4 lh + e - 4 (accumulator rows 8 (s % 2) + e of block s / 2)
+    // P^T fragment of 16-key step s: slot e is key 16 s + 8 lh + e (accumulator
+    // 8 (s % 2) + e of block s / 2)
     bf16x8 pf[4];
 #pragma unroll
     for (int s = 0; s < 4; ++s) {
@@ -229,10 +233,7 @@ __global__ __launch_bounds__(PF_THREADS) void k_attn_prefill(AttnArgs a) {
     for (int s = 0; s < 4; ++s) {  // the CB output blocks interleaved: independent chains
 #pragma unroll
       for (int cb = 0; cb < CB; ++cb) {
-        const unsigned char* vr = st0 + voff + ((s >> 1) * CB16 + 2 * cb) * VGS + (2 * (s & 1)) * 16 * 16;
-        const uint2 lo = *(const uint2*)vr;
-        const uint2 hi = *(const uint2*)(vr + 16 * 16);
-        const bf16x8 vf = __builtin_bit_cast(bf16x8, make_uint4(lo.x, lo.y, hi.x, hi.y));
+        const bf16x8 vf = *(const bf16x8*)(st0 + voff + ((s >> 1) * CB16 + 2 * cb) * VGS + (s & 1) * 32 * 16);
         o[cb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf, pf[s], o[cb], 0, 0, 0);
       }
     }
