@@ -12,6 +12,8 @@
 // split-K partials for small-M (decode) shapes. The L2 norms before the output and down
 // projections only scale a row, and the nGPT update normalises the projection's output,
 // so they need no work here.
+#include <type_traits>
+
 #include "common.h"
 #include "kernels.h"
 
@@ -294,6 +296,15 @@ typedef __attribute__((address_space(1))) void* gbl_void_t;
 template <int CPR>
 __device__ __forceinline__ int swzc(int row, int chunk) {
   return row * CPR + (chunk ^ (CPR == 8 ? ((row >> 1) & 7) : ((row >> 1) & 3)));
+}
+
+// One 16-byte-per-lane load from global memory straight into LDS (64 lanes fill 1 KiB
+// at lds) through a buffer resource over [base, base + nbytes): lanes whose offset voff
+// lies beyond nbytes read zeros; soff is a wave-uniform byte offset.
+__device__ __forceinline__ void buffer_load_lds16(const void* base, int nbytes, lds_void_t lds, int voff,
+                                                  int soff) {
+  const __amdgpu_buffer_rsrc_t r = __builtin_amdgcn_make_buffer_rsrc((void*)base, (short)0, nbytes, 0x00020000);
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(r, lds, 16, voff, soff, 0, 0);
 }
 
 // s_waitcnt vmcnt(n) for a run-time n <= 31 (other counters untouched)
@@ -596,6 +607,152 @@ __global__ __launch_bounds__(WMW * WNW * 64) void k_gemm_pipe32(GemmArgs g) {
   gemm_epilogue32<BM, BN, WMW, WNW, EPI>(g, acc, n_tile, m0, wm, wn, lane);
 }
 
+// 256x256 bf16 tiles with two wave groups one phase apart ("ping-pong"). Waves 0-3
+// (group 0) and 4-7 (group 1) put one wave of each group on every SIMD; wave (group,
+// wn) computes rows 128 group .. +127 and columns 64 wn .. +63 of the tile. Each wave
+// alternates two phases per 64-wide K slice, separated by work-group barriers:
+//   read phase:    all 24 A/B fragments of the slice, LDS -> registers;
+//                  group 0 also issues the direct-to-LDS loads of the next slice
+//   compute phase: the slice's 32 MFMAs (v_mfma_f32_32x32x16_bf16)
+// and group 1 runs one phase behind group 0, so on every SIMD one wave feeds the matrix
+// core while the other reads LDS. Slice s lives in LDS stage s % 2: group 0 issues it
+// during its read phase of slice s - 1 (both groups have then finished reading slice
+// s - 2 from that stage) and waits for it at the end of its next compute phase.
+template <int EPI>
+__global__ __launch_bounds__(512) void k_gemm_pp(GemmArgs g) {
+  constexpr int BM = 256, BN = 256, PBK = 64, CPR = PBK / 8;
+  constexpr int TM = 128, TN = 64, FM = TM / 32, FN = TN / 32, KST = PBK / 16;
+  constexpr int ACH = BM * CPR, BCH = BN * CPR;
+  constexpr int NI = (ACH + BCH) / 64 / 4;  // load instructions per group-0 wave per slice
+  static_assert(EPI != EPI_SWIGLU || FN % 2 == 0, "SwiGLU needs gate/up pairs per wave");
+
+  // one array per stage, so that the reads of one stage are known not to alias the
+  // direct-to-LDS loads in flight into the other
+  __shared__ __align__(16) uint4 sm0[ACH + BCH];
+  __shared__ __align__(16) uint4 sm1[ACH + BCH];
+
+  const int t = threadIdx.x, lane = t & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(t >> 6);
+  const int grp = wave >> 2, wn = wave & 3;
+  int n_tile, m_tile;
+  tile_coords<8>(&n_tile, &m_tile);
+  const int m0 = m_tile * BM;
+  const int nk = g.K / PBK;
+  const bf16_t* A = (const bf16_t*)g.A;
+  const bf16_t* B = (const bf16_t*)g.B;
+
+  auto stage = [&](auto S) -> uint4* {
+    if constexpr (decltype(S)::value == 0) return sm0;
+    else return sm1;
+  };
+  auto brow = [&](int r) -> int {
+    if (EPI == EPI_SWIGLU) {
+      const int c0 = n_tile * (BN / 2);
+      return r < BN / 2 ? c0 + r : g.n_half + c0 + (r - BN / 2);
+    }
+    return n_tile * BN + r;
+  };
+  // Group-0 wave wn issues load instructions wn, wn + 4, ... of a slice; instruction i
+  // fills LDS chunks 64 i .. 64 i + 63 (8 rows of 8 chunks), A rows for i < 32, then B.
+  // The swizzle of row 8 i + lane / 8 only depends on wn % 2 and the lane, so one per-lane
+  // offset serves every instruction. The loads go through buffer resources: A from the
+  // tile's first row, with a range check that returns zeros for rows at or beyond M (the
+  // row offset is in the per-lane offset); B with its row and K offset in the scalar
+  // offset.
+  const int lr = lane >> 3;
+  const int lc = (lane & 7) ^ ((4 * (wn & 1) + (lane >> 4)) & 7);
+  const long a_rest = (long)(g.M - m0) * g.lda * 2;
+  const int a_bytes = a_rest < 0x7fffffffL ? (int)a_rest : 0x7fffffff;
+  const int voA = (lr * g.lda + 8 * lc) * 2;
+  const int voB = (lr * g.K + 8 * lc) * 2;
+  const bf16_t* Am = A + (size_t)m0 * g.lda;
+  auto issue = [&](auto S, int k0, int va, int vb) {
+    uint4* dst0 = stage(S);
+#pragma unroll
+    for (int q = 0; q < NI; ++q) {
+      const int inst = wn + 4 * q;  // inst < 32 exactly for q < 8
+      if (q < NI / 2)
+        buffer_load_lds16(Am, a_bytes, (lds_void_t)(dst0 + inst * 64), va + 16 * g.lda * inst, 2 * k0);
+      else
+        buffer_load_lds16(B, 0x7fffffff, (lds_void_t)(dst0 + inst * 64), vb,
+                          2 * (brow(8 * (inst - NI * 2)) * g.K + k0));
+    }
+  };
+  auto bblock = [&](int j) -> int {
+    if (EPI == EPI_SWIGLU)
+      return j < FN / 2 ? wn * (TN / 2) + j * 32 : BN / 2 + wn * (TN / 2) + (j - FN / 2) * 32;
+    return wn * TN + j * 32;
+  };
+
+  f32x16 acc[FM][FN];
+#pragma unroll
+  for (int i = 0; i < FM; ++i)
+#pragma unroll
+    for (int j = 0; j < FN; ++j)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.f;
+  bf16x8 af[KST][FM], bfr[KST][FN];
+
+  auto read_phase = [&](auto S, int it) {
+    // per-lane bases made opaque here, so that the addresses derived from them are
+    // recomputed in each phase instead of being held in registers across the loop
+    int va = voA, vb = voB;
+    int ln = lane;
+    asm volatile("" : "+v"(va), "+v"(vb), "+v"(ln));
+    if (grp == 0 && it + 1 < nk) {
+      if constexpr (decltype(S)::value == 0) issue(std::integral_constant<int, 1>{}, PBK * (it + 1), va, vb);
+      else issue(std::integral_constant<int, 0>{}, PBK * (it + 1), va, vb);
+    }
+    const uint4* As = stage(S);
+    const uint4* Bs = As + ACH;
+#pragma unroll
+    for (int ks = 0; ks < KST; ++ks) {
+      const int ch = ks * 2 + (ln >> 5);
+#pragma unroll
+      for (int i = 0; i < FM; ++i)
+        af[ks][i] = __builtin_bit_cast(bf16x8, As[swzc<CPR>(grp * TM + i * 32 + (ln & 31), ch)]);
+#pragma unroll
+      for (int j = 0; j < FN; ++j)
+        bfr[ks][j] = __builtin_bit_cast(bf16x8, Bs[swzc<CPR>(bblock(j) + (ln & 31), ch)]);
+    }
+    asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+    __builtin_amdgcn_sched_barrier(0);
+  };
+  auto compute_phase = [&]() {
+#pragma unroll
+    for (int ks = 0; ks < KST; ++ks)
+#pragma unroll
+      for (int i = 0; i < FM; ++i)
+#pragma unroll
+        for (int j = 0; j < FN; ++j)
+          acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[ks][i], bfr[ks][j], acc[i][j], 0, 0, 0);
+    __builtin_amdgcn_sched_barrier(0);
+    if (grp == 0) asm volatile("s_waitcnt vmcnt(0)\n\ts_barrier" ::: "memory");
+    else asm volatile("s_barrier" ::: "memory");
+    __builtin_amdgcn_sched_barrier(0);
+  };
+
+  using S0 = std::integral_constant<int, 0>;
+  using S1 = std::integral_constant<int, 1>;
+  if (grp == 0) {
+    issue(S0{}, 0, voA, voB);
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+  } else {
+    asm volatile("s_barrier" ::: "memory");  // group 1 starts one phase behind
+  }
+  __builtin_amdgcn_sched_barrier(0);
+  for (int it = 0; it < nk; it += 2) {
+    read_phase(S0{}, it);
+    compute_phase();
+    if (it + 1 < nk) {
+      read_phase(S1{}, it + 1);
+      compute_phase();
+    }
+  }
+  gemm_epilogue32<BM, BN, 2, 4, EPI>(g, acc, n_tile, m0, grp, wn, lane);
+  if (grp == 0) asm volatile("s_barrier" ::: "memory");  // the barrier group 1 took first
+}
+
 // MXFP8 (W8A16) split-K tiles for decode-sized M, on v_mfma_f32_32x32x16_bf16. The
 // bf16 activations and the E4M3 weight codes stream straight into an LDS ring of
 // 64-wide K slices; each lane turns its 8 codes of a B fragment into bf16 just before
@@ -730,8 +887,8 @@ static hipError_t go_pipe(const GemmArgs& g, hipStream_t st, int ntiles_n) {
 }
 
 // Large-M (prefill) tiles for bf16 weights over n output columns (for SwiGLU, gate and
-// up columns together): 256x256 tiles when they fill the device, else 256x160 (waves
-// stacked along M) when n allows; hipErrorNotSupported when no tile shape divides n.
+// up columns together): 256x256 ping-pong tiles when they fill the device, else 256x160
+// (waves stacked along M) when n allows; hipErrorNotSupported when no tile shape divides n.
 template <int BM, int BN, int WMW, int WNW, int EPI, int STAGES>
 static hipError_t go_pipe32(const GemmArgs& g, hipStream_t st, int ntiles_n) {
   dim3 grid(ntiles_n, (g.M + BM - 1) / BM);
@@ -741,8 +898,12 @@ static hipError_t go_pipe32(const GemmArgs& g, hipStream_t st, int ntiles_n) {
 
 template <int EPI>
 static hipError_t go_big(const GemmArgs& g, hipStream_t st, int n) {
-  if (n % 256 == 0 && (EPI == EPI_SWIGLU || n / 256 * ((g.M + 255) / 256) >= 256)) {
-    return go_pipe32<256, 256, 2, 4, EPI, 2>(g, st, n / 256);
+  // the ping-pong kernel addresses A and B with 32-bit byte offsets
+  const bool offs32 = (long)g.N * g.K < (1L << 30) && g.lda < (1 << 20);
+  if (n % 256 == 0 && offs32 && (EPI == EPI_SWIGLU || n / 256 * ((g.M + 255) / 256) >= 256)) {
+    dim3 grid(n / 256, (g.M + 255) / 256);
+    hipLaunchKernelGGL((k_gemm_pp<EPI>), grid, dim3(512), 0, st, g);
+    return hipGetLastError();
   }
   if constexpr (EPI != EPI_SWIGLU)
     if (n % 160 == 0) return go_pipe32<256, 160, 4, 1, EPI, 2>(g, st, n / 160);

@@ -994,6 +994,43 @@ int dory_test_fill_kv(dory_ctx* ctx, void* stream, int32_t seq_id, int layer, in
   return DORY_OK;
 }
 
+int dory_test_gemm(void* stream, const void* A, int lda, const void* B, const uint8_t* B_scales,
+                   int wfmt, int M, int N, int K, int epi, void* C, int ldc, int* splits) {
+  const bool mx = wfmt == DORY_WFMT_MXFP8;
+  const bool ok_fmt = (wfmt == DORY_WFMT_BF16 && !B_scales) || (mx && B_scales);
+  const bool ok_epi = epi == EPI_F32 || epi == EPI_PARTIAL || epi == EPI_STORE_ACT || epi == EPI_SWIGLU;
+  if (!A || !B || !splits || !ok_fmt || !ok_epi || M < 1 || N < 64 || K < 64 || K % 64 || N % 64 ||
+      (epi == EPI_SWIGLU && N % 128) || lda < K || (C && ldc < (epi == EPI_SWIGLU ? N / 2 : N)) ||
+      (mx && epi != EPI_PARTIAL)) {
+    g_create_err = "bad GEMM argument";
+    return DORY_ERR_INVALID_ARG;
+  }
+  const int S = epi == EPI_PARTIAL ? gemm_pick_splits(M, N, K, mx ? W_MXFP8 : W_BF16) : 1;
+  *splits = S;
+  if (!C) return DORY_OK;
+  GemmArgs g;
+  g.A = A;
+  g.lda = lda;
+  g.B = B;
+  g.Bs = B_scales;
+  g.M = M;
+  g.N = N;
+  g.K = K;
+  g.act = ACT_BF16;
+  g.wfmt = mx ? W_MXFP8 : W_BF16;
+  g.epi = epi;
+  g.splits = S;
+  g.C = C;
+  g.ldc = ldc;
+  g.n_half = epi == EPI_SWIGLU ? N / 2 : 0;
+  const hipError_t e = launch_gemm(g, (hipStream_t)stream);
+  if (e != hipSuccess) {
+    g_create_err = hipGetErrorString(e);
+    return e == hipErrorInvalidValue ? DORY_ERR_INVALID_ARG : DORY_ERR_HIP;
+  }
+  return DORY_OK;
+}
+
 int dory_quantize_mxfp8(void* stream, const void* w, int w_dtype, int64_t rows, int64_t cols,
                         uint8_t* codes, uint8_t* scales) {
   if (!w || !codes || !scales || rows < 0 || cols < 0 || cols % 32 ||

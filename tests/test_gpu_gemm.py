@@ -1,0 +1,115 @@
+"""GPU: the projection GEMM kernels through the C ABI (dory_test_gemm), each shape routed
+to the kernel a layer call would use, against a plain float32 matmul of the same bf16
+(or dequantised MXFP8) operands. Shapes cover the 256x256 ping-pong tiles (every
+epilogue, ragged M, row stride > K), the 256x160 tiles and the split-K decode kernels.
+
+Tolerances: float outputs |d| <= 2e-3 * (|ref| + 1) (bf16 products, float32 sums in
+another order over K <= 4096 terms of size ~0.02); bf16 outputs additionally one
+rounding of the output (2^-8 relative)."""
+import pytest
+import torch
+
+from looped_ngpt_transformer_amd import dory as D
+
+pytestmark = pytest.mark.gpu
+
+SENTINEL = 8192.0  # exact in bf16 and float32
+
+
+def operands(M, N, K, seed, lda=None):
+    g = torch.Generator(device="cpu").manual_seed(seed)
+    lda = lda or K
+    Abig = torch.randn(M, lda, generator=g).to(torch.bfloat16).cuda()
+    B = (0.02 * torch.randn(N, K, generator=g)).to(torch.bfloat16).cuda()
+    return Abig[:, :K], B
+
+
+def reference(A, B):
+    return A.float() @ B.float().t()
+
+
+def check(out, ref, bf16_out):
+    tol = 2e-3 * (ref.abs() + 1.0)
+    if bf16_out:
+        tol = tol + ref.abs() * 2.0 ** -8
+    d = (out.float() - ref).abs()
+    bad = d > tol
+    assert not bad.any(), f"{int(bad.sum())} outside tolerance, max |d| {float(d.max()):.3e}"
+
+
+@pytest.mark.parametrize("M,N,K,lda", [
+    (2600, 6400, 2560, None),     # [q|k|v|gate] shape, 275 ping-pong tiles, ragged last row tile
+    (4096, 6400, 2560, 2624),     # full tiles, A row stride > K
+    (150, 6400, 2560, None),      # too few tiles for 256x256: 256x160 tiles
+])
+def test_store_bf16(M, N, K, lda):
+    A, B = operands(M, N, K, 1, lda)
+    out = torch.full((M + 4, N), SENTINEL, dtype=torch.bfloat16, device="cuda")
+    assert D.dory_test_gemm(A, B, D.EPI_STORE_BF16, out, M=M, lda=A.stride(0)) == 1
+    torch.cuda.synchronize()
+    check(out[:M], reference(A, B), True)
+    assert (out[M:].float() == SENTINEL).all(), "rows beyond M written"
+
+
+@pytest.mark.parametrize("M,N,K", [
+    (4000, 4096, 512),    # 256 ping-pong tiles with the float epilogue, ragged M
+    (1000, 2560, 4096),   # output / down projection shape: 256x160 tiles
+    (4096, 2560, 2560),
+])
+def test_f32(M, N, K):
+    A, B = operands(M, N, K, 2)
+    out = torch.full((M + 4, N), SENTINEL, dtype=torch.float32, device="cuda")
+    assert D.dory_test_gemm(A, B, D.EPI_F32, out, M=M) == 1
+    torch.cuda.synchronize()
+    check(out[:M], reference(A, B), False)
+    assert (out[M:] == SENTINEL).all()
+
+
+@pytest.mark.parametrize("M", [300, 4096, 37])
+def test_swiglu(M):
+    N, K = 8192, 2560  # gate rows then up rows, as W_gu
+    A, B = operands(M, N, K, 3)
+    out = torch.full((M + 4, N // 2), SENTINEL, dtype=torch.bfloat16, device="cuda")
+    assert D.dory_test_gemm(A, B, D.EPI_SWIGLU, out, M=M) == 1
+    torch.cuda.synchronize()
+    gu = reference(A, B)
+    gate, up = gu[:, : N // 2], gu[:, N // 2:]
+    ref = torch.nn.functional.silu(gate) * up
+    check(out[:M], ref, True)
+    assert (out[M:].float() == SENTINEL).all()
+
+
+@pytest.mark.parametrize("M,N,K", [(1, 6400, 2560), (32, 2560, 4096), (100, 8192, 2560), (128, 2560, 2560)])
+def test_split_k_bf16(M, N, K):
+    A, B = operands(M, N, K, 4)
+    S = D.dory_test_gemm(A, B, D.EPI_PARTIAL, None, M=M)
+    assert 1 <= S <= 32
+    out = torch.zeros((S, M, N), dtype=torch.float32, device="cuda")
+    assert D.dory_test_gemm(A, B, D.EPI_PARTIAL, out, M=M) == S
+    torch.cuda.synchronize()
+    check(out.sum(0), reference(A, B), False)
+
+
+def dequant_mxfp8(codes, scales):
+    w = codes.view(torch.float8_e4m3fn).float()
+    e = scales.to(torch.int32).float() - 127.0
+    return w * torch.exp2(e).repeat_interleave(32, dim=1)
+
+
+@pytest.mark.parametrize("M,N,K", [(1, 6400, 2560), (32, 2560, 4096), (128, 8192, 2560), (70, 2560, 2560)])
+def test_split_k_mxfp8(M, N, K):
+    A, B = operands(M, N, K, 5)
+    codes = torch.empty((N, K), dtype=torch.uint8, device="cuda")
+    scales = torch.empty((N, K // 32), dtype=torch.uint8, device="cuda")
+    D.dory_quantize_mxfp8(B, codes, scales)
+    S = D.dory_test_gemm(A, codes, D.EPI_PARTIAL, None, B_scales=scales, M=M)
+    out = torch.zeros((S, M, N), dtype=torch.float32, device="cuda")
+    assert D.dory_test_gemm(A, codes, D.EPI_PARTIAL, out, B_scales=scales, M=M) == S
+    torch.cuda.synchronize()
+    check(out.sum(0), A.float() @ dequant_mxfp8(codes, scales).t(), False)
+
+
+def test_rejects_bad_sizes():
+    A, B = operands(64, 128, 96, 6)
+    with pytest.raises(D.DoryError):
+        D.dory_test_gemm(A, B, D.EPI_F32, None)  # K % 64 != 0
