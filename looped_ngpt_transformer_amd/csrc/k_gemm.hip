@@ -508,7 +508,8 @@ __global__ __launch_bounds__(WMW * WNW * 64) void k_gemm_pipe32(GemmArgs g) {
 
   __shared__ __align__(16) uint4 sm[STAGES][ACH + BCH];
 
-  const int t = threadIdx.x, lane = t & 63, wave = t >> 6;
+  const int t = threadIdx.x, lane = t & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(t >> 6) & (NW - 1);  // uniform, < NW
   const int wm = wave / WNW, wn = wave % WNW;
   int n_tile, m_tile;
   tile_coords<8>(&n_tile, &m_tile);
@@ -525,23 +526,28 @@ __global__ __launch_bounds__(WMW * WNW * 64) void k_gemm_pipe32(GemmArgs g) {
     }
     return n_tile * BN + r;
   };
+  // Instruction i fills LDS chunks 64 i .. 64 i + 63 (8 rows of 8 chunks), A rows for
+  // i < ACH / 64, then B. The swizzle of row 8 i + lane / 8 depends only on i % 2 = wave
+  // % 2 and the lane, so one per-lane offset serves every instruction of the wave; A goes
+  // through a buffer resource from the tile's first row whose range check returns zeros
+  // for rows at or beyond M.
+  const int lr = lane >> 3;
+  const int lc = (lane & 7) ^ ((4 * (wave & 1) + (lane >> 4)) & 7);
+  const int voA = (lr * g.lda + 8 * lc) * 2;
+  const int voB = (lr * g.K + 8 * lc) * 2;
+  const long a_rest = (long)(g.M - m0) * g.lda * 2;
+  const int a_bytes = a_rest < 0x7fffffffL ? (int)a_rest : 0x7fffffff;
+  const bf16_t* Am = A + (size_t)m0 * g.lda;
   auto issue = [&](int slot, int k0) {
 #pragma unroll
     for (int q = 0; q < MAXI; ++q) {
       const int inst = wave + NW * q;
       if (inst < NINST) {
-        const int sidx = inst * 64 + lane;
-        const bf16_t* src;
-        if (sidx < ACH) {
-          const int r = sidx / CPR, c = swzc<CPR>(r, sidx % CPR) - r * CPR;
-          const int m = min(m0 + r, g.M - 1);
-          src = A + (size_t)m * g.lda + k0 + 8 * c;
-        } else {
-          const int s2 = sidx - ACH;
-          const int r = s2 / CPR, c = swzc<CPR>(r, s2 % CPR) - r * CPR;
-          src = B + (size_t)brow(r) * g.K + k0 + 8 * c;
-        }
-        __builtin_amdgcn_global_load_lds((gbl_void_t)src, (lds_void_t)(&sm[slot][inst * 64]), 16, 0, 0);
+        if (inst < ACH / 64)
+          buffer_load_lds16(Am, a_bytes, (lds_void_t)(&sm[slot][inst * 64]), voA + 16 * g.lda * inst, 2 * k0);
+        else
+          buffer_load_lds16(B, 0x7fffffff, (lds_void_t)(&sm[slot][inst * 64]), voB,
+                            2 * (brow(8 * (inst - ACH / 64)) * g.K + k0));
       }
     }
   };
@@ -898,9 +904,9 @@ static hipError_t go_pipe32(const GemmArgs& g, hipStream_t st, int ntiles_n) {
 
 template <int EPI>
 static hipError_t go_big(const GemmArgs& g, hipStream_t st, int n) {
-  // the ping-pong kernel addresses A and B with 32-bit byte offsets
-  const bool offs32 = (long)g.N * g.K < (1L << 30) && g.lda < (1 << 20);
-  if (n % 256 == 0 && offs32 && (EPI == EPI_SWIGLU || n / 256 * ((g.M + 255) / 256) >= 256)) {
+  // these kernels address A and B with 32-bit byte offsets
+  if ((long)g.N * g.K >= (1L << 30) || g.lda >= (1 << 20)) return hipErrorNotSupported;
+  if (n % 256 == 0 && (EPI == EPI_SWIGLU || n / 256 * ((g.M + 255) / 256) >= 256)) {
     dim3 grid(n / 256, (g.M + 255) / 256);
     hipLaunchKernelGGL((k_gemm_pp<EPI>), grid, dim3(512), 0, st, g);
     return hipGetLastError();
