@@ -613,24 +613,28 @@ __global__ __launch_bounds__(WMW * WNW * 64) void k_gemm_pipe32(GemmArgs g) {
   gemm_epilogue32<BM, BN, WMW, WNW, EPI>(g, acc, n_tile, m0, wm, wn, lane);
 }
 
-// 256x256 bf16 tiles with two wave groups one phase apart ("ping-pong"). Waves 0-3
-// (group 0) and 4-7 (group 1) put one wave of each group on every SIMD; wave (group,
-// wn) computes rows 128 group .. +127 and columns 64 wn .. +63 of the tile. Each wave
-// alternates two phases per 64-wide K slice, separated by work-group barriers:
+// 256 x BN bf16 tiles (BN 256 or 160) with two wave groups one phase apart
+// ("ping-pong"). Waves 0-3 (group 0) and 4-7 (group 1) put one wave of each group on
+// every SIMD; group g owns rows 128 g .. +127 of the tile, split among its four waves as
+// 128 x 64 column blocks (BN 256) or 32 x 160 row blocks (BN 160). Each wave alternates
+// two phases per 64-wide K slice, separated by work-group barriers:
 //   read phase:    all 24 A/B fragments of the slice, LDS -> registers;
 //                  group 0 also issues the direct-to-LDS loads of the next slice
-//   compute phase: the slice's 32 MFMAs (v_mfma_f32_32x32x16_bf16)
+//   compute phase: the slice's 32 or 20 MFMAs (v_mfma_f32_32x32x16_bf16)
 // and group 1 runs one phase behind group 0, so on every SIMD one wave feeds the matrix
 // core while the other reads LDS. Slice s lives in LDS stage s % 2: group 0 issues it
 // during its read phase of slice s - 1 (both groups have then finished reading slice
 // s - 2 from that stage) and waits for it at the end of its next compute phase.
-template <int EPI>
+template <int BN, int EPI>
 __global__ __launch_bounds__(512) void k_gemm_pp(GemmArgs g) {
-  constexpr int BM = 256, BN = 256, PBK = 64, CPR = PBK / 8;
-  constexpr int TM = 128, TN = 64, FM = TM / 32, FN = TN / 32, KST = PBK / 16;
-  constexpr int ACH = BM * CPR, BCH = BN * CPR;
+  constexpr int BM = 256, PBK = 64, CPR = PBK / 8;
+  constexpr int WMW = BN == 256 ? 2 : 8, WNW = BN == 256 ? 4 : 1;  // wave grid of the tile
+  constexpr int TM = BM / WMW, TN = BN / WNW, FM = TM / 32, FN = TN / 32, KST = PBK / 16;
+  constexpr int ACH = BM * CPR, BCH = BN * CPR, NA = ACH / 64;
   constexpr int NI = (ACH + BCH) / 64 / 4;  // load instructions per group-0 wave per slice
-  static_assert(EPI != EPI_SWIGLU || FN % 2 == 0, "SwiGLU needs gate/up pairs per wave");
+  static_assert(BN == 256 || BN == 160, "tile widths");
+  static_assert((ACH + BCH) % 256 == 0 && NA % 4 == 0, "load instructions split evenly");
+  static_assert(EPI != EPI_SWIGLU || (BN == 256 && FN % 2 == 0), "SwiGLU needs gate/up pairs per wave");
 
   // one array per stage, so that the reads of one stage are known not to alias the
   // direct-to-LDS loads in flight into the other
@@ -639,7 +643,8 @@ __global__ __launch_bounds__(512) void k_gemm_pp(GemmArgs g) {
 
   const int t = threadIdx.x, lane = t & 63;
   const int wave = __builtin_amdgcn_readfirstlane(t >> 6);
-  const int grp = wave >> 2, wn = wave & 3;
+  const int grp = wave >> 2, w4 = wave & 3;
+  const int wm = BN == 256 ? grp : 4 * grp + w4, wn = BN == 256 ? w4 : 0;
   int n_tile, m_tile;
   tile_coords<8>(&n_tile, &m_tile);
   const int m0 = m_tile * BM;
@@ -658,15 +663,15 @@ __global__ __launch_bounds__(512) void k_gemm_pp(GemmArgs g) {
     }
     return n_tile * BN + r;
   };
-  // Group-0 wave wn issues load instructions wn, wn + 4, ... of a slice; instruction i
+  // Group-0 wave w4 issues load instructions w4, w4 + 4, ... of a slice; instruction i
   // fills LDS chunks 64 i .. 64 i + 63 (8 rows of 8 chunks), A rows for i < 32, then B.
-  // The swizzle of row 8 i + lane / 8 only depends on wn % 2 and the lane, so one per-lane
+  // The swizzle of row 8 i + lane / 8 only depends on w4 % 2 and the lane, so one per-lane
   // offset serves every instruction. The loads go through buffer resources: A from the
   // tile's first row, with a range check that returns zeros for rows at or beyond M (the
   // row offset is in the per-lane offset); B with its row and K offset in the scalar
   // offset.
   const int lr = lane >> 3;
-  const int lc = (lane & 7) ^ ((4 * (wn & 1) + (lane >> 4)) & 7);
+  const int lc = (lane & 7) ^ ((4 * (w4 & 1) + (lane >> 4)) & 7);
   const long a_rest = (long)(g.M - m0) * g.lda * 2;
   const int a_bytes = a_rest < 0x7fffffffL ? (int)a_rest : 0x7fffffff;
   const int voA = (lr * g.lda + 8 * lc) * 2;
@@ -676,12 +681,12 @@ __global__ __launch_bounds__(512) void k_gemm_pp(GemmArgs g) {
     uint4* dst0 = stage(S);
 #pragma unroll
     for (int q = 0; q < NI; ++q) {
-      const int inst = wn + 4 * q;  // inst < 32 exactly for q < 8
-      if (q < NI / 2)
+      const int inst = w4 + 4 * q;  // inst < NA exactly for q < NA / 4
+      if (q < NA / 4)
         buffer_load_lds16(Am, a_bytes, (lds_void_t)(dst0 + inst * 64), va + 16 * g.lda * inst, 2 * k0);
       else
         buffer_load_lds16(B, 0x7fffffff, (lds_void_t)(dst0 + inst * 64), vb,
-                          2 * (brow(8 * (inst - NI * 2)) * g.K + k0));
+                          2 * (brow(8 * (inst - NA)) * g.K + k0));
     }
   };
   auto bblock = [&](int j) -> int {
@@ -716,7 +721,7 @@ __global__ __launch_bounds__(512) void k_gemm_pp(GemmArgs g) {
       const int ch = ks * 2 + (ln >> 5);
 #pragma unroll
       for (int i = 0; i < FM; ++i)
-        af[ks][i] = __builtin_bit_cast(bf16x8, As[swzc<CPR>(grp * TM + i * 32 + (ln & 31), ch)]);
+        af[ks][i] = __builtin_bit_cast(bf16x8, As[swzc<CPR>(wm * TM + i * 32 + (ln & 31), ch)]);
 #pragma unroll
       for (int j = 0; j < FN; ++j)
         bfr[ks][j] = __builtin_bit_cast(bf16x8, Bs[swzc<CPR>(bblock(j) + (ln & 31), ch)]);
@@ -755,7 +760,7 @@ __global__ __launch_bounds__(512) void k_gemm_pp(GemmArgs g) {
       compute_phase();
     }
   }
-  gemm_epilogue32<BM, BN, 2, 4, EPI>(g, acc, n_tile, m0, grp, wn, lane);
+  gemm_epilogue32<BM, BN, WMW, WNW, EPI>(g, acc, n_tile, m0, wm, wn, lane);
   if (grp == 0) asm volatile("s_barrier" ::: "memory");  // the barrier group 1 took first
 }
 
@@ -894,7 +899,8 @@ static hipError_t go_pipe(const GemmArgs& g, hipStream_t st, int ntiles_n) {
 
 // Large-M (prefill) tiles for bf16 weights over n output columns (for SwiGLU, gate and
 // up columns together): 256x256 ping-pong tiles when they fill the device, else 256x160
-// (waves stacked along M) when n allows; hipErrorNotSupported when no tile shape divides n.
+// ping-pong tiles when n allows; hipErrorNotSupported when no tile shape divides n or the
+// sizes need offsets beyond 32 bits.
 template <int BM, int BN, int WMW, int WNW, int EPI, int STAGES>
 static hipError_t go_pipe32(const GemmArgs& g, hipStream_t st, int ntiles_n) {
   dim3 grid(ntiles_n, (g.M + BM - 1) / BM);
@@ -908,11 +914,15 @@ static hipError_t go_big(const GemmArgs& g, hipStream_t st, int n) {
   if ((long)g.N * g.K >= (1L << 30) || g.lda >= (1 << 20)) return hipErrorNotSupported;
   if (n % 256 == 0 && (EPI == EPI_SWIGLU || n / 256 * ((g.M + 255) / 256) >= 256)) {
     dim3 grid(n / 256, (g.M + 255) / 256);
-    hipLaunchKernelGGL((k_gemm_pp<EPI>), grid, dim3(512), 0, st, g);
+    hipLaunchKernelGGL((k_gemm_pp<256, EPI>), grid, dim3(512), 0, st, g);
     return hipGetLastError();
   }
   if constexpr (EPI != EPI_SWIGLU)
-    if (n % 160 == 0) return go_pipe32<256, 160, 4, 1, EPI, 2>(g, st, n / 160);
+    if (n % 160 == 0) {
+      dim3 grid(n / 160, (g.M + 255) / 256);
+      hipLaunchKernelGGL((k_gemm_pp<160, EPI>), grid, dim3(512), 0, st, g);
+      return hipGetLastError();
+    }
   if (n % 256 == 0) return go_pipe32<256, 256, 2, 4, EPI, 2>(g, st, n / 256);
   return hipErrorNotSupported;
 }
