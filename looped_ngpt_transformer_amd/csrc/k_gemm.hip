@@ -618,13 +618,14 @@ __global__ __launch_bounds__(WMW * WNW * 64) void k_gemm_pipe32(GemmArgs g) {
 // every SIMD; group g owns rows 128 g .. +127 of the tile, split among its four waves as
 // 128 x 64 column blocks (BN 256) or 32 x 160 row blocks (BN 160). Each wave alternates
 // two phases per 64-wide K slice, separated by work-group barriers:
-//   read phase:    all 24 A/B fragments of the slice, LDS -> registers;
-//                  group 0 also issues the direct-to-LDS loads of the next slice
+//   read phase:    all 24 A/B fragments of the slice, LDS -> registers
 //   compute phase: the slice's 32 or 20 MFMAs (v_mfma_f32_32x32x16_bf16)
 // and group 1 runs one phase behind group 0, so on every SIMD one wave feeds the matrix
-// core while the other reads LDS. Slice s lives in LDS stage s % 2: group 0 issues it
-// during its read phase of slice s - 1 (both groups have then finished reading slice
-// s - 2 from that stage) and waits for it at the end of its next compute phase.
+// core while the other reads LDS. Slice s lives in LDS stage s % 2. Group 1 streams it
+// in with direct-to-LDS loads placed between the MFMAs of its compute phase of slice
+// s - 2 (both groups have read slice s - 2 from that stage by then), where the wave's
+// issue slots are otherwise idle, and waits for them at the end of its next read phase,
+// one slot before group 0 reads slice s.
 template <int BN, int EPI>
 __global__ __launch_bounds__(512) void k_gemm_pp(GemmArgs g) {
   constexpr int BM = 256, PBK = 64, CPR = PBK / 8;
@@ -663,7 +664,7 @@ __global__ __launch_bounds__(512) void k_gemm_pp(GemmArgs g) {
     }
     return n_tile * BN + r;
   };
-  // Group-0 wave w4 issues load instructions w4, w4 + 4, ... of a slice; instruction i
+  // Group-1 wave w4 issues load instructions w4, w4 + 4, ... of a slice; instruction i
   // fills LDS chunks 64 i .. 64 i + 63 (8 rows of 8 chunks), A rows for i < 32, then B.
   // The swizzle of row 8 i + lane / 8 only depends on w4 % 2 and the lane, so one per-lane
   // offset serves every instruction. The loads go through buffer resources: A from the
@@ -677,17 +678,14 @@ __global__ __launch_bounds__(512) void k_gemm_pp(GemmArgs g) {
   const int voA = (lr * g.lda + 8 * lc) * 2;
   const int voB = (lr * g.K + 8 * lc) * 2;
   const bf16_t* Am = A + (size_t)m0 * g.lda;
-  auto issue = [&](auto S, int k0, int va, int vb) {
+  auto issue_one = [&](auto S, int k0, int va, int vb, int q) {
     uint4* dst0 = stage(S);
-#pragma unroll
-    for (int q = 0; q < NI; ++q) {
-      const int inst = w4 + 4 * q;  // inst < NA exactly for q < NA / 4
-      if (q < NA / 4)
-        buffer_load_lds16(Am, a_bytes, (lds_void_t)(dst0 + inst * 64), va + 16 * g.lda * inst, 2 * k0);
-      else
-        buffer_load_lds16(B, 0x7fffffff, (lds_void_t)(dst0 + inst * 64), vb,
-                          2 * (brow(8 * (inst - NA)) * g.K + k0));
-    }
+    const int inst = w4 + 4 * q;  // inst < NA exactly for q < NA / 4
+    if (q < NA / 4)
+      buffer_load_lds16(Am, a_bytes, (lds_void_t)(dst0 + inst * 64), va + 16 * g.lda * inst, 2 * k0);
+    else
+      buffer_load_lds16(B, 0x7fffffff, (lds_void_t)(dst0 + inst * 64), vb,
+                        2 * (brow(8 * (inst - NA)) * g.K + k0));
   };
   auto bblock = [&](int j) -> int {
     if (EPI == EPI_SWIGLU)
@@ -704,16 +702,11 @@ __global__ __launch_bounds__(512) void k_gemm_pp(GemmArgs g) {
       for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.f;
   bf16x8 af[KST][FM], bfr[KST][FN];
 
-  auto read_phase = [&](auto S, int it) {
-    // per-lane bases made opaque here, so that the addresses derived from them are
+  auto read_phase = [&](auto S) {
+    // lane made opaque here, so that the fragment addresses derived from it are
     // recomputed in each phase instead of being held in registers across the loop
-    int va = voA, vb = voB;
     int ln = lane;
-    asm volatile("" : "+v"(va), "+v"(vb), "+v"(ln));
-    if (grp == 0 && it + 1 < nk) {
-      if constexpr (decltype(S)::value == 0) issue(std::integral_constant<int, 1>{}, PBK * (it + 1), va, vb);
-      else issue(std::integral_constant<int, 0>{}, PBK * (it + 1), va, vb);
-    }
+    asm volatile("" : "+v"(ln));
     const uint4* As = stage(S);
     const uint4* Bs = As + ACH;
 #pragma unroll
@@ -726,42 +719,59 @@ __global__ __launch_bounds__(512) void k_gemm_pp(GemmArgs g) {
       for (int j = 0; j < FN; ++j)
         bfr[ks][j] = __builtin_bit_cast(bf16x8, Bs[swzc<CPR>(bblock(j) + (ln & 31), ch)]);
     }
-    asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+    // group 1 also waits for the slice it streamed in during its last compute phase
+    if (grp == 1) asm volatile("s_waitcnt vmcnt(0) lgkmcnt(0)\n\ts_barrier" ::: "memory");
+    else asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
     __builtin_amdgcn_sched_barrier(0);
   };
-  auto compute_phase = [&]() {
+  constexpr int NMF = KST * FM * FN;  // MFMAs per slice
+  // compute phase of slice it, in stage S; group 1 streams slice it + 2 into that stage,
+  // load q right after MFMA q * NMF / NI so that the NI loads spread over the phase
+  auto compute_phase = [&](auto S, int it) {
+    const bool ld = grp == 1 && it + 2 < nk;  // wave-uniform
+    int va = voA, vb = voB;
+    asm volatile("" : "+v"(va), "+v"(vb));
 #pragma unroll
     for (int ks = 0; ks < KST; ++ks)
 #pragma unroll
       for (int i = 0; i < FM; ++i)
 #pragma unroll
-        for (int j = 0; j < FN; ++j)
+        for (int j = 0; j < FN; ++j) {
           acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[ks][i], bfr[ks][j], acc[i][j], 0, 0, 0);
+          const int idx = (ks * FM + i) * FN + j;
+#pragma unroll
+          for (int q = 0; q < NI; ++q)
+            if (q * NMF / NI == idx && ld) issue_one(S, PBK * (it + 2), va, vb, q);
+        }
     __builtin_amdgcn_sched_barrier(0);
-    if (grp == 0) asm volatile("s_waitcnt vmcnt(0)\n\ts_barrier" ::: "memory");
-    else asm volatile("s_barrier" ::: "memory");
+    asm volatile("s_barrier" ::: "memory");
     __builtin_amdgcn_sched_barrier(0);
   };
 
   using S0 = std::integral_constant<int, 0>;
   using S1 = std::integral_constant<int, 1>;
-  if (grp == 0) {
-    issue(S0{}, 0, voA, voB);
-    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+  if (grp == 1) {  // slices 0 and 1
+#pragma unroll
+    for (int q = 0; q < NI; ++q) issue_one(S0{}, 0, voA, voB, q);
+    if (nk > 1) {
+#pragma unroll
+      for (int q = 0; q < NI; ++q) issue_one(S1{}, PBK, voA, voB, q);
+    }
+    asm volatile("s_waitcnt vmcnt(0)\n\ts_barrier\n\ts_barrier" ::: "memory");  // + one phase behind
   } else {
-    asm volatile("s_barrier" ::: "memory");  // group 1 starts one phase behind
+    asm volatile("s_barrier" ::: "memory");
   }
   __builtin_amdgcn_sched_barrier(0);
   for (int it = 0; it < nk; it += 2) {
-    read_phase(S0{}, it);
-    compute_phase();
+    read_phase(S0{});
+    compute_phase(S0{}, it);
     if (it + 1 < nk) {
-      read_phase(S1{}, it + 1);
-      compute_phase();
+      read_phase(S1{});
+      compute_phase(S1{}, it + 1);
     }
   }
   gemm_epilogue32<BM, BN, WMW, WNW, EPI>(g, acc, n_tile, m0, wm, wn, lane);
-  if (grp == 0) asm volatile("s_barrier" ::: "memory");  // the barrier group 1 took first
+  if (grp == 0) asm volatile("s_barrier" ::: "memory");  // matches group 1's extra first barrier
 }
 
 // MXFP8 (W8A16) split-K tiles for decode-sized M, on v_mfma_f32_32x32x16_bf16. The
