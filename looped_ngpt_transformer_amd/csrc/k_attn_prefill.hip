@@ -6,21 +6,29 @@
 // attention").
 //
 // Work-group = (tile of <= 64 consecutive query rows of one sequence, KV head): 8
-// waves, wave = (query head g of the group, 32-row half of the tile), two waves per
-// SIMD. Per 64-key KV page, with v_mfma_f32_32x32x16_bf16 (on gfx950 about 1.5x the
-// rate of the 16x16x32 form):
+// waves, wave = (query head g of the group, 32-row half hh of the tile); the waves of
+// half 0 (group A) and half 1 (group B) put one wave of each group on every SIMD. Per
+// 64-key KV page, with v_mfma_f32_32x32x16_bf16 (on gfx950 about 1.5x the rate of the
+// 16x16x32 form):
 //   S^T = K Q^T   (A = K rows from LDS, B = Q in registers): two 32-key blocks whose
 //   rows are read in the key order 16 (r / 16) + 8 ((r / 4) % 2) + 4 ((r / 8) % 2) + r % 4,
 //   so that each lane's eight accumulators of a 16-key step hold 8 consecutive keys;
 //   online softmax per query in registers (lanes l and l + 32 share query l % 32),
 //   O^T += V^T P^T (A = V^T from LDS, one 16-byte chunk of 8 consecutive keys per lane;
 //   B = P straight from the S^T accumulators).
+// Each wave alternates two phases per page, separated by work-group barriers:
+//   matrix phase:  O^T += V^T P^T of the previous page, then S^T of this page (MFMA)
+//   softmax phase: masks, running maximum, exponentials, sums, rescale (VALU)
+// and group B runs one phase behind group A, so on every SIMD one wave's softmax
+// overlaps the other wave's MFMAs instead of both waiting for the same unit.
 // The page's K and V blocks are stored as 1 KiB groups of 16-byte chunks in MFMA
-// fragment order; they go straight from HBM into LDS (global_load_lds, three stages:
-// two pages in flight while one is consumed), the K groups at a padded stride so that
-// the 32x32 fragment reads are free of bank conflicts. Keys beyond the chunk's last position
-// are masked out of the softmax; their V entries are multiplied by zero probabilities
-// and hold zeros or stale finite values (pages are cleared when first allocated).
+// fragment order; they go straight from HBM into LDS (global_load_lds) through three
+// stages: group B issues page p + 2 during its softmax phase of page p and waits for it
+// at the end of its next matrix phase, one phase before group A first reads it. The K
+// groups sit at a padded stride so that the 32x32 fragment reads are free of bank
+// conflicts. Keys beyond the chunk's last position are masked out of the softmax; their
+// V entries are multiplied by zero probabilities and hold zeros or stale finite values
+// (pages are cleared when first allocated).
 #include <type_traits>
 
 #include "common.h"
@@ -37,20 +45,6 @@ constexpr int PF_MAX_PAGES = 4096;  // positions up to 262144
 typedef __attribute__((address_space(3))) void* pf_lds_t;
 typedef __attribute__((address_space(1))) void* pf_gbl_t;
 
-// s_waitcnt vmcnt(n) for the few run-time values the page pipeline needs
-__device__ __forceinline__ void pf_wait_vmcnt(int n) {
-  switch (n) {
-    case 0: asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); break;
-    case 1: asm volatile("s_waitcnt vmcnt(1)" ::: "memory"); break;
-    case 2: asm volatile("s_waitcnt vmcnt(2)" ::: "memory"); break;
-    case 3: asm volatile("s_waitcnt vmcnt(3)" ::: "memory"); break;
-    case 4: asm volatile("s_waitcnt vmcnt(4)" ::: "memory"); break;
-    case 5: asm volatile("s_waitcnt vmcnt(5)" ::: "memory"); break;
-    case 6: asm volatile("s_waitcnt vmcnt(6)" ::: "memory"); break;
-    default: asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); break;
-  }
-}
-
 template <int D>
 __global__ __launch_bounds__(PF_THREADS) void k_attn_prefill(AttnArgs a) {
   constexpr int G = 4;
@@ -66,9 +60,9 @@ __global__ __launch_bounds__(PF_THREADS) void k_attn_prefill(AttnArgs a) {
   constexpr int VGS = 1024;
   constexpr int STAGE = NG * (KGS + VGS);  // bytes per page stage
   constexpr int NSTAGE = 3;
-  constexpr int GPW = (2 * NG + PF_WAVES - 1) / PF_WAVES;  // load instructions per wave per page
+  constexpr int GPB = 2 * NG / 4;  // load instructions per group-B wave per page
   static_assert(D % 32 == 0 && DC >= 1 && (DC == 5 || 128 % DC == 0), "head dim");
-  static_assert(GPW <= 6, "vmcnt range of the page pipeline");
+  static_assert((2 * NG) % 4 == 0 && 2 * GPB <= 63, "page loads split over four waves, vmcnt range");
 
   // one array per stage: LDS reads of one stage are then known not to alias the
   // direct-to-LDS loads in flight into the others, so they need not wait for them
@@ -86,8 +80,9 @@ __global__ __launch_bounds__(PF_THREADS) void k_attn_prefill(AttnArgs a) {
   const int hk = blockIdx.y;
   const int32_t* tl = a.tiles + 4 * tile;
   const int row0 = tl[0], nrows = tl[1], pos0 = tl[2], seq = tl[3];
-  const int t = threadIdx.x, lane = t & 63, w = t >> 6;
-  const int g = w >> 1, hh = w & 1;  // query head, 32-row half
+  const int t = threadIdx.x, lane = t & 63;
+  const int w = __builtin_amdgcn_readfirstlane(t >> 6) & (PF_WAVES - 1);
+  const int g = w & 3, hh = w >> 2;  // query head, 32-row half = group (A: 0, B: 1)
   const int h = hk * G + g;
   const int HqD = a.Hq * D;
   const int l32 = lane & 31, lh = lane >> 5;
@@ -96,6 +91,7 @@ __global__ __launch_bounds__(PF_THREADS) void k_attn_prefill(AttnArgs a) {
   const bool full = a.window == 0;
   const int klo = full ? 0 : max(0, pos0 - a.window + 1);
   const int pg_lo = klo / PAGE, pg_hi = kmax / PAGE;
+  const int npg = pg_hi - pg_lo;  // pages pg_lo .. pg_lo + npg
   const int32_t* trow = a.kv.table + ((size_t)seq * a.kv.n_streams + a.stream_idx) * a.kv.tab_len;
   const bf16_t* pool = (const bf16_t*)a.kv.pool;
 
@@ -111,28 +107,26 @@ __global__ __launch_bounds__(PF_THREADS) void k_attn_prefill(AttnArgs a) {
     qf[c] = __builtin_bit_cast(bf16x8, v);
   }
 
-  for (int i = t; i <= pg_hi - pg_lo; i += PF_THREADS) pages[i] = trow[(pg_lo + i) % a.kv.ring];
+  for (int i = t; i <= npg; i += PF_THREADS) pages[i] = trow[(pg_lo + i) % a.kv.ring];
   __syncthreads();
 
-  // page pg -> stage: wave w loads groups w, w + 8, ... (K groups 0..NG-1, then V)
-  auto issue = [&](int pg, auto S) {
-    const int32_t page = pages[pg - pg_lo];
+  // relative page r -> its stage S (r % 3): group-B wave g loads groups g, g + 4, ...
+  // (K groups 0..NG-1, then V)
+  auto issue = [&](int r, auto S) {
+    const int32_t page = pages[r];
     const unsigned char* kb = (const unsigned char*)(pool + (size_t)page * a.kv.page_elems + (size_t)hk * 64 * D);
     const unsigned char* vb = (const unsigned char*)(pool + (size_t)page * a.kv.page_elems + (size_t)(a.kv.Hkv + hk) * 64 * D);
     unsigned char* st0 = stage_ptr(S);
 #pragma unroll
-    for (int q = 0; q < GPW; ++q) {
-      const int grp = w + PF_WAVES * q;
-      if (grp < 2 * NG) {
-        const bool isv = grp >= NG;
-        const int gi = isv ? grp - NG : grp;
-        const unsigned char* src = (isv ? vb : kb) + gi * 1024 + lane * 16;
-        unsigned char* dst = st0 + (isv ? NG * KGS + gi * VGS : gi * KGS);
-        __builtin_amdgcn_global_load_lds((pf_gbl_t)src, (pf_lds_t)dst, 16, 0, 0);
-      }
+    for (int q = 0; q < GPB; ++q) {
+      const int grp = g + 4 * q;
+      const bool isv = grp >= NG;
+      const int gi = isv ? grp - NG : grp;
+      const unsigned char* src = (isv ? vb : kb) + gi * 1024 + lane * 16;
+      unsigned char* dst = st0 + (isv ? NG * KGS + gi * VGS : gi * KGS);
+      __builtin_amdgcn_global_load_lds((pf_gbl_t)src, (pf_lds_t)dst, 16, 0, 0);
     }
   };
-  const int my_inst = __builtin_amdgcn_readfirstlane((2 * NG - w + PF_WAVES - 1) / PF_WAVES);
 
   // per-lane parts of the fragment addresses (bytes within a stage)
   //   K fragment (key block hf, 16-channel step c), A row l32 = key
@@ -150,47 +144,72 @@ __global__ __launch_bounds__(PF_THREADS) void k_attn_prefill(AttnArgs a) {
   for (int cb = 0; cb < CB; ++cb)
 #pragma unroll
     for (int r = 0; r < 16; ++r) o[cb][r] = 0.f;
+  // S^T[key 32 kb + 16 (r / 8) + 8 lh + r % 8][query l32] of the current page, and the
+  // previous page's probabilities as P^T fragments (slot e of 16-key step s: key
+  // 16 s + 8 lh + e, accumulator 8 (s % 2) + e of block s / 2)
+  f32x16 st[2];
+  bf16x8 pf[4];
 
-  // one page per step from LDS buffer (pg - pg_lo) & 1; the next page's tiles go to the
-  // other buffer (its readers passed the previous barrier) while the page after that is
-  // loaded into registers
-  auto compute = [&](int pg, auto S) {
-    const unsigned char* st0 = stage_ptr(S);
-    // S^T[key 32 kb + 16 (r / 8) + 8 lh + r % 8][query l32]
-    f32x16 st[2];
+  auto barrier = [&]() {
+    __builtin_amdgcn_sched_barrier(0);
+    asm volatile("s_barrier" ::: "memory");
+    __builtin_amdgcn_sched_barrier(0);
+  };
+  // matrix phase: O^T += V^T P^T of relative page r - 1 (stage SV), then S^T of page r
+  // (stage SK); group B then waits for the page it issued in its last softmax phase
+  auto matrix_phase = [&](bool pv, bool sk, auto SK, auto SV) {
+    if (pv) {
+      const unsigned char* sv = stage_ptr(SV);
 #pragma unroll
-    for (int kb = 0; kb < 2; ++kb)
+      for (int s = 0; s < 4; ++s)  // the CB output blocks interleaved: independent chains
 #pragma unroll
-      for (int r = 0; r < 16; ++r) st[kb][r] = 0.f;
-#pragma unroll
-    for (int c = 0; c < KS; ++c) {  // the two key blocks interleaved: independent chains
-#pragma unroll
-      for (int kb = 0; kb < 2; ++kb) {
-        const int off = (2 * kb * DC + (c >> 1)) * KGS + (c & 1) * 32 * 16;
-        const bf16x8 kf = *(const bf16x8*)(st0 + koff + off);
-        st[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf, qf[c], st[kb], 0, 0, 0);
-      }
+        for (int cb = 0; cb < CB; ++cb) {
+          const bf16x8 vf = *(const bf16x8*)(sv + voff + ((s >> 1) * CB16 + 2 * cb) * VGS + (s & 1) * 32 * 16);
+          o[cb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf, pf[s], o[cb], 0, 0, 0);
+        }
     }
-    // online softmax for query l32 over this lane's 32 keys and the partner lane's 32.
-    // Pages every query of the tile sees in full skip the per-key masks.
+    if (sk) {
+      const unsigned char* sk0 = stage_ptr(SK);
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) st[kb][r] = 0.f;
+#pragma unroll
+      for (int c = 0; c < KS; ++c)  // the two key blocks interleaved: independent chains
+#pragma unroll
+        for (int kb = 0; kb < 2; ++kb) {
+          const int off = (2 * kb * DC + (c >> 1)) * KGS + (c & 1) * 32 * 16;
+          const bf16x8 kf = *(const bf16x8*)(sk0 + koff + off);
+          st[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf, qf[c], st[kb], 0, 0, 0);
+        }
+    }
+    if (hh == 1) asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    barrier();
+  };
+  // softmax phase of relative page r (absolute pg_lo + r); group B also issues page
+  // r + 2 into stage SI
+  auto softmax_phase = [&](int r, auto SI) {
+    if (hh == 1 && r + 2 <= npg) issue(r + 2, SI);
+    const int pg = pg_lo + r;
+    // pages every query of the tile sees in full skip the per-key masks
     const bool all_vis = pg * PAGE + PAGE - 1 <= pos0 && (full || pos0 + nrows - 1 - pg * PAGE < a.window);
     float mt = -INFINITY;
     if (all_vis) {
 #pragma unroll
       for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
-        for (int r = 0; r < 16; ++r) mt = fmaxf(mt, st[kb][r]);
+        for (int e = 0; e < 16; ++e) mt = fmaxf(mt, st[kb][e]);
     } else {
       const int wlim = full ? 0x7fffffff : a.window;  // keys visible at 0 <= qpos - kpos < wlim
       const int d0 = qv ? qpos - pg * PAGE - 8 * lh : -1;
 #pragma unroll
       for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          const int dlt = d0 - (32 * kb + 16 * (r >> 3) + (r & 7));  // qpos - kpos
+        for (int e = 0; e < 16; ++e) {
+          const int dlt = d0 - (32 * kb + 16 * (e >> 3) + (e & 7));  // qpos - kpos
           const bool vis = (dlt >= 0) & (dlt < wlim);
-          st[kb][r] = vis ? st[kb][r] : -INFINITY;
-          mt = fmaxf(mt, st[kb][r]);
+          st[kb][e] = vis ? st[kb][e] : -INFINITY;
+          mt = fmaxf(mt, st[kb][e]);
         }
     }
     // raw logits so far: the running maximum is kept in scaled (log2) units, the scale
@@ -204,9 +223,9 @@ __global__ __launch_bounds__(PF_THREADS) void k_attn_prefill(AttnArgs a) {
 #pragma unroll
     for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        const float p = __builtin_amdgcn_exp2f(fmaf(st[kb][r], sl2, -m_ref));  // exp2(-inf) = 0
-        st[kb][r] = p;
+      for (int e = 0; e < 16; ++e) {
+        const float p = __builtin_amdgcn_exp2f(fmaf(st[kb][e], sl2, -m_ref));  // exp2(-inf) = 0
+        st[kb][e] = p;
         ps += p;
       }
     ps += __shfl_xor(ps, 32, 64);
@@ -218,9 +237,6 @@ __global__ __launch_bounds__(PF_THREADS) void k_attn_prefill(AttnArgs a) {
     }
     l_run += ps;
     m_run = m_new;
-    // P^T fragment of 16-key step s: slot e is key 16 s + 8 lh + e (accumulator
-    // 8 (s % 2) + e of block s / 2)
-    bf16x8 pf[4];
 #pragma unroll
     for (int s = 0; s < 4; ++s) {
       uint32_t u[4];
@@ -228,40 +244,56 @@ __global__ __launch_bounds__(PF_THREADS) void k_attn_prefill(AttnArgs a) {
       for (int e = 0; e < 8; e += 2) u[e / 2] = pack_bf16x2(st[s >> 1][8 * (s & 1) + e], st[s >> 1][8 * (s & 1) + e + 1]);
       pf[s] = __builtin_bit_cast(bf16x8, make_uint4(u[0], u[1], u[2], u[3]));
     }
-    // O^T[channel 32 cb + 8 (r / 4) + 4 lh + r % 4][query l32] += V^T P^T
-#pragma unroll
-    for (int s = 0; s < 4; ++s) {  // the CB output blocks interleaved: independent chains
-#pragma unroll
-      for (int cb = 0; cb < CB; ++cb) {
-        const bf16x8 vf = *(const bf16x8*)(st0 + voff + ((s >> 1) * CB16 + 2 * cb) * VGS + (s & 1) * 32 * 16);
-        o[cb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf, pf[s], o[cb], 0, 0, 0);
-      }
-    }
+    barrier();
   };
 
-  // three-stage page pipeline: pages pg+1 and pg+2 load while pg is consumed; the loop
-  // is unrolled by the stage count so every stage index is a compile-time constant
   using S0 = std::integral_constant<int, 0>;
   using S1 = std::integral_constant<int, 1>;
   using S2 = std::integral_constant<int, 2>;
-  auto step = [&](int pg, auto S, auto S_next2) {
-    pf_wait_vmcnt(pg + 1 <= pg_hi ? my_inst : 0);  // page pg has landed (this wave's part)
-    __syncthreads();                                // ... and every wave's; stage of pg-1 free
-    if (pg + 2 <= pg_hi) issue(pg + 2, S_next2);
-    compute(pg, S);
-  };
-  issue(pg_lo, S0{});
-  if (pg_lo + 1 <= pg_hi) issue(pg_lo + 1, S1{});
-  for (int pg = pg_lo; pg <= pg_hi; pg += 3) {
-    step(pg, S0{}, S2{});
-    if (pg + 1 <= pg_hi) step(pg + 1, S1{}, S0{});
-    if (pg + 2 <= pg_hi) step(pg + 2, S2{}, S1{});
+  if (hh == 1) {  // pages 0 and 1, then one phase behind group A
+    issue(0, S0{});
+    if (npg >= 1) issue(1, S1{});
+    asm volatile("s_waitcnt vmcnt(0)\n\ts_barrier\n\ts_barrier" ::: "memory");
+  } else {
+    asm volatile("s_barrier" ::: "memory");
+  }
+  __builtin_amdgcn_sched_barrier(0);
+  // relative page r lives in stage r % 3; the loop is unrolled by the stage count so
+  // every stage index is a compile-time constant
+  for (int r = 0; r <= npg; r += 3) {
+    matrix_phase(r > 0, true, S0{}, S2{});
+    softmax_phase(r, S2{});
+    if (r + 1 <= npg) {
+      matrix_phase(true, true, S1{}, S0{});
+      softmax_phase(r + 1, S0{});
+    }
+    if (r + 2 <= npg) {
+      matrix_phase(true, true, S2{}, S1{});
+      softmax_phase(r + 2, S1{});
+    }
+  }
+  // O^T += V^T P^T of the last page
+  switch (npg % 3) {
+    case 0: matrix_phase(true, false, S1{}, S0{}); break;
+    case 1: matrix_phase(true, false, S2{}, S1{}); break;
+    default: matrix_phase(true, false, S0{}, S2{}); break;
   }
 
-  // epilogue: normalise, gate, store; lane holds 4 consecutive channels per (cb, r / 4)
+  // epilogue: normalise, gate, store; lane holds 4 consecutive channels per (cb, r / 4).
+  // The bf16 gate pre-activations of those channels (8 bytes each) are all requested
+  // before the first is used.
   if (qv) {
     const float invl = 1.f / l_run;
     const size_t base = (size_t)(row0 + qi) * HqD + (size_t)h * D;
+    uint2 graw[CB][4];
+    const bool gbf = a.g && !a.g_f32;
+    if (gbf) {
+      const bf16_t* gr = (const bf16_t*)a.g + (size_t)(row0 + qi) * a.g_ld + (size_t)h * D + 4 * lh;
+#pragma unroll
+      for (int cb = 0; cb < CB; ++cb)
+#pragma unroll
+        for (int rb = 0; rb < 4; ++rb) graw[cb][rb] = *(const uint2*)(gr + 32 * cb + 8 * rb);
+    }
 #pragma unroll
     for (int cb = 0; cb < CB; ++cb) {
 #pragma unroll
@@ -270,7 +302,14 @@ __global__ __launch_bounds__(PF_THREADS) void k_attn_prefill(AttnArgs a) {
         float v[4];
 #pragma unroll
         for (int r = 0; r < 4; ++r) v[r] = o[cb][4 * rb + r] * invl;
-        if (a.g) {
+        if (gbf) {
+          const uint32_t gw[2] = {graw[cb][rb].x, graw[cb][rb].y};
+#pragma unroll
+          for (int r = 0; r < 4; ++r) {
+            const float x = __uint_as_float((gw[r >> 1] >> (16 * (r & 1))) << 16);
+            v[r] *= 1.f / (1.f + __expf(-x));
+          }
+        } else if (a.g) {
 #pragma unroll
           for (int r = 0; r < 4; ++r)
             v[r] *= gate_at(a.g, a.g_f32, a.g_ld, a.g_splits, a.g_sstride, row0 + qi, h * D + c + r);
@@ -282,6 +321,7 @@ __global__ __launch_bounds__(PF_THREADS) void k_attn_prefill(AttnArgs a) {
       }
     }
   }
+  if (hh == 0) asm volatile("s_barrier" ::: "memory");  // matches group B's extra first barrier
 }
 
 hipError_t launch_attn_prefill(const AttnArgs& a, hipStream_t st) {
