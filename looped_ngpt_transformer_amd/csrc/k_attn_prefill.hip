@@ -138,6 +138,23 @@ __global__ __launch_bounds__(PF_THREADS) void k_attn_prefill(AttnArgs a) {
   //   chunk (2 (s % 2) + lh) 16 + l32 % 16 (keys 16 s + 8 lh .. + 7 of channel l32)
   const int voff = NG * KGS + (l32 >> 4) * VGS + (lh * 16 + (l32 & 15)) * 16;
   const float sl2 = a.scale * 1.4426950408889634f;  // logits in log2 units
+  // With q and k L2-normalised and scaled by s_qk, |q.k| <= max s_qk^2, so no logit
+  // exceeds B = scale * max s_qk^2 (log2 units here, with a margin for the bf16 rounding
+  // of q and k). Softmax is unchanged by the shift, so B serves as a fixed reference in
+  // place of the running maximum whenever the smallest probability, 2^(-2B), stays a
+  // normal number: no maximum, no rescaling of the accumulators.
+  float bound = INFINITY;
+  if (a.s_qk) {
+    float m = 0.f;
+    for (int i = lane; i < D; i += 64) m = fmaxf(m, fabsf(a.s_qk[i]));
+#pragma unroll
+    for (int o2 = 32; o2 >= 1; o2 >>= 1) m = fmaxf(m, __shfl_xor(m, o2, 64));
+    bound = sl2 * m * m * 1.02f + 0.5f;
+  }
+  const bool fixed_ref = sl2 > 0.f && bound < 60.f;  // uniform over the work-group
+  // m_run: running maximum (log2 units) of the query's visible logits; l_run: this
+  // lane's part (its 32 keys of each page) of the softmax denominator, relative to the
+  // current reference
   float m_run = -INFINITY, l_run = 0.f;
   f32x16 o[CB];
 #pragma unroll
@@ -193,6 +210,29 @@ __global__ __launch_bounds__(PF_THREADS) void k_attn_prefill(AttnArgs a) {
     const int pg = pg_lo + r;
     // pages every query of the tile sees in full skip the per-key masks
     const bool all_vis = pg * PAGE + PAGE - 1 <= pos0 && (full || pos0 + nrows - 1 - pg * PAGE < a.window);
+    if (fixed_ref) {
+      if (!all_vis) {
+        const int wlim = full ? 0x7fffffff : a.window;  // keys visible at 0 <= qpos - kpos < wlim
+        const int d0 = qv ? qpos - pg * PAGE - 8 * lh : -1;
+#pragma unroll
+        for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+          for (int e = 0; e < 16; ++e) {
+            const int dlt = d0 - (32 * kb + 16 * (e >> 3) + (e & 7));  // qpos - kpos
+            st[kb][e] = (dlt >= 0) & (dlt < wlim) ? st[kb][e] : -INFINITY;
+          }
+      }
+      float ps[2] = {0.f, 0.f};
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+        for (int e = 0; e < 16; ++e) {
+          const float p = __builtin_amdgcn_exp2f(fmaf(st[kb][e], sl2, -bound));  // exp2(-inf) = 0
+          st[kb][e] = p;
+          ps[kb] += p;
+        }
+      l_run += ps[0] + ps[1];
+    } else {
     float mt = -INFINITY;
     if (all_vis) {
 #pragma unroll
@@ -219,24 +259,24 @@ __global__ __launch_bounds__(PF_THREADS) void k_attn_prefill(AttnArgs a) {
     // a query that has seen no visible key yet keeps m = -inf; its (all -inf) logits
     // give p = exp2(-inf) = 0 against a finite reference instead of NaN
     const float m_ref = m_new == -INFINITY ? 0.f : m_new;
-    float ps = 0.f;
+    float ps[2] = {0.f, 0.f};
 #pragma unroll
     for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
       for (int e = 0; e < 16; ++e) {
         const float p = __builtin_amdgcn_exp2f(fmaf(st[kb][e], sl2, -m_ref));  // exp2(-inf) = 0
         st[kb][e] = p;
-        ps += p;
+        ps[kb] += p;
       }
-    ps += __shfl_xor(ps, 32, 64);
     if (!__all(m_new == m_run)) {  // rescale only when some query's maximum moved
       const float corr = m_run == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(m_run - m_new);
       l_run *= corr;
 #pragma unroll
       for (int cb = 0; cb < CB; ++cb) o[cb] *= corr;
     }
-    l_run += ps;
+    l_run += ps[0] + ps[1];
     m_run = m_new;
+    }
 #pragma unroll
     for (int s = 0; s < 4; ++s) {
       uint32_t u[4];
@@ -282,8 +322,9 @@ __global__ __launch_bounds__(PF_THREADS) void k_attn_prefill(AttnArgs a) {
   // epilogue: normalise, gate, store; lane holds 4 consecutive channels per (cb, r / 4).
   // The bf16 gate pre-activations of those channels (8 bytes each) are all requested
   // before the first is used.
+  const float lsum = l_run + __shfl_xor(l_run, 32, 64);  // both halves of the query's keys
   if (qv) {
-    const float invl = 1.f / l_run;
+    const float invl = 1.f / lsum;
     const size_t base = (size_t)(row0 + qi) * HqD + (size_t)h * D;
     uint2 graw[CB][4];
     const bool gbf = a.g && !a.g_f32;

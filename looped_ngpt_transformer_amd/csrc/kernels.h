@@ -105,6 +105,9 @@ struct AttnArgs {
   const int32_t* row_seq = nullptr;
   int window = 0;                 // 0 = full attention
   float scale = 1.f;
+  // per-channel query-key scale when q and k were L2-normalised and scaled by it (null
+  // otherwise): then every logit is bounded by scale * max s_qk^2
+  const float* s_qk = nullptr;
   KVLayout kv;
   int stream_idx = 0;
   int max_pos = 0;                // largest position among the rows (host-known)

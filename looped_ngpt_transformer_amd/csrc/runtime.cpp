@@ -528,6 +528,7 @@ int run_layer(dory_ctx* ctx, hipStream_t st, const CallPlan& P, int l, int slot,
   aa.row_seq = meta + c.max_rows;
   aa.window = full ? 0 : c.window;
   aa.scale = c.attn_scale;
+  aa.s_qk = c.qk_norm ? w.s_qk : nullptr;
   aa.kv = ra.kv;
   aa.stream_idx = sidx;
   aa.max_pos = P.max_pos;

@@ -32,10 +32,12 @@ def sharpen(w, a_attn=1.0, a_mlp=0.5):
 
 
 def _run_case(shape, k, mode, schedule, max_rows=256, max_seq_len=512, max_seqs=4, wseed=7,
-              sharp=False):
+              sharp=False, wmod=None):
     w = gpu_weights(shape, wseed)
     if sharp:
         sharpen(w)
+    if wmod:
+        wmod(w)
     rt = DoryRuntime(shape, w, max_loops=4, max_seqs=max_seqs, max_seq_len=max_seq_len,
                      max_rows=max_rows, mode=mode, loops=k)
     got = run_schedule(rt, schedule)
@@ -93,6 +95,26 @@ def test_bf16_small_sharp_rates(mode):
              ("prefill", [(0, xin(S, 90, 73)), (1, xin(S, 20, 74))]),
              ("decode", [(1, xin(S, 1, 75)), (0, xin(S, 1, 76))])]
     _run_case(S, 2, mode, sched, max_rows=256, max_seq_len=512, max_seqs=2, sharp=True)
+
+
+@pytest.mark.parametrize("variant", ["no_qk_norm", "one_large_s_qk"])
+def test_bf16_attention_running_maximum(variant):
+    """The prefill attention's running-maximum softmax: without QK norm the logits have
+    no bound, and with one s_qk channel at 2.5 the bound (scale * max s_qk^2, about 116 in
+    log2 units) is too large for a fixed reference. (Raising every channel instead makes
+    the case chaotic: the oracle alone moves to cosine 0.95 when s_qk = 2 becomes 2.002.)
+    Sharp rates so attention errors reach the final states."""
+    S = dict(PSMALL, qk_norm=0) if variant == "no_qk_norm" else PSMALL
+
+    def widen(w):
+        for lw in w:
+            lw["s_qk"].fill_(1.0)
+            lw["s_qk"][-1] = 2.5
+    sched = [("prefill", [(0, xin(S, 150, 91))]),
+             ("decode", [(0, xin(S, 1, 92))]),
+             ("prefill", [(0, xin(S, 70, 93)), (1, xin(S, 40, 94))])]
+    _run_case(S, 2, "per_loop", sched, max_rows=256, max_seq_len=512, max_seqs=2, sharp=True,
+              wmod=widen if variant == "one_large_s_qk" else None)
 
 
 def test_tiny_fp32_sharp_rates():
