@@ -3,7 +3,8 @@
 // s <- N((1 - a) * s + a * N(y))  — the nGPT update ("Dory1.0-4B" paper summary,
 // nGPT prerequisite; arXiv summary §2: normalised sublayer output blended with the
 // normalised residual by per-channel rates, then normalised). y arrives as split-K
-// partial sums. The L2 norm the pages put before the output and down projections (arXiv
+// partial sums (decode) or as one bf16 array (prefill: the sublayer output in the
+// activation type). The L2 norm the pages put before the output and down projections (arXiv
 // §2) scales y's row by a positive factor, which N(y) removes, so it needs no work.
 // Loop boundaries (paper summary, core-method equation): at the end of the input block
 // x is saved and u_1 = N(x + x); at the end of loop t, s_t = N(.) and, unless t = k,
@@ -40,7 +41,9 @@ __global__ __launch_bounds__(UPD_THREADS) void k_update(UpdateArgs u) {
     float y = 0.f;
     sv[k] = av[k] = xv[k] = 0.f;
     if (i < H) {
-      for (int sp = 0; sp < u.splits; ++sp) y += u.y[(size_t)sp * u.M * H + row + i];
+      if (u.y_bf16) y = bf2f(((const bf16_t*)u.y)[row + i]);
+      else
+        for (int sp = 0; sp < u.splits; ++sp) y += u.y[(size_t)sp * u.M * H + row + i];
       sv[k] = u.s[row + i];
       av[k] = u.alpha[i];
       if (need_x) xv[k] = u.x[row + i];

@@ -48,6 +48,7 @@ struct UpdateArgs {
   const float* y = nullptr;  // [splits][M][H] raw sublayer output (partial sums); any
                              // positive row scale (the pre-projection norms) cancels in N(y)
   int splits = 1;
+  int y_bf16 = 0;            // y is one bf16 [M][H] array instead (splits == 1)
   float* s = nullptr;        // [M, H] state, updated in place
   float* s_out = nullptr;    // where the new state goes (== s, or the caller's output)
   void* sb = nullptr;        // [M, H] act-type copy of the new state (GEMM operand)

@@ -444,10 +444,11 @@ int run_layer(dory_ctx* ctx, hipStream_t st, const CallPlan& P, int l, int slot,
            (double)g.N * g.K * wbytes + (double)g.M * g.K * D.esz + (double)g.M * ncols * outb);
     return e;
   };
-  auto update = [&](int splits, const float* alpha, int b, float* sout) {
+  auto update = [&](int splits, const float* alpha, int b, float* sout, bool ybf = false) {
     UpdateArgs u;
     u.y = part;
     u.splits = splits;
+    u.y_bf16 = ybf;
     u.s = s;
     u.s_out = sout ? sout : s;
     u.sb = ws + W.sb;
@@ -459,7 +460,7 @@ int run_layer(dory_ctx* ctx, hipStream_t st, const CallPlan& P, int l, int slot,
     u.bnd = b;
     Prof pr(ctx, st, DORY_KC_UPDATE);
     const hipError_t e = launch_update(u, st);
-    pr.end(0, (double)M * D.H * (4.0 * splits + 4 + 4 + D.esz));
+    pr.end(0, (double)M * D.H * ((ybf ? 2.0 : 4.0 * splits) + 4 + 4 + D.esz));
     return e;
   };
 
@@ -552,7 +553,7 @@ int run_layer(dory_ctx* ctx, hipStream_t st, const CallPlan& P, int l, int slot,
            keys * 2.0 * D.Nkv * D.esz + (double)M * 3 * D.Nq * D.esz);
   }
 
-  // ---- output projection + nGPT update (pre-projection norm as a row scale)
+  // ---- output projection + nGPT update (the pre-projection norm cancels in N(y))
   if (f32) {
     HIPCHK(run_gemm(gemm(ws + W.o, D.Nq, w.w_o, nullptr, D.H, EPI_F32, part, D.H, 1)), "gemm o");
     HIPCHK(update(1, w.alpha_attn, BND_NONE, nullptr), "update attn");
@@ -560,9 +561,9 @@ int run_layer(dory_ctx* ctx, hipStream_t st, const CallPlan& P, int l, int slot,
     S = gemm_pick_splits(M, D.H, D.Nq, wf);
     HIPCHK(run_gemm(gemm(ws + W.o, D.Nq, w.w_o, w.s_o, D.H, EPI_PARTIAL, part, D.H, S)), "gemm o");
     HIPCHK(update(S, w.alpha_attn, BND_NONE, nullptr), "update attn");
-  } else {
-    HIPCHK(run_gemm(gemm(ws + W.o, D.Nq, w.w_o, w.s_o, D.H, EPI_F32, part, D.H, 1)), "gemm o");
-    HIPCHK(update(1, w.alpha_attn, BND_NONE, nullptr), "update attn");
+  } else {  // prefill: the sublayer output in the activation type (bf16)
+    HIPCHK(run_gemm(gemm(ws + W.o, D.Nq, w.w_o, w.s_o, D.H, EPI_STORE_ACT, part, D.H, 1)), "gemm o");
+    HIPCHK(update(1, w.alpha_attn, BND_NONE, nullptr, true), "update attn");
   }
 
   // ---- MLP sublayer
@@ -581,8 +582,8 @@ int run_layer(dory_ctx* ctx, hipStream_t st, const CallPlan& P, int l, int slot,
     GemmArgs g = gemm(ws + W.sb, D.H, w.w_gu, w.s_gu, 2 * D.I, EPI_SWIGLU, ws + W.h, D.I, 1);
     g.n_half = D.I;
     HIPCHK(run_gemm(g), "gemm gu");
-    HIPCHK(run_gemm(gemm(ws + W.h, D.I, w.w_down, w.s_down, D.H, EPI_F32, part, D.H, 1)), "gemm down");
-    HIPCHK(update(1, w.alpha_mlp, bnd, out), "update mlp");
+    HIPCHK(run_gemm(gemm(ws + W.h, D.I, w.w_down, w.s_down, D.H, EPI_STORE_ACT, part, D.H, 1)), "gemm down");
+    HIPCHK(update(1, w.alpha_mlp, bnd, out, true), "update mlp");
   }
   return DORY_OK;
 }
