@@ -17,11 +17,8 @@ __global__ __launch_bounds__(256) void k_swiglu(const float* gu, int splits, int
   const size_t row = (size_t)m * 2 * I;
   const int i1 = min(I, (b + 1) * 1024);
   for (int i = b * 1024 + threadIdx.x; i < i1; i += blockDim.x) {
-    float g = 0.f, u = 0.f;
-    for (int s = 0; s < splits; ++s) {
-      g += gu[s * sstride + row + i];
-      u += gu[s * sstride + row + I + i];
-    }
+    const float g = sum_splits(gu + row + i, sstride, splits);
+    const float u = sum_splits(gu + row + I + i, sstride, splits);
     st<T>(h, (size_t)m * I + i, g / (1.f + __expf(-g)) * u);
   }
 }

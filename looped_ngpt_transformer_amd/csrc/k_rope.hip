@@ -47,10 +47,7 @@ __global__ __launch_bounds__(256) void k_rope_kv(RopeArgs a) {
   const size_t split_stride = (size_t)a.M * a.Nqkvg;
   auto in = [&](int col) -> float {
     if (a.in_f32) {
-      const float* f = (const float*)a.qkvg;
-      float t = 0.f;
-      for (int s = 0; s < a.splits; ++s) t += f[s * split_stride + rowoff + col];
-      return t;
+      return sum_splits((const float*)a.qkvg + rowoff + col, split_stride, a.splits);
     }
     return bf2f(((const bf16_t*)a.qkvg)[rowoff + col]);
   };

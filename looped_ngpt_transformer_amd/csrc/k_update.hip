@@ -38,17 +38,36 @@ __global__ __launch_bounds__(UPD_THREADS) void k_update(UpdateArgs u) {
 #pragma unroll
   for (int k = 0; k < UPD_MAXPER; ++k) {
     const int i = threadIdx.x + k * UPD_THREADS;
-    float y = 0.f;
-    sv[k] = av[k] = xv[k] = 0.f;
+    yv[k] = sv[k] = av[k] = xv[k] = 0.f;
     if (i < H) {
-      if (u.y_bf16) y = bf2f(((const bf16_t*)u.y)[row + i]);
-      else
-        for (int sp = 0; sp < u.splits; ++sp) y += u.y[(size_t)sp * u.M * H + row + i];
+      if (u.y_bf16) yv[k] = bf2f(((const bf16_t*)u.y)[row + i]);
       sv[k] = u.s[row + i];
       av[k] = u.alpha[i];
       if (need_x) xv[k] = u.x[row + i];
     }
-    yv[k] = y;
+  }
+  if (!u.y_bf16) {
+    // split partials: QS splits of every element of the thread requested together
+    constexpr int QS = UPD_MAXPER >= 16 ? 1 : 16 / UPD_MAXPER;
+    const size_t sstride = (size_t)u.M * H;
+    for (int s0 = 0; s0 < u.splits; s0 += QS) {
+      float v[QS][UPD_MAXPER];
+#pragma unroll
+      for (int q = 0; q < QS; ++q)
+#pragma unroll
+        for (int k = 0; k < UPD_MAXPER; ++k) {
+          const int i = threadIdx.x + k * UPD_THREADS;
+          v[q][k] = (s0 + q < u.splits && i < H) ? u.y[(s0 + q) * sstride + row + i] : 0.f;
+        }
+#pragma unroll
+      for (int q = 0; q < QS; ++q)
+#pragma unroll
+        for (int k = 0; k < UPD_MAXPER; ++k) yv[k] += v[q][k];
+    }
+  }
+#pragma unroll
+  for (int k = 0; k < UPD_MAXPER; ++k) {
+    const float y = yv[k];
     const float bs = (1.f - av[k]) * sv[k], ay = av[k] * y;
     acc[0] += y * y;
     acc[1] += bs * bs;
