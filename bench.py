@@ -11,7 +11,7 @@ Also: --workload D runs decode steps of the 72-layer shape (batch 32 over a seed
 k = 4, last_loop); --ks 1,2,4 measures several loop counts.
 
 Prints one JSON line. The roofline object covers the dominant kernel class (the
-projection GEMMs for prefill, attention for decode) from HIP events around each launch
+projection GEMMs for prefill, the split-key attention kernel for decode) from HIP events around each launch
 over the timed region; cpu_baseline times the float64 oracle on a bounded sample.
 """
 from __future__ import annotations
@@ -102,7 +102,7 @@ def roofline_of(stats, kind, workload):
                 "launches": g["launches"], "avg_launch_us": round(1e3 * g["ms"] / g["launches"], 2)}
     a = stats["attention"]
     ach = a["bytes"] / (a["ms"] / 1e3) / 1e9
-    return {"bound": "hbm", "kernel": "attention (paged KV, split over keys)",
+    return {"bound": "hbm", "kernel": "k_attn_decode (split-key decode attention over the paged KV cache)",
             "achieved": round(ach, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
             "frac": round(ach / PEAK_HBM_GBS, 4),
             "traffic": measured_traffic("decode_attention", workload, ["k_attn.hip", "common.h", "kernels.h"]),

@@ -220,18 +220,21 @@ int dory_quantize_mxfp8(void* stream, const void* w, int w_dtype, int64_t rows,
 
 /* ---- tracing: per-kernel-class launch timing with HIP events on the call's stream */
 #define DORY_KC_GEMM 0   /* projections: [q|k|v|gate], output, SwiGLU gate/up, down */
-#define DORY_KC_ATTN 1   /* attention over the KV cache (incl. split combine and gate) */
+#define DORY_KC_ATTN 1   /* attention over the KV cache: the prefill kernel (with gate), or the
+                            split-key kernel of decode and fp32 calls */
 #define DORY_KC_ROPE 2   /* RoPE + QK norm + KV-cache write */
 #define DORY_KC_UPDATE 3 /* nGPT update / loop boundary, input staging */
 #define DORY_KC_SWIGLU 4 /* SwiGLU from split-K partials */
-#define DORY_KC_COUNT 5
+#define DORY_KC_MERGE 5  /* merge of the split-key partials, gate (decode and fp32 calls) */
+#define DORY_KC_COUNT 6
 typedef struct dory_kernel_stats {
   int64_t launches; /* kernel launches recorded */
   double ms;        /* summed event time of those launches */
   double flops;     /* algorithmic FLOPs: GEMM 2*M*N*K; attention 4*Hq*d per visible
                        (query, key) pair */
   double bytes;     /* algorithmic HBM bytes: GEMM weights (+ scales) + activations in and
-                       out; attention K/V entries read (once per row) */
+                       out; attention K/V entries read (once per row) + q; merge partials
+                       read + gate + o */
 } dory_kernel_stats;
 #define DORY_KC_ALL ((1 << DORY_KC_COUNT) - 1)
 /* Start recording the classes in class_mask (bit 1 << DORY_KC_*; counters cleared), or

@@ -425,7 +425,8 @@ __global__ __launch_bounds__(64) void k_decode_merge(AttnArgs a, int nsub) {
 // waves fill the device once (the resident count comes from the occupancy query); at
 // most max_sub splits per group (the merge weighs one split per lane: <= 64).
 template <int D, int NBUF, int WPE>
-static hipError_t launch_decode(const AttnArgs& a, int n_pages, int max_sub, hipStream_t st) {
+static hipError_t launch_decode(const AttnArgs& a, int n_pages, int max_sub, int phase, int* splits_out,
+                                hipStream_t st) {
   static int slots = 0;
   if (!slots) {
     int dev = 0, cus = 0, blocks = 0;
@@ -443,8 +444,11 @@ static hipError_t launch_decode(const AttnArgs& a, int n_pages, int max_sub, hip
   const int pps = (n_pages + nsub - 1) / nsub;
   nsub = (n_pages + pps - 1) / pps;
   const int waves = groups * nsub;
-  hipLaunchKernelGGL((k_attn_decode<D, NBUF, WPE>), dim3((waves + 3) / 4), dim3(256), 0, st, a, nsub, pps);
-  hipLaunchKernelGGL(k_decode_merge<D>, dim3(a.M * a.Hq), dim3(64), 0, st, a, nsub);
+  if (splits_out) *splits_out = nsub;
+  if (phase == ATTN_SPLITS)
+    hipLaunchKernelGGL((k_attn_decode<D, NBUF, WPE>), dim3((waves + 3) / 4), dim3(256), 0, st, a, nsub, pps);
+  else if (phase == ATTN_MERGE)
+    hipLaunchKernelGGL(k_decode_merge<D>, dim3(a.M * a.Hq), dim3(64), 0, st, a, nsub);
   return hipGetLastError();
 }
 
@@ -453,9 +457,9 @@ static hipError_t launch_decode(const AttnArgs& a, int n_pages, int max_sub, hip
 // a page per split, so that the whole range is requested at once.
 constexpr int DECODE_SHORT_PAGES = 32;
 template <int D>
-static hipError_t launch_decode_d(const AttnArgs& a, int n_pages, hipStream_t st) {
-  if (n_pages > DECODE_SHORT_PAGES) return launch_decode<D, 2, 1>(a, n_pages, 16, st);
-  return launch_decode<D, 1, 3>(a, n_pages, 64, st);
+static hipError_t launch_decode_d(const AttnArgs& a, int n_pages, int phase, int* splits, hipStream_t st) {
+  if (n_pages > DECODE_SHORT_PAGES) return launch_decode<D, 2, 1>(a, n_pages, 16, phase, splits, st);
+  return launch_decode<D, 1, 3>(a, n_pages, 64, phase, splits, st);
 }
 
 static int attn_pages_max(int max_pos, int window) {
@@ -479,15 +483,15 @@ size_t attn_rows_part_floats(int M, int Hq, int d, int max_pos, int window) {
   return (size_t)M * Hq * (d + 2);  // one split (minimum); more when the cap allows
 }
 
-hipError_t launch_attn_rows(const AttnArgs& a, hipStream_t st) {
+hipError_t launch_attn_rows(const AttnArgs& a, int phase, int* splits_out, hipStream_t st) {
   if (a.M == 0) return hipSuccess;
   const int G = a.Hq / a.Hkv;
   if (a.kv.act == ACT_BF16 && G == 4 && (a.d == 64 || a.d == 128 || a.d == 160)) {
     // MFMA decode kernel + split merge
     const int n_pages = attn_pages_max(a.max_pos, a.window);
-    if (a.d == 64) return launch_decode_d<64>(a, n_pages, st);
-    if (a.d == 128) return launch_decode_d<128>(a, n_pages, st);
-    return launch_decode_d<160>(a, n_pages, st);
+    if (a.d == 64) return launch_decode_d<64>(a, n_pages, phase, splits_out, st);
+    if (a.d == 128) return launch_decode_d<128>(a, n_pages, phase, splits_out, st);
+    return launch_decode_d<160>(a, n_pages, phase, splits_out, st);
   }
   if (G > ATT_MAXG || a.d > ATT_MAXD || a.d % 8 != 0) return hipErrorInvalidValue;
   const int n_pages = attn_pages_max(a.max_pos, a.window);
@@ -495,13 +499,15 @@ hipError_t launch_attn_rows(const AttnArgs& a, hipStream_t st) {
   attn_pick_splits(a.M, a.Hkv, n_pages, (size_t)a.part_cap, a.Hq, a.d, &splits, &pps);
   const size_t esz = a.kv.act == ACT_F32 ? 4 : 2;
   const size_t shmem = 2 * PAGE * a.d * esz + (ATT_MAXG * a.d + 4 * ATT_MAXG * PAGE + ATT_MAXG * PAGE) * 4;
+  if (splits_out) *splits_out = splits;
   dim3 grid(a.M, a.Hkv, splits);
+  const dim3 cgrid((a.M * a.Hq + 3) / 4);
   if (a.kv.act == ACT_F32) {
-    hipLaunchKernelGGL(k_attn_rows<float>, grid, dim3(ATT_THREADS), shmem, st, a, splits, pps);
-    hipLaunchKernelGGL(k_attn_combine<float>, dim3((a.M * a.Hq + 3) / 4), dim3(256), 0, st, a, splits);
+    if (phase == ATTN_SPLITS) hipLaunchKernelGGL(k_attn_rows<float>, grid, dim3(ATT_THREADS), shmem, st, a, splits, pps);
+    if (phase == ATTN_MERGE) hipLaunchKernelGGL(k_attn_combine<float>, cgrid, dim3(256), 0, st, a, splits);
   } else {
-    hipLaunchKernelGGL(k_attn_rows<bf16_t>, grid, dim3(ATT_THREADS), shmem, st, a, splits, pps);
-    hipLaunchKernelGGL(k_attn_combine<bf16_t>, dim3((a.M * a.Hq + 3) / 4), dim3(256), 0, st, a, splits);
+    if (phase == ATTN_SPLITS) hipLaunchKernelGGL(k_attn_rows<bf16_t>, grid, dim3(ATT_THREADS), shmem, st, a, splits, pps);
+    if (phase == ATTN_MERGE) hipLaunchKernelGGL(k_attn_combine<bf16_t>, cgrid, dim3(256), 0, st, a, splits);
   }
   return hipGetLastError();
 }

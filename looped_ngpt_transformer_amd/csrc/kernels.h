@@ -120,8 +120,12 @@ struct AttnArgs {
   int n_tiles = 0;
   int max_tile_rows = 0;
 };
-// Row-wise paged attention (any row count; split over keys) + combine + gate.
-hipError_t launch_attn_rows(const AttnArgs& a, hipStream_t st);
+// Row-wise paged attention (any row count; split over keys) + combine + gate, in two
+// phases launched separately: ATTN_SPLITS (the split-key kernel, writes partials) and
+// ATTN_MERGE (combines them, applies the gate, writes o). Both phases pick the same
+// split count for the same arguments; *splits_out receives it (may be null).
+enum AttnPhase { ATTN_SPLITS = 0, ATTN_MERGE = 1 };
+hipError_t launch_attn_rows(const AttnArgs& a, int phase, int* splits_out, hipStream_t st);
 // Prefill attention on bf16 with MFMA (query tiles of 64 rows); writes o.
 hipError_t launch_attn_prefill(const AttnArgs& a, hipStream_t st);
 size_t attn_rows_part_floats(int M, int Hq, int d, int max_pos, int window);

@@ -542,15 +542,25 @@ int run_layer(dory_ctx* ctx, hipStream_t st, const CallPlan& P, int l, int slot,
   {
     double pairs, keys;
     attn_work(P, full, c.window, &pairs, &keys);
-    Prof pr(ctx, st, DORY_KC_ATTN);
     const bool mfma_attn = !f32 && P.max_tile_rows > 1 && D.Hq == 4 * D.Hkv &&
                            (D.d == 64 || D.d == 128 || D.d == 160);
-    if (mfma_attn)
-      HIPCHK(launch_attn_prefill(aa, st), "attention (prefill)");
-    else
-      HIPCHK(launch_attn_rows(aa, st), "attention");
-    pr.end(4.0 * D.Hq * D.d * pairs,
-           keys * 2.0 * D.Nkv * D.esz + (double)M * 3 * D.Nq * D.esz);
+    int splits = 1;
+    {
+      // the prefill kernel also applies the gate and writes o; the split-key kernel reads
+      // K, V and q and leaves the rest to the merge
+      Prof pr(ctx, st, DORY_KC_ATTN);
+      if (mfma_attn)
+        HIPCHK(launch_attn_prefill(aa, st), "attention (prefill)");
+      else
+        HIPCHK(launch_attn_rows(aa, ATTN_SPLITS, &splits, st), "attention");
+      pr.end(4.0 * D.Hq * D.d * pairs,
+             keys * 2.0 * D.Nkv * D.esz + (double)M * (mfma_attn ? 3 : 1) * D.Nq * D.esz);
+    }
+    if (!mfma_attn) {
+      Prof pr(ctx, st, DORY_KC_MERGE);
+      HIPCHK(launch_attn_rows(aa, ATTN_MERGE, &splits, st), "attention merge");
+      pr.end(0, (double)M * D.Hq * splits * (D.d + 2) * 4 + (double)M * D.Nq * (2 * D.esz + (f32 ? 4.0 * S : 0)));
+    }
   }
 
   // ---- output projection + nGPT update (the pre-projection norm cancels in N(y))

@@ -54,9 +54,9 @@ class dory_kernel_stats(C.Structure):
                 ("bytes", C.c_double)]
 
 
-KC_GEMM, KC_ATTN, KC_ROPE, KC_UPDATE, KC_SWIGLU = range(5)
+KC_GEMM, KC_ATTN, KC_ROPE, KC_UPDATE, KC_SWIGLU, KC_MERGE = range(6)
 KC_NAMES = {KC_GEMM: "gemm", KC_ATTN: "attention", KC_ROPE: "rope_kv", KC_UPDATE: "update",
-            KC_SWIGLU: "swiglu"}
+            KC_SWIGLU: "swiglu", KC_MERGE: "attn_merge"}
 
 _P = C.c_void_p
 _I32P = C.POINTER(C.c_int32)
