@@ -327,7 +327,7 @@ __global__ __launch_bounds__(PF_THREADS) void k_attn_prefill(AttnArgs a) {
     const float invl = 1.f / lsum;
     const size_t base = (size_t)(row0 + qi) * HqD + (size_t)h * D;
     uint2 graw[CB][4];
-    const bool gbf = a.g && !a.g_f32;
+    const bool gbf = a.g != nullptr;  // bf16 (the launcher rejects float gates)
     if (gbf) {
       const bf16_t* gr = (const bf16_t*)a.g + (size_t)(row0 + qi) * a.g_ld + (size_t)h * D + 4 * lh;
 #pragma unroll
@@ -350,10 +350,6 @@ __global__ __launch_bounds__(PF_THREADS) void k_attn_prefill(AttnArgs a) {
             const float x = __uint_as_float((gw[r >> 1] >> (16 * (r & 1))) << 16);
             v[r] *= 1.f / (1.f + __expf(-x));
           }
-        } else if (a.g) {
-#pragma unroll
-          for (int r = 0; r < 4; ++r)
-            v[r] *= gate_at(a.g, a.g_f32, a.g_ld, a.g_splits, a.g_sstride, row0 + qi, h * D + c + r);
         }
         uint2 ov;
         ov.x = (uint32_t)f2bf(v[0]) | ((uint32_t)f2bf(v[1]) << 16);
@@ -367,7 +363,7 @@ __global__ __launch_bounds__(PF_THREADS) void k_attn_prefill(AttnArgs a) {
 
 hipError_t launch_attn_prefill(const AttnArgs& a, hipStream_t st) {
   if (a.n_tiles == 0) return hipSuccess;
-  if (a.kv.act != ACT_BF16 || a.Hq != 4 * a.Hkv) return hipErrorInvalidValue;
+  if (a.kv.act != ACT_BF16 || a.Hq != 4 * a.Hkv || (a.g && a.g_f32)) return hipErrorInvalidValue;
   if (a.max_pos / PAGE + 1 > PF_MAX_PAGES) return hipErrorInvalidValue;
   dim3 grid(a.n_tiles, a.Hkv);
   switch (a.d) {

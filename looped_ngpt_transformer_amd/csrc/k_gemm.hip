@@ -770,7 +770,50 @@ __global__ __launch_bounds__(512) void k_gemm_pp(GemmArgs g) {
       compute_phase(S1{}, it + 1);
     }
   }
-  gemm_epilogue32<BM, BN, WMW, WNW, EPI>(g, acc, n_tile, m0, wm, wn, lane);
+  if constexpr (EPI == EPI_STORE_ACT || EPI == EPI_SWIGLU) {
+    // bf16 outputs through LDS: every LDS read of the main loop is done (group 0's last
+    // barrier follows group 1's last read phase; no loads are in flight), so each wave
+    // writes its output block into its own LDS region and stores it back as 16-byte
+    // chunks of 8 consecutive columns. The two lane halves of a write hold rows r and
+    // r + 4: rows are padded by 32 bytes where the region allows, else (128-byte rows)
+    // the 64-byte halves of a row swap when bit 2 of the row is set, so that the halves
+    // land on different banks.
+    constexpr int TNO = EPI == EPI_SWIGLU ? TN / 2 : TN;  // output columns per wave
+    constexpr bool PAD = 4 * TM * (TNO * 2 + 32) <= (ACH + BCH) * 16;
+    constexpr int RS = PAD ? TNO * 2 + 32 : TNO * 2;      // LDS row stride (bytes)
+    static_assert(4 * TM * RS <= (ACH + BCH) * 16, "output staging fits one stage array");
+    static_assert(PAD || RS == 128, "swizzled staging assumes 128-byte rows");
+    auto soff = [&](int row, int byte) { return row * RS + (PAD ? byte : byte ^ (((row >> 2) & 1) << 6)); };
+    unsigned char* reg = (unsigned char*)(grp == 0 ? sm0 : sm1) + w4 * TM * RS;
+    const int l32 = lane & 31, lh = lane >> 5;
+#pragma unroll
+    for (int i = 0; i < FM; ++i)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const int row = i * 32 + 8 * (r >> 2) + 4 * lh + (r & 3);
+#pragma unroll
+        for (int j = 0; j < (EPI == EPI_SWIGLU ? FN / 2 : FN); ++j) {
+          float v = acc[i][j][r];
+          if constexpr (EPI == EPI_SWIGLU) {
+            const float up = acc[i][j + FN / 2][r];
+            v = v / (1.f + __expf(-v)) * up;
+          }
+          *(bf16_t*)(reg + soff(row, (j * 32 + l32) * 2)) = f2bf(v);
+        }
+      }
+    constexpr int CPRO = TNO / 8;  // 16-byte chunks per output row
+    static_assert((TM * CPRO) % 64 == 0, "whole store instructions per wave");
+    const int ocol0 = EPI == EPI_SWIGLU ? n_tile * (BN / 2) + wn * TNO : n_tile * BN + wn * TNO;
+    const int orow0 = m0 + wm * TM;
+#pragma unroll
+    for (int q = 0; q < TM * CPRO / 64; ++q) {
+      const int idx = q * 64 + lane, row = idx / CPRO, ch = idx % CPRO;
+      const uint4 v = *(const uint4*)(reg + soff(row, ch * 16));
+      if (orow0 + row < g.M) *(uint4*)((bf16_t*)g.C + (size_t)(orow0 + row) * g.ldc + ocol0 + 8 * ch) = v;
+    }
+  } else {
+    gemm_epilogue32<BM, BN, WMW, WNW, EPI>(g, acc, n_tile, m0, wm, wn, lane);
+  }
   if (grp == 0) asm volatile("s_barrier" ::: "memory");  // matches group 1's extra first barrier
 }
 
@@ -920,8 +963,10 @@ static hipError_t go_pipe32(const GemmArgs& g, hipStream_t st, int ntiles_n) {
 
 template <int EPI>
 static hipError_t go_big(const GemmArgs& g, hipStream_t st, int n) {
-  // these kernels address A and B with 32-bit byte offsets
+  // these kernels address A and B with 32-bit byte offsets, and store bf16 outputs as
+  // 16-byte chunks
   if ((long)g.N * g.K >= (1L << 30) || g.lda >= (1 << 20)) return hipErrorNotSupported;
+  if (EPI != EPI_F32 && (g.ldc % 8 != 0 || ((uintptr_t)g.C & 15) != 0)) return hipErrorNotSupported;
   if (n % 256 == 0 && (EPI == EPI_SWIGLU || n / 256 * ((g.M + 255) / 256) >= 256)) {
     dim3 grid(n / 256, (g.M + 255) / 256);
     hipLaunchKernelGGL((k_gemm_pp<256, EPI>), grid, dim3(512), 0, st, g);

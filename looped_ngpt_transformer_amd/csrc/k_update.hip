@@ -21,7 +21,7 @@
 
 namespace dory {
 
-// THREADS per row: 256 for many rows, 1024 for few rows (decode) so that each row's
+// THREADS per row: 512 for many rows, 1024 for few rows (decode) so that each row's
 // loads are spread over more waves.
 template <typename SB, int UPD_THREADS>
 __global__ __launch_bounds__(UPD_THREADS) void k_update(UpdateArgs u) {
@@ -144,10 +144,10 @@ hipError_t launch_update(const UpdateArgs& u, hipStream_t st) {
   const bool few = u.M < 512;
   if (u.act == ACT_F32) {
     if (few) hipLaunchKernelGGL((k_update<float, 1024>), dim3(u.M), dim3(1024), 0, st, u);
-    else hipLaunchKernelGGL((k_update<float, 256>), dim3(u.M), dim3(256), 0, st, u);
+    else hipLaunchKernelGGL((k_update<float, 512>), dim3(u.M), dim3(512), 0, st, u);
   } else {
     if (few) hipLaunchKernelGGL((k_update<bf16_t, 1024>), dim3(u.M), dim3(1024), 0, st, u);
-    else hipLaunchKernelGGL((k_update<bf16_t, 256>), dim3(u.M), dim3(256), 0, st, u);
+    else hipLaunchKernelGGL((k_update<bf16_t, 512>), dim3(u.M), dim3(512), 0, st, u);
   }
   return hipGetLastError();
 }

@@ -542,7 +542,9 @@ int run_layer(dory_ctx* ctx, hipStream_t st, const CallPlan& P, int l, int slot,
   {
     double pairs, keys;
     attn_work(P, full, c.window, &pairs, &keys);
-    const bool mfma_attn = !f32 && P.max_tile_rows > 1 && D.Hq == 4 * D.Hkv &&
+    // the MFMA prefill kernel takes the gate in bf16: small chunks, whose projection
+    // leaves float split partials, use the row-wise kernels
+    const bool mfma_attn = !f32 && !aa.g_f32 && P.max_tile_rows > 1 && D.Hq == 4 * D.Hkv &&
                            (D.d == 64 || D.d == 128 || D.d == 160);
     int splits = 1;
     {

@@ -37,18 +37,22 @@ def check(out, ref, bf16_out):
     assert not bad.any(), f"{int(bad.sum())} outside tolerance, max |d| {float(d.max()):.3e}"
 
 
-@pytest.mark.parametrize("M,N,K,lda", [
-    (2600, 6400, 2560, None),     # [q|k|v|gate] shape, 275 ping-pong tiles, ragged last row tile
-    (4096, 6400, 2560, 2624),     # full tiles, A row stride > K
-    (150, 6400, 2560, None),      # too few tiles for 256x256: 256x160 tiles
+@pytest.mark.parametrize("M,N,K,lda,ldc", [
+    (2600, 6400, 2560, None, None),   # [q|k|v|gate] shape, 275 ping-pong tiles, ragged last row tile
+    (4096, 6400, 2560, 2624, None),   # full tiles, A row stride > K
+    (150, 6400, 2560, None, None),    # too few tiles for 256x256: 256x160 tiles
+    (150, 6400, 2560, None, 6408),    # output row stride > N (16-byte stores)
+    (300, 6400, 2560, None, 6404),    # output rows not 16-byte aligned: register-staged tiles
 ])
-def test_store_bf16(M, N, K, lda):
+def test_store_bf16(M, N, K, lda, ldc):
     A, B = operands(M, N, K, 1, lda)
-    out = torch.full((M + 4, N), SENTINEL, dtype=torch.bfloat16, device="cuda")
-    assert D.dory_test_gemm(A, B, D.EPI_STORE_BF16, out, M=M, lda=A.stride(0)) == 1
+    ldc = ldc or N
+    out = torch.full((M + 4, ldc), SENTINEL, dtype=torch.bfloat16, device="cuda")
+    assert D.dory_test_gemm(A, B, D.EPI_STORE_BF16, out, M=M, N=N, lda=A.stride(0), ldc=ldc) == 1
     torch.cuda.synchronize()
-    check(out[:M], reference(A, B), True)
+    check(out[:M, :N], reference(A, B), True)
     assert (out[M:].float() == SENTINEL).all(), "rows beyond M written"
+    assert (out[:, N:].float() == SENTINEL).all(), "columns beyond N written"
 
 
 @pytest.mark.parametrize("M,N,K", [
