@@ -175,30 +175,49 @@ __global__ __launch_bounds__(PF_THREADS) void k_attn_prefill(AttnArgs a) {
   // matrix phase: O^T += V^T P^T of relative page r - 1 (stage SV), then S^T of page r
   // (stage SK); group B then waits for the page it issued in its last softmax phase
   auto matrix_phase = [&](bool pv, bool sk, auto SK, auto SV) {
+    // fragments double-buffered by step: the reads of step i + 1 are issued before the
+    // MFMAs of step i, so LDS latency overlaps the matrix core
     if (pv) {
-      const unsigned char* sv = stage_ptr(SV);
+      const unsigned char* sv = stage_ptr(SV) + voff;
+      bf16x8 vf[2][CB];
+      auto ldv = [&](int s, bf16x8 (&dst)[CB]) {
 #pragma unroll
-      for (int s = 0; s < 4; ++s)  // the CB output blocks interleaved: independent chains
+        for (int cb = 0; cb < CB; ++cb)
+          dst[cb] = *(const bf16x8*)(sv + ((s >> 1) * CB16 + 2 * cb) * VGS + (s & 1) * 32 * 16);
+      };
+      ldv(0, vf[0]);
 #pragma unroll
-        for (int cb = 0; cb < CB; ++cb) {
-          const bf16x8 vf = *(const bf16x8*)(sv + voff + ((s >> 1) * CB16 + 2 * cb) * VGS + (s & 1) * 32 * 16);
-          o[cb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf, pf[s], o[cb], 0, 0, 0);
-        }
+      for (int s = 0; s < 4; ++s) {
+        if (s + 1 < 4) ldv(s + 1, vf[(s + 1) & 1]);
+        __builtin_amdgcn_sched_barrier(0);  // keep the reads ahead of the MFMAs
+#pragma unroll
+        for (int cb = 0; cb < CB; ++cb)  // the CB output blocks: independent chains
+          o[cb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf[s & 1][cb], pf[s], o[cb], 0, 0, 0);
+        __builtin_amdgcn_sched_barrier(0);
+      }
     }
     if (sk) {
-      const unsigned char* sk0 = stage_ptr(SK);
+      const unsigned char* sk0 = stage_ptr(SK) + koff;
 #pragma unroll
       for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
         for (int r = 0; r < 16; ++r) st[kb][r] = 0.f;
+      bf16x8 kf[2][2];
+      auto ldk = [&](int c, bf16x8 (&dst)[2]) {
 #pragma unroll
-      for (int c = 0; c < KS; ++c)  // the two key blocks interleaved: independent chains
+        for (int kb = 0; kb < 2; ++kb)
+          dst[kb] = *(const bf16x8*)(sk0 + (2 * kb * DC + (c >> 1)) * KGS + (c & 1) * 32 * 16);
+      };
+      ldk(0, kf[0]);
 #pragma unroll
-        for (int kb = 0; kb < 2; ++kb) {
-          const int off = (2 * kb * DC + (c >> 1)) * KGS + (c & 1) * 32 * 16;
-          const bf16x8 kf = *(const bf16x8*)(sk0 + koff + off);
-          st[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf, qf[c], st[kb], 0, 0, 0);
-        }
+      for (int c = 0; c < KS; ++c) {
+        if (c + 1 < KS) ldk(c + 1, kf[(c + 1) & 1]);
+        __builtin_amdgcn_sched_barrier(0);  // keep the reads ahead of the MFMAs
+#pragma unroll
+        for (int kb = 0; kb < 2; ++kb)  // the two key blocks: independent chains
+          st[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf[c & 1][kb], qf[c], st[kb], 0, 0, 0);
+        __builtin_amdgcn_sched_barrier(0);
+      }
     }
     if (hh == 1) asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
     barrier();
