@@ -40,7 +40,6 @@ typedef float f32x16 __attribute__((ext_vector_type(16)));
 
 constexpr int PF_WAVES = 8;
 constexpr int PF_THREADS = PF_WAVES * 64;
-constexpr int PF_MAX_PAGES = 4096;  // positions up to 262144
 
 typedef __attribute__((address_space(3))) void* pf_lds_t;
 typedef __attribute__((address_space(1))) void* pf_gbl_t;
@@ -69,7 +68,6 @@ __global__ __launch_bounds__(PF_THREADS) void k_attn_prefill(AttnArgs a) {
   __shared__ __align__(16) unsigned char sm0[STAGE];
   __shared__ __align__(16) unsigned char sm1[STAGE];
   __shared__ __align__(16) unsigned char sm2[STAGE];
-  __shared__ int32_t pages[PF_MAX_PAGES];  // the tile's page ids
   auto stage_ptr = [&](auto S) -> unsigned char* {
     if constexpr (decltype(S)::value == 0) return sm0;
     else if constexpr (decltype(S)::value == 1) return sm1;
@@ -107,13 +105,12 @@ __global__ __launch_bounds__(PF_THREADS) void k_attn_prefill(AttnArgs a) {
     qf[c] = __builtin_bit_cast(bf16x8, v);
   }
 
-  for (int i = t; i <= npg; i += PF_THREADS) pages[i] = trow[(pg_lo + i) % a.kv.ring];
-  __syncthreads();
-
   // relative page r -> its stage S (r % 3): group-B wave g loads groups g, g + 4, ...
-  // (K groups 0..NG-1, then V)
+  // (K groups 0..NG-1, then V). The page id is a wave-uniform read of the page table in
+  // global memory: not through LDS, where it would queue behind the other group's
+  // fragment reads.
   auto issue = [&](int r, auto S) {
-    const int32_t page = pages[r];
+    const int32_t page = trow[(pg_lo + r) % a.kv.ring];
     const unsigned char* kb = (const unsigned char*)(pool + (size_t)page * a.kv.page_elems + (size_t)hk * 64 * D);
     const unsigned char* vb = (const unsigned char*)(pool + (size_t)page * a.kv.page_elems + (size_t)(a.kv.Hkv + hk) * 64 * D);
     unsigned char* st0 = stage_ptr(S);
@@ -383,7 +380,6 @@ __global__ __launch_bounds__(PF_THREADS) void k_attn_prefill(AttnArgs a) {
 hipError_t launch_attn_prefill(const AttnArgs& a, hipStream_t st) {
   if (a.n_tiles == 0) return hipSuccess;
   if (a.kv.act != ACT_BF16 || a.Hq != 4 * a.Hkv || (a.g && a.g_f32)) return hipErrorInvalidValue;
-  if (a.max_pos / PAGE + 1 > PF_MAX_PAGES) return hipErrorInvalidValue;
   dim3 grid(a.n_tiles, a.Hkv);
   switch (a.d) {
     case 64:
