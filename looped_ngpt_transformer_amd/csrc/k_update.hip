@@ -129,6 +129,102 @@ __global__ __launch_bounds__(UPD_THREADS) void k_update(UpdateArgs u) {
   }
 }
 
+// Prefill form (y one bf16 array, H % 8 == 0, H <= 8 T): each thread owns 8 consecutive
+// channels of the row, so every access is 16 or 32 bytes wide; same sums and algebra.
+template <typename SB, int T>
+__global__ __launch_bounds__(T) void k_update_vec(UpdateArgs u) {
+  constexpr int NW = T / WAVE;
+  constexpr int NS = 7;
+  __shared__ float red[NW][NS];
+  const int H = u.H;
+  const size_t row = (size_t)blockIdx.x * H;
+  const int i0 = threadIdx.x * 8;
+  const bool act = i0 < H;
+  const bool need_x = u.bnd == BND_LOOP_CONTINUE;
+  float yv[8], sv[8], av[8], xv[8];
+#pragma unroll
+  for (int e = 0; e < 8; ++e) yv[e] = sv[e] = av[e] = xv[e] = 0.f;
+  if (act) {
+    const uint4 yr = *(const uint4*)((const bf16_t*)u.y + row + i0);
+    const float4 s0 = *(const float4*)(u.s + row + i0), s1 = *(const float4*)(u.s + row + i0 + 4);
+    const float4 a0 = *(const float4*)(u.alpha + i0), a1 = *(const float4*)(u.alpha + i0 + 4);
+    const uint32_t yw[4] = {yr.x, yr.y, yr.z, yr.w};
+#pragma unroll
+    for (int e = 0; e < 8; ++e) yv[e] = __uint_as_float((e & 1) ? (yw[e / 2] & 0xFFFF0000u) : (yw[e / 2] << 16));
+    sv[0] = s0.x; sv[1] = s0.y; sv[2] = s0.z; sv[3] = s0.w; sv[4] = s1.x; sv[5] = s1.y; sv[6] = s1.z; sv[7] = s1.w;
+    av[0] = a0.x; av[1] = a0.y; av[2] = a0.z; av[3] = a0.w; av[4] = a1.x; av[5] = a1.y; av[6] = a1.z; av[7] = a1.w;
+    if (need_x) {
+      const float4 x0 = *(const float4*)(u.x + row + i0), x1 = *(const float4*)(u.x + row + i0 + 4);
+      xv[0] = x0.x; xv[1] = x0.y; xv[2] = x0.z; xv[3] = x0.w; xv[4] = x1.x; xv[5] = x1.y; xv[6] = x1.z; xv[7] = x1.w;
+    }
+  }
+  float acc[NS] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+  for (int e = 0; e < 8; ++e) {
+    const float bs = (1.f - av[e]) * sv[e], ay = av[e] * yv[e];
+    acc[0] += yv[e] * yv[e];
+    acc[1] += bs * bs;
+    acc[2] += bs * ay;
+    acc[3] += ay * ay;
+    acc[4] += bs * xv[e];
+    acc[5] += ay * xv[e];
+    acc[6] += xv[e] * xv[e];
+  }
+#pragma unroll
+  for (int q = 0; q < NS; ++q) acc[q] = wave_sum(acc[q]);
+  if ((threadIdx.x & (WAVE - 1)) == 0)
+#pragma unroll
+    for (int q = 0; q < NS; ++q) red[threadIdx.x / WAVE][q] = acc[q];
+  __syncthreads();
+  float tot[NS];
+#pragma unroll
+  for (int q = 0; q < NS; ++q) {
+    tot[q] = 0.f;
+#pragma unroll
+    for (int w = 0; w < NW; ++w) tot[q] += red[w][q];
+  }
+  const float ny = inv_norm(tot[0]);
+  const float tt = fmaxf(tot[1] + 2.f * tot[2] * ny + tot[3] * ny * ny, 0.f);
+  const float nt = inv_norm(tt);
+  float scale = nt, norm_sp = sqrtf(tt) * nt, add_x = 0.f;
+  if (u.bnd == BND_LOOP_CONTINUE || u.bnd == BND_LOOP_FINAL) {
+    const float n2 = inv_norm(norm_sp * norm_sp);
+    scale *= n2;
+    norm_sp *= n2;
+  }
+  float t[8];
+#pragma unroll
+  for (int e = 0; e < 8; ++e) t[e] = (1.f - av[e]) * sv[e] + av[e] * yv[e] * ny;
+  if (u.bnd == BND_LOOP_CONTINUE) {
+    const float dot = (tot[4] + tot[5] * ny) * scale;
+    const float n3 = inv_norm(norm_sp * norm_sp + 2.f * dot + tot[6]);
+    scale *= n3;
+    add_x = n3;
+  } else if (u.bnd == BND_SAVE_X) {
+    const float n3 = inv_norm(4.f * norm_sp * norm_sp);
+    if (act) {
+      *(float4*)(u.x + row + i0) = make_float4(t[0] * nt, t[1] * nt, t[2] * nt, t[3] * nt);
+      *(float4*)(u.x + row + i0 + 4) = make_float4(t[4] * nt, t[5] * nt, t[6] * nt, t[7] * nt);
+    }
+    scale *= 2.f * n3;
+  }
+  if (!act) return;
+  float v[8];
+#pragma unroll
+  for (int e = 0; e < 8; ++e) v[e] = t[e] * scale + add_x * xv[e];
+  *(float4*)(u.s_out + row + i0) = make_float4(v[0], v[1], v[2], v[3]);
+  *(float4*)(u.s_out + row + i0 + 4) = make_float4(v[4], v[5], v[6], v[7]);
+  if (u.sb) {
+    if constexpr (sizeof(SB) == 2) {
+      *(uint4*)((bf16_t*)u.sb + row + i0) =
+          make_uint4(pack_bf16x2(v[0], v[1]), pack_bf16x2(v[2], v[3]), pack_bf16x2(v[4], v[5]), pack_bf16x2(v[6], v[7]));
+    } else {
+      *(float4*)((float*)u.sb + row + i0) = make_float4(v[0], v[1], v[2], v[3]);
+      *(float4*)((float*)u.sb + row + i0 + 4) = make_float4(v[4], v[5], v[6], v[7]);
+    }
+  }
+}
+
 template <typename SB>
 __global__ __launch_bounds__(256) void k_stage_input(const float* x, float* s, SB* sb, size_t n) {
   for (size_t i = blockIdx.x * (size_t)blockDim.x + threadIdx.x; i < n;
@@ -142,6 +238,19 @@ __global__ __launch_bounds__(256) void k_stage_input(const float* x, float* s, S
 hipError_t launch_update(const UpdateArgs& u, hipStream_t st) {
   if (u.M == 0) return hipSuccess;
   const bool few = u.M < 512;
+  if (!few && u.y_bf16 && u.splits == 1 && u.H % 8 == 0 && u.H <= 8 * 1024) {
+    const int per = u.H / 8;  // threads carrying 8 channels each
+    if (u.act == ACT_F32) {
+      if (per <= 320) hipLaunchKernelGGL((k_update_vec<float, 320>), dim3(u.M), dim3(320), 0, st, u);
+      else if (per <= 512) hipLaunchKernelGGL((k_update_vec<float, 512>), dim3(u.M), dim3(512), 0, st, u);
+      else hipLaunchKernelGGL((k_update_vec<float, 1024>), dim3(u.M), dim3(1024), 0, st, u);
+    } else {
+      if (per <= 320) hipLaunchKernelGGL((k_update_vec<bf16_t, 320>), dim3(u.M), dim3(320), 0, st, u);
+      else if (per <= 512) hipLaunchKernelGGL((k_update_vec<bf16_t, 512>), dim3(u.M), dim3(512), 0, st, u);
+      else hipLaunchKernelGGL((k_update_vec<bf16_t, 1024>), dim3(u.M), dim3(1024), 0, st, u);
+    }
+    return hipGetLastError();
+  }
   if (u.act == ACT_F32) {
     if (few) hipLaunchKernelGGL((k_update<float, 1024>), dim3(u.M), dim3(1024), 0, st, u);
     else hipLaunchKernelGGL((k_update<float, 512>), dim3(u.M), dim3(512), 0, st, u);

@@ -117,6 +117,17 @@ def test_bf16_attention_running_maximum(variant):
               wmod=widen if variant == "one_large_s_qk" else None)
 
 
+@pytest.mark.parametrize("mode", ["per_loop", "last_loop"])
+def test_bf16_long_prefill(mode):
+    """A 600-row prefill: the row-vectorised update of long prefills (>= 512 rows; every
+    loop boundary occurs in it at k = 2), 256-row GEMM tiles with a ragged tail, then a
+    decode step."""
+    S = PSMALL
+    sched = [("prefill", [(0, xin(S, 600, 61))]),
+             ("decode", [(0, xin(S, 1, 62))])]
+    _run_case(S, 2, mode, sched, max_rows=640, max_seq_len=704, max_seqs=1)
+
+
 def test_tiny_fp32_sharp_rates():
     T = synth.config("T")
     sched = [("prefill", [(0, xin(T, 50, 81))])]
