@@ -105,12 +105,21 @@ __global__ __launch_bounds__(PF_THREADS) void k_attn_prefill(AttnArgs a) {
     qf[c] = __builtin_bit_cast(bf16x8, v);
   }
 
+  // Page ids of relative pages 64 c .. 64 c + 63 (chunk c), one per lane. A page id read
+  // from the table at issue time would put a dependent global-memory round trip in front
+  // of every page's loads; held in a register it costs one lane read, and the table is
+  // read again once every 64 pages.
+  auto load_ids = [&](int c) -> int {
+    const int rr = 64 * c + lane;
+    return rr <= npg ? trow[(pg_lo + rr) % a.kv.ring] : 0;
+  };
+  int ids = load_ids(0);
+
   // relative page r -> its stage S (r % 3): group-B wave g loads groups g, g + 4, ...
-  // (K groups 0..NG-1, then V). The page id is a wave-uniform read of the page table in
-  // global memory: not through LDS, where it would queue behind the other group's
-  // fragment reads.
+  // (K groups 0..NG-1, then V)
   auto issue = [&](int r, auto S) {
-    const int32_t page = trow[(pg_lo + r) % a.kv.ring];
+    if (r > 0 && (r & 63) == 0) ids = load_ids(r >> 6);
+    const int32_t page = __builtin_amdgcn_readlane(ids, r & 63);
     const unsigned char* kb = (const unsigned char*)(pool + (size_t)page * a.kv.page_elems + (size_t)hk * 64 * D);
     const unsigned char* vb = (const unsigned char*)(pool + (size_t)page * a.kv.page_elems + (size_t)(a.kv.Hkv + hk) * 64 * D);
     unsigned char* st0 = stage_ptr(S);

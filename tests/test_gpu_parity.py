@@ -243,3 +243,23 @@ def test_bf16_decode_over_seeded_context(mode, sharp):
             ref = O.prefill(cfg, W, stores[sid], to_np(X[j:j + 1]), k, mode)
             compare(got[j:j + 1], ref, S, f"step {step} seq {sid}")
     rt.close()
+
+
+@pytest.mark.parametrize("mode", ["per_loop", "last_loop"])
+def test_bf16_prefill_over_long_seeded_context(mode):
+    """A 100-row chunk continuing a seeded 4300-token context: the full-attention layer's
+    query tiles read 69 KV pages, past the 64 page ids a wave holds at once."""
+    from oracle import dory_oracle as O
+    from tests.helpers import to_np
+    S = PSMALL
+    k = 2
+    w = sharpen(gpu_weights(S, 8))
+    rt = DoryRuntime(S, w, max_loops=2, max_seqs=1, max_seq_len=4480, max_rows=256, mode=mode, loops=k)
+    stores = _seed_kv(rt, S, {0: 4300}, k, mode)
+    cfg, W = oracle_model(S, w)
+    X = xin(S, 100, 70)
+    y = rt.prefill([0], [100], X)
+    torch.cuda.synchronize()
+    ref = O.prefill(cfg, W, stores[0], to_np(X), k, mode)
+    compare(y.cpu().double().numpy(), ref, S, "chunk over 4300 tokens")
+    rt.close()
