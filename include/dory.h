@@ -184,6 +184,53 @@ int dory_kv_bytes_in_use(const dory_ctx* ctx, size_t* bytes);
  * n_in + n_out + k * n_rec. */
 int dory_last_layer_calls(const dory_ctx* ctx, int64_t* n);
 
+/* ---- vocabulary side: token embedding, LM head, top-p sampling
+ * The steps on either side of the stack ("Dory1.0-4B" pages: nGPT keeps embeddings on
+ * the unit sphere — paper summary, "prerequisites: nGPT"; logit-scale parameters —
+ * arXiv summary §2; generation settings temperature 1.0, top_p 0.95 — MXFP8 article,
+ * deployment section).
+ *  embed       [V, H] input token embedding
+ *  lm_head     [V, H] output embedding (may be the same array as embed)
+ *  logit_scale [V] float: effective per-token logit scale s_z
+ * Tables are float in an F32 context and bf16 (uint16) otherwise (both contexts'
+ * activation type: the pages keep embeddings and LM head out of weight quantisation,
+ * arXiv summary §5.1); V % 128 == 0, V <= 2^24. Device pointers, caller-owned, valid
+ * while the context uses them. */
+typedef struct dory_vocab_weights {
+  int64_t vocab;
+  const void* embed;
+  const void* lm_head;
+  const float* logit_scale;
+} dory_vocab_weights;
+/* Errors: INVALID_ARG (null pointers, V out of range or not a multiple of 128). */
+int dory_bind_vocab(dory_ctx* ctx, const dory_vocab_weights* v);
+
+/* Input states of tokens: x_out[i] = N(embed[ids[i]]) (device float [n, H]); ids device
+ * int32 [n]. An id outside [0, V) yields a zero row (the table is not read). The rows
+ * are unit-norm states as dory_prefill / dory_decode_step take them.
+ * 1 <= n <= max_rows. Errors: INVALID_ARG, STATE (vocabulary unbound), HIP. */
+int dory_embed(dory_ctx* ctx, void* stream, int n, const int32_t* ids, float* x_out);
+
+/* LM head: logits[i][v] = logit_scale[v] * (states[i] . lm_head[v]); states device float
+ * [n, H] (final states, e.g. y_out of a decode step), logits device float [n, V] (row
+ * stride V). The states enter the product in the context's activation type (bf16 in a
+ * bf16 context), as in the projections; float accumulation. Uses the workspace.
+ * 1 <= n <= max_rows. Errors: INVALID_ARG, STATE (vocabulary or workspace unbound), HIP. */
+int dory_logits(dory_ctx* ctx, void* stream, int n, const float* states, float* logits);
+
+/* Top-p sampling, one token per row: p = softmax(logits[i] / temperature); tokens in
+ * order of p, highest first, equal p by lower id; the nucleus is the shortest prefix of
+ * that order whose cumulative p reaches top_p; the token is the first of the nucleus
+ * whose cumulative p exceeds u[i] times the nucleus mass. logits device float [n, V],
+ * row stride ld >= V; u device float [n], each in [0, 1) (the random draws are inputs);
+ * tokens device int32 [n]. Probabilities and running sums are float32, summed in a fixed
+ * order, so the result is a deterministic function of the inputs; probabilities equal in
+ * float32 go by id. Logits must be finite. 1 <= V <= 2^24, temperature > 0,
+ * 0 < top_p <= 1. No context: INVALID_ARG before any device work (message in
+ * dory_last_error(NULL)), HIP. */
+int dory_sample_top_p(void* stream, int n, int64_t vocab, const float* logits, int64_t ld, float temperature,
+                      float top_p, const float* u, int32_t* tokens);
+
 /* ---- test and benchmark support: installing a seeded context without computing it */
 /* Extend sequence seq_id (created if new) by n_tokens positions and reserve their
  * pages; the entries are undefined until written by dory_test_fill_kv. */
@@ -226,7 +273,9 @@ int dory_quantize_mxfp8(void* stream, const void* w, int w_dtype, int64_t rows,
 #define DORY_KC_UPDATE 3 /* nGPT update / loop boundary, input staging */
 #define DORY_KC_SWIGLU 4 /* SwiGLU from split-K partials */
 #define DORY_KC_MERGE 5  /* merge of the split-key partials, gate (decode and fp32 calls) */
-#define DORY_KC_COUNT 6
+#define DORY_KC_VOCAB 6  /* vocabulary side: embedding, logit scale, top-p sampling (the LM-head
+                            product counts as GEMM) */
+#define DORY_KC_COUNT 7
 typedef struct dory_kernel_stats {
   int64_t launches; /* kernel launches recorded */
   double ms;        /* summed event time of those launches */

@@ -1,0 +1,265 @@
+// The steps on either side of the looped stack: token embedding, the LM head's logit
+// scale, and top-p sampling ("Dory1.0-4B" pages: nGPT keeps embeddings on the unit
+// sphere — paper summary, "prerequisites: nGPT"; logit-scale parameters — arXiv summary
+// §2; generation settings temperature 1.0, top_p 0.95 — MXFP8 article, deployment section).
+// The LM-head product itself is a projection GEMM (k_gemm.hip).
+#include <climits>
+
+#include "common.h"
+#include "kernels.h"
+
+namespace dory {
+
+// x[i] = N(E[ids[i]]) as float rows; an id outside [0, V) gives a zero row (the table
+// is never read out of range). One block per row.
+template <typename T>
+__global__ __launch_bounds__(256) void k_embed(const T* E, int64_t V, int H, const int32_t* ids, float* x) {
+  __shared__ float red[4];
+  const int i = blockIdx.x;
+  const int id = ids[i];
+  const bool ok = id >= 0 && id < V;  // uniform over the block
+  const T* row = E + (ok ? (size_t)id * H : 0);
+  float ss = 0.f;
+  if (ok)
+    for (int c = threadIdx.x; c < H; c += 256) {
+      const float v = ld(row, c);
+      ss += v * v;
+    }
+  const float inv = inv_norm(block_sum<4>(ss, red));
+  for (int c = threadIdx.x; c < H; c += 256) x[(size_t)i * H + c] = ok ? ld(row, c) * inv : 0.f;
+}
+
+// logits[i][v] = s_z[v] * sum_s part[s][i][v]: the per-token logit scale on the LM-head
+// product (split-K partials when the GEMM split K; part == logits for one split).
+__global__ __launch_bounds__(256) void k_logit_scale(const float* part, int splits, size_t sstride, float* logits,
+                                                     int64_t ld, int64_t V, const float* sz) {
+  const int i = blockIdx.y;
+  const int64_t v = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  if (v >= V) return;
+  const size_t o = (size_t)i * ld + v;
+  logits[o] = sz[v] * sum_splits(part + o, sstride, splits);
+}
+
+// ------------------------------------------------------------------ top-p sampling
+// One block of ST threads per row; thread t owns the consecutive ids [t C, t C + C).
+// Weights e_v = exp(l_v / T - max) (recomputed identically in every pass); their float
+// bit patterns order the tokens like their probabilities. The sorted order is e
+// descending, equal e by lower id. Each selection finds the first token of that order
+// whose running mass meets a target: eight passes over 4-bit digits of the bit pattern,
+// high to low, narrow the key down (per-thread digit masses in LDS, summed in a fixed
+// order), then the tokens with exactly that key are taken in id order. Every sum has a
+// fixed order, so the result is a deterministic function of the logits and u.
+constexpr int ST = 1024;
+
+struct SampleLds {
+  float bins[16][ST];  // per-thread mass of each digit
+  int cnt[16][ST];     // per-thread count of each digit
+  float binsum[16];
+  int bincnt[16];
+  float red[16];
+  int ired[16];
+  uint32_t prefix;
+  float above;
+};
+
+__device__ __forceinline__ float block_max16(float v, float* red) {
+  v = wave_max(v);
+  const int w = threadIdx.x / WAVE;
+  __syncthreads();
+  if ((threadIdx.x & (WAVE - 1)) == 0) red[w] = v;
+  __syncthreads();
+  float t = red[0];
+#pragma unroll
+  for (int i = 1; i < ST / WAVE; ++i) t = fmaxf(t, red[i]);
+  return t;
+}
+
+__device__ __forceinline__ int block_min_int(int v, int* red) {
+#pragma unroll
+  for (int m = 32; m >= 1; m >>= 1) v = min(v, __shfl_xor(v, m, WAVE));
+  const int w = threadIdx.x / WAVE;
+  __syncthreads();
+  if ((threadIdx.x & (WAVE - 1)) == 0) red[w] = v;
+  __syncthreads();
+  int t = red[0];
+#pragma unroll
+  for (int i = 1; i < ST / WAVE; ++i) t = min(t, red[i]);
+  return t;
+}
+
+__device__ __forceinline__ int block_sum_int(int v, int* red) {
+#pragma unroll
+  for (int m = 32; m >= 1; m >>= 1) v += __shfl_xor(v, m, WAVE);
+  const int w = threadIdx.x / WAVE;
+  __syncthreads();
+  if ((threadIdx.x & (WAVE - 1)) == 0) red[w] = v;
+  __syncthreads();
+  int t = 0;
+#pragma unroll
+  for (int i = 0; i < ST / WAVE; ++i) t += red[i];
+  return t;
+}
+
+// exclusive prefix sum of one int per thread, in thread order
+__device__ __forceinline__ int block_excl_scan(int v, int* red) {
+  const int lane = threadIdx.x & (WAVE - 1), w = threadIdx.x / WAVE;
+  int x = v;
+#pragma unroll
+  for (int d = 1; d < WAVE; d <<= 1) {
+    const int y = __shfl_up(x, d, WAVE);
+    if (lane >= d) x += y;
+  }
+  __syncthreads();
+  if (lane == WAVE - 1) red[w] = x;
+  __syncthreads();
+  int off = 0;
+  for (int i = 0; i < w; ++i) off += red[i];
+  return off + x - v;
+}
+
+// First token of the sorted order whose inclusive running mass reaches (incl) or
+// exceeds (!incl) target; if rounding leaves the target beyond the mass, the last token
+// of the order. Returns the token and sets cum to its inclusive running mass.
+__device__ int select_token(SampleLds& S, const float* L, int beg, int end, float inv_t, float m, float target,
+                            bool incl, float* cum) {
+  const int t = threadIdx.x, lane = t & (WAVE - 1), w = t / WAVE;
+  uint32_t prefix = 0;
+  float above = 0.f;  // mass of the tokens whose key lies above the digits chosen so far
+  for (int pass = 0; pass < 8; ++pass) {
+    const int sh = 28 - 4 * pass;
+#pragma unroll
+    for (int d = 0; d < 16; ++d) {
+      S.bins[d][t] = 0.f;
+      S.cnt[d][t] = 0;
+    }
+    for (int i = beg; i < end; ++i) {
+      const float e = expf(L[i] * inv_t - m);
+      const uint32_t key = __float_as_uint(e);
+      if (pass == 0 || (key >> (sh + 4)) == prefix) {
+        const int d = (key >> sh) & 15;
+        S.bins[d][t] += e;
+        S.cnt[d][t] += 1;
+      }
+    }
+    __syncthreads();
+    {  // wave w sums digit w over the threads, lane j taking threads j, j + 64, ...
+      float v = 0.f;
+      int c = 0;
+#pragma unroll
+      for (int j = 0; j < ST / WAVE; ++j) {
+        v += S.bins[w][j * WAVE + lane];
+        c += S.cnt[w][j * WAVE + lane];
+      }
+      v = wave_sum(v);
+#pragma unroll
+      for (int o = 32; o >= 1; o >>= 1) c += __shfl_xor(c, o, WAVE);
+      if (lane == 0) {
+        S.binsum[w] = v;
+        S.bincnt[w] = c;
+      }
+    }
+    __syncthreads();
+    if (t == 0) {
+      float acc = above, acc_last = above;
+      int sel = -1, last = -1;
+      for (int d = 15; d >= 0; --d) {
+        if (S.bincnt[d] == 0) continue;
+        last = d;
+        acc_last = acc;
+        const float nxt = acc + S.binsum[d];
+        if (incl ? nxt >= target : nxt > target) {
+          sel = d;
+          break;
+        }
+        acc = nxt;
+      }
+      if (sel < 0) {
+        sel = last;
+        acc = acc_last;
+      }
+      S.prefix = (prefix << 4) | (uint32_t)sel;
+      S.above = acc;
+    }
+    __syncthreads();
+    prefix = S.prefix;
+    above = S.above;
+    __syncthreads();
+  }
+  // tokens whose key is exactly `prefix`, in id order: the j-th (from 0) has running
+  // mass above + (j + 1) * e*
+  const float es = __uint_as_float(prefix);
+  int n_mine = 0;
+  for (int i = beg; i < end; ++i) n_mine += __float_as_uint(expf(L[i] * inv_t - m)) == prefix;
+  int j = block_excl_scan(n_mine, S.ired);
+  int cand = INT_MAX, last_mine = -1;
+  for (int i = beg; i < end; ++i) {
+    if (__float_as_uint(expf(L[i] * inv_t - m)) != prefix) continue;
+    last_mine = i;
+    const float c = above + (float)(j + 1) * es;
+    if (cand == INT_MAX && (incl ? c >= target : c > target)) cand = i;
+    ++j;
+  }
+  int tok = block_min_int(cand, S.ired);
+  if (tok == INT_MAX) tok = -block_min_int(-last_mine, S.ired);  // the last tied token
+  // its running mass follows from the number of tied tokens before it
+  int before = 0;
+  for (int i = beg; i < end && i < tok; ++i) before += __float_as_uint(expf(L[i] * inv_t - m)) == prefix;
+  const int n_before = block_sum_int(before, S.ired);
+  *cum = above + (float)(n_before + 1) * es;
+  return tok;
+}
+
+__global__ __launch_bounds__(ST) void k_sample_top_p(const float* logits, int64_t ld, int V, float inv_t,
+                                                     float top_p, const float* u, int32_t* out) {
+  __shared__ SampleLds S;
+  const int t = threadIdx.x;
+  const float* L = logits + (size_t)blockIdx.x * ld;
+  const int C = (V + ST - 1) / ST;
+  const int beg = min(t * C, V), end = min(beg + C, V);
+  float m = -INFINITY;
+  for (int i = beg; i < end; ++i) m = fmaxf(m, L[i] * inv_t);
+  m = block_max16(m, S.red);
+  float s = 0.f;
+  for (int i = beg; i < end; ++i) s += expf(L[i] * inv_t - m);
+  const float total = block_sum<ST / WAVE>(s, S.red);
+  // nucleus: the first token whose running mass reaches top_p of the total
+  float mass;
+  const int cut = select_token(S, L, beg, end, inv_t, m, top_p * total, true, &mass);
+  // the draw: the first token whose running mass exceeds u times the nucleus mass
+  float cum;
+  int tok = select_token(S, L, beg, end, inv_t, m, u[blockIdx.x] * mass, false, &cum);
+  // rounding may not place the draw after the cut: order (e descending, id ascending)
+  if (t == 0) {
+    const float ec = expf(L[cut] * inv_t - m), et = expf(L[tok] * inv_t - m);
+    if (et < ec || (et == ec && tok > cut)) tok = cut;
+    out[blockIdx.x] = tok;
+  }
+}
+
+hipError_t launch_embed(const void* E, int e_bf16, int64_t V, int H, const int32_t* ids, int n, float* x,
+                        hipStream_t st) {
+  if (n <= 0) return hipSuccess;
+  if (e_bf16)
+    hipLaunchKernelGGL(k_embed<bf16_t>, dim3(n), dim3(256), 0, st, (const bf16_t*)E, V, H, ids, x);
+  else
+    hipLaunchKernelGGL(k_embed<float>, dim3(n), dim3(256), 0, st, (const float*)E, V, H, ids, x);
+  return hipGetLastError();
+}
+
+hipError_t launch_logit_scale(const float* part, int splits, size_t sstride, float* logits, int64_t ld, int n,
+                              int64_t V, const float* sz, hipStream_t st) {
+  if (n <= 0) return hipSuccess;
+  dim3 grid((unsigned)((V + 255) / 256), n);
+  hipLaunchKernelGGL(k_logit_scale, grid, dim3(256), 0, st, part, splits, sstride, logits, ld, V, sz);
+  return hipGetLastError();
+}
+
+hipError_t launch_sample_top_p(const float* logits, int64_t ld, int n, int64_t V, float temperature, float top_p,
+                               const float* u, int32_t* out, hipStream_t st) {
+  if (n <= 0) return hipSuccess;
+  hipLaunchKernelGGL(k_sample_top_p, dim3(n), dim3(ST), 0, st, logits, ld, (int)V, 1.0f / temperature, top_p,
+                     u, out);
+  return hipGetLastError();
+}
+
+}  // namespace dory

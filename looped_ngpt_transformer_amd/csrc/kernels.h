@@ -144,4 +144,16 @@ hipError_t launch_fill_kv(const KVLayout& kv, int seq_slot, int stream_idx, int 
 hipError_t launch_quantize_mxfp8(const void* w, int w_bf16, int64_t rows, int64_t cols,
                                  uint8_t* codes, uint8_t* scales, hipStream_t st);
 
+// ------------------------------------------------- vocabulary side (k_vocab.hip)
+// x[i] = N(E[ids[i]]) float [n, H]; ids outside [0, V) give zero rows.
+hipError_t launch_embed(const void* E, int e_bf16, int64_t V, int H, const int32_t* ids, int n, float* x,
+                        hipStream_t st);
+// logits[i][v] = sz[v] * sum over splits of part[s][i][v] (row stride ld, split stride
+// sstride elements; part may be logits itself for one split).
+hipError_t launch_logit_scale(const float* part, int splits, size_t sstride, float* logits, int64_t ld, int n,
+                              int64_t V, const float* sz, hipStream_t st);
+// out[i] = the token u[i] draws from row i of logits under temperature and top-p.
+hipError_t launch_sample_top_p(const float* logits, int64_t ld, int n, int64_t V, float temperature, float top_p,
+                               const float* u, int32_t* out, hipStream_t st);
+
 }  // namespace dory

@@ -126,6 +126,8 @@ struct dory_ctx {
   int mode = DORY_KV_PER_LOOP;
   std::vector<dory_layer_weights> lw;
   std::vector<bool> lw_bound;
+  dory_vocab_weights vocab{};
+  bool vocab_bound = false;
   void* pool = nullptr;
   size_t pool_bytes = 0;
   int64_t n_pages = 0;
@@ -1005,6 +1007,110 @@ int dory_test_fill_kv(dory_ctx* ctx, void* stream, int32_t seq_id, int layer, in
   if ((r = flush_deltas(ctx, st, 0))) return r;
   HIPCHK(launch_fill_kv(kv_layout(ctx, layer), q.slot, ctx->stream_of(layer, slot), pos0, n, k, v, st),
          "fill_kv");
+  return DORY_OK;
+}
+
+int dory_bind_vocab(dory_ctx* ctx, const dory_vocab_weights* v) {
+  if (!ctx) return DORY_ERR_INVALID_ARG;
+  if (!v || !v->embed || !v->lm_head || !v->logit_scale) return ctx->fail(DORY_ERR_INVALID_ARG, "null vocabulary pointer");
+  if (v->vocab < 128 || v->vocab > (1 << 24) || v->vocab % 128)
+    return ctx->fail(DORY_ERR_INVALID_ARG, "vocabulary size must be a multiple of 128 in [128, 2^24]");
+  if (((uintptr_t)v->embed | (uintptr_t)v->lm_head) & 15)
+    return ctx->fail(DORY_ERR_INVALID_ARG, "vocabulary tables must be 16-byte aligned");
+  ctx->vocab = *v;
+  ctx->vocab_bound = true;
+  return DORY_OK;
+}
+
+int dory_embed(dory_ctx* ctx, void* stream, int n, const int32_t* ids, float* x_out) {
+  if (!ctx) return DORY_ERR_INVALID_ARG;
+  if (!ctx->vocab_bound) return ctx->fail(DORY_ERR_STATE, "vocabulary not bound");
+  if (n < 1 || n > ctx->cfg.max_rows || !ids || !x_out)
+    return ctx->fail(DORY_ERR_INVALID_ARG, "need 1 <= n <= max_rows and non-null ids, x_out");
+  hipStream_t st = (hipStream_t)stream;
+  Prof pr(ctx, st, DORY_KC_VOCAB);
+  HIPCHK(launch_embed(ctx->vocab.embed, ctx->cfg.act_dtype == DORY_DTYPE_BF16, ctx->vocab.vocab, ctx->D.H, ids, n,
+                      x_out, st),
+         "embedding");
+  pr.end(0.0, (double)n * ctx->D.H * (ctx->D.esz + 4) + 4.0 * n);
+  return DORY_OK;
+}
+
+int dory_logits(dory_ctx* ctx, void* stream, int n, const float* states, float* logits) {
+  if (!ctx) return DORY_ERR_INVALID_ARG;
+  if (!ctx->vocab_bound) return ctx->fail(DORY_ERR_STATE, "vocabulary not bound");
+  if (!ctx->ws) return ctx->fail(DORY_ERR_STATE, "workspace not bound");
+  if (n < 1 || n > ctx->cfg.max_rows || !states || !logits)
+    return ctx->fail(DORY_ERR_INVALID_ARG, "need 1 <= n <= max_rows and non-null states, logits");
+  hipStream_t st = (hipStream_t)stream;
+  const int H = ctx->D.H;
+  const int64_t V = ctx->vocab.vocab;
+  const bool f32 = ctx->cfg.act_dtype == DORY_DTYPE_F32;
+  char* ws = ctx->ws;
+  GemmArgs g;
+  g.B = ctx->vocab.lm_head;
+  g.M = n;
+  g.N = (int)V;
+  g.K = H;
+  g.lda = H;
+  g.C = logits;
+  g.ldc = (int)V;
+  int splits = 1;
+  if (f32) {
+    g.A = states;
+    g.act = ACT_F32;
+    g.wfmt = W_F32;
+    g.epi = EPI_F32;
+  } else {
+    // the states in the activation type, as the projections read them
+    Prof ps(ctx, st, DORY_KC_UPDATE);
+    HIPCHK(launch_stage_input(states, (float*)(ws + ctx->W.s), ws + ctx->W.sb, n, H, ACT_BF16, st), "LM-head input");
+    ps.end(0.0, (double)n * H * (4 + 4 + 2));
+    g.A = ws + ctx->W.sb;
+    g.act = ACT_BF16;
+    g.wfmt = W_BF16;
+    if (n <= SKINNY_M) {  // decode-sized: split-K streaming tiles
+      splits = gemm_pick_splits(n, (int)V, H, W_BF16);
+      g.epi = EPI_PARTIAL;
+      g.splits = splits;
+      if (splits > 1) {
+        if ((size_t)splits * n * V > ctx->W.part_floats)
+          return ctx->fail(DORY_ERR_UNSUPPORTED, "LM-head partials exceed the workspace");
+        g.C = ws + ctx->W.part;
+      }
+    } else {
+      g.epi = EPI_F32;
+    }
+  }
+  {
+    Prof pr(ctx, st, DORY_KC_GEMM);
+    const hipError_t e = launch_gemm(g, st);
+    if (e != hipSuccess) return hip_fail(ctx, e, "LM-head GEMM");
+    pr.end(2.0 * n * (double)V * H, (double)V * H * ctx->D.esz + (double)n * H * ctx->D.esz + 4.0 * n * V * splits);
+  }
+  {
+    Prof pr(ctx, st, DORY_KC_VOCAB);
+    const float* part = splits > 1 ? (const float*)(ws + ctx->W.part) : logits;
+    HIPCHK(launch_logit_scale(part, splits, (size_t)n * V, logits, V, n, V, ctx->vocab.logit_scale, st),
+           "logit scale");
+    pr.end(0.0, 4.0 * n * V * (splits + 1) + 4.0 * V);
+  }
+  return DORY_OK;
+}
+
+int dory_sample_top_p(void* stream, int n, int64_t vocab, const float* logits, int64_t ld, float temperature,
+                      float top_p, const float* u, int32_t* tokens) {
+  if (n < 1 || vocab < 1 || vocab > (1 << 24) || ld < vocab || !logits || !u || !tokens ||
+      !(temperature > 0.f) || !std::isfinite(temperature) || !(top_p > 0.f) || !(top_p <= 1.f)) {
+    g_create_err = "bad sampling argument (need n >= 1, 1 <= vocab <= 2^24, ld >= vocab, temperature > 0, "
+                   "0 < top_p <= 1, non-null pointers)";
+    return DORY_ERR_INVALID_ARG;
+  }
+  const hipError_t e = launch_sample_top_p(logits, ld, n, vocab, temperature, top_p, u, tokens, (hipStream_t)stream);
+  if (e != hipSuccess) {
+    g_create_err = hipGetErrorString(e);
+    return DORY_ERR_HIP;
+  }
   return DORY_OK;
 }
 

@@ -49,14 +49,19 @@ class dory_layer_weights(C.Structure):
                  "alpha_attn", "alpha_mlp", "s_qk")]
 
 
+class dory_vocab_weights(C.Structure):
+    _fields_ = [("vocab", C.c_int64), ("embed", C.c_void_p), ("lm_head", C.c_void_p),
+                ("logit_scale", C.c_void_p)]
+
+
 class dory_kernel_stats(C.Structure):
     _fields_ = [("launches", C.c_int64), ("ms", C.c_double), ("flops", C.c_double),
                 ("bytes", C.c_double)]
 
 
-KC_GEMM, KC_ATTN, KC_ROPE, KC_UPDATE, KC_SWIGLU, KC_MERGE = range(6)
+KC_GEMM, KC_ATTN, KC_ROPE, KC_UPDATE, KC_SWIGLU, KC_MERGE, KC_VOCAB = range(7)
 KC_NAMES = {KC_GEMM: "gemm", KC_ATTN: "attention", KC_ROPE: "rope_kv", KC_UPDATE: "update",
-            KC_SWIGLU: "swiglu", KC_MERGE: "attn_merge"}
+            KC_SWIGLU: "swiglu", KC_MERGE: "attn_merge", KC_VOCAB: "vocab"}
 
 _P = C.c_void_p
 _I32P = C.POINTER(C.c_int32)
@@ -86,6 +91,10 @@ _SIGS = {
     "dory_test_gemm": (C.c_int, [_P, _P, C.c_int, _P, _P, C.c_int, C.c_int, C.c_int, C.c_int, C.c_int, _P,
                                  C.c_int, C.POINTER(C.c_int)]),
     "dory_quantize_mxfp8": (C.c_int, [_P, _P, C.c_int, C.c_int64, C.c_int64, _P, _P]),
+    "dory_bind_vocab": (C.c_int, [_P, C.POINTER(dory_vocab_weights)]),
+    "dory_embed": (C.c_int, [_P, _P, C.c_int, _P, _P]),
+    "dory_logits": (C.c_int, [_P, _P, C.c_int, _P, _P]),
+    "dory_sample_top_p": (C.c_int, [_P, C.c_int, C.c_int64, _P, C.c_int64, C.c_float, C.c_float, _P, _P]),
     "dory_profile_enable": (C.c_int, [_P, C.c_int]),
     "dory_profile_read": (C.c_int, [_P, C.c_int, C.POINTER(dory_kernel_stats)]),
     "dory_sync": (C.c_int, [_P, _P]),
@@ -280,6 +289,28 @@ def dory_quantize_mxfp8(w, codes, scales, stream=None):
     wd = DTYPE_BF16 if w.dtype == torch.bfloat16 else DTYPE_F32
     rows, cols = w.shape
     _check(lib().dory_quantize_mxfp8(_stream(stream), _ptr(w), wd, rows, cols, _ptr(codes), _ptr(scales)))
+
+
+def dory_bind_vocab(ctx, embed, lm_head, logit_scale):
+    """Bind the vocabulary tables (device tensors [V, H] in the activation type, and the
+    float [V] logit scale); the caller keeps them alive."""
+    v = dory_vocab_weights(int(embed.shape[0]), embed.data_ptr(), lm_head.data_ptr(), logit_scale.data_ptr())
+    _check(lib().dory_bind_vocab(ctx, C.byref(v)), ctx)
+
+
+def dory_embed(ctx, ids, x_out, stream=None):
+    _check(lib().dory_embed(ctx, _stream(stream), int(ids.shape[0]), _ptr(ids), _ptr(x_out)), ctx)
+
+
+def dory_logits(ctx, states, logits, stream=None):
+    _check(lib().dory_logits(ctx, _stream(stream), int(states.shape[0]), _ptr(states), _ptr(logits)), ctx)
+
+
+def dory_sample_top_p(logits, u, tokens, temperature=1.0, top_p=0.95, vocab=None, stream=None):
+    n, ld = int(logits.shape[0]), int(logits.stride(0))
+    vocab = int(logits.shape[1]) if vocab is None else int(vocab)
+    _check(lib().dory_sample_top_p(_stream(stream), n, vocab, _ptr(logits), ld, float(temperature),
+                                   float(top_p), _ptr(u), _ptr(tokens)))
 
 
 def dory_sync(ctx=None, stream=None):

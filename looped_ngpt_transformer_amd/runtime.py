@@ -67,6 +67,25 @@ class DoryRuntime:
         D.dory_decode_step(self.ctx, seq_ids, x, y)
         return y
 
+    def bind_vocab(self, tables: dict):
+        """Bind embed / lm_head [V, H] (activation type) and logit_scale [V] (float)."""
+        t = {k: v.to(self.device).contiguous() for k, v in tables.items()}
+        self._keep.extend(t.values())
+        self.vocab = int(t["embed"].shape[0])
+        D.dory_bind_vocab(self.ctx, t["embed"], t["lm_head"], t["logit_scale"])
+
+    def embed(self, ids, x=None):
+        if x is None:
+            x = torch.empty((ids.shape[0], self.shape["hidden"]), dtype=torch.float32, device=self.device)
+        D.dory_embed(self.ctx, ids, x)
+        return x
+
+    def logits(self, states, out=None):
+        if out is None:
+            out = torch.empty((states.shape[0], self.vocab), dtype=torch.float32, device=self.device)
+        D.dory_logits(self.ctx, states, out)
+        return out
+
     def close(self):
         if self.ctx is not None:
             torch.cuda.synchronize(self.device)

@@ -16,7 +16,7 @@ oracle module):
   among the nGPT scales, initialised like the others). The effective vector is taken as
   given; how it is stored for training is out of scope.
 * sampling: temperature T and nucleus (top-p) sampling with the generation settings of
-  the MXFP8 article's model card (T = 1.0, top_p = 0.95): probabilities softmax(l / T);
+  the MXFP8 article's deployment section (T = 1.0, top_p = 0.95): probabilities softmax(l / T);
   tokens ordered by probability, highest first, equal probabilities by lower id first;
   the nucleus is the shortest prefix of that order whose cumulative probability reaches
   top_p; one uniform draw u in [0, 1) per row selects the first nucleus token whose

@@ -92,7 +92,10 @@ def _seed(*parts: int) -> int:
 
 
 _NAME_ID = {"w_qkvg": 1, "w_o": 2, "w_gu": 3, "w_down": 4, "alpha_attn": 5,
-            "alpha_mlp": 6, "s_qk": 7, "x": 8, "k": 9, "v": 10}
+            "alpha_mlp": 6, "s_qk": 7, "x": 8, "k": 9, "v": 10, "embed": 11, "lm_head": 12,
+            "logit_scale": 13, "ids": 14, "u": 15}
+
+VOCAB = 131072  # the tokenizer's vocabulary (MXFP8 article, checkpoint notes)
 
 
 def _gen(device, *parts):
@@ -157,3 +160,34 @@ def make_kv(cfg: dict, seed: int, seq: int, layer: int, slot: int, pos0: int, n:
     gv = _gen(device, seed, seq, layer, slot, pos0, _NAME_ID["v"])
     v = torch.randn((n, Hkv, d), generator=gv, device=device, dtype=torch.float32) * WEIGHT_STD
     return k.to(store).contiguous(), v.to(store).contiguous()
+
+
+def make_vocab(cfg: dict, vocab: int, seed: int, device="cpu", scale=(15.0, 25.0)) -> dict:
+    """Seeded vocabulary tables: input and output embeddings [vocab, H] whose rows are
+    Gaussian directions (unit norm, the sphere nGPT keeps embeddings on) stored in the
+    activation type, and a per-token logit scale drawn from U(scale) (the effective
+    scale; with unit-norm states and rows, logits span about +-scale / sqrt(H) * 3)."""
+    H = cfg["hidden"]
+    store = torch.float32 if cfg["act_dtype"] == "f32" else torch.bfloat16
+    out = {}
+    for name in ("embed", "lm_head"):
+        g = _gen(device, seed, vocab, _NAME_ID[name])
+        e = torch.randn((vocab, H), generator=g, device=device, dtype=torch.float32)
+        out[name] = (e / e.norm(dim=1, keepdim=True)).to(store).contiguous()
+    g = _gen(device, seed, vocab, _NAME_ID["logit_scale"])
+    lo, hi = scale
+    out["logit_scale"] = (lo + (hi - lo) * torch.rand((vocab,), generator=g, device=device,
+                                                       dtype=torch.float32)).contiguous()
+    return out
+
+
+def make_ids(n: int, vocab: int, seed: int, device="cpu") -> torch.Tensor:
+    """n seeded token ids, uniform over [0, vocab), int32."""
+    g = _gen(device, seed, vocab, _NAME_ID["ids"])
+    return torch.randint(0, vocab, (n,), generator=g, device=device, dtype=torch.int32)
+
+
+def make_draws(n: int, seed: int, stream: int = 0, device="cpu") -> torch.Tensor:
+    """n seeded uniform draws in [0, 1), float32 (the sampler's random numbers)."""
+    g = _gen(device, seed, stream, _NAME_ID["u"])
+    return torch.rand((n,), generator=g, device=device, dtype=torch.float32)

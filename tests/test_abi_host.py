@@ -202,3 +202,41 @@ def test_sequence_limits():
     assert e.value.code == D.ERR_INVALID_ARG
     assert D.dory_seq_len(ctx, 0) == 300
     D.dory_destroy(ctx)
+
+
+def test_vocabulary_calls_validate_before_device_work():
+    c = cfg()
+    ctx = ctx_with_fakes(c, bind_weights=True)
+    fake = 0x7F3000000000
+    with pytest.raises(D.DoryError) as e:      # vocabulary not bound yet
+        D._check(D.lib().dory_embed(ctx, None, 1, D.C.c_void_p(fake), D.C.c_void_p(fake)), ctx)
+    assert e.value.code == D.ERR_STATE
+    with pytest.raises(D.DoryError) as e:
+        D._check(D.lib().dory_logits(ctx, None, 1, D.C.c_void_p(fake), D.C.c_void_p(fake)), ctx)
+    assert e.value.code == D.ERR_STATE
+    for vocab, ptrs in ((100, (fake, fake, fake)), (0, (fake, fake, fake)), (1 << 25, (fake, fake, fake)),
+                        (1024, (0, fake, fake)), (1024, (fake + 8, fake, fake))):
+        v = D.dory_vocab_weights(vocab, *ptrs)
+        with pytest.raises(D.DoryError) as e:
+            D._check(D.lib().dory_bind_vocab(ctx, D.C.byref(v)), ctx)
+        assert e.value.code == D.ERR_INVALID_ARG
+    D._check(D.lib().dory_bind_vocab(ctx, D.C.byref(D.dory_vocab_weights(1024, fake, fake, fake))), ctx)
+    for n in (0, 257):                          # max_rows is 256
+        with pytest.raises(D.DoryError) as e:
+            D._check(D.lib().dory_logits(ctx, None, n, D.C.c_void_p(fake), D.C.c_void_p(fake)), ctx)
+        assert e.value.code == D.ERR_INVALID_ARG
+        with pytest.raises(D.DoryError) as e:
+            D._check(D.lib().dory_embed(ctx, None, n, D.C.c_void_p(fake), D.C.c_void_p(fake)), ctx)
+        assert e.value.code == D.ERR_INVALID_ARG
+    D.dory_destroy(ctx)
+
+
+@pytest.mark.parametrize("n,vocab,ld,temp,top_p", [
+    (0, 1000, 1000, 1.0, 0.95), (1, 0, 1000, 1.0, 0.95), (1, 1000, 999, 1.0, 0.95),
+    (1, 1000, 1000, 0.0, 0.95), (1, 1000, 1000, float("inf"), 0.95), (1, 1000, 1000, 1.0, 0.0),
+    (1, 1000, 1000, 1.0, 1.5), (1, 1000, 1000, 1.0, float("nan")), (1, (1 << 24) + 1, 1 << 25, 1.0, 0.9)])
+def test_sampler_rejects_bad_arguments(n, vocab, ld, temp, top_p):
+    fake = D.C.c_void_p(0x7F3000000000)
+    rc = D.lib().dory_sample_top_p(None, n, vocab, fake, ld, temp, top_p, fake, fake)
+    assert rc == D.ERR_INVALID_ARG
+    assert "sampling" in D.lib().dory_last_error(None).decode()
