@@ -8,7 +8,10 @@ and inputs are seeded synthetic data resident in HBM before timing starts.
 
 Also: --workload D runs decode steps of the 72-layer shape (batch 32 over a seeded
 32768-token KV context) and --workload Q the MXFP8 decode (batch 128, 8192 context,
-k = 4, last_loop); --ks 1,2,4 measures several loop counts.
+k = 4, last_loop); --ks 1,2,4 measures several loop counts. --workload G is D with
+the vocabulary side in the loop: each step's final states go through the LM head
+(131072 tokens), top-p sampling (T 1.0, p 0.95, seeded draws) and the embedding of the
+sampled tokens, which is the next step's input.
 
 Prints one JSON line. The roofline object covers the dominant kernel class (the
 projection GEMMs for prefill, the split-key attention kernel for decode) from HIP events around each launch
@@ -34,6 +37,8 @@ WORKLOAD_TEXT = {
     "Q": "16/40/16 (72 layers) MXFP8 W8A16, decode batch 128 over a seeded 8192-token KV context",
     "L": "16/40/16 (72 layers) bf16, batch 1, chunked prefill (chunks of 8192)",
     "T": "tiny looped nGPT fp32, prefill 64",
+    "G": "Full 16/40/16 (72 layers) bf16, generation batch 32 over a seeded 32768-token KV context: "
+         "decode step, LM head over 131072 tokens, top-p sampling, embedding of the sampled tokens",
 }
 
 
@@ -46,7 +51,7 @@ def parse():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=5)
     ap.add_argument("--warmup", type=int, default=2)
-    ap.add_argument("--workload", default="P", choices=["P", "D", "Q", "L", "T"])
+    ap.add_argument("--workload", default="P", choices=["P", "D", "Q", "L", "T", "G"])
     ap.add_argument("--k", type=int, default=None)
     ap.add_argument("--ks", default=None, help="comma list of loop counts to measure too")
     ap.add_argument("--mode", default=None, choices=["per_loop", "last_loop"])
@@ -107,6 +112,17 @@ def roofline_of(stats, kind, workload):
             "frac": round(ach / PEAK_HBM_GBS, 4),
             "traffic": measured_traffic("decode_attention", workload, ["k_attn.hip", "common.h", "kernels.h"]),
             "launches": a["launches"], "avg_launch_us": round(1e3 * a["ms"] / a["launches"], 2)}
+
+
+def lm_head_line(stats, steps):
+    """The LM head (logits GEMM over the vocabulary + logit scale + embedding lookup),
+    HBM-bound: algorithmic bytes (the [V, H] bf16 table once per step, states, logits)
+    over its summed HIP-event time."""
+    v = stats["vocab"]
+    ach = v["bytes"] / (v["ms"] / 1e3) / 1e9
+    return {"bound": "hbm", "achieved": round(ach, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
+            "frac": round(ach / PEAK_HBM_GBS, 4), "launches": v["launches"],
+            "ms_per_step": round(v["ms"] / steps, 3)}
 
 
 def time_prefill(rt, D, torch, X, tokens, steps, warmup, chunk=None):
@@ -215,11 +231,13 @@ def bench_prefill(args, torch, synth, D, DoryRuntime):
 
 def bench_decode(args, torch, synth, D, DoryRuntime):
     wl = args.workload
-    shape = synth.config(wl)
-    batch = args.batch or (32 if wl == "D" else 128)
-    ctx_len = args.context or (32768 if wl == "D" else 8192)
-    k = args.k or (2 if wl == "D" else 4)
-    mode = args.mode or ("per_loop" if wl == "D" else "last_loop")
+    gen = wl == "G"
+    shape = synth.config("D" if gen else wl)
+    dl = wl in ("D", "G")
+    batch = args.batch or (32 if dl else 128)
+    ctx_len = args.context or (32768 if dl else 8192)
+    k = args.k or (2 if dl else 4)
+    mode = args.mode or ("per_loop" if dl else "last_loop")
     ks = sorted({k} | ({int(x) for x in args.ks.split(",")} if args.ks else set()))
     log(f"[bench] workload {wl}: weights")
     weights = synth.make_weights(shape, 1234, "cuda")
@@ -242,14 +260,30 @@ def bench_decode(args, torch, synth, D, DoryRuntime):
         X = synth.make_inputs(batch * (steps + args.warmup), shape["hidden"], 77, device="cuda")
         Y = torch.empty((batch, shape["hidden"]), dtype=torch.float32, device="cuda")
         ids = list(range(batch))
+        if gen:
+            rt.bind_vocab(synth.make_vocab(shape, synth.VOCAB, 4321, "cuda"))
+            U = synth.make_draws(batch * (steps + args.warmup + 1), 99, device="cuda")
+            LG = torch.empty((batch, synth.VOCAB), dtype=torch.float32, device="cuda")
+            TOK = torch.empty((batch,), dtype=torch.int32, device="cuda")
+            XG = X[:batch].clone()
+
+        def step(s):
+            if not gen:
+                D.dory_decode_step(rt.ctx, ids, X[s * batch:(s + 1) * batch], Y)
+                return
+            D.dory_decode_step(rt.ctx, ids, XG, Y)
+            D.dory_logits(rt.ctx, Y, LG)
+            D.dory_sample_top_p(LG, U[s * batch:(s + 1) * batch], TOK, temperature=1.0, top_p=0.95)
+            D.dory_embed(rt.ctx, TOK, XG)
+
         for s in range(args.warmup):
-            D.dory_decode_step(rt.ctx, ids, X[s * batch:(s + 1) * batch], Y)
+            step(s)
         torch.cuda.synchronize()
-        # timed steps: HIP events around the attention launches only
-        D.dory_profile_enable(rt.ctx, [D.KC_ATTN])
+        # timed steps: HIP events around the attention launches (and the LM head) only
+        D.dory_profile_enable(rt.ctx, [D.KC_ATTN] + ([D.KC_VOCAB] if gen else []))
         t0 = time.perf_counter()
         for s in range(args.warmup, args.warmup + steps):
-            D.dory_decode_step(rt.ctx, ids, X[s * batch:(s + 1) * batch], Y)
+            step(s)
         torch.cuda.synchronize()
         dt = (time.perf_counter() - t0) / steps
         D.dory_profile_enable(rt.ctx, False)
@@ -257,7 +291,7 @@ def bench_decode(args, torch, synth, D, DoryRuntime):
         kvb = D.dory_kv_bytes_in_use(rt.ctx)
         # one more (untimed) step with every kernel class recorded, for the breakdown
         D.dory_profile_enable(rt.ctx, True)
-        D.dory_decode_step(rt.ctx, ids, X[:batch], Y)
+        step(args.warmup + steps)
         torch.cuda.synchronize()
         D.dory_profile_enable(rt.ctx, False)
         brk = kernel_stats(rt, D)
@@ -269,7 +303,8 @@ def bench_decode(args, torch, synth, D, DoryRuntime):
     dt, stats, kvb, brk = results[k]
     tot_bytes = sum(s["bytes"] for s in brk.values())
     out = {
-        "metric": "decode tokens/s (k=%d)" % k, "value": round(batch / dt, 2), "unit": "tokens/s",
+        "metric": ("generation" if gen else "decode") + " tokens/s (k=%d)" % k, "value": round(batch / dt, 2),
+        "unit": "tokens/s",
         "n_gpus": 1, "steps": steps, "warmup": args.warmup, "ms_per_step": round(dt * 1e3, 3),
         "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "bf16",
         "data": "synthetic (seeded random weights, seeded KV context, unit-norm inputs)",
@@ -277,6 +312,7 @@ def bench_decode(args, torch, synth, D, DoryRuntime):
                    "kv_mode": mode, "weights": shape["weight_format"],
                    "executed_layers": shape["n_in"] + shape["n_out"] + k * shape["n_rec"]},
         "roofline": roofline_of(stats, "hbm", wl),
+        **({"lm_head": lm_head_line(stats, steps)} if gen else {}),
         "step_hbm_gbs": round(tot_bytes / dt / 1e9, 1),
         "kv_bytes_in_use": kvb,
         "kernels": {n: {"launches": s["launches"], "ms": round(s["ms"], 3),

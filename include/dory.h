@@ -273,8 +273,8 @@ int dory_quantize_mxfp8(void* stream, const void* w, int w_dtype, int64_t rows,
 #define DORY_KC_UPDATE 3 /* nGPT update / loop boundary, input staging */
 #define DORY_KC_SWIGLU 4 /* SwiGLU from split-K partials */
 #define DORY_KC_MERGE 5  /* merge of the split-key partials, gate (decode and fp32 calls) */
-#define DORY_KC_VOCAB 6  /* vocabulary side: embedding, logit scale, top-p sampling (the LM-head
-                            product counts as GEMM) */
+#define DORY_KC_VOCAB 6  /* vocabulary side: the LM-head GEMM and its logit scale, the embedding
+                            lookup (the sampler takes no context and is not recorded) */
 #define DORY_KC_COUNT 7
 typedef struct dory_kernel_stats {
   int64_t launches; /* kernel launches recorded */

@@ -41,14 +41,17 @@ __global__ __launch_bounds__(256) void k_logit_scale(const float* part, int spli
 }
 
 // ------------------------------------------------------------------ top-p sampling
-// One block of ST threads per row; thread t owns the consecutive ids [t C, t C + C).
-// Weights e_v = exp(l_v / T - max) (recomputed identically in every pass); their float
-// bit patterns order the tokens like their probabilities. The sorted order is e
-// descending, equal e by lower id. Each selection finds the first token of that order
-// whose running mass meets a target: eight passes over 4-bit digits of the bit pattern,
-// high to low, narrow the key down (per-thread digit masses in LDS, summed in a fixed
-// order), then the tokens with exactly that key are taken in id order. Every sum has a
-// fixed order, so the result is a deterministic function of the logits and u.
+// One block of ST threads per row; thread t owns ids t, t + ST, t + 2 ST, ... (each load
+// instruction of a wave reads consecutive ids). Weights e_v = 2^((l_v - max) / T * log2 e)
+// are recomputed identically in every pass; their float bit patterns order the tokens
+// like their probabilities. The sorted order is e descending, equal e by lower id. Each
+// selection finds the first token of that order whose running mass meets a target:
+// eight passes over 4-bit digits of the bit pattern, high to low, narrow the key down
+// (per-thread digit masses in LDS, summed in a fixed order); the tokens with exactly that
+// key all weigh the same e*, so the j-th of them in id order has running mass
+// above + (j + 1) e*, which fixes j, and the token is the (j + 1)-th smallest id among
+// them. Every sum has a fixed order, so the result is a deterministic function of the
+// logits and u.
 constexpr int ST = 1024;
 
 struct SampleLds {
@@ -60,6 +63,7 @@ struct SampleLds {
   int ired[16];
   uint32_t prefix;
   float above;
+  int jsel;
 };
 
 __device__ __forceinline__ float block_max16(float v, float* red) {
@@ -100,28 +104,17 @@ __device__ __forceinline__ int block_sum_int(int v, int* red) {
   return t;
 }
 
-// exclusive prefix sum of one int per thread, in thread order
-__device__ __forceinline__ int block_excl_scan(int v, int* red) {
-  const int lane = threadIdx.x & (WAVE - 1), w = threadIdx.x / WAVE;
-  int x = v;
-#pragma unroll
-  for (int d = 1; d < WAVE; d <<= 1) {
-    const int y = __shfl_up(x, d, WAVE);
-    if (lane >= d) x += y;
-  }
-  __syncthreads();
-  if (lane == WAVE - 1) red[w] = x;
-  __syncthreads();
-  int off = 0;
-  for (int i = 0; i < w; ++i) off += red[i];
-  return off + x - v;
-}
+struct RowView {
+  const float* L;
+  int V;
+  float c, mz;  // e = 2^(l c - mz)
+  __device__ __forceinline__ float e(int i) const { return exp2f(L[i] * c - mz); }
+};
 
 // First token of the sorted order whose inclusive running mass reaches (incl) or
 // exceeds (!incl) target; if rounding leaves the target beyond the mass, the last token
 // of the order. Returns the token and sets cum to its inclusive running mass.
-__device__ int select_token(SampleLds& S, const float* L, int beg, int end, float inv_t, float m, float target,
-                            bool incl, float* cum) {
+__device__ int select_token(SampleLds& S, const RowView& R, float target, bool incl, float* cum) {
   const int t = threadIdx.x, lane = t & (WAVE - 1), w = t / WAVE;
   uint32_t prefix = 0;
   float above = 0.f;  // mass of the tokens whose key lies above the digits chosen so far
@@ -132,8 +125,8 @@ __device__ int select_token(SampleLds& S, const float* L, int beg, int end, floa
       S.bins[d][t] = 0.f;
       S.cnt[d][t] = 0;
     }
-    for (int i = beg; i < end; ++i) {
-      const float e = expf(L[i] * inv_t - m);
+    for (int i = t; i < R.V; i += ST) {
+      const float e = R.e(i);
       const uint32_t key = __float_as_uint(e);
       if (pass == 0 || (key >> (sh + 4)) == prefix) {
         const int d = (key >> sh) & 15;
@@ -185,27 +178,44 @@ __device__ int select_token(SampleLds& S, const float* L, int beg, int end, floa
     above = S.above;
     __syncthreads();
   }
-  // tokens whose key is exactly `prefix`, in id order: the j-th (from 0) has running
-  // mass above + (j + 1) * e*
+  // the tokens whose key is exactly `prefix`: their count (the last digit's count), the
+  // first j whose running mass above + (j + 1) e* meets the target (else the last one)
   const float es = __uint_as_float(prefix);
-  int n_mine = 0;
-  for (int i = beg; i < end; ++i) n_mine += __float_as_uint(expf(L[i] * inv_t - m)) == prefix;
-  int j = block_excl_scan(n_mine, S.ired);
-  int cand = INT_MAX, last_mine = -1;
-  for (int i = beg; i < end; ++i) {
-    if (__float_as_uint(expf(L[i] * inv_t - m)) != prefix) continue;
-    last_mine = i;
-    const float c = above + (float)(j + 1) * es;
-    if (cand == INT_MAX && (incl ? c >= target : c > target)) cand = i;
-    ++j;
+  const int n_tied = S.bincnt[prefix & 15];
+  if (t == 0) {
+    int j = n_tied - 1;
+    for (int q = 0; q < n_tied; ++q) {
+      const float c = above + (float)(q + 1) * es;
+      if (incl ? c >= target : c > target) {
+        j = q;
+        break;
+      }
+    }
+    S.jsel = j;
   }
-  int tok = block_min_int(cand, S.ired);
-  if (tok == INT_MAX) tok = -block_min_int(-last_mine, S.ired);  // the last tied token
-  // its running mass follows from the number of tied tokens before it
-  int before = 0;
-  for (int i = beg; i < end && i < tok; ++i) before += __float_as_uint(expf(L[i] * inv_t - m)) == prefix;
-  const int n_before = block_sum_int(before, S.ired);
-  *cum = above + (float)(n_before + 1) * es;
+  __syncthreads();
+  const int jsel = S.jsel;
+  *cum = above + (float)(jsel + 1) * es;
+  int tok;
+  if (n_tied == 1) {
+    int mine = INT_MAX;
+    for (int i = t; i < R.V; i += ST)
+      if (__float_as_uint(R.e(i)) == prefix) mine = i;
+    tok = block_min_int(mine, S.ired);
+  } else {
+    // the (jsel + 1)-th smallest id among them: the largest x with fewer than jsel + 1
+    // of them below x, by bisection on x
+    int lo = 0, hi = R.V;  // count(lo) <= jsel < count(hi)
+    while (hi - lo > 1) {
+      const int mid = (lo + hi) / 2;
+      int n = 0;
+      for (int i = t; i < mid; i += ST) n += __float_as_uint(R.e(i)) == prefix;
+      if (block_sum_int(n, S.ired) <= jsel) lo = mid;
+      else hi = mid;
+    }
+    tok = lo;
+  }
+  __syncthreads();
   return tok;
 }
 
@@ -213,24 +223,25 @@ __global__ __launch_bounds__(ST) void k_sample_top_p(const float* logits, int64_
                                                      float top_p, const float* u, int32_t* out) {
   __shared__ SampleLds S;
   const int t = threadIdx.x;
-  const float* L = logits + (size_t)blockIdx.x * ld;
-  const int C = (V + ST - 1) / ST;
-  const int beg = min(t * C, V), end = min(beg + C, V);
+  RowView R;
+  R.L = logits + (size_t)blockIdx.x * ld;
+  R.V = V;
+  R.c = inv_t * 1.4426950408889634f;
   float m = -INFINITY;
-  for (int i = beg; i < end; ++i) m = fmaxf(m, L[i] * inv_t);
-  m = block_max16(m, S.red);
+  for (int i = t; i < V; i += ST) m = fmaxf(m, R.L[i]);
+  R.mz = block_max16(m, S.red) * R.c;
   float s = 0.f;
-  for (int i = beg; i < end; ++i) s += expf(L[i] * inv_t - m);
+  for (int i = t; i < V; i += ST) s += R.e(i);
   const float total = block_sum<ST / WAVE>(s, S.red);
   // nucleus: the first token whose running mass reaches top_p of the total
   float mass;
-  const int cut = select_token(S, L, beg, end, inv_t, m, top_p * total, true, &mass);
+  const int cut = select_token(S, R, top_p * total, true, &mass);
   // the draw: the first token whose running mass exceeds u times the nucleus mass
   float cum;
-  int tok = select_token(S, L, beg, end, inv_t, m, u[blockIdx.x] * mass, false, &cum);
+  int tok = select_token(S, R, u[blockIdx.x] * mass, false, &cum);
   // rounding may not place the draw after the cut: order (e descending, id ascending)
   if (t == 0) {
-    const float ec = expf(L[cut] * inv_t - m), et = expf(L[tok] * inv_t - m);
+    const float ec = R.e(cut), et = R.e(tok);
     if (et < ec || (et == ec && tok > cut)) tok = cut;
     out[blockIdx.x] = tok;
   }

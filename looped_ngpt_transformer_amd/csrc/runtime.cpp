@@ -1083,7 +1083,7 @@ int dory_logits(dory_ctx* ctx, void* stream, int n, const float* states, float* 
     }
   }
   {
-    Prof pr(ctx, st, DORY_KC_GEMM);
+    Prof pr(ctx, st, DORY_KC_VOCAB);
     const hipError_t e = launch_gemm(g, st);
     if (e != hipSuccess) return hip_fail(ctx, e, "LM-head GEMM");
     pr.end(2.0 * n * (double)V * H, (double)V * H * ctx->D.esz + (double)n * H * ctx->D.esz + 4.0 * n * V * splits);
