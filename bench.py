@@ -269,7 +269,8 @@ def bench_decode(args, torch, synth, D, DoryRuntime):
 
         def step(s):
             if not gen:
-                D.dory_decode_step(rt.ctx, ids, X[s * batch:(s + 1) * batch], Y)
+                r = s % (steps + args.warmup)  # the untimed breakdown step reuses the first inputs
+                D.dory_decode_step(rt.ctx, ids, X[r * batch:(r + 1) * batch], Y)
                 return
             D.dory_decode_step(rt.ctx, ids, XG, Y)
             D.dory_logits(rt.ctx, Y, LG)
