@@ -170,3 +170,48 @@ def test_sampling_equal_logits_go_by_id():
     want = [OV.sample_top_p(np.zeros(4096), 1.0, 0.95, float(x)) for x in u.cpu().numpy()]
     assert list(toks) == want
     assert max(want) < 3892
+
+
+def test_generation_loop_against_oracle():
+    """Three generation steps on the Dory layer shape after a 40-token prompt: decode ->
+    LM head -> top-p -> embedding of the sampled token -> next decode input. Each step's
+    final states are compared with the oracle's decode of the same input, the logits
+    with the oracle's LM head on the GPU's states, the token for validity on the GPU's
+    logits, and the next input with the oracle's embedding of that token (which the
+    oracle then also takes as its next input)."""
+    from oracle import dory_oracle as O
+    from tests.gpu_helpers import compare, oracle_model
+    S = PSMALL
+    k, mode, V = 2, "per_loop", 8192
+    w = gpu_weights(S, 11)
+    rt = DoryRuntime(S, w, max_loops=2, max_seqs=1, max_seq_len=64, max_rows=64, mode=mode, loops=k)
+    tab = synth.make_vocab(S, V, 12, "cuda", scale=(300.0, 500.0))
+    rt.bind_vocab(tab)
+    cfg, W = oracle_model(S, w)
+    seq = O.Sequence(cfg)
+    X = synth.make_inputs(40, S["hidden"], 13, device="cuda")
+    y = rt.prefill([0], [40], X)
+    torch.cuda.synchronize()
+    compare(y.cpu().double().numpy(), O.prefill(cfg, W, seq, to_np(X), k, mode), S, "prompt")
+    emb, head, sz = to_np(tab["embed"]), to_np(tab["lm_head"]), to_np(tab["logit_scale"])
+    x = synth.make_inputs(1, S["hidden"], 14, device="cuda")
+    u = synth.make_draws(3, 15, device="cuda")
+    tokens = []
+    for step in range(3):
+        x_np = x.cpu().double().numpy()
+        y = rt.decode([0], x)
+        lg = rt.logits(y)
+        tok = torch.empty((1,), dtype=torch.int32, device="cuda")
+        D.dory_sample_top_p(lg, u[step:step + 1], tok)
+        x = rt.embed(tok)
+        torch.cuda.synchronize()
+        y_np = y.cpu().double().numpy()
+        compare(y_np, O.prefill(cfg, W, seq, x_np, k, mode), S, f"step {step}")
+        lg_np = lg.cpu().double().numpy()
+        d = np.abs(lg_np - OV.logits(y_np, head, sz))
+        assert np.all(d <= sz[None, :] * (2.0 ** -9 + 1e-5)), f"step {step}: logits max |d| {d.max():.3e}"
+        t = tok.cpu().numpy()
+        check_valid(lg_np, u[step:step + 1].cpu().numpy(), t, 1.0, 0.95)
+        assert np.abs(x.cpu().double().numpy() - OV.embed(emb, t)).max() <= 1e-6
+        tokens.append(int(t[0]))
+    rt.close()
