@@ -265,6 +265,18 @@ int dory_test_gemm(void* stream, const void* A, int lda, const void* B, const ui
 int dory_quantize_mxfp8(void* stream, const void* w, int w_dtype, int64_t rows,
                         int64_t cols, uint8_t* codes, uint8_t* scales);
 
+/* NVFP4 quantiser (W4A16; arXiv summary §5.1-5.2: dynamic MSE scale selection; paper
+ * summary: E2M1 elements with E4M3 scale factors): w [rows, cols] device (w_dtype F32 or
+ * BF16), cols % 16 == 0 -> codes [rows, cols/2] bytes (two E2M1 codes each, element 2j
+ * in the low nibble), scales [rows, cols/16] E4M3 bytes (one per 16 along a row) and
+ * g [1] float, the matrix scale 2^ceil(log2(amax / 2688)) (1 for an all-zero matrix).
+ * Each block of 16 takes the positive E4M3 scale code whose float32 sum of squared
+ * errors (element by element, in order, no fused multiply-add) is smallest, the smaller
+ * code on equal sums; elements round to the nearest E2M1 value, ties to even, saturating
+ * at 6. A dequantised weight e2m1 * e4m3 * g is exactly a bf16 value. */
+int dory_quantize_nvfp4(void* stream, const void* w, int w_dtype, int64_t rows, int64_t cols,
+                        uint8_t* codes, uint8_t* scales, float* g);
+
 /* ---- tracing: per-kernel-class launch timing with HIP events on the call's stream */
 #define DORY_KC_GEMM 0   /* projections: [q|k|v|gate], output, SwiGLU gate/up, down */
 #define DORY_KC_ATTN 1   /* attention over the KV cache: the prefill kernel (with gate), or the

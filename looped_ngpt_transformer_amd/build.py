@@ -17,7 +17,7 @@ LIB = os.path.join(HERE, "libdory.so")
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 ARCH = "gfx950"
 
-SOURCES = ["runtime.cpp", "k_update.hip", "k_rope.hip", "k_attn.hip", "k_attn_prefill.hip", "k_mlp.hip", "k_gemm.hip", "k_vocab.hip"]
+SOURCES = ["runtime.cpp", "k_update.hip", "k_rope.hip", "k_attn.hip", "k_attn_prefill.hip", "k_mlp.hip", "k_gemm.hip", "k_vocab.hip", "k_nvfp4.hip"]
 
 FLAGS = ["-O3", "-std=c++17", "-fPIC", f"--offload-arch={ARCH}",
          # packed fp32 VALU ops are kept off for every device pass

@@ -156,4 +156,13 @@ hipError_t launch_logit_scale(const float* part, int splits, size_t sstride, flo
 hipError_t launch_sample_top_p(const float* logits, int64_t ld, int n, int64_t V, float temperature, float top_p,
                                const float* u, int32_t* out, hipStream_t st);
 
+// ------------------------------------------------------- NVFP4 weights (k_nvfp4.hip)
+// codes [rows, cols/2] (two E2M1 codes a byte, element 2j in the low nibble), E4M3 block
+// scales [rows, cols/16], the power-of-two matrix scale g (one float).
+hipError_t launch_quantize_nvfp4(const void* w, int w_bf16, int64_t rows, int64_t cols, uint8_t* codes,
+                                 uint8_t* scales, float* g, hipStream_t st);
+// out [rows, cols] bf16 = e2m1 * e4m3 * g (exact)
+hipError_t launch_expand_nvfp4(const uint8_t* codes, const uint8_t* scales, const float* g, int64_t rows,
+                               int64_t cols, void* out, hipStream_t st);
+
 }  // namespace dory

@@ -1171,6 +1171,26 @@ int dory_quantize_mxfp8(void* stream, const void* w, int w_dtype, int64_t rows, 
   return DORY_OK;
 }
 
+int dory_quantize_nvfp4(void* stream, const void* w, int w_dtype, int64_t rows, int64_t cols, uint8_t* codes,
+                        uint8_t* scales, float* g) {
+  if (!w || !codes || !scales || !g || rows < 0 || cols < 0 || cols % 16 ||
+      (w_dtype != DORY_DTYPE_F32 && w_dtype != DORY_DTYPE_BF16)) {
+    g_create_err = "bad quantiser argument";
+    return DORY_ERR_INVALID_ARG;
+  }
+  if (rows * (cols / 16) > (int64_t)0x7fffffff * 64) {
+    g_create_err = "matrix too large";
+    return DORY_ERR_INVALID_ARG;
+  }
+  const hipError_t e = launch_quantize_nvfp4(w, w_dtype == DORY_DTYPE_BF16, rows, cols, codes, scales, g,
+                                             (hipStream_t)stream);
+  if (e != hipSuccess) {
+    g_create_err = hipGetErrorString(e);
+    return DORY_ERR_HIP;
+  }
+  return DORY_OK;
+}
+
 int dory_profile_enable(dory_ctx* ctx, int class_mask) {
   if (!ctx || class_mask < 0 || class_mask >= (1 << DORY_KC_COUNT)) return DORY_ERR_INVALID_ARG;
   if (class_mask) {

@@ -91,6 +91,7 @@ _SIGS = {
     "dory_test_gemm": (C.c_int, [_P, _P, C.c_int, _P, _P, C.c_int, C.c_int, C.c_int, C.c_int, C.c_int, _P,
                                  C.c_int, C.POINTER(C.c_int)]),
     "dory_quantize_mxfp8": (C.c_int, [_P, _P, C.c_int, C.c_int64, C.c_int64, _P, _P]),
+    "dory_quantize_nvfp4": (C.c_int, [_P, _P, C.c_int, C.c_int64, C.c_int64, _P, _P, _P]),
     "dory_bind_vocab": (C.c_int, [_P, C.POINTER(dory_vocab_weights)]),
     "dory_embed": (C.c_int, [_P, _P, C.c_int, _P, _P]),
     "dory_logits": (C.c_int, [_P, _P, C.c_int, _P, _P]),
@@ -311,6 +312,12 @@ def dory_sample_top_p(logits, u, tokens, temperature=1.0, top_p=0.95, vocab=None
     vocab = int(logits.shape[1]) if vocab is None else int(vocab)
     _check(lib().dory_sample_top_p(_stream(stream), n, vocab, _ptr(logits), ld, float(temperature),
                                    float(top_p), _ptr(u), _ptr(tokens)))
+
+
+def dory_quantize_nvfp4(w, codes, scales, g, stream=None):
+    wd = DTYPE_BF16 if str(w.dtype) == "torch.bfloat16" else DTYPE_F32
+    rows, cols = int(w.shape[0]), int(w.shape[1])
+    _check(lib().dory_quantize_nvfp4(_stream(stream), _ptr(w), wd, rows, cols, _ptr(codes), _ptr(scales), _ptr(g)))
 
 
 def dory_sync(ctx=None, stream=None):
