@@ -51,6 +51,8 @@ extern "C" {
 #define DORY_WFMT_F32 0
 #define DORY_WFMT_BF16 1
 #define DORY_WFMT_MXFP8 2 /* E4M3 codes + one E8M0 scale byte per 32 along K */
+#define DORY_WFMT_NVFP4 3 /* packed E2M1 codes + one E4M3 scale byte per 16 along K + a
+                             power-of-two float per matrix (dory_quantize_nvfp4) */
 
 /* ---- recurrent KV-cache modes (arXiv §6.1) */
 #define DORY_KV_PER_LOOP 0  /* k slots per recurrent attention layer, slot t-1 in loop t */
@@ -89,7 +91,7 @@ typedef struct dory_config {
   int32_t qk_norm;       /* 0 or 1 */
   int32_t attn_gate;     /* DORY_GATE_* */
   int32_t act_dtype;     /* DORY_DTYPE_*: activations fed to projections and KV cache */
-  int32_t weight_format; /* DORY_WFMT_*; F32 needs act F32; BF16/MXFP8 need act BF16 */
+  int32_t weight_format; /* DORY_WFMT_*; F32 needs act F32; BF16/MXFP8/NVFP4 need act BF16 */
   int32_t max_loops;     /* 1..DORY_MAX_LOOPS */
   int32_t max_seqs;      /* live sequences at once */
   int32_t max_seq_len;   /* positions per sequence, <= DORY_MAX_POSITIONS */
@@ -104,7 +106,10 @@ typedef struct dory_config {
  *  w_o    [H, Hq*d]
  *  w_gu   [2*I, H]                 rows: SwiGLU gate | up
  *  w_down [H, I]
- *  s_*    MXFP8 only: E8M0 scale bytes [rows, K/32] of the matching matrix (else NULL)
+ *  s_*    MXFP8: E8M0 scale bytes [rows, K/32] of the matching matrix; NVFP4: E4M3
+ *         block scale bytes [rows, K/16]; else NULL
+ *  g_*    NVFP4 only: the matching matrix's scale (one float, device); else NULL.
+ *         NVFP4 matrices hold packed codes [rows, K/2] (element 2j in the low nibble)
  *  alpha_attn, alpha_mlp [H] float: effective per-channel rates (arXiv §2: 0.05 init)
  *  s_qk   [d] float: effective query-key scale
  */
@@ -120,6 +125,10 @@ typedef struct dory_layer_weights {
   const float* alpha_attn;
   const float* alpha_mlp;
   const float* s_qk;
+  const float* g_qkvg;
+  const float* g_o;
+  const float* g_gu;
+  const float* g_down;
 } dory_layer_weights;
 
 /* Create a context for cfg. Checks shapes, formats and limits (INVALID_ARG /

@@ -474,7 +474,7 @@ int gemm_pick_splits(int M, int N, int K, int wfmt) {
   // enough work-groups to keep the weight stream in flight (each split a multiple of 64,
   // not too short)
   int tiles = (N / 64) * ((M + 127) / 128), cap = 32;
-  if (wfmt == W_MXFP8 && N % 128 == 0) {  // 32 or 64 activation rows per tile, <= 8 splits
+  if ((wfmt == W_MXFP8 || wfmt == W_NVFP4) && N % 128 == 0) {  // 32 or 64 activation rows per tile, <= 8 splits
     tiles = (N / 128) * ((M + (M <= 32 ? 31 : 63)) / (M <= 32 ? 32 : 64));
     cap = 8;
   }
@@ -943,6 +943,147 @@ static hipError_t go_mx(const GemmArgs& g, hipStream_t st) {
   return hipGetLastError();
 }
 
+// NVFP4 (W4A16) split-K tiles for decode-sized M, on v_mfma_f32_32x32x16_bf16: the
+// MXFP8 tiles' design with 4-bit codes. The bf16 activations and the packed E2M1 codes
+// (32 bytes per weight row per 64-wide slice) stream into an LDS ring; the E4M3 block
+// scales of the next slice (one per 16 along K, i.e. one per k-step: four bytes per
+// weight row) are loaded into registers a slice ahead. Each lane expands its 8 codes of
+// a B fragment with the hardware fp4 -> float conversion, multiplies by the block scale
+// times the power-of-two matrix scale (exact), and truncates to bf16 (exact: every such
+// product is a bf16 value). Output: fp32 split-K partials (EPI_PARTIAL).
+__device__ __forceinline__ float e4m3_scale_f32(uint32_t c) {
+  const uint32_t e = (c >> 3) & 15, m = c & 7;
+  return e == 0 ? (float)m * 0x1p-9f : __uint_as_float(((e + 120u) << 23) | (m << 20));
+}
+
+template <int BM, int BN, int WMW, int WNW, int STAGES>
+__global__ __launch_bounds__(GT) void k_gemm_nv32(GemmArgs g) {
+  constexpr int PBK = 64;
+  constexpr int TM = BM / WMW, TN = BN / WNW;
+  constexpr int FM = TM / 32, FN = TN / 32;
+  constexpr int ACH = BM * 8, BCH = BN * 2;   // 16-byte chunks of A (bf16) / B (packed codes)
+  constexpr int NINST = (ACH + BCH) / 64;
+  constexpr int MAXI = (NINST + 3) / 4;
+  static_assert(WMW * WNW == 4 && TM % 32 == 0 && TN % 32 == 0, "tile");
+  static_assert(ACH % 64 == 0 && BCH % 64 == 0, "tile rows");
+  static_assert((STAGES - 2) * MAXI <= 31 && STAGES >= 2, "pipeline");
+  __shared__ __align__(16) uint4 sm[STAGES][ACH + BCH];
+
+  const int t = threadIdx.x, lane = t & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(t >> 6);
+  const int wm = wave / WNW, wn = wave % WNW;
+  const int n_tile = blockIdx.x, m0 = blockIdx.y * BM, split = blockIdx.z;
+  const int Ks = g.K / g.splits, kbeg = split * Ks, nk = Ks / PBK;
+  const bf16_t* A = (const bf16_t*)g.A;
+  const uint8_t* B = (const uint8_t*)g.B;
+  const int my_inst = (NINST - wave + 3) / 4;
+  const int l32 = lane & 31, lh = lane >> 5;
+  const float gsc = g.Bg[0];
+
+  auto issue = [&](int slot, int k0) {
+#pragma unroll
+    for (int q = 0; q < MAXI; ++q) {
+      const int inst = wave + 4 * q;
+      if (inst < NINST) {
+        const int sidx = inst * 64 + lane;
+        const void* src;
+        if (sidx < ACH) {  // A row r, chunk c (8 bf16)
+          const int r = sidx >> 3, c = swzc<8>(r, sidx & 7) - r * 8;
+          src = A + (size_t)min(m0 + r, g.M - 1) * g.lda + k0 + 8 * c;
+        } else {           // B row r, chunk c (32 codes); chunk slot c ^ ((r >> 3) & 1)
+          const int s2 = sidx - ACH, r = s2 >> 1, c = (s2 & 1) ^ ((r >> 3) & 1);
+          src = B + (size_t)(n_tile * BN + r) * (g.K / 2) + k0 / 2 + 16 * c;
+        }
+        __builtin_amdgcn_global_load_lds((gbl_void_t)src, (lds_void_t)(&sm[slot][inst * 64]), 16, 0, 0);
+      }
+    }
+  };
+  // E4M3 scales of B fragment j for the four k-steps of slice k0, one byte each
+  auto ldscale = [&](int k0, uint32_t (&sc)[FN]) {
+#pragma unroll
+    for (int j = 0; j < FN; ++j) {
+      const int n = n_tile * BN + wn * TN + j * 32 + l32;
+      sc[j] = *(const uint32_t*)(g.Bs + (size_t)n * (g.K / 16) + k0 / 16);
+    }
+  };
+
+  f32x16 acc[FM][FN];
+#pragma unroll
+  for (int i = 0; i < FM; ++i)
+#pragma unroll
+    for (int j = 0; j < FN; ++j)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.f;
+
+  // The scale loads of slice it+1 are issued after the tile loads of this step, so the
+  // wait below (which counts only tile loads as newer than tile it) is conservative.
+  uint32_t scn[FN];
+#pragma unroll
+  for (int st = 0; st < STAGES - 1; ++st)
+    if (st < nk) issue(st, kbeg + PBK * st);
+  ldscale(kbeg, scn);
+  for (int it = 0; it < nk; ++it) {
+    wait_vmcnt(min(STAGES - 2, nk - 1 - it) * my_inst);
+    __syncthreads();
+    if (it + STAGES - 1 < nk) issue((it + STAGES - 1) % STAGES, kbeg + PBK * (it + STAGES - 1));
+    uint32_t sc[FN];
+#pragma unroll
+    for (int j = 0; j < FN; ++j) sc[j] = scn[j];
+    if (it + 1 < nk) ldscale(kbeg + PBK * (it + 1), scn);
+    const uint4* As = sm[it % STAGES];
+    const unsigned char* Bb = (const unsigned char*)(As + ACH);
+#pragma unroll
+    for (int ks = 0; ks < PBK / 16; ++ks) {
+      bf16x8 af[FM], bfr[FN];
+#pragma unroll
+      for (int i = 0; i < FM; ++i)
+        af[i] = __builtin_bit_cast(bf16x8, As[swzc<8>(wm * TM + i * 32 + l32, 2 * ks + lh)]);
+#pragma unroll
+      for (int j = 0; j < FN; ++j) {
+        const int r = wn * TN + j * 32 + l32;
+        // codes of K elements 16 ks + 8 lh .. + 7: bytes 8 ks + 4 lh .. + 3 of the row
+        const uint32_t cw = *(const uint32_t*)(Bb + (r * 2 + ((ks >> 1) ^ ((r >> 3) & 1))) * 16 + 8 * (ks & 1) + 4 * lh);
+        const float S = e4m3_scale_f32((sc[j] >> (8 * ks)) & 0xFF) * gsc;
+        uint32_t v[4];
+#pragma unroll
+        for (int b = 0; b < 4; ++b) {
+          f32x2 f;
+          if (b == 0) f = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(cw, 1.0f, 0);
+          else if (b == 1) f = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(cw, 1.0f, 1);
+          else if (b == 2) f = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(cw, 1.0f, 2);
+          else f = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(cw, 1.0f, 3);
+          const float x0 = f[0] * S, x1 = f[1] * S;
+          v[b] = (__float_as_uint(x0) >> 16) | (__float_as_uint(x1) & 0xFFFF0000u);
+        }
+        bfr[j] = __builtin_bit_cast(bf16x8, make_uint4(v[0], v[1], v[2], v[3]));
+      }
+#pragma unroll
+      for (int i = 0; i < FM; ++i)
+#pragma unroll
+        for (int j = 0; j < FN; ++j)
+          acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[i], bfr[j], acc[i][j], 0, 0, 0);
+    }
+  }
+  // split-K partials: register r of lane l = C[8 (r / 4) + 4 (l / 32) + r % 4][l % 32]
+  float* C = (float*)g.C + (size_t)split * g.M * g.ldc;
+#pragma unroll
+  for (int i = 0; i < FM; ++i)
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+      const int m = m0 + wm * TM + i * 32 + 8 * (r >> 2) + 4 * lh + (r & 3);
+      if (m >= g.M) continue;
+#pragma unroll
+      for (int j = 0; j < FN; ++j) C[(size_t)m * g.ldc + n_tile * BN + wn * TN + j * 32 + l32] = acc[i][j][r];
+    }
+}
+
+template <int BM, int BN, int WMW, int WNW, int STAGES>
+static hipError_t go_nv(const GemmArgs& g, hipStream_t st) {
+  dim3 grid(g.N / BN, (g.M + BM - 1) / BM, g.splits);
+  hipLaunchKernelGGL((k_gemm_nv32<BM, BN, WMW, WNW, STAGES>), grid, dim3(GT), 0, st, g);
+  return hipGetLastError();
+}
+
 template <int BM, int BN, int WMW, int WNW, int EPI, int STAGES, int PBK = 32>
 static hipError_t go_pipe(const GemmArgs& g, hipStream_t st, int ntiles_n) {
   dim3 grid(ntiles_n, (g.M + BM - 1) / BM, g.splits);
@@ -1002,6 +1143,7 @@ hipError_t launch_gemm(const GemmArgs& gin, hipStream_t st) {
     return hipGetLastError();
   }
   if (g.act != ACT_BF16 || g.K % BK != 0 || g.K % (g.splits * BK) != 0) return hipErrorInvalidValue;
+  if (g.wfmt == W_NVFP4 && g.epi != EPI_PARTIAL) return hipErrorInvalidValue;  // large M: expand to bf16 first
   const bool bf = g.wfmt == W_BF16;  // bf16 weights: direct-to-LDS pipeline
   switch (g.epi) {
     case EPI_PARTIAL:  // small M (decode): stream the weights, split K
@@ -1010,6 +1152,11 @@ hipError_t launch_gemm(const GemmArgs& gin, hipStream_t st) {
         if (g.M <= 32) return go_pipe<32, 64, 1, 4, EPI_PARTIAL, 4, 64>(g, st, g.N / 64);
         if (g.M <= 64) return go_pipe<64, 64, 1, 4, EPI_PARTIAL, 4, 64>(g, st, g.N / 64);
         return go_pipe<128, 64, 1, 4, EPI_PARTIAL, 3, 64>(g, st, g.N / 64);
+      }
+      if (g.wfmt == W_NVFP4) {  // 128 weight rows per tile
+        if (g.N % 128 || (g.K / g.splits) % 64 || !g.Bs || !g.Bg) return hipErrorInvalidValue;
+        if (g.M <= 32) return go_nv<32, 128, 1, 4, 4>(g, st);
+        return go_nv<64, 128, 1, 4, 4>(g, st);
       }
       if (g.N % 128 == 0) {  // MXFP8: 128 weight rows per tile
         if (g.M <= 32) return go_mx<32, 128, 1, 4, 4>(g, st);

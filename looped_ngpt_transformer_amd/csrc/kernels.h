@@ -8,7 +8,7 @@
 namespace dory {
 
 enum ActType { ACT_F32 = 0, ACT_BF16 = 1 };
-enum WFmt { W_F32 = 0, W_BF16 = 1, W_MXFP8 = 2 };
+enum WFmt { W_F32 = 0, W_BF16 = 1, W_MXFP8 = 2, W_NVFP4 = 3 };
 
 // ---------------------------------------------------------------- GEMM  C = A B^T
 enum Epi {
@@ -23,7 +23,8 @@ struct GemmArgs {
   const void* A = nullptr;  // [M, K] activations (act type), row stride lda
   int lda = 0;
   const void* B = nullptr;  // [N, K] weights (wfmt), row stride K
-  const uint8_t* Bs = nullptr;  // MXFP8 scales [N, K/32]
+  const uint8_t* Bs = nullptr;  // MXFP8 scales [N, K/32]; NVFP4 E4M3 block scales [N, K/16]
+  const float* Bg = nullptr;    // NVFP4 matrix scale (one float); B then holds packed codes [N, K/2]
   int M = 0, N = 0, K = 0;
   int act = ACT_BF16;
   int wfmt = W_BF16;

@@ -47,7 +47,7 @@ struct Dims {
 };
 
 struct WsLayout {
-  size_t table, meta, s, x, sb, qkvg, q, o, h, part, apart, total;
+  size_t table, meta, s, x, sb, qkvg, q, o, h, part, apart, wexp, total;
   size_t part_floats, apart_floats;
   size_t meta_ints;
 };
@@ -103,6 +103,10 @@ WsLayout layout_of(const dory_config& c, const Dims& D) {
   W.part = take(pf * 4);
   W.apart_floats = std::max<size_t>(R, 256) * D.Hq * (D.d + 2) * 8;
   W.apart = take(W.apart_floats * 4);
+  // NVFP4: one weight matrix expanded to bf16 for the large-M GEMMs
+  const size_t wmax = std::max({(size_t)D.Nqkvg * D.H, (size_t)D.H * D.Nq, (size_t)2 * D.I * D.H,
+                                (size_t)D.H * D.I});
+  W.wexp = take(c.weight_format == DORY_WFMT_NVFP4 ? wmax * 2 : 0);
   W.total = off;
   return W;
 }
@@ -240,10 +244,10 @@ int check_config(const dory_config* c, std::string& msg) {
   if (c->attn_gate != DORY_GATE_NONE && c->attn_gate != DORY_GATE_ELEMENTWISE)
     return bad("attn_gate must be DORY_GATE_NONE or DORY_GATE_ELEMENTWISE");
   if (c->act_dtype != DORY_DTYPE_F32 && c->act_dtype != DORY_DTYPE_BF16) return bad("bad act_dtype");
-  if (c->weight_format < DORY_WFMT_F32 || c->weight_format > DORY_WFMT_MXFP8)
+  if (c->weight_format < DORY_WFMT_F32 || c->weight_format > DORY_WFMT_NVFP4)
     return bad("bad weight_format");
   if ((c->weight_format == DORY_WFMT_F32) != (c->act_dtype == DORY_DTYPE_F32))
-    return bad("F32 weights go with F32 activations; BF16/MXFP8 weights with BF16");
+    return bad("F32 weights go with F32 activations; BF16/MXFP8/NVFP4 weights with BF16");
   if (c->max_loops < 1 || c->max_loops > DORY_MAX_LOOPS) return bad("max_loops must be 1..8");
   if (c->max_seqs < 1 || c->max_rows < 1) return bad("max_seqs and max_rows must be >= 1");
   if (c->max_seq_len < 1 || c->max_seq_len > DORY_MAX_POSITIONS)
@@ -411,7 +415,10 @@ int run_layer(dory_ctx* ctx, hipStream_t st, const CallPlan& P, int l, int slot,
   const dory_layer_weights& w = ctx->lw[l];
   const int M = P.M;
   const int act = c.act_dtype == DORY_DTYPE_F32 ? ACT_F32 : ACT_BF16;
-  const int wf = c.weight_format == DORY_WFMT_F32 ? W_F32 : (c.weight_format == DORY_WFMT_BF16 ? W_BF16 : W_MXFP8);
+  const int wf = c.weight_format == DORY_WFMT_F32   ? W_F32
+                 : c.weight_format == DORY_WFMT_BF16 ? W_BF16
+                 : c.weight_format == DORY_WFMT_MXFP8 ? W_MXFP8
+                                                      : W_NVFP4;
   const bool f32 = act == ACT_F32;
   const bool skinny = !f32 && M <= SKINNY_M;
   const int32_t* meta = (const int32_t*)(ws + W.meta);
@@ -436,9 +443,25 @@ int run_layer(dory_ctx* ctx, hipStream_t st, const CallPlan& P, int l, int slot,
     g.ldc = ldc;
     return g;
   };
-  const double wbytes = wf == W_F32 ? 4.0 : (wf == W_BF16 ? 2.0 : 1.0 + 1.0 / 32);
-  auto run_gemm = [&](const GemmArgs& g) -> hipError_t {
+  const double wbytes = wf == W_F32 ? 4.0 : wf == W_BF16 ? 2.0 : wf == W_MXFP8 ? 1.0 + 1.0 / 32 : 0.5 + 1.0 / 16;
+  // NVFP4: the matrix scale that goes with a weight matrix of this layer
+  auto nv_scale = [&](const void* B) -> const float* {
+    return B == w.w_qkvg ? w.g_qkvg : B == w.w_o ? w.g_o : B == w.w_gu ? w.g_gu : w.g_down;
+  };
+  auto run_gemm = [&](const GemmArgs& g0) -> hipError_t {
     Prof pr(ctx, st, DORY_KC_GEMM);
+    GemmArgs g = g0;
+    if (wf == W_NVFP4) {
+      g.Bg = nv_scale(g0.B);
+      if (g.epi != EPI_PARTIAL) {  // large M: expand the matrix to bf16, then the bf16 tiles
+        const hipError_t x = launch_expand_nvfp4((const uint8_t*)g.B, g.Bs, g.Bg, g.N, g.K, ws + W.wexp, st);
+        if (x != hipSuccess) return x;
+        g.B = ws + W.wexp;
+        g.Bs = nullptr;
+        g.Bg = nullptr;
+        g.wfmt = W_BF16;
+      }
+    }
     const hipError_t e = launch_gemm(g, st);
     const double outb = g.epi == EPI_STORE_ACT || g.epi == EPI_SWIGLU ? 2.0 : 4.0 * g.splits;
     const double ncols = g.epi == EPI_SWIGLU ? g.n_half : g.N;
@@ -843,6 +866,9 @@ int dory_bind_weights(dory_ctx* ctx, int layer, const dory_layer_weights* w) {
     return ctx->fail(DORY_ERR_INVALID_ARG, "null weight pointer");
   if (ctx->cfg.weight_format == DORY_WFMT_MXFP8 && (!w->s_qkvg || !w->s_o || !w->s_gu || !w->s_down))
     return ctx->fail(DORY_ERR_INVALID_ARG, "MXFP8 weights need scale arrays");
+  if (ctx->cfg.weight_format == DORY_WFMT_NVFP4 &&
+      (!w->s_qkvg || !w->s_o || !w->s_gu || !w->s_down || !w->g_qkvg || !w->g_o || !w->g_gu || !w->g_down))
+    return ctx->fail(DORY_ERR_INVALID_ARG, "NVFP4 weights need block and matrix scales");
   const uintptr_t mask = 15;
   if (((uintptr_t)w->w_qkvg | (uintptr_t)w->w_o | (uintptr_t)w->w_gu | (uintptr_t)w->w_down) & mask)
     return ctx->fail(DORY_ERR_INVALID_ARG, "weight matrices must be 16-byte aligned");

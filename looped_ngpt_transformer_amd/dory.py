@@ -18,7 +18,7 @@ LIB_PATH = os.path.join(HERE, "libdory.so")
 
 OK, ERR_INVALID_ARG, ERR_STATE, ERR_OUT_OF_KV, ERR_UNSUPPORTED, ERR_HIP = 0, -1, -2, -3, -4, -5
 DTYPE_F32, DTYPE_BF16 = 0, 1
-WFMT_F32, WFMT_BF16, WFMT_MXFP8 = 0, 1, 2
+WFMT_F32, WFMT_BF16, WFMT_MXFP8, WFMT_NVFP4 = 0, 1, 2, 3
 KV_PER_LOOP, KV_LAST_LOOP = 0, 1
 GATE_NONE, GATE_ELEMENTWISE = 0, 1
 PAGE_TOKENS = 64
@@ -46,7 +46,7 @@ class dory_config(C.Structure):
 class dory_layer_weights(C.Structure):
     _fields_ = [(n, C.c_void_p) for n in
                 ("w_qkvg", "w_o", "w_gu", "w_down", "s_qkvg", "s_o", "s_gu", "s_down",
-                 "alpha_attn", "alpha_mlp", "s_qk")]
+                 "alpha_attn", "alpha_mlp", "s_qk", "g_qkvg", "g_o", "g_gu", "g_down")]
 
 
 class dory_vocab_weights(C.Structure):
@@ -142,7 +142,7 @@ def _i32(values):
 
 
 _ACT = {"f32": DTYPE_F32, "bf16": DTYPE_BF16}
-_WF = {"f32": WFMT_F32, "bf16": WFMT_BF16, "mxfp8": WFMT_MXFP8}
+_WF = {"f32": WFMT_F32, "bf16": WFMT_BF16, "mxfp8": WFMT_MXFP8, "nvfp4": WFMT_NVFP4}
 
 
 def make_config(d: dict, max_loops=4, max_seqs=1, max_seq_len=4096, max_rows=4096) -> dory_config:

@@ -26,19 +26,29 @@ class DoryRuntime:
         D.dory_bind_workspace(self.ctx, self.ws.data_ptr(), self.ws_bytes)
         D.dory_bind_kv_pool(self.ctx, self.pool.data_ptr(), kv_pages * self.page_bytes)
         self._keep = []
-        self.mx = {}  # (layer, matrix name) -> (E4M3 codes, E8M0 scales), MXFP8 only
+        self.mx = {}  # (layer, matrix name) -> quantised codes and scales (MXFP8, NVFP4)
         self.bind_weights(weights)
         D.dory_set_kv_mode(self.ctx, D.MODES[mode])
         D.dory_set_loops(self.ctx, loops)
 
     def bind_weights(self, weights: list):
         mx = self.shape["weight_format"] == "mxfp8"
+        nv = self.shape["weight_format"] == "nvfp4"
         for l, w in enumerate(weights):
             lw = D.dory_layer_weights()
             for name in ("w_qkvg", "w_o", "w_gu", "w_down"):
                 t = w[name]
                 assert t.is_contiguous() and t.device.type == "cuda"
-                if mx:
+                if nv:
+                    codes = torch.empty((t.shape[0], t.shape[1] // 2), dtype=torch.uint8, device=t.device)
+                    scales = torch.empty((t.shape[0], t.shape[1] // 16), dtype=torch.uint8, device=t.device)
+                    g = torch.empty((1,), dtype=torch.float32, device=t.device)
+                    D.dory_quantize_nvfp4(t, codes, scales, g)
+                    self.mx[(l, name)] = (codes, scales, g)
+                    setattr(lw, name, codes.data_ptr())
+                    setattr(lw, "s_" + name[2:], scales.data_ptr())
+                    setattr(lw, "g_" + name[2:], g.data_ptr())
+                elif mx:
                     codes = torch.empty(t.shape, dtype=torch.uint8, device=t.device)
                     scales = torch.empty((t.shape[0], t.shape[1] // 32), dtype=torch.uint8, device=t.device)
                     D.dory_quantize_mxfp8(t, codes, scales)

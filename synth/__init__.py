@@ -20,7 +20,7 @@ import math
 import torch
 
 # --------------------------------------------------------------------------- shapes
-# act/weight formats: "f32", "bf16", "mxfp8" (weights only)
+# act/weight formats: "f32", "bf16", "mxfp8", "nvfp4" (the last two for weights only)
 
 _DORY = dict(hidden=2560, n_q_heads=16, n_kv_heads=4, head_dim=160, intermediate=4096,
              window=1024, full_period=4, theta_swa=1e4, theta_full=1e7,
@@ -40,6 +40,8 @@ CONFIGS = {
     "L": dict(_DORY, n_in=16, n_rec=40, n_out=16),
     # 72-layer shape with MXFP8 weights (E4M3 + E8M0 per 32 along K), bf16 activations
     "Q": dict(_DORY, n_in=16, n_rec=40, n_out=16, weight_format="mxfp8"),
+    # 72-layer shape with NVFP4 weights (E2M1 + E4M3 per 16 along K + matrix scale)
+    "N": dict(_DORY, n_in=16, n_rec=40, n_out=16, weight_format="nvfp4"),
 }
 
 WORKLOADS = {
@@ -48,6 +50,7 @@ WORKLOADS = {
     "D": dict(batch=32, context=32768, decode_steps=256, loops=(1, 2, 4)),
     "L": dict(batch=1, prefill=131072, chunk=8192, loops=(2,)),
     "Q": dict(batch=128, context=8192, loops=(4,), kv_mode="last_loop"),
+    "N": dict(batch=128, context=8192, loops=(4,), kv_mode="last_loop"),
 }
 
 WEIGHT_STD = 0.02

@@ -8,6 +8,7 @@ import torch
 import synth
 from oracle import dory_oracle as O
 from oracle import mxfp8 as MX
+from oracle import nvfp4 as NV
 from tests.helpers import oracle_weights, to_np
 
 BF16_COS = 0.9995
@@ -19,9 +20,22 @@ def gpu_weights(shape, seed, alpha="const"):
     return synth.make_weights(shape, seed, "cuda", alpha=alpha)
 
 
+_NV_CACHE = {}
+
+
+def _nvfp4_dequantised(w):
+    """The oracle's NVFP4 round trip of a weight matrix, cached by content (the exhaustive
+    float32 scale search is slow in NumPy and the tests reuse their seeded weights)."""
+    import hashlib
+    key = (w.shape, hashlib.sha1(np.ascontiguousarray(w).tobytes()).hexdigest())
+    if key not in _NV_CACHE:
+        _NV_CACHE[key] = NV.dequantize(*NV.quantize(w))
+    return _NV_CACHE[key]
+
+
 def oracle_model(shape, w_gpu, rt=None):
-    """Oracle weights: the same bf16/fp32 values, or dequantised MXFP8 codes produced by
-    the oracle's own quantiser from the same bf16 values."""
+    """Oracle weights: the same bf16/fp32 values, or dequantised MXFP8 / NVFP4 codes
+    produced by the oracle's own quantisers from the same bf16 values."""
     cfg = O.Config.from_dict(shape)
     cpu = [{k: v.detach().cpu() for k, v in w.items()} for w in w_gpu]
     if shape["weight_format"] == "mxfp8":
@@ -29,6 +43,10 @@ def oracle_model(shape, w_gpu, rt=None):
             for name in ("w_qkvg", "w_o", "w_gu", "w_down"):
                 codes, scales = MX.quantize(to_np(w[name]))
                 w[name] = torch.from_numpy(MX.dequantize(codes, scales))
+    if shape["weight_format"] == "nvfp4":
+        for w in cpu:
+            for name in ("w_qkvg", "w_o", "w_gu", "w_down"):
+                w[name] = torch.from_numpy(_nvfp4_dequantised(to_np(w[name])))
     return cfg, oracle_weights(shape, cpu)
 
 

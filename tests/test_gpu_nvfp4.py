@@ -40,3 +40,36 @@ def test_quantiser_bit_exact(dtype, shape, std):
 def test_quantiser_all_zero_matrix():
     c, s, gs = quantize_gpu(torch.zeros((4, 32), dtype=torch.bfloat16, device="cuda"))
     assert gs == 1.0 and np.all(c == 0) and np.all(s == 1)
+
+
+# forward parity with NVFP4 weights: the oracle runs on the dequantised codes its own
+# quantiser produces from the same bf16 weights (bit-identical codes, checked above). The
+# oracle's exhaustive float32 scale search is slow in NumPy, so the forward tests use a
+# narrow bf16 layer shape that routes to the same kernels: hidden 512, 4/1 heads of 128,
+# SwiGLU 1024, [q|k|v|gate] 1280 rows, one layer per block, window 64.
+from tests.test_gpu_parity import _run_case, xin  # noqa: E402
+import synth  # noqa: E402
+
+NSMALL = dict(synth.config("P", n_in=1, n_rec=1, n_out=1, window=64), hidden=512, n_q_heads=4, n_kv_heads=1,
+              head_dim=128, intermediate=1024, attn_scale=128 ** 0.5, weight_format="nvfp4")
+
+
+@pytest.mark.parametrize("mode", ["per_loop", "last_loop"])
+def test_nvfp4_small_forward(mode):
+    """A 150-row prefill (the large-M GEMMs on matrices expanded to bf16) and two decode
+    steps (the 4-bit split-K tiles), with undamped rates."""
+    S = NSMALL
+    sched = [("prefill", [(0, xin(S, 150, 41))]),
+             ("decode", [(0, xin(S, 1, 42))]),
+             ("decode", [(0, xin(S, 1, 43))])]
+    _run_case(S, 2, mode, sched, max_rows=256, max_seq_len=256, max_seqs=1, sharp=True)
+
+
+@pytest.mark.parametrize("batch", [1, 40, 128])
+def test_nvfp4_decode_batches(batch):
+    """NVFP4 weights at decode batch sizes (split-K tiles of 32 and 64 rows): prefill
+    `batch` short sequences in one call, then one decode step for all of them."""
+    S = NSMALL
+    sched = [("prefill", [(i, xin(S, 2 + i % 3, 700 + i)) for i in range(batch)]),
+             ("decode", [(i, xin(S, 1, 900 + i)) for i in range(batch)])]
+    _run_case(S, 2, "last_loop", sched, max_rows=512, max_seq_len=16, max_seqs=batch, sharp=True)
