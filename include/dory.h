@@ -253,19 +253,24 @@ int dory_test_fill_kv(dory_ctx* ctx, void* stream, int32_t seq_id, int layer, in
 
 /* One projection GEMM exactly as a layer call launches it (test support for the GEMM
  * kernels): C = A B^T, A [M, K] bf16 device rows with stride lda elements, B [N, K]
- * device weights in format wfmt (DORY_WFMT_BF16, or DORY_WFMT_MXFP8 codes with B_scales
- * [N, K/32] E8M0 bytes; B_scales NULL otherwise). epi selects the output the layers use:
+ * device weights in format wfmt: DORY_WFMT_BF16; DORY_WFMT_MXFP8 codes with B_scales
+ * [N, K/32] E8M0 bytes; or DORY_WFMT_NVFP4 packed codes [N, K/2] with B_scales [N, K/16]
+ * E4M3 bytes and B_gscale the matrix scale (one device float). B_scales and B_gscale are
+ * NULL when the format has none. epi selects the output the layers use:
  *   0: C float [M, N] (prefill output and down projections);
  *   1: C float split-K partials [splits][M][N] (decode projections), summed by the caller;
  *   2: C bf16 [M, N] ([q|k|v|gate] projection in prefill);
  *   4: SwiGLU: B rows [0, N/2) gate, [N/2, N) up; C bf16 [M, N/2] = SiLU(gate) * up.
- * ldc = row stride of C in elements. The kernel and tile shape are the ones a layer call
- * would pick for these sizes (K % 64 == 0; N % 64 == 0, for epi 4 N % 128 == 0).
- * *splits receives the split count (1 unless epi 1). With C == NULL the call only
- * reports *splits. The caller owns every buffer; C must hold splits * M * ldc elements
- * for epi 1. Invalid sizes return DORY_ERR_INVALID_ARG before any device work. */
+ * Quantised formats take epi 1 only (layers expand NVFP4 matrices to bf16 for the other
+ * epilogues). ldc = row stride of C in elements. The kernel and tile shape are the ones a
+ * layer call would pick for these sizes (K % 64 == 0; N % 64 == 0, for epi 4 N % 128 == 0,
+ * for NVFP4 N % 128 == 0). *splits receives the split count (1 unless epi 1). With
+ * C == NULL the call only reports *splits. The caller owns every buffer; C must hold
+ * splits * M * ldc elements for epi 1. Invalid sizes return DORY_ERR_INVALID_ARG before
+ * any device work. */
 int dory_test_gemm(void* stream, const void* A, int lda, const void* B, const uint8_t* B_scales,
-                   int wfmt, int M, int N, int K, int epi, void* C, int ldc, int* splits);
+                   const float* B_gscale, int wfmt, int M, int N, int K, int epi, void* C, int ldc,
+                   int* splits);
 
 /* MXFP8 quantiser (arXiv §5.2: maximum scaling, group 32): w [rows, cols] device
  * (w_dtype F32 or BF16), cols % 32 == 0 -> codes [rows, cols] E4M3 bytes and scales

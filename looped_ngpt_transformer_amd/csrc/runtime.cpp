@@ -1141,17 +1141,19 @@ int dory_sample_top_p(void* stream, int n, int64_t vocab, const float* logits, i
 }
 
 int dory_test_gemm(void* stream, const void* A, int lda, const void* B, const uint8_t* B_scales,
-                   int wfmt, int M, int N, int K, int epi, void* C, int ldc, int* splits) {
-  const bool mx = wfmt == DORY_WFMT_MXFP8;
-  const bool ok_fmt = (wfmt == DORY_WFMT_BF16 && !B_scales) || (mx && B_scales);
+                   const float* B_gscale, int wfmt, int M, int N, int K, int epi, void* C, int ldc, int* splits) {
+  const bool mx = wfmt == DORY_WFMT_MXFP8, nv = wfmt == DORY_WFMT_NVFP4;
+  const bool ok_fmt = (wfmt == DORY_WFMT_BF16 && !B_scales && !B_gscale) || (mx && B_scales && !B_gscale) ||
+                      (nv && B_scales && B_gscale);
   const bool ok_epi = epi == EPI_F32 || epi == EPI_PARTIAL || epi == EPI_STORE_ACT || epi == EPI_SWIGLU;
   if (!A || !B || !splits || !ok_fmt || !ok_epi || M < 1 || N < 64 || K < 64 || K % 64 || N % 64 ||
       (epi == EPI_SWIGLU && N % 128) || lda < K || (C && ldc < (epi == EPI_SWIGLU ? N / 2 : N)) ||
-      (mx && epi != EPI_PARTIAL)) {
+      ((mx || nv) && epi != EPI_PARTIAL) || (nv && N % 128)) {
     g_create_err = "bad GEMM argument";
     return DORY_ERR_INVALID_ARG;
   }
-  const int S = epi == EPI_PARTIAL ? gemm_pick_splits(M, N, K, mx ? W_MXFP8 : W_BF16) : 1;
+  const int wf = mx ? W_MXFP8 : nv ? W_NVFP4 : W_BF16;
+  const int S = epi == EPI_PARTIAL ? gemm_pick_splits(M, N, K, wf) : 1;
   *splits = S;
   if (!C) return DORY_OK;
   GemmArgs g;
@@ -1163,7 +1165,8 @@ int dory_test_gemm(void* stream, const void* A, int lda, const void* B, const ui
   g.N = N;
   g.K = K;
   g.act = ACT_BF16;
-  g.wfmt = mx ? W_MXFP8 : W_BF16;
+  g.wfmt = wf;
+  g.Bg = B_gscale;
   g.epi = epi;
   g.splits = S;
   g.C = C;

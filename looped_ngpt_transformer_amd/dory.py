@@ -88,7 +88,7 @@ _SIGS = {
     "dory_last_layer_calls": (C.c_int, [_P, C.POINTER(C.c_int64)]),
     "dory_test_reserve": (C.c_int, [_P, C.c_int32, C.c_int32]),
     "dory_test_fill_kv": (C.c_int, [_P, _P, C.c_int32, C.c_int, C.c_int, C.c_int32, C.c_int32, _P, _P]),
-    "dory_test_gemm": (C.c_int, [_P, _P, C.c_int, _P, _P, C.c_int, C.c_int, C.c_int, C.c_int, C.c_int, _P,
+    "dory_test_gemm": (C.c_int, [_P, _P, C.c_int, _P, _P, _P, C.c_int, C.c_int, C.c_int, C.c_int, C.c_int, _P,
                                  C.c_int, C.POINTER(C.c_int)]),
     "dory_quantize_mxfp8": (C.c_int, [_P, _P, C.c_int, C.c_int64, C.c_int64, _P, _P]),
     "dory_quantize_nvfp4": (C.c_int, [_P, _P, C.c_int, C.c_int64, C.c_int64, _P, _P, _P]),
@@ -269,19 +269,19 @@ EPI_F32, EPI_PARTIAL, EPI_STORE_BF16, EPI_SWIGLU = 0, 1, 2, 4
 
 
 def dory_test_gemm(A, B, epi, out=None, B_scales=None, stream=None, M=None, N=None, K=None, lda=None,
-                   ldc=None):
+                   ldc=None, B_gscale=None):
     """One projection GEMM as a layer launches it: out = A B^T with the layer's epilogue
-    (see dory.h). Returns the split count; with out None only the split count is
-    computed."""
+    (see dory.h). B_scales alone: MXFP8 codes; B_scales and B_gscale: NVFP4 packed codes.
+    Returns the split count; with out None only the split count is computed."""
     M = M if M is not None else A.shape[0]
     K = K if K is not None else A.shape[1]
     N = N if N is not None else B.shape[0]
     lda = lda if lda is not None else A.stride(0)
     ldc = ldc if ldc is not None else (out.shape[-1] if out is not None else 0)
-    wf = WFMT_MXFP8 if B_scales is not None else WFMT_BF16
+    wf = WFMT_NVFP4 if B_gscale is not None else WFMT_MXFP8 if B_scales is not None else WFMT_BF16
     splits = C.c_int(0)
-    _check(lib().dory_test_gemm(_stream(stream), _ptr(A), lda, _ptr(B), _ptr(B_scales), wf, M, N, K, epi,
-                                _ptr(out), ldc, C.byref(splits)))
+    _check(lib().dory_test_gemm(_stream(stream), _ptr(A), lda, _ptr(B), _ptr(B_scales), _ptr(B_gscale), wf, M, N,
+                                K, epi, _ptr(out), ldc, C.byref(splits)))
     return splits.value
 
 

@@ -117,3 +117,35 @@ def test_rejects_bad_sizes():
     A, B = operands(64, 128, 96, 6)
     with pytest.raises(D.DoryError):
         D.dory_test_gemm(A, B, D.EPI_F32, None)  # K % 64 != 0
+
+
+def nvfp4_operands(N, K, seed):
+    """Synthetic NVFP4 weights drawn directly as codes (not from the quantiser): random
+    E2M1 codes, E4M3 block scales in [2^-3, 2^3), a power-of-two matrix scale; and their
+    value by the format's definition (e2m1 * e4m3 * g)."""
+    g = torch.Generator(device="cpu").manual_seed(seed)
+    codes = torch.randint(0, 256, (N, K // 2), generator=g, dtype=torch.int32).to(torch.uint8)
+    scales = torch.randint(0x20, 0x50, (N, K // 16), generator=g, dtype=torch.int32).to(torch.uint8)
+    gs = torch.tensor([2.0 ** -9])
+    e2m1 = torch.tensor([0, .5, 1, 1.5, 2, 3, 4, 6, -0., -.5, -1, -1.5, -2, -3, -4, -6])
+    c = codes.to(torch.int64)
+    q = torch.stack([e2m1[c & 15], e2m1[c >> 4]], dim=2).reshape(N, K)
+    s = scales.to(torch.int64)
+    e, m = (s >> 3) & 15, (s & 7).to(torch.float32)
+    sv = torch.where(e == 0, m * 2.0 ** -9, (1 + m / 8) * torch.exp2(e.to(torch.float32) - 7))
+    W = q * sv.repeat_interleave(16, dim=1) * gs
+    return codes.cuda(), scales.cuda(), gs.cuda(), W
+
+
+@pytest.mark.parametrize("M,N,K", [(1, 6400, 2560), (32, 2560, 4096), (100, 8192, 2560), (128, 2560, 2560)])
+def test_split_k_nvfp4(M, N, K):
+    A, _ = operands(M, 64, K, 7)
+    codes, scales, gs, W = nvfp4_operands(N, K, 8)
+    S = D.dory_test_gemm(A, codes, D.EPI_PARTIAL, None, B_scales=scales, B_gscale=gs, M=M, N=N)
+    out = torch.zeros((S, M, N), dtype=torch.float32, device="cuda")
+    assert D.dory_test_gemm(A, codes, D.EPI_PARTIAL, out, B_scales=scales, B_gscale=gs, M=M, N=N) == S
+    torch.cuda.synchronize()
+    ref = A.float().cpu() @ W.t()
+    # weights of size up to 6 * 2^3 * 2^-9 ~ 0.1: scale the absolute term of the tolerance
+    d = (out.sum(0).cpu() - ref).abs()
+    assert not (d > 2e-3 * (ref.abs() + 5.0)).any(), f"max |d| {float(d.max()):.3e}"
