@@ -8,7 +8,8 @@ and inputs are seeded synthetic data resident in HBM before timing starts.
 
 Also: --workload D runs decode steps of the 72-layer shape (batch 32 over a seeded
 32768-token KV context) and --workload Q the MXFP8 decode (batch 128, 8192 context,
-k = 4, last_loop); --ks 1,2,4 measures several loop counts. --workload G is D with
+k = 4, last_loop) and --workload N the same with NVFP4 weights; --ks 1,2,4 measures
+several loop counts. --workload G is D with
 the vocabulary side in the loop: each step's final states go through the LM head
 (131072 tokens), top-p sampling (T 1.0, p 0.95, seeded draws) and the embedding of the
 sampled tokens, which is the next step's input.
@@ -35,6 +36,7 @@ WORKLOAD_TEXT = {
     "P": "Dory-shape 8/20/8 (36 layers) bf16, batch 1, 4096-token prefill",
     "D": "Full 16/40/16 (72 layers) bf16, decode batch 32 over a seeded 32768-token KV context",
     "Q": "16/40/16 (72 layers) MXFP8 W8A16, decode batch 128 over a seeded 8192-token KV context",
+    "N": "16/40/16 (72 layers) NVFP4 W4A16, decode batch 128 over a seeded 8192-token KV context",
     "L": "16/40/16 (72 layers) bf16, batch 1, chunked prefill (chunks of 8192)",
     "T": "tiny looped nGPT fp32, prefill 64",
     "G": "Full 16/40/16 (72 layers) bf16, generation batch 32 over a seeded 32768-token KV context: "
@@ -51,7 +53,7 @@ def parse():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=5)
     ap.add_argument("--warmup", type=int, default=2)
-    ap.add_argument("--workload", default="P", choices=["P", "D", "Q", "L", "T", "G"])
+    ap.add_argument("--workload", default="P", choices=["P", "D", "Q", "N", "L", "T", "G"])
     ap.add_argument("--k", type=int, default=None)
     ap.add_argument("--ks", default=None, help="comma list of loop counts to measure too")
     ap.add_argument("--mode", default=None, choices=["per_loop", "last_loop"])
