@@ -156,10 +156,21 @@ int dory_bind_kv_pool(dory_ctx* ctx, void* pool, size_t bytes);
  * tables, so it belongs to the context until destroy or rebind (STATE while live). */
 int dory_bind_workspace(dory_ctx* ctx, void* ws, size_t bytes);
 
-/* Loop count k (1..max_loops, else INVALID_ARG). In per_loop mode returns STATE while
- * a live sequence was built with a different k; in last_loop mode allowed any time. */
+/* Loop count k of the context (1..max_loops, else INVALID_ARG), allowed any time. Each
+ * sequence runs its own k (the paper summary's elastic depth: k chosen per request):
+ * a per_loop sequence the k its KV cache was built for (the context's k when it was
+ * created); a last_loop sequence the k set for it with dory_set_seq_loops, else the
+ * context's k at each call. One prefill or decode call may mix sequences of different
+ * k: the recurrent block runs max k times, loop t on the rows of the sequences with
+ * k >= t. */
 int dory_set_loops(dory_ctx* ctx, int k);
 int dory_get_loops(const dory_ctx* ctx, int* k);
+/* Loop count of live sequence seq_id for its next calls: 1..max_loops, or 0 to follow the
+ * context's k. last_loop mode: any value. per_loop mode: only 0 or the k its cache was
+ * built for (STATE otherwise). Unknown id: INVALID_ARG. */
+int dory_set_seq_loops(dory_ctx* ctx, int32_t seq_id, int k);
+/* The loop count seq_id runs with (INVALID_ARG for an unknown id). */
+int dory_seq_loops(const dory_ctx* ctx, int32_t seq_id, int* k);
 /* KV mode (DORY_KV_*). STATE while any sequence is live. */
 int dory_set_kv_mode(dory_ctx* ctx, int mode);
 int dory_get_kv_mode(const dory_ctx* ctx, int* mode);
@@ -190,7 +201,7 @@ int dory_live_seqs(const dory_ctx* ctx, int32_t* n);
 /* KV footprint: bytes of pages currently held by live sequences. */
 int dory_kv_bytes_in_use(const dory_ctx* ctx, size_t* bytes);
 /* Layer calls enqueued by the last prefill/decode call (host counter): E(k) =
- * n_in + n_out + k * n_rec. */
+ * n_in + n_out + k * n_rec, k the largest loop count of the call's sequences. */
 int dory_last_layer_calls(const dory_ctx* ctx, int64_t* n);
 
 /* ---- vocabulary side: token embedding, LM head, top-p sampling

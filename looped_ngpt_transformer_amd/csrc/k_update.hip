@@ -32,7 +32,8 @@ __global__ __launch_bounds__(UPD_THREADS) void k_update(UpdateArgs u) {
   const int m = blockIdx.x;
   const int H = u.H;
   const size_t row = (size_t)m * H;
-  const bool need_x = u.bnd == BND_LOOP_CONTINUE;
+  const int bnd = u.bnd == BND_LOOP_CONTINUE && m >= u.final_from ? BND_LOOP_FINAL : u.bnd;
+  const bool need_x = bnd == BND_LOOP_CONTINUE;
   float yv[UPD_MAXPER], sv[UPD_MAXPER], av[UPD_MAXPER], xv[UPD_MAXPER];
   float acc[NS] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
 #pragma unroll
@@ -96,17 +97,17 @@ __global__ __launch_bounds__(UPD_THREADS) void k_update(UpdateArgs u) {
   float scale = nt;          // s' = t * nt
   float norm_sp = sqrtf(tt) * nt;  // ||s'||
   float add_x = 0.f;         // coefficient of x in the result
-  if (u.bnd == BND_LOOP_CONTINUE || u.bnd == BND_LOOP_FINAL) {  // s_t = N(F(u_t))
+  if (bnd == BND_LOOP_CONTINUE || bnd == BND_LOOP_FINAL) {  // s_t = N(F(u_t))
     const float n2 = inv_norm(norm_sp * norm_sp);
     scale *= n2;
     norm_sp *= n2;
   }
-  if (u.bnd == BND_LOOP_CONTINUE) {  // u = N(s_t + x)
+  if (bnd == BND_LOOP_CONTINUE) {  // u = N(s_t + x)
     const float dot = (tot[4] + tot[5] * ny) * scale;  // s_t . x
     const float n3 = inv_norm(norm_sp * norm_sp + 2.f * dot + tot[6]);
     scale *= n3;
     add_x = n3;
-  } else if (u.bnd == BND_SAVE_X) {  // x = s'; u = N(s' + s')
+  } else if (bnd == BND_SAVE_X) {  // x = s'; u = N(s' + s')
     const float n3 = inv_norm(4.f * norm_sp * norm_sp);
     float* X = u.x;
 #pragma unroll
@@ -140,7 +141,8 @@ __global__ __launch_bounds__(T) void k_update_vec(UpdateArgs u) {
   const size_t row = (size_t)blockIdx.x * H;
   const int i0 = threadIdx.x * 8;
   const bool act = i0 < H;
-  const bool need_x = u.bnd == BND_LOOP_CONTINUE;
+  const int bnd = u.bnd == BND_LOOP_CONTINUE && (int)blockIdx.x >= u.final_from ? BND_LOOP_FINAL : u.bnd;
+  const bool need_x = bnd == BND_LOOP_CONTINUE;
   float yv[8], sv[8], av[8], xv[8];
 #pragma unroll
   for (int e = 0; e < 8; ++e) yv[e] = sv[e] = av[e] = xv[e] = 0.f;
@@ -187,7 +189,7 @@ __global__ __launch_bounds__(T) void k_update_vec(UpdateArgs u) {
   const float tt = fmaxf(tot[1] + 2.f * tot[2] * ny + tot[3] * ny * ny, 0.f);
   const float nt = inv_norm(tt);
   float scale = nt, norm_sp = sqrtf(tt) * nt, add_x = 0.f;
-  if (u.bnd == BND_LOOP_CONTINUE || u.bnd == BND_LOOP_FINAL) {
+  if (bnd == BND_LOOP_CONTINUE || bnd == BND_LOOP_FINAL) {
     const float n2 = inv_norm(norm_sp * norm_sp);
     scale *= n2;
     norm_sp *= n2;
@@ -195,12 +197,12 @@ __global__ __launch_bounds__(T) void k_update_vec(UpdateArgs u) {
   float t[8];
 #pragma unroll
   for (int e = 0; e < 8; ++e) t[e] = (1.f - av[e]) * sv[e] + av[e] * yv[e] * ny;
-  if (u.bnd == BND_LOOP_CONTINUE) {
+  if (bnd == BND_LOOP_CONTINUE) {
     const float dot = (tot[4] + tot[5] * ny) * scale;
     const float n3 = inv_norm(norm_sp * norm_sp + 2.f * dot + tot[6]);
     scale *= n3;
     add_x = n3;
-  } else if (u.bnd == BND_SAVE_X) {
+  } else if (bnd == BND_SAVE_X) {
     const float n3 = inv_norm(4.f * norm_sp * norm_sp);
     if (act) {
       *(float4*)(u.x + row + i0) = make_float4(t[0] * nt, t[1] * nt, t[2] * nt, t[3] * nt);
@@ -226,13 +228,28 @@ __global__ __launch_bounds__(T) void k_update_vec(UpdateArgs u) {
 }
 
 template <typename SB>
-__global__ __launch_bounds__(256) void k_stage_input(const float* x, float* s, SB* sb, size_t n) {
+__global__ __launch_bounds__(256) void k_stage_input(const float* x, float* s, SB* sb, size_t n, const int32_t* rows,
+                                                     int H) {
   for (size_t i = blockIdx.x * (size_t)blockDim.x + threadIdx.x; i < n;
        i += (size_t)gridDim.x * blockDim.x) {
-    const float v = x[i];
+    const size_t src = rows ? (size_t)rows[i / H] * H + i % H : i;
+    const float v = x[src];
     s[i] = v;
     st<SB>(sb, i, v);
   }
+}
+
+__global__ __launch_bounds__(256) void k_scatter_rows(const float* s, const int32_t* rows, int H, size_t n, float* y) {
+  for (size_t i = blockIdx.x * (size_t)blockDim.x + threadIdx.x; i < n; i += (size_t)gridDim.x * blockDim.x)
+    y[(size_t)rows[i / H] * H + i % H] = s[i];
+}
+
+hipError_t launch_scatter_rows(const float* s, const int32_t* rows, int M, int H, float* y, hipStream_t st) {
+  const size_t n = (size_t)M * H;
+  if (n == 0) return hipSuccess;
+  const unsigned blocks = (unsigned)std::min<size_t>((n + 255) / 256, 4096);
+  hipLaunchKernelGGL(k_scatter_rows, dim3(blocks), dim3(256), 0, st, s, rows, H, n, y);
+  return hipGetLastError();
 }
 
 hipError_t launch_update(const UpdateArgs& u, hipStream_t st) {
@@ -262,14 +279,14 @@ hipError_t launch_update(const UpdateArgs& u, hipStream_t st) {
 }
 
 hipError_t launch_stage_input(const float* x_in, float* s, void* sb, int M, int H, int act,
-                              hipStream_t st) {
+                              hipStream_t st, const int32_t* rows) {
   const size_t n = (size_t)M * H;
   if (n == 0) return hipSuccess;
   const int blocks = (int)((n + 255) / 256 < 4096 ? (n + 255) / 256 : 4096);
   if (act == ACT_F32)
-    hipLaunchKernelGGL(k_stage_input<float>, dim3(blocks), dim3(256), 0, st, x_in, s, (float*)sb, n);
+    hipLaunchKernelGGL(k_stage_input<float>, dim3(blocks), dim3(256), 0, st, x_in, s, (float*)sb, n, rows, H);
   else
-    hipLaunchKernelGGL(k_stage_input<bf16_t>, dim3(blocks), dim3(256), 0, st, x_in, s, (bf16_t*)sb, n);
+    hipLaunchKernelGGL(k_stage_input<bf16_t>, dim3(blocks), dim3(256), 0, st, x_in, s, (bf16_t*)sb, n, rows, H);
   return hipGetLastError();
 }
 

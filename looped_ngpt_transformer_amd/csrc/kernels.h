@@ -58,11 +58,15 @@ struct UpdateArgs {
   int M = 0, H = 0;
   int act = ACT_BF16;
   int bnd = BND_NONE;
+  int final_from = 0x7fffffff;  // with BND_LOOP_CONTINUE: rows >= this one end their last
+                                // loop here and take BND_LOOP_FINAL (mixed loop counts)
 };
 hipError_t launch_update(const UpdateArgs& u, hipStream_t st);
-// s = x_in; sb = act(x_in)
+// s = x_in; sb = act(x_in); with rows != NULL row r of s is row rows[r] of x_in
 hipError_t launch_stage_input(const float* x_in, float* s, void* sb, int M, int H, int act,
-                              hipStream_t st);
+                              hipStream_t st, const int32_t* rows = nullptr);
+// y[rows[r]] = s[r] for r < M (float rows of H)
+hipError_t launch_scatter_rows(const float* s, const int32_t* rows, int M, int H, float* y, hipStream_t st);
 
 // ------------------------------------------------------------ RoPE + QK norm + KV write
 struct KVLayout {

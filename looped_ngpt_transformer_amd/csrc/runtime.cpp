@@ -87,7 +87,7 @@ WsLayout layout_of(const dory_config& c, const Dims& D) {
   W.table = take((size_t)c.max_seqs * D.n_streams * D.tab_len * 4);
   // metadata per call: positions, row -> sequence slot, prefill tiles, RoPE frequency
   // tables (2 bases x 128 doubles), page-table updates
-  W.meta_ints = 2 * R + 4 * (size_t)D.max_tiles + ROPE_INTS + 2 * (size_t)DELTA_CAP;
+  W.meta_ints = 3 * R + 4 * (size_t)D.max_tiles + ROPE_INTS + 2 * (size_t)DELTA_CAP;
   W.meta = take(W.meta_ints * 4);
   W.s = take(R * D.H * 4);
   W.x = take(R * D.H * 4);
@@ -117,6 +117,7 @@ struct Seq {
   int64_t len = 0;
   int k_built = 1;
   int rec_slots = 1;
+  int k_set = 0;  // last_loop: loop count set for this sequence (0: the context's)
   std::vector<std::vector<int32_t>> pages;  // per stream: table entries (-1 = none)
 };
 
@@ -373,6 +374,11 @@ struct CallPlan {
   int n_tiles = 0;
   int max_tile_rows = 0;
   std::vector<std::pair<int64_t, int>> chunks;  // (first position, rows) per sequence
+  // Loop counts: sequences are ordered by loop count, largest first, so the rows still
+  // looping in loop t are a prefix: loop_rows[t], loop_tiles[t], loop_seqs[t] (t >= 1).
+  int k_max = 1;
+  std::vector<int> loop_rows, loop_tiles, loop_seqs;
+  bool reordered = false;  // rows are not in the caller's order (row map in the metadata)
 };
 
 // Algorithmic attention work of one layer call: visible (query, key) pairs and the
@@ -407,7 +413,7 @@ KVLayout kv_layout(dory_ctx* ctx, int l) {
 }
 
 int run_layer(dory_ctx* ctx, hipStream_t st, const CallPlan& P, int l, int slot, int bnd,
-              float* out) {
+              float* out, int final_from = 0x7fffffff) {
   const dory_config& c = ctx->cfg;
   const Dims& D = ctx->D;
   const WsLayout& W = ctx->W;
@@ -483,6 +489,7 @@ int run_layer(dory_ctx* ctx, hipStream_t st, const CallPlan& P, int l, int slot,
     u.H = D.H;
     u.act = act;
     u.bnd = b;
+    u.final_from = final_from;
     Prof pr(ctx, st, DORY_KC_UPDATE);
     const hipError_t e = launch_update(u, st);
     pr.end(0, (double)M * D.H * ((ybf ? 2.0 : 4.0 * splits) + 4 + 4 + D.esz));
@@ -629,9 +636,12 @@ int run_forward(dory_ctx* ctx, hipStream_t st, const CallPlan& P, const float* x
   const dory_config& c = ctx->cfg;
   char* ws = ctx->ws;
   const int act = c.act_dtype == DORY_DTYPE_F32 ? ACT_F32 : ACT_BF16;
+  const int R = c.max_rows;
+  const int32_t* rowmap = P.reordered ? (const int32_t*)(ws + ctx->W.meta) + 2 * R + 4 * ctx->D.max_tiles + ROPE_INTS
+                                      : nullptr;
   {
     Prof pr(ctx, st, DORY_KC_UPDATE);
-    HIPCHK(launch_stage_input(x_in, (float*)(ws + ctx->W.s), ws + ctx->W.sb, P.M, ctx->D.H, act, st),
+    HIPCHK(launch_stage_input(x_in, (float*)(ws + ctx->W.s), ws + ctx->W.sb, P.M, ctx->D.H, act, st, rowmap),
            "stage_input");
     pr.end(0, (double)P.M * ctx->D.H * (8.0 + ctx->D.esz));
   }
@@ -641,22 +651,42 @@ int run_forward(dory_ctx* ctx, hipStream_t st, const CallPlan& P, const float* x
     if ((r = run_layer(ctx, st, P, l, 0, l == c.n_in - 1 ? BND_SAVE_X : BND_NONE, nullptr))) return r;
     ++calls;
   }
-  for (int t = 1; t <= ctx->k; ++t) {
+  // loop t runs the recurrent block on the rows of the sequences with k >= t (a prefix);
+  // rows whose sequence ends at loop t take the final boundary there
+  for (int t = 1; t <= P.k_max; ++t) {
+    CallPlan Pt = P;
+    Pt.M = P.loop_rows[t];
+    Pt.n_tiles = P.loop_tiles[t];
+    Pt.chunks.resize(P.loop_seqs[t]);
     const int slot = ctx->mode == DORY_KV_PER_LOOP ? t - 1 : 0;
+    const int next = t < P.k_max ? P.loop_rows[t + 1] : 0;
     for (int l = c.n_in; l < c.n_in + c.n_rec; ++l) {
       int b = BND_NONE;
-      if (l == c.n_in + c.n_rec - 1) b = t < ctx->k ? BND_LOOP_CONTINUE : BND_LOOP_FINAL;
-      if ((r = run_layer(ctx, st, P, l, slot, b, nullptr))) return r;
+      if (l == c.n_in + c.n_rec - 1) b = t < P.k_max ? BND_LOOP_CONTINUE : BND_LOOP_FINAL;
+      if ((r = run_layer(ctx, st, Pt, l, slot, b, nullptr, next))) return r;
       ++calls;
     }
   }
   const int L = c.n_in + c.n_rec + c.n_out;
   for (int l = c.n_in + c.n_rec; l < L; ++l) {
-    if ((r = run_layer(ctx, st, P, l, 0, BND_NONE, l == L - 1 ? y_out : nullptr))) return r;
+    float* out = l == L - 1 && !P.reordered ? y_out : nullptr;
+    if ((r = run_layer(ctx, st, P, l, 0, BND_NONE, out))) return r;
     ++calls;
+  }
+  if (P.reordered) {
+    Prof pr(ctx, st, DORY_KC_UPDATE);
+    HIPCHK(launch_scatter_rows((const float*)(ws + ctx->W.s), rowmap, P.M, ctx->D.H, y_out, st), "output rows");
+    pr.end(0, (double)P.M * ctx->D.H * 8.0);
   }
   ctx->last_calls = calls;
   return DORY_OK;
+}
+
+// Loop count a sequence runs with: per_loop sequences the k their cache was built for;
+// last_loop sequences the count set for them, else the context's.
+int loops_of(const dory_ctx* ctx, const Seq& q) {
+  if (ctx->mode == DORY_KV_PER_LOOP) return q.k_built;
+  return q.k_set ? q.k_set : ctx->k;
 }
 
 // Shared body of prefill and decode: rows of each sequence, grown by n_new[i].
@@ -698,20 +728,13 @@ int step(dory_ctx* ctx, hipStream_t st, int n, const int32_t* ids, const int32_t
   }
   if (need > (int64_t)ctx->free_pages.size())
     return ctx->fail(DORY_ERR_OUT_OF_KV, "need %lld KV pages, %zu free", (long long)need, ctx->free_pages.size());
-  // per_loop sequences were built for one k
-  if (ctx->mode == DORY_KV_PER_LOOP)
-    for (int i = 0; i < n; ++i) {
-      auto it = ctx->seqs.find(ids[i]);
-      if (it != ctx->seqs.end() && it->second.k_built != ctx->k)
-        return ctx->fail(DORY_ERR_STATE, "sequence %d holds KV for k=%d", ids[i], it->second.k_built);
-    }
   int r = dev_init(ctx);
   if (r) return r;
 
   // commit: create, grow, build row metadata
   std::vector<int32_t>& meta = ctx->scratch;
   const int R = c.max_rows;
-  meta.assign(2 * (size_t)R + 4 * (size_t)ctx->D.max_tiles + ROPE_INTS, 0);
+  meta.assign(3 * (size_t)R + 4 * (size_t)ctx->D.max_tiles + ROPE_INTS, 0);
   {  // RoPE frequencies theta^(-2i/d), sliding base then full base
     double* fr = (double*)(meta.data() + 2 * (size_t)R + 4 * (size_t)ctx->D.max_tiles);
     const int d = ctx->D.d;
@@ -720,9 +743,30 @@ int step(dory_ctx* ctx, hipStream_t st, int n, const int32_t* ids, const int32_t
       fr[128 + i] = std::pow(c.theta_full, -2.0 * i / d);
     }
   }
+  // loop count of each sequence of the call; the plan orders sequences by it, largest
+  // first (stable), so that the rows still looping in loop t form a prefix
+  std::vector<int> kseq(n), order(n);
+  std::vector<int64_t> caller_row(n);
+  {
+    int64_t cr = 0;
+    for (int i = 0; i < n; ++i) {
+      auto it = ctx->seqs.find(ids[i]);
+      kseq[i] = it == ctx->seqs.end() ? ctx->k : loops_of(ctx, it->second);
+      caller_row[i] = cr;
+      cr += decode ? 1 : n_new[i];
+      order[i] = i;
+    }
+    std::stable_sort(order.begin(), order.end(), [&](int a, int b) { return kseq[a] > kseq[b]; });
+  }
   CallPlan P;
+  P.k_max = kseq[order[0]];
+  P.loop_rows.assign(P.k_max + 2, 0);
+  P.loop_tiles.assign(P.k_max + 2, 0);
+  P.loop_seqs.assign(P.k_max + 2, 0);
+  for (int i = 0; i < n; ++i) P.reordered |= order[i] != i;
   int row = 0;
-  for (int i = 0; i < n; ++i) {
+  for (int oi = 0; oi < n; ++oi) {
+    const int i = order[oi];
     auto it = ctx->seqs.find(ids[i]);
     if (it == ctx->seqs.end()) {
       Seq q;
@@ -741,6 +785,7 @@ int step(dory_ctx* ctx, hipStream_t st, int n, const int32_t* ids, const int32_t
     for (int j = 0; j < nn; ++j) {
       meta[row + j] = (int32_t)(p0 + j);
       meta[R + row + j] = q.slot;
+      meta[2 * R + 4 * ctx->D.max_tiles + ROPE_INTS + row + j] = (int32_t)(caller_row[i] + j);
     }
     for (int j = 0; j < nn; j += 64) {  // prefill tiles of <= 64 rows
       int32_t* tl = &meta[2 * R + 4 * P.n_tiles];
@@ -754,6 +799,11 @@ int step(dory_ctx* ctx, hipStream_t st, int n, const int32_t* ids, const int32_t
     P.chunks.emplace_back(p0, nn);
     P.max_pos = std::max<int>(P.max_pos, (int)(p0 + nn - 1));
     row += nn;
+    for (int t = 1; t <= kseq[i]; ++t) {  // prefixes: this sequence loops in loops 1..k
+      P.loop_rows[t] = row;
+      P.loop_tiles[t] = P.n_tiles;
+      P.loop_seqs[t] = oi + 1;
+    }
   }
   P.M = row;
   // deltas: whatever does not fit goes first in separate uploads
@@ -764,7 +814,7 @@ int step(dory_ctx* ctx, hipStream_t st, int n, const int32_t* ids, const int32_t
   if ((r = upload(ctx, st, meta.data(), meta.size()))) return r;
   if (nd)
     HIPCHK(launch_apply_deltas((int32_t*)(ctx->ws + ctx->W.table),
-                               (const int32_t*)(ctx->ws + ctx->W.meta) + 2 * R + 4 * ctx->D.max_tiles + ROPE_INTS,
+                               (const int32_t*)(ctx->ws + ctx->W.meta) + 3 * R + 4 * ctx->D.max_tiles + ROPE_INTS,
                                (int)nd, ctx->pool, ctx->D.page_bytes, st), "apply_deltas");
   return run_forward(ctx, st, P, x_in, y_out);
 }
@@ -905,11 +955,29 @@ int dory_bind_workspace(dory_ctx* ctx, void* ws, size_t bytes) {
 int dory_set_loops(dory_ctx* ctx, int k) {
   if (!ctx) return DORY_ERR_INVALID_ARG;
   if (k < 1 || k > ctx->cfg.max_loops) return ctx->fail(DORY_ERR_INVALID_ARG, "k=%d outside 1..%d", k, ctx->cfg.max_loops);
-  if (ctx->mode == DORY_KV_PER_LOOP)
-    for (auto& kv : ctx->seqs)
-      if (kv.second.k_built != k)
-        return ctx->fail(DORY_ERR_STATE, "per_loop sequence %d holds KV for k=%d", kv.first, kv.second.k_built);
   ctx->k = k;
+  return DORY_OK;
+}
+
+int dory_set_seq_loops(dory_ctx* ctx, int32_t seq_id, int k) {
+  if (!ctx) return DORY_ERR_INVALID_ARG;
+  auto it = ctx->seqs.find(seq_id);
+  if (it == ctx->seqs.end()) return ctx->fail(DORY_ERR_INVALID_ARG, "unknown sequence %d", seq_id);
+  if (k < 0 || k > ctx->cfg.max_loops) return ctx->fail(DORY_ERR_INVALID_ARG, "k=%d outside 0..%d", k, ctx->cfg.max_loops);
+  if (ctx->mode == DORY_KV_PER_LOOP) {
+    if (k != 0 && k != it->second.k_built)
+      return ctx->fail(DORY_ERR_STATE, "per_loop sequence %d holds KV for k=%d", seq_id, it->second.k_built);
+    return DORY_OK;
+  }
+  it->second.k_set = k;
+  return DORY_OK;
+}
+
+int dory_seq_loops(const dory_ctx* ctx, int32_t seq_id, int* k) {
+  if (!ctx || !k) return DORY_ERR_INVALID_ARG;
+  auto it = ctx->seqs.find(seq_id);
+  if (it == ctx->seqs.end()) return DORY_ERR_INVALID_ARG;
+  *k = loops_of(ctx, it->second);
   return DORY_OK;
 }
 
@@ -990,8 +1058,7 @@ int dory_test_reserve(dory_ctx* ctx, int32_t seq_id, int32_t n_tokens) {
   Seq probe;
   if (it != ctx->seqs.end()) probe = it->second;
   else probe.rec_slots = ctx->mode == DORY_KV_PER_LOOP ? ctx->k : 1;
-  if (it != ctx->seqs.end() && ctx->mode == DORY_KV_PER_LOOP && probe.k_built != ctx->k)
-    return ctx->fail(DORY_ERR_STATE, "sequence %d holds KV for k=%d", seq_id, probe.k_built);
+
   if (probe.len + n_tokens > ctx->cfg.max_seq_len)
     return ctx->fail(DORY_ERR_INVALID_ARG, "sequence would exceed max_seq_len");
   const int64_t need = pages_to_grow(ctx, probe, probe.len + n_tokens);

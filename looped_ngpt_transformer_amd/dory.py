@@ -77,6 +77,8 @@ _SIGS = {
     "dory_bind_workspace": (C.c_int, [_P, _P, C.c_size_t]),
     "dory_set_loops": (C.c_int, [_P, C.c_int]),
     "dory_get_loops": (C.c_int, [_P, C.POINTER(C.c_int)]),
+    "dory_set_seq_loops": (C.c_int, [_P, C.c_int32, C.c_int]),
+    "dory_seq_loops": (C.c_int, [_P, C.c_int32, C.POINTER(C.c_int)]),
     "dory_set_kv_mode": (C.c_int, [_P, C.c_int]),
     "dory_get_kv_mode": (C.c_int, [_P, C.POINTER(C.c_int)]),
     "dory_prefill": (C.c_int, [_P, _P, C.c_int, _I32P, _I32P, _P, _P]),
@@ -204,6 +206,16 @@ def dory_set_loops(ctx, k: int):
 def dory_get_loops(ctx) -> int:
     k = C.c_int()
     _check(lib().dory_get_loops(ctx, C.byref(k)), ctx)
+    return k.value
+
+
+def dory_set_seq_loops(ctx, seq_id: int, k: int):
+    _check(lib().dory_set_seq_loops(ctx, seq_id, k), ctx)
+
+
+def dory_seq_loops(ctx, seq_id: int) -> int:
+    k = C.c_int(0)
+    _check(lib().dory_seq_loops(ctx, seq_id, C.byref(k)), ctx)
     return k.value
 
 

@@ -157,15 +157,32 @@ def test_mode_and_loop_changes_with_live_sequences():
     with pytest.raises(D.DoryError) as e:
         D.dory_set_kv_mode(ctx, D.KV_LAST_LOOP)
     assert e.value.code == D.ERR_STATE
+    # per_loop: the context's k applies to sequences created later; a live sequence keeps
+    # the k its cache was built for (mixed loop counts in one call)
+    D.dory_set_loops(ctx, 3)
+    D.dory_test_reserve(ctx, 4, 50)
+    assert D.dory_seq_loops(ctx, 3) == 2 and D.dory_seq_loops(ctx, 4) == 3
     with pytest.raises(D.DoryError) as e:               # per_loop KV was built for k=2
-        D.dory_set_loops(ctx, 3)
+        D.dory_set_seq_loops(ctx, 3, 4)
     assert e.value.code == D.ERR_STATE
-    D.dory_set_loops(ctx, 2)
+    D.dory_set_seq_loops(ctx, 3, 2)                     # its own k: allowed
+    with pytest.raises(D.DoryError) as e:
+        D.dory_set_seq_loops(ctx, 99, 2)                # unknown sequence
+    assert e.value.code == D.ERR_INVALID_ARG
     D.dory_release_seq(ctx, 3)
+    D.dory_release_seq(ctx, 4)
     D.dory_set_kv_mode(ctx, D.KV_LAST_LOOP)
     D.dory_test_reserve(ctx, 3, 100)
     D.dory_set_loops(ctx, 4)                            # last_loop: allowed while live
-    D.dory_set_loops(ctx, 1)
+    assert D.dory_seq_loops(ctx, 3) == 4                # follows the context's k ...
+    D.dory_set_seq_loops(ctx, 3, 1)                     # ... until set for the sequence
+    D.dory_set_loops(ctx, 2)
+    assert D.dory_seq_loops(ctx, 3) == 1
+    D.dory_set_seq_loops(ctx, 3, 0)                     # 0: back to the context's
+    assert D.dory_seq_loops(ctx, 3) == 2
+    with pytest.raises(D.DoryError) as e:
+        D.dory_set_seq_loops(ctx, 3, 5)                 # max_loops is 4
+    assert e.value.code == D.ERR_INVALID_ARG
     D.dory_destroy(ctx)
 
 

@@ -263,3 +263,52 @@ def test_bf16_prefill_over_long_seeded_context(mode):
     ref = O.prefill(cfg, W, stores[0], to_np(X), k, mode)
     compare(y.cpu().double().numpy(), ref, S, "chunk over 4300 tokens")
     rt.close()
+
+
+@pytest.mark.parametrize("mode", ["per_loop", "last_loop"])
+def test_mixed_loop_counts_in_one_call(mode):
+    """Sequences running k = 1, 4 and 2 (caller order, so the rows are reordered by k
+    inside the call) in one prefill chunk and two decode steps: loop t runs on the rows
+    of the sequences with k >= t, and each sequence equals the oracle at its own k."""
+    from oracle import dory_oracle as O
+    from tests.helpers import to_np
+    S = PSMALL
+    ks = {0: 1, 1: 4, 2: 2}
+    w = sharpen(gpu_weights(S, 17))
+    rt = DoryRuntime(S, w, max_loops=4, max_seqs=3, max_seq_len=128, max_rows=128, mode=mode, loops=2)
+    cfg, W = oracle_model(S, w)
+    seqs = {i: O.Sequence(cfg) for i in ks}
+    first = {0: 24, 1: 30, 2: 20}
+    for i in ks:  # a new sequence runs the context's k (per_loop: for good)
+        D.dory_set_loops(rt.ctx, ks[i])
+        X = xin(S, first[i], 50 + i)
+        y = rt.prefill([i], [first[i]], X)
+        torch.cuda.synchronize()
+        compare(y.cpu().double().numpy(), O.prefill(cfg, W, seqs[i], to_np(X), ks[i], mode), S, f"seq {i} prompt")
+    D.dory_set_loops(rt.ctx, 2)
+    if mode == "last_loop":
+        D.dory_set_seq_loops(rt.ctx, 0, 1)
+        D.dory_set_seq_loops(rt.ctx, 1, 4)       # sequence 2 follows the context's k = 2
+    assert [D.dory_seq_loops(rt.ctx, i) for i in ks] == [1, 4, 2]
+    order = [0, 1, 2]
+    chunk = {0: 10, 1: 5, 2: 7}
+    Xs = {i: xin(S, chunk[i], 60 + i) for i in order}
+    y = rt.prefill(order, [chunk[i] for i in order], torch.cat([Xs[i] for i in order]))
+    torch.cuda.synchronize()
+    assert D.dory_last_layer_calls(rt.ctx) == S["n_in"] + S["n_out"] + 4 * S["n_rec"]
+    got = y.cpu().double().numpy()
+    r0 = 0
+    for i in order:
+        ref = O.prefill(cfg, W, seqs[i], to_np(Xs[i]), ks[i], mode)
+        compare(got[r0:r0 + chunk[i]], ref, S, f"mixed chunk, seq {i} (k={ks[i]})")
+        r0 += chunk[i]
+    for step in range(2):
+        dorder = [2, 0, 1] if step else [0, 2, 1]
+        X = xin(S, 3, 70 + step)
+        y = rt.decode(dorder, X)
+        torch.cuda.synchronize()
+        got = y.cpu().double().numpy()
+        for j, i in enumerate(dorder):
+            ref = O.prefill(cfg, W, seqs[i], to_np(X[j:j + 1]), ks[i], mode)
+            compare(got[j:j + 1], ref, S, f"decode {step}, seq {i} (k={ks[i]})")
+    rt.close()
