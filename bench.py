@@ -57,6 +57,9 @@ def parse():
     ap.add_argument("--k", type=int, default=None)
     ap.add_argument("--ks", default=None, help="comma list of loop counts to measure too")
     ap.add_argument("--mode", default=None, choices=["per_loop", "last_loop"])
+    ap.add_argument("--mix-k", default=None,
+                    help="decode: comma list of loop counts given to the batch's sequences in turn "
+                         "(one call mixes them)")
     ap.add_argument("--tokens", type=int, default=None, help="prefill length (P, L)")
     ap.add_argument("--context", type=int, default=None, help="seeded KV context (D, Q)")
     ap.add_argument("--batch", type=int, default=None, help="decode batch (D, Q)")
@@ -241,6 +244,10 @@ def bench_decode(args, torch, synth, D, DoryRuntime):
     k = args.k or (2 if dl else 4)
     mode = args.mode or ("per_loop" if dl else "last_loop")
     ks = sorted({k} | ({int(x) for x in args.ks.split(",")} if args.ks else set()))
+    mix = [int(x) for x in args.mix_k.split(",")] if args.mix_k else None
+    if mix:
+        k = max(mix)
+        ks = [k]
     log(f"[bench] workload {wl}: weights")
     weights = synth.make_weights(shape, 1234, "cuda")
     cfg_loops = max(ks)
@@ -256,7 +263,9 @@ def bench_decode(args, torch, synth, D, DoryRuntime):
                          kv_pages=pages, mode=mode, loops=kk)
         log(f"[bench] k={kk} {mode}: KV pool {pages * rt.page_bytes / 1e9:.1f} GB; seeding {ctx_len} tokens x {batch}")
         t0 = time.perf_counter()
-        seed_kv(rt, shape, synth, D, torch, batch, ctx_len, kk, mode)
+        kseq = [mix[b % len(mix)] for b in range(batch)] if mix else [kk] * batch
+        seed_kv(rt, shape, synth, D, torch, batch, ctx_len, kseq, mode)
+        D.dory_set_loops(rt.ctx, kk)
         torch.cuda.synchronize()
         log(f"[bench] seeded in {time.perf_counter() - t0:.1f} s")
         X = synth.make_inputs(batch * (steps + args.warmup), shape["hidden"], 77, device="cuda")
@@ -306,12 +315,14 @@ def bench_decode(args, torch, synth, D, DoryRuntime):
     dt, stats, kvb, brk = results[k]
     tot_bytes = sum(s["bytes"] for s in brk.values())
     out = {
-        "metric": ("generation" if gen else "decode") + " tokens/s (k=%d)" % k, "value": round(batch / dt, 2),
+        "metric": ("generation" if gen else "decode") + " tokens/s (k=%s)" % (args.mix_k if mix else k),
+        "value": round(batch / dt, 2),
         "unit": "tokens/s",
         "n_gpus": 1, "steps": steps, "warmup": args.warmup, "ms_per_step": round(dt * 1e3, 3),
         "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "bf16",
         "data": "synthetic (seeded random weights, seeded KV context, unit-norm inputs)",
-        "config": {"workload": WORKLOAD_TEXT[wl], "batch": batch, "context": ctx_len, "loops": k,
+        "config": {"workload": WORKLOAD_TEXT[wl], "batch": batch, "context": ctx_len,
+                   "loops": ("mixed " + args.mix_k) if mix else k,
                    "kv_mode": mode, "weights": shape["weight_format"],
                    "executed_layers": shape["n_in"] + shape["n_out"] + k * shape["n_rec"]},
         "roofline": roofline_of(stats, "hbm", wl),
@@ -327,13 +338,18 @@ def bench_decode(args, torch, synth, D, DoryRuntime):
     return out
 
 
-def seed_kv(rt, shape, synth, D, torch, batch, ctx_len, k, mode):
+def seed_kv(rt, shape, synth, D, torch, batch, ctx_len, kseq, mode):
     """Reserve ctx_len positions per sequence and write seeded K/V into every cache slot
-    the sequence holds (sliding layers: the last window of positions)."""
+    the sequence holds (sliding layers: the last window of positions). Sequence b runs
+    kseq[b] loops."""
     L = shape["n_in"] + shape["n_rec"] + shape["n_out"]
     W = shape["window"]
     for b in range(batch):
+        k = kseq[b]
+        D.dory_set_loops(rt.ctx, k)  # the loop count a new sequence takes
         D.dory_test_reserve(rt.ctx, b, ctx_len)
+        if mode == "last_loop":
+            D.dory_set_seq_loops(rt.ctx, b, k)
         for l in range(L):
             full = l % shape["full_period"] == shape["full_period"] - 1
             rec = shape["n_in"] <= l < shape["n_in"] + shape["n_rec"]
