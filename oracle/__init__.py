@@ -7,3 +7,4 @@ from .dory_oracle import *  # noqa: F401,F403
 from . import mxfp8  # noqa: F401
 from . import vocab  # noqa: F401
 from . import nvfp4  # noqa: F401
+from . import speculative  # noqa: F401
