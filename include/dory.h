@@ -165,9 +165,13 @@ int dory_bind_workspace(dory_ctx* ctx, void* ws, size_t bytes);
  * k >= t. */
 int dory_set_loops(dory_ctx* ctx, int k);
 int dory_get_loops(const dory_ctx* ctx, int* k);
-/* Loop count of live sequence seq_id for its next calls: 1..max_loops, or 0 to follow the
- * context's k. last_loop mode: any value. per_loop mode: only 0 or the k its cache was
- * built for (STATE otherwise). Unknown id: INVALID_ARG. */
+/* Loop count of live sequence seq_id for its next calls: 1..max_loops, or 0 for its
+ * mode's default (per_loop: the k its cache was built for; last_loop: the context's k).
+ * per_loop mode: at most the k its cache was built for (STATE otherwise); running fewer
+ * loops leaves the cache slots of the skipped loops unwritten for the new positions, so
+ * those positions must be truncated away and recomputed at the full k before a call at
+ * the full k reads them (self-speculative drafting, arXiv summary §6.2). Unknown id:
+ * INVALID_ARG. */
 int dory_set_seq_loops(dory_ctx* ctx, int32_t seq_id, int k);
 /* The loop count seq_id runs with (INVALID_ARG for an unknown id). */
 int dory_seq_loops(const dory_ctx* ctx, int32_t seq_id, int* k);
@@ -196,6 +200,10 @@ int dory_decode_step(dory_ctx* ctx, void* stream, int n_seqs, const int32_t* seq
                      const float* x_in, float* y_out);
 
 int dory_release_seq(dory_ctx* ctx, int32_t seq_id); /* frees its pages */
+/* Shorten live sequence seq_id to its first len positions (1 <= len <= its length): the
+ * next call continues at position len, rewriting the cache entries of the positions it
+ * covers (rejected speculative drafts). Host bookkeeping only; pages stay allocated. */
+int dory_truncate_seq(dory_ctx* ctx, int32_t seq_id, int64_t len);
 int dory_seq_len(const dory_ctx* ctx, int32_t seq_id, int64_t* len);
 int dory_live_seqs(const dory_ctx* ctx, int32_t* n);
 /* KV footprint: bytes of pages currently held by live sequences. */
@@ -289,6 +297,29 @@ int dory_test_gemm(void* stream, const void* A, int lda, const void* B, const ui
  * round-to-nearest-even with saturation at 448, all-zero group -> byte 0. */
 int dory_quantize_mxfp8(void* stream, const void* w, int w_dtype, int64_t rows,
                         int64_t cols, uint8_t* codes, uint8_t* scales);
+
+/* Self-speculative decoding's acceptance step (paper summary and arXiv summary §6.2: draft
+ * gamma tokens with one loop, verify with k loops, rejection sampling keeps the k-loop
+ * distribution). n sequences, V = vocab:
+ *   draft_logits  [gamma, n, V] position-major, row (j, b) at (j n + b) ld_d: the rows
+ *                 draft token j of sequence b was drawn from (one draft step's logits);
+ *   target_logits [n, gamma + 1, V] sequence-major, row (b, j) at (b (gamma+1) + j) ld_t:
+ *                 the verifying model at the same positions and one more (one chunk);
+ *   draft_tokens, u_accept [gamma, n] position-major; u_sample [n];
+ *   tokens [n, gamma + 1] out; n_out [n] out.
+ * Both rows of a position are processed as top-p sampling processes them (temperature,
+ * nucleus renormalised: p and q). Draft j is accepted when u_accept < p(x_j) / q(x_j)
+ * (never for an id outside [0, V) or outside q's nucleus); at the first rejection one
+ * token is drawn from max(0, p - q) renormalised, by inverse CDF over increasing ids with
+ * u_sample (from p if that is empty), and the step ends; if all are accepted, one more
+ * token is drawn from the last verifying row by dory_sample_top_p's rule with u_sample.
+ * tokens[b, 0 .. n_out[b] - 1] receive the accepted drafts and the drawn token, n_out[b]
+ * in 1..gamma+1; entries past n_out[b] are unspecified. Float32 sums in a fixed order:
+ * deterministic. 1 <= gamma <= 16; other limits as for dory_sample_top_p. INVALID_ARG
+ * before device work (dory_last_error(NULL)), HIP. */
+int dory_spec_accept(void* stream, int n, int gamma, int64_t vocab, const float* draft_logits, int64_t ld_d,
+                     const float* target_logits, int64_t ld_t, const int32_t* draft_tokens, float temperature,
+                     float top_p, const float* u_accept, const float* u_sample, int32_t* tokens, int32_t* n_out);
 
 /* NVFP4 quantiser (W4A16; arXiv summary §5.1-5.2: dynamic MSE scale selection; paper
  * summary: E2M1 elements with E4M3 scale factors): w [rows, cols] device (w_dtype F32 or

@@ -247,6 +247,150 @@ __global__ __launch_bounds__(ST) void k_sample_top_p(const float* logits, int64_
   }
 }
 
+// ------------------------------------------------------ speculative acceptance
+// A processed row: temperature, then the top-p nucleus renormalised. `init` finds the max,
+// the total weight, the nucleus cut (the sampler's first selection) and the nucleus mass;
+// prob(v) is the renormalised probability of token v (0 outside the nucleus).
+struct Processed {
+  RowView R;
+  int cut;
+  float ecut, mass;
+  __device__ void init(SampleLds& S, const float* L, int V, float inv_t, float top_p) {
+    const int t = threadIdx.x;
+    R.L = L;
+    R.V = V;
+    R.c = inv_t * 1.4426950408889634f;
+    float m = -INFINITY;
+    for (int i = t; i < V; i += ST) m = fmaxf(m, L[i]);
+    R.mz = block_max16(m, S.red) * R.c;
+    float s = 0.f;
+    for (int i = t; i < V; i += ST) s += R.e(i);
+    const float total = block_sum<ST / WAVE>(s, S.red);
+    cut = select_token(S, R, top_p * total, true, &mass);
+    ecut = R.e(cut);
+  }
+  __device__ float prob(int v) const {
+    const float e = R.e(v);
+    const bool in = e > ecut || (e == ecut && v <= cut);
+    return in ? e / mass : 0.f;
+  }
+};
+
+// Prefix sums of one float per thread in thread order (fixed order): returns the inclusive
+// sum, *excl the exclusive one (the same additions minus this thread's).
+__device__ __forceinline__ float block_scan_f(float v, float* red, float* excl) {
+  const int lane = threadIdx.x & (WAVE - 1), w = threadIdx.x / WAVE;
+  float x = v;
+#pragma unroll
+  for (int d = 1; d < WAVE; d <<= 1) {
+    const float y = __shfl_up(x, d, WAVE);
+    if (lane >= d) x += y;
+  }
+  const float xe = __shfl_up(x, 1, WAVE);
+  __syncthreads();
+  if (lane == WAVE - 1) red[w] = x;
+  __syncthreads();
+  float off = 0.f;
+  for (int i = 0; i < w; ++i) off += red[i];
+  *excl = lane ? off + xe : off;
+  return off + x;
+}
+
+// The token u draws from max(0, p - q) renormalised, by inverse CDF over increasing ids
+// (from p itself if the residual is empty). Thread t owns the ids [t C, t C + C).
+__device__ int residual_draw(SampleLds& S, const Processed& P, const Processed& Q, int V, float u) {
+  const int t = threadIdx.x, C = (V + ST - 1) / ST, beg = min(t * C, V), end = min(beg + C, V);
+  float mine = 0.f, acc;
+  for (int v = beg; v < end; ++v) mine += fmaxf(P.prob(v) - Q.prob(v), 0.f);
+  float incl = block_scan_f(mine, S.red, &acc);
+  __syncthreads();
+  if (t == ST - 1) S.above = incl;
+  __syncthreads();
+  const bool from_p = !(S.above > 0.f);
+  __syncthreads();
+  if (from_p) {  // empty residual
+    mine = 0.f;
+    for (int v = beg; v < end; ++v) mine += P.prob(v);
+    incl = block_scan_f(mine, S.red, &acc);
+    __syncthreads();
+    if (t == ST - 1) S.above = incl;
+    __syncthreads();
+  }
+  const float target = u * S.above;
+  int cand = INT_MAX, last = -1;
+  for (int v = beg; v < end; ++v) {
+    const float w = from_p ? P.prob(v) : fmaxf(P.prob(v) - Q.prob(v), 0.f);
+    if (w > 0.f) last = v;
+    acc += w;
+    if (cand == INT_MAX && acc > target && w > 0.f) cand = v;
+  }
+  int tok = block_min_int(cand, S.ired);
+  if (tok == INT_MAX) tok = -block_min_int(-last, S.ired);
+  return tok;
+}
+
+// One work-group per (sequence b, position j); draft rows, tokens and acceptance draws
+// are position-major ([gamma, n]), the verifying rows sequence-major ([n, gamma + 1]).
+// For j < gamma the draft token x_j is
+// accepted when u_accept < p_j(x_j) / q_j(x_j), else the group draws the residual token
+// with u_sample and lowers n_out[b] to j + 1 (an atomic minimum: the first rejection
+// wins); group j = gamma draws the token that follows if all are accepted. Every group
+// writes out[b, j]; n_out[b] starts at gamma + 1 (k_fill_n). The groups of later
+// positions do their work whether or not an earlier one rejects.
+__global__ void k_fill_n(int32_t* n_out, int n, int v) {
+  const int i = blockIdx.x * blockDim.x + threadIdx.x;
+  if (i < n) n_out[i] = v;
+}
+
+__global__ __launch_bounds__(ST) void k_spec_accept(int gamma, int V, const float* draft, int64_t ld_d,
+                                                    const float* target, int64_t ld_t, const int32_t* dtok,
+                                                    float inv_t, float top_p, const float* u_acc,
+                                                    const float* u_smp, int32_t* out, int32_t* n_out) {
+  __shared__ SampleLds S;
+  const int b = blockIdx.x, j = blockIdx.y, t = threadIdx.x;
+  const float* T = target + ((size_t)b * (gamma + 1) + j) * ld_t;
+  const float us = u_smp[b];
+  int32_t* o = out + (size_t)b * (gamma + 1) + j;
+  Processed P;
+  P.init(S, T, V, inv_t, top_p);
+  if (j == gamma) {  // all accepted: the verifying model's next token
+    float cum;
+    int tok = select_token(S, P.R, us * P.mass, false, &cum);
+    if (t == 0) {
+      const float et = P.R.e(tok);
+      if (et < P.ecut || (et == P.ecut && tok > P.cut)) tok = P.cut;
+      *o = tok;
+    }
+    return;
+  }
+  Processed Q;
+  const size_t dj = (size_t)j * gridDim.x + b;  // draft side: position-major
+  Q.init(S, draft + dj * ld_d, V, inv_t, top_p);
+  const int x = dtok[dj];
+  const bool valid = x >= 0 && x < V;
+  const float q = valid ? Q.prob(x) : 0.f;
+  const float ratio = q > 0.f ? P.prob(x) / q : 0.f;
+  if (u_acc[dj] < ratio) {
+    if (t == 0) *o = x;
+    return;
+  }
+  const int r = residual_draw(S, P, Q, V, us);
+  if (t == 0) {
+    *o = r;
+    atomicMin(n_out + b, j + 1);
+  }
+}
+
+hipError_t launch_spec_accept(int n, int gamma, int64_t V, const float* draft, int64_t ld_d, const float* target,
+                              int64_t ld_t, const int32_t* dtok, float temperature, float top_p, const float* u_acc,
+                              const float* u_smp, int32_t* out, int32_t* n_out, hipStream_t st) {
+  if (n <= 0) return hipSuccess;
+  hipLaunchKernelGGL(k_fill_n, dim3((n + 255) / 256), dim3(256), 0, st, n_out, n, gamma + 1);
+  hipLaunchKernelGGL(k_spec_accept, dim3(n, gamma + 1), dim3(ST), 0, st, gamma, (int)V, draft, ld_d, target, ld_t,
+                     dtok, 1.0f / temperature, top_p, u_acc, u_smp, out, n_out);
+  return hipGetLastError();
+}
+
 hipError_t launch_embed(const void* E, int e_bf16, int64_t V, int H, const int32_t* ids, int n, float* x,
                         hipStream_t st) {
   if (n <= 0) return hipSuccess;

@@ -161,6 +161,12 @@ hipError_t launch_logit_scale(const float* part, int splits, size_t sstride, flo
 hipError_t launch_sample_top_p(const float* logits, int64_t ld, int n, int64_t V, float temperature, float top_p,
                                const float* u, int32_t* out, hipStream_t st);
 
+// speculative acceptance (k_vocab.hip): per sequence, gamma draft tokens against the
+// verifying model's gamma + 1 rows; out [n, gamma + 1] tokens, n_out [n] emitted counts
+hipError_t launch_spec_accept(int n, int gamma, int64_t V, const float* draft, int64_t ld_d, const float* target,
+                              int64_t ld_t, const int32_t* dtok, float temperature, float top_p, const float* u_acc,
+                              const float* u_smp, int32_t* out, int32_t* n_out, hipStream_t st);
+
 // ------------------------------------------------------- NVFP4 weights (k_nvfp4.hip)
 // codes [rows, cols/2] (two E2M1 codes a byte, element 2j in the low nibble), E4M3 block
 // scales [rows, cols/16], the power-of-two matrix scale g (one float).

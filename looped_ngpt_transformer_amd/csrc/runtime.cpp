@@ -117,7 +117,7 @@ struct Seq {
   int64_t len = 0;
   int k_built = 1;
   int rec_slots = 1;
-  int k_set = 0;  // last_loop: loop count set for this sequence (0: the context's)
+  int k_set = 0;  // loop count set for this sequence (0: the default of its mode)
   std::vector<std::vector<int32_t>> pages;  // per stream: table entries (-1 = none)
 };
 
@@ -682,10 +682,10 @@ int run_forward(dory_ctx* ctx, hipStream_t st, const CallPlan& P, const float* x
   return DORY_OK;
 }
 
-// Loop count a sequence runs with: per_loop sequences the k their cache was built for;
-// last_loop sequences the count set for them, else the context's.
+// Loop count a sequence runs with: the count set for it, else per_loop sequences the k
+// their cache was built for and last_loop sequences the context's.
 int loops_of(const dory_ctx* ctx, const Seq& q) {
-  if (ctx->mode == DORY_KV_PER_LOOP) return q.k_built;
+  if (ctx->mode == DORY_KV_PER_LOOP) return q.k_set ? q.k_set : q.k_built;
   return q.k_set ? q.k_set : ctx->k;
 }
 
@@ -964,12 +964,37 @@ int dory_set_seq_loops(dory_ctx* ctx, int32_t seq_id, int k) {
   auto it = ctx->seqs.find(seq_id);
   if (it == ctx->seqs.end()) return ctx->fail(DORY_ERR_INVALID_ARG, "unknown sequence %d", seq_id);
   if (k < 0 || k > ctx->cfg.max_loops) return ctx->fail(DORY_ERR_INVALID_ARG, "k=%d outside 0..%d", k, ctx->cfg.max_loops);
-  if (ctx->mode == DORY_KV_PER_LOOP) {
-    if (k != 0 && k != it->second.k_built)
-      return ctx->fail(DORY_ERR_STATE, "per_loop sequence %d holds KV for k=%d", seq_id, it->second.k_built);
-    return DORY_OK;
-  }
+  if (ctx->mode == DORY_KV_PER_LOOP && k > it->second.k_built)
+    return ctx->fail(DORY_ERR_STATE, "per_loop sequence %d holds KV for k=%d", seq_id, it->second.k_built);
   it->second.k_set = k;
+  return DORY_OK;
+}
+
+int dory_truncate_seq(dory_ctx* ctx, int32_t seq_id, int64_t len) {
+  if (!ctx) return DORY_ERR_INVALID_ARG;
+  auto it = ctx->seqs.find(seq_id);
+  if (it == ctx->seqs.end()) return ctx->fail(DORY_ERR_INVALID_ARG, "unknown sequence %d", seq_id);
+  if (len < 1 || len > it->second.len)
+    return ctx->fail(DORY_ERR_INVALID_ARG, "length %lld outside 1..%lld", (long long)len, (long long)it->second.len);
+  it->second.len = len;  // the pages stay with the sequence; later positions are rewritten before use
+  return DORY_OK;
+}
+
+int dory_spec_accept(void* stream, int n, int gamma, int64_t vocab, const float* draft_logits, int64_t ld_d,
+                     const float* target_logits, int64_t ld_t, const int32_t* draft_tokens, float temperature,
+                     float top_p, const float* u_accept, const float* u_sample, int32_t* tokens, int32_t* n_out) {
+  if (n < 1 || gamma < 1 || gamma > 16 || vocab < 1 || vocab > (1 << 24) || ld_d < vocab || ld_t < vocab ||
+      !draft_logits || !target_logits || !draft_tokens || !u_accept || !u_sample || !tokens || !n_out ||
+      !(temperature > 0.f) || !std::isfinite(temperature) || !(top_p > 0.f) || !(top_p <= 1.f)) {
+    g_create_err = "bad speculative-acceptance argument";
+    return DORY_ERR_INVALID_ARG;
+  }
+  const hipError_t e = launch_spec_accept(n, gamma, vocab, draft_logits, ld_d, target_logits, ld_t, draft_tokens,
+                                          temperature, top_p, u_accept, u_sample, tokens, n_out, (hipStream_t)stream);
+  if (e != hipSuccess) {
+    g_create_err = hipGetErrorString(e);
+    return DORY_ERR_HIP;
+  }
   return DORY_OK;
 }
 

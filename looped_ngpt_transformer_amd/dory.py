@@ -79,6 +79,9 @@ _SIGS = {
     "dory_get_loops": (C.c_int, [_P, C.POINTER(C.c_int)]),
     "dory_set_seq_loops": (C.c_int, [_P, C.c_int32, C.c_int]),
     "dory_seq_loops": (C.c_int, [_P, C.c_int32, C.POINTER(C.c_int)]),
+    "dory_truncate_seq": (C.c_int, [_P, C.c_int32, C.c_int64]),
+    "dory_spec_accept": (C.c_int, [_P, C.c_int, C.c_int, C.c_int64, _P, C.c_int64, _P, C.c_int64, _P, C.c_float,
+                                   C.c_float, _P, _P, _P, _P]),
     "dory_set_kv_mode": (C.c_int, [_P, C.c_int]),
     "dory_get_kv_mode": (C.c_int, [_P, C.POINTER(C.c_int)]),
     "dory_prefill": (C.c_int, [_P, _P, C.c_int, _I32P, _I32P, _P, _P]),
@@ -217,6 +220,21 @@ def dory_seq_loops(ctx, seq_id: int) -> int:
     k = C.c_int(0)
     _check(lib().dory_seq_loops(ctx, seq_id, C.byref(k)), ctx)
     return k.value
+
+
+def dory_truncate_seq(ctx, seq_id: int, length: int):
+    _check(lib().dory_truncate_seq(ctx, seq_id, length), ctx)
+
+
+def dory_spec_accept(draft_logits, target_logits, draft_tokens, u_accept, u_sample, tokens, n_out,
+                     temperature=1.0, top_p=0.95, stream=None):
+    """draft_logits [gamma * n, V] and draft_tokens, u_accept [gamma, n] position-major;
+    target_logits [n * (gamma + 1), V] sequence-major; tokens [n, gamma + 1], n_out [n]."""
+    gamma, n = int(draft_tokens.shape[0]), int(draft_tokens.shape[1])
+    _check(lib().dory_spec_accept(_stream(stream), n, gamma, int(draft_logits.shape[1]), _ptr(draft_logits),
+                                  int(draft_logits.stride(0)), _ptr(target_logits), int(target_logits.stride(0)),
+                                  _ptr(draft_tokens), float(temperature), float(top_p), _ptr(u_accept),
+                                  _ptr(u_sample), _ptr(tokens), _ptr(n_out)))
 
 
 def dory_set_kv_mode(ctx, mode: int):

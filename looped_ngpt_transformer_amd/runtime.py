@@ -96,6 +96,50 @@ class DoryRuntime:
         D.dory_logits(self.ctx, states, out)
         return out
 
+    def sample(self, logits, u, tokens=None, temperature=1.0, top_p=0.95):
+        if tokens is None:
+            tokens = torch.empty((logits.shape[0],), dtype=torch.int32, device=self.device)
+        D.dory_sample_top_p(logits, u, tokens, temperature=temperature, top_p=top_p)
+        return tokens
+
+    def spec_step(self, seq_ids, cur, gamma, u_draft, u_accept, u_sample, temperature=1.0, top_p=0.95):
+        """One self-speculative step for live sequences seq_ids whose next input token is
+        cur [n] (int32, device): draft gamma tokens with one loop, truncate the drafts
+        away, verify cur and the drafts as one chunk at the sequences' own loop counts,
+        accept by rejection sampling, and keep the cache entries of the emitted positions.
+        u_draft, u_accept [gamma, n], u_sample [n]: uniform draws (device float).
+        Returns tokens [n, gamma + 1] and n_out [n] on the host, and the device tensors
+        used: draft logits [gamma * n, V], draft tokens [gamma, n], verifying logits
+        [n * (gamma + 1), V]."""
+        n = len(seq_ids)
+        ctx = self.ctx
+        L0 = [D.dory_seq_len(ctx, s) for s in seq_ids]
+        for s in seq_ids:
+            D.dory_set_seq_loops(ctx, s, 1)
+        V = self.vocab
+        draft = torch.empty((gamma * n, V), dtype=torch.float32, device=self.device)
+        xt = torch.empty((gamma, n), dtype=torch.int32, device=self.device)
+        tok = cur
+        try:
+            for j in range(gamma):
+                y = self.decode(seq_ids, self.embed(tok))
+                lg = self.logits(y, out=draft[j * n:(j + 1) * n])
+                tok = self.sample(lg, u_draft[j], xt[j], temperature, top_p)
+        finally:
+            for s, l0 in zip(seq_ids, L0):
+                D.dory_set_seq_loops(ctx, s, 0)
+                D.dory_truncate_seq(ctx, s, l0)
+        chunk = torch.cat([cur.view(n, 1), xt.t()], dim=1).contiguous().view(-1)
+        y = self.prefill(seq_ids, [gamma + 1] * n, self.embed(chunk))
+        target = self.logits(y)
+        out = torch.empty((n, gamma + 1), dtype=torch.int32, device=self.device)
+        n_out = torch.empty((n,), dtype=torch.int32, device=self.device)
+        D.dory_spec_accept(draft, target, xt, u_accept, u_sample, out, n_out, temperature=temperature, top_p=top_p)
+        out_h, n_h = out.cpu().numpy(), n_out.cpu().numpy()
+        for s, l0, m in zip(seq_ids, L0, n_h):
+            D.dory_truncate_seq(ctx, s, l0 + int(m))
+        return out_h, n_h, {"draft": draft, "drafts": xt, "target": target}
+
     def close(self):
         if self.ctx is not None:
             torch.cuda.synchronize(self.device)

@@ -96,7 +96,8 @@ def _seed(*parts: int) -> int:
 
 _NAME_ID = {"w_qkvg": 1, "w_o": 2, "w_gu": 3, "w_down": 4, "alpha_attn": 5,
             "alpha_mlp": 6, "s_qk": 7, "x": 8, "k": 9, "v": 10, "embed": 11, "lm_head": 12,
-            "logit_scale": 13, "ids": 14, "u": 15}
+            "logit_scale": 13, "ids": 14, "u": 15, "spec_base": 16, "spec_target": 17,
+            "spec_draft": 18}
 
 VOCAB = 131072  # the tokenizer's vocabulary (MXFP8 article, checkpoint notes)
 
@@ -194,3 +195,20 @@ def make_draws(n: int, seed: int, stream: int = 0, device="cpu") -> torch.Tensor
     """n seeded uniform draws in [0, 1), float32 (the sampler's random numbers)."""
     g = _gen(device, seed, stream, _NAME_ID["u"])
     return torch.rand((n,), generator=g, device=device, dtype=torch.float32)
+
+
+def make_spec_logits(n: int, gamma: int, vocab: int, seed: int, spread: float = 3.0, noise: float = 0.5,
+                     device="cpu"):
+    """Logit rows for a speculative step of n sequences: a shared base row per position
+    (Gaussian, std `spread`) plus independent Gaussian noise (std `noise`) for the
+    verifying model's gamma + 1 rows and the draft's gamma rows, so the two distributions
+    overlap without being equal. Returns (draft [gamma * n, V] position-major, target
+    [n * (gamma + 1), V] sequence-major)."""
+    g = _gen("cpu", seed, n, gamma, vocab, _NAME_ID["spec_base"])
+    base = torch.randn((n, gamma + 1, vocab), generator=g, dtype=torch.float32) * spread
+    g = _gen("cpu", seed, n, gamma, vocab, _NAME_ID["spec_target"])
+    target = base + torch.randn(base.shape, generator=g, dtype=torch.float32) * noise
+    g = _gen("cpu", seed, n, gamma, vocab, _NAME_ID["spec_draft"])
+    draft = base[:, :gamma] + torch.randn((n, gamma, vocab), generator=g, dtype=torch.float32) * noise
+    return (draft.transpose(0, 1).reshape(gamma * n, vocab).contiguous().to(device),
+            target.reshape(n * (gamma + 1), vocab).contiguous().to(device))

@@ -9,6 +9,7 @@ import synth
 from oracle import dory_oracle as O
 from oracle import mxfp8 as MX
 from oracle import nvfp4 as NV
+from oracle import vocab as OV
 from tests.helpers import oracle_weights, to_np
 
 BF16_COS = 0.9995
@@ -92,3 +93,39 @@ def oracle_schedule(cfg, W, schedule, k, mode, seqs=None):
             ys.append(O.prefill(cfg, W, seqs[sid], to_np(x), k, mode))
         outs.append(np.concatenate(ys))
     return outs
+
+
+# float32 sums of the sampler against the oracle's float64: the width of the band around
+# every boundary of u (and of the top_p cut) inside which either side is accepted
+TOL_U = 5e-5
+
+
+def check_valid(lg_np, u_np, toks, temperature, top_p):
+    """Every token valid; returns how many rows were far enough from every boundary to
+    demand the oracle's exact token (those must match)."""
+    exact = 0
+    for i in range(lg_np.shape[0]):
+        t = int(toks[i])
+        assert 0 <= t < lg_np.shape[1], f"row {i}: token {t}"
+        order, _, cum = OV.sorted_order(lg_np[i], temperature)
+        n = OV.nucleus_size(cum, top_p)
+        rank = int(np.nonzero(order == t)[0][0])
+        u = float(u_np[i])
+        # nucleus sizes a float32 sum may also find: cuts whose running mass is within
+        # TOL_U of top_p
+        sizes = [m for m in range(max(1, n - 1), min(cum.size, n + 1) + 1)
+                 if m == n or abs(cum[m - 1] - top_p) <= TOL_U or (m == n + 1 and abs(cum[n - 1] - top_p) <= TOL_U)]
+        ok, clear = False, True
+        for m in sizes:
+            if rank >= m:
+                clear = False
+                continue
+            lo = (cum[rank - 1] if rank else 0.0) / cum[m - 1]
+            hi = cum[rank] / cum[m - 1]
+            ok |= lo - TOL_U <= u <= hi + TOL_U
+            clear &= lo + TOL_U < u < hi - TOL_U
+        assert ok, f"row {i}: token {t} (rank {rank}, nucleus {n}) does not match u {u}"
+        if clear:
+            assert t == OV.sample_top_p(lg_np[i], temperature, top_p, u), f"row {i}: token {t}"
+            exact += 1
+    return exact

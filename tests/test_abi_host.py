@@ -165,7 +165,15 @@ def test_mode_and_loop_changes_with_live_sequences():
     with pytest.raises(D.DoryError) as e:               # per_loop KV was built for k=2
         D.dory_set_seq_loops(ctx, 3, 4)
     assert e.value.code == D.ERR_STATE
-    D.dory_set_seq_loops(ctx, 3, 2)                     # its own k: allowed
+    D.dory_set_seq_loops(ctx, 3, 1)                     # fewer loops (drafting): allowed
+    assert D.dory_seq_loops(ctx, 3) == 1
+    D.dory_set_seq_loops(ctx, 3, 0)                     # back to the k its cache holds
+    assert D.dory_seq_loops(ctx, 3) == 2
+    with pytest.raises(D.DoryError) as e:
+        D.dory_truncate_seq(ctx, 3, 101)                # longer than the sequence
+    assert e.value.code == D.ERR_INVALID_ARG
+    D.dory_truncate_seq(ctx, 3, 60)
+    assert D.dory_seq_len(ctx, 3) == 60
     with pytest.raises(D.DoryError) as e:
         D.dory_set_seq_loops(ctx, 99, 2)                # unknown sequence
     assert e.value.code == D.ERR_INVALID_ARG

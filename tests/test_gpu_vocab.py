@@ -18,14 +18,13 @@ import synth
 from looped_ngpt_transformer_amd import dory as D
 from looped_ngpt_transformer_amd.runtime import DoryRuntime
 from oracle import vocab as OV
-from tests.gpu_helpers import gpu_weights
+from tests.gpu_helpers import check_valid, gpu_weights
 from tests.helpers import to_np
 
 pytestmark = pytest.mark.gpu
 
 PSMALL = synth.config("P", n_in=1, n_rec=1, n_out=1, window=64)
 TSMALL = synth.config("T")
-TOL_U = 5e-5
 
 
 def runtime(shape, vocab, seed=21, max_rows=256, scale=(15.0, 25.0)):
@@ -92,37 +91,6 @@ def sample(lg, u, temperature=1.0, top_p=0.95):
     D.dory_sample_top_p(lg, u, tok, temperature=temperature, top_p=top_p)
     torch.cuda.synchronize()
     return tok.cpu().numpy()
-
-
-def check_valid(lg_np, u_np, toks, temperature, top_p):
-    """Every token valid; returns how many rows were far enough from every boundary to
-    demand the oracle's exact token (those must match)."""
-    exact = 0
-    for i in range(lg_np.shape[0]):
-        t = int(toks[i])
-        assert 0 <= t < lg_np.shape[1], f"row {i}: token {t}"
-        order, _, cum = OV.sorted_order(lg_np[i], temperature)
-        n = OV.nucleus_size(cum, top_p)
-        rank = int(np.nonzero(order == t)[0][0])
-        u = float(u_np[i])
-        # nucleus sizes a float32 sum may also find: cuts whose running mass is within
-        # TOL_U of top_p
-        sizes = [m for m in range(max(1, n - 1), min(cum.size, n + 1) + 1)
-                 if m == n or abs(cum[m - 1] - top_p) <= TOL_U or (m == n + 1 and abs(cum[n - 1] - top_p) <= TOL_U)]
-        ok, clear = False, True
-        for m in sizes:
-            if rank >= m:
-                clear = False
-                continue
-            lo = (cum[rank - 1] if rank else 0.0) / cum[m - 1]
-            hi = cum[rank] / cum[m - 1]
-            ok |= lo - TOL_U <= u <= hi + TOL_U
-            clear &= lo + TOL_U < u < hi - TOL_U
-        assert ok, f"row {i}: token {t} (rank {rank}, nucleus {n}) does not match u {u}"
-        if clear:
-            assert t == OV.sample_top_p(lg_np[i], temperature, top_p, u), f"row {i}: token {t}"
-            exact += 1
-    return exact
 
 
 @pytest.mark.parametrize("scale,min_exact", [((15.0, 25.0), 0), ((300.0, 500.0), 28)], ids=["flat", "peaked"])
