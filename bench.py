@@ -41,6 +41,8 @@ WORKLOAD_TEXT = {
     "T": "tiny looped nGPT fp32, prefill 64",
     "G": "Full 16/40/16 (72 layers) bf16, generation batch 32 over a seeded 32768-token KV context: "
          "decode step, LM head over 131072 tokens, top-p sampling, embedding of the sampled tokens",
+    "S": "Full 16/40/16 (72 layers) bf16, self-speculative generation over a seeded per_loop KV context: "
+         "gamma tokens drafted with one loop, verified as one chunk with k loops, rejection sampling",
 }
 
 
@@ -53,7 +55,8 @@ def parse():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=5)
     ap.add_argument("--warmup", type=int, default=2)
-    ap.add_argument("--workload", default="P", choices=["P", "D", "Q", "N", "L", "T", "G"])
+    ap.add_argument("--workload", default="P", choices=["P", "D", "Q", "N", "L", "T", "G", "S"])
+    ap.add_argument("--gamma", type=int, default=4, help="speculative draft length (S)")
     ap.add_argument("--k", type=int, default=None)
     ap.add_argument("--ks", default=None, help="comma list of loop counts to measure too")
     ap.add_argument("--mode", default=None, choices=["per_loop", "last_loop"])
@@ -338,6 +341,109 @@ def bench_decode(args, torch, synth, D, DoryRuntime):
     return out
 
 
+def bench_spec(args, torch, synth, D, DoryRuntime):
+    """Self-speculative generation against plain generation at the verifying loop count,
+    same batch, context and weights. A step emits 1..gamma+1 tokens per sequence; value
+    is emitted tokens per second. Random weights set the acceptance rate, so the line
+    also gives the cost of each part and the acceptance at which the two break even."""
+    shape = synth.config("D")
+    batch = args.batch or 32
+    ctx_len = args.context or 4096
+    k = args.k or 4
+    gamma = args.gamma
+    steps, warm = args.steps, args.warmup
+    n_tok = ctx_len + (steps + warm + 2) * (gamma + 1) + 2
+    weights = synth.make_weights(shape, 1234, "cuda")
+    pages = D.dory_kv_pages_needed(D.make_config(shape, max_loops=k, max_seqs=batch, max_seq_len=n_tok,
+                                                 max_rows=batch * (gamma + 1)), D.KV_PER_LOOP, k, n_tok, batch)
+    rt = DoryRuntime(shape, weights, max_loops=k, max_seqs=batch, max_seq_len=n_tok,
+                     max_rows=batch * (gamma + 1), kv_pages=pages, mode="per_loop", loops=k)
+    log(f"[bench] S: KV pool {pages * rt.page_bytes / 1e9:.1f} GB; seeding {ctx_len} tokens x {batch}")
+    seed_kv(rt, shape, synth, D, torch, batch, ctx_len, [k] * batch, "per_loop")
+    rt.bind_vocab(synth.make_vocab(shape, synth.VOCAB, 4321, "cuda"))
+    ids = list(range(batch))
+    nd = steps + warm
+    UD = synth.make_draws(nd * gamma * batch, 101, device="cuda").view(nd, gamma, batch)
+    UA = synth.make_draws(nd * gamma * batch, 102, device="cuda").view(nd, gamma, batch)
+    US = synth.make_draws(nd * batch, 103, device="cuda").view(nd, batch)
+    cur = synth.make_ids(batch, synth.VOCAB, 104, "cuda")
+    emitted, accepted = 0, 0
+    for s in range(nd):
+        if s == warm:
+            torch.cuda.synchronize()
+            t0 = time.perf_counter()
+        out, n_out, _ = rt.spec_step(ids, cur, gamma, UD[s], UA[s], US[s])
+        cur = torch.tensor([int(out[b, n_out[b] - 1]) for b in ids], dtype=torch.int32, device="cuda")
+        if s >= warm:
+            emitted += int(n_out.sum())
+            accepted += int((n_out - 1).sum())
+    torch.cuda.synchronize()
+    dt = (time.perf_counter() - t0) / steps
+    log(f"[bench] spec: {dt * 1e3:.2f} ms/step, {emitted / steps / dt:.1f} tok/s")
+
+    # the parts, timed alone on the same context (each restores the lengths it changed)
+    lens = [D.dory_seq_len(rt.ctx, b) for b in ids]
+    V = synth.VOCAB
+    LG = torch.empty((batch, V), dtype=torch.float32, device="cuda")
+    TOK = torch.empty((batch,), dtype=torch.int32, device="cuda")
+    Y = torch.empty((batch, shape["hidden"]), dtype=torch.float32, device="cuda")
+
+    def gen_step(loops, r):
+        for b in ids:
+            D.dory_set_seq_loops(rt.ctx, b, loops)
+        x = rt.embed(TOK if r else cur)
+        D.dory_decode_step(rt.ctx, ids, x, Y)
+        D.dory_logits(rt.ctx, Y, LG)
+        D.dory_sample_top_p(LG, US[r % nd], TOK)
+
+    def timed(fn, reps):
+        fn(0)
+        torch.cuda.synchronize()
+        t = time.perf_counter()
+        for r in range(reps):
+            fn(r + 1)
+        torch.cuda.synchronize()
+        el = (time.perf_counter() - t) / reps
+        for b, l0 in zip(ids, lens):
+            D.dory_set_seq_loops(rt.ctx, b, 0)
+            D.dory_truncate_seq(rt.ctx, b, l0)
+        return el
+
+    t_ar = timed(lambda r: gen_step(0, r), gamma)   # plain generation at k loops
+    t_draft = timed(lambda r: gen_step(1, r), gamma)  # one draft step at one loop
+    XV = synth.make_inputs(batch * (gamma + 1), shape["hidden"], 105, device="cuda")
+    YV = torch.empty_like(XV)
+    LV = torch.empty((batch * (gamma + 1), V), dtype=torch.float32, device="cuda")
+
+    def verify(r):
+        for b, l0 in zip(ids, lens):
+            D.dory_truncate_seq(rt.ctx, b, l0)
+        D.dory_prefill(rt.ctx, ids, [gamma + 1] * batch, XV, YV)
+        D.dory_logits(rt.ctx, YV, LV)
+
+    t_verify = timed(verify, 3)
+    rt.close()
+    ar_tps = batch / t_ar
+    spec_tps = emitted / steps / dt
+    out = {
+        "metric": "self-speculative generation tokens/s (draft 1 loop, verify k=%d, gamma=%d)" % (k, gamma),
+        "value": round(spec_tps, 2), "unit": "tokens/s", "n_gpus": 1, "steps": steps, "warmup": warm,
+        "ms_per_step": round(dt * 1e3, 3), "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+        "dtype": "bf16", "data": "synthetic (seeded random weights, seeded per_loop KV context, seeded draws)",
+        "config": {"workload": WORKLOAD_TEXT["S"], "batch": batch, "context": ctx_len, "loops": k,
+                   "gamma": gamma, "kv_mode": "per_loop", "weights": shape["weight_format"]},
+        "spec": {"accepted_per_step": round(accepted / steps / batch, 3),
+                 "emitted_per_step": round(emitted / steps / batch, 3),
+                 "autoregressive_k_tokens_per_s": round(ar_tps, 2),
+                 "ratio_to_autoregressive": round(spec_tps / ar_tps, 3),
+                 "ms_autoregressive_step": round(t_ar * 1e3, 3),
+                 "ms_draft_step": round(t_draft * 1e3, 3),
+                 "ms_verify_chunk": round(t_verify * 1e3, 3),
+                 "breakeven_emitted_per_step": round((gamma * t_draft + t_verify) / t_ar, 3)},
+    }
+    return out
+
+
 def seed_kv(rt, shape, synth, D, torch, batch, ctx_len, kseq, mode):
     """Reserve ctx_len positions per sequence and write seeded K/V into every cache slot
     the sequence holds (sliding layers: the last window of positions). Sequence b runs
@@ -380,6 +486,8 @@ def main():
         del src, dst
     if args.workload in ("P", "L", "T"):
         out = bench_prefill(args, torch, synth, D, DoryRuntime)
+    elif args.workload == "S":
+        out = bench_spec(args, torch, synth, D, DoryRuntime)
     else:
         out = bench_decode(args, torch, synth, D, DoryRuntime)
     out["env"] = {"torch": torch.__version__, "hip": getattr(torch.version, "hip", None),

@@ -278,14 +278,25 @@ int64_t pages_for_stream(int64_t len, bool full, int ring) {
   return full ? np : std::min<int64_t>(np, ring);
 }
 
-// Pages a sequence must newly allocate to grow from len0 to len1.
+// Pages a sequence must newly allocate to grow from its length to len1: the page-table
+// entries grow() would fill that hold no page yet (a truncated sequence keeps the pages
+// past its length, so only the others count).
 int64_t pages_to_grow(const dory_ctx* c, const Seq& q, int64_t len1) {
   int64_t need = 0;
+  const int64_t lp0 = (q.len + DORY_PAGE_TOKENS - 1) / DORY_PAGE_TOKENS;
+  const int64_t lp1 = (len1 + DORY_PAGE_TOKENS - 1) / DORY_PAGE_TOKENS;
   for (int s = 0; s < c->D.n_streams; ++s) {
     if (!c->stream_used(q, s)) continue;
     const int l = c->layer_of_stream(s);
-    need += pages_for_stream(len1, c->is_full(l), c->ring_of(l)) -
-            pages_for_stream(q.len, c->is_full(l), c->ring_of(l));
+    const int ring = c->ring_of(l);
+    const bool full = c->is_full(l);
+    const std::vector<int32_t>* tab = (size_t)s < q.pages.size() ? &q.pages[s] : nullptr;
+    // a ring stream visits each entry at most once however far it grows
+    const int64_t end = full ? lp1 : std::min(lp1, lp0 + ring);
+    for (int64_t lp = lp0; lp < end; ++lp) {
+      const int64_t idx = full ? lp : lp % ring;
+      if (!tab || (int64_t)tab->size() <= idx || (*tab)[idx] < 0) ++need;
+    }
   }
   return need;
 }

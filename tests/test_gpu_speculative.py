@@ -280,3 +280,27 @@ def test_spec_step_matches_oracle(mode):
         cur = torch.tensor([out[b, n_out[b] - 1] for b in range(n)], dtype=torch.int32, device="cuda")
     assert len(alive) >= 2 and emitted >= 6
     rt.close()
+
+
+def test_truncated_sequence_regrows_into_its_own_pages():
+    """A pool sized exactly for 130 positions: a one-loop draft step past a page boundary
+    takes the last free pages; after truncation the verifying step must reuse them
+    rather than ask the empty pool for more."""
+    from looped_ngpt_transformer_amd.runtime import DoryRuntime
+    from tests.gpu_helpers import gpu_weights
+    S = synth.config("T")
+    cfg = D.make_config(S, max_loops=2, max_seqs=1, max_seq_len=130, max_rows=128)
+    pages = D.dory_kv_pages_needed(cfg, D.KV_PER_LOOP, 2, 130, 1)
+    rt = DoryRuntime(S, gpu_weights(S, 91), max_loops=2, max_seqs=1, max_seq_len=130, max_rows=128,
+                     kv_pages=pages, mode="per_loop", loops=2)
+    rt.prefill([0], [128], synth.make_inputs(128, S["hidden"], 92, device="cuda"))
+    x = synth.make_inputs(2, S["hidden"], 93, device="cuda")
+    D.dory_set_seq_loops(rt.ctx, 0, 1)
+    rt.decode([0], x[:1])
+    assert D.dory_kv_bytes_in_use(rt.ctx) == pages * rt.page_bytes      # every page taken
+    D.dory_set_seq_loops(rt.ctx, 0, 0)
+    D.dory_truncate_seq(rt.ctx, 0, 128)
+    rt.prefill([0], [2], x)
+    torch.cuda.synchronize()
+    assert D.dory_seq_len(rt.ctx, 0) == 130
+    rt.close()
