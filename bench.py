@@ -422,6 +422,13 @@ def bench_spec(args, torch, synth, D, DoryRuntime):
         D.dory_logits(rt.ctx, YV, LV)
 
     t_verify = timed(verify, 3)
+    D.dory_profile_enable(rt.ctx, True)   # one more verifying chunk, every kernel class timed
+    verify(0)
+    torch.cuda.synchronize()
+    D.dory_profile_enable(rt.ctx, False)
+    vbrk = kernel_stats(rt, D)
+    for b, l0 in zip(ids, lens):
+        D.dory_truncate_seq(rt.ctx, b, l0)
     rt.close()
     ar_tps = batch / t_ar
     spec_tps = emitted / steps / dt
@@ -439,7 +446,8 @@ def bench_spec(args, torch, synth, D, DoryRuntime):
                  "ms_autoregressive_step": round(t_ar * 1e3, 3),
                  "ms_draft_step": round(t_draft * 1e3, 3),
                  "ms_verify_chunk": round(t_verify * 1e3, 3),
-                 "breakeven_emitted_per_step": round((gamma * t_draft + t_verify) / t_ar, 3)},
+                 "breakeven_emitted_per_step": round((gamma * t_draft + t_verify) / t_ar, 3),
+                 "verify_kernels": {n: {"launches": v["launches"], "ms": round(v["ms"], 3)} for n, v in vbrk.items()}},
     }
     return out
 

@@ -29,7 +29,7 @@ namespace {
 
 constexpr int NSTAGE = 4;          // pinned staging buffers in rotation
 constexpr int DELTA_CAP = 65536;   // page-table updates per upload
-constexpr int SKINNY_M = 128;      // rows up to which projections use split-K tiles
+constexpr int SKINNY_M = 256;      // rows up to which projections use split-K tiles
 constexpr size_t ALIGN = 256;
 constexpr int ROPE_INTS = 2 * 128 * 2;  // two tables of up to 128 doubles
 
