@@ -205,20 +205,43 @@ constexpr int BUF_RSRC_WORD3 = 0x00020000;  // buffer resource flags: raw 32-bit
 
 // NBUF: register sets of K/V fragments per wave (2: the next half-page is in flight
 // while the current one is computed); WPE: waves per SIMD the registers are cut for.
-template <int D, int NBUF, int WPE>
+// QUAD: a wave takes up to four consecutive rows of one chunk (a quad of a prefill tile)
+// as columns 4 r + g of the B operand, so a short chunk reads its keys once per quad
+// instead of once per row; each column masks its own key range.
+template <int D, int NBUF, int WPE, bool QUAD>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(WPE))) void k_attn_decode(AttnArgs a, int nsub, int pps) {
   constexpr int G = 4, DC = D / 32, CB = D / 16;
   constexpr int PSTRIDE = 2 * G + G * D;  // floats per partial: m[G], l[G], o[G][D]
   const int lane = threadIdx.x & 63;
   // wave-uniform indices in scalar registers: page addresses become scalar bases
   const int wid = __builtin_amdgcn_readfirstlane(blockIdx.x * 4 + (threadIdx.x >> 6));
-  if (wid >= a.M * a.Hkv * nsub) return;
+  if (wid >= (QUAD ? a.n_quads : a.M) * a.Hkv * nsub) return;
   const int sub = wid % nsub, grp = wid / nsub;
-  const int hk = grp % a.Hkv, m = grp / a.Hkv;
+  const int hk = grp % a.Hkv;
+  int m = grp / a.Hkv, R = 1;  // first row, rows taken
+  if constexpr (QUAD) {
+    // quad index -> (tile, quad of the tile): tiles hold <= 64 rows, ceil(rows / 4) quads
+    const int quad = m;
+    int t = 0, q0 = 0, nr = 0;
+    for (; t < a.n_tiles; ++t) {
+      nr = a.tiles[4 * t + 1];
+      const int nq = (nr + 3) >> 2;
+      if (quad < q0 + nq) break;
+      q0 += nq;
+    }
+    m = a.tiles[4 * t] + 4 * (quad - q0);
+    R = min(4, nr - 4 * (quad - q0));
+  }
   const int lq = lane & 15, lk = lane >> 4;
-  const int p = a.pos[m];
+  const int rq = min(lq >> 2, R - 1);  // this column's row (columns 4R.. repeat the last)
+  const int p_col = a.pos[m + rq];
+  const int lo_col = a.window > 0 ? max(0, p_col - a.window + 1) : 0;
+  // the rows' positions are consecutive: the key range of the quad and the part every
+  // column sees
+  const int p = a.pos[m + R - 1], p_min = a.pos[m];
   const int seq = a.row_seq[m];
-  const int lo = a.window > 0 ? max(0, p - a.window + 1) : 0;
+  const int lo = a.window > 0 ? max(0, p_min - a.window + 1) : 0;
+  const int lo_max = a.window > 0 ? max(0, p - a.window + 1) : 0;
   const int pg_lo = lo / PAGE, pg_hi = p / PAGE;
   const int pa = pg_lo + sub * pps;
   const int pb = min(pg_hi, pa + pps - 1);
@@ -229,7 +252,9 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(WPE))) void
 #pragma unroll
   for (int c = 0; c < DC; ++c) {
     uint4 v = make_uint4(0, 0, 0, 0);
-    if (lq < G) v = *(const uint4*)((const bf16_t*)a.q + (size_t)m * a.Hq * D + (size_t)(hk * G + lq) * D + 32 * c + 8 * lk);
+    if (lq < G * R)
+      v = *(const uint4*)((const bf16_t*)a.q + (size_t)(m + (lq >> 2)) * a.Hq * D + (size_t)(hk * G + (lq & 3)) * D +
+                          32 * c + 8 * lk);
     qf[c] = __builtin_bit_cast(bf16x8, v);
   }
   const float sl2 = a.scale * 1.4426950408889634f;
@@ -269,7 +294,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(WPE))) void
   auto compute = [&](int hp, const Half& H) {
     const int pg = hp >> 1, hf = hp & 1;
     const int kbase = pg * PAGE + 32 * hf + 8 * lk;  // this lane's first key
-    const bool whole = pg * PAGE + 32 * hf >= lo && pg * PAGE + 32 * hf + 31 <= p;
+    const bool whole = pg * PAGE + 32 * hf >= lo_max && pg * PAGE + 32 * hf + 31 <= p_min;
     f32x4 st[2];
 #pragma unroll
     for (int kb = 0; kb < 2; ++kb) {
@@ -284,7 +309,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(WPE))) void
 #pragma unroll
     for (int e = 0; e < 8; ++e) {
       const int key = kbase + e;
-      const bool vis = key >= lo && key <= p;
+      const bool vis = key >= lo_col && key <= p_col;
       sv[e] = vis ? st[e >> 2][e & 3] * sl2 : -INFINITY;
       mt = fmaxf(mt, sv[e]);
     }
@@ -351,16 +376,17 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(WPE))) void
     }
   }
 
-  // ---- publish this split's partial: O^T[channel 16 cb + 4 lk + r][head lq]
-  float* const gbase = a.part + (size_t)grp * nsub * PSTRIDE;
-  if (lq < G) {
-    float* mine = gbase + (size_t)sub * PSTRIDE;
+  // ---- publish this split's partial: O^T[channel 16 cb + 4 lk + r][column lq], column
+  // 4 r + g being head g of row m + r
+  if (lq < G * R) {
+    const int g = lq & 3;
+    float* mine = a.part + ((size_t)((m + (lq >> 2)) * a.Hkv + hk) * nsub + sub) * PSTRIDE;
     if (lk == 0) {
-      mine[lq] = m_run;
-      mine[G + lq] = l_run;
+      mine[g] = m_run;
+      mine[G + g] = l_run;
     }
 #pragma unroll
-    for (int cb = 0; cb < CB; ++cb) *(f32x4*)(mine + 2 * G + lq * D + 16 * cb + 4 * lk) = o[cb];
+    for (int cb = 0; cb < CB; ++cb) *(f32x4*)(mine + 2 * G + g * D + 16 * cb + 4 * lk) = o[cb];
   }
 }
 
@@ -424,7 +450,7 @@ __global__ __launch_bounds__(64) void k_decode_merge(AttnArgs a, int nsub) {
 // One launch of the decode kernel: (row, KV head) groups split over keys so that the
 // waves fill the device once (the resident count comes from the occupancy query); at
 // most max_sub splits per group (the merge weighs one split per lane: <= 64).
-template <int D, int NBUF, int WPE>
+template <int D, int NBUF, int WPE, bool QUAD>
 static hipError_t launch_decode(const AttnArgs& a, int n_pages, int max_sub, int phase, int* splits_out,
                                 hipStream_t st) {
   static int slots = 0;
@@ -432,12 +458,13 @@ static hipError_t launch_decode(const AttnArgs& a, int n_pages, int max_sub, int
     int dev = 0, cus = 0, blocks = 0;
     if (hipGetDevice(&dev) != hipSuccess ||
         hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
-        hipOccupancyMaxActiveBlocksPerMultiprocessor(&blocks, k_attn_decode<D, NBUF, WPE>, 256, 0) != hipSuccess ||
+        hipOccupancyMaxActiveBlocksPerMultiprocessor(&blocks, k_attn_decode<D, NBUF, WPE, QUAD>, 256, 0) !=
+            hipSuccess ||
         cus <= 0 || blocks <= 0)
       return hipErrorInvalidValue;
     slots = cus * blocks * 4;
   }
-  const int groups = a.M * a.Hkv;
+  const int groups = (QUAD ? a.n_quads : a.M) * a.Hkv;
   int nsub = std::max(1, slots / groups);
   nsub = std::min({nsub, n_pages, max_sub, 64});
   while (nsub > 1 && (size_t)a.M * a.Hq * nsub * (a.d + 2) > (size_t)a.part_cap) nsub = (nsub + 1) / 2;
@@ -446,7 +473,7 @@ static hipError_t launch_decode(const AttnArgs& a, int n_pages, int max_sub, int
   const int waves = groups * nsub;
   if (splits_out) *splits_out = nsub;
   if (phase == ATTN_SPLITS)
-    hipLaunchKernelGGL((k_attn_decode<D, NBUF, WPE>), dim3((waves + 3) / 4), dim3(256), 0, st, a, nsub, pps);
+    hipLaunchKernelGGL((k_attn_decode<D, NBUF, WPE, QUAD>), dim3((waves + 3) / 4), dim3(256), 0, st, a, nsub, pps);
   else if (phase == ATTN_MERGE)
     hipLaunchKernelGGL(k_decode_merge<D>, dim3(a.M * a.Hq), dim3(64), 0, st, a, nsub);
   return hipGetLastError();
@@ -456,10 +483,17 @@ static hipError_t launch_decode(const AttnArgs& a, int n_pages, int max_sub, int
 // Short ranges (sliding windows, short contexts): one register set, three waves per SIMD,
 // a page per split, so that the whole range is requested at once.
 constexpr int DECODE_SHORT_PAGES = 32;
+// Chunks of several rows (max_tile_rows > 1) go by quads of rows, whose key range is up
+// to three positions longer than a row's (one more page at most).
 template <int D>
 static hipError_t launch_decode_d(const AttnArgs& a, int n_pages, int phase, int* splits, hipStream_t st) {
-  if (n_pages > DECODE_SHORT_PAGES) return launch_decode<D, 2, 1>(a, n_pages, 16, phase, splits, st);
-  return launch_decode<D, 1, 3>(a, n_pages, 64, phase, splits, st);
+  if (a.max_tile_rows > 1 && a.n_quads > 0 && a.tiles) {
+    if (a.window > 0) ++n_pages;
+    if (n_pages > DECODE_SHORT_PAGES) return launch_decode<D, 2, 1, true>(a, n_pages, 16, phase, splits, st);
+    return launch_decode<D, 1, 3, true>(a, n_pages, 64, phase, splits, st);
+  }
+  if (n_pages > DECODE_SHORT_PAGES) return launch_decode<D, 2, 1, false>(a, n_pages, 16, phase, splits, st);
+  return launch_decode<D, 1, 3, false>(a, n_pages, 64, phase, splits, st);
 }
 
 static int attn_pages_max(int max_pos, int window) {

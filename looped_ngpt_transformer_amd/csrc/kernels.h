@@ -124,6 +124,7 @@ struct AttnArgs {
   const int32_t* tiles = nullptr; // [n_tiles][4]: row0, nrows, pos0, seq slot
   int n_tiles = 0;
   int max_tile_rows = 0;
+  int n_quads = 0;                // sum over tiles of ceil(rows / 4): row-wise kernel by quads
 };
 // Row-wise paged attention (any row count; split over keys) + combine + gate, in two
 // phases launched separately: ATTN_SPLITS (the split-key kernel, writes partials) and

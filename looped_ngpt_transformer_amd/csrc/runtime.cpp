@@ -384,11 +384,12 @@ struct CallPlan {
   int max_pos = 0;
   int n_tiles = 0;
   int max_tile_rows = 0;
+  int n_quads = 0;  // sum over tiles of ceil(rows / 4)
   std::vector<std::pair<int64_t, int>> chunks;  // (first position, rows) per sequence
   // Loop counts: sequences are ordered by loop count, largest first, so the rows still
   // looping in loop t are a prefix: loop_rows[t], loop_tiles[t], loop_seqs[t] (t >= 1).
   int k_max = 1;
-  std::vector<int> loop_rows, loop_tiles, loop_seqs;
+  std::vector<int> loop_rows, loop_tiles, loop_seqs, loop_quads;
   bool reordered = false;  // rows are not in the caller's order (row map in the metadata)
 };
 
@@ -582,6 +583,7 @@ int run_layer(dory_ctx* ctx, hipStream_t st, const CallPlan& P, int l, int slot,
   aa.tiles = meta + 2 * c.max_rows;
   aa.n_tiles = P.n_tiles;
   aa.max_tile_rows = P.max_tile_rows;
+  aa.n_quads = P.n_quads;
   {
     double pairs, keys;
     attn_work(P, full, c.window, &pairs, &keys);
@@ -668,6 +670,7 @@ int run_forward(dory_ctx* ctx, hipStream_t st, const CallPlan& P, const float* x
     CallPlan Pt = P;
     Pt.M = P.loop_rows[t];
     Pt.n_tiles = P.loop_tiles[t];
+    Pt.n_quads = P.loop_quads[t];
     Pt.chunks.resize(P.loop_seqs[t]);
     const int slot = ctx->mode == DORY_KV_PER_LOOP ? t - 1 : 0;
     const int next = t < P.k_max ? P.loop_rows[t + 1] : 0;
@@ -773,6 +776,7 @@ int step(dory_ctx* ctx, hipStream_t st, int n, const int32_t* ids, const int32_t
   P.k_max = kseq[order[0]];
   P.loop_rows.assign(P.k_max + 2, 0);
   P.loop_tiles.assign(P.k_max + 2, 0);
+  P.loop_quads.assign(P.k_max + 2, 0);
   P.loop_seqs.assign(P.k_max + 2, 0);
   for (int i = 0; i < n; ++i) P.reordered |= order[i] != i;
   int row = 0;
@@ -805,6 +809,7 @@ int step(dory_ctx* ctx, hipStream_t st, int n, const int32_t* ids, const int32_t
       tl[2] = (int32_t)(p0 + j);
       tl[3] = q.slot;
       ++P.n_tiles;
+      P.n_quads += (tl[1] + 3) / 4;
     }
     P.max_tile_rows = std::min(64, std::max(P.max_tile_rows, nn));
     P.chunks.emplace_back(p0, nn);
@@ -813,6 +818,7 @@ int step(dory_ctx* ctx, hipStream_t st, int n, const int32_t* ids, const int32_t
     for (int t = 1; t <= kseq[i]; ++t) {  // prefixes: this sequence loops in loops 1..k
       P.loop_rows[t] = row;
       P.loop_tiles[t] = P.n_tiles;
+      P.loop_quads[t] = P.n_quads;
       P.loop_seqs[t] = oi + 1;
     }
   }
