@@ -108,8 +108,28 @@ struct RowView {
   const float* L;
   int V;
   float c, mz;  // e = 2^(l c - mz)
-  __device__ __forceinline__ float e(int i) const { return exp2f(L[i] * c - mz); }
+  __device__ __forceinline__ float ew(float l) const { return exp2f(l * c - mz); }
+  __device__ __forceinline__ float e(int i) const { return ew(L[i]); }
 };
+
+// f(i, L[i]) for the ids i < n a thread owns, in increasing order (t, t + ST, ...), with
+// SU loads in flight per thread: a pass over the row is bound by how many L2 requests
+// are outstanding, not by the arithmetic.
+constexpr int SU = 16;
+template <typename F>
+__device__ __forceinline__ void row_for(const float* L, int n, F&& f) {
+  for (int i0 = threadIdx.x; i0 < n; i0 += ST * SU) {
+    float v[SU];
+#pragma unroll
+    for (int u = 0; u < SU; ++u) {
+      const int i = i0 + u * ST;
+      v[u] = i < n ? L[i] : 0.f;
+    }
+#pragma unroll
+    for (int u = 0; u < SU; ++u)
+      if (i0 + u * ST < n) f(i0 + u * ST, v[u]);
+  }
+}
 
 // First token of the sorted order whose inclusive running mass reaches (incl) or
 // exceeds (!incl) target; if rounding leaves the target beyond the mass, the last token
@@ -125,15 +145,15 @@ __device__ int select_token(SampleLds& S, const RowView& R, float target, bool i
       S.bins[d][t] = 0.f;
       S.cnt[d][t] = 0;
     }
-    for (int i = t; i < R.V; i += ST) {
-      const float e = R.e(i);
+    row_for(R.L, R.V, [&](int, float l) {
+      const float e = R.ew(l);
       const uint32_t key = __float_as_uint(e);
       if (pass == 0 || (key >> (sh + 4)) == prefix) {
         const int d = (key >> sh) & 15;
         S.bins[d][t] += e;
         S.cnt[d][t] += 1;
       }
-    }
+    });
     __syncthreads();
     {  // wave w sums digit w over the threads, lane j taking threads j, j + 64, ...
       float v = 0.f;
@@ -199,8 +219,9 @@ __device__ int select_token(SampleLds& S, const RowView& R, float target, bool i
   int tok;
   if (n_tied == 1) {
     int mine = INT_MAX;
-    for (int i = t; i < R.V; i += ST)
-      if (__float_as_uint(R.e(i)) == prefix) mine = i;
+    row_for(R.L, R.V, [&](int i, float l) {
+      if (__float_as_uint(R.ew(l)) == prefix) mine = i;
+    });
     tok = block_min_int(mine, S.ired);
   } else {
     // the (jsel + 1)-th smallest id among them: the largest x with fewer than jsel + 1
@@ -209,7 +230,7 @@ __device__ int select_token(SampleLds& S, const RowView& R, float target, bool i
     while (hi - lo > 1) {
       const int mid = (lo + hi) / 2;
       int n = 0;
-      for (int i = t; i < mid; i += ST) n += __float_as_uint(R.e(i)) == prefix;
+      row_for(R.L, mid, [&](int, float l) { n += __float_as_uint(R.ew(l)) == prefix; });
       if (block_sum_int(n, S.ired) <= jsel) lo = mid;
       else hi = mid;
     }
@@ -228,10 +249,10 @@ __global__ __launch_bounds__(ST) void k_sample_top_p(const float* logits, int64_
   R.V = V;
   R.c = inv_t * 1.4426950408889634f;
   float m = -INFINITY;
-  for (int i = t; i < V; i += ST) m = fmaxf(m, R.L[i]);
+  row_for(R.L, V, [&](int, float l) { m = fmaxf(m, l); });
   R.mz = block_max16(m, S.red) * R.c;
   float s = 0.f;
-  for (int i = t; i < V; i += ST) s += R.e(i);
+  row_for(R.L, V, [&](int, float l) { s += R.ew(l); });
   const float total = block_sum<ST / WAVE>(s, S.red);
   // nucleus: the first token whose running mass reaches top_p of the total
   float mass;
@@ -261,19 +282,20 @@ struct Processed {
     R.V = V;
     R.c = inv_t * 1.4426950408889634f;
     float m = -INFINITY;
-    for (int i = t; i < V; i += ST) m = fmaxf(m, L[i]);
+    row_for(L, V, [&](int, float l) { m = fmaxf(m, l); });
     R.mz = block_max16(m, S.red) * R.c;
     float s = 0.f;
-    for (int i = t; i < V; i += ST) s += R.e(i);
+    row_for(L, V, [&](int, float l) { s += R.ew(l); });
     const float total = block_sum<ST / WAVE>(s, S.red);
     cut = select_token(S, R, top_p * total, true, &mass);
     ecut = R.e(cut);
   }
-  __device__ float prob(int v) const {
-    const float e = R.e(v);
+  __device__ float prob_l(int v, float l) const {  // l = the row's logit of token v
+    const float e = R.ew(l);
     const bool in = e > ecut || (e == ecut && v <= cut);
     return in ? e / mass : 0.f;
   }
+  __device__ float prob(int v) const { return prob_l(v, R.L[v]); }
 };
 
 // Prefix sums of one float per thread in thread order (fixed order): returns the inclusive
@@ -300,8 +322,26 @@ __device__ __forceinline__ float block_scan_f(float v, float* red, float* excl) 
 // (from p itself if the residual is empty). Thread t owns the ids [t C, t C + C).
 __device__ int residual_draw(SampleLds& S, const Processed& P, const Processed& Q, int V, float u) {
   const int t = threadIdx.x, C = (V + ST - 1) / ST, beg = min(t * C, V), end = min(beg + C, V);
+  // f(v, residual weight, p weight) over the thread's ids in increasing order, 8 loads
+  // of each row in flight
+  auto chunk = [&](auto&& f) {
+    for (int v0 = beg; v0 < end; v0 += 8) {
+      float lp[8], lq[8];
+#pragma unroll
+      for (int u = 0; u < 8; ++u) {
+        lp[u] = v0 + u < end ? P.R.L[v0 + u] : 0.f;
+        lq[u] = v0 + u < end ? Q.R.L[v0 + u] : 0.f;
+      }
+#pragma unroll
+      for (int u = 0; u < 8; ++u)
+        if (v0 + u < end) {
+          const float pv = P.prob_l(v0 + u, lp[u]);
+          f(v0 + u, fmaxf(pv - Q.prob_l(v0 + u, lq[u]), 0.f), pv);
+        }
+    }
+  };
   float mine = 0.f, acc;
-  for (int v = beg; v < end; ++v) mine += fmaxf(P.prob(v) - Q.prob(v), 0.f);
+  chunk([&](int, float r, float) { mine += r; });
   float incl = block_scan_f(mine, S.red, &acc);
   __syncthreads();
   if (t == ST - 1) S.above = incl;
@@ -310,7 +350,7 @@ __device__ int residual_draw(SampleLds& S, const Processed& P, const Processed& 
   __syncthreads();
   if (from_p) {  // empty residual
     mine = 0.f;
-    for (int v = beg; v < end; ++v) mine += P.prob(v);
+    chunk([&](int, float, float pv) { mine += pv; });
     incl = block_scan_f(mine, S.red, &acc);
     __syncthreads();
     if (t == ST - 1) S.above = incl;
@@ -318,12 +358,12 @@ __device__ int residual_draw(SampleLds& S, const Processed& P, const Processed& 
   }
   const float target = u * S.above;
   int cand = INT_MAX, last = -1;
-  for (int v = beg; v < end; ++v) {
-    const float w = from_p ? P.prob(v) : fmaxf(P.prob(v) - Q.prob(v), 0.f);
+  chunk([&](int v, float r, float pv) {
+    const float w = from_p ? pv : r;
     if (w > 0.f) last = v;
     acc += w;
     if (cand == INT_MAX && acc > target && w > 0.f) cand = v;
-  }
+  });
   int tok = block_min_int(cand, S.ired);
   if (tok == INT_MAX) tok = -block_min_int(-last, S.ired);
   return tok;
