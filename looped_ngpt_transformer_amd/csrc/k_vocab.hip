@@ -64,7 +64,14 @@ struct SampleLds {
   uint32_t prefix;
   float above;
   int jsel;
+  float tgt, cumsel;   // the selection's target; the chosen token's running mass
+  int selcnt, ncand;   // tokens under the chosen digits; candidates collected
+  float b0sum[16];     // the first pass's digit masses and counts, kept for the next
+  int b0cnt[16];       // selection over the same row
 };
+// At most this many tokens left under the chosen digits: collect them, sort them in LDS
+// (e descending, id ascending) and finish with one fixed-order scan.
+constexpr int CAND = 2 * ST;
 
 __device__ __forceinline__ float block_max16(float v, float* red) {
   v = wave_max(v);
@@ -131,48 +138,89 @@ __device__ __forceinline__ void row_for(const float* L, int n, F&& f) {
   }
 }
 
+// Prefix sums of one float per thread in thread order (fixed order): returns the inclusive
+// sum, *excl the exclusive one (the same additions minus this thread's).
+__device__ __forceinline__ float block_scan_f(float v, float* red, float* excl) {
+  const int lane = threadIdx.x & (WAVE - 1), w = threadIdx.x / WAVE;
+  float x = v;
+#pragma unroll
+  for (int d = 1; d < WAVE; d <<= 1) {
+    const float y = __shfl_up(x, d, WAVE);
+    if (lane >= d) x += y;
+  }
+  const float xe = __shfl_up(x, 1, WAVE);
+  __syncthreads();
+  if (lane == WAVE - 1) red[w] = x;
+  __syncthreads();
+  float off = 0.f;
+  for (int i = 0; i < w; ++i) off += red[i];
+  *excl = lane ? off + xe : off;
+  return off + x;
+}
+
 // First token of the sorted order whose inclusive running mass reaches (incl) or
 // exceeds (!incl) target; if rounding leaves the target beyond the mass, the last token
 // of the order. Returns the token and sets cum to its inclusive running mass.
-__device__ int select_token(SampleLds& S, const RowView& R, float target, bool incl, float* cum) {
+// frac >= 0: the target is frac times the row's total mass (taken from the first pass's
+// digit masses, summed high digit first). reuse0: the previous selection ran over the
+// same row; its first pass is taken from LDS instead of being recomputed.
+__device__ int select_token(SampleLds& S, const RowView& R, float target, bool incl, float* cum,
+                            float frac = -1.f, bool reuse0 = false) {
   const int t = threadIdx.x, lane = t & (WAVE - 1), w = t / WAVE;
   uint32_t prefix = 0;
   float above = 0.f;  // mass of the tokens whose key lies above the digits chosen so far
   for (int pass = 0; pass < 8; ++pass) {
     const int sh = 28 - 4 * pass;
+    if (!(pass == 0 && reuse0)) {
 #pragma unroll
-    for (int d = 0; d < 16; ++d) {
-      S.bins[d][t] = 0.f;
-      S.cnt[d][t] = 0;
-    }
-    row_for(R.L, R.V, [&](int, float l) {
-      const float e = R.ew(l);
-      const uint32_t key = __float_as_uint(e);
-      if (pass == 0 || (key >> (sh + 4)) == prefix) {
-        const int d = (key >> sh) & 15;
-        S.bins[d][t] += e;
-        S.cnt[d][t] += 1;
+      for (int d = 0; d < 16; ++d) {
+        S.bins[d][t] = 0.f;
+        S.cnt[d][t] = 0;
       }
-    });
-    __syncthreads();
-    {  // wave w sums digit w over the threads, lane j taking threads j, j + 64, ...
-      float v = 0.f;
-      int c = 0;
+      row_for(R.L, R.V, [&](int, float l) {
+        const float e = R.ew(l);
+        const uint32_t key = __float_as_uint(e);
+        if (pass == 0 || (key >> (sh + 4)) == prefix) {
+          const int d = (key >> sh) & 15;
+          S.bins[d][t] += e;
+          S.cnt[d][t] += 1;
+        }
+      });
+      __syncthreads();
+      {  // wave w sums digit w over the threads, lane j taking threads j, j + 64, ...
+        float v = 0.f;
+        int c = 0;
 #pragma unroll
-      for (int j = 0; j < ST / WAVE; ++j) {
-        v += S.bins[w][j * WAVE + lane];
-        c += S.cnt[w][j * WAVE + lane];
-      }
-      v = wave_sum(v);
+        for (int j = 0; j < ST / WAVE; ++j) {
+          v += S.bins[w][j * WAVE + lane];
+          c += S.cnt[w][j * WAVE + lane];
+        }
+        v = wave_sum(v);
 #pragma unroll
-      for (int o = 32; o >= 1; o >>= 1) c += __shfl_xor(c, o, WAVE);
-      if (lane == 0) {
-        S.binsum[w] = v;
-        S.bincnt[w] = c;
+        for (int o = 32; o >= 1; o >>= 1) c += __shfl_xor(c, o, WAVE);
+        if (lane == 0) {
+          S.binsum[w] = v;
+          S.bincnt[w] = c;
+          if (pass == 0) {
+            S.b0sum[w] = v;
+            S.b0cnt[w] = c;
+          }
+        }
       }
+    } else if (t < 16) {
+      S.binsum[t] = S.b0sum[t];
+      S.bincnt[t] = S.b0cnt[t];
     }
     __syncthreads();
     if (t == 0) {
+      if (pass == 0) {
+        if (frac >= 0.f) {
+          float total = 0.f;
+          for (int d = 15; d >= 0; --d) total += S.binsum[d];
+          target = frac * total;
+        }
+        S.tgt = target;
+      }
       float acc = above, acc_last = above;
       int sel = -1, last = -1;
       for (int d = 15; d >= 0; --d) {
@@ -192,11 +240,76 @@ __device__ int select_token(SampleLds& S, const RowView& R, float target, bool i
       }
       S.prefix = (prefix << 4) | (uint32_t)sel;
       S.above = acc;
+      S.selcnt = S.bincnt[sel];
     }
     __syncthreads();
     prefix = S.prefix;
     above = S.above;
+    target = S.tgt;
+    const int n = S.selcnt;
     __syncthreads();
+    if (pass < 7 && n <= CAND) {
+      // few tokens left under these digits: collect (e, id), sort, scan
+      float* ce = &S.bins[0][0];        // CAND floats (bins[0], bins[1])
+      int* cid = (int*)&S.bins[2][0];   // CAND ints (bins[2], bins[3])
+      if (t == 0) S.ncand = 0;
+      __syncthreads();
+      row_for(R.L, R.V, [&](int i, float l) {
+        const float e = R.ew(l);
+        if ((__float_as_uint(e) >> sh) == prefix) {
+          const int k = atomicAdd(&S.ncand, 1);
+          if (k < CAND) {
+            ce[k] = e;
+            cid[k] = i;
+          }
+        }
+      });
+      __syncthreads();
+      int np2 = 1;
+      while (np2 < n) np2 <<= 1;
+      for (int k = n + t; k < np2; k += ST) {
+        ce[k] = -1.f;
+        cid[k] = INT_MAX;
+      }
+      __syncthreads();
+      // bitonic sort into the sorted order: e descending, equal e by lower id
+      for (int size = 2; size <= np2; size <<= 1)
+        for (int stride = size >> 1; stride > 0; stride >>= 1) {
+          for (int k = t; k < np2 / 2; k += ST) {
+            const int i = 2 * stride * (k / stride) + k % stride, j = i + stride;
+            const float ea = ce[i], eb = ce[j];
+            const int ia = cid[i], ib = cid[j];
+            const bool a_first = ea > eb || (ea == eb && ia < ib);
+            if (a_first != ((i & size) == 0)) {
+              ce[i] = eb;
+              ce[j] = ea;
+              cid[i] = ib;
+              cid[j] = ia;
+            }
+          }
+          __syncthreads();
+        }
+      // running mass in that order, two candidates per thread
+      const int i0 = 2 * t, i1 = 2 * t + 1;
+      const float e0 = i0 < n ? ce[i0] : 0.f, e1 = i1 < n ? ce[i1] : 0.f;
+      float excl;
+      block_scan_f(e0 + e1, S.red, &excl);
+      const float c0 = above + (excl + e0), c1 = above + ((excl + e0) + e1);
+      int hit = INT_MAX;
+      if (i0 < n && (incl ? c0 >= target : c0 > target)) hit = i0;
+      else if (i1 < n && (incl ? c1 >= target : c1 > target)) hit = i1;
+      int first = block_min_int(hit, S.ired);
+      if (first == INT_MAX) first = n - 1;
+      if (t == first / 2) {
+        S.jsel = cid[first];
+        S.cumsel = (first & 1) ? c1 : c0;
+      }
+      __syncthreads();
+      const int tok = S.jsel;
+      *cum = S.cumsel;
+      __syncthreads();
+      return tok;
+    }
   }
   // the tokens whose key is exactly `prefix`: their count (the last digit's count), the
   // first j whose running mass above + (j + 1) e* meets the target (else the last one)
@@ -251,15 +364,12 @@ __global__ __launch_bounds__(ST) void k_sample_top_p(const float* logits, int64_
   float m = -INFINITY;
   row_for(R.L, V, [&](int, float l) { m = fmaxf(m, l); });
   R.mz = block_max16(m, S.red) * R.c;
-  float s = 0.f;
-  row_for(R.L, V, [&](int, float l) { s += R.ew(l); });
-  const float total = block_sum<ST / WAVE>(s, S.red);
   // nucleus: the first token whose running mass reaches top_p of the total
   float mass;
-  const int cut = select_token(S, R, top_p * total, true, &mass);
+  const int cut = select_token(S, R, 0.f, true, &mass, top_p);
   // the draw: the first token whose running mass exceeds u times the nucleus mass
   float cum;
-  int tok = select_token(S, R, u[blockIdx.x] * mass, false, &cum);
+  int tok = select_token(S, R, u[blockIdx.x] * mass, false, &cum, -1.f, true);
   // rounding may not place the draw after the cut: order (e descending, id ascending)
   if (t == 0) {
     const float ec = R.e(cut), et = R.e(tok);
@@ -284,10 +394,7 @@ struct Processed {
     float m = -INFINITY;
     row_for(L, V, [&](int, float l) { m = fmaxf(m, l); });
     R.mz = block_max16(m, S.red) * R.c;
-    float s = 0.f;
-    row_for(L, V, [&](int, float l) { s += R.ew(l); });
-    const float total = block_sum<ST / WAVE>(s, S.red);
-    cut = select_token(S, R, top_p * total, true, &mass);
+    cut = select_token(S, R, 0.f, true, &mass, top_p);
     ecut = R.e(cut);
   }
   __device__ float prob_l(int v, float l) const {  // l = the row's logit of token v
@@ -297,26 +404,6 @@ struct Processed {
   }
   __device__ float prob(int v) const { return prob_l(v, R.L[v]); }
 };
-
-// Prefix sums of one float per thread in thread order (fixed order): returns the inclusive
-// sum, *excl the exclusive one (the same additions minus this thread's).
-__device__ __forceinline__ float block_scan_f(float v, float* red, float* excl) {
-  const int lane = threadIdx.x & (WAVE - 1), w = threadIdx.x / WAVE;
-  float x = v;
-#pragma unroll
-  for (int d = 1; d < WAVE; d <<= 1) {
-    const float y = __shfl_up(x, d, WAVE);
-    if (lane >= d) x += y;
-  }
-  const float xe = __shfl_up(x, 1, WAVE);
-  __syncthreads();
-  if (lane == WAVE - 1) red[w] = x;
-  __syncthreads();
-  float off = 0.f;
-  for (int i = 0; i < w; ++i) off += red[i];
-  *excl = lane ? off + xe : off;
-  return off + x;
-}
 
 // The token u draws from max(0, p - q) renormalised, by inverse CDF over increasing ids
 // (from p itself if the residual is empty). Thread t owns the ids [t C, t C + C).
@@ -395,7 +482,7 @@ __global__ __launch_bounds__(ST) void k_spec_accept(int gamma, int V, const floa
   P.init(S, T, V, inv_t, top_p);
   if (j == gamma) {  // all accepted: the verifying model's next token
     float cum;
-    int tok = select_token(S, P.R, us * P.mass, false, &cum);
+    int tok = select_token(S, P.R, us * P.mass, false, &cum, -1.f, true);
     if (t == 0) {
       const float et = P.R.e(tok);
       if (et < P.ecut || (et == P.ecut && tok > P.cut)) tok = P.cut;
