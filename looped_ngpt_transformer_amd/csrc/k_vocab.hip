@@ -123,17 +123,17 @@ struct RowView {
 // SU loads in flight per thread: a pass over the row is bound by how many L2 requests
 // are outstanding, not by the arithmetic.
 constexpr int SU = 16;
-template <typename F>
+template <int U = SU, typename F>
 __device__ __forceinline__ void row_for(const float* L, int n, F&& f) {
-  for (int i0 = threadIdx.x; i0 < n; i0 += ST * SU) {
-    float v[SU];
+  for (int i0 = threadIdx.x; i0 < n; i0 += ST * U) {
+    float v[U];
 #pragma unroll
-    for (int u = 0; u < SU; ++u) {
+    for (int u = 0; u < U; ++u) {
       const int i = i0 + u * ST;
       v[u] = i < n ? L[i] : 0.f;
     }
 #pragma unroll
-    for (int u = 0; u < SU; ++u)
+    for (int u = 0; u < U; ++u)
       if (i0 + u * ST < n) f(i0 + u * ST, v[u]);
   }
 }
@@ -164,6 +164,8 @@ __device__ __forceinline__ float block_scan_f(float v, float* red, float* excl) 
 // frac >= 0: the target is frac times the row's total mass (taken from the first pass's
 // digit masses, summed high digit first). reuse0: the previous selection ran over the
 // same row; its first pass is taken from LDS instead of being recomputed.
+// U: loads in flight per thread in each pass.
+template <int U = SU>
 __device__ int select_token(SampleLds& S, const RowView& R, float target, bool incl, float* cum,
                             float frac = -1.f, bool reuse0 = false) {
   const int t = threadIdx.x, lane = t & (WAVE - 1), w = t / WAVE;
@@ -177,7 +179,7 @@ __device__ int select_token(SampleLds& S, const RowView& R, float target, bool i
         S.bins[d][t] = 0.f;
         S.cnt[d][t] = 0;
       }
-      row_for(R.L, R.V, [&](int, float l) {
+      row_for<U>(R.L, R.V, [&](int, float l) {
         const float e = R.ew(l);
         const uint32_t key = __float_as_uint(e);
         if (pass == 0 || (key >> (sh + 4)) == prefix) {
@@ -254,7 +256,7 @@ __device__ int select_token(SampleLds& S, const RowView& R, float target, bool i
       int* cid = (int*)&S.bins[2][0];   // CAND ints (bins[2], bins[3])
       if (t == 0) S.ncand = 0;
       __syncthreads();
-      row_for(R.L, R.V, [&](int i, float l) {
+      row_for<U>(R.L, R.V, [&](int i, float l) {
         const float e = R.ew(l);
         if ((__float_as_uint(e) >> sh) == prefix) {
           const int k = atomicAdd(&S.ncand, 1);
@@ -332,7 +334,7 @@ __device__ int select_token(SampleLds& S, const RowView& R, float target, bool i
   int tok;
   if (n_tied == 1) {
     int mine = INT_MAX;
-    row_for(R.L, R.V, [&](int i, float l) {
+    row_for<U>(R.L, R.V, [&](int i, float l) {
       if (__float_as_uint(R.ew(l)) == prefix) mine = i;
     });
     tok = block_min_int(mine, S.ired);
@@ -343,7 +345,7 @@ __device__ int select_token(SampleLds& S, const RowView& R, float target, bool i
     while (hi - lo > 1) {
       const int mid = (lo + hi) / 2;
       int n = 0;
-      row_for(R.L, mid, [&](int, float l) { n += __float_as_uint(R.ew(l)) == prefix; });
+      row_for<U>(R.L, mid, [&](int, float l) { n += __float_as_uint(R.ew(l)) == prefix; });
       if (block_sum_int(n, S.ired) <= jsel) lo = mid;
       else hi = mid;
     }
@@ -354,7 +356,7 @@ __device__ int select_token(SampleLds& S, const RowView& R, float target, bool i
 }
 
 __global__ __launch_bounds__(ST) void k_sample_top_p(const float* logits, int64_t ld, int V, float inv_t,
-                                                     float top_p, const float* u, int32_t* out) {
+                                                     float top_p, const float* u, int32_t* out, int out_stride) {
   __shared__ SampleLds S;
   const int t = threadIdx.x;
   RowView R;
@@ -374,7 +376,7 @@ __global__ __launch_bounds__(ST) void k_sample_top_p(const float* logits, int64_
   if (t == 0) {
     const float ec = R.e(cut), et = R.e(tok);
     if (et < ec || (et == ec && tok > cut)) tok = cut;
-    out[blockIdx.x] = tok;
+    out[(size_t)blockIdx.x * out_stride] = tok;
   }
 }
 
@@ -386,15 +388,16 @@ struct Processed {
   RowView R;
   int cut;
   float ecut, mass;
+  template <int U = SU>
   __device__ void init(SampleLds& S, const float* L, int V, float inv_t, float top_p) {
     const int t = threadIdx.x;
     R.L = L;
     R.V = V;
     R.c = inv_t * 1.4426950408889634f;
     float m = -INFINITY;
-    row_for(L, V, [&](int, float l) { m = fmaxf(m, l); });
+    row_for<U>(L, V, [&](int, float l) { m = fmaxf(m, l); });
     R.mz = block_max16(m, S.red) * R.c;
-    cut = select_token(S, R, 0.f, true, &mass, top_p);
+    cut = select_token<U>(S, R, 0.f, true, &mass, top_p);
     ecut = R.e(cut);
   }
   __device__ float prob_l(int v, float l) const {  // l = the row's logit of token v
@@ -456,14 +459,14 @@ __device__ int residual_draw(SampleLds& S, const Processed& P, const Processed& 
   return tok;
 }
 
-// One work-group per (sequence b, position j); draft rows, tokens and acceptance draws
-// are position-major ([gamma, n]), the verifying rows sequence-major ([n, gamma + 1]).
-// For j < gamma the draft token x_j is
-// accepted when u_accept < p_j(x_j) / q_j(x_j), else the group draws the residual token
-// with u_sample and lowers n_out[b] to j + 1 (an atomic minimum: the first rejection
-// wins); group j = gamma draws the token that follows if all are accepted. Every group
-// writes out[b, j]; n_out[b] starts at gamma + 1 (k_fill_n). The groups of later
-// positions do their work whether or not an earlier one rejects.
+// One work-group per (sequence b, position j < gamma); draft rows, tokens and acceptance
+// draws are position-major ([gamma, n]), the verifying rows sequence-major
+// ([n, gamma + 1]). The draft token x_j is accepted when u_accept < p_j(x_j) / q_j(x_j),
+// else the group draws the residual token with u_sample and lowers n_out[b] to j + 1 (an
+// atomic minimum: the first rejection wins). Every group writes out[b, j]; n_out[b]
+// starts at gamma + 1 (k_fill_n), and the token that follows a fully accepted block is
+// the top-p sampler's on the verifier's last row (k_sample_top_p, launched beside). The
+// groups of later positions do their work whether or not an earlier one rejects.
 __global__ void k_fill_n(int32_t* n_out, int n, int v) {
   const int i = blockIdx.x * blockDim.x + threadIdx.x;
   if (i < n) n_out[i] = v;
@@ -475,24 +478,17 @@ __global__ __launch_bounds__(ST) void k_spec_accept(int gamma, int V, const floa
                                                     const float* u_smp, int32_t* out, int32_t* n_out) {
   __shared__ SampleLds S;
   const int b = blockIdx.x, j = blockIdx.y, t = threadIdx.x;
-  const float* T = target + ((size_t)b * (gamma + 1) + j) * ld_t;
-  const float us = u_smp[b];
-  int32_t* o = out + (size_t)b * (gamma + 1) + j;
-  Processed P;
-  P.init(S, T, V, inv_t, top_p);
-  if (j == gamma) {  // all accepted: the verifying model's next token
-    float cum;
-    int tok = select_token(S, P.R, us * P.mass, false, &cum, -1.f, true);
-    if (t == 0) {
-      const float et = P.R.e(tok);
-      if (et < P.ecut || (et == P.ecut && tok > P.cut)) tok = P.cut;
-      *o = tok;
-    }
-    return;
-  }
-  Processed Q;
   const size_t dj = (size_t)j * gridDim.x + b;  // draft side: position-major
-  Q.init(S, draft + dj * ld_d, V, inv_t, top_p);
+  // the verifier's row, then the draft's, through one copy of the code (registers)
+  Processed P, Q;
+#pragma nounroll
+  for (int which = 0; which < 2; ++which) {
+    Processed X;
+    X.init<8>(S, which ? draft + dj * ld_d : target + ((size_t)b * (gamma + 1) + j) * ld_t, V, inv_t, top_p);
+    if (which) Q = X;
+    else P = X;
+  }
+  int32_t* o = out + (size_t)b * (gamma + 1) + j;
   const int x = dtok[dj];
   const bool valid = x >= 0 && x < V;
   const float q = valid ? Q.prob(x) : 0.f;
@@ -501,7 +497,7 @@ __global__ __launch_bounds__(ST) void k_spec_accept(int gamma, int V, const floa
     if (t == 0) *o = x;
     return;
   }
-  const int r = residual_draw(S, P, Q, V, us);
+  const int r = residual_draw(S, P, Q, V, u_smp[b]);
   if (t == 0) {
     *o = r;
     atomicMin(n_out + b, j + 1);
@@ -513,8 +509,11 @@ hipError_t launch_spec_accept(int n, int gamma, int64_t V, const float* draft, i
                               const float* u_smp, int32_t* out, int32_t* n_out, hipStream_t st) {
   if (n <= 0) return hipSuccess;
   hipLaunchKernelGGL(k_fill_n, dim3((n + 255) / 256), dim3(256), 0, st, n_out, n, gamma + 1);
-  hipLaunchKernelGGL(k_spec_accept, dim3(n, gamma + 1), dim3(ST), 0, st, gamma, (int)V, draft, ld_d, target, ld_t,
+  hipLaunchKernelGGL(k_spec_accept, dim3(n, gamma), dim3(ST), 0, st, gamma, (int)V, draft, ld_d, target, ld_t,
                      dtok, 1.0f / temperature, top_p, u_acc, u_smp, out, n_out);
+  // the token after a fully accepted block: row gamma of each sequence's verifying rows
+  hipLaunchKernelGGL(k_sample_top_p, dim3(n), dim3(ST), 0, st, target + (size_t)gamma * ld_t, ld_t * (gamma + 1),
+                     (int)V, 1.0f / temperature, top_p, u_smp, out + gamma, gamma + 1);
   return hipGetLastError();
 }
 
@@ -540,7 +539,7 @@ hipError_t launch_sample_top_p(const float* logits, int64_t ld, int n, int64_t V
                                const float* u, int32_t* out, hipStream_t st) {
   if (n <= 0) return hipSuccess;
   hipLaunchKernelGGL(k_sample_top_p, dim3(n), dim3(ST), 0, st, logits, ld, (int)V, 1.0f / temperature, top_p,
-                     u, out);
+                     u, out, 1);
   return hipGetLastError();
 }
 
