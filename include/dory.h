@@ -159,8 +159,8 @@ int dory_bind_workspace(dory_ctx* ctx, void* ws, size_t bytes);
 /* Loop count k of the context (1..max_loops, else INVALID_ARG), allowed any time. Each
  * sequence runs its own k (the paper summary's elastic depth: k chosen per request):
  * a per_loop sequence the k its KV cache was built for (the context's k when it was
- * created); a last_loop sequence the k set for it with dory_set_seq_loops, else the
- * context's k at each call. One prefill or decode call may mix sequences of different
+ * created) unless dory_set_seq_loops set a smaller one; a last_loop sequence the k set
+ * for it with dory_set_seq_loops, else the context's k at each call. One prefill or decode call may mix sequences of different
  * k: the recurrent block runs max k times, loop t on the rows of the sequences with
  * k >= t. */
 int dory_set_loops(dory_ctx* ctx, int k);
