@@ -304,3 +304,45 @@ def test_truncated_sequence_regrows_into_its_own_pages():
     torch.cuda.synchronize()
     assert D.dory_seq_len(rt.ctx, 0) == 130
     rt.close()
+
+
+@pytest.mark.parametrize("mode", ["per_loop", "last_loop"])
+def test_drafts_leave_no_trace_bf16(mode):
+    """bf16 stack (chunk attention by quads of rows): the verifying rows of a speculative
+    step equal, bit for bit, those of a second context that never drafted and prefills
+    the same chunk, and after the step both contexts give identical decode rows; so the
+    one-loop drafts, truncated away, leave nothing behind that a later call reads."""
+    from looped_ngpt_transformer_amd.runtime import DoryRuntime
+    from tests.gpu_helpers import gpu_weights
+    S = synth.config("P", n_in=1, n_rec=1, n_out=1, window=64)
+    k, V, n, gamma = 2, 4096, 2, 3
+    w = gpu_weights(S, 95)
+    tab = synth.make_vocab(S, V, 96, "cuda")
+    rts = []
+    for _ in range(2):
+        rt = DoryRuntime(S, w, max_loops=2, max_seqs=n, max_seq_len=160, max_rows=96, mode=mode, loops=k)
+        rt.bind_vocab(tab)
+        for b in range(n):
+            rt.prefill([b], [60 + 13 * b], synth.make_inputs(60 + 13 * b, S["hidden"], 97 + b, device="cuda"))
+        rts.append(rt)
+    a, ref = rts
+    cur = synth.make_ids(n, V, 99, "cuda")
+    ud = synth.make_draws(gamma * n, 100, device="cuda").view(gamma, n)
+    ua = synth.make_draws(gamma * n, 101, device="cuda").view(gamma, n)
+    us = synth.make_draws(n, 102, device="cuda")
+    out, n_out, info = a.spec_step(list(range(n)), cur, gamma, ud, ua, us)
+    chunk = torch.cat([cur.view(n, 1), info["drafts"].t()], dim=1).contiguous().view(-1)
+    y = ref.prefill(list(range(n)), [gamma + 1] * n, ref.embed(chunk))
+    target = ref.logits(y)
+    torch.cuda.synchronize()
+    assert torch.equal(target, info["target"])
+    L = [D.dory_seq_len(a.ctx, b) for b in range(n)]
+    for b in range(n):
+        D.dory_truncate_seq(ref.ctx, b, L[b])
+    nxt = torch.tensor([out[b, n_out[b] - 1] for b in range(n)], dtype=torch.int32, device="cuda")
+    ya = a.decode(list(range(n)), a.embed(nxt))
+    yr = ref.decode(list(range(n)), ref.embed(nxt))
+    torch.cuda.synchronize()
+    assert torch.equal(ya, yr)
+    for rt in rts:
+        rt.close()
