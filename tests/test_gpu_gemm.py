@@ -83,7 +83,8 @@ def test_swiglu(M):
     assert (out[M:].float() == SENTINEL).all()
 
 
-@pytest.mark.parametrize("M,N,K", [(1, 6400, 2560), (32, 2560, 4096), (100, 8192, 2560), (128, 2560, 2560)])
+@pytest.mark.parametrize("M,N,K", [(1, 6400, 2560), (32, 2560, 4096), (100, 8192, 2560), (128, 2560, 2560),
+                                   (160, 6400, 2560), (256, 2560, 4096)])
 def test_split_k_bf16(M, N, K):
     A, B = operands(M, N, K, 4)
     S = D.dory_test_gemm(A, B, D.EPI_PARTIAL, None, M=M)
@@ -100,7 +101,8 @@ def dequant_mxfp8(codes, scales):
     return w * torch.exp2(e).repeat_interleave(32, dim=1)
 
 
-@pytest.mark.parametrize("M,N,K", [(1, 6400, 2560), (32, 2560, 4096), (128, 8192, 2560), (70, 2560, 2560)])
+@pytest.mark.parametrize("M,N,K", [(1, 6400, 2560), (32, 2560, 4096), (128, 8192, 2560), (70, 2560, 2560),
+                                   (200, 2560, 2560)])
 def test_split_k_mxfp8(M, N, K):
     A, B = operands(M, N, K, 5)
     codes = torch.empty((N, K), dtype=torch.uint8, device="cuda")
@@ -137,7 +139,8 @@ def nvfp4_operands(N, K, seed):
     return codes.cuda(), scales.cuda(), gs.cuda(), W
 
 
-@pytest.mark.parametrize("M,N,K", [(1, 6400, 2560), (32, 2560, 4096), (100, 8192, 2560), (128, 2560, 2560)])
+@pytest.mark.parametrize("M,N,K", [(1, 6400, 2560), (32, 2560, 4096), (100, 8192, 2560), (128, 2560, 2560),
+                                   (160, 6400, 2560), (256, 2560, 4096)])
 def test_split_k_nvfp4(M, N, K):
     A, _ = operands(M, 64, K, 7)
     codes, scales, gs, W = nvfp4_operands(N, K, 8)
