@@ -57,6 +57,8 @@ def parse():
     ap.add_argument("--warmup", type=int, default=2)
     ap.add_argument("--workload", default="P", choices=["P", "D", "Q", "N", "L", "T", "G", "S"])
     ap.add_argument("--gamma", type=int, default=4, help="speculative draft length (S)")
+    ap.add_argument("--reuse", action="store_true",
+                    help="S: verification starts at loop 2 from the drafts' activations")
     ap.add_argument("--k", type=int, default=None)
     ap.add_argument("--ks", default=None, help="comma list of loop counts to measure too")
     ap.add_argument("--mode", default=None, choices=["per_loop", "last_loop"])
@@ -372,7 +374,7 @@ def bench_spec(args, torch, synth, D, DoryRuntime):
         if s == warm:
             torch.cuda.synchronize()
             t0 = time.perf_counter()
-        out, n_out, _ = rt.spec_step(ids, cur, gamma, UD[s], UA[s], US[s])
+        out, n_out, _ = rt.spec_step(ids, cur, gamma, UD[s], UA[s], US[s], reuse=args.reuse)
         cur = torch.tensor([int(out[b, n_out[b] - 1]) for b in ids], dtype=torch.int32, device="cuda")
         if s >= warm:
             emitted += int(n_out.sum())
@@ -438,7 +440,8 @@ def bench_spec(args, torch, synth, D, DoryRuntime):
         "ms_per_step": round(dt * 1e3, 3), "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
         "dtype": "bf16", "data": "synthetic (seeded random weights, seeded per_loop KV context, seeded draws)",
         "config": {"workload": WORKLOAD_TEXT["S"], "batch": batch, "context": ctx_len, "loops": k,
-                   "gamma": gamma, "kv_mode": "per_loop", "weights": shape["weight_format"]},
+                   "gamma": gamma, "kv_mode": "per_loop", "weights": shape["weight_format"],
+                   "verify": "from loop 2 on the drafts' activations" if args.reuse else "recomputed"},
         "spec": {"accepted_per_step": round(accepted / steps / batch, 3),
                  "emitted_per_step": round(emitted / steps / batch, 3),
                  "autoregressive_k_tokens_per_s": round(ar_tps, 2),

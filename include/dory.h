@@ -298,6 +298,22 @@ int dory_test_gemm(void* stream, const void* A, int lda, const void* B, const ui
 int dory_quantize_mxfp8(void* stream, const void* w, int w_dtype, int64_t rows,
                         int64_t cols, uint8_t* codes, uint8_t* scales);
 
+/* Activation reuse for self-speculative decoding (arXiv summary §6.2: verification reuses
+ * what the draft computed). Both set one-shot options of the next dory_prefill or
+ * dory_decode_step call on ctx (that call consumes them whatever its outcome).
+ * dory_capture_states: every sequence of that call must run one loop (INVALID_ARG
+ * otherwise); it writes each row's input-block output x and first-loop state s_1 to
+ * x_out and s1_out (device float [rows, H], the call's row order); with
+ * skip_output_block the output block is not run and y_out is not written.
+ * dory_resume_states: every sequence of that call must run two loops or more; the call
+ * takes x and s_1 of its rows from x_in and s1_in (device float [rows, H], the call's row
+ * order), runs neither the input block nor loop 1 (their cache entries for these
+ * positions must already hold what a pass over them wrote: a draft at one loop), and
+ * starts at loop 2 from N(s_1 + x); x_in of the call itself is not read. Buffers must
+ * stay valid until the call's work on its stream is done. */
+int dory_capture_states(dory_ctx* ctx, float* x_out, float* s1_out, int skip_output_block);
+int dory_resume_states(dory_ctx* ctx, const float* x_in, const float* s1_in);
+
 /* Self-speculative decoding's acceptance step (paper summary and arXiv summary §6.2: draft
  * gamma tokens with one loop, verify with k loops, rejection sampling keeps the k-loop
  * distribution). n sequences, V = vocab:

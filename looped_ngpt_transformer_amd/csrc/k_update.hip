@@ -244,6 +244,41 @@ __global__ __launch_bounds__(256) void k_scatter_rows(const float* s, const int3
     y[(size_t)rows[i / H] * H + i % H] = s[i];
 }
 
+// Verification that reuses a draft's activations (self-speculative decoding, arXiv
+// summary §6.2): x and the first loop's state s_1 of each row come from the draft pass;
+// the state entering loop 2 is u_2 = N(s_1 + x). One block per row; rows[r] names the
+// caller's row of internal row r (null: the same).
+template <typename SB>
+__global__ __launch_bounds__(256) void k_resume_state(const float* x_in, const float* s1_in, const int32_t* rows,
+                                                      int H, float* x, float* s, SB* sb) {
+  __shared__ float red[4];
+  const size_t r = blockIdx.x;
+  const size_t src = (rows ? (size_t)rows[r] : r) * H;
+  float ss = 0.f;
+  for (int c = threadIdx.x; c < H; c += 256) {
+    const float v = s1_in[src + c] + x_in[src + c];
+    ss += v * v;
+  }
+  const float inv = inv_norm(block_sum<4>(ss, red));
+  for (int c = threadIdx.x; c < H; c += 256) {
+    const float xv = x_in[src + c];
+    const float v = (s1_in[src + c] + xv) * inv;
+    x[r * H + c] = xv;
+    s[r * H + c] = v;
+    st<SB>(sb, r * H + c, v);
+  }
+}
+
+hipError_t launch_resume_state(const float* x_in, const float* s1_in, const int32_t* rows, int M, int H, float* x,
+                               float* s, void* sb, int act, hipStream_t st) {
+  if (M <= 0) return hipSuccess;
+  if (act == ACT_F32)
+    hipLaunchKernelGGL(k_resume_state<float>, dim3(M), dim3(256), 0, st, x_in, s1_in, rows, H, x, s, (float*)sb);
+  else
+    hipLaunchKernelGGL(k_resume_state<bf16_t>, dim3(M), dim3(256), 0, st, x_in, s1_in, rows, H, x, s, (bf16_t*)sb);
+  return hipGetLastError();
+}
+
 hipError_t launch_scatter_rows(const float* s, const int32_t* rows, int M, int H, float* y, hipStream_t st) {
   const size_t n = (size_t)M * H;
   if (n == 0) return hipSuccess;

@@ -67,6 +67,10 @@ hipError_t launch_stage_input(const float* x_in, float* s, void* sb, int M, int 
                               hipStream_t st, const int32_t* rows = nullptr);
 // y[rows[r]] = s[r] for r < M (float rows of H)
 hipError_t launch_scatter_rows(const float* s, const int32_t* rows, int M, int H, float* y, hipStream_t st);
+// x = x_in, s = N(s1_in + x_in) (and its act copy sb) per row, from the caller's rows
+// (rows[r]: caller row of internal row r; null: the same)
+hipError_t launch_resume_state(const float* x_in, const float* s1_in, const int32_t* rows, int M, int H, float* x,
+                               float* s, void* sb, int act, hipStream_t st);
 
 // ------------------------------------------------------------ RoPE + QK norm + KV write
 struct KVLayout {

@@ -144,6 +144,12 @@ struct dory_ctx {
   std::vector<int32_t> pending;  // (flat table index, page) pairs
   std::string err;
   int64_t last_calls = 0;
+  // one-shot options of the next prefill / decode call (speculative activation reuse)
+  float* cap_x = nullptr;
+  float* cap_s1 = nullptr;
+  bool cap_skip_out = false;
+  const float* res_x = nullptr;
+  const float* res_s1 = nullptr;
   bool dev_ready = false;
   int32_t* stage[NSTAGE] = {};
   hipEvent_t ev[NSTAGE] = {};
@@ -391,6 +397,13 @@ struct CallPlan {
   int k_max = 1;
   std::vector<int> loop_rows, loop_tiles, loop_seqs, loop_quads;
   bool reordered = false;  // rows are not in the caller's order (row map in the metadata)
+  // activation reuse: capture x and s_1 (caller order), skip the output block; or start
+  // at loop 2 from given x and s_1
+  float* cap_x = nullptr;
+  float* cap_s1 = nullptr;
+  bool skip_out = false;
+  const float* res_x = nullptr;
+  const float* res_s1 = nullptr;
 };
 
 // Algorithmic attention work of one layer call: visible (query, key) pairs and the
@@ -652,21 +665,41 @@ int run_forward(dory_ctx* ctx, hipStream_t st, const CallPlan& P, const float* x
   const int R = c.max_rows;
   const int32_t* rowmap = P.reordered ? (const int32_t*)(ws + ctx->W.meta) + 2 * R + 4 * ctx->D.max_tiles + ROPE_INTS
                                       : nullptr;
-  {
+  const int H = ctx->D.H;
+  // rows of the workspace state (internal order) into a caller-order array
+  auto export_rows = [&](size_t off, float* dst, const char* what) -> int {
     Prof pr(ctx, st, DORY_KC_UPDATE);
-    HIPCHK(launch_stage_input(x_in, (float*)(ws + ctx->W.s), ws + ctx->W.sb, P.M, ctx->D.H, act, st, rowmap),
-           "stage_input");
-    pr.end(0, (double)P.M * ctx->D.H * (8.0 + ctx->D.esz));
-  }
+    if (rowmap)
+      HIPCHK(launch_scatter_rows((const float*)(ws + off), rowmap, P.M, H, dst, st), what);
+    else
+      HIPCHK(hipMemcpyAsync(dst, ws + off, (size_t)P.M * H * 4, hipMemcpyDeviceToDevice, st), what);
+    pr.end(0, (double)P.M * H * 8.0);
+    return DORY_OK;
+  };
   int64_t calls = 0;
   int r;
-  for (int l = 0; l < c.n_in; ++l) {
-    if ((r = run_layer(ctx, st, P, l, 0, l == c.n_in - 1 ? BND_SAVE_X : BND_NONE, nullptr))) return r;
-    ++calls;
+  if (P.res_x) {  // start at loop 2 from the given x and s_1
+    Prof pr(ctx, st, DORY_KC_UPDATE);
+    HIPCHK(launch_resume_state(P.res_x, P.res_s1, rowmap, P.M, H, (float*)(ws + ctx->W.x), (float*)(ws + ctx->W.s),
+                               ws + ctx->W.sb, act, st),
+           "resume state");
+    pr.end(0, (double)P.M * H * (16.0 + 8.0 + ctx->D.esz));
+  } else {
+    {
+      Prof pr(ctx, st, DORY_KC_UPDATE);
+      HIPCHK(launch_stage_input(x_in, (float*)(ws + ctx->W.s), ws + ctx->W.sb, P.M, H, act, st, rowmap),
+             "stage_input");
+      pr.end(0, (double)P.M * H * (8.0 + ctx->D.esz));
+    }
+    for (int l = 0; l < c.n_in; ++l) {
+      if ((r = run_layer(ctx, st, P, l, 0, l == c.n_in - 1 ? BND_SAVE_X : BND_NONE, nullptr))) return r;
+      ++calls;
+    }
+    if (P.cap_x && (r = export_rows(ctx->W.x, P.cap_x, "capture x"))) return r;
   }
   // loop t runs the recurrent block on the rows of the sequences with k >= t (a prefix);
   // rows whose sequence ends at loop t take the final boundary there
-  for (int t = 1; t <= P.k_max; ++t) {
+  for (int t = P.res_x ? 2 : 1; t <= P.k_max; ++t) {
     CallPlan Pt = P;
     Pt.M = P.loop_rows[t];
     Pt.n_tiles = P.loop_tiles[t];
@@ -680,6 +713,11 @@ int run_forward(dory_ctx* ctx, hipStream_t st, const CallPlan& P, const float* x
       if ((r = run_layer(ctx, st, Pt, l, slot, b, nullptr, next))) return r;
       ++calls;
     }
+    if (t == 1 && P.cap_s1 && (r = export_rows(ctx->W.s, P.cap_s1, "capture s1"))) return r;
+  }
+  if (P.skip_out) {
+    ctx->last_calls = calls;
+    return DORY_OK;
   }
   const int L = c.n_in + c.n_rec + c.n_out;
   for (int l = c.n_in + c.n_rec; l < L; ++l) {
@@ -707,6 +745,14 @@ int loops_of(const dory_ctx* ctx, const Seq& q) {
 int step(dory_ctx* ctx, hipStream_t st, int n, const int32_t* ids, const int32_t* n_new,
          const float* x_in, float* y_out, bool decode) {
   const dory_config& c = ctx->cfg;
+  float* const cap_x = ctx->cap_x;  // one-shot: consumed by this call whatever its outcome
+  float* const cap_s1 = ctx->cap_s1;
+  const bool skip_out = ctx->cap_skip_out;
+  const float* const res_x = ctx->res_x;
+  const float* const res_s1 = ctx->res_s1;
+  ctx->cap_x = ctx->cap_s1 = nullptr;
+  ctx->cap_skip_out = false;
+  ctx->res_x = ctx->res_s1 = nullptr;
   if (!bound(ctx)) return ctx->fail(DORY_ERR_STATE, "weights, KV pool and workspace must be bound");
   if (n < 1 || !ids || (!decode && !n_new) || !x_in || !y_out)
     return ctx->fail(DORY_ERR_INVALID_ARG, "null argument or n_seqs < 1");
@@ -772,7 +818,20 @@ int step(dory_ctx* ctx, hipStream_t st, int n, const int32_t* ids, const int32_t
     }
     std::stable_sort(order.begin(), order.end(), [&](int a, int b) { return kseq[a] > kseq[b]; });
   }
+  for (int i = 0; i < n; ++i) {
+    if (cap_x && kseq[i] != 1)
+      return ctx->fail(DORY_ERR_INVALID_ARG, "capture needs every sequence at one loop (sequence %d runs %d)", ids[i],
+                       kseq[i]);
+    if (res_x && kseq[i] < 2)
+      return ctx->fail(DORY_ERR_INVALID_ARG, "resume needs every sequence at two loops or more (sequence %d runs %d)",
+                       ids[i], kseq[i]);
+  }
   CallPlan P;
+  P.cap_x = cap_x;
+  P.cap_s1 = cap_s1;
+  P.skip_out = skip_out;
+  P.res_x = res_x;
+  P.res_s1 = res_s1;
   P.k_max = kseq[order[0]];
   P.loop_rows.assign(P.k_max + 2, 0);
   P.loop_tiles.assign(P.k_max + 2, 0);
@@ -994,6 +1053,23 @@ int dory_truncate_seq(dory_ctx* ctx, int32_t seq_id, int64_t len) {
   if (len < 1 || len > it->second.len)
     return ctx->fail(DORY_ERR_INVALID_ARG, "length %lld outside 1..%lld", (long long)len, (long long)it->second.len);
   it->second.len = len;  // the pages stay with the sequence; later positions are rewritten before use
+  return DORY_OK;
+}
+
+int dory_capture_states(dory_ctx* ctx, float* x_out, float* s1_out, int skip_output_block) {
+  if (!ctx) return DORY_ERR_INVALID_ARG;
+  if (!x_out || !s1_out) return ctx->fail(DORY_ERR_INVALID_ARG, "null capture buffer");
+  ctx->cap_x = x_out;
+  ctx->cap_s1 = s1_out;
+  ctx->cap_skip_out = skip_output_block != 0;
+  return DORY_OK;
+}
+
+int dory_resume_states(dory_ctx* ctx, const float* x_in, const float* s1_in) {
+  if (!ctx) return DORY_ERR_INVALID_ARG;
+  if (!x_in || !s1_in) return ctx->fail(DORY_ERR_INVALID_ARG, "null state buffer");
+  ctx->res_x = x_in;
+  ctx->res_s1 = s1_in;
   return DORY_OK;
 }
 

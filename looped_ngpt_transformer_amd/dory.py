@@ -80,6 +80,8 @@ _SIGS = {
     "dory_set_seq_loops": (C.c_int, [_P, C.c_int32, C.c_int]),
     "dory_seq_loops": (C.c_int, [_P, C.c_int32, C.POINTER(C.c_int)]),
     "dory_truncate_seq": (C.c_int, [_P, C.c_int32, C.c_int64]),
+    "dory_capture_states": (C.c_int, [_P, _P, _P, C.c_int]),
+    "dory_resume_states": (C.c_int, [_P, _P, _P]),
     "dory_spec_accept": (C.c_int, [_P, C.c_int, C.c_int, C.c_int64, _P, C.c_int64, _P, C.c_int64, _P, C.c_float,
                                    C.c_float, _P, _P, _P, _P]),
     "dory_set_kv_mode": (C.c_int, [_P, C.c_int]),
@@ -224,6 +226,14 @@ def dory_seq_loops(ctx, seq_id: int) -> int:
 
 def dory_truncate_seq(ctx, seq_id: int, length: int):
     _check(lib().dory_truncate_seq(ctx, seq_id, length), ctx)
+
+
+def dory_capture_states(ctx, x_out, s1_out, skip_output_block=False):
+    _check(lib().dory_capture_states(ctx, _ptr(x_out), _ptr(s1_out), int(bool(skip_output_block))), ctx)
+
+
+def dory_resume_states(ctx, x_in, s1_in):
+    _check(lib().dory_resume_states(ctx, _ptr(x_in), _ptr(s1_in)), ctx)
 
 
 def dory_spec_accept(draft_logits, target_logits, draft_tokens, u_accept, u_sample, tokens, n_out,

@@ -102,12 +102,16 @@ class DoryRuntime:
         D.dory_sample_top_p(logits, u, tokens, temperature=temperature, top_p=top_p)
         return tokens
 
-    def spec_step(self, seq_ids, cur, gamma, u_draft, u_accept, u_sample, temperature=1.0, top_p=0.95):
+    def spec_step(self, seq_ids, cur, gamma, u_draft, u_accept, u_sample, temperature=1.0, top_p=0.95,
+                  reuse=False):
         """One self-speculative step for live sequences seq_ids whose next input token is
         cur [n] (int32, device): draft gamma tokens with one loop, truncate the drafts
         away, verify cur and the drafts as one chunk at the sequences' own loop counts,
         accept by rejection sampling, and keep the cache entries of the emitted positions.
         u_draft, u_accept [gamma, n], u_sample [n]: uniform draws (device float).
+        reuse: the drafts keep their input-block output and first-loop state, one more
+        one-loop pass (no output block) gives them for the last draft token, and the
+        verifying chunk starts at loop 2 from them (sequences must verify at k >= 2).
         Returns tokens [n, gamma + 1] and n_out [n] on the host, and the device tensors
         used: draft logits [gamma * n, V], draft tokens [gamma, n], verifying logits
         [n * (gamma + 1), V]."""
@@ -119,18 +123,33 @@ class DoryRuntime:
         V = self.vocab
         draft = torch.empty((gamma * n, V), dtype=torch.float32, device=self.device)
         xt = torch.empty((gamma, n), dtype=torch.int32, device=self.device)
+        H = self.shape["hidden"]
+        if reuse:
+            XC = torch.empty((gamma + 1, n, H), dtype=torch.float32, device=self.device)
+            SC = torch.empty_like(XC)
         tok = cur
         try:
             for j in range(gamma):
+                if reuse:
+                    D.dory_capture_states(ctx, XC[j], SC[j])
                 y = self.decode(seq_ids, self.embed(tok))
                 lg = self.logits(y, out=draft[j * n:(j + 1) * n])
                 tok = self.sample(lg, u_draft[j], xt[j], temperature, top_p)
+            if reuse:  # the last draft token through the input block and loop 1 only
+                D.dory_capture_states(ctx, XC[gamma], SC[gamma], skip_output_block=True)
+                self.decode(seq_ids, self.embed(tok))
         finally:
             for s, l0 in zip(seq_ids, L0):
                 D.dory_set_seq_loops(ctx, s, 0)
                 D.dory_truncate_seq(ctx, s, l0)
-        chunk = torch.cat([cur.view(n, 1), xt.t()], dim=1).contiguous().view(-1)
-        y = self.prefill(seq_ids, [gamma + 1] * n, self.embed(chunk))
+        if reuse:
+            X = XC.transpose(0, 1).contiguous().view(n * (gamma + 1), H)
+            S1 = SC.transpose(0, 1).contiguous().view(n * (gamma + 1), H)
+            D.dory_resume_states(ctx, X, S1)
+            y = self.prefill(seq_ids, [gamma + 1] * n, X)
+        else:
+            chunk = torch.cat([cur.view(n, 1), xt.t()], dim=1).contiguous().view(-1)
+            y = self.prefill(seq_ids, [gamma + 1] * n, self.embed(chunk))
         target = self.logits(y)
         out = torch.empty((n, gamma + 1), dtype=torch.int32, device=self.device)
         n_out = torch.empty((n,), dtype=torch.int32, device=self.device)

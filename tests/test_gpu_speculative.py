@@ -231,12 +231,14 @@ def oracle_spec(cfg, W, seq, tab, cur, gamma, ud, ua, us, k, mode, gpu, b, n, T=
     return out
 
 
+@pytest.mark.parametrize("reuse", [False, True], ids=["recompute", "reuse"])
 @pytest.mark.parametrize("mode", ["per_loop", "last_loop"])
-def test_spec_step_matches_oracle(mode):
+def test_spec_step_matches_oracle(mode, reuse):
     """Two speculative steps (gamma = 3, drafts with one loop, verification with two) for
     three sequences of an fp32 stack, against the oracle model run the same way: draft
     rows, draft tokens, verifying rows, accepted count and emitted tokens, and the cache
-    left behind (the next step's rows read it)."""
+    left behind (the next step's rows read it). With reuse the verifying chunk starts at
+    loop 2 from the drafts' x and s_1; the oracle recomputes everything."""
     from looped_ngpt_transformer_amd.runtime import DoryRuntime
     from tests.gpu_helpers import gpu_weights, oracle_model
     from tests.helpers import to_np
@@ -261,7 +263,7 @@ def test_spec_step_matches_oracle(mode):
         ua = synth.make_draws(gamma * n, 88, step, device="cuda").view(gamma, n)
         us = synth.make_draws(n, 89, step, device="cuda")
         lens = [D.dory_seq_len(rt.ctx, b) for b in range(n)]
-        out, n_out, info = rt.spec_step(list(range(n)), cur, gamma, ud, ua, us)
+        out, n_out, info = rt.spec_step(list(range(n)), cur, gamma, ud, ua, us, reuse=reuse)
         gpu = {"draft": info["draft"].cpu().double().numpy(), "drafts": info["drafts"].cpu().numpy(),
                "target": info["target"].cpu().double().numpy()}
         udn, uan, usn = ud.cpu().numpy(), ua.cpu().numpy(), us.cpu().numpy()
@@ -346,3 +348,27 @@ def test_drafts_leave_no_trace_bf16(mode):
     assert torch.equal(ya, yr)
     for rt in rts:
         rt.close()
+
+
+def test_capture_and_resume_arguments():
+    """The one-shot options check the loop counts of the call that consumes them, and are
+    consumed even when it fails."""
+    from looped_ngpt_transformer_amd.runtime import DoryRuntime
+    from tests.gpu_helpers import gpu_weights
+    S = synth.config("T")
+    rt = DoryRuntime(S, gpu_weights(S, 103), max_loops=2, max_seqs=1, max_seq_len=64, max_rows=32, loops=2)
+    X = synth.make_inputs(4, S["hidden"], 104, device="cuda")
+    buf = torch.empty_like(X)
+    D.dory_capture_states(rt.ctx, buf, buf)
+    with pytest.raises(D.DoryError) as e:                 # k = 2: no capture
+        rt.prefill([0], [4], X)
+    assert e.value.code == D.ERR_INVALID_ARG
+    rt.prefill([0], [4], X)                              # option consumed
+    D.dory_set_seq_loops(rt.ctx, 0, 1)
+    D.dory_resume_states(rt.ctx, X, X)
+    with pytest.raises(D.DoryError) as e:                 # k = 1: no resume
+        rt.decode([0], X[:1])
+    assert e.value.code == D.ERR_INVALID_ARG
+    with pytest.raises(D.DoryError):
+        D.dory_capture_states(rt.ctx, None, buf)
+    rt.close()
