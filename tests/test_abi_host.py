@@ -265,3 +265,23 @@ def test_sampler_rejects_bad_arguments(n, vocab, ld, temp, top_p):
     rc = D.lib().dory_sample_top_p(None, n, vocab, fake, ld, temp, top_p, fake, fake)
     assert rc == D.ERR_INVALID_ARG
     assert "sampling" in D.lib().dory_last_error(None).decode()
+
+
+def test_capture_and_resume_options():
+    """The activation-reuse options are host bookkeeping: null buffers are refused, others
+    are taken without touching them, and a call on an unbound context still fails as a
+    state error with the options set (that the options are consumed is checked on the GPU)."""
+    ctx = D.dory_create(cfg())
+    buf = 4096   # an address never dereferenced: no call here reaches device work
+    with pytest.raises(D.DoryError) as e:
+        D._check(D.lib().dory_capture_states(ctx, None, buf, 0), ctx)
+    assert e.value.code == D.ERR_INVALID_ARG
+    with pytest.raises(D.DoryError) as e:
+        D._check(D.lib().dory_resume_states(ctx, buf, None), ctx)
+    assert e.value.code == D.ERR_INVALID_ARG
+    D._check(D.lib().dory_capture_states(ctx, buf, buf, 1), ctx)
+    D._check(D.lib().dory_resume_states(ctx, buf, buf), ctx)
+    with pytest.raises(D.DoryError) as e:
+        D._check(D.lib().dory_prefill(ctx, None, 1, None, None, None, None), ctx)
+    assert e.value.code == D.ERR_STATE
+    D.dory_destroy(ctx)
