@@ -57,8 +57,9 @@ def parse():
     ap.add_argument("--warmup", type=int, default=2)
     ap.add_argument("--workload", default="P", choices=["P", "D", "Q", "N", "L", "T", "G", "S"])
     ap.add_argument("--gamma", type=int, default=4, help="speculative draft length (S)")
-    ap.add_argument("--reuse", action="store_true",
-                    help="S: verification starts at loop 2 from the drafts' activations")
+    ap.add_argument("--no-reuse", dest="reuse", action="store_false",
+                    help="S: recompute the drafted positions' input block and loop 1 in the verifying "
+                         "chunk instead of starting at loop 2 from the drafts' activations")
     ap.add_argument("--k", type=int, default=None)
     ap.add_argument("--ks", default=None, help="comma list of loop counts to measure too")
     ap.add_argument("--mode", default=None, choices=["per_loop", "last_loop"])
