@@ -372,3 +372,38 @@ def test_capture_and_resume_arguments():
     with pytest.raises(D.DoryError):
         D.dory_capture_states(rt.ctx, None, buf)
     rt.close()
+
+
+@pytest.mark.parametrize("mode", ["per_loop", "last_loop"])
+def test_captured_states_match_the_oracle(mode):
+    """dory_capture_states on a one-loop decode of two sequences (fp32 stack): the captured
+    x is the oracle's input-block output and s_1 its first-loop state, row by row."""
+    from looped_ngpt_transformer_amd.runtime import DoryRuntime
+    from oracle import dory_oracle as O
+    from tests.gpu_helpers import gpu_weights, oracle_model
+    from tests.helpers import to_np
+    S = synth.config("T")
+    w = gpu_weights(S, 105)
+    rt = DoryRuntime(S, w, max_loops=2, max_seqs=2, max_seq_len=64, max_rows=32, mode=mode, loops=2)
+    cfg, W = oracle_model(S, w)
+    seqs = [O.Sequence(cfg) for _ in range(2)]
+    for b in range(2):
+        X = synth.make_inputs(9 + 5 * b, S["hidden"], 106 + b, device="cuda")
+        rt.prefill([b], [X.shape[0]], X)
+        O.prefill(cfg, W, seqs[b], to_np(X), 2, mode)
+        D.dory_set_seq_loops(rt.ctx, b, 1)
+    x = synth.make_inputs(2, S["hidden"], 108, device="cuda")
+    xc, sc = torch.empty_like(x), torch.empty_like(x)
+    D.dory_capture_states(rt.ctx, xc, sc)
+    y = rt.decode([0, 1], x)
+    torch.cuda.synchronize()
+    for b in range(2):
+        states = []
+        pos = np.array([seqs[b].length])
+        want_y = O.forward_chunk(cfg, W, to_np(x[b:b + 1]), pos, 1, mode, seqs[b].kv, states=states)
+        want_x = [v for tag, l, v in states if tag == "in"][-1]
+        want_s1 = [v for tag, t, v in states if tag == "s" and t == 1][0]
+        assert np.abs(xc[b].cpu().double().numpy() - want_x[0]).max() <= 1e-5
+        assert np.abs(sc[b].cpu().double().numpy() - want_s1[0]).max() <= 1e-5
+        assert np.abs(y[b].cpu().double().numpy() - want_y[0]).max() <= 1e-5
+    rt.close()
