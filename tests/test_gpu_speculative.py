@@ -310,6 +310,19 @@ def test_truncated_sequence_regrows_into_its_own_pages():
 
 @pytest.mark.parametrize("mode", ["per_loop", "last_loop"])
 def test_drafts_leave_no_trace_bf16(mode):
+    check_against_undrafted_context(mode, reuse=False)
+
+
+@pytest.mark.parametrize("mode", ["per_loop", "last_loop"])
+def test_reused_activations_bf16(mode):
+    """The same with the verifying chunk resumed at loop 2 from the drafts' x and s_1: the
+    drafts' first-loop states come from one-row decode GEMMs instead of the chunk's, so
+    the verifying logits agree with the undrafted context's to bf16 rounding (cosine of
+    every row >= 0.9999) rather than bit for bit."""
+    check_against_undrafted_context(mode, reuse=True)
+
+
+def check_against_undrafted_context(mode, reuse):
     """bf16 stack (chunk attention by quads of rows): the verifying rows of a speculative
     step equal, bit for bit, those of a second context that never drafted and prefills
     the same chunk, and after the step both contexts give identical decode rows; so the
@@ -332,11 +345,17 @@ def test_drafts_leave_no_trace_bf16(mode):
     ud = synth.make_draws(gamma * n, 100, device="cuda").view(gamma, n)
     ua = synth.make_draws(gamma * n, 101, device="cuda").view(gamma, n)
     us = synth.make_draws(n, 102, device="cuda")
-    out, n_out, info = a.spec_step(list(range(n)), cur, gamma, ud, ua, us)
+    out, n_out, info = a.spec_step(list(range(n)), cur, gamma, ud, ua, us, reuse=reuse)
     chunk = torch.cat([cur.view(n, 1), info["drafts"].t()], dim=1).contiguous().view(-1)
     y = ref.prefill(list(range(n)), [gamma + 1] * n, ref.embed(chunk))
     target = ref.logits(y)
     torch.cuda.synchronize()
+    if reuse:
+        cos = torch.nn.functional.cosine_similarity(target.double(), info["target"].double(), dim=1)
+        assert cos.min().item() >= 0.9999, f"min cosine {cos.min().item():.6f}"
+        for rt in rts:
+            rt.close()
+        return
     assert torch.equal(target, info["target"])
     L = [D.dory_seq_len(a.ctx, b) for b in range(n)]
     for b in range(n):
