@@ -247,21 +247,57 @@ def test_bf16_decode_over_seeded_context(mode, sharp):
 
 @pytest.mark.parametrize("mode", ["per_loop", "last_loop"])
 def test_bf16_prefill_over_long_seeded_context(mode):
-    """A 100-row chunk continuing a seeded 4300-token context: the full-attention layer's
-    query tiles read 69 KV pages, past the 64 page ids a wave holds at once."""
+    """A 300-row chunk (above the 256 rows that go by split-K tiles and quads of rows, so
+    the MFMA prefill attention runs) continuing a seeded 4300-token context: the
+    full-attention layer's query tiles read up to 73 KV pages, past the 64 page ids a wave
+    holds at once."""
     from oracle import dory_oracle as O
     from tests.helpers import to_np
     S = PSMALL
     k = 2
     w = sharpen(gpu_weights(S, 8))
-    rt = DoryRuntime(S, w, max_loops=2, max_seqs=1, max_seq_len=4480, max_rows=256, mode=mode, loops=k)
+    rt = DoryRuntime(S, w, max_loops=2, max_seqs=1, max_seq_len=4672, max_rows=320, mode=mode, loops=k)
     stores = _seed_kv(rt, S, {0: 4300}, k, mode)
     cfg, W = oracle_model(S, w)
-    X = xin(S, 100, 70)
-    y = rt.prefill([0], [100], X)
+    X = xin(S, 300, 70)
+    y = rt.prefill([0], [300], X)
     torch.cuda.synchronize()
     ref = O.prefill(cfg, W, stores[0], to_np(X), k, mode)
     compare(y.cpu().double().numpy(), ref, S, "chunk over 4300 tokens")
+    rt.close()
+
+
+@pytest.mark.parametrize("mode", ["per_loop", "last_loop"])
+def test_bf16_short_chunks_over_seeded_contexts(mode):
+    """Verifying-chunk shapes: chunks of 5, 3 and 8 rows continuing seeded 4300-, 1500-
+    and 900-token contexts in one call, whose attention goes by quads of rows (a ragged
+    last quad, key ranges across many pages and the sliding window's edge), then a decode
+    step."""
+    from oracle import dory_oracle as O
+    from tests.helpers import to_np
+    S = PSMALL
+    k = 2
+    w = sharpen(gpu_weights(S, 8))
+    rt = DoryRuntime(S, w, max_loops=2, max_seqs=3, max_seq_len=4480, max_rows=64, mode=mode, loops=k)
+    stores = _seed_kv(rt, S, {0: 4300, 1: 1500, 2: 900}, k, mode)
+    cfg, W = oracle_model(S, w)
+    rows = {0: 5, 1: 3, 2: 8}
+    Xs = {sid: xin(S, rows[sid], 80 + sid) for sid in rows}
+    order = [2, 0, 1]
+    y = rt.prefill(order, [rows[i] for i in order], torch.cat([Xs[i] for i in order]))
+    torch.cuda.synchronize()
+    got = y.cpu().double().numpy()
+    r0 = 0
+    for sid in order:
+        ref = O.prefill(cfg, W, stores[sid], to_np(Xs[sid]), k, mode)
+        compare(got[r0:r0 + rows[sid]], ref, S, f"chunk seq {sid}")
+        r0 += rows[sid]
+    X = xin(S, 3, 90)
+    y = rt.decode([0, 1, 2], X)
+    torch.cuda.synchronize()
+    got = y.cpu().double().numpy()
+    for j in range(3):
+        compare(got[j:j + 1], O.prefill(cfg, W, stores[j], to_np(X[j:j + 1]), k, mode), S, f"decode seq {j}")
     rt.close()
 
 
