@@ -56,13 +56,14 @@ NSMALL = dict(synth.config("P", n_in=1, n_rec=1, n_out=1, window=64), hidden=512
 
 @pytest.mark.parametrize("mode", ["per_loop", "last_loop"])
 def test_nvfp4_small_forward(mode):
-    """A 150-row prefill (the large-M GEMMs on matrices expanded to bf16) and two decode
-    steps (the 4-bit split-K tiles), with undamped rates."""
+    """A 300-row prefill (the large-M GEMMs on matrices expanded to bf16), a 100-row chunk
+    and two decode steps (the 4-bit split-K tiles), with undamped rates."""
     S = NSMALL
-    sched = [("prefill", [(0, xin(S, 150, 41))]),
+    sched = [("prefill", [(0, xin(S, 300, 41))]),
+             ("prefill", [(0, xin(S, 100, 44))]),
              ("decode", [(0, xin(S, 1, 42))]),
              ("decode", [(0, xin(S, 1, 43))])]
-    _run_case(S, 2, mode, sched, max_rows=256, max_seq_len=256, max_seqs=1, sharp=True)
+    _run_case(S, 2, mode, sched, max_rows=320, max_seq_len=512, max_seqs=1, sharp=True)
 
 
 @pytest.mark.parametrize("batch", [1, 40, 128])

@@ -75,7 +75,7 @@ def test_tiny_fp32_chunked_and_batched(mode):
 @pytest.mark.parametrize("mode", ["per_loop", "last_loop"])
 @pytest.mark.parametrize("k", [1, 2])
 def test_bf16_small_prefill_then_decode(k, mode):
-    """bf16, Dory layer shape: a 150-row prefill (MFMA tiles + ragged tail), two decode
+    """bf16, Dory layer shape: a 150-row prefill (split-K tiles, attention by quads of rows), two decode
     steps on two sequences, then a chunk continuing one of them."""
     S = PSMALL
     sched = [("prefill", [(0, xin(S, 150, 11))]),
@@ -159,10 +159,13 @@ def test_mxfp8_quantiser_bit_exact():
 
 
 def test_mxfp8_small_forward():
+    """MXFP8: a 300-row prefill (the large-M dequantising GEMMs), a 150-row chunk (the
+    split-K MXFP8 tiles and attention by quads of rows) and a decode step."""
     S = dict(PSMALL, weight_format="mxfp8")
-    sched = [("prefill", [(0, xin(S, 150, 31))]),
+    sched = [("prefill", [(0, xin(S, 300, 31))]),
+             ("prefill", [(0, xin(S, 150, 33))]),
              ("decode", [(0, xin(S, 1, 32))])]
-    _run_case(S, 2, "last_loop", sched, max_rows=256, max_seq_len=256, max_seqs=1)
+    _run_case(S, 2, "last_loop", sched, max_rows=320, max_seq_len=512, max_seqs=1)
 
 
 @pytest.mark.parametrize("batch", [40, 128])

@@ -49,9 +49,9 @@ def test_embedding(shape):
     rt.close()
 
 
-@pytest.mark.parametrize("n", [1, 32, 200])
+@pytest.mark.parametrize("n", [1, 32, 200, 300])
 def test_logits_bf16(n):
-    rt, tab = runtime(PSMALL, 8192)
+    rt, tab = runtime(PSMALL, 8192, max_rows=320)
     s = synth.make_inputs(n, PSMALL["hidden"], 31, device="cuda")
     lg = rt.logits(s)
     torch.cuda.synchronize()
