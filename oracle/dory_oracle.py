@@ -29,8 +29,8 @@ Normalized-GPT"; page names below are those of the five web pages):
   "memory-friendly KV cache").
 
 Readings where the pages are silent are listed in the design notes and restated at
-each function. No tiling, fusion or reordering: the visible-key set of every query is
-built explicitly and softmax is taken over it.
+each function. No tiling, fusion or reordering: every query's visible keys are marked
+explicitly (causal, and the window on sliding layers) and softmax runs over them alone.
 """
 from __future__ import annotations
 
@@ -248,15 +248,23 @@ def attention(cfg: Config, lw: LayerWeights, s: np.ndarray, pos: np.ndarray, lay
         k = lw.s_qk * l2n(k)
     kv.write(layer, slot, pos, k, v)
 
+    # Keys any row of the chunk may see: [lo, hi]. Row t sees key j iff j <= p_t and,
+    # on sliding layers, p_t - j < W; the other logits of its row are -inf, so softmax
+    # gives them weight exactly 0 and runs over the visible set alone.
+    p = pos.astype(np.int64)
+    lo = 0 if full else max(0, int(p.min()) - cfg.window + 1)
+    hi = int(p.max())
+    K, V = kv.read(layer, slot, lo, hi)
+    j = np.arange(lo, hi + 1)
+    visible = j[None, :] <= p[:, None]
+    if not full:
+        visible &= p[:, None] - j[None, :] < cfg.window
     out = np.zeros((T, Hq, d))
-    for t in range(T):
-        p = int(pos[t])
-        lo = 0 if full else max(0, p - cfg.window + 1)
-        K, V = kv.read(layer, slot, lo, p)            # visible keys j in [lo, p]
-        for h in range(Hq):
-            hk = (h * Hkv) // Hq                      # GQA: query head -> KV head
-            a = softmax(cfg.attn_scale * (K[:, hk, :] @ q[t, h]))
-            out[t, h] = a @ V[:, hk, :]
+    for h in range(Hq):
+        hk = (h * Hkv) // Hq                          # GQA: query head -> KV head
+        logits = cfg.attn_scale * (q[:, h, :] @ K[:, hk, :].T)   # [T, keys]
+        a = softmax(np.where(visible, logits, -np.inf))
+        out[:, h] = a @ V[:, hk, :]
     o = out.reshape(T, Hq * d)
     if cfg.attn_gate:
         o = sigmoid(s @ lw.wg.T) * o
