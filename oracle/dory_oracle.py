@@ -59,7 +59,11 @@ class Config:
     attn_scale: float = 1.0
     qk_norm: int = 1
     attn_gate: int = 1
-    pre_proj_norm: bool = True  # the extra norms before W_o and W_down
+    # the extra norms before W_o and W_down: True = over the whole row (the reading
+    # taken), False = none, "per_head" = the attention output normalised per head (an
+    # alternative reading of the same passage; the MLP activation has no heads and keeps
+    # the row norm)
+    pre_proj_norm: bool | str = True
 
     @staticmethod
     def from_dict(d: dict) -> "Config":
@@ -268,7 +272,9 @@ def attention(cfg: Config, lw: LayerWeights, s: np.ndarray, pos: np.ndarray, lay
     o = out.reshape(T, Hq * d)
     if cfg.attn_gate:
         o = sigmoid(s @ lw.wg.T) * o
-    if cfg.pre_proj_norm:
+    if cfg.pre_proj_norm == "per_head":
+        o = l2n(o.reshape(T, Hq, d)).reshape(T, Hq * d)
+    elif cfg.pre_proj_norm:
         o = l2n(o)
     return o @ lw.wo.T
 

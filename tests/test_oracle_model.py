@@ -208,6 +208,23 @@ def test_zero_rate_is_identity(mode):
         np.testing.assert_allclose(y, X, atol=1e-14)
 
 
+def test_per_head_pre_output_norm_is_another_model():
+    """The arXiv summary (section 2) says the gated attention output is L2-normalised
+    before the output projection, without saying over what. The row-wise reading (taken)
+    only scales the projection's output, which the update normalises away; a per-head
+    norm, like the QK norm, reweights the heads and changes the result well beyond the
+    bf16 tolerance, so the two readings are distinguishable and the choice is visible."""
+    cfg, W, _ = model(SMALL, seed=34)
+    X = inputs(SMALL, 6, seed=13)
+    row = _run(cfg, W, [X], 2, "per_loop")
+    ph = copy.copy(cfg)
+    ph.pre_proj_norm = "per_head"
+    head = _run(ph, W, [X], 2, "per_loop")
+    assert np.all(np.abs(np.sum(head * head, axis=1) - 1.0) < 1e-12)   # still unit states
+    cos = np.sum(row * head, axis=1)
+    assert cos.min() < 0.9995, cos.min()          # beyond the bf16 parity tolerance
+
+
 def test_pre_projection_norms_are_scale_only():
     cfg, W, _ = model(SMALL, seed=33)
     X = inputs(SMALL, 6, seed=12)
