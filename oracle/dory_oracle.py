@@ -28,6 +28,9 @@ Normalized-GPT"; page names below are those of the five web pages):
   see the final-loop entries of prior tokens (arXiv summary 6.1; model-card digest,
   "memory-friendly KV cache").
 
+Arrays keep the type of the inputs: the oracle is float64 (its callers pass float64);
+the benchmark also times it once on float32 inputs.
+
 Readings where the pages are silent are listed in the design notes and restated at
 each function. No tiling, fusion or reordering: every query's visible keys are marked
 explicitly (causal, and the window on sliding layers) and softmax runs over them alone.
@@ -136,8 +139,8 @@ def rope(x: np.ndarray, pos: np.ndarray, theta: float) -> np.ndarray:
     half = d // 2
     freq = theta ** (-2.0 * np.arange(half, dtype=np.float64) / d)
     ang = pos.astype(np.float64)[:, None] * freq[None, :]          # [T, half]
-    c = np.cos(ang)[:, None, :]
-    s = np.sin(ang)[:, None, :]
+    c = np.cos(ang).astype(x.dtype)[:, None, :]
+    s = np.sin(ang).astype(x.dtype)[:, None, :]
     x1, x2 = x[..., :half], x[..., half:]
     return np.concatenate([x1 * c - x2 * s, x1 * s + x2 * c], axis=-1)
 
@@ -191,18 +194,18 @@ class KVStore:
         self.v: dict = {}
         self.valid: dict = {}
 
-    def _ensure(self, key, hi):
+    def _ensure(self, key, hi, dtype=np.float64):
         if key not in self.k:
             cap = max(64, hi)
             shp = (cap, self.cfg.n_kv_heads, self.cfg.head_dim)
-            self.k[key] = np.zeros(shp)
-            self.v[key] = np.zeros(shp)
+            self.k[key] = np.zeros(shp, dtype=dtype)
+            self.v[key] = np.zeros(shp, dtype=dtype)
             self.valid[key] = np.zeros(cap, dtype=bool)
         cap = self.k[key].shape[0]
         if hi > cap:
             new = max(hi, 2 * cap)
             for d in (self.k, self.v):
-                a = np.zeros((new,) + d[key].shape[1:])
+                a = np.zeros((new,) + d[key].shape[1:], dtype=d[key].dtype)
                 a[:cap] = d[key]
                 d[key] = a
             vv = np.zeros(new, dtype=bool)
@@ -211,7 +214,7 @@ class KVStore:
 
     def write(self, layer: int, slot: int, pos: np.ndarray, k: np.ndarray, v: np.ndarray):
         key = (layer, slot)
-        self._ensure(key, int(pos.max()) + 1)
+        self._ensure(key, int(pos.max()) + 1, k.dtype)
         self.k[key][pos] = k
         self.v[key][pos] = v
         self.valid[key][pos] = True
@@ -263,7 +266,7 @@ def attention(cfg: Config, lw: LayerWeights, s: np.ndarray, pos: np.ndarray, lay
     visible = j[None, :] <= p[:, None]
     if not full:
         visible &= p[:, None] - j[None, :] < cfg.window
-    out = np.zeros((T, Hq, d))
+    out = np.zeros((T, Hq, d), dtype=q.dtype)
     for h in range(Hq):
         hk = (h * Hkv) // Hq                          # GQA: query head -> KV head
         logits = cfg.attn_scale * (q[:, h, :] @ K[:, hk, :].T)   # [T, keys]
@@ -315,7 +318,8 @@ def forward_chunk(cfg: Config, weights: list, X: np.ndarray, pos: np.ndarray, k:
     unit-norm checks.
     """
     assert mode in ("per_loop", "last_loop") and k >= 1
-    s = np.asarray(X, dtype=np.float64)
+    s = np.asarray(X)
+    s = s.astype(np.result_type(s.dtype, np.float32))  # float64 in, float64 out
     pos = np.asarray(pos)
     rec0 = cfg.n_in
     out0 = cfg.n_in + cfg.n_rec
@@ -348,7 +352,8 @@ def forward_chunk(cfg: Config, weights: list, X: np.ndarray, pos: np.ndarray, k:
 def forward_plain(cfg: Config, weights: list, X: np.ndarray, pos: np.ndarray,
                   kv: KVStore) -> np.ndarray:
     """A plain, non-looped stack: every physical layer once, slot 0, no boundary ops."""
-    s = np.asarray(X, dtype=np.float64)
+    s = np.asarray(X)
+    s = s.astype(np.result_type(s.dtype, np.float32))  # float64 in, float64 out
     for l in range(cfg.n_layers):
         s = layer(cfg, weights[l], s, np.asarray(pos), l, kv, 0)
     return s
