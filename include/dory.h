@@ -14,15 +14,23 @@
  * overwritten every loop (last_loop) — arXiv §6.1, model-card digest §2.
  *
  * Conventions for every call:
- *  - Return value: DORY_OK or a negative DORY_ERR_* code. On error nothing has been
- *    launched and the context is unchanged; dory_last_error() gives a message.
- *    DORY_ERR_HIP reports a failed HIP call (possibly from earlier asynchronous work).
+ *  - Return value: DORY_OK or a negative DORY_ERR_* code; dory_last_error() gives a
+ *    message. Every error but DORY_ERR_HIP is found before any device work, and the
+ *    context is unchanged. After DORY_ERR_HIP (a failed HIP call, possibly reporting
+ *    earlier asynchronous work) the context's sequences are as before the call
+ *    (lengths, pages, live set, page-table updates still to apply), but device work
+ *    enqueued before the failing step may still run: it can write the call's output
+ *    rows and cache entries at positions the sequences do not hold yet, which later
+ *    calls write again before any call reads them.
  *  - "device" pointers are HIP device memory owned by the caller; the library never
  *    allocates or frees device memory. "host" pointers are read during the call only.
  *  - `stream` is a hipStream_t passed as void* (NULL = the default stream). Device
  *    work is enqueued asynchronously on it; results are valid after the stream is
  *    synchronised. Host arrays may be reused as soon as a call returns.
- *  - One context is used from one host thread at a time.
+ *  - One context is used from one host thread at a time. Calls on one context may use
+ *    different streams: a call whose stream differs from the previous call's first
+ *    makes its stream wait for the previous call's device work (the workspace and page
+ *    tables are shared), so consecutive calls never overlap on the device.
  *  - Matrices are row-major. A weight W is [N_out, K_in] and a projection is
  *    y = s W^T.
  */
@@ -180,7 +188,11 @@ int dory_set_kv_mode(dory_ctx* ctx, int mode);
 int dory_get_kv_mode(const dory_ctx* ctx, int* mode);
 
 /*
- * Prefill: append n_new[i] tokens to sequence seq_ids[i] for i < n_seqs (host arrays).
+ * Prefill: the looped forward pass over new tokens (paper summary, core-method equation:
+ * input block once giving x, s_0 = x, u_t = N(s_{t-1} + x), s_t = N(F(u_t)) for t = 1..k,
+ * output block once; arXiv summary §3.2), writing each attention layer's cache entries
+ * for the new positions into the slot the KV mode gives (arXiv summary §6.1).
+ * Append n_new[i] tokens to sequence seq_ids[i] for i < n_seqs (host arrays).
  * A new id starts a sequence at position 0; a live id continues it (chunked prefill).
  * x_in  device float [sum n_new, H]: unit-norm input states, rows grouped by sequence
  *       in seq_ids order, positions increasing.
@@ -194,7 +206,10 @@ int dory_get_kv_mode(const dory_ctx* ctx, int* mode);
 int dory_prefill(dory_ctx* ctx, void* stream, int n_seqs, const int32_t* seq_ids,
                  const int32_t* n_new, const float* x_in, float* y_out);
 
-/* One decode step: one new token for each listed live sequence (a chunk of one row).
+/* One decode step: the same looped forward pass (paper summary, core method; arXiv
+ * summary §3.2 and §6.1) for one new token of each listed live sequence (a chunk of one
+ * row at position = the sequence's length), whose queries read the cached keys and
+ * values of all earlier positions (the sliding window's last W on sliding layers).
  * x_in, y_out device float [n_seqs, H]. Errors as prefill; unknown id -> INVALID_ARG. */
 int dory_decode_step(dory_ctx* ctx, void* stream, int n_seqs, const int32_t* seq_ids,
                      const float* x_in, float* y_out);
@@ -269,6 +284,13 @@ int dory_test_reserve(dory_ctx* ctx, int32_t seq_id, int32_t n_tokens);
  * the window ring. */
 int dory_test_fill_kv(dory_ctx* ctx, void* stream, int32_t seq_id, int layer, int slot,
                       int32_t pos0, int32_t n, const void* k, const void* v);
+
+/* Make the next dory_prefill / dory_decode_step on ctx fail with DORY_ERR_HIP after it
+ * has committed (sequences created and grown, pages taken) and before the step named by
+ * `at` enqueues anything: 0 = the upload of the call's metadata, n >= 1 = layer call n;
+ * -1 disarms. Consumed by the next call whatever its outcome. Test support for the error
+ * contract above; no device work fails. */
+int dory_test_inject_failure(dory_ctx* ctx, int at);
 
 /* One projection GEMM exactly as a layer call launches it (test support for the GEMM
  * kernels): C = A B^T, A [M, K] bf16 device rows with stride lda elements, B [N, K]

@@ -155,6 +155,14 @@ struct dory_ctx {
   hipEvent_t ev[NSTAGE] = {};
   int stage_i = 0;
   std::vector<int32_t> scratch;
+  // calls are ordered across streams: each call's device work ends with done_ev on its
+  // stream, and a call on another stream first waits for it (the workspace is shared)
+  hipEvent_t done_ev = nullptr;
+  hipStream_t last_st = nullptr;
+  bool have_last = false;
+  // test hook: fail the next prefill/decode call after it has committed (0: at the
+  // metadata upload; n >= 1: before layer call n), then disarm
+  int inject_at = -1;
   // tracing
   int prof = 0;  // bit mask of kernel classes being timed
   struct ProfRec { int kc; int ev; double flops, bytes; };
@@ -307,7 +315,15 @@ int64_t pages_to_grow(const dory_ctx* c, const Seq& q, int64_t len1) {
   return need;
 }
 
-void grow(dory_ctx* c, Seq& q, int64_t len1) {
+// One page a call took from the free list: enough to give it back (rollback).
+struct Taken {
+  int32_t id;
+  int stream;
+  int idx;
+  int32_t page;
+};
+
+void grow(dory_ctx* c, Seq& q, int64_t len1, std::vector<Taken>* journal = nullptr) {
   const int64_t len0 = q.len;
   for (int s = 0; s < c->D.n_streams; ++s) {
     if (!c->stream_used(q, s)) continue;
@@ -325,6 +341,7 @@ void grow(dory_ctx* c, Seq& q, int64_t len1) {
       if (tab[idx] < 0) {
         tab[idx] = c->free_pages.back();
         c->free_pages.pop_back();
+        if (journal) journal->push_back({q.id, s, idx, tab[idx]});
         const int64_t flat = ((int64_t)q.slot * c->D.n_streams + s) * c->D.tab_len + idx;
         c->pending.push_back((int32_t)flat);
         c->pending.push_back(tab[idx]);
@@ -348,7 +365,26 @@ int dev_init(dory_ctx* ctx) {
     HIPCHK(hipHostMalloc((void**)&ctx->stage[i], bytes, hipHostMallocDefault), "hipHostMalloc");
     HIPCHK(hipEventCreateWithFlags(&ctx->ev[i], hipEventDisableTiming), "hipEventCreate");
   }
+  HIPCHK(hipEventCreateWithFlags(&ctx->done_ev, hipEventDisableTiming), "hipEventCreate");
   ctx->dev_ready = true;
+  return DORY_OK;
+}
+
+// Start of a call's device work on st: wait for the previous call's work if it ran on
+// another stream.
+int enter(dory_ctx* ctx, hipStream_t st) {
+  int r = dev_init(ctx);
+  if (r) return r;
+  if (ctx->have_last && ctx->last_st != st) HIPCHK(hipStreamWaitEvent(st, ctx->done_ev, 0), "hipStreamWaitEvent");
+  return DORY_OK;
+}
+
+// End of a call's device work on st (also after a failure part-way: whatever was
+// enqueued is ordered before the next call).
+int leave(dory_ctx* ctx, hipStream_t st) {
+  HIPCHK(hipEventRecord(ctx->done_ev, st), "hipEventRecord");
+  ctx->last_st = st;
+  ctx->have_last = true;
   return DORY_OK;
 }
 
@@ -385,8 +421,37 @@ bool bound(dory_ctx* ctx) {
   return true;
 }
 
+// Host state a prefill/decode call changes when it commits.
+struct Journal {
+  std::vector<Taken> taken;                       // pages taken, in order
+  std::vector<std::pair<int32_t, int64_t>> lens;  // (id, length before) of live sequences
+  std::vector<int32_t> created;                   // ids the call created, in order
+  std::vector<int32_t> pending;                   // page-table deltas queued before the call
+};
+
+// Undo a committed call that failed before finishing: the pages go back to the free list
+// in reverse order (restoring it exactly), lengths are reset, new sequences are removed
+// and the page-table deltas queued before the call are queued again (re-applying one
+// only clears a page that holds no entry a sequence can read). The device table may
+// still hold entries of the returned pages; they sit past the sequences' lengths, are
+// never read, and are overwritten when the sequences grow into them again.
+void rollback(dory_ctx* ctx, Journal&& jr) {
+  for (auto it = jr.taken.rbegin(); it != jr.taken.rend(); ++it) {
+    ctx->seqs[it->id].pages[it->stream][it->idx] = -1;
+    ctx->free_pages.push_back(it->page);
+  }
+  for (auto& l : jr.lens) ctx->seqs[l.first].len = l.second;
+  for (auto it = jr.created.rbegin(); it != jr.created.rend(); ++it) {
+    auto q = ctx->seqs.find(*it);
+    ctx->free_slots.push_back(q->second.slot);
+    ctx->seqs.erase(q);
+  }
+  ctx->pending = std::move(jr.pending);
+}
+
 struct CallPlan {
   int M = 0;
+  int inject_at = -1;  // test hook: fail before layer call inject_at (>= 1)
   int max_pos = 0;
   int n_tiles = 0;
   int max_tile_rows = 0;
@@ -678,6 +743,10 @@ int run_forward(dory_ctx* ctx, hipStream_t st, const CallPlan& P, const float* x
   };
   int64_t calls = 0;
   int r;
+  auto injected = [&]() {
+    return P.inject_at == calls + 1 ? ctx->fail(DORY_ERR_HIP, "injected failure before layer call %lld", (long long)(calls + 1))
+                                    : DORY_OK;
+  };
   if (P.res_x) {  // start at loop 2 from the given x and s_1
     Prof pr(ctx, st, DORY_KC_UPDATE);
     HIPCHK(launch_resume_state(P.res_x, P.res_s1, rowmap, P.M, H, (float*)(ws + ctx->W.x), (float*)(ws + ctx->W.s),
@@ -692,7 +761,7 @@ int run_forward(dory_ctx* ctx, hipStream_t st, const CallPlan& P, const float* x
       pr.end(0, (double)P.M * H * (8.0 + ctx->D.esz));
     }
     for (int l = 0; l < c.n_in; ++l) {
-      if ((r = run_layer(ctx, st, P, l, 0, l == c.n_in - 1 ? BND_SAVE_X : BND_NONE, nullptr))) return r;
+      if ((r = injected()) || (r = run_layer(ctx, st, P, l, 0, l == c.n_in - 1 ? BND_SAVE_X : BND_NONE, nullptr))) return r;
       ++calls;
     }
     if (P.cap_x && (r = export_rows(ctx->W.x, P.cap_x, "capture x"))) return r;
@@ -710,7 +779,7 @@ int run_forward(dory_ctx* ctx, hipStream_t st, const CallPlan& P, const float* x
     for (int l = c.n_in; l < c.n_in + c.n_rec; ++l) {
       int b = BND_NONE;
       if (l == c.n_in + c.n_rec - 1) b = t < P.k_max ? BND_LOOP_CONTINUE : BND_LOOP_FINAL;
-      if ((r = run_layer(ctx, st, Pt, l, slot, b, nullptr, next))) return r;
+      if ((r = injected()) || (r = run_layer(ctx, st, Pt, l, slot, b, nullptr, next))) return r;
       ++calls;
     }
     if (t == 1 && P.cap_s1 && (r = export_rows(ctx->W.s, P.cap_s1, "capture s1"))) return r;
@@ -722,7 +791,7 @@ int run_forward(dory_ctx* ctx, hipStream_t st, const CallPlan& P, const float* x
   const int L = c.n_in + c.n_rec + c.n_out;
   for (int l = c.n_in + c.n_rec; l < L; ++l) {
     float* out = l == L - 1 && !P.reordered ? y_out : nullptr;
-    if ((r = run_layer(ctx, st, P, l, 0, BND_NONE, out))) return r;
+    if ((r = injected()) || (r = run_layer(ctx, st, P, l, 0, BND_NONE, out))) return r;
     ++calls;
   }
   if (P.reordered) {
@@ -788,8 +857,8 @@ int step(dory_ctx* ctx, hipStream_t st, int n, const int32_t* ids, const int32_t
   }
   if (need > (int64_t)ctx->free_pages.size())
     return ctx->fail(DORY_ERR_OUT_OF_KV, "need %lld KV pages, %zu free", (long long)need, ctx->free_pages.size());
-  int r = dev_init(ctx);
-  if (r) return r;
+  const int inject = ctx->inject_at;  // test hook, consumed by this call
+  ctx->inject_at = -1;
 
   // commit: create, grow, build row metadata
   std::vector<int32_t>& meta = ctx->scratch;
@@ -826,7 +895,13 @@ int step(dory_ctx* ctx, hipStream_t st, int n, const int32_t* ids, const int32_t
       return ctx->fail(DORY_ERR_INVALID_ARG, "resume needs every sequence at two loops or more (sequence %d runs %d)",
                        ids[i], kseq[i]);
   }
+  int r = enter(ctx, st);
+  if (r) return r;
+  // what the commit changes, so that a failure after it can be undone
+  Journal jr;
+  jr.pending = ctx->pending;
   CallPlan P;
+  P.inject_at = inject;
   P.cap_x = cap_x;
   P.cap_s1 = cap_s1;
   P.skip_out = skip_out;
@@ -851,11 +926,14 @@ int step(dory_ctx* ctx, hipStream_t st, int n, const int32_t* ids, const int32_t
       q.rec_slots = ctx->mode == DORY_KV_PER_LOOP ? ctx->k : 1;
       q.pages.assign(ctx->D.n_streams, {});
       it = ctx->seqs.emplace(ids[i], std::move(q)).first;
+      jr.created.push_back(ids[i]);
+    } else {
+      jr.lens.emplace_back(ids[i], it->second.len);
     }
     Seq& q = it->second;
     const int nn = decode ? 1 : n_new[i];
     const int64_t p0 = q.len;
-    grow(ctx, q, q.len + nn);
+    grow(ctx, q, q.len + nn, &jr.taken);
     for (int j = 0; j < nn; ++j) {
       meta[row + j] = (int32_t)(p0 + j);
       meta[R + row + j] = q.slot;
@@ -882,17 +960,87 @@ int step(dory_ctx* ctx, hipStream_t st, int n, const int32_t* ids, const int32_t
     }
   }
   P.M = row;
-  // deltas: whatever does not fit goes first in separate uploads
-  if ((r = flush_deltas(ctx, st, DELTA_CAP))) return r;
-  const size_t nd = ctx->pending.size() / 2;
-  meta.insert(meta.end(), ctx->pending.begin(), ctx->pending.end());
-  ctx->pending.clear();
-  if ((r = upload(ctx, st, meta.data(), meta.size()))) return r;
-  if (nd)
-    HIPCHK(launch_apply_deltas((int32_t*)(ctx->ws + ctx->W.table),
-                               (const int32_t*)(ctx->ws + ctx->W.meta) + 3 * R + 4 * ctx->D.max_tiles + ROPE_INTS,
-                               (int)nd, ctx->pool, ctx->D.page_bytes, st), "apply_deltas");
-  return run_forward(ctx, st, P, x_in, y_out);
+  r = [&]() -> int {
+    // deltas: whatever does not fit goes first in separate uploads
+    int rr;
+    if ((rr = flush_deltas(ctx, st, DELTA_CAP))) return rr;
+    const size_t nd = ctx->pending.size() / 2;
+    meta.insert(meta.end(), ctx->pending.begin(), ctx->pending.end());
+    ctx->pending.clear();
+    if (inject == 0) return ctx->fail(DORY_ERR_HIP, "injected failure at the metadata upload");
+    if ((rr = upload(ctx, st, meta.data(), meta.size()))) return rr;
+    if (nd)
+      HIPCHK(launch_apply_deltas((int32_t*)(ctx->ws + ctx->W.table),
+                                 (const int32_t*)(ctx->ws + ctx->W.meta) + 3 * R + 4 * ctx->D.max_tiles + ROPE_INTS,
+                                 (int)nd, ctx->pool, ctx->D.page_bytes, st), "apply_deltas");
+    return run_forward(ctx, st, P, x_in, y_out);
+  }();
+  if (r) rollback(ctx, std::move(jr));
+  const int rl = leave(ctx, st);
+  return r ? r : rl;
+}
+
+int logits_check(dory_ctx* ctx, int n, const float* states, float* logits) {
+  if (!ctx->vocab_bound) return ctx->fail(DORY_ERR_STATE, "vocabulary not bound");
+  if (n < 1 || n > ctx->cfg.max_rows || !states || !logits)
+    return ctx->fail(DORY_ERR_INVALID_ARG, "need 1 <= n <= max_rows and non-null states, logits");
+  return DORY_OK;
+}
+
+// split-K factor of the LM-head GEMM for n rows (1 in fp32 contexts and above the
+// split-K sizes)
+int logits_splits(const dory_ctx* ctx, int n) {
+  if (ctx->cfg.act_dtype == DORY_DTYPE_F32 || n > SKINNY_M) return 1;
+  return gemm_pick_splits(n, (int)ctx->vocab.vocab, ctx->D.H, W_BF16);
+}
+
+// The LM head: logits = s_z * (states . lm_head) over n rows. bf16 contexts stage the
+// states (float copy s_buf, bf16 copy sb_buf, n x H each) and, with splits > 1, take
+// fp32 split-K partials in part (splits x n x V) that the logit-scale kernel sums.
+int logits_run(dory_ctx* ctx, hipStream_t st, int n, const float* states, float* logits, float* s_buf, void* sb_buf,
+               float* part, int splits) {
+  const int H = ctx->D.H;
+  const int64_t V = ctx->vocab.vocab;
+  const bool f32 = ctx->cfg.act_dtype == DORY_DTYPE_F32;
+  GemmArgs g;
+  g.B = ctx->vocab.lm_head;
+  g.M = n;
+  g.N = (int)V;
+  g.K = H;
+  g.lda = H;
+  g.C = logits;
+  g.ldc = (int)V;
+  if (f32) {
+    g.A = states;
+    g.act = ACT_F32;
+    g.wfmt = W_F32;
+    g.epi = EPI_F32;
+  } else {
+    g.A = sb_buf;  // the states in the activation type, as the projections read them
+    g.act = ACT_BF16;
+    g.wfmt = W_BF16;
+    if (n <= SKINNY_M) {  // decode-sized: split-K streaming tiles
+      g.epi = EPI_PARTIAL;
+      g.splits = splits;
+      if (splits > 1) g.C = part;
+    } else {
+      g.epi = EPI_F32;
+    }
+    Prof ps(ctx, st, DORY_KC_UPDATE);
+    HIPCHK(launch_stage_input(states, s_buf, sb_buf, n, H, ACT_BF16, st), "LM-head input");
+    ps.end(0.0, (double)n * H * (4 + 4 + 2));
+  }
+  {
+    Prof pr(ctx, st, DORY_KC_VOCAB);
+    HIPCHK(launch_gemm(g, st), "LM-head GEMM");
+    pr.end(2.0 * n * (double)V * H, (double)V * H * ctx->D.esz + (double)n * H * ctx->D.esz + 4.0 * n * V * splits);
+  }
+  Prof pr(ctx, st, DORY_KC_VOCAB);
+  HIPCHK(launch_logit_scale(splits > 1 ? part : logits, splits, (size_t)n * V, logits, V, n, V, ctx->vocab.logit_scale,
+                            st),
+         "logit scale");
+  pr.end(0.0, 4.0 * n * V * (splits + 1) + 4.0 * V);
+  return DORY_OK;
 }
 
 }  // namespace
@@ -930,6 +1078,10 @@ int dory_destroy(dory_ctx* ctx) {
   for (auto e : ctx->pev) {
     (void)hipEventSynchronize(e);
     (void)hipEventDestroy(e);
+  }
+  if (ctx->done_ev) {
+    (void)hipEventSynchronize(ctx->done_ev);
+    (void)hipEventDestroy(ctx->done_ev);
   }
   for (int i = 0; i < NSTAGE; ++i) {
     if (ctx->ev[i]) {
@@ -1196,6 +1348,13 @@ int dory_test_reserve(dory_ctx* ctx, int32_t seq_id, int32_t n_tokens) {
   return DORY_OK;
 }
 
+int dory_test_inject_failure(dory_ctx* ctx, int at) {
+  if (!ctx) return DORY_ERR_INVALID_ARG;
+  if (at < -1) return ctx->fail(DORY_ERR_INVALID_ARG, "at must be >= -1");
+  ctx->inject_at = at;
+  return DORY_OK;
+}
+
 int dory_test_fill_kv(dory_ctx* ctx, void* stream, int32_t seq_id, int layer, int slot, int32_t pos0,
                       int32_t n, const void* k, const void* v) {
   if (!ctx) return DORY_ERR_INVALID_ARG;
@@ -1213,12 +1372,14 @@ int dory_test_fill_kv(dory_ctx* ctx, void* stream, int32_t seq_id, int layer, in
     if (pos0 < first_ok) return ctx->fail(DORY_ERR_INVALID_ARG, "position %d left the sliding-window ring", pos0);
   }
   hipStream_t st = (hipStream_t)stream;
-  int r = dev_init(ctx);
+  int r = enter(ctx, st);
   if (r) return r;
-  if ((r = flush_deltas(ctx, st, 0))) return r;
-  HIPCHK(launch_fill_kv(kv_layout(ctx, layer), q.slot, ctx->stream_of(layer, slot), pos0, n, k, v, st),
-         "fill_kv");
-  return DORY_OK;
+  if (!(r = flush_deltas(ctx, st, 0))) {
+    const hipError_t e = launch_fill_kv(kv_layout(ctx, layer), q.slot, ctx->stream_of(layer, slot), pos0, n, k, v, st);
+    if (e != hipSuccess) r = hip_fail(ctx, e, "fill_kv");
+  }
+  const int rl = leave(ctx, st);
+  return r ? r : rl;
 }
 
 int dory_bind_vocab(dory_ctx* ctx, const dory_vocab_weights* v) {
@@ -1249,64 +1410,18 @@ int dory_embed(dory_ctx* ctx, void* stream, int n, const int32_t* ids, float* x_
 
 int dory_logits(dory_ctx* ctx, void* stream, int n, const float* states, float* logits) {
   if (!ctx) return DORY_ERR_INVALID_ARG;
-  if (!ctx->vocab_bound) return ctx->fail(DORY_ERR_STATE, "vocabulary not bound");
   if (!ctx->ws) return ctx->fail(DORY_ERR_STATE, "workspace not bound");
-  if (n < 1 || n > ctx->cfg.max_rows || !states || !logits)
-    return ctx->fail(DORY_ERR_INVALID_ARG, "need 1 <= n <= max_rows and non-null states, logits");
+  int r = logits_check(ctx, n, states, logits);
+  if (r) return r;
   hipStream_t st = (hipStream_t)stream;
-  const int H = ctx->D.H;
-  const int64_t V = ctx->vocab.vocab;
-  const bool f32 = ctx->cfg.act_dtype == DORY_DTYPE_F32;
-  char* ws = ctx->ws;
-  GemmArgs g;
-  g.B = ctx->vocab.lm_head;
-  g.M = n;
-  g.N = (int)V;
-  g.K = H;
-  g.lda = H;
-  g.C = logits;
-  g.ldc = (int)V;
-  int splits = 1;
-  if (f32) {
-    g.A = states;
-    g.act = ACT_F32;
-    g.wfmt = W_F32;
-    g.epi = EPI_F32;
-  } else {
-    // the states in the activation type, as the projections read them
-    Prof ps(ctx, st, DORY_KC_UPDATE);
-    HIPCHK(launch_stage_input(states, (float*)(ws + ctx->W.s), ws + ctx->W.sb, n, H, ACT_BF16, st), "LM-head input");
-    ps.end(0.0, (double)n * H * (4 + 4 + 2));
-    g.A = ws + ctx->W.sb;
-    g.act = ACT_BF16;
-    g.wfmt = W_BF16;
-    if (n <= SKINNY_M) {  // decode-sized: split-K streaming tiles
-      splits = gemm_pick_splits(n, (int)V, H, W_BF16);
-      g.epi = EPI_PARTIAL;
-      g.splits = splits;
-      if (splits > 1) {
-        if ((size_t)splits * n * V > ctx->W.part_floats)
-          return ctx->fail(DORY_ERR_UNSUPPORTED, "LM-head partials exceed the workspace");
-        g.C = ws + ctx->W.part;
-      }
-    } else {
-      g.epi = EPI_F32;
-    }
-  }
-  {
-    Prof pr(ctx, st, DORY_KC_VOCAB);
-    const hipError_t e = launch_gemm(g, st);
-    if (e != hipSuccess) return hip_fail(ctx, e, "LM-head GEMM");
-    pr.end(2.0 * n * (double)V * H, (double)V * H * ctx->D.esz + (double)n * H * ctx->D.esz + 4.0 * n * V * splits);
-  }
-  {
-    Prof pr(ctx, st, DORY_KC_VOCAB);
-    const float* part = splits > 1 ? (const float*)(ws + ctx->W.part) : logits;
-    HIPCHK(launch_logit_scale(part, splits, (size_t)n * V, logits, V, n, V, ctx->vocab.logit_scale, st),
-           "logit scale");
-    pr.end(0.0, 4.0 * n * V * (splits + 1) + 4.0 * V);
-  }
-  return DORY_OK;
+  const int splits = logits_splits(ctx, n);
+  if ((size_t)splits * n * ctx->vocab.vocab > ctx->W.part_floats)
+    return ctx->fail(DORY_ERR_UNSUPPORTED, "LM-head partials exceed the workspace");
+  if ((r = enter(ctx, st))) return r;
+  r = logits_run(ctx, st, n, states, logits, (float*)(ctx->ws + ctx->W.s), ctx->ws + ctx->W.sb,
+                 (float*)(ctx->ws + ctx->W.part), splits);
+  const int rl = leave(ctx, st);
+  return r ? r : rl;
 }
 
 int dory_sample_top_p(void* stream, int n, int64_t vocab, const float* logits, int64_t ld, float temperature,

@@ -95,6 +95,7 @@ _SIGS = {
     "dory_last_layer_calls": (C.c_int, [_P, C.POINTER(C.c_int64)]),
     "dory_test_reserve": (C.c_int, [_P, C.c_int32, C.c_int32]),
     "dory_test_fill_kv": (C.c_int, [_P, _P, C.c_int32, C.c_int, C.c_int, C.c_int32, C.c_int32, _P, _P]),
+    "dory_test_inject_failure": (C.c_int, [_P, C.c_int]),
     "dory_test_gemm": (C.c_int, [_P, _P, C.c_int, _P, _P, _P, C.c_int, C.c_int, C.c_int, C.c_int, C.c_int, _P,
                                  C.c_int, C.POINTER(C.c_int)]),
     "dory_quantize_mxfp8": (C.c_int, [_P, _P, C.c_int, C.c_int64, C.c_int64, _P, _P]),
@@ -303,6 +304,10 @@ def dory_test_reserve(ctx, seq_id: int, n_tokens: int):
 def dory_test_fill_kv(ctx, seq_id, layer, slot, pos0, k, v, stream=None):
     n = k.shape[0]
     _check(lib().dory_test_fill_kv(ctx, _stream(stream), seq_id, layer, slot, pos0, n, _ptr(k), _ptr(v)), ctx)
+
+
+def dory_test_inject_failure(ctx, at: int):
+    _check(lib().dory_test_inject_failure(ctx, at), ctx)
 
 
 EPI_F32, EPI_PARTIAL, EPI_STORE_BF16, EPI_SWIGLU = 0, 1, 2, 4

@@ -34,6 +34,19 @@ def _nvfp4_dequantised(w):
     return _NV_CACHE[key]
 
 
+_MX_CACHE = {}
+
+
+def _mxfp8_dequantised(w):
+    """The oracle's MXFP8 round trip of a weight matrix, cached by content (several
+    parity cases reuse the same seeded weights)."""
+    import hashlib
+    key = (w.shape, hashlib.sha1(np.ascontiguousarray(w).tobytes()).hexdigest())
+    if key not in _MX_CACHE:
+        _MX_CACHE[key] = MX.dequantize(*MX.quantize(w))
+    return _MX_CACHE[key]
+
+
 def oracle_model(shape, w_gpu, rt=None):
     """Oracle weights: the same bf16/fp32 values, or dequantised MXFP8 / NVFP4 codes
     produced by the oracle's own quantisers from the same bf16 values."""
@@ -42,8 +55,7 @@ def oracle_model(shape, w_gpu, rt=None):
     if shape["weight_format"] == "mxfp8":
         for w in cpu:
             for name in ("w_qkvg", "w_o", "w_gu", "w_down"):
-                codes, scales = MX.quantize(to_np(w[name]))
-                w[name] = torch.from_numpy(MX.dequantize(codes, scales))
+                w[name] = torch.from_numpy(_mxfp8_dequantised(to_np(w[name])))
     if shape["weight_format"] == "nvfp4":
         for w in cpu:
             for name in ("w_qkvg", "w_o", "w_gu", "w_down"):
@@ -129,3 +141,37 @@ def check_valid(lg_np, u_np, toks, temperature, top_p):
             assert t == OV.sample_top_p(lg_np[i], temperature, top_p, u), f"row {i}: token {t}"
             exact += 1
     return exact
+
+
+def seed_context(rt, shape, seqs, k, mode, keep=None, seed=9, swa_tail=None, extra=64):
+    """Install a seeded context without computing it: reserve seqs[sid] positions for each
+    sequence and write seeded K/V (synth.make_kv, drawn on the device by torch) into every
+    cache slot the sequence holds; sliding layers get only their last `swa_tail` positions
+    (default window + 64). Returns oracle sequences holding the same entries (float64) for
+    the ids in `keep` (default all), with room for `extra` more positions."""
+    cfg = O.Config.from_dict(shape)
+    L = shape["n_in"] + shape["n_rec"] + shape["n_out"]
+    keep = set(seqs) if keep is None else set(keep)
+    tail = shape["window"] + 64 if swa_tail is None else swa_tail
+    from looped_ngpt_transformer_amd import dory as D
+    stores = {}
+    for sid, C in seqs.items():
+        D.dory_test_reserve(rt.ctx, sid, C)
+        seq = None
+        if sid in keep:
+            seq = O.Sequence(cfg)
+            seq.length = C
+        for l in range(L):
+            rec = shape["n_in"] <= l < shape["n_in"] + shape["n_rec"]
+            slots = k if (rec and mode == "per_loop") else 1
+            p0 = 0 if O.layer_is_full(cfg, l) else max(0, C - tail)
+            for s in range(slots):
+                kk, vv = synth.make_kv(shape, seed, sid, l, s, p0, C - p0, device="cuda")
+                D.dory_test_fill_kv(rt.ctx, sid, l, s, p0, kk, vv)
+                if seq is not None:
+                    seq.kv._ensure((l, s), C + extra)   # room for the positions the test appends
+                    seq.kv.write(l, s, np.arange(p0, C), to_np(kk), to_np(vv))
+        if seq is not None:
+            stores[sid] = seq
+    torch.cuda.synchronize()
+    return stores

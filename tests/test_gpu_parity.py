@@ -8,7 +8,7 @@ import torch
 import synth
 from looped_ngpt_transformer_amd import dory as D
 from looped_ngpt_transformer_amd.runtime import DoryRuntime
-from tests.gpu_helpers import compare, gpu_weights, oracle_model, oracle_schedule, run_schedule
+from tests.gpu_helpers import compare, gpu_weights, oracle_model, oracle_schedule, run_schedule, seed_context
 
 pytestmark = pytest.mark.gpu
 
@@ -158,14 +158,42 @@ def test_mxfp8_quantiser_bit_exact():
     np.testing.assert_array_equal(codes.cpu().numpy(), c_ref)
 
 
-def test_mxfp8_small_forward():
-    """MXFP8: a 300-row prefill (the large-M dequantising GEMMs), a 150-row chunk (the
-    split-K MXFP8 tiles and attention by quads of rows) and a decode step."""
+@pytest.mark.parametrize("mode", ["per_loop", "last_loop"])
+@pytest.mark.parametrize("k", [1, 2, 4])
+def test_mxfp8_small_forward(k, mode):
+    """MXFP8 at every loop count in both KV modes: a 300-row prefill (the large-M GEMMs),
+    a 150-row chunk (the split-K MXFP8 tiles and attention by quads of rows), a chunk
+    of a second sequence and two decode steps of both."""
     S = dict(PSMALL, weight_format="mxfp8")
     sched = [("prefill", [(0, xin(S, 300, 31))]),
-             ("prefill", [(0, xin(S, 150, 33))]),
-             ("decode", [(0, xin(S, 1, 32))])]
-    _run_case(S, 2, "last_loop", sched, max_rows=320, max_seq_len=512, max_seqs=1)
+             ("prefill", [(0, xin(S, 150, 33)), (1, xin(S, 40, 34))]),
+             ("decode", [(0, xin(S, 1, 32)), (1, xin(S, 1, 35))]),
+             ("decode", [(1, xin(S, 1, 36)), (0, xin(S, 1, 37))])]
+    _run_case(S, k, mode, sched, max_rows=320, max_seq_len=512, max_seqs=2)
+
+
+@pytest.mark.parametrize("mode", ["per_loop", "last_loop"])
+def test_mxfp8_decode_over_seeded_context(mode):
+    """MXFP8, k = 4: decode steps of two sequences over seeded 3000- and 900-token
+    contexts (the long one goes by the two-register-set split-key kernel, more than 2048
+    keys), with undamped rates so that attention errors reach the final states."""
+    from oracle import dory_oracle as O
+    from tests.helpers import to_np
+    S = dict(PSMALL, weight_format="mxfp8")
+    k = 4
+    w = sharpen(gpu_weights(S, 8))
+    rt = DoryRuntime(S, w, max_loops=4, max_seqs=2, max_seq_len=3072, max_rows=64, mode=mode, loops=k)
+    stores = _seed_kv(rt, S, {0: 3000, 1: 900}, k, mode)
+    cfg, W = oracle_model(S, w)
+    for step in range(2):
+        X = xin(S, 2, 260 + step)
+        y = rt.decode([0, 1], X)
+        torch.cuda.synchronize()
+        got = y.cpu().double().numpy()
+        for j in range(2):
+            ref = O.prefill(cfg, W, stores[j], to_np(X[j:j + 1]), k, mode)
+            compare(got[j:j + 1], ref, S, f"step {step} seq {j}")
+    rt.close()
 
 
 @pytest.mark.parametrize("batch", [40, 128])
@@ -197,28 +225,8 @@ def test_bitwise_deterministic_and_batch_permutation():
 
 
 def _seed_kv(rt, shape, seqs, k, mode, seed=9):
-    """Reserve each sequence's context and write seeded K/V into every cache slot it
-    holds (sliding layers: the last 128 positions). Returns the oracle's stores."""
-    from oracle import dory_oracle as O
-    from tests.helpers import to_np
-    cfg = O.Config.from_dict(shape)
-    L = shape["n_in"] + shape["n_rec"] + shape["n_out"]
-    stores = {}
-    for sid, C in seqs.items():
-        D.dory_test_reserve(rt.ctx, sid, C)
-        seq = O.Sequence(cfg)
-        seq.length = C
-        for l in range(L):
-            rec = shape["n_in"] <= l < shape["n_in"] + shape["n_rec"]
-            slots = k if (rec and mode == "per_loop") else 1
-            p0 = 0 if O.layer_is_full(cfg, l) else max(0, C - 128)
-            for s in range(slots):
-                kk, vv = synth.make_kv(shape, seed, sid, l, s, p0, C - p0, device="cuda")
-                D.dory_test_fill_kv(rt.ctx, sid, l, s, p0, kk, vv)
-                seq.kv.write(l, s, np.arange(p0, C), to_np(kk), to_np(vv))
-        stores[sid] = seq
-    torch.cuda.synchronize()
-    return stores
+    """Seeded contexts for PSMALL (sliding layers: the last 128 positions)."""
+    return seed_context(rt, shape, seqs, k, mode, seed=seed, swa_tail=128)
 
 
 @pytest.mark.parametrize("sharp", [False, True])
