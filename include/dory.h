@@ -261,6 +261,21 @@ int dory_embed(dory_ctx* ctx, void* stream, int n, const int32_t* ids, float* x_
  * 1 <= n <= max_rows. Errors: INVALID_ARG, STATE (vocabulary or workspace unbound), HIP. */
 int dory_logits(dory_ctx* ctx, void* stream, int n, const float* states, float* logits);
 
+/* dory_logits for callers that cannot allocate device memory or bind a workspace (code
+ * under HIP graph capture, tight serving loops, harnesses that forbid allocation): the
+ * same result, with the staged states and split-K partials in a scratch array the
+ * library holds on each GPU (32 MiB, from the first call on a device until the process
+ * ends) instead of the workspace. Needs the vocabulary bound, not the workspace. Limit:
+ * n * H * 6 bytes (bf16 contexts; none in fp32 ones), plus splits * n * V * 4 when the
+ * LM-head GEMM splits K (small vocabularies only: below 25600 tokens at n <= 128; the
+ * 131072-token vocabulary never does), at most 32 MiB (INVALID_ARG beyond, before any
+ * device work). Nothing needs clearing between calls: each call writes every scratch
+ * byte it reads. Calls no hipMalloc or hipFree.
+ * Every call on a GPU uses that GPU's one array: calls that overlap on a GPU (other
+ * streams, other contexts, other threads) race, and must be ordered by the caller.
+ * Errors as dory_logits, except that no workspace is needed. */
+int dory_logits_noalloc(dory_ctx* ctx, void* stream, int n, const float* states, float* logits);
+
 /* Top-p sampling, one token per row: p = softmax(logits[i] / temperature); tokens in
  * order of p, highest first, equal p by lower id; the nucleus is the shortest prefix of
  * that order whose cumulative p reaches top_p; the token is the first of the nucleus

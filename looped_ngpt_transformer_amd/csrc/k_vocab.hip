@@ -4,6 +4,7 @@
 // §2; generation settings temperature 1.0, top_p 0.95 — MXFP8 article, deployment section).
 // The LM-head product itself is a projection GEMM (k_gemm.hip).
 #include <climits>
+#include <mutex>
 
 #include "common.h"
 #include "kernels.h"
@@ -541,6 +542,33 @@ hipError_t launch_sample_top_p(const float* logits, int64_t ld, int n, int64_t V
   hipLaunchKernelGGL(k_sample_top_p, dim3(n), dim3(ST), 0, st, logits, ld, (int)V, 1.0f / temperature, top_p,
                      u, out, 1);
   return hipGetLastError();
+}
+
+// Device scratch of the LM-head entry point that allocates nothing (dory_logits_noalloc):
+// the staged states and split-K partials live here instead of in a bound workspace.
+// Each GPU the library runs on holds its own copy for the life of the process, and
+// every call on that GPU shares it.
+static __device__ __align__(256) unsigned char scratch[NOALLOC_SCRATCH_BYTES];
+
+// The device address of this GPU's scratch (the current device). The array's name is a
+// host-side stand-in, so its address is looked up once per device with the device
+// current and kept; kernels get the looked-up pointer.
+hipError_t noalloc_scratch(void** out) {
+  static std::mutex mu;
+  static void* addr[MAX_DEVICES] = {};
+  int dev = -1;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  if (dev < 0 || dev >= MAX_DEVICES) return hipErrorInvalidDevice;
+  std::lock_guard<std::mutex> lock(mu);
+  if (!addr[dev]) {
+    void* p = nullptr;
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess) return e;
+    addr[dev] = p;
+  }
+  *out = addr[dev];
+  return hipSuccess;
 }
 
 }  // namespace dory

@@ -162,6 +162,11 @@ hipError_t launch_embed(const void* E, int e_bf16, int64_t V, int H, const int32
 // sstride elements; part may be logits itself for one split).
 hipError_t launch_logit_scale(const float* part, int splits, size_t sstride, float* logits, int64_t ld, int n,
                               int64_t V, const float* sz, hipStream_t st);
+// Static device scratch for dory_logits_noalloc: NOALLOC_SCRATCH_BYTES per GPU; the
+// address on the current device (looked up once per device).
+constexpr size_t NOALLOC_SCRATCH_BYTES = (size_t)32 << 20;
+constexpr int MAX_DEVICES = 64;
+hipError_t noalloc_scratch(void** out);
 // out[i] = the token u[i] draws from row i of logits under temperature and top-p.
 hipError_t launch_sample_top_p(const float* logits, int64_t ld, int n, int64_t V, float temperature, float top_p,
                                const float* u, int32_t* out, hipStream_t st);

@@ -1424,6 +1424,24 @@ int dory_logits(dory_ctx* ctx, void* stream, int n, const float* states, float* 
   return r ? r : rl;
 }
 
+int dory_logits_noalloc(dory_ctx* ctx, void* stream, int n, const float* states, float* logits) {
+  if (!ctx) return DORY_ERR_INVALID_ARG;
+  int r = logits_check(ctx, n, states, logits);
+  if (r) return r;
+  const int splits = logits_splits(ctx, n);
+  const bool f32 = ctx->cfg.act_dtype == DORY_DTYPE_F32;
+  const size_t rows = f32 ? 0 : (size_t)n * ctx->D.H;
+  const size_t o_sb = al(rows * 4), o_part = o_sb + al(rows * 2);
+  const size_t need = o_part + (splits > 1 ? (size_t)splits * n * ctx->vocab.vocab * 4 : 0);
+  if (need > NOALLOC_SCRATCH_BYTES)
+    return ctx->fail(DORY_ERR_INVALID_ARG, "%d rows need %zu bytes of scratch, more than the %zu the library holds", n,
+                     need, NOALLOC_SCRATCH_BYTES);
+  void* base = nullptr;
+  HIPCHK(noalloc_scratch(&base), "scratch address");
+  char* b = (char*)base;
+  return logits_run(ctx, (hipStream_t)stream, n, states, logits, (float*)b, b + o_sb, (float*)(b + o_part), splits);
+}
+
 int dory_sample_top_p(void* stream, int n, int64_t vocab, const float* logits, int64_t ld, float temperature,
                       float top_p, const float* u, int32_t* tokens) {
   if (n < 1 || vocab < 1 || vocab > (1 << 24) || ld < vocab || !logits || !u || !tokens ||

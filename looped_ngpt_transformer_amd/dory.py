@@ -103,6 +103,7 @@ _SIGS = {
     "dory_bind_vocab": (C.c_int, [_P, C.POINTER(dory_vocab_weights)]),
     "dory_embed": (C.c_int, [_P, _P, C.c_int, _P, _P]),
     "dory_logits": (C.c_int, [_P, _P, C.c_int, _P, _P]),
+    "dory_logits_noalloc": (C.c_int, [_P, _P, C.c_int, _P, _P]),
     "dory_sample_top_p": (C.c_int, [_P, C.c_int, C.c_int64, _P, C.c_int64, C.c_float, C.c_float, _P, _P]),
     "dory_profile_enable": (C.c_int, [_P, C.c_int]),
     "dory_profile_read": (C.c_int, [_P, C.c_int, C.POINTER(dory_kernel_stats)]),
@@ -350,6 +351,10 @@ def dory_embed(ctx, ids, x_out, stream=None):
 
 def dory_logits(ctx, states, logits, stream=None):
     _check(lib().dory_logits(ctx, _stream(stream), int(states.shape[0]), _ptr(states), _ptr(logits)), ctx)
+
+
+def dory_logits_noalloc(ctx, states, logits, stream=None):
+    _check(lib().dory_logits_noalloc(ctx, _stream(stream), int(states.shape[0]), _ptr(states), _ptr(logits)), ctx)
 
 
 def dory_sample_top_p(logits, u, tokens, temperature=1.0, top_p=0.95, vocab=None, stream=None):
