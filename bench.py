@@ -69,7 +69,9 @@ def parse():
     ap.add_argument("--tokens", type=int, default=None, help="prefill length (P, L)")
     ap.add_argument("--context", type=int, default=None, help="seeded KV context (D, Q)")
     ap.add_argument("--batch", type=int, default=None, help="decode batch (D, Q)")
-    ap.add_argument("--cpu-rows", type=int, default=768)
+    ap.add_argument("--cpu-rows", type=int, default=1024)
+    ap.add_argument("--no-decode-leg", action="store_true", help="P: skip the 72-layer decode leg")
+    ap.add_argument("--decode-steps", type=int, default=8, help="decode leg: timed steps per k")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--copy-probe", action="store_true",
                     help="run out = src * 1 over 1 GiB first (counter calibration for rocprofv3 --pmc)")
@@ -138,8 +140,10 @@ def lm_head_line(stats, steps):
 
 def time_prefill(rt, D, torch, X, tokens, steps, warmup, chunk=None):
     """Each step: prefill a fresh sequence (in chunks if given), then release it. The
-    timed steps carry HIP events around the GEMM launches only; one more untimed step
-    records every kernel class for the per-class breakdown."""
+    timed steps carry no events (wall clock around `steps` steps); the same number of
+    steps is then run again with HIP events around the GEMM launches only (the roofline
+    of the dominant kernel class), and one more step records every kernel class for the
+    per-class breakdown."""
     chunk = chunk or tokens
     Y = torch.empty((chunk, X.shape[1]), dtype=torch.float32, device="cuda")
 
@@ -152,12 +156,15 @@ def time_prefill(rt, D, torch, X, tokens, steps, warmup, chunk=None):
     for _ in range(warmup):
         one()
     torch.cuda.synchronize()
-    D.dory_profile_enable(rt.ctx, [D.KC_GEMM])
     t0 = time.perf_counter()
     for _ in range(steps):
         one()
     torch.cuda.synchronize()
     t1 = time.perf_counter()
+    D.dory_profile_enable(rt.ctx, [D.KC_GEMM])
+    for _ in range(steps):
+        one()
+    torch.cuda.synchronize()
     D.dory_profile_enable(rt.ctx, False)
     timed = kernel_stats(rt, D)
     D.dory_profile_enable(rt.ctx, True)
@@ -167,27 +174,51 @@ def time_prefill(rt, D, torch, X, tokens, steps, warmup, chunk=None):
     return (t1 - t0) / steps, timed, kernel_stats(rt, D), Y
 
 
+def cpu_model():
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return None
+
+
 def cpu_baseline_prefill(shape, weights, X, k, mode, rows, y_gpu):
     """The float64 oracle on the first `rows` tokens of the prefill (a causal prefix,
-    so its outputs are exactly the first rows of the full prefill)."""
+    so its outputs are exactly the first rows of the full prefill), with its BLAS
+    threads set to the cores this process may run on; then the same prefix with the
+    weights and input rows in float32 (a timing variant: NumPy then multiplies in
+    float32; the oracle's result is the float64 one)."""
     import numpy as np
-    from threadpoolctl import threadpool_info
+    from threadpoolctl import threadpool_info, threadpool_limits
 
     from oracle import dory_oracle as O
+    cores = len(os.sched_getaffinity(0))
     cfg = O.Config.from_dict(shape)
-    W = [O.LayerWeights.from_packed(cfg, *(w[n].cpu().double().numpy() for n in
-                                          ("w_qkvg", "w_o", "w_gu", "w_down", "alpha_attn",
-                                           "alpha_mlp", "s_qk"))) for w in weights]
+    names = ("w_qkvg", "w_o", "w_gu", "w_down", "alpha_attn", "alpha_mlp", "s_qk")
+    W = [O.LayerWeights.from_packed(cfg, *(w[n].cpu().double().numpy() for n in names)) for w in weights]
     Xs = X[:rows].cpu().double().numpy()
-    t0 = time.perf_counter()
-    ref = O.prefill(cfg, W, O.Sequence(cfg), Xs, k, mode)
-    dt = time.perf_counter() - t0
+    with threadpool_limits(limits=cores):
+        threads = max([p.get("num_threads", 1) for p in threadpool_info()] + [1])
+        t0 = time.perf_counter()
+        ref = O.prefill(cfg, W, O.Sequence(cfg), Xs, k, mode)
+        dt = time.perf_counter() - t0
+        W32 = [O.LayerWeights(*(None if a is None else a.astype(np.float32) for a in
+                                (lw.wq, lw.wk, lw.wv, lw.wg, lw.wo, lw.wgate, lw.wup, lw.wdown,
+                                 lw.alpha_attn, lw.alpha_mlp, lw.s_qk))) for lw in W]
+        t0 = time.perf_counter()
+        O.prefill(cfg, W32, O.Sequence(cfg), Xs.astype(np.float32), k, mode)
+        dt32 = time.perf_counter() - t0
     g = y_gpu[:rows].cpu().double().numpy()
     cos = np.sum(g * ref, 1) / (np.linalg.norm(g, axis=1) * np.linalg.norm(ref, axis=1))
-    threads = max([p.get("num_threads", 1) for p in threadpool_info()] + [1])
     return ({"value": round(rows / dt, 3), "unit": "tokens/s", "cores": threads, "kind": "oracle",
-             "sample": f"first {rows} tokens of the prefill (causal prefix), all "
-                       f"{O.effective_depth(cfg, k)} layer calls, float64, {dt:.1f} s"},
+             "sample": f"first {rows} of the 4096 tokens of the prefill (a causal prefix: its attention "
+                       f"covers at most {rows} keys, so the rate is higher than the whole prefill's), all "
+                       f"{O.effective_depth(cfg, k)} layer calls, float64, {dt:.1f} s",
+             "cpu": cpu_model(), "affinity_cores": cores,
+             "float32_value": round(rows / dt32, 3), "float32_s": round(dt32, 1)},
             {"rows": rows, "max_abs": float(np.abs(g - ref).max()), "min_cos": float(cos.min())})
 
 
@@ -198,7 +229,8 @@ def bench_prefill(args, torch, synth, D, DoryRuntime):
     mode = args.mode or "per_loop"
     tokens = args.tokens or (4096 if wl == "P" else 131072 if wl == "L" else 64)
     chunk = 8192 if wl == "L" else None
-    ks = sorted({k} | ({int(x) for x in args.ks.split(",")} if args.ks else set()))
+    default_ks = {1, 2, 4} if wl == "P" else set()
+    ks = sorted({k} | ({int(x) for x in args.ks.split(",")} if args.ks else default_ks))
     log(f"[bench] workload {wl}: generating weights")
     weights = synth.make_weights(shape, 1234, "cuda")
     max_rows = min(tokens, chunk or tokens)
@@ -229,15 +261,107 @@ def bench_prefill(args, torch, synth, D, DoryRuntime):
     if len(ks) > 1:
         out["by_loops"] = {str(kk): {"tokens_per_s": round(tokens / r[0], 1),
                                      "ms_per_step": round(r[0] * 1e3, 3),
-                                     "gemm_tflops": round(r[1]["gemm"]["flops"] / r[1]["gemm"]["ms"] / 1e9, 1)}
+                                     "gemm_tflops": round(r[1]["gemm"]["flops"] / r[1]["gemm"]["ms"] / 1e9, 1),
+                                     "gemm_frac": round(r[1]["gemm"]["flops"] / r[1]["gemm"]["ms"] / 1e9
+                                                        / PEAK_BF16_TFLOPS, 4)}
                            for kk, r in results.items()}
+    rt.close()
+    del rt
+    torch.cuda.empty_cache()
+    if wl == "P" and not args.no_decode_leg:
+        out["decode_leg"] = decode_leg(args, torch, synth, D, DoryRuntime)
     if not args.no_cpu_baseline and wl in ("P", "T"):
         log(f"[bench] cpu baseline: oracle on the first {args.cpu_rows} tokens")
         cb, par = cpu_baseline_prefill(shape, weights, X, k, mode, min(args.cpu_rows, tokens), Y)
         out["cpu_baseline"] = cb
         out["parity_prefix"] = par
-    rt.close()
     return out
+
+
+def decode_step_bytes(shape, k, batch, ctx):
+    """Algorithmic HBM bytes of one decode step: every executed layer's weights once, and
+    the K and V entries each query row's attention reads (full layers: the whole context;
+    sliding layers: the last W positions), once per loop (the same in both KV modes)."""
+    H, I = shape["hidden"], shape["intermediate"]
+    qd, kd = shape["n_q_heads"] * shape["head_dim"], shape["n_kv_heads"] * shape["head_dim"]
+    params = (qd + 2 * kd + (qd if shape["attn_gate"] else 0)) * H + H * qd + 2 * I * H + H * I
+    wbytes = {"bf16": 2.0, "mxfp8": 1.0 + 1.0 / 32, "nvfp4": 0.5 + 1.0 / 16}[shape["weight_format"]]
+    L = synth_layers(shape)
+    kv_tok = 2 * kd * 2  # K and V of one position, bf16
+    total_w = total_kv = 0.0
+    for l, reps in L:
+        total_w += reps(k) * params * wbytes
+        full = l % shape["full_period"] == shape["full_period"] - 1
+        keys = ctx + 1 if full else min(ctx + 1, shape["window"])
+        total_kv += reps(k) * batch * keys * kv_tok
+    return total_w, total_kv
+
+
+def synth_layers(shape):
+    """(physical layer, calls as a function of k) for every layer."""
+    n_in, n_rec, n_out = shape["n_in"], shape["n_rec"], shape["n_out"]
+    out = [(l, lambda k: 1) for l in range(n_in)]
+    out += [(l, lambda k: k) for l in range(n_in, n_in + n_rec)]
+    out += [(l, lambda k: 1) for l in range(n_in + n_rec, n_in + n_rec + n_out)]
+    return out
+
+
+def decode_leg(args, torch, synth, D, DoryRuntime):
+    """The 72-layer decode shape (batch 32 over a seeded 32768-token context) at k = 1, 2
+    and 4 in last_loop mode, whose cache holds one slot per layer whatever k is, so one
+    seeded context serves every loop count. Per k: wall-clock ms per step (no events),
+    the whole step's HBM fraction (weights and KV bytes of the method per step over that
+    time, against 8 TB/s), and, from a separate pass with HIP events around its launches,
+    the split-key attention kernel's own fraction."""
+    shape = synth.config("D")
+    batch, ctx_len, mode = 32, 32768, "last_loop"
+    ks = [1, 2, 4]
+    steps, warm = args.decode_steps, 2
+    n_pos = ctx_len + len(ks) * (2 * steps + warm + 1) + 1
+    weights = synth.make_weights(shape, 1234, "cuda")
+    c = D.make_config(shape, max_loops=max(ks), max_seqs=batch, max_seq_len=n_pos, max_rows=batch)
+    pages = D.dory_kv_pages_needed(c, D.MODES[mode], max(ks), n_pos, batch)
+    rt = DoryRuntime(shape, weights, max_loops=max(ks), max_seqs=batch, max_seq_len=n_pos, max_rows=batch,
+                     kv_pages=pages, mode=mode, loops=2)
+    log(f"[bench] decode leg: seeding {ctx_len} tokens x {batch} (last_loop)")
+    seed_kv(rt, shape, synth, D, torch, batch, ctx_len, [2] * batch, mode)
+    for b in range(batch):
+        D.dory_set_seq_loops(rt.ctx, b, 0)  # follow the context's k
+    torch.cuda.synchronize()
+    X = synth.make_inputs(batch, shape["hidden"], 77, device="cuda")
+    Y = torch.empty((batch, shape["hidden"]), dtype=torch.float32, device="cuda")
+    ids = list(range(batch))
+    res = {}
+    for kk in ks:
+        D.dory_set_loops(rt.ctx, kk)
+        for _ in range(warm):
+            D.dory_decode_step(rt.ctx, ids, X, Y)
+        torch.cuda.synchronize()
+        ctx_now = D.dory_seq_len(rt.ctx, 0)
+        t0 = time.perf_counter()
+        for _ in range(steps):
+            D.dory_decode_step(rt.ctx, ids, X, Y)
+        torch.cuda.synchronize()
+        dt = (time.perf_counter() - t0) / steps
+        D.dory_profile_enable(rt.ctx, [D.KC_ATTN])
+        for _ in range(steps):
+            D.dory_decode_step(rt.ctx, ids, X, Y)
+        torch.cuda.synchronize()
+        D.dory_profile_enable(rt.ctx, False)
+        a = D.dory_profile_read(rt.ctx, D.KC_ATTN)
+        wb, kvb = decode_step_bytes(shape, kk, batch, ctx_now + steps // 2)
+        att = a["bytes"] / (a["ms"] / 1e3) / 1e9
+        res[str(kk)] = {"tokens_per_s": round(batch / dt, 1), "ms_per_step": round(dt * 1e3, 3),
+                        "step_gb": round((wb + kvb) / 1e9, 2),
+                        "step_hbm_frac": round((wb + kvb) / dt / 1e9 / PEAK_HBM_GBS, 4),
+                        "attention_hbm_frac": round(att / PEAK_HBM_GBS, 4)}
+        log(f"[bench] decode k={kk}: {dt * 1e3:.2f} ms/step, {batch / dt:.0f} tok/s, "
+            f"step {res[str(kk)]['step_hbm_frac']:.3f} of HBM")
+    rt.close()
+    del rt, weights
+    torch.cuda.empty_cache()
+    return {"workload": WORKLOAD_TEXT["D"] + ", last_loop", "batch": batch, "context": ctx_len,
+            "steps": steps, "warmup": warm, "by_loops": res}
 
 
 def bench_decode(args, torch, synth, D, DoryRuntime):
