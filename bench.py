@@ -67,6 +67,8 @@ def parse():
                     help="decode: comma list of loop counts given to the batch's sequences in turn "
                          "(one call mixes them)")
     ap.add_argument("--tokens", type=int, default=None, help="prefill length (P, L)")
+    ap.add_argument("--weights", default=None, choices=["bf16", "mxfp8", "nvfp4"],
+                    help="prefill (P, L): weight format (default bf16)")
     ap.add_argument("--context", type=int, default=None, help="seeded KV context (D, Q)")
     ap.add_argument("--batch", type=int, default=None, help="decode batch (D, Q)")
     ap.add_argument("--cpu-rows", type=int, default=1024)
@@ -224,7 +226,7 @@ def cpu_baseline_prefill(shape, weights, X, k, mode, rows, y_gpu):
 
 def bench_prefill(args, torch, synth, D, DoryRuntime):
     wl = args.workload
-    shape = synth.config(wl)
+    shape = synth.config(wl, **({"weight_format": args.weights} if args.weights else {}))
     k = args.k or 2
     mode = args.mode or "per_loop"
     tokens = args.tokens or (4096 if wl == "P" else 131072 if wl == "L" else 64)
@@ -252,7 +254,9 @@ def bench_prefill(args, torch, synth, D, DoryRuntime):
         "ms_per_step": round(dt * 1e3, 3), "higher_is_better": True, "scaling": "weak",
         "vs_baseline": None, "dtype": "bf16" if shape["act_dtype"] == "bf16" else "f32",
         "data": "synthetic (seeded random weights N(0,0.02) and unit-norm input states)",
-        "config": {"workload": WORKLOAD_TEXT[wl], "tokens": tokens, "loops": k, "kv_mode": mode,
+        "config": {"workload": WORKLOAD_TEXT[wl] + ("" if shape["weight_format"] == "bf16" else
+                                                     ", %s weights" % shape["weight_format"].upper()),
+                   "tokens": tokens, "loops": k, "kv_mode": mode,
                    "executed_layers": shape["n_in"] + shape["n_out"] + k * shape["n_rec"],
                    "chunk": chunk or tokens},
         "roofline": roofline_of(stats, "mfma", wl),

@@ -317,8 +317,8 @@ int dory_test_inject_failure(dory_ctx* ctx, int at);
  *   1: C float split-K partials [splits][M][N] (decode projections), summed by the caller;
  *   2: C bf16 [M, N] ([q|k|v|gate] projection in prefill);
  *   4: SwiGLU: B rows [0, N/2) gate, [N/2, N) up; C bf16 [M, N/2] = SiLU(gate) * up.
- * Quantised formats take epi 1 only (layers expand NVFP4 matrices to bf16 for the other
- * epilogues). ldc = row stride of C in elements. The kernel and tile shape are the ones a
+ * Quantised formats take epi 1 only (layers expand MXFP8 and NVFP4 matrices to bf16,
+ * exactly, for the other epilogues). ldc = row stride of C in elements. The kernel and tile shape are the ones a
  * layer call would pick for these sizes (K % 64 == 0; N % 64 == 0, for epi 4 N % 128 == 0,
  * for NVFP4 N % 128 == 0). *splits receives the split count (1 unless epi 1). With
  * C == NULL the call only reports *splits. The caller owns every buffer; C must hold

@@ -37,6 +37,38 @@ __device__ __forceinline__ void dq4(uint32_t word, float sc, uint32_t* out) {
   out[1] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8((int)word, sc, true));
 }
 
+// W = E4M3 code * 2^(scale - 127) as bf16 (MXFP8 weights for the large-M GEMMs, which
+// then run on the bf16 tiles), one thread per group of 32 along K: 32 code bytes and a
+// scale byte in, 64 bytes out, with the same exact scaled conversion as the split-K
+// tiles.
+__global__ __launch_bounds__(256) void k_mxfp8_expand(const uint8_t* codes, const uint8_t* scales, int64_t ngroups,
+                                                      bf16_t* out) {
+  const int64_t gi = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  if (gi >= ngroups) return;
+  const float sc = e8m0_to_f32(scales[gi]);
+  const uint4* src = (const uint4*)(codes + (size_t)gi * 32);
+  uint4* dst = (uint4*)(out + (size_t)gi * 32);
+#pragma unroll
+  for (int h = 0; h < 2; ++h) {
+    const uint4 c = src[h];
+    const uint32_t w[4] = {c.x, c.y, c.z, c.w};
+    uint32_t o[8];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) dq4(w[i], sc, o + 2 * i);
+    dst[2 * h] = make_uint4(o[0], o[1], o[2], o[3]);
+    dst[2 * h + 1] = make_uint4(o[4], o[5], o[6], o[7]);
+  }
+}
+
+hipError_t launch_expand_mxfp8(const uint8_t* codes, const uint8_t* scales, int64_t rows, int64_t cols, void* out,
+                               hipStream_t st) {
+  const int64_t ng = rows * (cols / 32);
+  if (ng == 0) return hipSuccess;
+  hipLaunchKernelGGL(k_mxfp8_expand, dim3((unsigned)((ng + 255) / 256)), dim3(256), 0, st, codes, scales, ng,
+                     (bf16_t*)out);
+  return hipGetLastError();
+}
+
 // Epilogue: lane holds C[m = i*16 + 4*(lane>>4) + r][n = j*16 + (lane&15)] of its wave tile.
 template <int BM, int BN, int WMW, int WNW, int EPI>
 __device__ __forceinline__ void gemm_epilogue(const GemmArgs& g, f32x4 (&acc)[BM / WMW / 16][BN / WNW / 16],
@@ -1123,13 +1155,12 @@ static hipError_t go_big(const GemmArgs& g, hipStream_t st, int n) {
   return hipErrorNotSupported;
 }
 
-template <int BM, int BN, int WMW, int WNW, int EPI>
+// Register-staged tiles: MXFP8 split-K when N is not a multiple of 128, and the bf16
+// shapes the ping-pong tiles cannot take.
+template <int BM, int BN, int WMW, int WNW, int EPI, int WF>
 static hipError_t go(const GemmArgs& g, hipStream_t st, int ntiles_n) {
   dim3 grid(ntiles_n, (g.M + BM - 1) / BM, g.splits);
-  if (g.wfmt == W_MXFP8)
-    hipLaunchKernelGGL((k_gemm_mfma<BM, BN, WMW, WNW, EPI, W_MXFP8>), grid, dim3(GT), 0, st, g);
-  else
-    hipLaunchKernelGGL((k_gemm_mfma<BM, BN, WMW, WNW, EPI, W_BF16>), grid, dim3(GT), 0, st, g);
+  hipLaunchKernelGGL((k_gemm_mfma<BM, BN, WMW, WNW, EPI, WF>), grid, dim3(GT), 0, st, g);
   return hipGetLastError();
 }
 
@@ -1143,7 +1174,8 @@ hipError_t launch_gemm(const GemmArgs& gin, hipStream_t st) {
     return hipGetLastError();
   }
   if (g.act != ACT_BF16 || g.K % BK != 0 || g.K % (g.splits * BK) != 0) return hipErrorInvalidValue;
-  if (g.wfmt == W_NVFP4 && g.epi != EPI_PARTIAL) return hipErrorInvalidValue;  // large M: expand to bf16 first
+  // quantised weights at large M: the caller expands them to bf16 first
+  if ((g.wfmt == W_NVFP4 || g.wfmt == W_MXFP8) && g.epi != EPI_PARTIAL) return hipErrorInvalidValue;
   const bool bf = g.wfmt == W_BF16;  // bf16 weights: direct-to-LDS pipeline
   switch (g.epi) {
     case EPI_PARTIAL:  // small M (decode): stream the weights, split K
@@ -1162,32 +1194,29 @@ hipError_t launch_gemm(const GemmArgs& gin, hipStream_t st) {
         if (g.M <= 32) return go_mx<32, 128, 1, 4, 4>(g, st);
         return go_mx<64, 128, 1, 4, 4>(g, st);
       }
-      if (g.M <= 32) return go<32, 64, 1, 4, EPI_PARTIAL>(g, st, g.N / 64);
-      if (g.M <= 64) return go<64, 64, 1, 4, EPI_PARTIAL>(g, st, g.N / 64);
-      return go<128, 64, 1, 4, EPI_PARTIAL>(g, st, g.N / 64);
-    case EPI_STORE_ACT:
+      if (g.M <= 32) return go<32, 64, 1, 4, EPI_PARTIAL, W_MXFP8>(g, st, g.N / 64);
+      if (g.M <= 64) return go<64, 64, 1, 4, EPI_PARTIAL, W_MXFP8>(g, st, g.N / 64);
+      return go<128, 64, 1, 4, EPI_PARTIAL, W_MXFP8>(g, st, g.N / 64);
+    case EPI_STORE_ACT: {
       if (g.splits != 1) return hipErrorInvalidValue;
-      if (bf) {
-        const hipError_t e = go_big<EPI_STORE_ACT>(g, st, g.N);
-        if (e != hipErrorNotSupported) return e;
-      }
+      const hipError_t e = go_big<EPI_STORE_ACT>(g, st, g.N);
+      if (e != hipErrorNotSupported) return e;
       if (g.N % 128) return hipErrorInvalidValue;
-      return go<128, 128, 2, 2, EPI_STORE_ACT>(g, st, g.N / 128);
-    case EPI_F32:  // large M: fp32 output for the nGPT update
+      return go<128, 128, 2, 2, EPI_STORE_ACT, W_BF16>(g, st, g.N / 128);
+    }
+    case EPI_F32: {  // large M: fp32 output for the nGPT update
       if (g.splits != 1) return hipErrorInvalidValue;
-      if (bf) {
-        const hipError_t e = go_big<EPI_F32>(g, st, g.N);
-        if (e != hipErrorNotSupported) return e;
-      }
+      const hipError_t e = go_big<EPI_F32>(g, st, g.N);
+      if (e != hipErrorNotSupported) return e;
       if (g.N % 128) return hipErrorInvalidValue;
-      return go<128, 128, 2, 2, EPI_F32>(g, st, g.N / 128);
-    case EPI_SWIGLU:
+      return go<128, 128, 2, 2, EPI_F32, W_BF16>(g, st, g.N / 128);
+    }
+    case EPI_SWIGLU: {
       if (g.n_half % 64 || g.splits != 1) return hipErrorInvalidValue;
-      if (g.wfmt == W_BF16) {  // tiles interleave gate and up halves
-        const hipError_t e = go_big<EPI_SWIGLU>(g, st, 2 * g.n_half);
-        if (e != hipErrorNotSupported) return e;
-      }
-      return go<128, 128, 2, 2, EPI_SWIGLU>(g, st, g.n_half / 64);
+      const hipError_t e = go_big<EPI_SWIGLU>(g, st, 2 * g.n_half);  // tiles interleave gate and up halves
+      if (e != hipErrorNotSupported) return e;
+      return go<128, 128, 2, 2, EPI_SWIGLU, W_BF16>(g, st, g.n_half / 64);
+    }
     default:
       return hipErrorInvalidValue;
   }

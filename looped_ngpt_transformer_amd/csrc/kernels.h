@@ -34,6 +34,9 @@ struct GemmArgs {
   int ldc = 0;
   int n_half = 0;
 };
+// out [rows, cols] bf16 = E4M3 code * 2^(E8M0 scale - 127), groups of 32 along a row (exact)
+hipError_t launch_expand_mxfp8(const uint8_t* codes, const uint8_t* scales, int64_t rows, int64_t cols, void* out,
+                               hipStream_t st);
 // Split count the launcher would use for a decode-shaped GEMM (EPI_PARTIAL).
 int gemm_pick_splits(int M, int N, int K, int wfmt);
 hipError_t launch_gemm(const GemmArgs& g, hipStream_t st);

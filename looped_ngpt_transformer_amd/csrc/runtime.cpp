@@ -103,10 +103,11 @@ WsLayout layout_of(const dory_config& c, const Dims& D) {
   W.part = take(pf * 4);
   W.apart_floats = std::max<size_t>(R, 256) * D.Hq * (D.d + 2) * 8;
   W.apart = take(W.apart_floats * 4);
-  // NVFP4: one weight matrix expanded to bf16 for the large-M GEMMs
+  // MXFP8 / NVFP4: one weight matrix expanded to bf16 for the large-M GEMMs
   const size_t wmax = std::max({(size_t)D.Nqkvg * D.H, (size_t)D.H * D.Nq, (size_t)2 * D.I * D.H,
                                 (size_t)D.H * D.I});
-  W.wexp = take(c.weight_format == DORY_WFMT_NVFP4 ? wmax * 2 : 0);
+  const bool quant = c.weight_format == DORY_WFMT_NVFP4 || c.weight_format == DORY_WFMT_MXFP8;
+  W.wexp = take(quant && c.max_rows > SKINNY_M ? wmax * 2 : 0);
   W.total = off;
   return W;
 }
@@ -547,16 +548,16 @@ int run_layer(dory_ctx* ctx, hipStream_t st, const CallPlan& P, int l, int slot,
   auto run_gemm = [&](const GemmArgs& g0) -> hipError_t {
     Prof pr(ctx, st, DORY_KC_GEMM);
     GemmArgs g = g0;
-    if (wf == W_NVFP4) {
-      g.Bg = nv_scale(g0.B);
-      if (g.epi != EPI_PARTIAL) {  // large M: expand the matrix to bf16, then the bf16 tiles
-        const hipError_t x = launch_expand_nvfp4((const uint8_t*)g.B, g.Bs, g.Bg, g.N, g.K, ws + W.wexp, st);
-        if (x != hipSuccess) return x;
-        g.B = ws + W.wexp;
-        g.Bs = nullptr;
-        g.Bg = nullptr;
-        g.wfmt = W_BF16;
-      }
+    if (wf == W_NVFP4) g.Bg = nv_scale(g0.B);
+    if ((wf == W_NVFP4 || wf == W_MXFP8) && g.epi != EPI_PARTIAL) {
+      // large M: expand the matrix to bf16 (exact), then the bf16 tiles
+      const hipError_t x = wf == W_NVFP4 ? launch_expand_nvfp4((const uint8_t*)g.B, g.Bs, g.Bg, g.N, g.K, ws + W.wexp, st)
+                                         : launch_expand_mxfp8((const uint8_t*)g.B, g.Bs, g.N, g.K, ws + W.wexp, st);
+      if (x != hipSuccess) return x;
+      g.B = ws + W.wexp;
+      g.Bs = nullptr;
+      g.Bg = nullptr;
+      g.wfmt = W_BF16;
     }
     const hipError_t e = launch_gemm(g, st);
     const double outb = g.epi == EPI_STORE_ACT || g.epi == EPI_SWIGLU ? 2.0 : 4.0 * g.splits;

@@ -6,6 +6,9 @@
 
 namespace dory {
 int gemm_pick_splits(int, int, int, int) { return 1; }
+hipError_t launch_expand_mxfp8(const uint8_t*, const uint8_t*, int64_t, int64_t, void*, hipStream_t) {
+  return hipErrorNotSupported;
+}
 hipError_t launch_gemm(const GemmArgs&, hipStream_t) { return hipErrorNotSupported; }
 hipError_t launch_update(const UpdateArgs&, hipStream_t) { return hipErrorNotSupported; }
 hipError_t launch_stage_input(const float*, float*, void*, int, int, int, hipStream_t, const int32_t*) {
