@@ -1,17 +1,20 @@
 // Projections C = A B^T of the looped nGPT layer: [q|k|v|gate], attention output,
 // SwiGLU gate/up and down ("Dory1.0-4B" paper summary / arXiv §2; shapes from the
-// MXFP8 article's config fields).
+// MXFP8 article's config fields), all on gfx950 bf16 MFMA with fp32 accumulation.
 //
-// bf16 / MXFP8 weights: one MFMA kernel (v_mfma_f32_16x16x32_bf16, wave64) with A and B
-// tiles staged in LDS (16-byte chunks, XOR-swizzled per row against bank conflicts) and
-// the next K-tile prefetched into registers while the current one is multiplied.
-// MXFP8 weights (E4M3 + one E8M0 scale per 32 along K, W8A16: arXiv §5, MXFP8 article)
-// are dequantised to bf16 exactly while staged into LDS, so the MFMAs are bf16 x bf16
-// with fp32 accumulation.
-// Epilogues fuse what follows each projection: bf16 store; fp32 store; SwiGLU; or fp32
-// split-K partials for small-M (decode) shapes. The L2 norms before the output and down
-// projections only scale a row, and the nGPT update normalises the projection's output,
-// so they need no work here.
+// Large M (prefill, > 256 rows): k_gemm_pp, 256 x 256 or 256 x 160 tiles on 8 waves in
+// two groups one phase apart (one group feeds the matrix cores while the other reads
+// LDS), 64-wide K slices streamed straight into two LDS stages. Quantised weights
+// (MXFP8: E4M3 + one E8M0 scale per 32 along K, W8A16, arXiv §5; NVFP4) are first
+// expanded to bf16 exactly (k_mxfp8_expand here, k_nvfp4_expand), so these tiles serve
+// every format.
+// Small M (decode, <= 256 rows): split-K streaming tiles that read each weight once
+// (k_gemm_pipe for bf16, k_gemm_mx32 / k_gemm_nv32 converting MXFP8 / NVFP4 codes to
+// bf16 in registers just before the MFMA) and leave fp32 partials for the consumer.
+// k_gemm_mfma (register-staged tiles) covers the shapes the others cannot take.
+// Epilogues fuse what follows each projection: bf16 store; fp32 store; SwiGLU; or the
+// split-K partials. The L2 norms before the output and down projections only scale a
+// row, and the nGPT update normalises the projection's output, so they need no work.
 #include <type_traits>
 
 #include "common.h"
