@@ -8,9 +8,11 @@
 // (MXFP8: E4M3 + one E8M0 scale per 32 along K, W8A16, arXiv §5; NVFP4) are first
 // expanded to bf16 exactly (k_mxfp8_expand here, k_nvfp4_expand), so these tiles serve
 // every format.
-// Small M (decode, <= 256 rows): split-K streaming tiles that read each weight once
-// (k_gemm_pipe for bf16, k_gemm_mx32 / k_gemm_nv32 converting MXFP8 / NVFP4 codes to
-// bf16 in registers just before the MFMA) and leave fp32 partials for the consumer.
+// Small M (decode, <= 256 rows): split-K streaming kernels that read each weight once
+// and leave fp32 partials for the consumer: k_gemv (bf16, <= 32 rows: weights straight
+// into registers, every load of a wave in flight at once), k_gemm_pipe (bf16, more
+// rows), k_gemm_mx32 / k_gemm_nv32 (MXFP8 / NVFP4 codes converted to bf16 in registers
+// just before the MFMA).
 // k_gemm_mfma (register-staged tiles) covers the shapes the others cannot take.
 // Epilogues fuse what follows each projection: bf16 store; fp32 store; SwiGLU; or the
 // split-K partials. The L2 norms before the output and down projections only scale a
@@ -459,6 +461,71 @@ __global__ __launch_bounds__(GT) void k_gemm_pipe(GemmArgs g) {
   gemm_epilogue<BM, BN, WMW, WNW, EPI>(g, acc, n_tile, m0, split, wm, wn, lane);
 }
 
+// Decode GEMV for bf16 weights and at most 32 activation rows, bound by the weight
+// stream. A work-group of 4 waves owns 64 weight rows over a K range of 32 KW; each wave
+// streams its 16 rows straight into registers, all KW loads in flight before the first
+// MFMA (16 KW bytes per lane), so a launch keeps the whole weight matrix in flight.
+// The activation slice (32 rows x 32 KW, rows beyond M repeat the last row) goes to LDS
+// once per work-group with direct-to-LDS loads, 16-byte chunks XOR-swizzled by row.
+// v_mfma_f32_16x16x32_bf16 with the activations as the A operand: lane l holds weight
+// row l % 16, K elements 8 (l / 16) .. + 7 of each 32-wide step (64 contiguous bytes of
+// a row per 16 lanes). Output: fp32 split-K partials, split = K range.
+template <int KW>
+__global__ __launch_bounds__(256) void k_gemv(GemmArgs g) {
+  constexpr int KS = 32 * KW;       // K range of one work-group (one split)
+  constexpr int CH = KS / 8;        // 16-byte chunks per activation row
+  constexpr int AI = 32 * CH / 256; // activation load instructions per thread
+  static_assert(KW == 8 || KW == 16, "K range of 256 or 512");
+  __shared__ __align__(16) uint4 sa[32 * CH];
+
+  const int t = threadIdx.x, lane = t & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(t >> 6);
+  const int n0 = blockIdx.x * 64 + wave * 16;
+  const int split = blockIdx.y;
+  const int kbeg = split * KS;
+  const bf16_t* A = (const bf16_t*)g.A;
+  const bf16_t* B = (const bf16_t*)g.B;
+
+  // LDS slot p = 256 q + t holds chunk (p % CH) ^ (row % 8) of activation row p / CH
+#pragma unroll
+  for (int q = 0; q < AI; ++q) {
+    const int p = q * 256 + t, row = p / CH, sl = p % CH;
+    const int m = min(row, g.M - 1);
+    const bf16_t* src = A + (size_t)m * g.lda + kbeg + 8 * (sl ^ (row & 7));
+    __builtin_amdgcn_global_load_lds((gbl_void_t)src, (lds_void_t)(sa + q * 256 + (t & ~63)), 16, 0, 0);
+  }
+  __builtin_amdgcn_sched_barrier(0);
+  uint4 bw[KW];
+  const bf16_t* brow = B + (size_t)(n0 + (lane & 15)) * g.K + kbeg + 8 * (lane >> 4);
+#pragma unroll
+  for (int ks = 0; ks < KW; ++ks) bw[ks] = *(const uint4*)(brow + 32 * ks);
+  __builtin_amdgcn_sched_barrier(0);
+  // the activation slice (issued first) has landed once at most KW loads are pending;
+  // a bare barrier (no fence) leaves the weight loads in flight
+  wait_vmcnt(KW);
+  asm volatile("s_barrier" ::: "memory");
+
+  f32x4 acc0 = {0.f, 0.f, 0.f, 0.f}, acc1 = {0.f, 0.f, 0.f, 0.f};
+  const int r0 = lane & 15, cq = lane >> 4;
+#pragma unroll
+  for (int ks = 0; ks < KW; ++ks) {
+    const int c = 4 * ks + cq;
+    const bf16x8 a0 = __builtin_bit_cast(bf16x8, sa[r0 * CH + (c ^ (r0 & 7))]);
+    const bf16x8 a1 = __builtin_bit_cast(bf16x8, sa[(16 + r0) * CH + (c ^ (r0 & 7))]);
+    const bf16x8 b = __builtin_bit_cast(bf16x8, bw[ks]);
+    acc0 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a0, b, acc0, 0, 0, 0);
+    acc1 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a1, b, acc1, 0, 0, 0);
+  }
+  // lane l: column n0 + l % 16, rows 4 (l / 16) + i of each 16-row block
+  float* C = (float*)g.C + (size_t)split * g.M * g.ldc + n0 + (lane & 15);
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int m = 4 * cq + i;
+    if (m < g.M) C[(size_t)m * g.ldc] = acc0[i];
+    if (m + 16 < g.M) C[(size_t)(m + 16) * g.ldc] = acc1[i];
+  }
+}
+
 // ------------------------------------------------------------------ fp32 GEMM (T)
 // Plain LDS-tiled FMA kernel for the fp32 configuration: 64x64 tile, 4x4 per thread.
 __global__ __launch_bounds__(256) void k_gemm_f32(GemmArgs g) {
@@ -504,7 +571,16 @@ __global__ __launch_bounds__(256) void k_gemm_f32(GemmArgs g) {
 // ------------------------------------------------------------------------ dispatch
 constexpr int SPLITK_WG = 400;    // work-groups a decode GEMM aims for
 constexpr int SPLITK_MINK = 128;  // shortest K range of one split
+// k_gemv takes bf16 weights, M <= 32 and splits of 256 or 512 along K (at most 32)
+static int gemv_splits(int M, int N, int K, int wfmt) {
+  if (wfmt != W_BF16 || M > 32 || N % 64) return 0;
+  if (K % 512 == 0 && (N / 64) * (K / 512) >= 300 && K / 512 <= 32) return K / 512;
+  if (K % 256 == 0 && K / 256 <= 32) return K / 256;
+  return 0;
+}
+
 int gemm_pick_splits(int M, int N, int K, int wfmt) {
+  if (const int s = gemv_splits(M, N, K, wfmt)) return s;
   // small-M (decode) tiles are BN = 64 wide (128 for MXFP8); split K until there are
   // enough work-groups to keep the weight stream in flight (each split a multiple of 64,
   // not too short)
@@ -728,128 +804,146 @@ __global__ __launch_bounds__(512) void k_gemm_pp(GemmArgs g) {
     return wn * TN + j * 32;
   };
 
-  f32x16 acc[FM][FN];
-#pragma unroll
-  for (int i = 0; i < FM; ++i)
-#pragma unroll
-    for (int j = 0; j < FN; ++j)
-#pragma unroll
-      for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.f;
-  bf16x8 af[KST][FM], bfr[KST][FN];
-
-  auto read_phase = [&](auto S) {
-    // lane made opaque here, so that the fragment addresses derived from it are
-    // recomputed in each phase instead of being held in registers across the loop
-    int ln = lane;
-    asm volatile("" : "+v"(ln));
-    const uint4* As = stage(S);
-    const uint4* Bs = As + ACH;
-#pragma unroll
-    for (int ks = 0; ks < KST; ++ks) {
-      const int ch = ks * 2 + (ln >> 5);
-#pragma unroll
-      for (int i = 0; i < FM; ++i)
-        af[ks][i] = __builtin_bit_cast(bf16x8, As[swzc<CPR>(wm * TM + i * 32 + (ln & 31), ch)]);
-#pragma unroll
-      for (int j = 0; j < FN; ++j)
-        bfr[ks][j] = __builtin_bit_cast(bf16x8, Bs[swzc<CPR>(bblock(j) + (ln & 31), ch)]);
-    }
-    // group 1 also waits for the slice it streamed in during its last compute phase
-    if (grp == 1) asm volatile("s_waitcnt vmcnt(0) lgkmcnt(0)\n\ts_barrier" ::: "memory");
-    else asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
-    __builtin_amdgcn_sched_barrier(0);
-  };
-  constexpr int NMF = KST * FM * FN;  // MFMAs per slice
-  // compute phase of slice it, in stage S; group 1 streams slice it + 2 into that stage,
-  // load q right after MFMA q * NMF / NI so that the NI loads spread over the phase
-  auto compute_phase = [&](auto S, int it) {
-    const bool ld = grp == 1 && it + 2 < nk;  // wave-uniform
-    int va = voA, vb = voB;
-    asm volatile("" : "+v"(va), "+v"(vb));
-#pragma unroll
-    for (int ks = 0; ks < KST; ++ks)
-#pragma unroll
-      for (int i = 0; i < FM; ++i)
-#pragma unroll
-        for (int j = 0; j < FN; ++j) {
-          acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[ks][i], bfr[ks][j], acc[i][j], 0, 0, 0);
-          const int idx = (ks * FM + i) * FN + j;
-#pragma unroll
-          for (int q = 0; q < NI; ++q)
-            if (q * NMF / NI == idx && ld) issue_one(S, PBK * (it + 2), va, vb, q);
-        }
-    __builtin_amdgcn_sched_barrier(0);
-    asm volatile("s_barrier" ::: "memory");
-    __builtin_amdgcn_sched_barrier(0);
-  };
-
-  using S0 = std::integral_constant<int, 0>;
-  using S1 = std::integral_constant<int, 1>;
-  if (grp == 1) {  // slices 0 and 1
-#pragma unroll
-    for (int q = 0; q < NI; ++q) issue_one(S0{}, 0, voA, voB, q);
-    if (nk > 1) {
-#pragma unroll
-      for (int q = 0; q < NI; ++q) issue_one(S1{}, PBK, voA, voB, q);
-    }
-    asm volatile("s_waitcnt vmcnt(0)\n\ts_barrier\n\ts_barrier" ::: "memory");  // + one phase behind
-  } else {
-    asm volatile("s_barrier" ::: "memory");
-  }
-  __builtin_amdgcn_sched_barrier(0);
-  for (int it = 0; it < nk; it += 2) {
-    read_phase(S0{});
-    compute_phase(S0{}, it);
-    if (it + 1 < nk) {
-      read_phase(S1{});
-      compute_phase(S1{}, it + 1);
-    }
-  }
-  if constexpr (EPI == EPI_STORE_ACT || EPI == EPI_SWIGLU) {
-    // bf16 outputs through LDS: every LDS read of the main loop is done (group 0's last
-    // barrier follows group 1's last read phase; no loads are in flight), so each wave
-    // writes its output block into its own LDS region and stores it back as 16-byte
-    // chunks of 8 consecutive columns. The two lane halves of a write hold rows r and
-    // r + 4: rows are padded by 32 bytes where the region allows, else (128-byte rows)
-    // the 64-byte halves of a row swap when bit 2 of the row is set, so that the halves
-    // land on different banks.
-    constexpr int TNO = EPI == EPI_SWIGLU ? TN / 2 : TN;  // output columns per wave
-    constexpr bool PAD = 4 * TM * (TNO * 2 + 32) <= (ACH + BCH) * 16;
-    constexpr int RS = PAD ? TNO * 2 + 32 : TNO * 2;      // LDS row stride (bytes)
-    static_assert(4 * TM * RS <= (ACH + BCH) * 16, "output staging fits one stage array");
-    static_assert(PAD || RS == 128, "swizzled staging assumes 128-byte rows");
-    auto soff = [&](int row, int byte) { return row * RS + (PAD ? byte : byte ^ (((row >> 2) & 1) << 6)); };
-    unsigned char* reg = (unsigned char*)(grp == 0 ? sm0 : sm1) + w4 * TM * RS;
-    const int l32 = lane & 31, lh = lane >> 5;
+  // Everything from here on is instantiated once per wave group, so that the group's
+  // role (who streams the slices, which waits it owns) is known at compile time and
+  // its loop is one straight run of MFMAs and loads.
+  auto body = [&](auto G) {
+    constexpr bool G1 = decltype(G)::value;
+    f32x16 acc[FM][FN];
 #pragma unroll
     for (int i = 0; i < FM; ++i)
 #pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        const int row = i * 32 + 8 * (r >> 2) + 4 * lh + (r & 3);
+      for (int j = 0; j < FN; ++j)
 #pragma unroll
-        for (int j = 0; j < (EPI == EPI_SWIGLU ? FN / 2 : FN); ++j) {
-          float v = acc[i][j][r];
-          if constexpr (EPI == EPI_SWIGLU) {
-            const float up = acc[i][j + FN / 2][r];
-            v = v / (1.f + __expf(-v)) * up;
-          }
-          *(bf16_t*)(reg + soff(row, (j * 32 + l32) * 2)) = f2bf(v);
-        }
+        for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.f;
+    bf16x8 af[KST][FM], bfr[KST][FN];
+
+    auto read_phase = [&](auto S) {
+      // lane made opaque here, so that the fragment addresses derived from it are
+      // recomputed in each phase instead of being held in registers across the loop
+      int ln = lane;
+      asm volatile("" : "+v"(ln));
+      const uint4* As = stage(S);
+      const uint4* Bs = As + ACH;
+#pragma unroll
+      for (int ks = 0; ks < KST; ++ks) {
+        const int ch = ks * 2 + (ln >> 5);
+#pragma unroll
+        for (int i = 0; i < FM; ++i)
+          af[ks][i] = __builtin_bit_cast(bf16x8, As[swzc<CPR>(wm * TM + i * 32 + (ln & 31), ch)]);
+#pragma unroll
+        for (int j = 0; j < FN; ++j)
+          bfr[ks][j] = __builtin_bit_cast(bf16x8, Bs[swzc<CPR>(bblock(j) + (ln & 31), ch)]);
       }
-    constexpr int CPRO = TNO / 8;  // 16-byte chunks per output row
-    static_assert((TM * CPRO) % 64 == 0, "whole store instructions per wave");
-    const int ocol0 = EPI == EPI_SWIGLU ? n_tile * (BN / 2) + wn * TNO : n_tile * BN + wn * TNO;
-    const int orow0 = m0 + wm * TM;
+      // group 1 also waits for the slice it streamed in during its last compute phase
+      if constexpr (G1) asm volatile("s_waitcnt vmcnt(0) lgkmcnt(0)\n\ts_barrier" ::: "memory");
+      else asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+      __builtin_amdgcn_sched_barrier(0);
+    };
+    constexpr int NMF = KST * FM * FN;  // MFMAs per slice
+    // compute phase of slice it, in stage S. With LD (group 1, while slice it + 2 exists)
+    // the wave streams slice it + 2 into that stage, load q right after MFMA q * NMF / NI
+    // so that the NI loads spread over the phase; LD is a compile-time flag, so the
+    // phase's MFMAs and loads form one straight run of instructions.
+    auto compute_phase = [&](auto S, int it, auto LD) {
+      int va = voA, vb = voB;
+      asm volatile("" : "+v"(va), "+v"(vb));
 #pragma unroll
-    for (int q = 0; q < TM * CPRO / 64; ++q) {
-      const int idx = q * 64 + lane, row = idx / CPRO, ch = idx % CPRO;
-      const uint4 v = *(const uint4*)(reg + soff(row, ch * 16));
-      if (orow0 + row < g.M) *(uint4*)((bf16_t*)g.C + (size_t)(orow0 + row) * g.ldc + ocol0 + 8 * ch) = v;
+      for (int ks = 0; ks < KST; ++ks)
+#pragma unroll
+        for (int i = 0; i < FM; ++i)
+#pragma unroll
+          for (int j = 0; j < FN; ++j) {
+            acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[ks][i], bfr[ks][j], acc[i][j], 0, 0, 0);
+            if constexpr (decltype(LD)::value) {
+              const int idx = (ks * FM + i) * FN + j;
+#pragma unroll
+              for (int q = 0; q < NI; ++q)
+                if (q * NMF / NI == idx) issue_one(S, PBK * (it + 2), va, vb, q);
+            }
+          }
+      __builtin_amdgcn_sched_barrier(0);
+      asm volatile("s_barrier" ::: "memory");
+      __builtin_amdgcn_sched_barrier(0);
+    };
+
+    using S0 = std::integral_constant<int, 0>;
+    using S1 = std::integral_constant<int, 1>;
+    if constexpr (G1) {  // slices 0 and 1
+#pragma unroll
+      for (int q = 0; q < NI; ++q) issue_one(S0{}, 0, voA, voB, q);
+      if (nk > 1) {
+#pragma unroll
+        for (int q = 0; q < NI; ++q) issue_one(S1{}, PBK, voA, voB, q);
+      }
+      asm volatile("s_waitcnt vmcnt(0)\n\ts_barrier\n\ts_barrier" ::: "memory");  // + one phase behind
+    } else {
+      asm volatile("s_barrier" ::: "memory");
     }
-  } else {
-    gemm_epilogue32<BM, BN, WMW, WNW, EPI>(g, acc, n_tile, m0, wm, wn, lane);
-  }
-  if (grp == 0) asm volatile("s_barrier" ::: "memory");  // matches group 1's extra first barrier
+    __builtin_amdgcn_sched_barrier(0);
+    using LD = std::integral_constant<bool, G1>;  // group 1 streams the slices in
+    using LDN = std::false_type;
+    // nk is even (the launcher checks): slices it + 2 and it + 3 exist for every pair
+    // but the last
+    int it = 0;
+    for (; it + 2 < nk; it += 2) {
+      read_phase(S0{});
+      compute_phase(S0{}, it, LD{});
+      read_phase(S1{});
+      compute_phase(S1{}, it + 1, LD{});
+    }
+    read_phase(S0{});
+    compute_phase(S0{}, it, LDN{});
+    read_phase(S1{});
+    compute_phase(S1{}, it + 1, LDN{});
+    if constexpr (EPI == EPI_STORE_ACT || EPI == EPI_SWIGLU) {
+      // bf16 outputs through LDS: every LDS read of the main loop is done (group 0's last
+      // barrier follows group 1's last read phase; no loads are in flight), so each wave
+      // writes its output block into its own LDS region and stores it back as 16-byte
+      // chunks of 8 consecutive columns. The two lane halves of a write hold rows r and
+      // r + 4: rows are padded by 32 bytes where the region allows, else (128-byte rows)
+      // the 64-byte halves of a row swap when bit 2 of the row is set, so that the halves
+      // land on different banks.
+      constexpr int TNO = EPI == EPI_SWIGLU ? TN / 2 : TN;  // output columns per wave
+      constexpr bool PAD = 4 * TM * (TNO * 2 + 32) <= (ACH + BCH) * 16;
+      constexpr int RS = PAD ? TNO * 2 + 32 : TNO * 2;      // LDS row stride (bytes)
+      static_assert(4 * TM * RS <= (ACH + BCH) * 16, "output staging fits one stage array");
+      static_assert(PAD || RS == 128, "swizzled staging assumes 128-byte rows");
+      auto soff = [&](int row, int byte) { return row * RS + (PAD ? byte : byte ^ (((row >> 2) & 1) << 6)); };
+      unsigned char* reg = (unsigned char*)(G1 ? sm1 : sm0) + w4 * TM * RS;
+      const int l32 = lane & 31, lh = lane >> 5;
+#pragma unroll
+      for (int i = 0; i < FM; ++i)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const int row = i * 32 + 8 * (r >> 2) + 4 * lh + (r & 3);
+#pragma unroll
+          for (int j = 0; j < (EPI == EPI_SWIGLU ? FN / 2 : FN); ++j) {
+            float v = acc[i][j][r];
+            if constexpr (EPI == EPI_SWIGLU) {
+              const float up = acc[i][j + FN / 2][r];
+              v = v / (1.f + __expf(-v)) * up;
+            }
+            *(bf16_t*)(reg + soff(row, (j * 32 + l32) * 2)) = f2bf(v);
+          }
+        }
+      constexpr int CPRO = TNO / 8;  // 16-byte chunks per output row
+      static_assert((TM * CPRO) % 64 == 0, "whole store instructions per wave");
+      const int ocol0 = EPI == EPI_SWIGLU ? n_tile * (BN / 2) + wn * TNO : n_tile * BN + wn * TNO;
+      const int orow0 = m0 + wm * TM;
+#pragma unroll
+      for (int q = 0; q < TM * CPRO / 64; ++q) {
+        const int idx = q * 64 + lane, row = idx / CPRO, ch = idx % CPRO;
+        const uint4 v = *(const uint4*)(reg + soff(row, ch * 16));
+        if (orow0 + row < g.M) *(uint4*)((bf16_t*)g.C + (size_t)(orow0 + row) * g.ldc + ocol0 + 8 * ch) = v;
+      }
+    } else {
+      gemm_epilogue32<BM, BN, WMW, WNW, EPI>(g, acc, n_tile, m0, wm, wn, lane);
+    }
+    if constexpr (!G1) asm volatile("s_barrier" ::: "memory");  // matches group 1's extra first barrier
+  };
+  if (grp == 1) body(std::true_type{});
+  else body(std::false_type{});
 }
 
 // MXFP8 (W8A16) split-K tiles for decode-sized M, on v_mfma_f32_32x32x16_bf16. The
@@ -1143,13 +1237,14 @@ static hipError_t go_big(const GemmArgs& g, hipStream_t st, int n) {
   // 16-byte chunks
   if ((long)g.N * g.K >= (1L << 30) || g.lda >= (1 << 20)) return hipErrorNotSupported;
   if (EPI != EPI_F32 && (g.ldc % 8 != 0 || ((uintptr_t)g.C & 15) != 0)) return hipErrorNotSupported;
-  if (n % 256 == 0 && (EPI == EPI_SWIGLU || n / 256 * ((g.M + 255) / 256) >= 256)) {
+  const bool pp = (g.K / BK) % 2 == 0;  // the ping-pong tiles take K slices in pairs
+  if (pp && n % 256 == 0 && (EPI == EPI_SWIGLU || n / 256 * ((g.M + 255) / 256) >= 256)) {
     dim3 grid(n / 256, (g.M + 255) / 256);
     hipLaunchKernelGGL((k_gemm_pp<256, EPI>), grid, dim3(512), 0, st, g);
     return hipGetLastError();
   }
   if constexpr (EPI != EPI_SWIGLU)
-    if (n % 160 == 0) {
+    if (pp && n % 160 == 0) {
       dim3 grid(n / 160, (g.M + 255) / 256);
       hipLaunchKernelGGL((k_gemm_pp<160, EPI>), grid, dim3(512), 0, st, g);
       return hipGetLastError();
@@ -1184,6 +1279,12 @@ hipError_t launch_gemm(const GemmArgs& gin, hipStream_t st) {
     case EPI_PARTIAL:  // small M (decode): stream the weights, split K
       if (g.N % 64) return hipErrorInvalidValue;
       if (bf) {
+        if (g.M <= 32 && (g.K / g.splits == 256 || g.K / g.splits == 512)) {
+          dim3 grid(g.N / 64, g.splits);
+          if (g.K / g.splits == 512) hipLaunchKernelGGL(k_gemv<16>, grid, dim3(256), 0, st, g);
+          else hipLaunchKernelGGL(k_gemv<8>, grid, dim3(256), 0, st, g);
+          return hipGetLastError();
+        }
         if (g.M <= 32) return go_pipe<32, 64, 1, 4, EPI_PARTIAL, 4, 64>(g, st, g.N / 64);
         if (g.M <= 64) return go_pipe<64, 64, 1, 4, EPI_PARTIAL, 4, 64>(g, st, g.N / 64);
         return go_pipe<128, 64, 1, 4, EPI_PARTIAL, 3, 64>(g, st, g.N / 64);

@@ -43,6 +43,7 @@ def check(out, ref, bf16_out):
     (150, 6400, 2560, None, None),    # too few tiles for 256x256: 256x160 tiles
     (150, 6400, 2560, None, 6408),    # output row stride > N (16-byte stores)
     (300, 6400, 2560, None, 6404),    # output rows not 16-byte aligned: register-staged tiles
+    (600, 6400, 2624, None, None),    # odd number of 64-wide K slices: not the ping-pong tiles
 ])
 def test_store_bf16(M, N, K, lda, ldc):
     A, B = operands(M, N, K, 1, lda)
