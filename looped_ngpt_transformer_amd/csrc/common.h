@@ -18,12 +18,8 @@ constexpr float NORM_EPS = 1e-12f;
 
 __device__ __forceinline__ float bf2f(bf16_t h) { return __uint_as_float(((uint32_t)h) << 16); }
 
-// float -> bf16, round to nearest even (inputs here are finite)
-__device__ __forceinline__ bf16_t f2bf(float f) {
-  uint32_t u = __float_as_uint(f);
-  u += 0x7FFFu + ((u >> 16) & 1u);
-  return (bf16_t)(u >> 16);
-}
+// float -> bf16, round to nearest even (gfx950's v_cvt_pk_bf16_f32, one instruction)
+__device__ __forceinline__ bf16_t f2bf(float f) { return __builtin_bit_cast(bf16_t, (__bf16)f); }
 
 // two floats -> packed bf16 pair (a in the low half), round to nearest even, with the
 // hardware conversion (v_cvt_pk_bf16_f32)
@@ -123,6 +119,11 @@ __device__ __forceinline__ float sum_splits(const float* p, size_t stride, int n
   return t;
 }
 
+// 1 / (1 + e^-x) and x / (1 + e^-x) with the hardware reciprocal (about 1 ulp; every
+// use ends in a bf16 value or a product with one), in place of an IEEE division
+__device__ __forceinline__ float sigmoid(float x) { return __builtin_amdgcn_rcpf(1.f + __expf(-x)); }
+__device__ __forceinline__ float silu(float x) { return x * sigmoid(x); }
+
 // sigmoid gate value for (row m, channel c) from the projection output (bf16 [M, ld]
 // or float split partials [splits][M][ld])
 __device__ __forceinline__ float gate_at(const void* g, int f32, int ld, int splits, size_t sstride,
@@ -133,7 +134,7 @@ __device__ __forceinline__ float gate_at(const void* g, int f32, int ld, int spl
   } else {
     x = bf2f(((const bf16_t*)g)[(size_t)m * ld + c]);
   }
-  return 1.f / (1.f + __expf(-x));
+  return sigmoid(x);
 }
 
 }  // namespace dory

@@ -373,7 +373,7 @@ __global__ __launch_bounds__(PF_THREADS) void k_attn_prefill(AttnArgs a) {
 #pragma unroll
           for (int r = 0; r < 4; ++r) {
             const float x = __uint_as_float((gw[r >> 1] >> (16 * (r & 1))) << 16);
-            v[r] *= 1.f / (1.f + __expf(-x));
+            v[r] *= sigmoid(x);
           }
         }
         uint2 ov;

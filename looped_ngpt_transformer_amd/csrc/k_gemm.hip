@@ -94,7 +94,7 @@ __device__ __forceinline__ void gemm_epilogue(const GemmArgs& g, f32x4 (&acc)[BM
 #pragma unroll
         for (int j = 0; j < FN / 2; ++j) {
           const float gt = acc[i][j][r], up = acc[i][j + FN / 2][r];
-          H[(size_t)m * g.ldc + c0 + j * 16] = f2bf(gt / (1.f + __expf(-gt)) * up);
+          H[(size_t)m * g.ldc + c0 + j * 16] = f2bf(silu(gt) * up);
         }
       }
     }
@@ -143,7 +143,7 @@ __device__ __forceinline__ void gemm_epilogue32(const GemmArgs& g, f32x16 (&acc)
 #pragma unroll
         for (int j = 0; j < FN / 2; ++j) {
           const float gt = acc[i][j][r], up = acc[i][j + FN / 2][r];
-          H[(size_t)m * g.ldc + c0 + j * 32] = f2bf(gt / (1.f + __expf(-gt)) * up);
+          H[(size_t)m * g.ldc + c0 + j * 32] = f2bf(silu(gt) * up);
         }
       }
     return;
@@ -922,7 +922,7 @@ __global__ __launch_bounds__(512) void k_gemm_pp(GemmArgs g) {
             float v = acc[i][j][r];
             if constexpr (EPI == EPI_SWIGLU) {
               const float up = acc[i][j + FN / 2][r];
-              v = v / (1.f + __expf(-v)) * up;
+              v = silu(v) * up;
             }
             *(bf16_t*)(reg + soff(row, (j * 32 + l32) * 2)) = f2bf(v);
           }

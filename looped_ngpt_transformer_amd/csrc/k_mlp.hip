@@ -19,7 +19,7 @@ __global__ __launch_bounds__(256) void k_swiglu(const float* gu, int splits, int
   for (int i = b * 1024 + threadIdx.x; i < i1; i += blockDim.x) {
     const float g = sum_splits(gu + row + i, sstride, splits);
     const float u = sum_splits(gu + row + I + i, sstride, splits);
-    st<T>(h, (size_t)m * I + i, g / (1.f + __expf(-g)) * u);
+    st<T>(h, (size_t)m * I + i, silu(g) * u);
   }
 }
 
