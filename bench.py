@@ -75,6 +75,8 @@ def parse():
     ap.add_argument("--no-decode-leg", action="store_true", help="P: skip the 72-layer decode leg")
     ap.add_argument("--decode-steps", type=int, default=8, help="decode leg: timed steps per k")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-gemm-context", action="store_true",
+                    help="P: skip the sustained-MFMA and platform-BLAS measurements")
     ap.add_argument("--copy-probe", action="store_true",
                     help="run out = src * 1 over 1 GiB first (counter calibration for rocprofv3 --pmc)")
     return ap.parse_args()
@@ -272,6 +274,8 @@ def bench_prefill(args, torch, synth, D, DoryRuntime):
     rt.close()
     del rt
     torch.cuda.empty_cache()
+    if wl == "P" and not args.no_gemm_context:
+        out["gemm_context"] = gemm_context(torch, D, shape, tokens)
     if wl == "P" and not args.no_decode_leg:
         out["decode_leg"] = decode_leg(args, torch, synth, D, DoryRuntime)
     if not args.no_cpu_baseline and wl in ("P", "T"):
@@ -280,6 +284,76 @@ def bench_prefill(args, torch, synth, D, DoryRuntime):
         out["cpu_baseline"] = cb
         out["parity_prefix"] = par
     return out
+
+
+def gemm_context(torch, D, shape, M):
+    """What bounds the projection GEMMs on this device, measured beside them (context for
+    the roofline, not the headline):
+      * mfma_sustained: the rate of the bf16 matrix instruction itself, every compute unit
+        running independent chains on register operands (dory_test_mfma_rate). Under
+        dense matrix work the chip holds a lower clock than the one its 2.5 PFLOP/s is
+        quoted at; this is the practical ceiling;
+      * the four projection shapes at this prefill's M, each timed alone (50 back-to-back
+        launches, HIP events): through dory_test_gemm (this library's tiles), and through
+        torch.mm (the platform's BLAS library, hipBLASLt) on the same bf16 operands."""
+    log("[bench] gemm context: sustained MFMA rate, projection shapes vs the platform BLAS")
+    n_cu = torch.cuda.get_device_properties(0).multi_processor_count
+    cyc = torch.zeros(n_cu, dtype=torch.int64, device="cuda")
+    sink = torch.zeros(n_cu * 512, dtype=torch.float32, device="cuda")
+    iters = 20000
+    D.dory_test_mfma_rate(1000, cyc, sink)
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    n_wg = D.dory_test_mfma_rate(iters, cyc, sink)
+    e1.record()
+    torch.cuda.synchronize()
+    t = e0.elapsed_time(e1) / 1e3
+    mf_tflops = n_wg * 8 * 8 * iters * 32768.0 / t / 1e12
+    clock = float(cyc.double().mean()) / t / 1e9
+    H, I = shape["hidden"], shape["intermediate"]
+    qd, kd = shape["n_q_heads"] * shape["head_dim"], shape["n_kv_heads"] * shape["head_dim"]
+    nqkvg = qd + 2 * kd + (qd if shape["attn_gate"] else 0)
+    shapes = [("qkvg", nqkvg, H, D.EPI_STORE_BF16), ("o", H, qd, D.EPI_STORE_BF16),
+              ("gate_up", 2 * I, H, D.EPI_SWIGLU), ("down", H, I, D.EPI_STORE_BF16)]
+    g = torch.Generator(device="cuda").manual_seed(7)
+
+    def timed(fn, reps=50):
+        for _ in range(5):
+            fn()
+        torch.cuda.synchronize()
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record()
+        for _ in range(reps):
+            fn()
+        b.record()
+        torch.cuda.synchronize()
+        return a.elapsed_time(b) * 1e3 / reps
+
+    per, ours_us, blas_us, flops = {}, 0.0, 0.0, 0.0
+    for name, N, K, epi in shapes:
+        A = (torch.randn((M, K), generator=g, device="cuda") * 0.1).to(torch.bfloat16)
+        B = (torch.randn((N, K), generator=g, device="cuda") * 0.02).to(torch.bfloat16)
+        C = torch.empty((M, N // 2 if epi == D.EPI_SWIGLU else N), dtype=torch.bfloat16, device="cuda")
+        Cb = torch.empty((M, N), dtype=torch.bfloat16, device="cuda")
+        Bt = B.t()
+        u_o = timed(lambda: D.dory_test_gemm(A, B, epi, out=C))
+        u_b = timed(lambda: torch.mm(A, Bt, out=Cb))
+        f = 2.0 * M * N * K
+        per[name] = {"M": M, "N": N, "K": K, "us": round(u_o, 1), "blas_us": round(u_b, 1),
+                     "frac": round(f / u_o / 1e6 / PEAK_BF16_TFLOPS, 4),
+                     "blas_frac": round(f / u_b / 1e6 / PEAK_BF16_TFLOPS, 4)}
+        ours_us, blas_us, flops = ours_us + u_o, blas_us + u_b, flops + f
+        del A, B, C, Cb
+    torch.cuda.empty_cache()
+    return {"mfma_sustained": {"tflops": round(mf_tflops, 1), "frac_of_peak": round(mf_tflops / PEAK_BF16_TFLOPS, 4),
+                               "clock_ghz": round(clock, 3), "work_groups": n_wg},
+            "shapes": per,
+            "ours": {"us": round(ours_us, 1), "frac": round(flops / ours_us / 1e6 / PEAK_BF16_TFLOPS, 4),
+                     "frac_of_sustained": round(flops / ours_us / 1e6 / mf_tflops, 4)},
+            "blas": {"library": "torch.mm (hipBLASLt)", "us": round(blas_us, 1),
+                     "frac": round(flops / blas_us / 1e6 / PEAK_BF16_TFLOPS, 4),
+                     "frac_of_sustained": round(flops / blas_us / 1e6 / mf_tflops, 4)}}
 
 
 def decode_step_bytes(shape, k, batch, ctx):

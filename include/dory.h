@@ -328,6 +328,18 @@ int dory_test_gemm(void* stream, const void* A, int lda, const void* B, const ui
                    const float* B_gscale, int wfmt, int M, int N, int K, int epi, void* C, int ldc,
                    int* splits);
 
+/* Sustained rate of the bf16 matrix instruction the projection GEMMs run on
+ * (v_mfma_f32_32x32x16_bf16, 32768 flops each): one work-group of 8 waves per compute
+ * unit, each wave running 8 independent accumulator chains of `iters` instructions on
+ * register operands that hold non-zero data (the clock the chip sustains under dense
+ * matrix work depends on the data). Measurement support for the roofline's practical
+ * ceiling; the caller times the call on `stream`. cycles: device int64 array with one
+ * entry per compute unit, receives the shader-clock cycles each work-group spent in its
+ * loop; sink: device float array of 512 entries per compute unit (the results, so that
+ * no work is elided); *n_wg receives the number of work-groups (the compute-unit count).
+ * 1 <= iters <= 1000000, else DORY_ERR_INVALID_ARG before any device work. */
+int dory_test_mfma_rate(void* stream, int iters, long long* cycles, float* sink, int* n_wg);
+
 /* MXFP8 quantiser (arXiv §5.2: maximum scaling, group 32): w [rows, cols] device
  * (w_dtype F32 or BF16), cols % 32 == 0 -> codes [rows, cols] E4M3 bytes and scales
  * [rows, cols/32] E8M0 bytes (device). Scale 2^(floor(log2 amax) - 8), elements

@@ -526,6 +526,46 @@ __global__ __launch_bounds__(256) void k_gemv(GemmArgs g) {
   }
 }
 
+// Sustained rate of v_mfma_f32_32x32x16_bf16 on this device (the practical ceiling the
+// projection GEMMs are measured against): 8 waves per work-group (two per SIMD), each
+// running 8 independent accumulator chains of `iters` instructions on register operands
+// holding non-zero data; thread 0 records the shader-clock cycles of the loop.
+__global__ __launch_bounds__(512) void k_mfma_rate(int iters, long long* cycles, float* sink) {
+  const int t = threadIdx.x;
+  bf16x8 a, b;
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    a[i] = (__bf16)((float)((t * 7 + i * 13) % 17 - 8) * 0.0625f);
+    b[i] = (__bf16)((float)((t * 5 + i * 11) % 19 - 9) * 0.03125f);
+  }
+  f32x16 acc[8];
+#pragma unroll
+  for (int j = 0; j < 8; ++j)
+#pragma unroll
+    for (int r = 0; r < 16; ++r) acc[j][r] = 0.f;
+  __syncthreads();
+  const long long c0 = clock64();
+  for (int it = 0; it < iters; ++it) {
+#pragma unroll
+    for (int j = 0; j < 8; ++j) acc[j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, acc[j], 0, 0, 0);
+  }
+  __syncthreads();
+  const long long c1 = clock64();
+  float sum = 0.f;
+#pragma unroll
+  for (int j = 0; j < 8; ++j)
+#pragma unroll
+    for (int r = 0; r < 16; ++r) sum += acc[j][r];
+  sink[(size_t)blockIdx.x * 512 + t] = sum;
+  if (t == 0) cycles[blockIdx.x] = c1 - c0;
+}
+
+hipError_t launch_mfma_rate(int iters, int n_wg, long long* cycles, float* sink, hipStream_t st) {
+  if (iters < 1 || n_wg < 1 || !cycles || !sink) return hipErrorInvalidValue;
+  hipLaunchKernelGGL(k_mfma_rate, dim3(n_wg), dim3(512), 0, st, iters, cycles, sink);
+  return hipGetLastError();
+}
+
 // ------------------------------------------------------------------ fp32 GEMM (T)
 // Plain LDS-tiled FMA kernel for the fp32 configuration: 64x64 tile, 4x4 per thread.
 __global__ __launch_bounds__(256) void k_gemm_f32(GemmArgs g) {

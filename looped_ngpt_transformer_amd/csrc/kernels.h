@@ -40,6 +40,9 @@ hipError_t launch_expand_mxfp8(const uint8_t* codes, const uint8_t* scales, int6
 // Split count the launcher would use for a decode-shaped GEMM (EPI_PARTIAL).
 int gemm_pick_splits(int M, int N, int K, int wfmt);
 hipError_t launch_gemm(const GemmArgs& g, hipStream_t st);
+// n_wg work-groups of 8 waves, each running 8 chains of iters bf16 MFMAs (32x32x16);
+// cycles[n_wg] shader-clock cycles, sink[n_wg * 512] results
+hipError_t launch_mfma_rate(int iters, int n_wg, long long* cycles, float* sink, hipStream_t st);
 
 // ------------------------------------------------------- nGPT update / loop boundary
 enum Boundary {

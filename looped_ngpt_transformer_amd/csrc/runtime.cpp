@@ -1499,6 +1499,22 @@ int dory_test_gemm(void* stream, const void* A, int lda, const void* B, const ui
   return DORY_OK;
 }
 
+int dory_test_mfma_rate(void* stream, int iters, long long* cycles, float* sink, int* n_wg) {
+  int dev = 0, cus = 0;
+  if (iters < 1 || iters > 1000000 || !cycles || !sink || !n_wg || hipGetDevice(&dev) != hipSuccess ||
+      hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cus < 1) {
+    g_create_err = "bad MFMA-rate argument (or no device)";
+    return DORY_ERR_INVALID_ARG;
+  }
+  *n_wg = cus;
+  const hipError_t e = launch_mfma_rate(iters, cus, cycles, sink, (hipStream_t)stream);
+  if (e != hipSuccess) {
+    g_create_err = hipGetErrorString(e);
+    return DORY_ERR_HIP;
+  }
+  return DORY_OK;
+}
+
 int dory_quantize_mxfp8(void* stream, const void* w, int w_dtype, int64_t rows, int64_t cols,
                         uint8_t* codes, uint8_t* scales) {
   if (!w || !codes || !scales || rows < 0 || cols < 0 || cols % 32 ||

@@ -98,6 +98,7 @@ _SIGS = {
     "dory_test_inject_failure": (C.c_int, [_P, C.c_int]),
     "dory_test_gemm": (C.c_int, [_P, _P, C.c_int, _P, _P, _P, C.c_int, C.c_int, C.c_int, C.c_int, C.c_int, _P,
                                  C.c_int, C.POINTER(C.c_int)]),
+    "dory_test_mfma_rate": (C.c_int, [_P, C.c_int, _P, _P, C.POINTER(C.c_int)]),
     "dory_quantize_mxfp8": (C.c_int, [_P, _P, C.c_int, C.c_int64, C.c_int64, _P, _P]),
     "dory_quantize_nvfp4": (C.c_int, [_P, _P, C.c_int, C.c_int64, C.c_int64, _P, _P, _P]),
     "dory_bind_vocab": (C.c_int, [_P, C.POINTER(dory_vocab_weights)]),
@@ -329,6 +330,14 @@ def dory_test_gemm(A, B, epi, out=None, B_scales=None, stream=None, M=None, N=No
     _check(lib().dory_test_gemm(_stream(stream), _ptr(A), lda, _ptr(B), _ptr(B_scales), _ptr(B_gscale), wf, M, N,
                                 K, epi, _ptr(out), ldc, C.byref(splits)))
     return splits.value
+
+
+def dory_test_mfma_rate(iters, cycles, sink, stream=None):
+    """Sustained bf16 MFMA rate probe (see dory.h): cycles int64 [n_cu], sink float
+    [n_cu * 512] device tensors. Returns the number of work-groups launched."""
+    n = C.c_int(0)
+    _check(lib().dory_test_mfma_rate(_stream(stream), int(iters), _ptr(cycles), _ptr(sink), C.byref(n)))
+    return n.value
 
 
 def dory_quantize_mxfp8(w, codes, scales, stream=None):
