@@ -119,6 +119,7 @@ __global__ __launch_bounds__(256) void k_rope_kv(RopeArgs a) {
 // channel) are written whole; chunks the quarter covers only in part are written
 // element by element.
 constexpr int RT_ROWS = 16;
+constexpr int IPG = 5;  // (row, head) items a 16-lane group loads at once
 
 template <int D>
 __global__ __launch_bounds__(256) void k_rope_tile(RopeArgs a) {
@@ -140,7 +141,35 @@ __global__ __launch_bounds__(256) void k_rope_tile(RopeArgs a) {
   const bf16_t* X = (const bf16_t*)a.qkvg;
   bf16_t* Q = (bf16_t*)a.q_out;
 
+  // V rows -> LDS (16-byte chunks)
+  const int vcol0 = a.Hq * D + a.Hkv * D + hk * D;
+  for (int c = threadIdx.x; c < nrows * (D / 8); c += 256) {
+    const int i = c / (D / 8), k8 = c % (D / 8);
+    *(uint4*)(Vs + i * VR + 8 * k8) = *(const uint4*)(X + (size_t)(row0 + i) * a.Nqkvg + vcol0 + 8 * k8);
+  }
+  // (row, head) items of q heads hk*G .. hk*G+G-1 and K head hk: group gi = 4 wave + grp
+  // takes items gi, gi + 16, ...; the IPG items of a batch are loaded before any is used,
+  // so that a group keeps IPG x 32 bytes per lane in flight
+  const int items = nrows * (G + 1);
+  const int gi = wave * 4 + grp;
+  uint4 u1[IPG], u2[IPG];
+  auto load_batch = [&](int b0) {
+#pragma unroll
+    for (int u = 0; u < IPG; ++u) {
+      const int item = b0 + gi + 16 * u;
+      if (item < items && j < HC) {
+        const int i = item / (G + 1), hi = item % (G + 1);
+        const int col0 = hi == G ? a.Hq * D + hk * D : (hk * G + hi) * D;
+        const bf16_t* x = X + (size_t)(row0 + i) * a.Nqkvg + col0 + 8 * j;
+        u1[u] = *(const uint4*)x;
+        u2[u] = *(const uint4*)(x + HALF);
+      }
+    }
+  };
+  load_batch(0);
+
   // angles p * theta^(-2i/d) in double, reduced modulo 2*pi before the float sin/cos
+  // (while the first batch is in flight)
   for (int c = threadIdx.x; c < nrows * HALF; c += 256) {
     const int i = c / HALF, k = c % HALF;
     double ang = (double)(pos0 + i) * a.freq[k];
@@ -149,66 +178,61 @@ __global__ __launch_bounds__(256) void k_rope_tile(RopeArgs a) {
     sincosf((float)ang, &sn, &cs);
     CS[c] = make_float2(cs, sn);
   }
-  // V rows -> LDS (16-byte chunks)
-  const int vcol0 = a.Hq * D + a.Hkv * D + hk * D;
-  for (int c = threadIdx.x; c < nrows * (D / 8); c += 256) {
-    const int i = c / (D / 8), k8 = c % (D / 8);
-    *(uint4*)(Vs + i * VR + 8 * k8) = *(const uint4*)(X + (size_t)(row0 + i) * a.Nqkvg + vcol0 + 8 * k8);
-  }
   __syncthreads();
 
-  // rotation + norm of the q heads hk*G .. hk*G+G-1 and of K head hk, one item per group
-  const int items = nrows * (G + 1);
-  for (int it0 = wave * 4; it0 < items; it0 += 16) {
-    const int item = it0 + grp;
-    const bool act = item < items && j < HC;
-    const int i = act ? item / (G + 1) : 0, hi = act ? item % (G + 1) : 0;
-    const bool is_k = hi == G;
-    const int p = pos0 + i;
-    const int col0 = is_k ? a.Hq * D + hk * D : (hk * G + hi) * D;
-    float r1[8], r2[8];
-    float sq = 0.f;
-    if (act) {
-      const uint4 u1 = *(const uint4*)(X + (size_t)(row0 + i) * a.Nqkvg + col0 + 8 * j);
-      const uint4 u2 = *(const uint4*)(X + (size_t)(row0 + i) * a.Nqkvg + col0 + HALF + 8 * j);
-      const uint32_t w1[4] = {u1.x, u1.y, u1.z, u1.w}, w2[4] = {u2.x, u2.y, u2.z, u2.w};
-      const float2* cs = CS + i * HALF + 8 * j;
+  // rotation + norm, one item per 16-lane group (lanes j < HC hold chunk j of both halves)
+  for (int b0 = 0; b0 < items; b0 += 16 * IPG) {
+    if (b0 > 0) load_batch(b0);
 #pragma unroll
-      for (int e = 0; e < 8; ++e) {
-        const float x1 = __uint_as_float((e & 1) ? (w1[e / 2] & 0xFFFF0000u) : (w1[e / 2] << 16));
-        const float x2 = __uint_as_float((e & 1) ? (w2[e / 2] & 0xFFFF0000u) : (w2[e / 2] << 16));
-        const float2 t = cs[e];
-        r1[e] = x1 * t.x - x2 * t.y;
-        r2[e] = x1 * t.y + x2 * t.x;
-        sq += r1[e] * r1[e] + r2[e] * r2[e];
+    for (int u = 0; u < IPG; ++u) {
+      const int item = b0 + gi + 16 * u;
+      if (item >= items) break;  // uniform over the 16-lane group
+      const bool act = j < HC;
+      const int i = item / (G + 1), hi = item % (G + 1);
+      const bool is_k = hi == G;
+      const int p = pos0 + i;
+      float r1[8], r2[8];
+      float sq = 0.f;
+      if (act) {
+        const uint32_t w1[4] = {u1[u].x, u1[u].y, u1[u].z, u1[u].w}, w2[4] = {u2[u].x, u2[u].y, u2[u].z, u2[u].w};
+        const float2* cs = CS + i * HALF + 8 * j;
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+          const float x1 = __uint_as_float((e & 1) ? (w1[e / 2] & 0xFFFF0000u) : (w1[e / 2] << 16));
+          const float x2 = __uint_as_float((e & 1) ? (w2[e / 2] & 0xFFFF0000u) : (w2[e / 2] << 16));
+          const float2 t = cs[e];
+          r1[e] = x1 * t.x - x2 * t.y;
+          r2[e] = x1 * t.y + x2 * t.x;
+          sq += r1[e] * r1[e] + r2[e] * r2[e];
+        }
       }
-    }
 #pragma unroll
-    for (int m = 8; m >= 1; m >>= 1) sq += __shfl_xor(sq, m, 64);  // within the 16-lane group
-    if (!act) continue;
-    float sc = 1.f;
-    if (a.qk_norm) sc = inv_norm(sq);
-    uint32_t o1[4], o2[4];
+      for (int m = 8; m >= 1; m >>= 1) sq += __shfl_xor(sq, m, 64);  // within the 16-lane group
+      if (!act) continue;
+      float sc = 1.f;
+      if (a.qk_norm) sc = inv_norm(sq);
+      uint32_t o1[4], o2[4];
 #pragma unroll
-    for (int e = 0; e < 8; e += 2) {
-      float a0 = r1[e] * sc, a1 = r1[e + 1] * sc, b0 = r2[e] * sc, b1 = r2[e + 1] * sc;
-      if (a.qk_norm) {
-        a0 *= a.s_qk[8 * j + e];
-        a1 *= a.s_qk[8 * j + e + 1];
-        b0 *= a.s_qk[HALF + 8 * j + e];
-        b1 *= a.s_qk[HALF + 8 * j + e + 1];
+      for (int e = 0; e < 8; e += 2) {
+        float a0 = r1[e] * sc, a1 = r1[e + 1] * sc, b0v = r2[e] * sc, b1 = r2[e + 1] * sc;
+        if (a.qk_norm) {
+          a0 *= a.s_qk[8 * j + e];
+          a1 *= a.s_qk[8 * j + e + 1];
+          b0v *= a.s_qk[HALF + 8 * j + e];
+          b1 *= a.s_qk[HALF + 8 * j + e + 1];
+        }
+        o1[e / 2] = pack_bf16x2(a0, a1);
+        o2[e / 2] = pack_bf16x2(b0v, b1);
       }
-      o1[e / 2] = pack_bf16x2(a0, a1);
-      o2[e / 2] = pack_bf16x2(b0, b1);
-    }
-    if (!is_k) {
-      bf16_t* q = Q + (size_t)(row0 + i) * a.Hq * D + (hk * G + hi) * D;
-      *(uint4*)(q + 8 * j) = make_uint4(o1[0], o1[1], o1[2], o1[3]);
-      *(uint4*)(q + HALF + 8 * j) = make_uint4(o2[0], o2[1], o2[2], o2[3]);
-    } else {
-      bf16_t* kb = kv_kblock(kv_page<bf16_t>(a.kv, seq, a.stream_idx, p), a.kv, hk);
-      *(uint4*)(kb + kv_k_off(p % PAGE, 8 * j, D)) = make_uint4(o1[0], o1[1], o1[2], o1[3]);
-      *(uint4*)(kb + kv_k_off(p % PAGE, HALF + 8 * j, D)) = make_uint4(o2[0], o2[1], o2[2], o2[3]);
+      if (!is_k) {
+        bf16_t* q = Q + (size_t)(row0 + i) * a.Hq * D + (hk * G + hi) * D;
+        *(uint4*)(q + 8 * j) = make_uint4(o1[0], o1[1], o1[2], o1[3]);
+        *(uint4*)(q + HALF + 8 * j) = make_uint4(o2[0], o2[1], o2[2], o2[3]);
+      } else {
+        bf16_t* kb = kv_kblock(kv_page<bf16_t>(a.kv, seq, a.stream_idx, p), a.kv, hk);
+        *(uint4*)(kb + kv_k_off(p % PAGE, 8 * j, D)) = make_uint4(o1[0], o1[1], o1[2], o1[3]);
+        *(uint4*)(kb + kv_k_off(p % PAGE, HALF + 8 * j, D)) = make_uint4(o2[0], o2[1], o2[2], o2[3]);
+      }
     }
   }
 
