@@ -438,8 +438,40 @@ def decode_leg(args, torch, synth, D, DoryRuntime):
     rt.close()
     del rt, weights
     torch.cuda.empty_cache()
+    hbm = hbm_probe(torch)
+    for r in res.values():
+        r["step_frac_of_copy"] = round(r["step_hbm_frac"] * PEAK_HBM_GBS / hbm["copy_gbs"], 4)
     return {"workload": WORKLOAD_TEXT["D"] + ", last_loop", "batch": batch, "context": ctx_len,
-            "steps": steps, "warmup": warm, "by_loops": res}
+            "steps": steps, "warmup": warm, "by_loops": res, "hbm_measured": hbm}
+
+
+def hbm_probe(torch):
+    """What HBM delivers to plain kernels on this device, for the decode fractions: a
+    1 GiB copy (bytes read + written per second) and row sums over 1 GiB (rows of 4 KiB:
+    bytes read per second), each the best of 10 timed launches."""
+    n = 2 ** 28
+    src = torch.ones(n, dtype=torch.float32, device="cuda")
+    dst = torch.empty_like(src)
+
+    def best(fn):
+        ts = []
+        for i in range(13):
+            a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            a.record()
+            fn()
+            b.record()
+            torch.cuda.synchronize()
+            if i >= 3:
+                ts.append(a.elapsed_time(b) / 1e3)
+        return min(ts)
+
+    rows = torch.empty(n // 1024, dtype=torch.float32, device="cuda")
+    t_copy = best(lambda: dst.copy_(src))
+    t_read = best(lambda: torch.sum(src.view(-1, 1024), dim=1, out=rows))
+    del src, dst
+    torch.cuda.empty_cache()
+    return {"copy_gbs": round(2 * 4 * n / t_copy / 1e9, 1), "read_gbs": round(4 * n / t_read / 1e9, 1),
+            "peak_gbs": PEAK_HBM_GBS}
 
 
 def bench_decode(args, torch, synth, D, DoryRuntime):
@@ -543,6 +575,10 @@ def bench_decode(args, torch, synth, D, DoryRuntime):
     if len(ks) > 1:
         out["by_loops"] = {str(kk): {"tokens_per_s": round(batch / r[0], 2), "ms_per_step": round(r[0] * 1e3, 3),
                                      "kv_bytes_in_use": r[2]} for kk, r in results.items()}
+    del weights
+    torch.cuda.empty_cache()
+    out["hbm_measured"] = hbm_probe(torch)
+    out["step_frac_of_copy"] = round(out["step_hbm_gbs"] / out["hbm_measured"]["copy_gbs"], 4)
     return out
 
 

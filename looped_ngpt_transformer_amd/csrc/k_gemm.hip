@@ -611,9 +611,11 @@ __global__ __launch_bounds__(256) void k_gemm_f32(GemmArgs g) {
 // ------------------------------------------------------------------------ dispatch
 constexpr int SPLITK_WG = 400;    // work-groups a decode GEMM aims for
 constexpr int SPLITK_MINK = 128;  // shortest K range of one split
-// k_gemv takes bf16 weights, M <= 32 and splits of 256 or 512 along K (at most 32)
+// k_gemv takes bf16 weights, M <= 32 and splits of 256 or 512 along K (at most 32); a
+// matrix with enough 64-column tiles to fill the device unsplit (the LM head) streams
+// through k_gemm_pipe without partials instead
 static int gemv_splits(int M, int N, int K, int wfmt) {
-  if (wfmt != W_BF16 || M > 32 || N % 64) return 0;
+  if (wfmt != W_BF16 || M > 32 || N % 64 || N / 64 >= SPLITK_WG) return 0;
   if (K % 512 == 0 && (N / 64) * (K / 512) >= 300 && K / 512 <= 32) return K / 512;
   if (K % 256 == 0 && K / 256 <= 32) return K / 256;
   return 0;

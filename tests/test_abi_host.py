@@ -285,3 +285,16 @@ def test_capture_and_resume_options():
         D._check(D.lib().dory_prefill(ctx, None, 1, None, None, None, None), ctx)
     assert e.value.code == D.ERR_STATE
     D.dory_destroy(ctx)
+
+
+def test_decode_split_counts():
+    """The split-K count a decode-shaped projection takes (host only: with no output the
+    call just reports it). bf16 at <= 32 rows: K ranges of 512 where that leaves >= 300
+    work-groups, else 256; a matrix whose 64-column tiles fill the device unsplit (the LM
+    head over 131072 tokens) takes no split, so its partials stay within the workspace."""
+    import torch
+    A = torch.zeros((32, 4096), dtype=torch.bfloat16)
+    B = torch.zeros((64, 64), dtype=torch.bfloat16)  # never read: no output, no launch
+    cases = {(6400, 2560): 5, (8192, 2560): 5, (2560, 2560): 10, (2560, 4096): 8, (131072, 2560): 1}
+    for (N, K), want in cases.items():
+        assert D.dory_test_gemm(A, B, D.EPI_PARTIAL, None, stream=0, M=32, N=N, K=K) == want, (N, K)
