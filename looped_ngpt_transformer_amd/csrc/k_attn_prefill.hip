@@ -24,9 +24,8 @@
 // The page's K and V blocks are stored as 1 KiB groups of 16-byte chunks in MFMA
 // fragment order; they go straight from HBM into LDS (global_load_lds) through three
 // stages: group B issues page p + 2 during its softmax phase of page p and waits for it
-// at the end of its next matrix phase, one phase before group A first reads it. The K
-// groups sit at a padded stride so that the 32x32 fragment reads are free of bank
-// conflicts. Keys beyond the chunk's last position are masked out of the softmax; their
+// at the end of its next matrix phase, one phase before group A first reads it. The
+// 32x32 fragment reads of the stages are free of bank conflicts. Keys beyond the chunk's last position are masked out of the softmax; their
 // V entries are multiplied by zero probabilities and hold zeros or stale finite values
 // (pages are cleared when first allocated).
 #include <type_traits>
@@ -52,10 +51,11 @@ __global__ __launch_bounds__(PF_THREADS) void k_attn_prefill(AttnArgs a) {
   constexpr int DC = D / 32;       // 32-channel chunks of a K fragment group
   constexpr int CB16 = D / 16;     // 16-channel blocks of V
   constexpr int NG = D / 8;        // 1 KiB groups per K (or V) block of one head
-  // K fragments read two groups DC apart in the same LDS cycle: pad their stride so the
-  // two land on opposite halves of the banks. V fragments read 256 contiguous bytes per
-  // 16 lanes.
-  constexpr int KGS = 1024 + (DC == 5 ? 128 : 128 / DC);
+  // K and V groups at a 1 KiB stride: the fragment reads (16-byte chunks of two groups
+  // DC apart for K, 256 contiguous bytes per 16 lanes for V) then take no bank
+  // conflicts (counted: a 128-byte pad on the K stride made every K read conflict
+  // two-way; 256 and 512 are conflict-free as well)
+  constexpr int KGS = 1024;
   constexpr int VGS = 1024;
   constexpr int STAGE = NG * (KGS + VGS);  // bytes per page stage
   constexpr int NSTAGE = 3;
