@@ -911,14 +911,15 @@ __global__ __launch_bounds__(512) void k_gemm_pp(GemmArgs g) {
 
     using S0 = std::integral_constant<int, 0>;
     using S1 = std::integral_constant<int, 1>;
-    if constexpr (G1) {  // slices 0 and 1
+    if constexpr (G1) {  // slices 0 and 1 (nk >= 2)
 #pragma unroll
       for (int q = 0; q < NI; ++q) issue_one(S0{}, 0, voA, voB, q);
-      if (nk > 1) {
 #pragma unroll
-        for (int q = 0; q < NI; ++q) issue_one(S1{}, PBK, voA, voB, q);
-      }
-      asm volatile("s_waitcnt vmcnt(0)\n\ts_barrier\n\ts_barrier" ::: "memory");  // + one phase behind
+      for (int q = 0; q < NI; ++q) issue_one(S1{}, PBK, voA, voB, q);
+      // slice 0 only: slice 1 is waited for at the end of this group's first read phase,
+      // before group 0 reads it
+      wait_vmcnt(NI);
+      asm volatile("s_barrier\n\ts_barrier" ::: "memory");  // + one phase behind
     } else {
       asm volatile("s_barrier" ::: "memory");
     }
