@@ -120,6 +120,11 @@ typedef struct dory_config {
  *         NVFP4 matrices hold packed codes [rows, K/2] (element 2j in the low nibble)
  *  alpha_attn, alpha_mlp [H] float: effective per-channel rates (arXiv §2: 0.05 init)
  *  s_qk   [d] float: effective query-key scale
+ *  f_*    bf16 contexts, optional: the matching matrix in fragment order, as written by
+ *         dory_arrange_weights (same bytes, another order; 16-byte aligned). When set,
+ *         projections of at most 32 rows (decode) read it instead of w_*, with one
+ *         contiguous KiB per load instruction; the results are bitwise the same. NULL:
+ *         they read w_*.
  */
 typedef struct dory_layer_weights {
   const void* w_qkvg;
@@ -137,6 +142,10 @@ typedef struct dory_layer_weights {
   const float* g_o;
   const float* g_gu;
   const float* g_down;
+  const void* f_qkvg;
+  const void* f_o;
+  const void* f_gu;
+  const void* f_down;
 } dory_layer_weights;
 
 /* Create a context for cfg. Checks shapes, formats and limits (INVALID_ARG /
@@ -320,13 +329,25 @@ int dory_test_inject_failure(dory_ctx* ctx, int at);
  * Quantised formats take epi 1 only (layers expand MXFP8 and NVFP4 matrices to bf16,
  * exactly, for the other epilogues). ldc = row stride of C in elements. The kernel and tile shape are the ones a
  * layer call would pick for these sizes (K % 64 == 0; N % 64 == 0, for epi 4 N % 128 == 0,
- * for NVFP4 N % 128 == 0). *splits receives the split count (1 unless epi 1). With
- * C == NULL the call only reports *splits. The caller owns every buffer; C must hold
+ * for NVFP4 N % 128 == 0). *splits receives the split count (1 unless epi 1). B_frag: optional
+ * fragment-order copy of a bf16 B (dory_arrange_weights), read where a layer would read
+ * it (epi 1, M <= 32). With C == NULL the call only reports *splits. The caller owns every buffer; C must hold
  * splits * M * ldc elements for epi 1. Invalid sizes return DORY_ERR_INVALID_ARG before
  * any device work. */
 int dory_test_gemm(void* stream, const void* A, int lda, const void* B, const uint8_t* B_scales,
                    const float* B_gscale, int wfmt, int M, int N, int K, int epi, void* C, int ldc,
-                   int* splits);
+                   int* splits, const void* B_frag);
+
+/* Fragment-order copy of a bf16 weight matrix, for the f_* fields of
+ * dory_layer_weights: w [N, K] row-major bf16 (device) -> out [N * K] bf16 (device,
+ * caller-owned, 16-byte aligned, not overlapping w) as 1 KiB blocks, block
+ * (n / 16) * (K / 32) + k / 32 holding rows 16 (n / 16) .. + 15 at columns
+ * 32 (k / 32) .. + 31, element (n, k) at position 8 * (16 * ((k % 32) / 8) + n % 16)
+ * + k % 8 of its block: each block is one v_mfma_f32_16x16x32_bf16 B operand in lane
+ * order. Layout of the library's own making (no page defines it); asynchronous on
+ * `stream`. N % 16 == 0 and K % 32 == 0, non-null pointers, else DORY_ERR_INVALID_ARG
+ * before any device work. */
+int dory_arrange_weights(void* stream, const void* w, int64_t N, int64_t K, void* out);
 
 /* Sustained rate of the bf16 matrix instruction the projection GEMMs run on
  * (v_mfma_f32_32x32x16_bf16, 32768 flops each): one work-group of 8 waves per compute

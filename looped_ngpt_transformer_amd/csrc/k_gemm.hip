@@ -461,6 +461,25 @@ __global__ __launch_bounds__(GT) void k_gemm_pipe(GemmArgs g) {
   gemm_epilogue<BM, BN, WMW, WNW, EPI>(g, acc, n_tile, m0, split, wm, wn, lane);
 }
 
+// Weights in fragment order for the decode GEMV: thread c copies output chunk c (16
+// bytes): block c / 64, lane l = c % 64 of that block's MFMA B operand.
+__global__ __launch_bounds__(256) void k_arrange_frag(const bf16_t* w, int64_t N, int64_t K, bf16_t* out) {
+  const int64_t c = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  if (c >= N * K / 8) return;
+  const int64_t blk = c >> 6, kb = K / 32;
+  const int l = (int)(c & 63);
+  const int64_t row = (blk / kb) * 16 + (l & 15), k0 = (blk % kb) * 32 + 8 * (l >> 4);
+  *(uint4*)(out + 8 * c) = *(const uint4*)(w + row * K + k0);
+}
+
+hipError_t launch_arrange_frag(const void* w, int64_t N, int64_t K, void* out, hipStream_t st) {
+  if (!w || !out || N < 16 || K < 32 || N % 16 || K % 32) return hipErrorInvalidValue;
+  const int64_t chunks = N * K / 8;
+  hipLaunchKernelGGL(k_arrange_frag, dim3((unsigned)((chunks + 255) / 256)), dim3(256), 0, st, (const bf16_t*)w, N, K,
+                     (bf16_t*)out);
+  return hipGetLastError();
+}
+
 // Decode GEMV for bf16 weights and at most 32 activation rows, bound by the weight
 // stream. A work-group of 4 waves owns 64 weight rows over a K range of 32 KW; each wave
 // streams its 16 rows straight into registers, all KW loads in flight before the first
@@ -468,9 +487,11 @@ __global__ __launch_bounds__(GT) void k_gemm_pipe(GemmArgs g) {
 // The activation slice (32 rows x 32 KW, rows beyond M repeat the last row) goes to LDS
 // once per work-group with direct-to-LDS loads, 16-byte chunks XOR-swizzled by row.
 // v_mfma_f32_16x16x32_bf16 with the activations as the A operand: lane l holds weight
-// row l % 16, K elements 8 (l / 16) .. + 7 of each 32-wide step (64 contiguous bytes of
-// a row per 16 lanes). Output: fp32 split-K partials, split = K range.
-template <int KW>
+// row l % 16, K elements 8 (l / 16) .. + 7 of each 32-wide step. From the row-major
+// matrix a load instruction reads 64 contiguous bytes of each of 16 rows; from the
+// fragment-order copy (FRAG) one contiguous KiB, and a wave's KW loads one contiguous
+// 16 KW KiB. Same values, same arithmetic. Output: fp32 split-K partials, split = K range.
+template <int KW, bool FRAG>
 __global__ __launch_bounds__(256) void k_gemv(GemmArgs g) {
   constexpr int KS = 32 * KW;       // K range of one work-group (one split)
   constexpr int CH = KS / 8;        // 16-byte chunks per activation row
@@ -496,9 +517,10 @@ __global__ __launch_bounds__(256) void k_gemv(GemmArgs g) {
   }
   __builtin_amdgcn_sched_barrier(0);
   uint4 bw[KW];
-  const bf16_t* brow = B + (size_t)(n0 + (lane & 15)) * g.K + kbeg + 8 * (lane >> 4);
+  const bf16_t* bsrc = FRAG ? (const bf16_t*)g.Bf + ((size_t)(n0 / 16) * (g.K / 32) + kbeg / 32) * 512 + 8 * lane
+                            : B + (size_t)(n0 + (lane & 15)) * g.K + kbeg + 8 * (lane >> 4);
 #pragma unroll
-  for (int ks = 0; ks < KW; ++ks) bw[ks] = *(const uint4*)(brow + 32 * ks);
+  for (int ks = 0; ks < KW; ++ks) bw[ks] = *(const uint4*)(bsrc + (FRAG ? 512 : 32) * ks);
   __builtin_amdgcn_sched_barrier(0);
   // the activation slice (issued first) has landed once at most KW loads are pending;
   // a bare barrier (no fence) leaves the weight loads in flight
@@ -1324,8 +1346,14 @@ hipError_t launch_gemm(const GemmArgs& gin, hipStream_t st) {
       if (bf) {
         if (g.M <= 32 && (g.K / g.splits == 256 || g.K / g.splits == 512)) {
           dim3 grid(g.N / 64, g.splits);
-          if (g.K / g.splits == 512) hipLaunchKernelGGL(k_gemv<16>, grid, dim3(256), 0, st, g);
-          else hipLaunchKernelGGL(k_gemv<8>, grid, dim3(256), 0, st, g);
+          const bool frag = g.Bf != nullptr;
+          if (g.K / g.splits == 512) {
+            if (frag) hipLaunchKernelGGL((k_gemv<16, true>), grid, dim3(256), 0, st, g);
+            else hipLaunchKernelGGL((k_gemv<16, false>), grid, dim3(256), 0, st, g);
+          } else {
+            if (frag) hipLaunchKernelGGL((k_gemv<8, true>), grid, dim3(256), 0, st, g);
+            else hipLaunchKernelGGL((k_gemv<8, false>), grid, dim3(256), 0, st, g);
+          }
           return hipGetLastError();
         }
         if (g.M <= 32) return go_pipe<32, 64, 1, 4, EPI_PARTIAL, 4, 64>(g, st, g.N / 64);

@@ -23,6 +23,8 @@ struct GemmArgs {
   const void* A = nullptr;  // [M, K] activations (act type), row stride lda
   int lda = 0;
   const void* B = nullptr;  // [N, K] weights (wfmt), row stride K
+  const void* Bf = nullptr; // bf16: the same weights in fragment order (launch_arrange_frag),
+                            // read by the decode GEMV when set; else null
   const uint8_t* Bs = nullptr;  // MXFP8 scales [N, K/32]; NVFP4 E4M3 block scales [N, K/16]
   const float* Bg = nullptr;    // NVFP4 matrix scale (one float); B then holds packed codes [N, K/2]
   int M = 0, N = 0, K = 0;
@@ -37,6 +39,10 @@ struct GemmArgs {
 // out [rows, cols] bf16 = E4M3 code * 2^(E8M0 scale - 127), groups of 32 along a row (exact)
 hipError_t launch_expand_mxfp8(const uint8_t* codes, const uint8_t* scales, int64_t rows, int64_t cols, void* out,
                                hipStream_t st);
+// out [N*K] bf16 = w [N, K] bf16 in fragment order: 1 KiB block (n/16) (K/32) + k/32
+// holds rows 16 (n/16) .. + 15 at K 32 (k/32) .. + 31, element (n, k) at 8 (16 ((k %
+// 32) / 8) + n % 16) + k % 8 (one 16x16x32 MFMA B operand per block, in lane order)
+hipError_t launch_arrange_frag(const void* w, int64_t N, int64_t K, void* out, hipStream_t st);
 // Split count the launcher would use for a decode-shaped GEMM (EPI_PARTIAL).
 int gemm_pick_splits(int M, int N, int K, int wfmt);
 hipError_t launch_gemm(const GemmArgs& g, hipStream_t st);

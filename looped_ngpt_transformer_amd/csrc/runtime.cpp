@@ -545,10 +545,15 @@ int run_layer(dory_ctx* ctx, hipStream_t st, const CallPlan& P, int l, int slot,
   auto nv_scale = [&](const void* B) -> const float* {
     return B == w.w_qkvg ? w.g_qkvg : B == w.w_o ? w.g_o : B == w.w_gu ? w.g_gu : w.g_down;
   };
+  // bf16: the fragment-order copy of a weight matrix of this layer, if bound
+  auto frag_of = [&](const void* B) -> const void* {
+    return B == w.w_qkvg ? w.f_qkvg : B == w.w_o ? w.f_o : B == w.w_gu ? w.f_gu : B == w.w_down ? w.f_down : nullptr;
+  };
   auto run_gemm = [&](const GemmArgs& g0) -> hipError_t {
     Prof pr(ctx, st, DORY_KC_GEMM);
     GemmArgs g = g0;
     if (wf == W_NVFP4) g.Bg = nv_scale(g0.B);
+    if (wf == W_BF16 && g.epi == EPI_PARTIAL) g.Bf = frag_of(g0.B);
     if ((wf == W_NVFP4 || wf == W_MXFP8) && g.epi != EPI_PARTIAL) {
       // large M: expand the matrix to bf16 (exact), then the bf16 tiles
       const hipError_t x = wf == W_NVFP4 ? launch_expand_nvfp4((const uint8_t*)g.B, g.Bs, g.Bg, g.N, g.K, ws + W.wexp, st)
@@ -1151,6 +1156,10 @@ int dory_bind_weights(dory_ctx* ctx, int layer, const dory_layer_weights* w) {
   const uintptr_t mask = 15;
   if (((uintptr_t)w->w_qkvg | (uintptr_t)w->w_o | (uintptr_t)w->w_gu | (uintptr_t)w->w_down) & mask)
     return ctx->fail(DORY_ERR_INVALID_ARG, "weight matrices must be 16-byte aligned");
+  if ((w->f_qkvg || w->f_o || w->f_gu || w->f_down) && ctx->cfg.weight_format != DORY_WFMT_BF16)
+    return ctx->fail(DORY_ERR_INVALID_ARG, "fragment-order copies are for bf16 weights");
+  if (((uintptr_t)w->f_qkvg | (uintptr_t)w->f_o | (uintptr_t)w->f_gu | (uintptr_t)w->f_down) & mask)
+    return ctx->fail(DORY_ERR_INVALID_ARG, "fragment-order copies must be 16-byte aligned");
   ctx->lw[layer] = *w;
   ctx->lw_bound[layer] = true;
   return DORY_OK;
@@ -1460,14 +1469,15 @@ int dory_sample_top_p(void* stream, int n, int64_t vocab, const float* logits, i
 }
 
 int dory_test_gemm(void* stream, const void* A, int lda, const void* B, const uint8_t* B_scales,
-                   const float* B_gscale, int wfmt, int M, int N, int K, int epi, void* C, int ldc, int* splits) {
+                   const float* B_gscale, int wfmt, int M, int N, int K, int epi, void* C, int ldc, int* splits,
+                   const void* B_frag) {
   const bool mx = wfmt == DORY_WFMT_MXFP8, nv = wfmt == DORY_WFMT_NVFP4;
   const bool ok_fmt = (wfmt == DORY_WFMT_BF16 && !B_scales && !B_gscale) || (mx && B_scales && !B_gscale) ||
                       (nv && B_scales && B_gscale);
   const bool ok_epi = epi == EPI_F32 || epi == EPI_PARTIAL || epi == EPI_STORE_ACT || epi == EPI_SWIGLU;
   if (!A || !B || !splits || !ok_fmt || !ok_epi || M < 1 || N < 64 || K < 64 || K % 64 || N % 64 ||
       (epi == EPI_SWIGLU && N % 128) || lda < K || (C && ldc < (epi == EPI_SWIGLU ? N / 2 : N)) ||
-      ((mx || nv) && epi != EPI_PARTIAL) || (nv && N % 128)) {
+      ((mx || nv) && epi != EPI_PARTIAL) || (nv && N % 128) || (B_frag && (mx || nv || ((uintptr_t)B_frag & 15)))) {
     g_create_err = "bad GEMM argument";
     return DORY_ERR_INVALID_ARG;
   }
@@ -1491,10 +1501,32 @@ int dory_test_gemm(void* stream, const void* A, int lda, const void* B, const ui
   g.C = C;
   g.ldc = ldc;
   g.n_half = epi == EPI_SWIGLU ? N / 2 : 0;
+  g.Bf = epi == EPI_PARTIAL ? B_frag : nullptr;
   const hipError_t e = launch_gemm(g, (hipStream_t)stream);
   if (e != hipSuccess) {
     g_create_err = hipGetErrorString(e);
     return e == hipErrorInvalidValue ? DORY_ERR_INVALID_ARG : DORY_ERR_HIP;
+  }
+  return DORY_OK;
+}
+
+int dory_arrange_weights(void* stream, const void* w, int64_t N, int64_t K, void* out) {
+  if (!w || !out || N < 16 || K < 32 || N % 16 || K % 32 || ((uintptr_t)w & 15) || ((uintptr_t)out & 15) ||
+      N > (int64_t)1 << 30 || K > (int64_t)1 << 30) {
+    g_create_err = "bad arrangement argument (non-null, 16-byte aligned, N % 16 == 0, K % 32 == 0)";
+    return DORY_ERR_INVALID_ARG;
+  }
+  const char* a = (const char*)w;
+  const char* b = (const char*)out;
+  const size_t bytes = (size_t)N * (size_t)K * 2;
+  if (a < b + bytes && b < a + bytes) {
+    g_create_err = "arrangement output overlaps its input";
+    return DORY_ERR_INVALID_ARG;
+  }
+  const hipError_t e = launch_arrange_frag(w, N, K, out, (hipStream_t)stream);
+  if (e != hipSuccess) {
+    g_create_err = hipGetErrorString(e);
+    return DORY_ERR_HIP;
   }
   return DORY_OK;
 }

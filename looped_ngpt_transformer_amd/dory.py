@@ -46,7 +46,8 @@ class dory_config(C.Structure):
 class dory_layer_weights(C.Structure):
     _fields_ = [(n, C.c_void_p) for n in
                 ("w_qkvg", "w_o", "w_gu", "w_down", "s_qkvg", "s_o", "s_gu", "s_down",
-                 "alpha_attn", "alpha_mlp", "s_qk", "g_qkvg", "g_o", "g_gu", "g_down")]
+                 "alpha_attn", "alpha_mlp", "s_qk", "g_qkvg", "g_o", "g_gu", "g_down",
+                 "f_qkvg", "f_o", "f_gu", "f_down")]
 
 
 class dory_vocab_weights(C.Structure):
@@ -97,7 +98,8 @@ _SIGS = {
     "dory_test_fill_kv": (C.c_int, [_P, _P, C.c_int32, C.c_int, C.c_int, C.c_int32, C.c_int32, _P, _P]),
     "dory_test_inject_failure": (C.c_int, [_P, C.c_int]),
     "dory_test_gemm": (C.c_int, [_P, _P, C.c_int, _P, _P, _P, C.c_int, C.c_int, C.c_int, C.c_int, C.c_int, _P,
-                                 C.c_int, C.POINTER(C.c_int)]),
+                                 C.c_int, C.POINTER(C.c_int), _P]),
+    "dory_arrange_weights": (C.c_int, [_P, _P, C.c_int64, C.c_int64, _P]),
     "dory_test_mfma_rate": (C.c_int, [_P, C.c_int, _P, _P, C.POINTER(C.c_int)]),
     "dory_quantize_mxfp8": (C.c_int, [_P, _P, C.c_int, C.c_int64, C.c_int64, _P, _P]),
     "dory_quantize_nvfp4": (C.c_int, [_P, _P, C.c_int, C.c_int64, C.c_int64, _P, _P, _P]),
@@ -316,7 +318,7 @@ EPI_F32, EPI_PARTIAL, EPI_STORE_BF16, EPI_SWIGLU = 0, 1, 2, 4
 
 
 def dory_test_gemm(A, B, epi, out=None, B_scales=None, stream=None, M=None, N=None, K=None, lda=None,
-                   ldc=None, B_gscale=None):
+                   ldc=None, B_gscale=None, B_frag=None):
     """One projection GEMM as a layer launches it: out = A B^T with the layer's epilogue
     (see dory.h). B_scales alone: MXFP8 codes; B_scales and B_gscale: NVFP4 packed codes.
     Returns the split count; with out None only the split count is computed."""
@@ -328,8 +330,15 @@ def dory_test_gemm(A, B, epi, out=None, B_scales=None, stream=None, M=None, N=No
     wf = WFMT_NVFP4 if B_gscale is not None else WFMT_MXFP8 if B_scales is not None else WFMT_BF16
     splits = C.c_int(0)
     _check(lib().dory_test_gemm(_stream(stream), _ptr(A), lda, _ptr(B), _ptr(B_scales), _ptr(B_gscale), wf, M, N,
-                                K, epi, _ptr(out), ldc, C.byref(splits)))
+                                K, epi, _ptr(out), ldc, C.byref(splits), _ptr(B_frag)))
     return splits.value
+
+
+def dory_arrange_weights(w, out, stream=None):
+    """Fragment-order copy of the bf16 matrix w [N, K] into out (N * K bf16 elements)
+    for the f_* fields of dory_layer_weights (see dory.h)."""
+    N, K = w.shape
+    _check(lib().dory_arrange_weights(_stream(stream), _ptr(w), N, K, _ptr(out)))
 
 
 def dory_test_mfma_rate(iters, cycles, sink, stream=None):

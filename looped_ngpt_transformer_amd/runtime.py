@@ -11,8 +11,12 @@ from . import dory as D
 class DoryRuntime:
     def __init__(self, shape: dict, weights: list, *, max_loops=4, max_seqs=1,
                  max_seq_len=4096, max_rows=4096, kv_pages: int | None = None,
-                 mode: str = "per_loop", loops: int = 2, device="cuda"):
+                 mode: str = "per_loop", loops: int = 2, device="cuda", arrange: bool = True):
+        """arrange: with bf16 weights, also bind fragment-order copies of the four
+        matrices (dory_arrange_weights), which the decode projections read with
+        contiguous loads; it doubles the weights' device memory."""
         self.shape = shape
+        self.arrange = arrange and shape["weight_format"] == "bf16" and shape.get("act_dtype", "bf16") == "bf16"
         self.device = torch.device(device)
         self.cfg = D.make_config(shape, max_loops=max_loops, max_seqs=max_seqs,
                                  max_seq_len=max_seq_len, max_rows=max_rows)
@@ -58,6 +62,11 @@ class DoryRuntime:
                 else:
                     self._keep.append(t)
                     setattr(lw, name, t.data_ptr())
+                    if self.arrange:
+                        f = torch.empty_like(t)
+                        D.dory_arrange_weights(t, f)
+                        self._keep.append(f)
+                        setattr(lw, "f_" + name[2:], f.data_ptr())
             for name in ("alpha_attn", "alpha_mlp", "s_qk"):
                 t = w[name].to(self.device, torch.float32).contiguous()
                 self._keep.append(t)

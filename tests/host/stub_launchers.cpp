@@ -13,6 +13,7 @@ hipError_t launch_expand_mxfp8(const uint8_t*, const uint8_t*, int64_t, int64_t,
   return g_stub_launch;
 }
 hipError_t launch_gemm(const GemmArgs&, hipStream_t) { return g_stub_launch; }
+hipError_t launch_arrange_frag(const void*, int64_t, int64_t, void*, hipStream_t) { return g_stub_launch; }
 hipError_t launch_mfma_rate(int, int, long long*, float*, hipStream_t) { return g_stub_launch; }
 hipError_t launch_update(const UpdateArgs&, hipStream_t) { return g_stub_launch; }
 hipError_t launch_stage_input(const float*, float*, void*, int, int, int, hipStream_t, const int32_t*) {

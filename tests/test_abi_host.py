@@ -298,3 +298,17 @@ def test_decode_split_counts():
     cases = {(6400, 2560): 5, (8192, 2560): 5, (2560, 2560): 10, (2560, 4096): 8, (131072, 2560): 1}
     for (N, K), want in cases.items():
         assert D.dory_test_gemm(A, B, D.EPI_PARTIAL, None, stream=0, M=32, N=N, K=K) == want, (N, K)
+
+
+def test_arrange_weights_validates_before_device_work():
+    """dory_arrange_weights refuses bad shapes, null pointers and overlap on the host."""
+    import torch
+    w = torch.zeros((64, 128), dtype=torch.bfloat16)
+    out = torch.zeros(64 * 128, dtype=torch.bfloat16)
+    for bad in (torch.zeros((60, 128), dtype=torch.bfloat16), torch.zeros((64, 100), dtype=torch.bfloat16)):
+        with pytest.raises(D.DoryError):
+            D.dory_arrange_weights(bad, out, stream=0)
+    with pytest.raises(D.DoryError):
+        D.dory_arrange_weights(w, w, stream=0)  # in place: overlaps
+    with pytest.raises(D.DoryError):
+        D.dory_arrange_weights(w, None, stream=0)

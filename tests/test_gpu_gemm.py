@@ -153,3 +153,36 @@ def test_split_k_nvfp4(M, N, K):
     # weights of size up to 6 * 2^3 * 2^-9 ~ 0.1: scale the absolute term of the tolerance
     d = (out.sum(0).cpu() - ref).abs()
     assert not (d > 2e-3 * (ref.abs() + 5.0)).any(), f"max |d| {float(d.max()):.3e}"
+
+
+def test_fragment_order_copy_is_the_documented_permutation():
+    """dory_arrange_weights against the layout dory.h states, built by reshaping:
+    element (n, k) of block (n/16)(K/32) + k/32 at 8 (16 ((k % 32) / 8) + n % 16) + k % 8."""
+    N, K = 2560, 4096
+    g = torch.Generator(device="cuda").manual_seed(11)
+    W = torch.randn((N, K), generator=g, device="cuda").to(torch.bfloat16)
+    out = torch.empty(N * K, dtype=torch.bfloat16, device="cuda")
+    D.dory_arrange_weights(W, out)
+    ref = W.view(N // 16, 16, K // 32, 4, 8).permute(0, 2, 3, 1, 4).contiguous().view(-1)
+    torch.cuda.synchronize()
+    assert torch.equal(out.view(torch.int16), ref.view(torch.int16))
+
+
+@pytest.mark.parametrize("M", [1, 32])
+@pytest.mark.parametrize("N,K", [(6400, 2560), (2560, 2560), (8192, 2560), (2560, 4096)])
+def test_decode_gemv_on_fragment_copy_is_bitwise_the_same(M, N, K):
+    """The decode GEMV reading the fragment-order copy gives bitwise the partials it gives
+    reading the row-major matrix (same values, same arithmetic order), and both match a
+    float32 matmul."""
+    A, B = operands(M, N, K, 12)
+    Bf = torch.empty(N * K, dtype=torch.bfloat16, device="cuda")
+    D.dory_arrange_weights(B, Bf)
+    S = D.dory_test_gemm(A, B, D.EPI_PARTIAL, None)
+    outs = []
+    for frag in (None, Bf):
+        C = torch.full((S, M, N), SENTINEL, dtype=torch.float32, device="cuda")
+        assert D.dory_test_gemm(A, B, D.EPI_PARTIAL, C, B_frag=frag) == S
+        outs.append(C)
+    torch.cuda.synchronize()
+    assert torch.equal(outs[0], outs[1])
+    check(outs[1].sum(0), reference(A, B), False)
