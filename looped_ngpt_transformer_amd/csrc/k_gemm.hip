@@ -11,8 +11,9 @@
 // Small M (decode, <= 256 rows): split-K streaming kernels that read each weight once
 // and leave fp32 partials for the consumer: k_gemv (bf16, <= 32 rows: weights straight
 // into registers, every load of a wave in flight at once), k_gemm_pipe (bf16, more
-// rows), k_gemm_mx32 / k_gemm_nv32 (MXFP8 / NVFP4 codes converted to bf16 in registers
-// just before the MFMA).
+// rows), k_gemv_mx (MXFP8, 33-128 rows: codes in registers, the activations through
+// LDS, each weight read once), k_gemm_mx32 / k_gemm_nv32 (MXFP8 / NVFP4 codes converted
+// to bf16 in registers just before the MFMA).
 // k_gemm_mfma (register-staged tiles) covers the shapes the others cannot take.
 // Epilogues fuse what follows each projection: bf16 store; fp32 store; SwiGLU; or the
 // split-K partials. The L2 norms before the output and down projections only scale a
@@ -548,6 +549,110 @@ __global__ __launch_bounds__(256) void k_gemv(GemmArgs g) {
   }
 }
 
+// MXFP8 decode GEMM for 33-128 activation rows (W8A16), bound by the codes, the
+// activations and the split partials together: at 128 rows an activation slice is as
+// large as the codes of a 64-row weight block, and every split adds 128 x N x 4 bytes of
+// partials. A work-group of 4 waves owns 64 weight rows over a long K range (NCH chunks
+// of 128, few splits); each wave holds its 16 rows' codes for the whole range in
+// registers (issued before anything else), while the activations (128 rows, rows beyond
+// M repeat the last) stream through two LDS stages of one 128-wide chunk each. Per
+// 32-wide step a wave converts its B fragment (8 codes, the group's E8M0 scale, exact)
+// once and runs it against the 8 row blocks of 16 (v_mfma_f32_16x16x32_bf16).
+// K order inside a 64-wide block: lane l loads the 16 codes at 16 (l / 16) .. + 15 and
+// uses the first 8 in the block's first step, the other 8 in its second; the activation
+// fragments take the same order (a permutation of the contraction index, so the sums
+// are the same products). Output: fp32 split-K partials, split = K range.
+template <int NCH>
+__global__ __launch_bounds__(256) void k_gemv_mx(GemmArgs g) {
+  constexpr int KS = 128 * NCH;   // K range of the work-group
+  __shared__ __align__(16) uint4 sa0[128 * 16];  // chunk stages: 128 rows x 16 chunks of 8 bf16
+  __shared__ __align__(16) uint4 sa1[128 * 16];
+
+  const int t = threadIdx.x, lane = t & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(t >> 6);
+  const int n0 = blockIdx.x * 64 + wave * 16;
+  const int split = blockIdx.y;
+  const int kbeg = split * KS;
+  const int r16 = lane & 15, q = lane >> 4;
+  const bf16_t* A = (const bf16_t*)g.A;
+
+  // codes: 16 bytes per 64-wide block (row n0 + r16, K kbeg + 64 b + 16 q ..), and the
+  // row's four E8M0 scales of each chunk (groups kbeg / 32 + 4 c ..)
+  uint4 cw[2 * NCH];
+  uint32_t sc4[NCH];
+  {
+    const uint8_t* crow = (const uint8_t*)g.B + (size_t)(n0 + r16) * g.K + kbeg + 16 * q;
+    const uint8_t* srow = g.Bs + (size_t)(n0 + r16) * (g.K / 32) + kbeg / 32;
+#pragma unroll
+    for (int b = 0; b < 2 * NCH; ++b) cw[b] = *(const uint4*)(crow + 64 * b);
+#pragma unroll
+    for (int c = 0; c < NCH; ++c) sc4[c] = *(const uint32_t*)(srow + 4 * c);
+  }
+  // activation chunk c into a stage: slot p (row p / 16, slot p % 16) holds chunk
+  // (p % 16) ^ (row % 16) of that row's 128-wide chunk; 8 loads per thread
+  auto issue = [&](int c, auto S) {
+    uint4* st0 = decltype(S)::value == 0 ? sa0 : sa1;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      const int p = i * 256 + t, row = p >> 4, sl = p & 15;
+      const bf16_t* src = A + (size_t)min(row, g.M - 1) * g.lda + kbeg + 128 * c + 8 * (sl ^ (row & 15));
+      __builtin_amdgcn_global_load_lds((gbl_void_t)src, (lds_void_t)(st0 + i * 256 + (t & ~63)), 16, 0, 0);
+    }
+  };
+  f32x4 acc[8];
+#pragma unroll
+  for (int mb = 0; mb < 8; ++mb) acc[mb] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+  auto compute = [&](int c, auto S) {
+    const uint4* st0 = decltype(S)::value == 0 ? sa0 : sa1;
+#pragma unroll
+    for (int h2 = 0; h2 < 2; ++h2) {
+      const uint4 w = cw[2 * c + h2];
+      const float scf = e8m0_to_f32((sc4[c] >> (8 * (2 * h2 + (q >> 1)))) & 0xFFu);
+#pragma unroll
+      for (int h = 0; h < 2; ++h) {
+        uint32_t v[4];
+        dq4(h ? w.z : w.x, scf, v);
+        dq4(h ? w.w : w.y, scf, v + 2);
+        const bf16x8 bfrag = __builtin_bit_cast(bf16x8, make_uint4(v[0], v[1], v[2], v[3]));
+        const int ch = 8 * h2 + 2 * q + h;  // 16-byte chunk of the stage row
+#pragma unroll
+        for (int mb = 0; mb < 8; ++mb) {
+          const int row = 16 * mb + r16;
+          const bf16x8 afrag = __builtin_bit_cast(bf16x8, st0[row * 16 + (ch ^ r16)]);
+          acc[mb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(afrag, bfrag, acc[mb], 0, 0, 0);
+        }
+      }
+    }
+  };
+
+  using S0 = std::integral_constant<int, 0>;
+  using S1 = std::integral_constant<int, 1>;
+  issue(0, S0{});
+  asm volatile("s_waitcnt vmcnt(0)\n\ts_barrier" ::: "memory");  // codes, scales, chunk 0
+#pragma unroll
+  for (int c = 0; c < NCH; ++c) {
+    // stage (c + 1) % 2 last held chunk c - 1, which every wave finished before the
+    // barrier that ended the previous step
+    if (c + 1 < NCH) {
+      if (c % 2 == 0) issue(c + 1, S1{});
+      else issue(c + 1, S0{});
+    }
+    if (c % 2 == 0) compute(c, S0{});
+    else compute(c, S1{});
+    if (c + 1 < NCH) asm volatile("s_waitcnt vmcnt(0)\n\ts_barrier" ::: "memory");
+  }
+  // lane l: column n0 + l % 16, rows 16 mb + 4 (l / 16) + i
+  float* C = (float*)g.C + (size_t)split * g.M * g.ldc + n0 + r16;
+#pragma unroll
+  for (int mb = 0; mb < 8; ++mb)
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int m = 16 * mb + 4 * q + i;
+      if (m < g.M) C[(size_t)m * g.ldc] = acc[mb][i];
+    }
+}
+
 // Sustained rate of v_mfma_f32_32x32x16_bf16 on this device (the practical ceiling the
 // projection GEMMs are measured against): 8 waves per work-group (two per SIMD), each
 // running 8 independent accumulator chains of `iters` instructions on register operands
@@ -643,8 +748,19 @@ static int gemv_splits(int M, int N, int K, int wfmt) {
   return 0;
 }
 
+// k_gemv_mx takes MXFP8 weights, 33-128 rows and K ranges of NCH chunks of 128 with NCH
+// in {2, 4, 5, 8, 10}: the fewest splits that give at least 192 work-groups
+static bool gemv_mx_nch_ok(int nch) { return nch == 2 || nch == 4 || nch == 5 || nch == 8 || nch == 10; }
+static int gemv_mx_splits(int M, int N, int K, int wfmt) {
+  if (wfmt != W_MXFP8 || M <= 32 || M > 128 || N % 64 || K % 128) return 0;
+  for (int s = 1; s <= 32; ++s)
+    if (K % (128 * s) == 0 && gemv_mx_nch_ok(K / (128 * s)) && (N / 64) * s >= 192) return s;
+  return 0;
+}
+
 int gemm_pick_splits(int M, int N, int K, int wfmt) {
   if (const int s = gemv_splits(M, N, K, wfmt)) return s;
+  if (const int s = gemv_mx_splits(M, N, K, wfmt)) return s;
   // small-M (decode) tiles are BN = 64 wide (128 for MXFP8); split K until there are
   // enough work-groups to keep the weight stream in flight (each split a multiple of 64,
   // not too short)
@@ -1364,6 +1480,20 @@ hipError_t launch_gemm(const GemmArgs& gin, hipStream_t st) {
         if (g.N % 128 || (g.K / g.splits) % 64 || !g.Bs || !g.Bg) return hipErrorInvalidValue;
         if (g.M <= 32) return go_nv<32, 128, 1, 4, 4>(g, st);
         return go_nv<64, 128, 1, 4, 4>(g, st);
+      }
+      // 16-byte code and activation loads, 4-byte scale loads
+      if (g.M > 32 && g.M <= 128 && g.K % (128 * g.splits) == 0 && gemv_mx_nch_ok(g.K / (128 * g.splits)) &&
+          g.Bs && ((uintptr_t)g.Bs & 3) == 0 && ((uintptr_t)g.B & 15) == 0 && ((uintptr_t)g.A & 15) == 0 &&
+          g.lda % 8 == 0) {
+        dim3 grid(g.N / 64, g.splits);
+        switch (g.K / (128 * g.splits)) {
+          case 2: hipLaunchKernelGGL((k_gemv_mx<2>), grid, dim3(256), 0, st, g); break;
+          case 4: hipLaunchKernelGGL((k_gemv_mx<4>), grid, dim3(256), 0, st, g); break;
+          case 5: hipLaunchKernelGGL((k_gemv_mx<5>), grid, dim3(256), 0, st, g); break;
+          case 8: hipLaunchKernelGGL((k_gemv_mx<8>), grid, dim3(256), 0, st, g); break;
+          default: hipLaunchKernelGGL((k_gemv_mx<10>), grid, dim3(256), 0, st, g); break;
+        }
+        return hipGetLastError();
       }
       if (g.N % 128 == 0) {  // MXFP8: 128 weight rows per tile
         if (g.M <= 32) return go_mx<32, 128, 1, 4, 4>(g, st);

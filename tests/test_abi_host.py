@@ -300,6 +300,25 @@ def test_decode_split_counts():
         assert D.dory_test_gemm(A, B, D.EPI_PARTIAL, None, stream=0, M=32, N=N, K=K) == want, (N, K)
 
 
+def test_mxfp8_decode_split_counts():
+    """MXFP8 projections at 33-128 rows split K into ranges of 2, 4, 5, 8 or 10 chunks of
+    128, the fewest splits that give >= 192 work-groups of 64 weight rows; at <= 32 and
+    above 128 rows the 128-row tiles keep their own rule (host only, no launch)."""
+    import torch
+    A = torch.zeros((128, 4096), dtype=torch.bfloat16)
+    B = torch.zeros((64, 64), dtype=torch.uint8)
+    Bs = torch.zeros((64, 2), dtype=torch.uint8)
+    cases = {(128, 6400, 2560): 2, (128, 8192, 2560): 2, (128, 2560, 2560): 5, (128, 2560, 4096): 8,
+             (33, 1280, 2560): 10, (40, 12288, 1024): 1, (97, 6144, 1280): 2, (70, 2560, 2560): 5}
+    for (M, N, K), want in cases.items():
+        got = D.dory_test_gemm(A, B, D.EPI_PARTIAL, None, B_scales=Bs, stream=0, M=M, N=N, K=K)
+        assert got == want, (M, N, K, got)
+    # outside 33-128 rows: the tile rule (K / 64 even splits, at most 8)
+    for M in (32, 129):
+        got = D.dory_test_gemm(A, B, D.EPI_PARTIAL, None, B_scales=Bs, stream=0, M=M, N=2560, K=2560)
+        assert got in (1, 2, 4, 8), (M, got)
+
+
 def test_arrange_weights_validates_before_device_work():
     """dory_arrange_weights refuses bad shapes, null pointers and overlap on the host."""
     import torch

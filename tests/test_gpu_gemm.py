@@ -102,8 +102,12 @@ def dequant_mxfp8(codes, scales):
     return w * torch.exp2(e).repeat_interleave(32, dim=1)
 
 
+# 33-128 rows take k_gemv_mx: K ranges of 10 chunks of 128 (128 x 8192 x 2560, 33 x 6400),
+# 5 (97 x 6144 x 1280), 4 (70 x 2560 x 2560, 128 x 2560 x 4096), 8 (40 x 12288 x 1024)
+# and 2 (33 x 1280 x 2560)
 @pytest.mark.parametrize("M,N,K", [(1, 6400, 2560), (32, 2560, 4096), (128, 8192, 2560), (70, 2560, 2560),
-                                   (200, 2560, 2560)])
+                                   (200, 2560, 2560), (33, 6400, 2560), (97, 6144, 1280), (128, 2560, 4096),
+                                   (40, 12288, 1024), (33, 1280, 2560)])
 def test_split_k_mxfp8(M, N, K):
     A, B = operands(M, N, K, 5)
     codes = torch.empty((N, K), dtype=torch.uint8, device="cuda")
