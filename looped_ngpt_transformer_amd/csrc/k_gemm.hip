@@ -1401,10 +1401,6 @@ static hipError_t go_pipe(const GemmArgs& g, hipStream_t st, int ntiles_n) {
   return hipGetLastError();
 }
 
-// Large-M (prefill) tiles for bf16 weights over n output columns (for SwiGLU, gate and
-// up columns together): 256x256 ping-pong tiles when they fill the device, else 256x160
-// ping-pong tiles when n allows; hipErrorNotSupported when no tile shape divides n or the
-// sizes need offsets beyond 32 bits.
 template <int BM, int BN, int WMW, int WNW, int EPI, int STAGES>
 static hipError_t go_pipe32(const GemmArgs& g, hipStream_t st, int ntiles_n) {
   dim3 grid(ntiles_n, (g.M + BM - 1) / BM);
@@ -1412,6 +1408,44 @@ static hipError_t go_pipe32(const GemmArgs& g, hipStream_t st, int ntiles_n) {
   return hipGetLastError();
 }
 
+// compute units of the current device (one ping-pong work-group fits a CU at a time)
+static int device_cus() {
+  static int cus = 0;
+  if (!cus) {
+    int dev = 0, n = 0;
+    cus = hipGetDevice(&dev) == hipSuccess &&
+                  hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) == hipSuccess && n > 0
+              ? n
+              : 256;
+  }
+  return cus;
+}
+
+// Columns [0, 256 a) on 256x256 tiles and [256 a, n) on 256x160 tiles (a = 0 or
+// 256 a = n: one launch). One work-group runs per CU, so a launch of t tiles takes
+// ceil(t / CUs) rounds, and a 256-wide tile takes about 1.4 times as long as a 160-wide
+// one (measured on the prefill shapes); a is the split with the fewest estimated tile
+// times. For 4096 x 6400 (the [q|k|v|gate] projection of a 4096-token prefill) that is 15
+// wide and 16 narrow column tiles, one round each, instead of two rounds of 25 wide ones.
+static int pp_wide_columns(int M, int n) {
+  const int mt = (M + 255) / 256, cus = device_cus();
+  int best_a = -1;
+  long best = 0;
+  for (int a = n / 256; a >= 0; --a) {
+    const int rest = n - 256 * a;
+    if (rest % 160) continue;
+    const long t = 14L * ((a * mt + cus - 1) / cus) + 10L * ((rest / 160 * mt + cus - 1) / cus);
+    if (best_a < 0 || t < best) best = t, best_a = a;
+  }
+  return best_a;
+}
+
+// Large-M (prefill) tiles for bf16 weights over n output columns (for SwiGLU, gate and
+// up columns together): SwiGLU on 256x256 ping-pong tiles; the other epilogues on
+// 256x256 and/or 256x160 ping-pong tiles as pp_wide_columns splits the columns; the
+// pipelined 256x256 tiles when K has an odd number of 64-wide slices;
+// hipErrorNotSupported when no tile shape divides n or the sizes need offsets beyond 32
+// bits.
 template <int EPI>
 static hipError_t go_big(const GemmArgs& g, hipStream_t st, int n) {
   // these kernels address A and B with 32-bit byte offsets, and store bf16 outputs as
@@ -1419,17 +1453,31 @@ static hipError_t go_big(const GemmArgs& g, hipStream_t st, int n) {
   if ((long)g.N * g.K >= (1L << 30) || g.lda >= (1 << 20)) return hipErrorNotSupported;
   if (EPI != EPI_F32 && (g.ldc % 8 != 0 || ((uintptr_t)g.C & 15) != 0)) return hipErrorNotSupported;
   const bool pp = (g.K / BK) % 2 == 0;  // the ping-pong tiles take K slices in pairs
-  if (pp && n % 256 == 0 && (EPI == EPI_SWIGLU || n / 256 * ((g.M + 255) / 256) >= 256)) {
-    dim3 grid(n / 256, (g.M + 255) / 256);
-    hipLaunchKernelGGL((k_gemm_pp<256, EPI>), grid, dim3(512), 0, st, g);
-    return hipGetLastError();
-  }
-  if constexpr (EPI != EPI_SWIGLU)
-    if (pp && n % 160 == 0) {
-      dim3 grid(n / 160, (g.M + 255) / 256);
-      hipLaunchKernelGGL((k_gemm_pp<160, EPI>), grid, dim3(512), 0, st, g);
+  const int mt = (g.M + 255) / 256;
+  if constexpr (EPI == EPI_SWIGLU) {
+    if (pp && n % 256 == 0) {
+      hipLaunchKernelGGL((k_gemm_pp<256, EPI>), dim3(n / 256, mt), dim3(512), 0, st, g);
       return hipGetLastError();
     }
+  } else if (pp) {
+    const int a = pp_wide_columns(g.M, n);
+    if (a >= 0) {
+      if (a > 0) {
+        GemmArgs w = g;
+        w.N = 256 * a;
+        hipLaunchKernelGGL((k_gemm_pp<256, EPI>), dim3(a, mt), dim3(512), 0, st, w);
+      }
+      if (256 * a < n) {
+        GemmArgs r = g;
+        const size_t esz = EPI == EPI_F32 ? 4 : 2;
+        r.B = (const bf16_t*)g.B + (size_t)256 * a * g.K;
+        r.C = (char*)g.C + (size_t)256 * a * esz;
+        r.N = n - 256 * a;
+        hipLaunchKernelGGL((k_gemm_pp<160, EPI>), dim3(r.N / 160, mt), dim3(512), 0, st, r);
+      }
+      return hipGetLastError();
+    }
+  }
   if (n % 256 == 0) return go_pipe32<256, 256, 2, 4, EPI, 2>(g, st, n / 256);
   return hipErrorNotSupported;
 }

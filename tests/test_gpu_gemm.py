@@ -1,7 +1,8 @@
 """GPU: the projection GEMM kernels through the C ABI (dory_test_gemm), each shape routed
 to the kernel a layer call would use, against a plain float32 matmul of the same bf16
 (or dequantised MXFP8) operands. Shapes cover the 256x256 ping-pong tiles (every
-epilogue, ragged M, row stride > K), the 256x160 tiles and the split-K decode kernels.
+epilogue, ragged M, row stride > K), the 256x160 tiles, launches that split the columns
+between the two, and the split-K decode kernels.
 
 Tolerances: float outputs |d| <= 2e-3 * (|ref| + 1) (bf16 products, float32 sums in
 another order over K <= 4096 terms of size ~0.02); bf16 outputs additionally one
@@ -38,8 +39,9 @@ def check(out, ref, bf16_out):
 
 
 @pytest.mark.parametrize("M,N,K,lda,ldc", [
-    (2600, 6400, 2560, None, None),   # [q|k|v|gate] shape, 275 ping-pong tiles, ragged last row tile
-    (4096, 6400, 2560, 2624, None),   # full tiles, A row stride > K
+    (2600, 6400, 2560, None, None),   # [q|k|v|gate] shape: 15 wide + 16 narrow column tiles, ragged M
+    (4096, 6400, 2560, 2624, None),   # the same split on full row tiles, A row stride > K
+    (8192, 6400, 2560, None, None),   # 8192-row chunk: two rounds of each tile width
     (150, 6400, 2560, None, None),    # too few tiles for 256x256: 256x160 tiles
     (150, 6400, 2560, None, 6408),    # output row stride > N (16-byte stores)
     (300, 6400, 2560, None, 6404),    # output rows not 16-byte aligned: register-staged tiles
@@ -58,6 +60,7 @@ def test_store_bf16(M, N, K, lda, ldc):
 
 @pytest.mark.parametrize("M,N,K", [
     (4000, 4096, 512),    # 256 ping-pong tiles with the float epilogue, ragged M
+    (4096, 6400, 512),    # float epilogue on a column split (wide then narrow tiles)
     (1000, 2560, 4096),   # output / down projection shape: 256x160 tiles
     (4096, 2560, 2560),
 ])
