@@ -117,7 +117,9 @@ def roofline_of(stats, kind, workload):
     if kind == "mfma":
         g = stats["gemm"]
         ach = g["flops"] / (g["ms"] / 1e3) / 1e12
-        return {"bound": "mfma", "kernel": "gemm (bf16 MFMA projections)",
+        return {"bound": "mfma",
+                "kernel": "gemm (bf16 MFMA projections; a launch here is one projection call, the "
+                          "[q|k|v|gate] call being two kernels over its column tiles)",
                 "achieved": round(ach, 1), "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
                 "frac": round(ach / PEAK_BF16_TFLOPS, 4),
                 "traffic": measured_traffic("prefill_gemm", workload, ["k_gemm.hip", "common.h", "kernels.h"]),
