@@ -630,6 +630,12 @@ __global__ __launch_bounds__(256) void k_gemv_mx(GemmArgs g) {
   using S1 = std::integral_constant<int, 1>;
   issue(0, S0{});
   asm volatile("s_waitcnt vmcnt(0)\n\ts_barrier" ::: "memory");  // codes, scales, chunk 0
+  // the codes and scales are used here once, so that the compiler's own wait for them
+  // falls before the next chunk's loads go out (after them it would wait for those too)
+#pragma unroll
+  for (int b = 0; b < 2 * NCH; ++b) asm volatile("" ::"v"(cw[b].x), "v"(cw[b].y), "v"(cw[b].z), "v"(cw[b].w));
+#pragma unroll
+  for (int c = 0; c < NCH; ++c) asm volatile("" ::"v"(sc4[c]));
 #pragma unroll
   for (int c = 0; c < NCH; ++c) {
     // stage (c + 1) % 2 last held chunk c - 1, which every wave finished before the
@@ -638,6 +644,9 @@ __global__ __launch_bounds__(256) void k_gemv_mx(GemmArgs g) {
       if (c % 2 == 0) issue(c + 1, S1{});
       else issue(c + 1, S0{});
     }
+    // the next chunk's loads all leave before this chunk's work (left to itself the
+    // scheduler spreads them through it, and the last ones then meet the wait below)
+    __builtin_amdgcn_sched_barrier(0);
     if (c % 2 == 0) compute(c, S0{});
     else compute(c, S1{});
     if (c + 1 < NCH) asm volatile("s_waitcnt vmcnt(0)\n\ts_barrier" ::: "memory");
