@@ -132,6 +132,9 @@ __global__ __launch_bounds__(UPD_THREADS) void k_update(UpdateArgs u) {
 
 // Prefill form (y one bf16 array, H % 8 == 0, H <= 8 T): each thread owns 8 consecutive
 // channels of the row, so every access is 16 or 32 bytes wide; same sums and algebra.
+// With state_act the state between sublayers is the bf16 GEMM operand itself, read from
+// sb and rewritten in place (each thread rewrites only the channels it read), so an
+// update moves y, s and the new s in bf16: 6 bytes per element instead of 14.
 template <typename SB, int T>
 __global__ __launch_bounds__(T) void k_update_vec(UpdateArgs u) {
   constexpr int NW = T / WAVE;
@@ -148,12 +151,19 @@ __global__ __launch_bounds__(T) void k_update_vec(UpdateArgs u) {
   for (int e = 0; e < 8; ++e) yv[e] = sv[e] = av[e] = xv[e] = 0.f;
   if (act) {
     const uint4 yr = *(const uint4*)((const bf16_t*)u.y + row + i0);
-    const float4 s0 = *(const float4*)(u.s + row + i0), s1 = *(const float4*)(u.s + row + i0 + 4);
     const float4 a0 = *(const float4*)(u.alpha + i0), a1 = *(const float4*)(u.alpha + i0 + 4);
     const uint32_t yw[4] = {yr.x, yr.y, yr.z, yr.w};
 #pragma unroll
     for (int e = 0; e < 8; ++e) yv[e] = __uint_as_float((e & 1) ? (yw[e / 2] & 0xFFFF0000u) : (yw[e / 2] << 16));
-    sv[0] = s0.x; sv[1] = s0.y; sv[2] = s0.z; sv[3] = s0.w; sv[4] = s1.x; sv[5] = s1.y; sv[6] = s1.z; sv[7] = s1.w;
+    if (u.state_act) {  // bf16 state: 8 channels in one 16-byte load
+      const uint4 sr = *(const uint4*)((const bf16_t*)u.sb + row + i0);
+      const uint32_t sw[4] = {sr.x, sr.y, sr.z, sr.w};
+#pragma unroll
+      for (int e = 0; e < 8; ++e) sv[e] = __uint_as_float((e & 1) ? (sw[e / 2] & 0xFFFF0000u) : (sw[e / 2] << 16));
+    } else {
+      const float4 s0 = *(const float4*)(u.s + row + i0), s1 = *(const float4*)(u.s + row + i0 + 4);
+      sv[0] = s0.x; sv[1] = s0.y; sv[2] = s0.z; sv[3] = s0.w; sv[4] = s1.x; sv[5] = s1.y; sv[6] = s1.z; sv[7] = s1.w;
+    }
     av[0] = a0.x; av[1] = a0.y; av[2] = a0.z; av[3] = a0.w; av[4] = a1.x; av[5] = a1.y; av[6] = a1.z; av[7] = a1.w;
     if (need_x) {
       const float4 x0 = *(const float4*)(u.x + row + i0), x1 = *(const float4*)(u.x + row + i0 + 4);
@@ -214,8 +224,10 @@ __global__ __launch_bounds__(T) void k_update_vec(UpdateArgs u) {
   float v[8];
 #pragma unroll
   for (int e = 0; e < 8; ++e) v[e] = t[e] * scale + add_x * xv[e];
-  *(float4*)(u.s_out + row + i0) = make_float4(v[0], v[1], v[2], v[3]);
-  *(float4*)(u.s_out + row + i0 + 4) = make_float4(v[4], v[5], v[6], v[7]);
+  if (u.s_out) {
+    *(float4*)(u.s_out + row + i0) = make_float4(v[0], v[1], v[2], v[3]);
+    *(float4*)(u.s_out + row + i0 + 4) = make_float4(v[4], v[5], v[6], v[7]);
+  }
   if (u.sb) {
     if constexpr (sizeof(SB) == 2) {
       *(uint4*)((bf16_t*)u.sb + row + i0) =
@@ -227,6 +239,114 @@ __global__ __launch_bounds__(T) void k_update_vec(UpdateArgs u) {
   }
 }
 
+// Prefill form with the bf16 state (state_act, H = 512 NC): one wave per row, lane l
+// holding channels 512 c + 8 l .. + 7 (c < NC) of y, s and the rates, so each load
+// instruction of a wave reads one contiguous KiB. Four rows per work-group and no LDS or
+// barrier: every row of the launch has its loads in flight in one round, and the 7 row
+// sums are wave reductions only. y and s stay packed in registers and are widened where
+// they are used.
+template <int NC>
+__global__ __launch_bounds__(256) void k_update_wave(UpdateArgs u) {
+  constexpr int NS = 7;
+  const int lane = threadIdx.x & (WAVE - 1);
+  const int m = blockIdx.x * 4 + (threadIdx.x >> 6);
+  if (m >= u.M) return;
+  const size_t row = (size_t)m * u.H;
+  const int bnd = u.bnd == BND_LOOP_CONTINUE && m >= u.final_from ? BND_LOOP_FINAL : u.bnd;
+  const bool need_x = bnd == BND_LOOP_CONTINUE;
+  const bf16_t* Y = (const bf16_t*)u.y + row;
+  bf16_t* S = (bf16_t*)u.sb + row;
+  uint4 yr[NC], sr[NC];
+  float av[NC][8];
+#pragma unroll
+  for (int c = 0; c < NC; ++c) {
+    const int i = 512 * c + 8 * lane;
+    yr[c] = *(const uint4*)(Y + i);
+    sr[c] = *(const uint4*)(S + i);
+  }
+#pragma unroll
+  for (int c = 0; c < NC; ++c) {
+    const int i = 512 * c + 8 * lane;
+    const float4 a0 = *(const float4*)(u.alpha + i), a1 = *(const float4*)(u.alpha + i + 4);
+    av[c][0] = a0.x; av[c][1] = a0.y; av[c][2] = a0.z; av[c][3] = a0.w;
+    av[c][4] = a1.x; av[c][5] = a1.y; av[c][6] = a1.z; av[c][7] = a1.w;
+  }
+  auto widen = [](const uint4& w, int e) -> float {
+    const uint32_t x = e < 2 ? w.x : e < 4 ? w.y : e < 6 ? w.z : w.w;
+    return __uint_as_float((e & 1) ? (x & 0xFFFF0000u) : (x << 16));
+  };
+  float acc[NS] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+  for (int c = 0; c < NC; ++c)
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      const float y = widen(yr[c], e), bs = (1.f - av[c][e]) * widen(sr[c], e), ay = av[c][e] * y;
+      acc[0] += y * y;
+      acc[1] += bs * bs;
+      acc[2] += bs * ay;
+      acc[3] += ay * ay;
+    }
+  if (need_x) {
+#pragma unroll
+    for (int c = 0; c < NC; ++c) {
+      const float4 x0 = *(const float4*)(u.x + row + 512 * c + 8 * lane);
+      const float4 x1 = *(const float4*)(u.x + row + 512 * c + 8 * lane + 4);
+      const float xs[8] = {x0.x, x0.y, x0.z, x0.w, x1.x, x1.y, x1.z, x1.w};
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        const float bs = (1.f - av[c][e]) * widen(sr[c], e), ay = av[c][e] * widen(yr[c], e);
+        acc[4] += bs * xs[e];
+        acc[5] += ay * xs[e];
+        acc[6] += xs[e] * xs[e];
+      }
+    }
+  }
+#pragma unroll
+  for (int q = 0; q < NS; ++q) acc[q] = wave_sum(acc[q]);
+  const float ny = inv_norm(acc[0]);
+  const float tt = fmaxf(acc[1] + 2.f * acc[2] * ny + acc[3] * ny * ny, 0.f);
+  const float nt = inv_norm(tt);
+  float scale = nt, norm_sp = sqrtf(tt) * nt, add_x = 0.f;
+  if (bnd == BND_LOOP_CONTINUE || bnd == BND_LOOP_FINAL) {
+    const float n2 = inv_norm(norm_sp * norm_sp);
+    scale *= n2;
+    norm_sp *= n2;
+  }
+  if (bnd == BND_LOOP_CONTINUE) {
+    const float dot = (acc[4] + acc[5] * ny) * scale;
+    const float n3 = inv_norm(norm_sp * norm_sp + 2.f * dot + acc[6]);
+    scale *= n3;
+    add_x = n3;
+  } else if (bnd == BND_SAVE_X) {
+    scale *= 2.f * inv_norm(4.f * norm_sp * norm_sp);
+  }
+#pragma unroll
+  for (int c = 0; c < NC; ++c) {
+    const size_t i = row + 512 * c + 8 * lane;
+    float xs[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+    if (need_x) {  // x again (from L2): it is read only at a loop's end
+      const float4 x0 = *(const float4*)(u.x + i), x1 = *(const float4*)(u.x + i + 4);
+      xs[0] = x0.x; xs[1] = x0.y; xs[2] = x0.z; xs[3] = x0.w; xs[4] = x1.x; xs[5] = x1.y; xs[6] = x1.z; xs[7] = x1.w;
+    }
+    float t[8], v[8];
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      t[e] = (1.f - av[c][e]) * widen(sr[c], e) + av[c][e] * widen(yr[c], e) * ny;
+      v[e] = t[e] * scale + add_x * xs[e];
+    }
+    if (bnd == BND_SAVE_X) {
+      *(float4*)(u.x + i) = make_float4(t[0] * nt, t[1] * nt, t[2] * nt, t[3] * nt);
+      *(float4*)(u.x + i + 4) = make_float4(t[4] * nt, t[5] * nt, t[6] * nt, t[7] * nt);
+    }
+    *(uint4*)((bf16_t*)u.sb + i) =
+        make_uint4(pack_bf16x2(v[0], v[1]), pack_bf16x2(v[2], v[3]), pack_bf16x2(v[4], v[5]), pack_bf16x2(v[6], v[7]));
+    if (u.s_out) {
+      *(float4*)(u.s_out + i) = make_float4(v[0], v[1], v[2], v[3]);
+      *(float4*)(u.s_out + i + 4) = make_float4(v[4], v[5], v[6], v[7]);
+    }
+  }
+}
+
 template <typename SB>
 __global__ __launch_bounds__(256) void k_stage_input(const float* x, float* s, SB* sb, size_t n, const int32_t* rows,
                                                      int H) {
@@ -234,7 +354,7 @@ __global__ __launch_bounds__(256) void k_stage_input(const float* x, float* s, S
        i += (size_t)gridDim.x * blockDim.x) {
     const size_t src = rows ? (size_t)rows[i / H] * H + i % H : i;
     const float v = x[src];
-    s[i] = v;
+    if (s) s[i] = v;
     st<SB>(sb, i, v);
   }
 }
@@ -290,7 +410,23 @@ hipError_t launch_scatter_rows(const float* s, const int32_t* rows, int M, int H
 hipError_t launch_update(const UpdateArgs& u, hipStream_t st) {
   if (u.M == 0) return hipSuccess;
   const bool few = u.M < 512;
-  if (!few && u.y_bf16 && u.splits == 1 && u.H % 8 == 0 && u.H <= 8 * 1024) {
+  const bool vec = !few && u.y_bf16 && u.splits == 1 && u.H % 8 == 0 && u.H <= 8 * 1024;
+  if (u.state_act && (!vec || u.act != ACT_BF16 || !u.sb)) return hipErrorInvalidValue;
+  if (u.state_act && u.H % 512 == 0 && u.H / 512 <= 8) {
+    const dim3 grid((u.M + 3) / 4);
+    switch (u.H / 512) {
+      case 1: hipLaunchKernelGGL(k_update_wave<1>, grid, dim3(256), 0, st, u); break;
+      case 2: hipLaunchKernelGGL(k_update_wave<2>, grid, dim3(256), 0, st, u); break;
+      case 3: hipLaunchKernelGGL(k_update_wave<3>, grid, dim3(256), 0, st, u); break;
+      case 4: hipLaunchKernelGGL(k_update_wave<4>, grid, dim3(256), 0, st, u); break;
+      case 5: hipLaunchKernelGGL(k_update_wave<5>, grid, dim3(256), 0, st, u); break;
+      case 6: hipLaunchKernelGGL(k_update_wave<6>, grid, dim3(256), 0, st, u); break;
+      case 7: hipLaunchKernelGGL(k_update_wave<7>, grid, dim3(256), 0, st, u); break;
+      default: hipLaunchKernelGGL(k_update_wave<8>, grid, dim3(256), 0, st, u); break;
+    }
+    return hipGetLastError();
+  }
+  if (vec) {
     const int per = u.H / 8;  // threads carrying 8 channels each
     if (u.act == ACT_F32) {
       if (per <= 320) hipLaunchKernelGGL((k_update_vec<float, 320>), dim3(u.M), dim3(320), 0, st, u);

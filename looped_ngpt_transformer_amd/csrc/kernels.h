@@ -72,6 +72,9 @@ struct UpdateArgs {
   int bnd = BND_NONE;
   int final_from = 0x7fffffff;  // with BND_LOOP_CONTINUE: rows >= this one end their last
                                 // loop here and take BND_LOOP_FINAL (mixed loop counts)
+  int state_act = 0;  // the state lives only in sb (bf16, read and rewritten in place); s is
+                      // not read, and s_out, when set, receives a float copy of the new
+                      // state (prefill form only: y_bf16, >= 512 rows, act bf16)
 };
 hipError_t launch_update(const UpdateArgs& u, hipStream_t st);
 // s = x_in; sb = act(x_in); with rows != NULL row r of s is row rows[r] of x_in

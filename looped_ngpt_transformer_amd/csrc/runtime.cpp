@@ -29,6 +29,7 @@ namespace {
 
 constexpr int NSTAGE = 4;          // pinned staging buffers in rotation
 constexpr int DELTA_CAP = 65536;   // page-table updates per upload
+constexpr int ACT_STATE_MIN_ROWS = 512;  // rows from which a prefill keeps its state in bf16 only
 constexpr int SKINNY_M = 256;      // rows up to which projections use split-K tiles
 constexpr size_t ALIGN = 256;
 constexpr int ROPE_INTS = 2 * 128 * 2;  // two tables of up to 128 doubles
@@ -470,6 +471,9 @@ struct CallPlan {
   bool skip_out = false;
   const float* res_x = nullptr;
   const float* res_s1 = nullptr;
+  // the state between sublayers is kept only as the bf16 GEMM operand (every layer call
+  // of the call takes the vectorised prefill update); the last layer writes a float copy
+  bool act_state = false;
 };
 
 // Algorithmic attention work of one layer call: visible (query, key) pairs and the
@@ -577,7 +581,8 @@ int run_layer(dory_ctx* ctx, hipStream_t st, const CallPlan& P, int l, int slot,
     u.splits = splits;
     u.y_bf16 = ybf;
     u.s = s;
-    u.s_out = sout ? sout : s;
+    u.s_out = sout ? sout : P.act_state ? nullptr : s;
+    u.state_act = P.act_state;
     u.sb = ws + W.sb;
     u.x = (float*)(ws + W.x);
     u.alpha = alpha;
@@ -588,7 +593,8 @@ int run_layer(dory_ctx* ctx, hipStream_t st, const CallPlan& P, int l, int slot,
     u.final_from = final_from;
     Prof pr(ctx, st, DORY_KC_UPDATE);
     const hipError_t e = launch_update(u, st);
-    pr.end(0, (double)M * D.H * ((ybf ? 2.0 : 4.0 * splits) + 4 + 4 + D.esz));
+    const double sbytes = P.act_state ? 2.0 * D.esz + (sout ? 4 : 0) : 4 + 4 + D.esz;
+    pr.end(0, (double)M * D.H * ((ybf ? 2.0 : 4.0 * splits) + sbytes));
     return e;
   };
 
@@ -762,9 +768,10 @@ int run_forward(dory_ctx* ctx, hipStream_t st, const CallPlan& P, const float* x
   } else {
     {
       Prof pr(ctx, st, DORY_KC_UPDATE);
-      HIPCHK(launch_stage_input(x_in, (float*)(ws + ctx->W.s), ws + ctx->W.sb, P.M, H, act, st, rowmap),
+      HIPCHK(launch_stage_input(x_in, P.act_state ? nullptr : (float*)(ws + ctx->W.s), ws + ctx->W.sb, P.M, H, act,
+                                st, rowmap),
              "stage_input");
-      pr.end(0, (double)P.M * H * (8.0 + ctx->D.esz));
+      pr.end(0, (double)P.M * H * ((P.act_state ? 4.0 : 8.0) + ctx->D.esz));
     }
     for (int l = 0; l < c.n_in; ++l) {
       if ((r = injected()) || (r = run_layer(ctx, st, P, l, 0, l == c.n_in - 1 ? BND_SAVE_X : BND_NONE, nullptr))) return r;
@@ -796,7 +803,9 @@ int run_forward(dory_ctx* ctx, hipStream_t st, const CallPlan& P, const float* x
   }
   const int L = c.n_in + c.n_rec + c.n_out;
   for (int l = c.n_in + c.n_rec; l < L; ++l) {
-    float* out = l == L - 1 && !P.reordered ? y_out : nullptr;
+    // the last layer's update writes the float result: into the caller's array, or into
+    // the state array that the row scatter reads
+    float* out = l < L - 1 ? nullptr : P.reordered ? (float*)(ws + ctx->W.s) : y_out;
     if ((r = injected()) || (r = run_layer(ctx, st, P, l, 0, BND_NONE, out))) return r;
     ++calls;
   }
@@ -966,6 +975,12 @@ int step(dory_ctx* ctx, hipStream_t st, int n, const int32_t* ids, const int32_t
     }
   }
   P.M = row;
+  {  // bf16 state when every layer call of this call takes the vectorised prefill update
+    int min_rows = P.M;
+    for (int t = 1; t <= P.k_max; ++t) min_rows = std::min(min_rows, P.loop_rows[t]);
+    P.act_state = c.act_dtype != DORY_DTYPE_F32 && min_rows >= ACT_STATE_MIN_ROWS && !P.cap_x && !P.cap_s1 &&
+                  !P.res_x && !P.skip_out;
+  }
   r = [&]() -> int {
     // deltas: whatever does not fit goes first in separate uploads
     int rr;

@@ -119,9 +119,9 @@ def test_bf16_attention_running_maximum(variant):
 
 @pytest.mark.parametrize("mode", ["per_loop", "last_loop"])
 def test_bf16_long_prefill(mode):
-    """A 600-row prefill: the row-vectorised update of long prefills (>= 512 rows; every
-    loop boundary occurs in it at k = 2), 256-row GEMM tiles with a ragged tail, then a
-    decode step."""
+    """A 600-row prefill: the update of long prefills (>= 512 rows: one wave per row, the
+    state between sublayers kept in bf16 only; every loop boundary occurs in it at k = 2),
+    256-row GEMM tiles with a ragged tail, then a decode step."""
     S = PSMALL
     sched = [("prefill", [(0, xin(S, 600, 61))]),
              ("decode", [(0, xin(S, 1, 62))])]
@@ -358,4 +358,41 @@ def test_mixed_loop_counts_in_one_call(mode):
         for j, i in enumerate(dorder):
             ref = O.prefill(cfg, W, seqs[i], to_np(X[j:j + 1]), ks[i], mode)
             compare(got[j:j + 1], ref, S, f"decode {step}, seq {i} (k={ks[i]})")
+    rt.close()
+
+
+@pytest.mark.parametrize("mode", ["per_loop", "last_loop"])
+def test_long_mixed_loop_chunks_state_forms(mode):
+    """Long prefill chunks of sequences at k = 1 and k = 2 in one call (caller order
+    [k = 1, k = 2], so the rows are reordered by k inside the call). First call: 520 rows
+    still loop in loop 2, so every layer call has >= 512 rows and the state between
+    sublayers is kept in bf16 only, with the last layer writing the float rows that the
+    row scatter reads. Second call: 300 rows loop in loop 2, so the call keeps the float
+    state (the vectorised update on 600 rows, the per-row one on 300). Each sequence
+    equals the oracle at its own k."""
+    from oracle import dory_oracle as O
+    from tests.helpers import to_np
+    S = PSMALL
+    ks = {0: 1, 1: 2}
+    w = gpu_weights(S, 19)
+    rt = DoryRuntime(S, w, max_loops=2, max_seqs=2, max_seq_len=1024, max_rows=640, mode=mode, loops=2)
+    cfg, W = oracle_model(S, w)
+    seqs = {i: O.Sequence(cfg) for i in ks}
+    for i in ks:  # each sequence is created at its own k
+        D.dory_set_loops(rt.ctx, ks[i])
+        X = xin(S, 8, 80 + i)
+        y = rt.prefill([i], [8], X)
+        torch.cuda.synchronize()
+        compare(y.cpu().double().numpy(), O.prefill(cfg, W, seqs[i], to_np(X), ks[i], mode), S, f"seq {i} prompt")
+    D.dory_set_loops(rt.ctx, 2)
+    if mode == "last_loop":
+        D.dory_set_seq_loops(rt.ctx, 0, 1)
+    for call, chunk in enumerate(({0: 100, 1: 520}, {0: 300, 1: 300})):
+        Xs = {i: xin(S, chunk[i], 90 + 2 * call + i) for i in ks}
+        y = rt.prefill([0, 1], [chunk[0], chunk[1]], torch.cat([Xs[0], Xs[1]]))
+        torch.cuda.synchronize()
+        assert D.dory_last_layer_calls(rt.ctx) == S["n_in"] + S["n_out"] + 2 * S["n_rec"]
+        got = y.cpu().double().numpy()
+        compare(got[:chunk[0]], O.prefill(cfg, W, seqs[0], to_np(Xs[0]), 1, mode), S, f"call {call}, seq 0 (k=1)")
+        compare(got[chunk[0]:], O.prefill(cfg, W, seqs[1], to_np(Xs[1]), 2, mode), S, f"call {call}, seq 1 (k=2)")
     rt.close()
