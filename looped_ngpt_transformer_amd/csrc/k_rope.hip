@@ -167,6 +167,22 @@ __global__ __launch_bounds__(256) void k_rope_tile(RopeArgs a) {
     }
   };
   load_batch(0);
+  // the lane's query-key scales (its 8 channels of each half), and the K pages of the
+  // quarter's rows (at most two), looked up once
+  float sq1[8], sq2[8];
+#pragma unroll
+  for (int e = 0; e < 8; ++e) sq1[e] = sq2[e] = 1.f;
+  if (a.qk_norm && j < HC) {
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      sq1[e] = a.s_qk[8 * j + e];
+      sq2[e] = a.s_qk[HALF + 8 * j + e];
+    }
+  }
+  bf16_t* const pg_lo = kv_page<bf16_t>(a.kv, seq, a.stream_idx, pos0);
+  bf16_t* const pg_hi = kv_page<bf16_t>(a.kv, seq, a.stream_idx, pos0 + nrows - 1);
+  const int lp_lo = pos0 / PAGE;
+  auto page_of = [&](int p) { return p / PAGE == lp_lo ? pg_lo : pg_hi; };
 
   // angles p * theta^(-2i/d) in double, reduced modulo 2*pi before the float sin/cos
   // (while the first batch is in flight)
@@ -214,13 +230,8 @@ __global__ __launch_bounds__(256) void k_rope_tile(RopeArgs a) {
       uint32_t o1[4], o2[4];
 #pragma unroll
       for (int e = 0; e < 8; e += 2) {
-        float a0 = r1[e] * sc, a1 = r1[e + 1] * sc, b0v = r2[e] * sc, b1 = r2[e + 1] * sc;
-        if (a.qk_norm) {
-          a0 *= a.s_qk[8 * j + e];
-          a1 *= a.s_qk[8 * j + e + 1];
-          b0v *= a.s_qk[HALF + 8 * j + e];
-          b1 *= a.s_qk[HALF + 8 * j + e + 1];
-        }
+        const float a0 = r1[e] * sc * sq1[e], a1 = r1[e + 1] * sc * sq1[e + 1];
+        const float b0v = r2[e] * sc * sq2[e], b1 = r2[e + 1] * sc * sq2[e + 1];
         o1[e / 2] = pack_bf16x2(a0, a1);
         o2[e / 2] = pack_bf16x2(b0v, b1);
       }
@@ -229,7 +240,7 @@ __global__ __launch_bounds__(256) void k_rope_tile(RopeArgs a) {
         *(uint4*)(q + 8 * j) = make_uint4(o1[0], o1[1], o1[2], o1[3]);
         *(uint4*)(q + HALF + 8 * j) = make_uint4(o2[0], o2[1], o2[2], o2[3]);
       } else {
-        bf16_t* kb = kv_kblock(kv_page<bf16_t>(a.kv, seq, a.stream_idx, p), a.kv, hk);
+        bf16_t* kb = kv_kblock(page_of(p), a.kv, hk);
         *(uint4*)(kb + kv_k_off(p % PAGE, 8 * j, D)) = make_uint4(o1[0], o1[1], o1[2], o1[3]);
         *(uint4*)(kb + kv_k_off(p % PAGE, HALF + 8 * j, D)) = make_uint4(o2[0], o2[1], o2[2], o2[3]);
       }
@@ -241,7 +252,7 @@ __global__ __launch_bounds__(256) void k_rope_tile(RopeArgs a) {
   for (int c = threadIdx.x; c < (g_hi - g_lo + 1) * D; c += 256) {
     const int g8 = g_lo + c / D, ch = c % D;
     const int p0 = 8 * g8;
-    bf16_t* vb = kv_vblock(kv_page<bf16_t>(a.kv, seq, a.stream_idx, p0), a.kv, hk);
+    bf16_t* vb = kv_vblock(page_of(p0), a.kv, hk);
     bf16_t* dst = vb + kv_v_off(p0 % PAGE, ch, D);
     if (p0 >= pos0 && p0 + 7 <= pos0 + nrows - 1) {
       uint32_t u[4];
