@@ -68,6 +68,7 @@ __global__ __launch_bounds__(PF_THREADS) void k_attn_prefill(AttnArgs a) {
   __shared__ __align__(16) unsigned char sm0[STAGE];
   __shared__ __align__(16) unsigned char sm1[STAGE];
   __shared__ __align__(16) unsigned char sm2[STAGE];
+  __shared__ __align__(16) float sqk_lds[D];  // query-key scales for the query prologue
   auto stage_ptr = [&](auto S) -> unsigned char* {
     if constexpr (decltype(S)::value == 0) return sm0;
     else if constexpr (decltype(S)::value == 1) return sm1;
@@ -97,13 +98,7 @@ __global__ __launch_bounds__(PF_THREADS) void k_attn_prefill(AttnArgs a) {
   const int qi = 32 * hh + l32;
   const bool qv = qi < nrows;
   const int qpos = pos0 + qi;
-  bf16x8 qf[KS];
-#pragma unroll
-  for (int c = 0; c < KS; ++c) {
-    uint4 v = make_uint4(0, 0, 0, 0);
-    if (qv) v = *(const uint4*)((const bf16_t*)a.q + (size_t)(row0 + qi) * HqD + (size_t)h * D + 16 * c + 8 * lh);
-    qf[c] = __builtin_bit_cast(bf16x8, v);
-  }
+  bf16x8 qf[KS];  // filled below, after group B has issued its first pages
 
   // Page ids of relative pages 64 c .. 64 c + 63 (chunk c), one per lane. A page id read
   // from the table at issue time would put a dependent global-memory round trip in front
@@ -315,13 +310,96 @@ __global__ __launch_bounds__(PF_THREADS) void k_attn_prefill(AttnArgs a) {
   using S0 = std::integral_constant<int, 0>;
   using S1 = std::integral_constant<int, 1>;
   using S2 = std::integral_constant<int, 2>;
-  if (hh == 1) {  // pages 0 and 1, then one phase behind group A
+  auto load_q = [&]() {
+    if (a.rope_cs) {
+      // unrotated q from the projection output: channel x (< D/2) pairs with x + D/2,
+      // which this lane holds in fragment c + KS/2; lane ^ 32 holds the rest of the row.
+      // The tile's (cos, sin) rows (nrows * D/2 pairs: at most 64 * D * 4 bytes, the size
+      // of a page stage) go straight into stage 2, which no page uses before group B's
+      // first softmax phase, and the query-key scales into LDS: each is read from HBM or
+      // L2 once per work-group instead of once per wave.
+      constexpr int HS = KS / 2, HALF = D / 2;
+      static_assert(64 * HALF * 8 == STAGE, "a tile's (cos, sin) rows fill one stage");
+      const int nchunk = nrows * HALF / 2;  // 16-byte chunks of the tile's rows
+      const unsigned char* csg = (const unsigned char*)(a.rope_cs + 2 * (size_t)row0 * HALF);
+      for (int b = w; b * 64 < nchunk; b += PF_WAVES)
+        if (b * 64 + lane < nchunk)
+          __builtin_amdgcn_global_load_lds((pf_gbl_t)(csg + (size_t)b * 1024 + lane * 16), (pf_lds_t)(sm2 + b * 1024),
+                                           16, 0, 0);
+      const bf16_t* qr = (const bf16_t*)a.q_raw + (size_t)(row0 + qi) * a.q_ld + (size_t)h * D + 8 * lh;
+      uint4 x1[HS], x2[HS];
+#pragma unroll
+      for (int c = 0; c < HS; ++c) {
+        x1[c] = x2[c] = make_uint4(0, 0, 0, 0);
+        if (qv) {
+          x1[c] = *(const uint4*)(qr + 16 * c);
+          x2[c] = *(const uint4*)(qr + HALF + 16 * c);
+        }
+      }
+      if (t < D) sqk_lds[t] = a.s_qk ? a.s_qk[t] : 1.f;
+      asm volatile("s_waitcnt vmcnt(0)" ::: "memory");  // this wave's (cos, sin) chunks are in LDS
+      __syncthreads();
+      const unsigned char* csl = sm2 + ((size_t)qi * HALF + 8 * lh) * 8;
+      float r1[HS][8], r2[HS][8];
+      float sq = 0.f;
+#pragma unroll
+      for (int c = 0; c < HS; ++c) {
+        float4 cs[4] = {};
+        if (qv) {
+#pragma unroll
+          for (int e = 0; e < 4; ++e) cs[e] = *(const float4*)(csl + 128 * c + 16 * e);
+        }
+        float s1[8], s2[8];
+#pragma unroll
+        for (int e = 0; e < 8; e += 4) {
+          const float4 v1 = *(const float4*)(sqk_lds + 16 * c + 8 * lh + e);
+          const float4 v2 = *(const float4*)(sqk_lds + HALF + 16 * c + 8 * lh + e);
+          s1[e] = v1.x; s1[e + 1] = v1.y; s1[e + 2] = v1.z; s1[e + 3] = v1.w;
+          s2[e] = v2.x; s2[e + 1] = v2.y; s2[e + 2] = v2.z; s2[e + 3] = v2.w;
+        }
+        const uint32_t w1[4] = {x1[c].x, x1[c].y, x1[c].z, x1[c].w}, w2[4] = {x2[c].x, x2[c].y, x2[c].z, x2[c].w};
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+          const float a1 = __uint_as_float((e & 1) ? (w1[e / 2] & 0xFFFF0000u) : (w1[e / 2] << 16));
+          const float a2 = __uint_as_float((e & 1) ? (w2[e / 2] & 0xFFFF0000u) : (w2[e / 2] << 16));
+          const float co = (e & 1) ? cs[e / 2].z : cs[e / 2].x, sn = (e & 1) ? cs[e / 2].w : cs[e / 2].y;
+          const float v1 = a1 * co - a2 * sn, v2 = a1 * sn + a2 * co;
+          sq += v1 * v1 + v2 * v2;
+          r1[c][e] = v1 * s1[e];
+          r2[c][e] = v2 * s2[e];
+        }
+      }
+      sq += __shfl_xor(sq, 32, 64);
+      const float sc = a.s_qk ? inv_norm(sq) : 1.f;
+#pragma unroll
+      for (int c = 0; c < HS; ++c) {
+        uint32_t o1[4], o2[4];
+#pragma unroll
+        for (int e = 0; e < 8; e += 2) {
+          o1[e / 2] = pack_bf16x2(r1[c][e] * sc, r1[c][e + 1] * sc);
+          o2[e / 2] = pack_bf16x2(r2[c][e] * sc, r2[c][e + 1] * sc);
+        }
+        qf[c] = __builtin_bit_cast(bf16x8, make_uint4(o1[0], o1[1], o1[2], o1[3]));
+        qf[c + HS] = __builtin_bit_cast(bf16x8, make_uint4(o2[0], o2[1], o2[2], o2[3]));
+      }
+    } else {
+#pragma unroll
+      for (int c = 0; c < KS; ++c) {
+        uint4 v = make_uint4(0, 0, 0, 0);
+        if (qv) v = *(const uint4*)((const bf16_t*)a.q + (size_t)(row0 + qi) * HqD + (size_t)h * D + 16 * c + 8 * lh);
+        qf[c] = __builtin_bit_cast(bf16x8, v);
+      }
+    }
+  };
+  // group B issues pages 0 and 1 before the query loads, so their latencies overlap;
+  // then it runs one phase behind group A
+  if (hh == 1) {
     issue(0, S0{});
     if (npg >= 1) issue(1, S1{});
-    asm volatile("s_waitcnt vmcnt(0)\n\ts_barrier\n\ts_barrier" ::: "memory");
-  } else {
-    asm volatile("s_barrier" ::: "memory");
   }
+  load_q();
+  if (hh == 1) asm volatile("s_waitcnt vmcnt(0)\n\ts_barrier\n\ts_barrier" ::: "memory");
+  else asm volatile("s_barrier" ::: "memory");
   __builtin_amdgcn_sched_barrier(0);
   // relative page r lives in stage r % 3; the loop is unrolled by the stage count so
   // every stage index is a compile-time constant

@@ -111,13 +111,14 @@ __global__ __launch_bounds__(256) void k_rope_kv(RopeArgs a) {
 }
 
 // Prefill form: one work-group per (16-row quarter of a tile of <= 64 consecutive rows
-// of one sequence, KV head), bf16 projection output. The rotation angles of the rows
-// are computed once into LDS; a 16-lane group then rotates one (row, head) with each
-// lane holding 8 consecutive channels of both halves of the RoPE pairs, so q and K are
-// read and written as 16-byte chunks (a K chunk of the page is 8 channels of one
-// token). V is transposed through LDS so that its page chunks (8 tokens of one
-// channel) are written whole; chunks the quarter covers only in part are written
-// element by element.
+// of one sequence, KV head), bf16 projection output. The (cos, sin) pairs of the rows
+// come from the call's table (k_rope_table, once per forward call for both bases) into
+// LDS; a 16-lane group then rotates one (row, head) with each lane holding 8
+// consecutive channels of both halves of the RoPE pairs, so q and K are read and
+// written as 16-byte chunks (a K chunk of the page is 8 channels of one token). With
+// q_out null only K and V are handled: the MFMA attention rotates q as it loads it. V
+// is transposed through LDS so that its page chunks (8 tokens of one channel) are
+// written whole; chunks the quarter covers only in part are written element by element.
 constexpr int RT_ROWS = 16;
 constexpr int IPG = 5;  // (row, head) items a 16-lane group loads at once
 
@@ -147,10 +148,12 @@ __global__ __launch_bounds__(256) void k_rope_tile(RopeArgs a) {
     const int i = c / (D / 8), k8 = c % (D / 8);
     *(uint4*)(Vs + i * VR + 8 * k8) = *(const uint4*)(X + (size_t)(row0 + i) * a.Nqkvg + vcol0 + 8 * k8);
   }
-  // (row, head) items of q heads hk*G .. hk*G+G-1 and K head hk: group gi = 4 wave + grp
-  // takes items gi, gi + 16, ...; the IPG items of a batch are loaded before any is used,
-  // so that a group keeps IPG x 32 bytes per lane in flight
-  const int items = nrows * (G + 1);
+  // (row, head) items of q heads hk*G .. hk*G+G-1 (unless q is left to the attention)
+  // and K head hk: group gi = 4 wave + grp takes items gi, gi + 16, ...; the IPG items of
+  // a batch are loaded before any is used, so that a group keeps IPG x 32 bytes per lane
+  // in flight
+  const int NQ = Q ? G : 0;  // q heads per row here
+  const int items = nrows * (NQ + 1);
   const int gi = wave * 4 + grp;
   uint4 u1[IPG], u2[IPG];
   auto load_batch = [&](int b0) {
@@ -158,8 +161,8 @@ __global__ __launch_bounds__(256) void k_rope_tile(RopeArgs a) {
     for (int u = 0; u < IPG; ++u) {
       const int item = b0 + gi + 16 * u;
       if (item < items && j < HC) {
-        const int i = item / (G + 1), hi = item % (G + 1);
-        const int col0 = hi == G ? a.Hq * D + hk * D : (hk * G + hi) * D;
+        const int i = item / (NQ + 1), hi = item % (NQ + 1);
+        const int col0 = hi == NQ ? a.Hq * D + hk * D : (hk * G + hi) * D;
         const bf16_t* x = X + (size_t)(row0 + i) * a.Nqkvg + col0 + 8 * j;
         u1[u] = *(const uint4*)x;
         u2[u] = *(const uint4*)(x + HALF);
@@ -184,15 +187,11 @@ __global__ __launch_bounds__(256) void k_rope_tile(RopeArgs a) {
   const int lp_lo = pos0 / PAGE;
   auto page_of = [&](int p) { return p / PAGE == lp_lo ? pg_lo : pg_hi; };
 
-  // angles p * theta^(-2i/d) in double, reduced modulo 2*pi before the float sin/cos
+  // (cos, sin) of the quarter's rows from the call's table, two pairs per 16-byte load
   // (while the first batch is in flight)
-  for (int c = threadIdx.x; c < nrows * HALF; c += 256) {
-    const int i = c / HALF, k = c % HALF;
-    double ang = (double)(pos0 + i) * a.freq[k];
-    ang -= 6.283185307179586 * rint(ang * 0.15915494309189535);
-    float sn, cs;
-    sincosf((float)ang, &sn, &cs);
-    CS[c] = make_float2(cs, sn);
+  for (int c = threadIdx.x; c < nrows * HALF / 2; c += 256) {
+    const int i = c / (HALF / 2), k2 = c % (HALF / 2);
+    *(float4*)(CS + i * HALF + 2 * k2) = *(const float4*)(a.cs + 2 * ((size_t)(row0 + i) * HALF + 2 * k2));
   }
   __syncthreads();
 
@@ -204,8 +203,8 @@ __global__ __launch_bounds__(256) void k_rope_tile(RopeArgs a) {
       const int item = b0 + gi + 16 * u;
       if (item >= items) break;  // uniform over the 16-lane group
       const bool act = j < HC;
-      const int i = item / (G + 1), hi = item % (G + 1);
-      const bool is_k = hi == G;
+      const int i = item / (NQ + 1), hi = item % (NQ + 1);
+      const bool is_k = hi == NQ;
       const int p = pos0 + i;
       float r1[8], r2[8];
       float sq = 0.f;
@@ -271,7 +270,7 @@ __global__ __launch_bounds__(256) void k_rope_tile(RopeArgs a) {
 
 hipError_t launch_rope_kv_tiles(const RopeArgs& a, hipStream_t st) {
   if (a.n_tiles == 0) return hipSuccess;
-  if (a.in_f32 || a.kv.act != ACT_BF16 || !a.freq || !a.tiles || a.Hq % a.Hkv) return hipErrorInvalidValue;
+  if (a.in_f32 || a.kv.act != ACT_BF16 || !a.cs || !a.tiles || a.Hq % a.Hkv) return hipErrorInvalidValue;
   dim3 grid(a.n_tiles, a.Hkv, 64 / RT_ROWS);
   switch (a.d) {
     case 64: hipLaunchKernelGGL(k_rope_tile<64>, grid, dim3(256), 0, st, a); break;
@@ -279,6 +278,32 @@ hipError_t launch_rope_kv_tiles(const RopeArgs& a, hipStream_t st) {
     case 160: hipLaunchKernelGGL(k_rope_tile<160>, grid, dim3(256), 0, st, a); break;
     default: return hipErrorInvalidValue;
   }
+  return hipGetLastError();
+}
+
+// One thread per (base, row, pair).
+__global__ __launch_bounds__(256) void k_rope_table(const int32_t* pos, const double* freq, int M, int half,
+                                                    size_t ld, float* cs) {
+  const size_t n = (size_t)M * half;
+  for (size_t t = blockIdx.x * (size_t)blockDim.x + threadIdx.x; t < 2 * n; t += (size_t)gridDim.x * blockDim.x) {
+    const int b = t >= n;
+    const size_t r = t - b * n;
+    const int m = (int)(r / half), i = (int)(r % half);
+    double ang = (double)pos[m] * freq[128 * b + i];
+    ang -= 6.283185307179586 * rint(ang * 0.15915494309189535);
+    float sn, c;
+    sincosf((float)ang, &sn, &c);
+    *(float2*)(cs + 2 * (b * ld + r)) = make_float2(c, sn);
+  }
+}
+
+hipError_t launch_rope_table(const int32_t* pos, const double* freq, int M, int half, size_t ld, float* cs,
+                             hipStream_t st) {
+  if (M <= 0) return hipSuccess;
+  if (half > 128 || (size_t)M * half > ld) return hipErrorInvalidValue;
+  const size_t n = 2 * (size_t)M * half;
+  const unsigned blocks = (unsigned)std::min<size_t>((n + 255) / 256, 4096);
+  hipLaunchKernelGGL(k_rope_table, dim3(blocks), dim3(256), 0, st, pos, freq, M, half, ld, cs);
   return hipGetLastError();
 }
 

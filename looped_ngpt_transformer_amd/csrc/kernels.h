@@ -112,14 +112,27 @@ struct RopeArgs {
   int stream_idx = 0;           // (layer, slot) stream within the sequence
   const int32_t* tiles = nullptr;  // prefill tiles [n_tiles][4]: row0, nrows, pos0, seq slot
   int n_tiles = 0;
+  const float* cs = nullptr;    // tiled form: [M][d/2] (cos, sin) pairs of this layer's angles
 };
 hipError_t launch_rope_kv(const RopeArgs& a, hipStream_t st);
-// Prefill form over the tiles (bf16 projection output, d in {64, 128, 160}).
+// Prefill form over the tiles (bf16 projection output, d in {64, 128, 160}); q_out null:
+// only K and V (the MFMA attention rotates q itself).
 hipError_t launch_rope_kv_tiles(const RopeArgs& a, hipStream_t st);
+// (cos, sin) of pos[m] * freq[b][i] for both bases b (0 sliding, 1 full; freq [2][128]
+// doubles, angle reduced modulo 2 pi in double, sin/cos in float): cs[b][m][i] as float
+// pairs at cs + 2 (b * ld + m * half + i), rows m < M, i < half.
+hipError_t launch_rope_table(const int32_t* pos, const double* freq, int M, int half, size_t ld, float* cs,
+                             hipStream_t st);
 
 // ------------------------------------------------------------------------ attention
 struct AttnArgs {
   const void* q = nullptr;        // act [M, Hq*d] (rotated, normalised)
+  // MFMA prefill with rope_cs: q is read unrotated from the projection output (row m,
+  // head h at q_raw[m * q_ld + h * d], bf16) and rotated by rope_cs ([M][d/2] (cos, sin)),
+  // normalised and scaled by s_qk (when set) in the kernel; q is then not read
+  const void* q_raw = nullptr;
+  int q_ld = 0;
+  const float* rope_cs = nullptr;
   // gate pre-activation, read where the projection left it: row m, channel c at
   // g[m * g_ld + c] (+ split s at s * g_sstride for float partials, summed over g_splits)
   const void* g = nullptr;        // null: no gate

@@ -48,7 +48,7 @@ struct Dims {
 };
 
 struct WsLayout {
-  size_t table, meta, s, x, sb, qkvg, q, o, h, part, apart, wexp, total;
+  size_t table, meta, s, x, sb, qkvg, q, o, h, part, apart, wexp, rcs, total;
   size_t part_floats, apart_floats;
   size_t meta_ints;
 };
@@ -109,6 +109,8 @@ WsLayout layout_of(const dory_config& c, const Dims& D) {
                                 (size_t)D.H * D.I});
   const bool quant = c.weight_format == DORY_WFMT_NVFP4 || c.weight_format == DORY_WFMT_MXFP8;
   W.wexp = take(quant && c.max_rows > SKINNY_M ? wmax * 2 : 0);
+  // (cos, sin) of every row's RoPE angles for both bases (prefill calls): [2][R][d/2] pairs
+  W.rcs = take(R * D.d * 8);
   W.total = off;
   return W;
 }
@@ -634,15 +636,30 @@ int run_layer(dory_ctx* ctx, hipStream_t st, const CallPlan& P, int l, int slot,
   ra.stream_idx = sidx;
   ra.tiles = meta + 2 * c.max_rows;
   ra.n_tiles = P.n_tiles;
+  const bool tiled = !ra.in_f32 && P.max_tile_rows > 1 && (D.d == 64 || D.d == 128 || D.d == 160);
+  // the MFMA prefill kernel takes the gate in bf16: small chunks, whose projection
+  // leaves float split partials, use the row-wise kernels
+  const bool mfma_attn = !f32 && !(ra.in_f32 && D.Ng) && P.max_tile_rows > 1 && D.Hq == 4 * D.Hkv &&
+                         (D.d == 64 || D.d == 128 || D.d == 160);
+  // with both, the attention rotates q as it loads it and the RoPE kernel does K and V
+  const bool q_in_attn = tiled && mfma_attn;
+  if (tiled) ra.cs = (const float*)(ws + W.rcs) + (full ? (size_t)c.max_rows * D.d : 0);
+  if (q_in_attn) ra.q_out = nullptr;
   {
     Prof pr(ctx, st, DORY_KC_ROPE);
-    const bool tiled = !ra.in_f32 && P.max_tile_rows > 1 && (D.d == 64 || D.d == 128 || D.d == 160);
     HIPCHK(tiled ? launch_rope_kv_tiles(ra, st) : launch_rope_kv(ra, st), "rope_kv");
-    pr.end(0, (double)M * (D.Nqkvg * (ra.in_f32 ? 4.0 * S : D.esz) + (2 * D.Nq + 2 * D.Nkv) * D.esz));
+    const double qb = q_in_attn ? 0.0 : 2.0 * D.Nq * D.esz;  // q read and written
+    pr.end(0, tiled ? (double)M * (qb + 4.0 * D.Nkv * D.esz)
+                    : (double)M * (D.Nqkvg * (ra.in_f32 ? 4.0 * S : D.esz) + (2 * D.Nq + 2 * D.Nkv) * D.esz));
   }
 
   AttnArgs aa;
   aa.q = ws + W.q;
+  if (q_in_attn) {
+    aa.q_raw = ws + W.qkvg;
+    aa.q_ld = D.Nqkvg;
+    aa.rope_cs = ra.cs;
+  }
   if (D.Ng) {  // the gate columns of the [q|k|v|gate] projection output
     const int gcol = D.Nq + 2 * D.Nkv;
     aa.g_ld = D.Nqkvg;
@@ -677,10 +694,6 @@ int run_layer(dory_ctx* ctx, hipStream_t st, const CallPlan& P, int l, int slot,
   {
     double pairs, keys;
     attn_work(P, full, c.window, &pairs, &keys);
-    // the MFMA prefill kernel takes the gate in bf16: small chunks, whose projection
-    // leaves float split partials, use the row-wise kernels
-    const bool mfma_attn = !f32 && !aa.g_f32 && P.max_tile_rows > 1 && D.Hq == 4 * D.Hkv &&
-                           (D.d == 64 || D.d == 128 || D.d == 160);
     int splits = 1;
     {
       // the prefill kernel also applies the gate and writes o; the split-key kernel reads
@@ -753,6 +766,15 @@ int run_forward(dory_ctx* ctx, hipStream_t st, const CallPlan& P, const float* x
     pr.end(0, (double)P.M * H * 8.0);
     return DORY_OK;
   };
+  if (act == ACT_BF16 && P.max_tile_rows > 1 && P.M > 0) {  // RoPE (cos, sin) of every row, both bases
+    const int half = ctx->D.d / 2;
+    Prof pr(ctx, st, DORY_KC_ROPE);
+    HIPCHK(launch_rope_table((const int32_t*)(ws + ctx->W.meta),
+                             (const double*)((const int32_t*)(ws + ctx->W.meta) + 2 * R + 4 * ctx->D.max_tiles), P.M,
+                             half, (size_t)R * half, (float*)(ws + ctx->W.rcs), st),
+           "rope table");
+    pr.end(0, (double)P.M * half * 16.0);
+  }
   int64_t calls = 0;
   int r;
   auto injected = [&]() {
