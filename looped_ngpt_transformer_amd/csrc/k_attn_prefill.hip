@@ -314,18 +314,18 @@ __global__ __launch_bounds__(PF_THREADS) void k_attn_prefill(AttnArgs a) {
     if (a.rope_cs) {
       // unrotated q from the projection output: channel x (< D/2) pairs with x + D/2,
       // which this lane holds in fragment c + KS/2; lane ^ 32 holds the rest of the row.
-      // The tile's (cos, sin) rows (nrows * D/2 pairs: at most 64 * D * 4 bytes, the size
-      // of a page stage) go straight into stage 2, which no page uses before group B's
-      // first softmax phase, and the query-key scales into LDS: each is read from HBM or
-      // L2 once per work-group instead of once per wave.
+      // The tile's block of the (cos, sin) table (64 rows x D/2 pairs, chunk-major: the
+      // size of a page stage) goes straight into stage 2, which no page uses before group
+      // B's first softmax phase, and the query-key scales into LDS: each is read from HBM
+      // or L2 once per work-group instead of once per wave. Chunk-major, the 16-byte reads
+      // of 32 consecutive rows below are consecutive, free of bank conflicts.
       constexpr int HS = KS / 2, HALF = D / 2;
-      static_assert(64 * HALF * 8 == STAGE, "a tile's (cos, sin) rows fill one stage");
-      const int nchunk = nrows * HALF / 2;  // 16-byte chunks of the tile's rows
-      const unsigned char* csg = (const unsigned char*)(a.rope_cs + 2 * (size_t)row0 * HALF);
-      for (int b = w; b * 64 < nchunk; b += PF_WAVES)
-        if (b * 64 + lane < nchunk)
-          __builtin_amdgcn_global_load_lds((pf_gbl_t)(csg + (size_t)b * 1024 + lane * 16), (pf_lds_t)(sm2 + b * 1024),
-                                           16, 0, 0);
+      static_assert(64 * HALF * 8 == STAGE && STAGE % (PF_WAVES * 1024) == 0, "a tile's block fills one stage");
+      const unsigned char* csg = (const unsigned char*)(a.rope_cs + (size_t)tile * 64 * D);
+#pragma unroll
+      for (int b = w; b < STAGE / 1024; b += PF_WAVES)
+        __builtin_amdgcn_global_load_lds((pf_gbl_t)(csg + (size_t)b * 1024 + lane * 16), (pf_lds_t)(sm2 + b * 1024), 16,
+                                         0, 0);
       const bf16_t* qr = (const bf16_t*)a.q_raw + (size_t)(row0 + qi) * a.q_ld + (size_t)h * D + 8 * lh;
       uint4 x1[HS], x2[HS];
 #pragma unroll
@@ -339,7 +339,7 @@ __global__ __launch_bounds__(PF_THREADS) void k_attn_prefill(AttnArgs a) {
       if (t < D) sqk_lds[t] = a.s_qk ? a.s_qk[t] : 1.f;
       asm volatile("s_waitcnt vmcnt(0)" ::: "memory");  // this wave's (cos, sin) chunks are in LDS
       __syncthreads();
-      const unsigned char* csl = sm2 + ((size_t)qi * HALF + 8 * lh) * 8;
+      const unsigned char* csl = sm2 + (size_t)(64 * 4 * lh + qi) * 16;  // chunk 4 lh of row qi
       float r1[HS][8], r2[HS][8];
       float sq = 0.f;
 #pragma unroll
@@ -347,7 +347,7 @@ __global__ __launch_bounds__(PF_THREADS) void k_attn_prefill(AttnArgs a) {
         float4 cs[4] = {};
         if (qv) {
 #pragma unroll
-          for (int e = 0; e < 4; ++e) cs[e] = *(const float4*)(csl + 128 * c + 16 * e);
+          for (int e = 0; e < 4; ++e) cs[e] = *(const float4*)(csl + (8 * c + e) * 64 * 16);  // chunk 8 c + 4 lh + e
         }
         float s1[8], s2[8];
 #pragma unroll

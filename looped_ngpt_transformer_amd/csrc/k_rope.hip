@@ -187,11 +187,12 @@ __global__ __launch_bounds__(256) void k_rope_tile(RopeArgs a) {
   const int lp_lo = pos0 / PAGE;
   auto page_of = [&](int p) { return p / PAGE == lp_lo ? pg_lo : pg_hi; };
 
-  // (cos, sin) of the quarter's rows from the call's table, two pairs per 16-byte load
-  // (while the first batch is in flight)
+  // (cos, sin) of the quarter's rows from the tile's block of the call's table, two pairs
+  // per 16-byte load (while the first batch is in flight)
+  const float* cst = a.cs + (size_t)blockIdx.x * 64 * D;
   for (int c = threadIdx.x; c < nrows * HALF / 2; c += 256) {
-    const int i = c / (HALF / 2), k2 = c % (HALF / 2);
-    *(float4*)(CS + i * HALF + 2 * k2) = *(const float4*)(a.cs + 2 * ((size_t)(row0 + i) * HALF + 2 * k2));
+    const int i = c % nrows, k2 = c / nrows;
+    *(float4*)(CS + i * HALF + 2 * k2) = *(const float4*)(cst + 4 * (64 * k2 + r0 + i));
   }
   __syncthreads();
 
@@ -281,29 +282,35 @@ hipError_t launch_rope_kv_tiles(const RopeArgs& a, hipStream_t st) {
   return hipGetLastError();
 }
 
-// One thread per (base, row, pair).
-__global__ __launch_bounds__(256) void k_rope_table(const int32_t* pos, const double* freq, int M, int half,
+// One thread per (base, tile, chunk of two pairs, row).
+__global__ __launch_bounds__(256) void k_rope_table(const int32_t* tiles, int n_tiles, const double* freq, int half,
                                                     size_t ld, float* cs) {
-  const size_t n = (size_t)M * half;
+  const int nk = half / 2;
+  const size_t n = (size_t)n_tiles * nk * 64;
   for (size_t t = blockIdx.x * (size_t)blockDim.x + threadIdx.x; t < 2 * n; t += (size_t)gridDim.x * blockDim.x) {
     const int b = t >= n;
-    const size_t r = t - b * n;
-    const int m = (int)(r / half), i = (int)(r % half);
-    double ang = (double)pos[m] * freq[128 * b + i];
-    ang -= 6.283185307179586 * rint(ang * 0.15915494309189535);
-    float sn, c;
-    sincosf((float)ang, &sn, &c);
-    *(float2*)(cs + 2 * (b * ld + r)) = make_float2(c, sn);
+    const size_t q = t - b * n;
+    const int r = (int)(q % 64), k = (int)((q / 64) % nk), tile = (int)(q / (64 * (size_t)nk));
+    const int32_t* tl = tiles + 4 * tile;
+    if (r >= tl[1]) continue;
+    float v[4];
+#pragma unroll
+    for (int e = 0; e < 2; ++e) {
+      double ang = (double)(tl[2] + r) * freq[128 * b + 2 * k + e];
+      ang -= 6.283185307179586 * rint(ang * 0.15915494309189535);
+      sincosf((float)ang, &v[2 * e + 1], &v[2 * e]);
+    }
+    *(float4*)(cs + b * ld + (size_t)tile * 256 * nk + 4 * (64 * (size_t)k + r)) = make_float4(v[0], v[1], v[2], v[3]);
   }
 }
 
-hipError_t launch_rope_table(const int32_t* pos, const double* freq, int M, int half, size_t ld, float* cs,
+hipError_t launch_rope_table(const int32_t* tiles, int n_tiles, const double* freq, int half, size_t ld, float* cs,
                              hipStream_t st) {
-  if (M <= 0) return hipSuccess;
-  if (half > 128 || (size_t)M * half > ld) return hipErrorInvalidValue;
-  const size_t n = 2 * (size_t)M * half;
+  if (n_tiles <= 0) return hipSuccess;
+  if (half > 128 || half % 2 || (size_t)n_tiles * 128 * half > ld) return hipErrorInvalidValue;
+  const size_t n = 2 * (size_t)n_tiles * (half / 2) * 64;
   const unsigned blocks = (unsigned)std::min<size_t>((n + 255) / 256, 4096);
-  hipLaunchKernelGGL(k_rope_table, dim3(blocks), dim3(256), 0, st, pos, freq, M, half, ld, cs);
+  hipLaunchKernelGGL(k_rope_table, dim3(blocks), dim3(256), 0, st, tiles, n_tiles, freq, half, ld, cs);
   return hipGetLastError();
 }
 

@@ -112,24 +112,27 @@ struct RopeArgs {
   int stream_idx = 0;           // (layer, slot) stream within the sequence
   const int32_t* tiles = nullptr;  // prefill tiles [n_tiles][4]: row0, nrows, pos0, seq slot
   int n_tiles = 0;
-  const float* cs = nullptr;    // tiled form: [M][d/2] (cos, sin) pairs of this layer's angles
+  const float* cs = nullptr;    // tiled form: this layer's (cos, sin) table (launch_rope_table)
 };
 hipError_t launch_rope_kv(const RopeArgs& a, hipStream_t st);
 // Prefill form over the tiles (bf16 projection output, d in {64, 128, 160}); q_out null:
 // only K and V (the MFMA attention rotates q itself).
 hipError_t launch_rope_kv_tiles(const RopeArgs& a, hipStream_t st);
-// (cos, sin) of pos[m] * freq[b][i] for both bases b (0 sliding, 1 full; freq [2][128]
-// doubles, angle reduced modulo 2 pi in double, sin/cos in float): cs[b][m][i] as float
-// pairs at cs + 2 (b * ld + m * half + i), rows m < M, i < half.
-hipError_t launch_rope_table(const int32_t* pos, const double* freq, int M, int half, size_t ld, float* cs,
+// (cos, sin) of p * freq[b][i] for both bases b (0 sliding, 1 full; freq [2][128] doubles,
+// angle reduced modulo 2 pi in double, sin/cos in float) for the rows of the prefill
+// tiles, one block of 64 rows per tile: row r (position tile.pos0 + r, r < tile.nrows) of
+// tile t, pairs 2k and 2k + 1, as 4 floats at cs + b * ld + t * 64 * 2 half + 4 (64 k + r)
+// (chunk-major, so that 16-byte reads of consecutive rows are consecutive).
+hipError_t launch_rope_table(const int32_t* tiles, int n_tiles, const double* freq, int half, size_t ld, float* cs,
                              hipStream_t st);
 
 // ------------------------------------------------------------------------ attention
 struct AttnArgs {
   const void* q = nullptr;        // act [M, Hq*d] (rotated, normalised)
   // MFMA prefill with rope_cs: q is read unrotated from the projection output (row m,
-  // head h at q_raw[m * q_ld + h * d], bf16) and rotated by rope_cs ([M][d/2] (cos, sin)),
-  // normalised and scaled by s_qk (when set) in the kernel; q is then not read
+  // head h at q_raw[m * q_ld + h * d], bf16) and rotated by rope_cs (this layer's table
+  // of launch_rope_table), normalised and scaled by s_qk (when set) in the kernel; q is
+  // then not read
   const void* q_raw = nullptr;
   int q_ld = 0;
   const float* rope_cs = nullptr;

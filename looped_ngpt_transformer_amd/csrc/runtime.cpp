@@ -76,6 +76,9 @@ Dims dims_of(const dory_config& c) {
   return D;
 }
 
+// floats of one base's RoPE (cos, sin) table: a block of 64 rows x d/2 pairs per tile
+size_t rope_table_floats(const Dims& D) { return (size_t)D.max_tiles * 64 * D.d; }
+
 WsLayout layout_of(const dory_config& c, const Dims& D) {
   WsLayout W{};
   const size_t R = (size_t)c.max_rows;
@@ -109,8 +112,8 @@ WsLayout layout_of(const dory_config& c, const Dims& D) {
                                 (size_t)D.H * D.I});
   const bool quant = c.weight_format == DORY_WFMT_NVFP4 || c.weight_format == DORY_WFMT_MXFP8;
   W.wexp = take(quant && c.max_rows > SKINNY_M ? wmax * 2 : 0);
-  // (cos, sin) of every row's RoPE angles for both bases (prefill calls): [2][R][d/2] pairs
-  W.rcs = take(R * D.d * 8);
+  // (cos, sin) of the prefill tiles' RoPE angles for both bases (64-row blocks per tile)
+  W.rcs = take(2 * rope_table_floats(D) * 4);
   W.total = off;
   return W;
 }
@@ -643,7 +646,7 @@ int run_layer(dory_ctx* ctx, hipStream_t st, const CallPlan& P, int l, int slot,
                          (D.d == 64 || D.d == 128 || D.d == 160);
   // with both, the attention rotates q as it loads it and the RoPE kernel does K and V
   const bool q_in_attn = tiled && mfma_attn;
-  if (tiled) ra.cs = (const float*)(ws + W.rcs) + (full ? (size_t)c.max_rows * D.d : 0);
+  if (tiled) ra.cs = (const float*)(ws + W.rcs) + (full ? rope_table_floats(D) : 0);
   if (q_in_attn) ra.q_out = nullptr;
   {
     Prof pr(ctx, st, DORY_KC_ROPE);
@@ -766,12 +769,12 @@ int run_forward(dory_ctx* ctx, hipStream_t st, const CallPlan& P, const float* x
     pr.end(0, (double)P.M * H * 8.0);
     return DORY_OK;
   };
-  if (act == ACT_BF16 && P.max_tile_rows > 1 && P.M > 0) {  // RoPE (cos, sin) of every row, both bases
+  if (act == ACT_BF16 && P.max_tile_rows > 1 && P.n_tiles > 0) {  // RoPE (cos, sin) of every tile row, both bases
     const int half = ctx->D.d / 2;
+    const int32_t* meta = (const int32_t*)(ws + ctx->W.meta);
     Prof pr(ctx, st, DORY_KC_ROPE);
-    HIPCHK(launch_rope_table((const int32_t*)(ws + ctx->W.meta),
-                             (const double*)((const int32_t*)(ws + ctx->W.meta) + 2 * R + 4 * ctx->D.max_tiles), P.M,
-                             half, (size_t)R * half, (float*)(ws + ctx->W.rcs), st),
+    HIPCHK(launch_rope_table(meta + 2 * R, P.n_tiles, (const double*)(meta + 2 * R + 4 * ctx->D.max_tiles), half,
+                             rope_table_floats(ctx->D), (float*)(ws + ctx->W.rcs), st),
            "rope table");
     pr.end(0, (double)P.M * half * 16.0);
   }

@@ -26,7 +26,7 @@ hipError_t launch_resume_state(const float*, const float*, const int32_t*, int, 
 }
 hipError_t launch_rope_kv(const RopeArgs&, hipStream_t) { return g_stub_launch; }
 hipError_t launch_rope_kv_tiles(const RopeArgs&, hipStream_t) { return g_stub_launch; }
-hipError_t launch_rope_table(const int32_t*, const double*, int, int, size_t, float*, hipStream_t) {
+hipError_t launch_rope_table(const int32_t*, int, const double*, int, size_t, float*, hipStream_t) {
   return g_stub_launch;
 }
 hipError_t launch_attn_rows(const AttnArgs&, int, int*, hipStream_t) { return g_stub_launch; }
