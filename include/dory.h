@@ -118,7 +118,8 @@ typedef struct dory_config {
  *         block scale bytes [rows, K/16]; else NULL
  *  g_*    NVFP4 only: the matching matrix's scale (one float, device); else NULL.
  *         NVFP4 matrices hold packed codes [rows, K/2] (element 2j in the low nibble)
- *  alpha_attn, alpha_mlp [H] float: effective per-channel rates (arXiv §2: 0.05 init)
+ *  alpha_attn, alpha_mlp [H] float, 16-byte aligned: effective per-channel rates
+ *         (arXiv §2: 0.05 init)
  *  s_qk   [d] float: effective query-key scale
  *  f_*    bf16 contexts, optional: the matching matrix in fragment order, as written by
  *         dory_arrange_weights (same bytes, another order; 16-byte aligned). When set,
@@ -206,8 +207,9 @@ int dory_get_kv_mode(const dory_ctx* ctx, int* mode);
  * x_in  device float [sum n_new, H]: unit-norm input states, rows grouped by sequence
  *       in seq_ids order, positions increasing.
  * y_out device float [sum n_new, H]: final states (output of the output block).
+ * x_in and y_out are 16-byte aligned (the update kernels move 16 bytes per access).
  * Errors: INVALID_ARG (ids repeated, n_new < 1, sum n_new > max_rows, position would
- * reach max_seq_len, too many live sequences, null pointers), STATE (weights, pool or
+ * reach max_seq_len, too many live sequences, null or misaligned pointers), STATE (weights, pool or
  * workspace unbound), OUT_OF_KV (pool too small; nothing reserved), HIP.
  * In last_loop mode results depend on the chunk schedule (earlier chunks' tokens are
  * seen with their final-loop entries).
@@ -219,7 +221,8 @@ int dory_prefill(dory_ctx* ctx, void* stream, int n_seqs, const int32_t* seq_ids
  * summary §3.2 and §6.1) for one new token of each listed live sequence (a chunk of one
  * row at position = the sequence's length), whose queries read the cached keys and
  * values of all earlier positions (the sliding window's last W on sliding layers).
- * x_in, y_out device float [n_seqs, H]. Errors as prefill; unknown id -> INVALID_ARG. */
+ * x_in, y_out device float [n_seqs, H], 16-byte aligned. Errors as prefill; unknown id
+ * -> INVALID_ARG. */
 int dory_decode_step(dory_ctx* ctx, void* stream, int n_seqs, const int32_t* seq_ids,
                      const float* x_in, float* y_out);
 

@@ -23,9 +23,47 @@ __global__ __launch_bounds__(256) void k_swiglu(const float* gu, int splits, int
   }
 }
 
+// I % 4 == 0: each thread owns 4 consecutive columns of gate and of up, and requests
+// their partials of up to 8 splits at once (16-byte loads; summed in split order).
+template <typename T>
+__global__ __launch_bounds__(256) void k_swiglu4(const float* gu, int splits, int M, int I, T* h) {
+  constexpr int QS = 8;
+  const int m = blockIdx.x;
+  const int i = 4 * (blockIdx.y * 256 + threadIdx.x);
+  if (i >= I) return;
+  const size_t sstride = (size_t)M * 2 * I;
+  const float* p = gu + (size_t)m * 2 * I + i;
+  float g[4] = {0.f, 0.f, 0.f, 0.f}, u[4] = {0.f, 0.f, 0.f, 0.f};
+  for (int s0 = 0; s0 < splits; s0 += QS) {
+    float4 vg[QS], vu[QS];
+#pragma unroll
+    for (int q = 0; q < QS; ++q) {
+      const bool ok = s0 + q < splits;
+      vg[q] = ok ? *(const float4*)(p + (s0 + q) * sstride) : make_float4(0.f, 0.f, 0.f, 0.f);
+      vu[q] = ok ? *(const float4*)(p + (s0 + q) * sstride + I) : make_float4(0.f, 0.f, 0.f, 0.f);
+    }
+#pragma unroll
+    for (int q = 0; q < QS; ++q) {
+      g[0] += vg[q].x; g[1] += vg[q].y; g[2] += vg[q].z; g[3] += vg[q].w;
+      u[0] += vu[q].x; u[1] += vu[q].y; u[2] += vu[q].z; u[3] += vu[q].w;
+    }
+  }
+  const size_t o = (size_t)m * I + i;
+#pragma unroll
+  for (int e = 0; e < 4; ++e) st<T>(h, o + e, silu(g[e]) * u[e]);
+}
+
 hipError_t launch_swiglu(const float* gu, int splits, int M, int I, void* h, int act,
                          hipStream_t st) {
   if (M == 0) return hipSuccess;
+  if (I % 4 == 0) {
+    const dim3 grid(M, (I / 4 + 255) / 256);
+    if (act == ACT_F32)
+      hipLaunchKernelGGL(k_swiglu4<float>, grid, dim3(256), 0, st, gu, splits, M, I, (float*)h);
+    else
+      hipLaunchKernelGGL(k_swiglu4<bf16_t>, grid, dim3(256), 0, st, gu, splits, M, I, (bf16_t*)h);
+    return hipGetLastError();
+  }
   const dim3 grid(M, (I + 1023) / 1024);
   if (act == ACT_F32)
     hipLaunchKernelGGL(k_swiglu<float>, grid, dim3(256), 0, st, gu, splits, M, I, (float*)h);

@@ -130,6 +130,93 @@ __global__ __launch_bounds__(UPD_THREADS) void k_update(UpdateArgs u) {
   }
 }
 
+// Decode form (y as split partials, H % 256 == 0, H <= 4096): H / 4 threads per row, each
+// owning 4 consecutive channels, so that every access is one 16-byte load or store and a
+// thread requests the partials of up to 16 splits at once (summed in split order).
+template <typename SB>
+__global__ __launch_bounds__(1024) void k_update_split4(UpdateArgs u) {
+  constexpr int NS = 7, QS = 16;
+  __shared__ float red[1024 / WAVE][NS];
+  const int H = u.H, NW = blockDim.x / WAVE;
+  const size_t row = (size_t)blockIdx.x * H;
+  const int i0 = 4 * threadIdx.x;
+  const int bnd = u.bnd == BND_LOOP_CONTINUE && (int)blockIdx.x >= u.final_from ? BND_LOOP_FINAL : u.bnd;
+  const bool need_x = bnd == BND_LOOP_CONTINUE;
+  const size_t sstride = (size_t)u.M * H;
+  const float4 s4 = *(const float4*)(u.s + row + i0), a4 = *(const float4*)(u.alpha + i0);
+  const float4 x4 = need_x ? *(const float4*)(u.x + row + i0) : make_float4(0.f, 0.f, 0.f, 0.f);
+  float yv[4] = {0.f, 0.f, 0.f, 0.f};
+  for (int s0 = 0; s0 < u.splits; s0 += QS) {
+    float4 v[QS];
+#pragma unroll
+    for (int q = 0; q < QS; ++q)
+      v[q] = s0 + q < u.splits ? *(const float4*)(u.y + (s0 + q) * sstride + row + i0) : make_float4(0.f, 0.f, 0.f, 0.f);
+#pragma unroll
+    for (int q = 0; q < QS; ++q) {
+      yv[0] += v[q].x;
+      yv[1] += v[q].y;
+      yv[2] += v[q].z;
+      yv[3] += v[q].w;
+    }
+  }
+  const float sv[4] = {s4.x, s4.y, s4.z, s4.w}, av[4] = {a4.x, a4.y, a4.z, a4.w}, xv[4] = {x4.x, x4.y, x4.z, x4.w};
+  float acc[NS] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+  for (int e = 0; e < 4; ++e) {
+    const float bs = (1.f - av[e]) * sv[e], ay = av[e] * yv[e];
+    acc[0] += yv[e] * yv[e];
+    acc[1] += bs * bs;
+    acc[2] += bs * ay;
+    acc[3] += ay * ay;
+    acc[4] += bs * xv[e];
+    acc[5] += ay * xv[e];
+    acc[6] += xv[e] * xv[e];
+  }
+#pragma unroll
+  for (int q = 0; q < NS; ++q) acc[q] = wave_sum(acc[q]);
+  if ((threadIdx.x & (WAVE - 1)) == 0)
+#pragma unroll
+    for (int q = 0; q < NS; ++q) red[threadIdx.x / WAVE][q] = acc[q];
+  __syncthreads();
+  float tot[NS];
+#pragma unroll
+  for (int q = 0; q < NS; ++q) {
+    tot[q] = 0.f;
+    for (int w = 0; w < NW; ++w) tot[q] += red[w][q];
+  }
+  const float ny = inv_norm(tot[0]);
+  const float tt = fmaxf(tot[1] + 2.f * tot[2] * ny + tot[3] * ny * ny, 0.f);
+  const float nt = inv_norm(tt);
+  float scale = nt, norm_sp = sqrtf(tt) * nt, add_x = 0.f;
+  if (bnd == BND_LOOP_CONTINUE || bnd == BND_LOOP_FINAL) {
+    const float n2 = inv_norm(norm_sp * norm_sp);
+    scale *= n2;
+    norm_sp *= n2;
+  }
+  float t[4], v[4];
+#pragma unroll
+  for (int e = 0; e < 4; ++e) t[e] = (1.f - av[e]) * sv[e] + av[e] * yv[e] * ny;
+  if (bnd == BND_LOOP_CONTINUE) {
+    const float dot = (tot[4] + tot[5] * ny) * scale;
+    const float n3 = inv_norm(norm_sp * norm_sp + 2.f * dot + tot[6]);
+    scale *= n3;
+    add_x = n3;
+  } else if (bnd == BND_SAVE_X) {
+    const float n3 = inv_norm(4.f * norm_sp * norm_sp);
+    *(float4*)(u.x + row + i0) = make_float4(t[0] * nt, t[1] * nt, t[2] * nt, t[3] * nt);
+    scale *= 2.f * n3;
+  }
+#pragma unroll
+  for (int e = 0; e < 4; ++e) v[e] = t[e] * scale + add_x * xv[e];
+  *(float4*)(u.s_out + row + i0) = make_float4(v[0], v[1], v[2], v[3]);
+  if (u.sb) {
+    if constexpr (sizeof(SB) == 2)
+      *(uint2*)((bf16_t*)u.sb + row + i0) = make_uint2(pack_bf16x2(v[0], v[1]), pack_bf16x2(v[2], v[3]));
+    else
+      *(float4*)((float*)u.sb + row + i0) = make_float4(v[0], v[1], v[2], v[3]);
+  }
+}
+
 // Prefill form (y one bf16 array, H % 8 == 0, H <= 8 T): each thread owns 8 consecutive
 // channels of the row, so every access is 16 or 32 bytes wide; same sums and algebra.
 // With state_act the state between sublayers is the bf16 GEMM operand itself, read from
@@ -437,6 +524,11 @@ hipError_t launch_update(const UpdateArgs& u, hipStream_t st) {
       else if (per <= 512) hipLaunchKernelGGL((k_update_vec<bf16_t, 512>), dim3(u.M), dim3(512), 0, st, u);
       else hipLaunchKernelGGL((k_update_vec<bf16_t, 1024>), dim3(u.M), dim3(1024), 0, st, u);
     }
+    return hipGetLastError();
+  }
+  if (few && !u.y_bf16 && u.H % 256 == 0 && u.H <= 4096) {
+    if (u.act == ACT_F32) hipLaunchKernelGGL(k_update_split4<float>, dim3(u.M), dim3(u.H / 4), 0, st, u);
+    else hipLaunchKernelGGL(k_update_split4<bf16_t>, dim3(u.M), dim3(u.H / 4), 0, st, u);
     return hipGetLastError();
   }
   if (u.act == ACT_F32) {

@@ -865,6 +865,7 @@ int step(dory_ctx* ctx, hipStream_t st, int n, const int32_t* ids, const int32_t
   if (!bound(ctx)) return ctx->fail(DORY_ERR_STATE, "weights, KV pool and workspace must be bound");
   if (n < 1 || !ids || (!decode && !n_new) || !x_in || !y_out)
     return ctx->fail(DORY_ERR_INVALID_ARG, "null argument or n_seqs < 1");
+  if (((uintptr_t)x_in | (uintptr_t)y_out) & 15) return ctx->fail(DORY_ERR_INVALID_ARG, "x_in and y_out must be 16-byte aligned");
   std::set<int32_t> seen;
   int64_t rows = 0;
   int n_newseq = 0;
@@ -1196,6 +1197,8 @@ int dory_bind_weights(dory_ctx* ctx, int layer, const dory_layer_weights* w) {
   const uintptr_t mask = 15;
   if (((uintptr_t)w->w_qkvg | (uintptr_t)w->w_o | (uintptr_t)w->w_gu | (uintptr_t)w->w_down) & mask)
     return ctx->fail(DORY_ERR_INVALID_ARG, "weight matrices must be 16-byte aligned");
+  if (((uintptr_t)w->alpha_attn | (uintptr_t)w->alpha_mlp) & mask)
+    return ctx->fail(DORY_ERR_INVALID_ARG, "alpha_attn and alpha_mlp must be 16-byte aligned");
   if ((w->f_qkvg || w->f_o || w->f_gu || w->f_down) && ctx->cfg.weight_format != DORY_WFMT_BF16)
     return ctx->fail(DORY_ERR_INVALID_ARG, "fragment-order copies are for bf16 weights");
   if (((uintptr_t)w->f_qkvg | (uintptr_t)w->f_o | (uintptr_t)w->f_gu | (uintptr_t)w->f_down) & mask)

@@ -96,3 +96,30 @@ def test_calls_on_different_streams_are_ordered():
         assert torch.equal(p, q), f"call {i}"
     a.close()
     b.close()
+
+
+def test_misaligned_states_are_refused_before_any_work():
+    """x_in and y_out must be 16-byte aligned: a call with either off by one float fails
+    with DORY_ERR_INVALID_ARG and leaves the context as it was."""
+    w = gpu_weights(S, 5)
+    rt = DoryRuntime(S, w, max_loops=2, max_seqs=2, max_seq_len=256, max_rows=64, mode="per_loop", loops=2)
+    rt.prefill([0], [20], xin(20, 1))
+    torch.cuda.synchronize()
+    before = state(rt, [0, 1])
+    H = S["hidden"]
+    xbuf = torch.empty(8 * H + 1, dtype=torch.float32, device="cuda")
+    ybuf = torch.empty(8 * H + 1, dtype=torch.float32, device="cuda")
+    x_ok, x_off = xbuf[:8 * H].view(8, H), xbuf[1:].view(8, H)
+    x_ok.copy_(xin(8, 2))
+    x_off.copy_(xin(8, 2))
+    y_ok, y_off = ybuf[:8 * H].view(8, H), ybuf[1:].view(8, H)
+    for x, y in ((x_off, y_ok), (x_ok, y_off)):
+        with pytest.raises(D.DoryError) as e:
+            rt.prefill([1], [8], x, y)
+        assert e.value.code == D.ERR_INVALID_ARG
+        with pytest.raises(D.DoryError) as e:
+            rt.decode([0], x[:1], y[:1])
+        assert e.value.code == D.ERR_INVALID_ARG
+    torch.cuda.synchronize()
+    assert state(rt, [0, 1]) == before
+    rt.close()
