@@ -34,9 +34,13 @@ __device__ __forceinline__ KV* kv_vblock(KV* page, const KVLayout& kv, int head)
 }
 
 // grid (M rows, head groups + 1): block y < n_hb rotates heads 4y .. 4y+3 (one per wave,
-// queries then keys); the last block copies v to the cache.
+// queries then keys); the last block copies v to the cache. A lane takes up to 4 input
+// columns (channels lane and lane + 64 of both halves, or up to 4 v columns) and requests
+// every split partial of all of them before summing any (each column's sum in split
+// order), so the partial sums cost one round trip to memory instead of one per column.
 template <typename OUT>
 __global__ __launch_bounds__(256) void k_rope_kv(RopeArgs a) {
+  constexpr int NC = 4;  // input columns per lane
   const int m = blockIdx.x;
   const int lane = threadIdx.x & (WAVE - 1);
   const int wave = threadIdx.x / WAVE;
@@ -45,11 +49,32 @@ __global__ __launch_bounds__(256) void k_rope_kv(RopeArgs a) {
   const int seq = a.row_seq[m];
   const size_t rowoff = (size_t)m * a.Nqkvg;
   const size_t split_stride = (size_t)a.M * a.Nqkvg;
-  auto in = [&](int col) -> float {
-    if (a.in_f32) {
-      return sum_splits((const float*)a.qkvg + rowoff + col, split_stride, a.splits);
+  // x[c] = input column col[c] (summed over the splits) where ok[c]
+  auto gather = [&](const int (&col)[NC], const bool (&ok)[NC], float (&x)[NC]) {
+#pragma unroll
+    for (int c = 0; c < NC; ++c) x[c] = 0.f;
+    if (!a.in_f32) {
+#pragma unroll
+      for (int c = 0; c < NC; ++c)
+        if (ok[c]) x[c] = bf2f(((const bf16_t*)a.qkvg)[rowoff + col[c]]);
+      return;
     }
-    return bf2f(((const bf16_t*)a.qkvg)[rowoff + col]);
+    const float* base = (const float*)a.qkvg + rowoff;
+    // the split offsets in vector registers: eight scalar 64-bit bases would not fit
+    size_t sstr = split_stride;
+    asm volatile("" : "+v"(sstr));
+    for (int s0 = 0; s0 < a.splits; s0 += 8) {
+      float v[8][NC];
+#pragma unroll
+      for (int q = 0; q < 8; ++q)
+#pragma unroll
+        for (int c = 0; c < NC; ++c)
+          v[q][c] = (s0 + q < a.splits && ok[c]) ? base[(size_t)(s0 + q) * sstr + col[c]] : 0.f;
+#pragma unroll
+      for (int q = 0; q < 8; ++q)
+#pragma unroll
+        for (int c = 0; c < NC; ++c) x[c] += v[q][c];
+    }
   };
   const int n_heads = a.Hq + a.Hkv;
   const int n_hb = (n_heads + 3) / 4;
@@ -58,6 +83,12 @@ __global__ __launch_bounds__(256) void k_rope_kv(RopeArgs a) {
     if (h >= n_heads) return;
     const bool is_q = h < a.Hq;
     const int col0 = is_q ? h * d : a.Hq * d + (h - a.Hq) * d;
+    // columns: (i, i + half) for i = lane and lane + 64
+    const int col[NC] = {col0 + lane, col0 + lane + half, col0 + lane + WAVE, col0 + lane + WAVE + half};
+    const bool ok[NC] = {lane < half, lane < half, lane + WAVE < half, lane + WAVE < half};
+    float x[NC];
+    gather(col, ok, x);
+    OUT* kb = is_q ? nullptr : kv_kblock(kv_page<OUT>(a.kv, seq, a.stream_idx, p), a.kv, h - a.Hq);
     float r[4];
     float sq = 0.f;
 #pragma unroll
@@ -69,7 +100,7 @@ __global__ __launch_bounds__(256) void k_rope_kv(RopeArgs a) {
         ang -= 6.283185307179586 * rint(ang * 0.15915494309189535);
         float sn, cs;
         sincosf((float)ang, &sn, &cs);
-        const float x1 = in(col0 + i), x2 = in(col0 + i + half);
+        const float x1 = x[2 * j], x2 = x[2 * j + 1];
         r[2 * j] = x1 * cs - x2 * sn;
         r[2 * j + 1] = x1 * sn + x2 * cs;
         sq += r[2 * j] * r[2 * j] + r[2 * j + 1] * r[2 * j + 1];
@@ -94,7 +125,6 @@ __global__ __launch_bounds__(256) void k_rope_kv(RopeArgs a) {
         st<OUT>(qo, o + i, v1);
         st<OUT>(qo, o + i + half, v2);
       } else {
-        OUT* kb = kv_kblock(kv_page<OUT>(a.kv, seq, a.stream_idx, p), a.kv, h - a.Hq);
         st<OUT>(kb, kv_k_off(p % PAGE, i, d), v1);
         st<OUT>(kb, kv_k_off(p % PAGE, i + half, d), v2);
       }
@@ -104,9 +134,24 @@ __global__ __launch_bounds__(256) void k_rope_kv(RopeArgs a) {
   // v -> V page (unrotated); the gate stays in the projection output
   const int vcol0 = a.Hq * d + a.Hkv * d;
   OUT* pgp = kv_page<OUT>(a.kv, seq, a.stream_idx, p);
-  for (int c = threadIdx.x; c < a.Hkv * d; c += blockDim.x) {
-    const int hk = c / d, j = c % d;
-    st<OUT>(kv_vblock(pgp, a.kv, hk), kv_v_off(p % PAGE, j, d), in(vcol0 + c));
+  const int nv = a.Hkv * d;
+  for (int c0 = threadIdx.x; c0 < nv; c0 += NC * blockDim.x) {
+    int col[NC];
+    bool ok[NC];
+#pragma unroll
+    for (int c = 0; c < NC; ++c) {
+      ok[c] = c0 + c * (int)blockDim.x < nv;
+      col[c] = vcol0 + c0 + c * blockDim.x;
+    }
+    float x[NC];
+    gather(col, ok, x);
+#pragma unroll
+    for (int c = 0; c < NC; ++c) {
+      if (!ok[c]) continue;
+      const int cc = c0 + c * blockDim.x;
+      const int hk = cc / d, jj = cc % d;
+      st<OUT>(kv_vblock(pgp, a.kv, hk), kv_v_off(p % PAGE, jj, d), x[c]);
+    }
   }
 }
 
