@@ -21,6 +21,23 @@
 
 namespace dory {
 
+// 8 fp16 values (one 16-byte chunk) <-> floats; the stores round to nearest even
+__device__ __forceinline__ void f16x8_to_f32(const uint4& w, float* out) {
+  typedef _Float16 h2 __attribute__((ext_vector_type(2)));
+  const uint32_t ws[4] = {w.x, w.y, w.z, w.w};
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const h2 h = __builtin_bit_cast(h2, ws[i]);
+    out[2 * i] = (float)h[0];
+    out[2 * i + 1] = (float)h[1];
+  }
+}
+__device__ __forceinline__ uint32_t pack_f16x2(float a, float b) {
+  typedef _Float16 h2 __attribute__((ext_vector_type(2)));
+  const h2 h = {(_Float16)a, (_Float16)b};
+  return __builtin_bit_cast(uint32_t, h);
+}
+
 // THREADS per row: 512 for many rows, 1024 for few rows (decode) so that each row's
 // loads are spread over more waves.
 template <typename SB, int UPD_THREADS>
@@ -219,9 +236,9 @@ __global__ __launch_bounds__(1024) void k_update_split4(UpdateArgs u) {
 
 // Prefill form (y one bf16 array, H % 8 == 0, H <= 8 T): each thread owns 8 consecutive
 // channels of the row, so every access is 16 or 32 bytes wide; same sums and algebra.
-// With state_act the state between sublayers is the bf16 GEMM operand itself, read from
-// sb and rewritten in place (each thread rewrites only the channels it read), so an
-// update moves y, s and the new s in bf16: 6 bytes per element instead of 14.
+// With state_act the state between sublayers is kept in fp16 (s16, rewritten in place:
+// each thread rewrites only the channels it read) beside its bf16 GEMM copy, so an update
+// moves y, s, the new s and its copy at 2 bytes each: 8 bytes per element instead of 14.
 template <typename SB, int T>
 __global__ __launch_bounds__(T) void k_update_vec(UpdateArgs u) {
   constexpr int NW = T / WAVE;
@@ -242,11 +259,8 @@ __global__ __launch_bounds__(T) void k_update_vec(UpdateArgs u) {
     const uint32_t yw[4] = {yr.x, yr.y, yr.z, yr.w};
 #pragma unroll
     for (int e = 0; e < 8; ++e) yv[e] = __uint_as_float((e & 1) ? (yw[e / 2] & 0xFFFF0000u) : (yw[e / 2] << 16));
-    if (u.state_act) {  // bf16 state: 8 channels in one 16-byte load
-      const uint4 sr = *(const uint4*)((const bf16_t*)u.sb + row + i0);
-      const uint32_t sw[4] = {sr.x, sr.y, sr.z, sr.w};
-#pragma unroll
-      for (int e = 0; e < 8; ++e) sv[e] = __uint_as_float((e & 1) ? (sw[e / 2] & 0xFFFF0000u) : (sw[e / 2] << 16));
+    if (u.state_act) {  // fp16 state: 8 channels in one 16-byte load
+      f16x8_to_f32(*(const uint4*)((const uint16_t*)u.s16 + row + i0), sv);
     } else {
       const float4 s0 = *(const float4*)(u.s + row + i0), s1 = *(const float4*)(u.s + row + i0 + 4);
       sv[0] = s0.x; sv[1] = s0.y; sv[2] = s0.z; sv[3] = s0.w; sv[4] = s1.x; sv[5] = s1.y; sv[6] = s1.z; sv[7] = s1.w;
@@ -315,6 +329,9 @@ __global__ __launch_bounds__(T) void k_update_vec(UpdateArgs u) {
     *(float4*)(u.s_out + row + i0) = make_float4(v[0], v[1], v[2], v[3]);
     *(float4*)(u.s_out + row + i0 + 4) = make_float4(v[4], v[5], v[6], v[7]);
   }
+  if (u.state_act)
+    *(uint4*)((uint16_t*)u.s16 + row + i0) =
+        make_uint4(pack_f16x2(v[0], v[1]), pack_f16x2(v[2], v[3]), pack_f16x2(v[4], v[5]), pack_f16x2(v[6], v[7]));
   if (u.sb) {
     if constexpr (sizeof(SB) == 2) {
       *(uint4*)((bf16_t*)u.sb + row + i0) =
@@ -326,12 +343,12 @@ __global__ __launch_bounds__(T) void k_update_vec(UpdateArgs u) {
   }
 }
 
-// Prefill form with the bf16 state (state_act, H = 512 NC): one wave per row, lane l
+// Prefill form with the fp16 state (state_act, H = 512 NC): one wave per row, lane l
 // holding channels 512 c + 8 l .. + 7 (c < NC) of y, s and the rates, so each load
 // instruction of a wave reads one contiguous KiB. Four rows per work-group and no LDS or
 // barrier: every row of the launch has its loads in flight in one round, and the 7 row
-// sums are wave reductions only. y and s stay packed in registers and are widened where
-// they are used.
+// sums are wave reductions only. y (bf16) and s (fp16) stay packed in registers and are
+// widened where they are used; the new state goes out as fp16 and as the bf16 GEMM copy.
 template <int NC>
 __global__ __launch_bounds__(256) void k_update_wave(UpdateArgs u) {
   constexpr int NS = 7;
@@ -342,7 +359,7 @@ __global__ __launch_bounds__(256) void k_update_wave(UpdateArgs u) {
   const int bnd = u.bnd == BND_LOOP_CONTINUE && m >= u.final_from ? BND_LOOP_FINAL : u.bnd;
   const bool need_x = bnd == BND_LOOP_CONTINUE;
   const bf16_t* Y = (const bf16_t*)u.y + row;
-  bf16_t* S = (bf16_t*)u.sb + row;
+  const uint16_t* S = (const uint16_t*)u.s16 + row;
   uint4 yr[NC], sr[NC];
   float av[NC][8];
 #pragma unroll
@@ -358,16 +375,20 @@ __global__ __launch_bounds__(256) void k_update_wave(UpdateArgs u) {
     av[c][0] = a0.x; av[c][1] = a0.y; av[c][2] = a0.z; av[c][3] = a0.w;
     av[c][4] = a1.x; av[c][5] = a1.y; av[c][6] = a1.z; av[c][7] = a1.w;
   }
-  auto widen = [](const uint4& w, int e) -> float {
+  auto widen = [](const uint4& w, int e) -> float {  // bf16 element e
     const uint32_t x = e < 2 ? w.x : e < 4 ? w.y : e < 6 ? w.z : w.w;
     return __uint_as_float((e & 1) ? (x & 0xFFFF0000u) : (x << 16));
+  };
+  auto widen_h = [](const uint4& w, int e) -> float {  // fp16 element e
+    const uint32_t x = e < 2 ? w.x : e < 4 ? w.y : e < 6 ? w.z : w.w;
+    return (float)__builtin_bit_cast(_Float16, (uint16_t)((e & 1) ? x >> 16 : x & 0xFFFFu));
   };
   float acc[NS] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
 #pragma unroll
   for (int c = 0; c < NC; ++c)
 #pragma unroll
     for (int e = 0; e < 8; ++e) {
-      const float y = widen(yr[c], e), bs = (1.f - av[c][e]) * widen(sr[c], e), ay = av[c][e] * y;
+      const float y = widen(yr[c], e), bs = (1.f - av[c][e]) * widen_h(sr[c], e), ay = av[c][e] * y;
       acc[0] += y * y;
       acc[1] += bs * bs;
       acc[2] += bs * ay;
@@ -381,7 +402,7 @@ __global__ __launch_bounds__(256) void k_update_wave(UpdateArgs u) {
       const float xs[8] = {x0.x, x0.y, x0.z, x0.w, x1.x, x1.y, x1.z, x1.w};
 #pragma unroll
       for (int e = 0; e < 8; ++e) {
-        const float bs = (1.f - av[c][e]) * widen(sr[c], e), ay = av[c][e] * widen(yr[c], e);
+        const float bs = (1.f - av[c][e]) * widen_h(sr[c], e), ay = av[c][e] * widen(yr[c], e);
         acc[4] += bs * xs[e];
         acc[5] += ay * xs[e];
         acc[6] += xs[e] * xs[e];
@@ -418,7 +439,7 @@ __global__ __launch_bounds__(256) void k_update_wave(UpdateArgs u) {
     float t[8], v[8];
 #pragma unroll
     for (int e = 0; e < 8; ++e) {
-      t[e] = (1.f - av[c][e]) * widen(sr[c], e) + av[c][e] * widen(yr[c], e) * ny;
+      t[e] = (1.f - av[c][e]) * widen_h(sr[c], e) + av[c][e] * widen(yr[c], e) * ny;
       v[e] = t[e] * scale + add_x * xs[e];
     }
     if (bnd == BND_SAVE_X) {
@@ -427,6 +448,8 @@ __global__ __launch_bounds__(256) void k_update_wave(UpdateArgs u) {
     }
     *(uint4*)((bf16_t*)u.sb + i) =
         make_uint4(pack_bf16x2(v[0], v[1]), pack_bf16x2(v[2], v[3]), pack_bf16x2(v[4], v[5]), pack_bf16x2(v[6], v[7]));
+    *(uint4*)((uint16_t*)u.s16 + i) =
+        make_uint4(pack_f16x2(v[0], v[1]), pack_f16x2(v[2], v[3]), pack_f16x2(v[4], v[5]), pack_f16x2(v[6], v[7]));
     if (u.s_out) {
       *(float4*)(u.s_out + i) = make_float4(v[0], v[1], v[2], v[3]);
       *(float4*)(u.s_out + i + 4) = make_float4(v[4], v[5], v[6], v[7]);
@@ -436,12 +459,13 @@ __global__ __launch_bounds__(256) void k_update_wave(UpdateArgs u) {
 
 template <typename SB>
 __global__ __launch_bounds__(256) void k_stage_input(const float* x, float* s, SB* sb, size_t n, const int32_t* rows,
-                                                     int H) {
+                                                     int H, _Float16* s16) {
   for (size_t i = blockIdx.x * (size_t)blockDim.x + threadIdx.x; i < n;
        i += (size_t)gridDim.x * blockDim.x) {
     const size_t src = rows ? (size_t)rows[i / H] * H + i % H : i;
     const float v = x[src];
     if (s) s[i] = v;
+    if (s16) s16[i] = (_Float16)v;
     st<SB>(sb, i, v);
   }
 }
@@ -498,7 +522,7 @@ hipError_t launch_update(const UpdateArgs& u, hipStream_t st) {
   if (u.M == 0) return hipSuccess;
   const bool few = u.M < 512;
   const bool vec = !few && u.y_bf16 && u.splits == 1 && u.H % 8 == 0 && u.H <= 8 * 1024;
-  if (u.state_act && (!vec || u.act != ACT_BF16 || !u.sb)) return hipErrorInvalidValue;
+  if (u.state_act && (!vec || u.act != ACT_BF16 || !u.sb || !u.s16)) return hipErrorInvalidValue;
   if (u.state_act && u.H % 512 == 0 && u.H / 512 <= 8) {
     const dim3 grid((u.M + 3) / 4);
     switch (u.H / 512) {
@@ -542,14 +566,16 @@ hipError_t launch_update(const UpdateArgs& u, hipStream_t st) {
 }
 
 hipError_t launch_stage_input(const float* x_in, float* s, void* sb, int M, int H, int act,
-                              hipStream_t st, const int32_t* rows) {
+                              hipStream_t st, const int32_t* rows, void* s16) {
   const size_t n = (size_t)M * H;
   if (n == 0) return hipSuccess;
   const int blocks = (int)((n + 255) / 256 < 4096 ? (n + 255) / 256 : 4096);
   if (act == ACT_F32)
-    hipLaunchKernelGGL(k_stage_input<float>, dim3(blocks), dim3(256), 0, st, x_in, s, (float*)sb, n, rows, H);
+    hipLaunchKernelGGL(k_stage_input<float>, dim3(blocks), dim3(256), 0, st, x_in, s, (float*)sb, n, rows, H,
+                       (_Float16*)s16);
   else
-    hipLaunchKernelGGL(k_stage_input<bf16_t>, dim3(blocks), dim3(256), 0, st, x_in, s, (bf16_t*)sb, n, rows, H);
+    hipLaunchKernelGGL(k_stage_input<bf16_t>, dim3(blocks), dim3(256), 0, st, x_in, s, (bf16_t*)sb, n, rows, H,
+                       (_Float16*)s16);
   return hipGetLastError();
 }
 

@@ -72,14 +72,17 @@ struct UpdateArgs {
   int bnd = BND_NONE;
   int final_from = 0x7fffffff;  // with BND_LOOP_CONTINUE: rows >= this one end their last
                                 // loop here and take BND_LOOP_FINAL (mixed loop counts)
-  int state_act = 0;  // the state lives only in sb (bf16, read and rewritten in place); s is
-                      // not read, and s_out, when set, receives a float copy of the new
-                      // state (prefill form only: y_bf16, >= 512 rows, act bf16)
+  int state_act = 0;  // the state lives in s16 (fp16, read and rewritten in place) beside
+                      // its bf16 copy sb; s is not read, and s_out, when set, receives a
+                      // float copy of the new state (prefill form only: y_bf16, >= 512
+                      // rows, act bf16)
+  void* s16 = nullptr;  // [M, H] fp16 state (state_act)
 };
 hipError_t launch_update(const UpdateArgs& u, hipStream_t st);
-// s = x_in; sb = act(x_in); with rows != NULL row r of s is row rows[r] of x_in
+// s = x_in; sb = act(x_in); s16 = fp16(x_in) when set; with rows != NULL row r of s is
+// row rows[r] of x_in; s may be null
 hipError_t launch_stage_input(const float* x_in, float* s, void* sb, int M, int H, int act,
-                              hipStream_t st, const int32_t* rows = nullptr);
+                              hipStream_t st, const int32_t* rows = nullptr, void* s16 = nullptr);
 // y[rows[r]] = s[r] for r < M (float rows of H)
 hipError_t launch_scatter_rows(const float* s, const int32_t* rows, int M, int H, float* y, hipStream_t st);
 // x = x_in, s = N(s1_in + x_in) (and its act copy sb) per row, from the caller's rows

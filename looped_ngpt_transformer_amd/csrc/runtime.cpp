@@ -29,7 +29,7 @@ namespace {
 
 constexpr int NSTAGE = 4;          // pinned staging buffers in rotation
 constexpr int DELTA_CAP = 65536;   // page-table updates per upload
-constexpr int ACT_STATE_MIN_ROWS = 512;  // rows from which a prefill keeps its state in bf16 only
+constexpr int ACT_STATE_MIN_ROWS = 512;  // rows from which a prefill keeps its state in fp16
 constexpr int SKINNY_M = 256;      // rows up to which projections use split-K tiles
 constexpr size_t ALIGN = 256;
 constexpr int ROPE_INTS = 2 * 128 * 2;  // two tables of up to 128 doubles
@@ -48,7 +48,7 @@ struct Dims {
 };
 
 struct WsLayout {
-  size_t table, meta, s, x, sb, qkvg, q, o, h, part, apart, wexp, rcs, total;
+  size_t table, meta, s, x, sb, s16, qkvg, q, o, h, part, apart, wexp, rcs, total;
   size_t part_floats, apart_floats;
   size_t meta_ints;
 };
@@ -96,6 +96,7 @@ WsLayout layout_of(const dory_config& c, const Dims& D) {
   W.s = take(R * D.H * 4);
   W.x = take(R * D.H * 4);
   W.sb = take(R * D.H * D.esz);
+  W.s16 = take(c.act_dtype == DORY_DTYPE_BF16 ? R * D.H * 2 : 0);  // fp16 state of long prefills
   W.qkvg = take(R * D.Nqkvg * D.esz);
   W.q = take(R * D.Nq * D.esz);
   W.o = take(R * D.Nq * D.esz);
@@ -476,8 +477,8 @@ struct CallPlan {
   bool skip_out = false;
   const float* res_x = nullptr;
   const float* res_s1 = nullptr;
-  // the state between sublayers is kept only as the bf16 GEMM operand (every layer call
-  // of the call takes the vectorised prefill update); the last layer writes a float copy
+  // the state between sublayers is kept in fp16 beside its bf16 GEMM copy (every layer
+  // call of the call takes the vectorised prefill update); the last layer writes floats
   bool act_state = false;
 };
 
@@ -588,6 +589,7 @@ int run_layer(dory_ctx* ctx, hipStream_t st, const CallPlan& P, int l, int slot,
     u.s = s;
     u.s_out = sout ? sout : P.act_state ? nullptr : s;
     u.state_act = P.act_state;
+    u.s16 = ws + W.s16;
     u.sb = ws + W.sb;
     u.x = (float*)(ws + W.x);
     u.alpha = alpha;
@@ -598,7 +600,7 @@ int run_layer(dory_ctx* ctx, hipStream_t st, const CallPlan& P, int l, int slot,
     u.final_from = final_from;
     Prof pr(ctx, st, DORY_KC_UPDATE);
     const hipError_t e = launch_update(u, st);
-    const double sbytes = P.act_state ? 2.0 * D.esz + (sout ? 4 : 0) : 4 + 4 + D.esz;
+    const double sbytes = P.act_state ? 4.0 + D.esz + (sout ? 4 : 0) : 4 + 4 + D.esz;
     pr.end(0, (double)M * D.H * ((ybf ? 2.0 : 4.0 * splits) + sbytes));
     return e;
   };
@@ -794,9 +796,9 @@ int run_forward(dory_ctx* ctx, hipStream_t st, const CallPlan& P, const float* x
     {
       Prof pr(ctx, st, DORY_KC_UPDATE);
       HIPCHK(launch_stage_input(x_in, P.act_state ? nullptr : (float*)(ws + ctx->W.s), ws + ctx->W.sb, P.M, H, act,
-                                st, rowmap),
+                                st, rowmap, P.act_state ? ws + ctx->W.s16 : nullptr),
              "stage_input");
-      pr.end(0, (double)P.M * H * ((P.act_state ? 4.0 : 8.0) + ctx->D.esz));
+      pr.end(0, (double)P.M * H * ((P.act_state ? 6.0 : 8.0) + ctx->D.esz));
     }
     for (int l = 0; l < c.n_in; ++l) {
       if ((r = injected()) || (r = run_layer(ctx, st, P, l, 0, l == c.n_in - 1 ? BND_SAVE_X : BND_NONE, nullptr))) return r;
@@ -1001,7 +1003,7 @@ int step(dory_ctx* ctx, hipStream_t st, int n, const int32_t* ids, const int32_t
     }
   }
   P.M = row;
-  {  // bf16 state when every layer call of this call takes the vectorised prefill update
+  {  // fp16 state when every layer call of this call takes the vectorised prefill update
     int min_rows = P.M;
     for (int t = 1; t <= P.k_max; ++t) min_rows = std::min(min_rows, P.loop_rows[t]);
     P.act_state = c.act_dtype != DORY_DTYPE_F32 && min_rows >= ACT_STATE_MIN_ROWS && !P.cap_x && !P.cap_s1 &&

@@ -16,7 +16,7 @@ hipError_t launch_gemm(const GemmArgs&, hipStream_t) { return g_stub_launch; }
 hipError_t launch_arrange_frag(const void*, int64_t, int64_t, void*, hipStream_t) { return g_stub_launch; }
 hipError_t launch_mfma_rate(int, int, long long*, float*, hipStream_t) { return g_stub_launch; }
 hipError_t launch_update(const UpdateArgs&, hipStream_t) { return g_stub_launch; }
-hipError_t launch_stage_input(const float*, float*, void*, int, int, int, hipStream_t, const int32_t*) {
+hipError_t launch_stage_input(const float*, float*, void*, int, int, int, hipStream_t, const int32_t*, void*) {
   return g_stub_launch;
 }
 hipError_t launch_scatter_rows(const float*, const int32_t*, int, int, float*, hipStream_t) { return g_stub_launch; }
