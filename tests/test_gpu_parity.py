@@ -120,7 +120,7 @@ def test_bf16_attention_running_maximum(variant):
 @pytest.mark.parametrize("mode", ["per_loop", "last_loop"])
 def test_bf16_long_prefill(mode):
     """A 600-row prefill: the update of long prefills (>= 512 rows: one wave per row, the
-    state between sublayers kept in bf16 only; every loop boundary occurs in it at k = 2),
+    state between sublayers kept in fp16; every loop boundary occurs in it at k = 2),
     256-row GEMM tiles with a ragged tail, then a decode step."""
     S = PSMALL
     sched = [("prefill", [(0, xin(S, 600, 61))]),
@@ -366,7 +366,7 @@ def test_long_mixed_loop_chunks_state_forms(mode):
     """Long prefill chunks of sequences at k = 1 and k = 2 in one call (caller order
     [k = 1, k = 2], so the rows are reordered by k inside the call). First call: 520 rows
     still loop in loop 2, so every layer call has >= 512 rows and the state between
-    sublayers is kept in bf16 only, with the last layer writing the float rows that the
+    sublayers is kept in fp16, with the last layer writing the float rows that the
     row scatter reads. Second call: 300 rows loop in loop 2, so the call keeps the float
     state (the vectorised update on 600 rows, the per-row one on 300). Each sequence
     equals the oracle at its own k."""
