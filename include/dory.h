@@ -33,6 +33,12 @@
  *    tables are shared), so consecutive calls never overlap on the device.
  *  - Matrices are row-major. A weight W is [N_out, K_in] and a projection is
  *    y = s W^T.
+ *  - Tracing: with DORY_TRACE=1 in the environment, dory_prefill and dory_decode_step
+ *    open one marker range per call, nested ranges for the input block, each loop and
+ *    the output block, and one range per layer call inside those (rocprofv3
+ *    --marker-trace records them). The marker library (librocprofiler-sdk-roctx.so.1,
+ *    or the file DORY_TRACE_LIB names) is opened on the first traced call; if it
+ *    cannot be opened, calls run untraced.
  */
 #ifndef DORY_H
 #define DORY_H

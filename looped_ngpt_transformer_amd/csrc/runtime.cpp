@@ -8,12 +8,14 @@
 // s_t = N(.) and u_{t+1} = N(s_t + x); the output block once (slot 0).
 // KV slots (arXiv §6.1): per_loop keeps k slots per recurrent attention layer,
 // last_loop one slot that every loop overwrites.
+#include <dlfcn.h>
 #include <hip/hip_runtime.h>
 
 #include <algorithm>
 #include <cmath>
 #include <cstdarg>
 #include <cstdio>
+#include <cstdlib>
 #include <cstring>
 #include <map>
 #include <set>
@@ -228,6 +230,47 @@ int prof_event(dory_ctx* ctx, hipStream_t st) {
   if (hipEventRecord(ctx->pev[i], st) != hipSuccess) return -1;
   return i;
 }
+
+// Optional marker ranges (DORY_TRACE=1 in the environment): one range per boundary
+// call, per block of the schedule (input block, each loop, output block) and per layer
+// call, named after what they cover; rocprofv3 --marker-trace shows them beside the
+// kernels. The marker library (librocprofiler-sdk-roctx, or the one DORY_TRACE_LIB
+// names) is opened on the first traced call, so the library does not link against it
+// and an untraced call costs one environment lookup per range.
+struct TraceApi {
+  int (*push)(const char*);
+  int (*pop)();
+};
+const TraceApi* trace_api() {
+  static const TraceApi* api = []() -> const TraceApi* {
+    const char* lib = std::getenv("DORY_TRACE_LIB");
+    void* h = dlopen(lib && *lib ? lib : "librocprofiler-sdk-roctx.so.1", RTLD_NOW | RTLD_LOCAL);
+    if (!h) return nullptr;
+    static TraceApi a;
+    a.push = (int (*)(const char*))dlsym(h, "roctxRangePushA");
+    a.pop = (int (*)())dlsym(h, "roctxRangePop");
+    return a.push && a.pop ? &a : nullptr;
+  }();
+  return api;
+}
+struct Trace {
+  const TraceApi* api = nullptr;
+  explicit Trace(const char* fmt, ...) {
+    const char* e = std::getenv("DORY_TRACE");
+    if (!e || !*e || (e[0] == '0' && !e[1]) || !(api = trace_api())) return;
+    char buf[128];
+    va_list ap;
+    va_start(ap, fmt);
+    vsnprintf(buf, sizeof buf, fmt, ap);
+    va_end(ap);
+    api->push(buf);
+  }
+  ~Trace() {
+    if (api) api->pop();
+  }
+  Trace(const Trace&) = delete;
+  Trace& operator=(const Trace&) = delete;
+};
 
 struct Prof {
   dory_ctx* ctx;
@@ -521,6 +564,7 @@ int run_layer(dory_ctx* ctx, hipStream_t st, const CallPlan& P, int l, int slot,
   char* ws = ctx->ws;
   const dory_layer_weights& w = ctx->lw[l];
   const int M = P.M;
+  Trace tr("layer %d, KV slot %d, %d rows", l, slot, M);
   const int act = c.act_dtype == DORY_DTYPE_F32 ? ACT_F32 : ACT_BF16;
   const int wf = c.weight_format == DORY_WFMT_F32   ? W_F32
                  : c.weight_format == DORY_WFMT_BF16 ? W_BF16
@@ -793,6 +837,7 @@ int run_forward(dory_ctx* ctx, hipStream_t st, const CallPlan& P, const float* x
            "resume state");
     pr.end(0, (double)P.M * H * (16.0 + 8.0 + ctx->D.esz));
   } else {
+    Trace tb("input block");
     {
       Prof pr(ctx, st, DORY_KC_UPDATE);
       HIPCHK(launch_stage_input(x_in, P.act_state ? nullptr : (float*)(ws + ctx->W.s), ws + ctx->W.sb, P.M, H, act,
@@ -809,6 +854,7 @@ int run_forward(dory_ctx* ctx, hipStream_t st, const CallPlan& P, const float* x
   // loop t runs the recurrent block on the rows of the sequences with k >= t (a prefix);
   // rows whose sequence ends at loop t take the final boundary there
   for (int t = P.res_x ? 2 : 1; t <= P.k_max; ++t) {
+    Trace tt("loop %d of %d", t, P.k_max);
     CallPlan Pt = P;
     Pt.M = P.loop_rows[t];
     Pt.n_tiles = P.loop_tiles[t];
@@ -828,6 +874,7 @@ int run_forward(dory_ctx* ctx, hipStream_t st, const CallPlan& P, const float* x
     ctx->last_calls = calls;
     return DORY_OK;
   }
+  Trace to("output block");
   const int L = c.n_in + c.n_rec + c.n_out;
   for (int l = c.n_in + c.n_rec; l < L; ++l) {
     // the last layer's update writes the float result: into the caller's array, or into
@@ -855,6 +902,7 @@ int loops_of(const dory_ctx* ctx, const Seq& q) {
 // Shared body of prefill and decode: rows of each sequence, grown by n_new[i].
 int step(dory_ctx* ctx, hipStream_t st, int n, const int32_t* ids, const int32_t* n_new,
          const float* x_in, float* y_out, bool decode) {
+  Trace tc("%s: %d sequences", decode ? "dory_decode_step" : "dory_prefill", n);
   const dory_config& c = ctx->cfg;
   float* const cap_x = ctx->cap_x;  // one-shot: consumed by this call whatever its outcome
   float* const cap_s1 = ctx->cap_s1;
