@@ -140,10 +140,14 @@ __global__ __launch_bounds__(PF_THREADS) void k_attn_prefill(AttnArgs a) {
   const int voff = NG * KGS + (l32 >> 4) * VGS + (lh * 16 + (l32 & 15)) * 16;
   const float sl2 = a.scale * 1.4426950408889634f;  // logits in log2 units
   // With q and k L2-normalised and scaled by s_qk, |q.k| <= max s_qk^2, so no logit
-  // exceeds B = scale * max s_qk^2 (log2 units here, with a margin for the bf16 rounding
-  // of q and k). Softmax is unchanged by the shift, so B serves as a fixed reference in
-  // place of the running maximum whenever the smallest probability, 2^(-2B), stays a
-  // normal number: no maximum, no rescaling of the accumulators.
+  // exceeds B = scale * max s_qk^2 in magnitude (log2 units here, with a margin for the
+  // bf16 rounding of q and k). Softmax is unchanged by a common shift of the logits, and
+  // for B < 60 every 2^logit lies in [2^-60, 2^60], well inside the normal range of
+  // float and bf16, with row sums far from overflow; then the probabilities are taken
+  // as 2^logit directly: no running maximum, no rescaling of the accumulators. In that
+  // case q carries the factor scale * log2(e) (folded into its normalisation), so that
+  // the S^T accumulators already hold log2-unit logits and each probability is one
+  // exponential.
   float bound = INFINITY;
   if (a.s_qk) {
     float m = 0.f;
@@ -153,6 +157,7 @@ __global__ __launch_bounds__(PF_THREADS) void k_attn_prefill(AttnArgs a) {
     bound = sl2 * m * m * 1.02f + 0.5f;
   }
   const bool fixed_ref = sl2 > 0.f && bound < 60.f;  // uniform over the work-group
+  const float qscale = fixed_ref ? sl2 : 1.f;         // factor carried by q
   // m_run: running maximum (log2 units) of the query's visible logits; l_run: this
   // lane's part (its 32 keys of each page) of the softmax denominator, relative to the
   // current reference
@@ -247,7 +252,7 @@ __global__ __launch_bounds__(PF_THREADS) void k_attn_prefill(AttnArgs a) {
       for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
         for (int e = 0; e < 16; ++e) {
-          const float p = __builtin_amdgcn_exp2f(fmaf(st[kb][e], sl2, -bound));  // exp2(-inf) = 0
+          const float p = __builtin_amdgcn_exp2f(st[kb][e]);  // log2 units already; exp2(-inf) = 0
           st[kb][e] = p;
           ps[kb] += p;
         }
@@ -370,7 +375,7 @@ __global__ __launch_bounds__(PF_THREADS) void k_attn_prefill(AttnArgs a) {
         }
       }
       sq += __shfl_xor(sq, 32, 64);
-      const float sc = a.s_qk ? inv_norm(sq) : 1.f;
+      const float sc = (a.s_qk ? inv_norm(sq) : 1.f) * qscale;
 #pragma unroll
       for (int c = 0; c < HS; ++c) {
         uint32_t o1[4], o2[4];
@@ -387,6 +392,13 @@ __global__ __launch_bounds__(PF_THREADS) void k_attn_prefill(AttnArgs a) {
       for (int c = 0; c < KS; ++c) {
         uint4 v = make_uint4(0, 0, 0, 0);
         if (qv) v = *(const uint4*)((const bf16_t*)a.q + (size_t)(row0 + qi) * HqD + (size_t)h * D + 16 * c + 8 * lh);
+        if (fixed_ref) {
+          uint32_t wv[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+          for (int e = 0; e < 4; ++e)
+            wv[e] = pack_bf16x2(__uint_as_float(wv[e] << 16) * qscale, __uint_as_float(wv[e] & 0xFFFF0000u) * qscale);
+          v = make_uint4(wv[0], wv[1], wv[2], wv[3]);
+        }
         qf[c] = __builtin_bit_cast(bf16x8, v);
       }
     }
