@@ -721,7 +721,7 @@ def seed_kv(rt, shape, synth, D, torch, batch, ctx_len, kseq, mode):
 def main():
     args = parse()
     if args.gpus != 1:
-        print(json.dumps({"error": "this build runs on one GPU; --gpus must be 1",
+        print(json.dumps({"error": "the library runs on one GPU; --gpus must be 1",
                           "n_gpus": args.gpus}))
         sys.exit(2)
     import torch

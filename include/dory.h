@@ -55,7 +55,7 @@ extern "C" {
 #define DORY_ERR_INVALID_ARG (-1) /* bad argument: shape, pointer, id, range */
 #define DORY_ERR_STATE (-2)       /* call not allowed in the context's state */
 #define DORY_ERR_OUT_OF_KV (-3)   /* the bound KV pool has too few free pages */
-#define DORY_ERR_UNSUPPORTED (-4) /* valid, but not a shape/format this build runs */
+#define DORY_ERR_UNSUPPORTED (-4) /* valid, but not a shape/format this library runs */
 #define DORY_ERR_HIP (-5)         /* a HIP runtime call failed */
 
 /* ---- element types */

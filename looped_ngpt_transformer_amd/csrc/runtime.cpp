@@ -318,7 +318,7 @@ int check_config(const dory_config* c, std::string& msg) {
   if (c->max_seqs < 1 || c->max_rows < 1) return bad("max_seqs and max_rows must be >= 1");
   if (c->max_seq_len < 1 || c->max_seq_len > DORY_MAX_POSITIONS)
     return bad("max_seq_len must be 1..262144");
-  // what the kernels of this build run
+  // what the kernels of this library run
   const int G = c->n_q_heads / c->n_kv_heads;
   if (G > 4) return uns("more than 4 query heads per KV head");
   if (c->head_dim % 32 || c->head_dim > 256) return uns("head_dim must be a multiple of 32, <= 256 (KV page fragments)");
