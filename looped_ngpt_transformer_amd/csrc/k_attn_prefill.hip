@@ -75,8 +75,24 @@ __global__ __launch_bounds__(PF_THREADS) void k_attn_prefill(AttnArgs a) {
     else return sm2;
   };
 
-  const int tile = a.n_tiles - 1 - blockIdx.x;  // longest (latest) tiles first
-  const int hk = blockIdx.y;
+  // Work-groups go to the 8 XCDs (each with its own L2) round-robin in linear id order.
+  // Each XCD takes the tiles of one KV head (8 / Hkv XCDs per head, interleaved tile by
+  // tile, so that each gets long and short tiles alike), so that the K/V pages the
+  // tiles of a head share are fetched into one or two L2s instead of all eight; the
+  // longest (latest) tiles of each XCD go first. Other shapes keep the plain order.
+  int tile, hk;
+  {
+    const int n = a.n_tiles, nh = gridDim.y, xph = 8 / nh;
+    const int id = blockIdx.x + blockIdx.y * n;
+    if (nh <= 8 && 8 % nh == 0 && n % xph == 0) {  // a bijection of the grid onto (tile, head)
+      const int x = id & 7, j = id >> 3;
+      hk = x / xph;
+      tile = n - 1 - (xph * j + x % xph);
+    } else {
+      tile = n - 1 - blockIdx.x;
+      hk = blockIdx.y;
+    }
+  }
   const int32_t* tl = a.tiles + 4 * tile;
   const int row0 = tl[0], nrows = tl[1], pos0 = tl[2], seq = tl[3];
   const int t = threadIdx.x, lane = t & 63;
