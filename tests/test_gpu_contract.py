@@ -6,7 +6,8 @@
   or a layer call), so no device work fails. Afterwards the context computes exactly what
   a context that never saw the failure computes (bitwise).
 * Calls on one context from different streams are ordered: the results equal those of
-  the same calls on one stream."""
+  the same calls on one stream.
+* Marker ranges (DORY_TRACE=1) leave the results bitwise unchanged."""
 import pytest
 import torch
 
@@ -123,3 +124,25 @@ def test_misaligned_states_are_refused_before_any_work():
     torch.cuda.synchronize()
     assert state(rt, [0, 1]) == before
     rt.close()
+
+
+def test_trace_ranges_leave_results_unchanged(monkeypatch):
+    """With DORY_TRACE=1 every prefill and decode call pushes and pops marker ranges
+    through the platform's marker library; the results are bitwise those of untraced
+    calls. The library is loaded the way the runtime loads it."""
+    import ctypes
+    ctypes.CDLL("librocprofiler-sdk-roctx.so.1")  # the marker library the runtime opens
+    w = gpu_weights(S, 5)
+    X, xd = xin(300, 6), xin(2, 7)
+    out = []
+    for traced in (False, True):
+        if traced:
+            monkeypatch.setenv("DORY_TRACE", "1")
+        rt = DoryRuntime(S, w, max_loops=2, max_seqs=2, max_seq_len=512, max_rows=300, mode="per_loop", loops=2)
+        y0 = rt.prefill([0, 1], [200, 100], X)
+        y1 = rt.decode([0, 1], xd)
+        torch.cuda.synchronize()
+        out.append((y0.clone(), y1.clone()))
+        rt.close()
+    monkeypatch.delenv("DORY_TRACE")
+    assert torch.equal(out[0][0], out[1][0]) and torch.equal(out[0][1], out[1][1])
